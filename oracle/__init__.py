@@ -1,0 +1,21 @@
+"""fp64 CPU oracle for the GRPO loss hot path (test infrastructure only).
+
+Only tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package; the HIP library never does.
+"""
+
+from .grpo_oracle import (  # noqa: F401
+    REDUCTIONS,
+    LossConfig,
+    OracleInputError,
+    OracleResult,
+    group_advantages,
+    group_offsets,
+    grpo_advantages,
+    grpo_loss_fwd_bwd,
+    grpo_token_loss,
+    logits_rows,
+    row_logsumexp,
+    sequence_weights,
+    token_terms,
+)

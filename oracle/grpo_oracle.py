@@ -1,0 +1,411 @@
+"""Plain fp64 CPU oracle for the GRPO loss hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it.  It shares no code, constants or helpers with the HIP
+library under ``rl_post_loss_amd/``.
+
+Everything is computed in float64 with numpy (or Python floats, which are the
+same IEEE binary64), in the plain order the definitions give.  No blocking, no
+online softmax, no fusion: a reader can check each function against the pages.
+
+Sources, cited by page title and section:
+
+* [GRPO-LOSS]  RL-Kernel documentation, "GRPO Loss" (sections: Group
+  specification, Tensor Contract, Normalizer semantics, Accuracy).
+* [REAL-BLOG]  ms-swift blog post on the REAL loss, background section on the
+  GRPO objective and its per-token gradient weight (clip indicator times
+  A * e^s).
+* [RPP]        Relax documentation, "REINFORCE++ and REINFORCE++-baseline"
+  (sections: Notation and mask contract, PPO and KL reduction, Formula-level
+  comparison).
+* [GRPO-CPP]   grpo.cpp README (sections: The length-normalization detail,
+  CUDA).
+* [DOCKYARD]   dockyard_rl design doc, "GRPO and the clipped policy-gradient
+  loss" (sections: Advantage estimation, One loss many algorithms,
+  Reference-KL penalty).
+
+Readings taken where the pages are silent or ambiguous (each is listed in the
+repository design notes as well):
+
+* KL estimator: k3 = exp(d) - d - 1 with d = logp_ref - logp_theta; its
+  gradient with respect to logp_theta is the pathwise derivative 1 - exp(d)
+  (autograd of the loss as written), not a score-function variant.
+* Group std: population std (ddof = 0), floored at ``std_eps`` (default 1e-6).
+* Leave-one-out with std scaling divides the leave-one-out difference by the
+  whole group's population std.
+* Sequence-mean denominator: all B sequences, each sequence's own count
+  clamped to >= 1.
+* Length-alpha weighting: per-token weight L_i**(alpha - 1) / B, i.e. a total
+  weight of L_i**alpha / B for response i; 0 when L_i = 0.
+* Token-mean with no active token: weight 1 / max(N, 1); every term is then 0.
+* Clipping: a token is clipped only when rho lies strictly outside the band on
+  the side selected by the sign of A; at the exact bound the gradient still
+  flows (inclusive clamp, tie split of the minimum sums to the full gradient).
+* Masked slots are never read (boolean selection), so NaN/Inf or garbage ids
+  stored there cannot reach any output.
+
+Parity pins: every function here is pinned by CPU tests in
+``tests/test_oracle_pins.py`` (closed forms, library routines, finite
+differences, an independent autograd formulation, invariants).  The absolute
+loss values of the synthetic workloads are not printed by the pages, so those
+are pinned only through the checks above.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+REDUCTIONS = ("token_mean", "sequence_mean", "length_alpha")
+
+
+class OracleInputError(ValueError):
+    """Raised for inputs that violate the operation's contract."""
+
+
+# ---------------------------------------------------------------------------
+# Group specification  ([GRPO-LOSS] Group specification)
+# ---------------------------------------------------------------------------
+
+def group_offsets(B, samples_per_prompt=None, group_boundaries=None):
+    """CSR offsets (length G+1) describing the reward groups.
+
+    [GRPO-LOSS] Group specification: exactly one of a uniform
+    ``samples_per_prompt`` or CSR ``group_boundaries`` (offsets of length
+    num_groups + 1) is given.  Uniform groups need B to be a multiple of the
+    group size.  Groups must tile [0, B) in order, and a group needs at least
+    two members (a population std over one sample is rejected on the pages).
+    """
+    if (samples_per_prompt is None) == (group_boundaries is None):
+        raise OracleInputError("give exactly one of samples_per_prompt / group_boundaries")
+    if samples_per_prompt is not None:
+        n = int(samples_per_prompt)
+        if n < 2 or B % n != 0:
+            raise OracleInputError("samples_per_prompt must be >= 2 and divide B")
+        return np.arange(0, B + 1, n, dtype=np.int64)
+    off = np.asarray(group_boundaries, dtype=np.int64)
+    if off.ndim != 1 or off.size < 2 or off[0] != 0 or off[-1] != B:
+        raise OracleInputError("group_boundaries must start at 0 and end at B")
+    if np.any(np.diff(off) < 2):
+        raise OracleInputError("every group needs at least two members")
+    return off
+
+
+# ---------------------------------------------------------------------------
+# Group-relative advantages  ([GRPO-LOSS] Accuracy; [DOCKYARD] Advantage
+# estimation)
+# ---------------------------------------------------------------------------
+
+def group_advantages(rewards, offsets, leave_one_out=False, scale_by_std=True,
+                     std_eps=1e-6):
+    """Per-sequence advantage A_i, float64.
+
+    For a group g = [s, e) of n members, in index order:
+      S = sum of r (sequential), mean = S / n,
+      var = (sum of (r - mean)^2, sequential) / n, std = sqrt(var).
+    Baseline b_i = mean, or with leave-one-out b_i = (S - r_i) / (n - 1).
+    A_i = (r_i - b_i) / max(std, std_eps) when scaling by std, else r_i - b_i.
+    """
+    r = [float(v) for v in np.asarray(rewards, dtype=np.float64).ravel()]
+    A = np.zeros(len(r), dtype=np.float64)
+    for g in range(len(offsets) - 1):
+        s, e = int(offsets[g]), int(offsets[g + 1])
+        n = e - s
+        total = 0.0
+        for j in range(s, e):
+            total = total + r[j]
+        mean = total / n
+        sq = 0.0
+        for j in range(s, e):
+            dev = r[j] - mean
+            sq = sq + dev * dev
+        std = math.sqrt(sq / n)
+        denom = max(std, std_eps)
+        for j in range(s, e):
+            base = (total - r[j]) / (n - 1) if leave_one_out else mean
+            diff = r[j] - base
+            A[j] = diff / denom if scale_by_std else diff
+    return A
+
+
+# ---------------------------------------------------------------------------
+# Token counts and per-sequence weights  ([GRPO-LOSS] Normalizer semantics;
+# [RPP] PPO and KL reduction; [GRPO-CPP] The length-normalization detail)
+# ---------------------------------------------------------------------------
+
+def sequence_weights(mask, reduction="token_mean", alpha=None):
+    """Return (L [B] int64, N int, omega [B] float64).
+
+    omega_i is the weight every active token of sequence i carries in the
+    scalar loss:
+      token_mean     1 / max(N, 1)                 (global active-token mean)
+      sequence_mean  1 / (B * max(L_i, 1))          (mean within, then over B)
+      length_alpha   L_i**alpha / (B * L_i), 0 if L_i = 0
+    """
+    m = np.asarray(mask).astype(bool)
+    if m.ndim != 2:
+        raise OracleInputError("mask must be [B, T]")
+    B = m.shape[0]
+    L = m.sum(axis=1).astype(np.int64)
+    N = int(L.sum())
+    if reduction == "token_mean":
+        w = np.full(B, 1.0 / max(N, 1), dtype=np.float64)
+    elif reduction == "sequence_mean":
+        w = 1.0 / (float(B) * np.maximum(L, 1).astype(np.float64))
+    elif reduction == "length_alpha":
+        if alpha is None or not (0.0 <= alpha <= 1.0):
+            raise OracleInputError("length_alpha needs alpha in [0, 1]")
+        Lf = L.astype(np.float64)
+        if alpha == 0.0:
+            num = np.ones(B, dtype=np.float64)
+        elif alpha == 0.5:
+            num = np.sqrt(Lf)
+        elif alpha == 1.0:
+            num = Lf
+        else:
+            num = np.power(Lf, float(alpha))
+        w = np.where(L > 0, num / (float(B) * np.maximum(Lf, 1.0)), 0.0)
+    else:
+        raise OracleInputError(f"unknown reduction {reduction!r}")
+    return L, N, w
+
+
+# ---------------------------------------------------------------------------
+# Per-token objective  ([GRPO-LOSS] Accuracy; [REAL-BLOG] background;
+# [DOCKYARD] One loss many algorithms, Reference-KL penalty)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LossConfig:
+    """Objective settings.  A symmetric clip sets eps_low = eps_high."""
+    eps_low: float = 0.2
+    eps_high: float = 0.2
+    beta: float = 0.04
+    reduction: str = "token_mean"
+    alpha: float | None = None
+
+
+def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig):
+    """Per-token quantities, all float64 arrays of the broadcast shape.
+
+    rho   = exp(logp - old_logp)                          importance ratio
+    d     = logp_ref - logp,  k3 = exp(d) - d - 1         reference KL (k3)
+    loss  = -min(rho * A, clip(rho, 1 - eps_low, 1 + eps_high) * A)
+    clipped = (A > 0 and rho > 1 + eps_high) or (A < 0 and rho < 1 - eps_low)
+    dloss = d loss / d logp = -A * rho unless clipped, else 0
+    dkl   = d k3 / d logp   = 1 - exp(d)
+    """
+    logp = np.asarray(logp, dtype=np.float64)
+    old = np.asarray(old_logp, dtype=np.float64)
+    A = np.asarray(adv, dtype=np.float64)
+    rho = np.exp(logp - old)
+    if logp_ref is None:
+        d = np.zeros_like(logp)
+    else:
+        d = np.asarray(logp_ref, dtype=np.float64) - logp
+    k3 = np.expm1(d) - d
+    lo = 1.0 - cfg.eps_low
+    hi = 1.0 + cfg.eps_high
+    unclipped_obj = rho * A
+    clipped_obj = np.clip(rho, lo, hi) * A
+    loss = -np.minimum(unclipped_obj, clipped_obj)
+    clipped = ((A > 0) & (rho > hi)) | ((A < 0) & (rho < lo))
+    dloss = np.where(clipped, 0.0, -A * rho)
+    dkl = -np.expm1(d)
+    return dict(rho=rho, d=d, k3=k3, loss=loss, clipped=clipped, dloss=dloss, dkl=dkl)
+
+
+def _check_cfg(cfg: LossConfig, have_ref: bool):
+    if not (0.0 <= cfg.eps_low < 1.0) or cfg.eps_high < 0.0 or cfg.beta < 0.0:
+        raise OracleInputError("bad clip range or beta")
+    if cfg.beta > 0.0 and not have_ref:
+        raise OracleInputError("beta > 0 needs reference log-probs")
+    if cfg.reduction not in REDUCTIONS:
+        raise OracleInputError("unknown reduction")
+
+
+@dataclass
+class OracleResult:
+    loss: float
+    policy_loss: float
+    kl: float
+    advantages: np.ndarray          # [B] float64
+    seq_policy: np.ndarray          # [B] sum over active tokens of the token loss
+    seq_kl: np.ndarray              # [B] sum over active tokens of k3
+    seq_weight: np.ndarray          # [B] omega_i
+    seq_tokens: np.ndarray          # [B] L_i
+    num_tokens: int                 # N
+    clipped: int                    # number of clipped active tokens
+    tok: dict = field(default_factory=dict)   # per-token arrays [B, T] (0 at masked slots)
+    grad: np.ndarray | None = None  # d loss / d logits [B, T, V] or d loss / d logp [B, T]
+
+
+def _reduce(P, K, w, beta):
+    """Fixed-order scalar reduction: sum_i w_i * P_i, sum_i w_i * K_i."""
+    policy_loss = 0.0
+    kl = 0.0
+    for i in range(len(w)):
+        policy_loss = policy_loss + float(w[i]) * float(P[i])
+        kl = kl + float(w[i]) * float(K[i])
+    return policy_loss + beta * kl, policy_loss, kl
+
+
+# ---------------------------------------------------------------------------
+# Logprob-level token loss  ([GRPO-CPP] CUDA: the token-loss kernels take
+# per-token log-probs and return dlogp)
+# ---------------------------------------------------------------------------
+
+def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: LossConfig,
+                    grad_scale=1.0):
+    """GRPO loss from per-token log-probs.  ``grad`` is d loss / d logp [B, T].
+
+    ``groups`` is a dict with keys samples_per_prompt | group_boundaries and
+    optional leave_one_out, scale_by_std, std_eps.
+    """
+    logp = np.asarray(logp)
+    B, T = logp.shape
+    _check_cfg(cfg, ref_logp is not None)
+    m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    A = group_advantages(rewards, off, groups.get("leave_one_out", False),
+                         groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha)
+
+    ii, tt = np.nonzero(m)                      # boolean selection: masked slots never read
+    lp = np.asarray(logp, dtype=np.float64)[ii, tt]
+    old = np.asarray(old_logp, dtype=np.float64)[ii, tt]
+    ref = None if ref_logp is None else np.asarray(ref_logp, dtype=np.float64)[ii, tt]
+    terms = token_terms(lp, old, ref, A[ii], cfg)
+    return _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale,
+                     grad=None, logp_active=lp)
+
+
+def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_active):
+    P = np.zeros(B)
+    K = np.zeros(B)
+    C = np.zeros(B, dtype=np.int64)
+    # per-sequence sums (exactly rounded); ii is sorted, so each sequence's
+    # active tokens form one contiguous run
+    bounds = np.searchsorted(ii, np.arange(B + 1))
+    for i in range(B):
+        s, e = int(bounds[i]), int(bounds[i + 1])
+        P[i] = math.fsum(terms["loss"][s:e])
+        K[i] = math.fsum(terms["k3"][s:e])
+        C[i] = int(np.count_nonzero(terms["clipped"][s:e]))
+    loss, policy_loss, kl = _reduce(P, K, w, cfg.beta)
+    G = w[ii] * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
+    tok = {}
+    for name in ("rho", "d", "k3", "loss", "dloss", "dkl"):
+        full = np.zeros((B, T))
+        full[ii, tt] = terms[name]
+        tok[name] = full
+    full = np.zeros((B, T), dtype=bool)
+    full[ii, tt] = terms["clipped"]
+    tok["clipped"] = full
+    Gfull = np.zeros((B, T))
+    Gfull[ii, tt] = G
+    tok["G"] = Gfull
+    lfull = np.zeros((B, T))
+    lfull[ii, tt] = logp_active
+    tok["logp"] = lfull
+    if grad is None:
+        grad = Gfull.copy()           # token-level: d loss / d logp = m * G
+    return OracleResult(loss=loss, policy_loss=policy_loss, kl=kl, advantages=A,
+                        seq_policy=P, seq_kl=K, seq_weight=w, seq_tokens=L,
+                        num_tokens=N, clipped=int(C.sum()), tok=tok, grad=grad)
+
+
+# ---------------------------------------------------------------------------
+# Log-softmax of a vocabulary row  ([GRPO-LOSS] intro: ratio and KL come from
+# log-softmax over the vocabulary at the taken token)
+# ---------------------------------------------------------------------------
+
+def row_logsumexp(rows):
+    """log(sum_v exp(x_v)) per row, float64: M + log(sum exp(x - M))."""
+    x = np.asarray(rows, dtype=np.float64)
+    M = np.max(x, axis=-1, keepdims=True)
+    return (M + np.log(np.sum(np.exp(x - M), axis=-1, keepdims=True)))[..., 0]
+
+
+def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.0,
+                want_grad=True):
+    """Forward + gradient for a set of active rows (each row one token slot).
+
+    x_rows, y_rows: [n, V] policy / reference logits (y_rows may be None when
+    beta == 0); ids [n]; old [n]; adv [n] = A of the row's sequence; w [n] =
+    omega of the row's sequence.  Returns the per-row terms, LSEs, G and the
+    gradient rows g_v = G * (onehot(a)_v - softmax(x)_v).
+    """
+    x = np.asarray(x_rows, dtype=np.float64)
+    n, V = x.shape
+    ids = np.asarray(ids, dtype=np.int64)
+    if np.any(ids < 0) or np.any(ids >= V):
+        raise OracleInputError("action id out of range at an active slot")
+    r = np.arange(n)
+    lse = row_logsumexp(x)
+    logp = x[r, ids] - lse
+    if y_rows is not None:
+        y = np.asarray(y_rows, dtype=np.float64)
+        lse_ref = row_logsumexp(y)
+        logp_ref = y[r, ids] - lse_ref
+    else:
+        lse_ref = None
+        logp_ref = None
+    terms = token_terms(logp, old, logp_ref, adv, cfg)
+    G = np.asarray(w, dtype=np.float64) * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
+    out = dict(terms, lse=lse, lse_ref=lse_ref, logp=logp, logp_ref=logp_ref, G=G)
+    if want_grad:
+        p = np.exp(x - lse[:, None])
+        g = -G[:, None] * p
+        g[r, ids] = G * (1.0 - p[r, ids])
+        out["grad"] = g
+    return out
+
+
+def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, rewards, *,
+                      groups, cfg: LossConfig, grad_scale=1.0, want_grad=True,
+                      row_chunk=4096):
+    """GRPO loss and d loss / d policy_logits from [B, T, V] logits.
+
+    Masked rows get an all-zero gradient row and are never read.
+    """
+    x = np.asarray(policy_logits)
+    if x.ndim != 3:
+        raise OracleInputError("policy_logits must be [B, T, V]")
+    B, T, V = x.shape
+    _check_cfg(cfg, ref_logits is not None)
+    m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    A = group_advantages(rewards, off, groups.get("leave_one_out", False),
+                         groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha)
+    ii, tt = np.nonzero(m)
+    ids = np.asarray(action_ids)[ii, tt].astype(np.int64)
+    old = np.asarray(old_logps, dtype=np.float64)[ii, tt]
+    grad = np.zeros((B, T, V)) if want_grad else None
+    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "k3", "loss", "dloss", "dkl", "logp")}
+    acc["clipped"] = np.zeros(len(ii), dtype=bool)
+    for s in range(0, len(ii), row_chunk):
+        sl = slice(s, s + row_chunk)
+        xr = x[ii[sl], tt[sl]]
+        yr = None if ref_logits is None else np.asarray(ref_logits)[ii[sl], tt[sl]]
+        out = logits_rows(xr, yr, ids[sl], old[sl], A[ii[sl]], w[ii[sl]], cfg,
+                          grad_scale, want_grad)
+        for k in acc:
+            acc[k][sl] = out[k]
+        if want_grad:
+            grad[ii[sl], tt[sl]] = out["grad"]
+    res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=grad,
+                    logp_active=acc["logp"])
+    return res
+
+
+def grpo_advantages(rewards, *, groups):
+    """Advantages alone, as the boundary's advantage entry point returns them."""
+    r = np.asarray(rewards)
+    off = group_offsets(r.shape[0], groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    return group_advantages(r, off, groups.get("leave_one_out", False),
+                            groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
