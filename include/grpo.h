@@ -1,0 +1,246 @@
+/*
+ * libgrpo -- the GRPO loss hot path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a plain pointer plus sizes; no framework
+ * types appear here.  Pointers are DEVICE pointers unless a comment says
+ * HOST.  Every entry point is asynchronous on the given HIP stream (passed as
+ * `void *stream`, a hipStream_t; NULL selects the default stream) and never
+ * synchronises the host; results are valid once the stream reaches them.
+ * The library never allocates or frees memory: the caller owns every buffer,
+ * including the workspace sized by grpo_workspace_bytes().
+ *
+ * What is computed follows these pages (cited by title and section):
+ *   [GRPO-LOSS]  RL-Kernel docs, "GRPO Loss": Entry Point, Group
+ *                specification, Tensor Contract, Normalizer semantics,
+ *                Accuracy.
+ *   [REAL-BLOG]  ms-swift blog on the REAL loss, background: the GRPO
+ *                objective and its per-token gradient weight.
+ *   [RPP]        Relax docs, "REINFORCE++ and REINFORCE++-baseline": Notation
+ *                and mask contract, PPO and KL reduction.
+ *   [GRPO-CPP]   grpo.cpp README: The length-normalization detail, CUDA.
+ *   [DOCKYARD]   dockyard_rl, "GRPO and the clipped policy-gradient loss":
+ *                Advantage estimation, One loss many algorithms,
+ *                Reference-KL penalty.
+ *
+ * Objective (per active token (i, t) of sequence i, action a = action_ids[i,t]):
+ *   logp     = log softmax(policy_logits[i,t,:])[a]
+ *   logp_ref = log softmax(ref_logits[i,t,:])[a]
+ *   rho      = exp(logp - old_logps[i,t])
+ *   d        = logp_ref - logp,   k3 = exp(d) - d - 1
+ *   l        = -min(rho * A_i, clip(rho, 1 - eps_low, 1 + eps_high) * A_i)
+ *   policy_loss = sum_i w_i * sum_t m_it * l_it,   kl = sum_i w_i * sum_t m_it * k3_it
+ *   loss        = policy_loss + beta * kl
+ * with A_i the group-relative advantage and w_i the per-sequence token weight
+ * of the chosen reduction (see grpo_reduction).  The gradient is analytic:
+ *   d loss / d logits[i,t,v] = G_it * (onehot(a)_v - softmax(policy_logits[i,t,:])_v)
+ *   G_it = w_i * grad_scale * ( (clipped ? 0 : -A_i * rho) + beta * (1 - exp(d)) )
+ * A token is clipped when rho lies strictly outside [1 - eps_low, 1 + eps_high]
+ * on the side that the sign of A_i selects; at the exact bound the gradient
+ * flows.
+ *
+ * Masks: a nonzero byte marks an active slot ([GRPO-LOSS] Tensor Contract;
+ * torch.bool and uint8 both work).  Selection is boolean ([RPP] Notation and
+ * mask contract): values stored at masked slots never influence any result,
+ * and masked logits rows are not read at all.
+ *
+ * Determinism: there are no floating-point atomics.  Every reduction runs in
+ * a fixed order, so repeated calls with the same inputs and sizes give
+ * bit-identical outputs.
+ *
+ * Workspace: grpo_workspace_bytes() bytes of device memory, 256-byte aligned,
+ * ZERO-FILLED before its first use (grpo_workspace_init() does that).  The
+ * library keeps its internal completion counters at zero at the end of every
+ * call, so a workspace can be reused without clearing it again.  A workspace
+ * serves one call at a time: calls that share a workspace must be ordered on
+ * one stream.  grpo_loss_fwd_bwd() with grad_out == NULL leaves per-row
+ * state in the workspace that grpo_loss_bwd() consumes; it stays valid until
+ * the next call that uses the same workspace.
+ *
+ * Errors: every entry point validates its arguments on the host and returns a
+ * grpo_status without launching anything when they are wrong.  Faults that
+ * depend on device data are reported as bits in outputs->status (see
+ * GRPO_FAULT_*), never by reading or writing out of bounds.
+ */
+#ifndef GRPO_H
+#define GRPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GRPO_ABI_VERSION 1
+
+#ifndef GRPO_API
+#define GRPO_API __attribute__((visibility("default")))
+#endif
+
+typedef enum grpo_status {
+  GRPO_OK = 0,
+  GRPO_ERR_NULL = 1,       /* a required pointer is NULL */
+  GRPO_ERR_SHAPE = 2,      /* B, T or V not positive, a row stride < V, or sizes overflow */
+  GRPO_ERR_DTYPE = 3,      /* unknown dtype code */
+  GRPO_ERR_GROUPS = 4,     /* group specification invalid ([GRPO-LOSS] Group specification) */
+  GRPO_ERR_CONFIG = 5,     /* eps/beta/reduction/alpha invalid, or beta > 0 without a reference */
+  GRPO_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or smaller than grpo_workspace_bytes() */
+  GRPO_ERR_ALIAS = 7,      /* grad_out overlaps policy_logits without being exactly in place */
+  GRPO_ERR_HIP = 8         /* a HIP runtime call or kernel launch failed */
+} grpo_status;
+
+/* Floating-point storage of logits and gradients. */
+typedef enum grpo_fdtype { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_fdtype;
+
+/* Integer storage of action ids. */
+typedef enum grpo_idtype { GRPO_I64 = 0, GRPO_I32 = 1 } grpo_idtype;
+
+/* Per-sequence token weight w_i ([GRPO-LOSS] Normalizer semantics; [RPP] PPO
+ * and KL reduction; [GRPO-CPP] The length-normalization detail).  L_i is the
+ * number of active tokens of sequence i and N = sum_i L_i.
+ *   GRPO_TOKEN_MEAN     w_i = 1 / max(N, 1)              (global token mean)
+ *   GRPO_SEQUENCE_MEAN  w_i = 1 / (B * max(L_i, 1))      (mean in sequence, then over B)
+ *   GRPO_LENGTH_ALPHA   w_i = L_i^alpha / (B * L_i), 0 when L_i = 0
+ * The weights are computed in binary64 and are bit-exact for alpha in
+ * {0, 0.5, 1}; other alpha use pow() and may differ in the last bit. */
+typedef enum grpo_reduction {
+  GRPO_TOKEN_MEAN = 0,
+  GRPO_SEQUENCE_MEAN = 1,
+  GRPO_LENGTH_ALPHA = 2
+} grpo_reduction;
+
+/* Device-detected data faults, OR-ed into outputs->status (which each call
+ * overwrites). */
+#define GRPO_FAULT_BAD_ACTION 1u  /* an active slot's action id is outside [0, V): that slot
+                                     contributes no loss, no KL and a zero gradient row */
+#define GRPO_FAULT_NO_TOKENS 2u   /* no active token at all (N = 0): loss = 0, gradient = 0 */
+#define GRPO_FAULT_NONFINITE 4u   /* a non-finite per-token value at an active slot */
+
+/* Reward groups ([GRPO-LOSS] Group specification; [DOCKYARD] Advantage
+ * estimation).  Give exactly one of samples_per_prompt > 0 (uniform groups,
+ * B must be a multiple) or group_boundaries (CSR offsets, HOST memory,
+ * num_groups + 1 strictly increasing entries from 0 to B).  Every group needs
+ * at least two members.  Advantages, per group g = [s, e) of n members, in
+ * binary64 and index order:
+ *   S = sum r, mean = S / n, var = sum (r - mean)^2 / n, std = sqrt(var)
+ *   baseline b_i = mean, or (S - r_i) / (n - 1) with leave_one_out
+ *   A_i = (r_i - b_i) / max(std, std_eps) if scale_by_std, else r_i - b_i
+ * rounded once to float.  With leave_one_out the difference is divided by
+ * the whole group's population std. */
+typedef struct grpo_groups {
+  int32_t samples_per_prompt;       /* > 1, or 0 when group_boundaries is given */
+  int32_t num_groups;               /* CSR: number of groups; ignored for uniform groups */
+  const int64_t *group_boundaries;  /* HOST pointer or NULL; copied during the call */
+  int32_t leave_one_out;            /* 0 or 1 */
+  int32_t scale_by_std;             /* 0 or 1 (the usual GRPO setting is 1) */
+  double std_eps;                   /* floor of the std, > 0 (usually 1e-6) */
+} grpo_groups;
+
+/* Objective settings.  A symmetric clip sets eps_low == eps_high. */
+typedef struct grpo_cfg {
+  double eps_low;     /* in [0, 1) */
+  double eps_high;    /* >= 0 */
+  double beta;        /* reference-KL coefficient, >= 0 */
+  int32_t reduction;  /* grpo_reduction */
+  double alpha;       /* in [0, 1]; used by GRPO_LENGTH_ALPHA only */
+} grpo_cfg;
+
+/* Outputs (DEVICE pointers).  Only `scalars` is required; any other field may
+ * be NULL.  Per-sequence arrays have B entries; per-token arrays B * T
+ * (row-major [B, T], 0 at masked slots). */
+typedef struct grpo_outputs {
+  float *scalars;      /* [3] loss, policy_loss, kl (float32) */
+  float *advantages;   /* [B] A_i */
+  float *seq_policy;   /* [B] sum over the sequence's active tokens of l */
+  float *seq_kl;       /* [B] sum over the sequence's active tokens of k3 */
+  float *seq_weight;   /* [B] w_i */
+  int32_t *seq_tokens; /* [B] L_i */
+  int64_t *counts;     /* [2] N (active tokens), number of clipped active tokens */
+  uint32_t *status;    /* [1] GRPO_FAULT_* bits of this call */
+  float *tok_logp;     /* [B*T] logp of the taken token (logits entry points only) */
+  float *tok_loss;     /* [B*T] token loss l */
+  float *tok_kl;       /* [B*T] k3 */
+} grpo_outputs;
+
+/* ABI version of the loaded library (GRPO_ABI_VERSION it was built with). */
+GRPO_API int grpo_abi_version(void);
+
+/* Static text for a status code. */
+GRPO_API const char *grpo_status_str(int status);
+
+/* Workspace bytes needed for B sequences of T slots and, for CSR groups,
+ * num_groups groups (pass 0 for uniform groups).  Returns 0 when the sizes
+ * are not positive or overflow.  One workspace of this size serves every
+ * entry point below for these sizes. */
+GRPO_API size_t grpo_workspace_bytes(int64_t B, int64_t T, int32_t num_groups);
+
+/* Zero-fills a workspace (needed once, before its first use). */
+GRPO_API grpo_status grpo_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Group-relative advantages alone ([GRPO-LOSS] Accuracy; [DOCKYARD]
+ * Advantage estimation).  rewards: [B] float32.  adv_out: [B] float32. */
+GRPO_API grpo_status grpo_advantages(const float *rewards, int64_t B, const grpo_groups *groups,
+                            float *adv_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Logprob-level token loss ([GRPO-CPP] CUDA: token loss from per-token
+ * log-probs, returning dlogp).  logp, old_logp, ref_logp: [B, T] float32,
+ * contiguous; ref_logp may be NULL only when beta == 0 (then d = 0).
+ * mask: [B, T] bytes or NULL (all active).  rewards: [B] float32.
+ * dlogp_out: [B, T] float32, d loss / d logp (0 at masked slots), or NULL
+ * for the forward only.  grad_scale: device float scalar multiplying every
+ * gradient, or NULL for 1.  The per-token outputs tok_logp are not written
+ * by this entry point. */
+GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, const float *ref_logp,
+                            const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
+                            const grpo_groups *groups, const grpo_cfg *cfg, float *dlogp_out,
+                            const float *grad_scale, const grpo_outputs *out, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Fused loss forward + analytic backward from vocabulary logits
+ * ([GRPO-LOSS] Entry Point, Tensor Contract; [GRPO-CPP] CUDA, fused
+ * logits boundary).
+ *   policy_logits, ref_logits: [B, T, V] in logits_dtype, row (i, t) starting
+ *     at element (i*T + t) * row_stride, row_stride >= V.  ref_logits may be
+ *     NULL only when beta == 0.  ref_logits may equal policy_logits.
+ *   action_ids: [B, T] in ids_dtype, contiguous.
+ *   old_logps: [B, T] float32.  mask: [B, T] bytes or NULL.  rewards: [B].
+ *   grad_out: [B, T, V] in grad_dtype with row stride grad_row_stride >= V;
+ *     masked rows are written with zeros.  grad_out may be policy_logits
+ *     itself (in place; then grad_dtype, grad_row_stride must equal
+ *     logits_dtype, row_stride).  grad_out == NULL runs the forward only and
+ *     keeps per-row state in the workspace for grpo_loss_bwd().
+ *   grad_scale: device float scalar (autograd's upstream gradient) or NULL
+ *     for 1.
+ * Vector (16-byte) loads are used when every row of every logits/grad tensor
+ * is 16-byte aligned; other layouts take a slower scalar path. */
+GRPO_API grpo_status grpo_loss_fwd_bwd(const void *policy_logits, const void *ref_logits,
+                              int32_t logits_dtype, int64_t row_stride, const void *action_ids,
+                              int32_t ids_dtype, const float *old_logps, const uint8_t *mask,
+                              const float *rewards, int64_t B, int64_t T, int64_t V,
+                              const grpo_groups *groups, const grpo_cfg *cfg, void *grad_out,
+                              int32_t grad_dtype, int64_t grad_row_stride,
+                              const float *grad_scale, const grpo_outputs *out, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* Backward of a preceding grpo_loss_fwd_bwd(..., grad_out = NULL, ...) call on
+ * the same workspace and the same policy_logits/action_ids/mask/sizes:
+ * writes d loss / d policy_logits, multiplied by *grad_scale (device float,
+ * NULL = 1) on top of any scale the forward applied. */
+GRPO_API grpo_status grpo_loss_bwd(const void *policy_logits, int32_t logits_dtype, int64_t row_stride,
+                          const void *action_ids, int32_t ids_dtype, const uint8_t *mask,
+                          int64_t B, int64_t T, int64_t V, void *grad_out, int32_t grad_dtype,
+                          int64_t grad_row_stride, const float *grad_scale, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Optional timing hook for profiling tools: when both are non-NULL, the
+ * logits entry points record `start` right before and `stop` right after
+ * the launch of their vocabulary-streaming kernel, on the call's stream.
+ * The events are hipEvent_t handles owned by the caller; pass NULLs to turn
+ * the hook off.  Not thread-safe: set it from the thread that launches. */
+GRPO_API void grpo_set_timing_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_H */

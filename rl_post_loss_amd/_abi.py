@@ -1,0 +1,100 @@
+"""ctypes declarations mirroring include/grpo.h (argument marshalling only)."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgrpo.so")
+
+GRPO_ABI_VERSION = 1
+
+GRPO_F32, GRPO_BF16 = 0, 1
+GRPO_I64, GRPO_I32 = 0, 1
+GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA = 0, 1, 2
+REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE_MEAN,
+                   "length_alpha": GRPO_LENGTH_ALPHA}
+
+GRPO_FAULT_BAD_ACTION = 1
+GRPO_FAULT_NO_TOKENS = 2
+GRPO_FAULT_NONFINITE = 4
+
+STATUS_NAMES = {0: "GRPO_OK", 1: "GRPO_ERR_NULL", 2: "GRPO_ERR_SHAPE", 3: "GRPO_ERR_DTYPE",
+                4: "GRPO_ERR_GROUPS", 5: "GRPO_ERR_CONFIG", 6: "GRPO_ERR_WORKSPACE",
+                7: "GRPO_ERR_ALIAS", 8: "GRPO_ERR_HIP"}
+
+# Every function the header declares, with its ctypes signature.
+vp = C.c_void_p
+i32, i64, sz, f64 = C.c_int32, C.c_int64, C.c_size_t, C.c_double
+
+
+class GrpoGroups(C.Structure):
+    _fields_ = [("samples_per_prompt", i32), ("num_groups", i32),
+                ("group_boundaries", C.POINTER(C.c_int64)), ("leave_one_out", i32),
+                ("scale_by_std", i32), ("std_eps", f64)]
+
+
+class GrpoCfg(C.Structure):
+    _fields_ = [("eps_low", f64), ("eps_high", f64), ("beta", f64), ("reduction", i32),
+                ("alpha", f64)]
+
+
+class GrpoOutputs(C.Structure):
+    _fields_ = [("scalars", vp), ("advantages", vp), ("seq_policy", vp), ("seq_kl", vp),
+                ("seq_weight", vp), ("seq_tokens", vp), ("counts", vp), ("status", vp),
+                ("tok_logp", vp), ("tok_loss", vp), ("tok_kl", vp)]
+
+
+SIGNATURES = {
+    "grpo_abi_version": (C.c_int, []),
+    "grpo_status_str": (C.c_char_p, [C.c_int]),
+    "grpo_workspace_bytes": (sz, [i64, i64, i32]),
+    "grpo_workspace_init": (C.c_int, [vp, sz, vp]),
+    "grpo_advantages": (C.c_int, [vp, i64, C.POINTER(GrpoGroups), vp, vp, sz, vp]),
+    "grpo_token_loss": (C.c_int, [vp, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
+                                  C.POINTER(GrpoCfg), vp, vp, C.POINTER(GrpoOutputs), vp, sz,
+                                  vp]),
+    "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, i64, i64, i64,
+                                    C.POINTER(GrpoGroups), C.POINTER(GrpoCfg), vp, i32, i64, vp,
+                                    C.POINTER(GrpoOutputs), vp, sz, vp]),
+    "grpo_loss_bwd": (C.c_int, [vp, i32, i64, vp, i32, vp, i64, i64, i64, vp, i32, i64, vp, vp,
+                                sz, vp]),
+    "grpo_set_timing_events": (None, [vp, vp]),
+}
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Loads libgrpo.so (built in-tree) and declares its signatures.  Raises
+    RuntimeError if the library is missing: there is no fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libgrpo.so not found at {p}; build it with "
+                           "`python -m rl_post_loss_amd.build` (hipcc, gfx950)")
+    lib = C.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.grpo_abi_version() != GRPO_ABI_VERSION:
+        raise RuntimeError("libgrpo ABI version mismatch")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class GrpoError(RuntimeError):
+    def __init__(self, code, lib=None):
+        text = lib.grpo_status_str(code).decode() if lib is not None else ""
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {text}")
+        self.code = code
+
+
+def check(code, lib):
+    if code != 0:
+        raise GrpoError(code, lib)

@@ -1,0 +1,420 @@
+// libgrpo C ABI: argument validation, workspace layout and kernel launches.
+// The declarations, with the meaning, layout, ownership and error behaviour of
+// every argument, are in include/grpo.h.
+
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/grpo.h"
+#include "grpo_internal.hpp"
+
+namespace grpo {
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_token(const TokenArgs& a, hipStream_t stream);
+hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
+}  // namespace grpo
+
+using namespace grpo;
+
+namespace {
+
+hipEvent_t g_ev_start = nullptr;
+hipEvent_t g_ev_stop = nullptr;
+
+// Largest element count we accept for one tensor: keeps every byte offset
+// far inside int64 and every row index inside the kernels' arithmetic.
+constexpr int64_t kMaxElems = int64_t(1) << 50;
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
+  if (a <= 0 || b <= 0) return false;
+  if (a > limit / b) return false;
+  *out = a * b;
+  return true;
+}
+
+// Validated group description.  For CSR groups the host offsets are checked
+// here and copied into the workspace by the caller of check_groups.
+grpo_status check_groups(const grpo_groups* g, int64_t B) {
+  if (!g) return GRPO_ERR_NULL;
+  const bool uniform = g->samples_per_prompt > 0;
+  const bool csr = g->group_boundaries != nullptr;
+  if (uniform == csr) return GRPO_ERR_GROUPS;
+  if (g->leave_one_out != 0 && g->leave_one_out != 1) return GRPO_ERR_GROUPS;
+  if (g->scale_by_std != 0 && g->scale_by_std != 1) return GRPO_ERR_GROUPS;
+  if (!(g->std_eps > 0.0) || !isfinite(g->std_eps)) return GRPO_ERR_GROUPS;
+  if (uniform) {
+    if (g->samples_per_prompt < 2 || B % g->samples_per_prompt != 0) return GRPO_ERR_GROUPS;
+    return GRPO_OK;
+  }
+  if (g->num_groups < 1) return GRPO_ERR_GROUPS;
+  const int64_t* o = g->group_boundaries;
+  if (o[0] != 0 || o[g->num_groups] != B) return GRPO_ERR_GROUPS;
+  for (int32_t k = 0; k < g->num_groups; ++k)
+    if (o[k + 1] - o[k] < 2) return GRPO_ERR_GROUPS;
+  return GRPO_OK;
+}
+
+grpo_status check_cfg(const grpo_cfg* c, bool has_ref) {
+  if (!c) return GRPO_ERR_NULL;
+  if (!(c->eps_low >= 0.0 && c->eps_low < 1.0)) return GRPO_ERR_CONFIG;
+  if (!(c->eps_high >= 0.0) || !isfinite(c->eps_high)) return GRPO_ERR_CONFIG;
+  if (!(c->beta >= 0.0) || !isfinite(c->beta)) return GRPO_ERR_CONFIG;
+  if (c->beta > 0.0 && !has_ref) return GRPO_ERR_CONFIG;
+  if (c->reduction < GRPO_TOKEN_MEAN || c->reduction > GRPO_LENGTH_ALPHA) return GRPO_ERR_CONFIG;
+  if (c->reduction == GRPO_LENGTH_ALPHA && !(c->alpha >= 0.0 && c->alpha <= 1.0))
+    return GRPO_ERR_CONFIG;
+  return GRPO_OK;
+}
+
+struct Ws {
+  WsLayout l;
+  char* base;
+  WsHeader* hdr() const { return reinterpret_cast<WsHeader*>(base + l.hdr); }
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(base + off); }
+};
+
+grpo_status check_ws(void* ws, size_t ws_bytes, int64_t B, int64_t T, int32_t num_groups, Ws* out) {
+  if (!ws) return GRPO_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return GRPO_ERR_WORKSPACE;
+  const size_t need = grpo_workspace_bytes(B, T, num_groups);
+  if (need == 0) return GRPO_ERR_SHAPE;
+  if (ws_bytes < need) return GRPO_ERR_WORKSPACE;
+  out->l = ws_layout(B, T, num_groups);
+  out->base = static_cast<char*>(ws);
+  return GRPO_OK;
+}
+
+// Prep launch shared by every entry point: copies CSR offsets, then counts,
+// advantages and (optionally) weights.
+grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int64_t B, int64_t T,
+                     const grpo_groups* g, const grpo_cfg* cfg, bool want_weights,
+                     const grpo_outputs* out, float* adv_out, hipStream_t s) {
+  PrepArgs a{};
+  a.mask = mask;
+  a.rewards = rewards;
+  a.B = B;
+  a.T = T;
+  a.spp = g->samples_per_prompt;
+  a.num_groups = g->samples_per_prompt > 0 ? 0 : g->num_groups;
+  a.offsets = nullptr;
+  if (a.num_groups > 0) {
+    int64_t* dev = w.at<int64_t>(w.l.offsets);
+    if (hipMemcpyAsync(dev, g->group_boundaries, size_t(a.num_groups + 1) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return GRPO_ERR_HIP;
+    a.offsets = dev;
+  }
+  a.leave_one_out = g->leave_one_out;
+  a.scale_by_std = g->scale_by_std;
+  a.std_eps = g->std_eps;
+  a.reduction = cfg ? cfg->reduction : GRPO_TOKEN_MEAN;
+  a.alpha = cfg ? cfg->alpha : 0.0;
+  a.want_weights = want_weights ? 1 : 0;
+  a.hdr = w.hdr();
+  a.L = w.at<int32_t>(w.l.L);
+  a.A = w.at<float>(w.l.A);
+  a.w = w.at<double>(w.l.w);
+  a.adv_out = adv_out ? adv_out : (out ? out->advantages : nullptr);
+  a.seq_weight_out = out ? out->seq_weight : nullptr;
+  a.seq_tokens_out = out ? out->seq_tokens : nullptr;
+  return launch_prep(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+int fdtype_size(int32_t dt) { return dt == GRPO_F32 ? 4 : (dt == GRPO_BF16 ? 2 : 0); }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int choose_nt(int64_t V, int esize) {
+  const int64_t bytes = V * esize;
+  if (bytes <= 4096) return 64;
+  if (bytes <= 65536) return 256;
+  return 512;
+}
+
+}  // namespace
+
+extern "C" {
+
+int grpo_abi_version(void) { return GRPO_ABI_VERSION; }
+
+const char* grpo_status_str(int status) {
+  switch (status) {
+    case GRPO_OK: return "ok";
+    case GRPO_ERR_NULL: return "a required pointer is NULL";
+    case GRPO_ERR_SHAPE: return "invalid or overflowing sizes or row stride";
+    case GRPO_ERR_DTYPE: return "unknown dtype";
+    case GRPO_ERR_GROUPS: return "invalid group specification";
+    case GRPO_ERR_CONFIG: return "invalid loss configuration";
+    case GRPO_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GRPO_ERR_ALIAS: return "gradient output overlaps an input without being exactly in place";
+    case GRPO_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t grpo_workspace_bytes(int64_t B, int64_t T, int32_t num_groups) {
+  int64_t rows;
+  if (!mul_ok(B, T, kMaxElems, &rows)) return 0;
+  if (num_groups < 0 || num_groups > B) return 0;
+  return ws_layout(B, T, num_groups).total;
+}
+
+grpo_status grpo_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return GRPO_ERR_WORKSPACE;
+  return launch_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? GRPO_OK
+                                                                                    : GRPO_ERR_HIP;
+}
+
+void grpo_set_timing_events(void* start, void* stop) {
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+}
+
+grpo_status grpo_advantages(const float* rewards, int64_t B, const grpo_groups* groups,
+                            float* adv_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!rewards || !adv_out || !groups) return GRPO_ERR_NULL;
+  if (B <= 0 || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  grpo_status st = check_groups(groups, B);
+  if (st != GRPO_OK) return st;
+  const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
+  Ws w;
+  st = check_ws(ws, ws_bytes, B, 1, ng, &w);
+  if (st != GRPO_OK) return st;
+  return run_prep(w, rewards, nullptr, B, 0, groups, nullptr, false, nullptr, adv_out,
+                  static_cast<hipStream_t>(stream));
+}
+
+grpo_status grpo_token_loss(const float* logp, const float* old_logp, const float* ref_logp,
+                            const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
+                            const grpo_groups* groups, const grpo_cfg* cfg, float* dlogp_out,
+                            const float* grad_scale, const grpo_outputs* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!logp || !old_logp || !rewards || !out || !out->scalars) return GRPO_ERR_NULL;
+  int64_t rows;
+  if (!mul_ok(B, T, kMaxElems, &rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  grpo_status st = check_groups(groups, B);
+  if (st != GRPO_OK) return st;
+  st = check_cfg(cfg, ref_logp != nullptr);
+  if (st != GRPO_OK) return st;
+  const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
+  Ws w;
+  st = check_ws(ws, ws_bytes, B, T, ng, &w);
+  if (st != GRPO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s);
+  if (st != GRPO_OK) return st;
+  TokenArgs a{};
+  a.logp = logp;
+  a.old = old_logp;
+  a.ref = ref_logp;
+  a.mask = mask;
+  a.B = B;
+  a.T = T;
+  a.lo = float(1.0 - cfg->eps_low);
+  a.hi = float(1.0 + cfg->eps_high);
+  a.beta = float(cfg->beta);
+  a.grad_scale = grad_scale;
+  a.dlogp = dlogp_out;
+  a.hdr = w.hdr();
+  a.A = w.at<float>(w.l.A);
+  a.w = w.at<double>(w.l.w);
+  a.P = w.at<double>(w.l.P);
+  a.K = w.at<double>(w.l.K);
+  a.C = w.at<int64_t>(w.l.C);
+  a.scalars = out->scalars;
+  a.seq_policy = out->seq_policy;
+  a.seq_kl = out->seq_kl;
+  a.counts = out->counts;
+  a.status = out->status;
+  a.out_loss = out->tok_loss;
+  a.out_kl = out->tok_kl;
+  return launch_token(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype,
+                                        int64_t row_stride, const void* action_ids,
+                                        int32_t ids_dtype, int64_t B, int64_t T, int64_t V,
+                                        void* grad_out, int32_t grad_dtype,
+                                        int64_t grad_row_stride, int64_t* rows) {
+  if (!policy || !action_ids) return GRPO_ERR_NULL;
+  if (fdtype_size(logits_dtype) == 0 || (ids_dtype != GRPO_I64 && ids_dtype != GRPO_I32))
+    return GRPO_ERR_DTYPE;
+  if (grad_out && fdtype_size(grad_dtype) == 0) return GRPO_ERR_DTYPE;
+  int64_t tmp;
+  if (!mul_ok(B, T, kMaxElems, rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if (V <= 0 || row_stride < V || !mul_ok(*rows, row_stride, kMaxElems, &tmp))
+    return GRPO_ERR_SHAPE;
+  if (V > (int64_t(1) << 40)) return GRPO_ERR_SHAPE;
+  if (grad_out && (grad_row_stride < V || !mul_ok(*rows, grad_row_stride, kMaxElems, &tmp)))
+    return GRPO_ERR_SHAPE;
+  return GRPO_OK;
+}
+
+static grpo_status check_alias(const void* policy, const void* ref, int32_t logits_dtype,
+                               int64_t row_stride, int64_t rows, int64_t V, const void* grad_out,
+                               int32_t grad_dtype, int64_t grad_row_stride) {
+  if (!grad_out) return GRPO_OK;
+  const size_t xs = size_t((rows - 1) * row_stride + V) * size_t(fdtype_size(logits_dtype));
+  const size_t gs = size_t((rows - 1) * grad_row_stride + V) * size_t(fdtype_size(grad_dtype));
+  if (grad_out == policy) {
+    if (grad_dtype != logits_dtype || grad_row_stride != row_stride) return GRPO_ERR_ALIAS;
+  } else if (overlaps(grad_out, gs, policy, xs)) {
+    return GRPO_ERR_ALIAS;
+  }
+  if (ref && ref != policy && overlaps(grad_out, gs, ref, xs)) return GRPO_ERR_ALIAS;
+  return GRPO_OK;
+}
+
+static bool rows_vectorizable(const void* x, const void* y, int64_t ld, int32_t xdt, const void* g,
+                              int64_t ldg, int32_t gdt) {
+  const uintptr_t m = 15;
+  if ((reinterpret_cast<uintptr_t>(x) & m) || (reinterpret_cast<uintptr_t>(y) & m)) return false;
+  if ((ld * fdtype_size(xdt)) & 15) return false;
+  if (g && ((reinterpret_cast<uintptr_t>(g) & m) || ((ldg * fdtype_size(gdt)) & 15))) return false;
+  return true;
+}
+
+grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
+                              int32_t logits_dtype, int64_t row_stride, const void* action_ids,
+                              int32_t ids_dtype, const float* old_logps, const uint8_t* mask,
+                              const float* rewards, int64_t B, int64_t T, int64_t V,
+                              const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
+                              int32_t grad_dtype, int64_t grad_row_stride,
+                              const float* grad_scale, const grpo_outputs* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!old_logps || !rewards || !out || !out->scalars) return GRPO_ERR_NULL;
+  int64_t rows = 0;
+  grpo_status st = logits_common_checks(policy_logits, logits_dtype, row_stride, action_ids,
+                                        ids_dtype, B, T, V, grad_out, grad_dtype,
+                                        grad_row_stride, &rows);
+  if (st != GRPO_OK) return st;
+  st = check_groups(groups, B);
+  if (st != GRPO_OK) return st;
+  st = check_cfg(cfg, ref_logits != nullptr);
+  if (st != GRPO_OK) return st;
+  st = check_alias(policy_logits, ref_logits, logits_dtype, row_stride, rows, V, grad_out,
+                   grad_dtype, grad_row_stride);
+  if (st != GRPO_OK) return st;
+  const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
+  Ws w;
+  st = check_ws(ws, ws_bytes, B, T, ng, &w);
+  if (st != GRPO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s);
+  if (st != GRPO_OK) return st;
+
+  RowArgs a{};
+  a.x = policy_logits;
+  a.y = ref_logits;
+  a.ld = row_stride;
+  a.ids = action_ids;
+  a.ids_i32 = ids_dtype == GRPO_I32 ? 1 : 0;
+  a.old = old_logps;
+  a.mask = mask;
+  a.T = T;
+  a.V = V;
+  a.rows = rows;
+  a.lo = float(1.0 - cfg->eps_low);
+  a.hi = float(1.0 + cfg->eps_high);
+  a.beta = float(cfg->beta);
+  a.grad_scale = grad_scale;
+  a.g = grad_out;
+  a.ldg = grad_out ? grad_row_stride : 0;
+  a.hdr = w.hdr();
+  a.A = w.at<float>(w.l.A);
+  a.w = w.at<double>(w.l.w);
+  a.tok_loss = w.at<float>(w.l.tok_loss);
+  a.tok_kl = w.at<float>(w.l.tok_kl);
+  a.flags = w.at<uint8_t>(w.l.flags);
+  a.stash = w.at<RowStash>(w.l.stash);
+  a.out_logp = out->tok_logp;
+  a.out_loss = out->tok_loss;
+  a.out_kl = out->tok_kl;
+  RowLaunch l{};
+  l.mode = grad_out ? 0 : 1;
+  l.tin_bf16 = logits_dtype == GRPO_BF16;
+  l.tg_bf16 = grad_out ? (grad_dtype == GRPO_BF16) : l.tin_bf16;
+  l.nt = choose_nt(V, fdtype_size(logits_dtype));
+  l.vec = rows_vectorizable(policy_logits, ref_logits, row_stride, logits_dtype, grad_out,
+                            grad_row_stride, grad_dtype);
+  const bool timed = g_ev_start && g_ev_stop;
+  if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
+
+  ReduceArgs r{};
+  r.B = B;
+  r.T = T;
+  r.beta = float(cfg->beta);
+  r.hdr = w.hdr();
+  r.tok_loss = a.tok_loss;
+  r.tok_kl = a.tok_kl;
+  r.flags = a.flags;
+  r.w = a.w;
+  r.P = w.at<double>(w.l.P);
+  r.K = w.at<double>(w.l.K);
+  r.C = w.at<int64_t>(w.l.C);
+  r.scalars = out->scalars;
+  r.seq_policy = out->seq_policy;
+  r.seq_kl = out->seq_kl;
+  r.counts = out->counts;
+  r.status = out->status;
+  return launch_reduce(r, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64_t row_stride,
+                          const void* action_ids, int32_t ids_dtype, const uint8_t* mask,
+                          int64_t B, int64_t T, int64_t V, void* grad_out, int32_t grad_dtype,
+                          int64_t grad_row_stride, const float* grad_scale, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!grad_out) return GRPO_ERR_NULL;
+  int64_t rows = 0;
+  grpo_status st = logits_common_checks(policy_logits, logits_dtype, row_stride, action_ids,
+                                        ids_dtype, B, T, V, grad_out, grad_dtype,
+                                        grad_row_stride, &rows);
+  if (st != GRPO_OK) return st;
+  st = check_alias(policy_logits, nullptr, logits_dtype, row_stride, rows, V, grad_out,
+                   grad_dtype, grad_row_stride);
+  if (st != GRPO_OK) return st;
+  Ws w;
+  st = check_ws(ws, ws_bytes, B, T, 0, &w);  // the stash offset does not depend on groups
+  if (st != GRPO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RowArgs a{};
+  a.x = policy_logits;
+  a.y = nullptr;
+  a.ld = row_stride;
+  a.ids = action_ids;
+  a.ids_i32 = ids_dtype == GRPO_I32 ? 1 : 0;
+  a.mask = mask;
+  a.T = T;
+  a.V = V;
+  a.rows = rows;
+  a.grad_scale = grad_scale;
+  a.g = grad_out;
+  a.ldg = grad_row_stride;
+  a.hdr = w.hdr();
+  a.stash = w.at<RowStash>(w.l.stash);
+  RowLaunch l{};
+  l.mode = 2;
+  l.tin_bf16 = logits_dtype == GRPO_BF16;
+  l.tg_bf16 = grad_dtype == GRPO_BF16;
+  l.nt = choose_nt(V, fdtype_size(logits_dtype));
+  l.vec = rows_vectorizable(policy_logits, nullptr, row_stride, logits_dtype, grad_out,
+                            grad_row_stride, grad_dtype);
+  const bool timed = g_ev_start && g_ev_stop;
+  if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+}  // extern "C"

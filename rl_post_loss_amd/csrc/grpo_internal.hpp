@@ -1,0 +1,164 @@
+// Host/device shared definitions of libgrpo: workspace layout and kernel
+// argument blocks.  Internal to the library.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace grpo {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace header (first 256 bytes).
+struct WsHeader {
+  uint32_t ticket_prep;   // completion counter of the prep kernel
+  uint32_t ticket_final;  // completion counter of the final reduction
+  uint32_t status;        // GRPO_FAULT_* bits gathered during the call
+  uint32_t pad0;
+  int64_t num_tokens;     // N
+};
+
+// Per-row state handed from the forward pass to the gradient pass.
+struct RowStash {
+  float G;     // d loss / d logp of the row (0: masked, bad id, or no gradient)
+  float c;     // base-2 log-normaliser: p_v = 2^(x_v * log2e - c)
+  float omp;   // 1 - p_a, computed without cancellation
+  float pad;
+};
+
+struct WsLayout {
+  size_t hdr, L, A, w, P, K, C, offsets, tok_loss, tok_kl, flags, stash, total;
+};
+
+inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
+  WsLayout l{};
+  size_t o = 0;
+  const size_t rows = size_t(B) * size_t(T);
+  l.hdr = o; o = align_up(o + sizeof(WsHeader));
+  l.L = o; o = align_up(o + size_t(B) * 4);
+  l.A = o; o = align_up(o + size_t(B) * 4);
+  l.w = o; o = align_up(o + size_t(B) * 8);
+  l.P = o; o = align_up(o + size_t(B) * 8);
+  l.K = o; o = align_up(o + size_t(B) * 8);
+  l.C = o; o = align_up(o + size_t(B) * 8);
+  l.tok_loss = o; o = align_up(o + rows * 4);
+  l.tok_kl = o; o = align_up(o + rows * 4);
+  l.flags = o; o = align_up(o + rows);
+  l.stash = o; o = align_up(o + rows * sizeof(RowStash));
+  // last, so that every other offset is independent of the group count
+  l.offsets = o; o = align_up(o + size_t(num_groups > 0 ? num_groups + 1 : 1) * 8);
+  l.total = o;
+  return l;
+}
+
+// Group / advantage / weight preparation.
+struct PrepArgs {
+  const uint8_t* mask;      // [B, T] or null (all active)
+  const float* rewards;     // [B]
+  int64_t B, T;             // T == 0: advantages only
+  int32_t spp;              // uniform group size, or 0 for CSR
+  int32_t num_groups;
+  const int64_t* offsets;   // device copy of the CSR offsets (num_groups + 1)
+  int32_t leave_one_out, scale_by_std;
+  double std_eps;
+  int32_t reduction;
+  double alpha;
+  int32_t want_weights;     // 0: advantages only
+  // workspace
+  WsHeader* hdr;
+  int32_t* L;
+  float* A;
+  double* w;
+  // outputs (nullable)
+  float* adv_out;
+  float* seq_weight_out;
+  int32_t* seq_tokens_out;
+};
+
+// Forward/backward over vocabulary rows.
+struct RowArgs {
+  const void* x;            // policy logits
+  const void* y;            // reference logits (null when beta == 0)
+  int64_t ld;               // row stride of x and y, elements
+  const void* ids;
+  int32_t ids_i32;
+  const float* old;
+  const uint8_t* mask;
+  int64_t T, V, rows;
+  float lo, hi, beta;       // clip band [lo, hi] and KL coefficient
+  const float* grad_scale;  // null = 1
+  void* g;                  // gradient out (null in forward-only mode)
+  int64_t ldg;
+  // workspace
+  WsHeader* hdr;
+  const float* A;
+  const double* w;
+  float* tok_loss;
+  float* tok_kl;
+  uint8_t* flags;
+  RowStash* stash;
+  // per-token outputs (nullable)
+  float* out_logp;
+  float* out_loss;
+  float* out_kl;
+};
+
+// Row-kernel instantiation choice.
+struct RowLaunch {
+  int mode;      // 0 fused forward+backward, 1 forward only, 2 backward only
+  int tin_bf16;  // logits are bf16 (else f32)
+  int tg_bf16;   // gradient is bf16 (else f32)
+  int nt;        // threads per row: 64, 256, 512 or 1024
+  int vec;       // every row is 16-byte aligned: 16-byte chunks
+};
+
+// Per-sequence and scalar reduction.
+struct ReduceArgs {
+  int64_t B, T;
+  float beta;
+  WsHeader* hdr;
+  const float* tok_loss;
+  const float* tok_kl;
+  const uint8_t* flags;
+  const double* w;
+  double* P;
+  double* K;
+  int64_t* C;
+  // outputs
+  float* scalars;
+  float* seq_policy;
+  float* seq_kl;
+  int64_t* counts;
+  uint32_t* status;
+};
+
+// Logprob-level token loss.
+struct TokenArgs {
+  const float* logp;
+  const float* old;
+  const float* ref;         // null when beta == 0
+  const uint8_t* mask;
+  int64_t B, T;
+  float lo, hi, beta;
+  const float* grad_scale;
+  float* dlogp;
+  // workspace
+  WsHeader* hdr;
+  const float* A;
+  const double* w;
+  double* P;
+  double* K;
+  int64_t* C;
+  // outputs
+  float* scalars;
+  float* seq_policy;
+  float* seq_kl;
+  int64_t* counts;
+  uint32_t* status;
+  float* out_loss;
+  float* out_kl;
+};
+
+}  // namespace grpo

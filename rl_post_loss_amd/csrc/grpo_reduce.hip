@@ -1,0 +1,214 @@
+// Fixed-order reductions and the logprob-level token loss.
+//
+// Two nested reductions with fixed extents, as "GRPO Loss" (RL-Kernel docs,
+// Tensor and Data Parallel) lays them out: the token slots of one sequence
+// reduce to a per-sequence total, then the B totals reduce to the scalar.
+// Both stages run in a fixed tree in binary64 without atomics, so results
+// are bit-identical from run to run.  The grpo.cpp README (CUDA section)
+// measures per-token atomics against block reduction for the same loss; here
+// no float atomic is used at all: the last block to finish (an integer
+// ticket) does the scalar stage.
+
+#include "../../include/grpo.h"
+#include "grpo_device.hpp"
+#include "grpo_internal.hpp"
+
+namespace grpo {
+
+constexpr int kRedThreads = 256;
+
+// Scalar stage: policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i (binary64),
+// written as float32, plus the token and clip counts and the fault bits.
+// Run by every thread of the last block.
+__device__ void final_scalars(int64_t B, float beta, WsHeader* hdr, const double* w,
+                              const double* P, const double* K, const int64_t* C,
+                              float* scalars, int64_t* counts, uint32_t* status,
+                              double* sh_f64, long long* sh_i64) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x;
+  double pl = 0.0, kl = 0.0;
+  long long ct = 0;
+  for (int64_t j = tid; j < B; j += kRedThreads) {
+    pl = pl + w[j] * P[j];
+    kl = kl + w[j] * K[j];
+    ct += C[j];
+  }
+  pl = block_sum_f64<kRedThreads>(pl, sh_f64);
+  kl = block_sum_f64<kRedThreads>(kl, sh_f64);
+  ct = block_sum_i64<kRedThreads>(ct, sh_i64);
+  if (tid == 0) {
+    const double loss = pl + double(beta) * kl;
+    scalars[0] = float(loss);
+    scalars[1] = float(pl);
+    scalars[2] = float(kl);
+    if (counts) {
+      counts[0] = hdr->num_tokens;
+      counts[1] = ct;
+    }
+    const uint32_t st = atomicOr(&hdr->status, 0u);
+    if (status) *status = st;
+    atomicAnd(&hdr->status, 0u);  // the workspace starts the next call clean
+  }
+}
+
+// Stage 1 over the per-token values the row kernel left in the workspace.
+__global__ __launch_bounds__(kRedThreads) void grpo_reduce_kernel(ReduceArgs a) {
+#pragma clang fp contract(off)
+  __shared__ double sh_f64[kRedThreads / kWave];
+  __shared__ long long sh_i64[kRedThreads / kWave];
+  __shared__ int sh_flag;
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = i * a.T;
+  double p = 0.0, k = 0.0;
+  long long c = 0;
+  for (int64_t t = tid; t < a.T; t += kRedThreads) {
+    p = p + double(a.tok_loss[base + t]);
+    k = k + double(a.tok_kl[base + t]);
+    c += a.flags[base + t] & 1;
+  }
+  p = block_sum_f64<kRedThreads>(p, sh_f64);
+  k = block_sum_f64<kRedThreads>(k, sh_f64);
+  c = block_sum_i64<kRedThreads>(c, sh_i64);
+  if (tid == 0) {
+    a.P[i] = p;
+    a.K[i] = k;
+    a.C[i] = c;
+    if (a.seq_policy) a.seq_policy[i] = float(p);
+    if (a.seq_kl) a.seq_kl[i] = float(k);
+  }
+  if (last_block(&a.hdr->ticket_final, unsigned(gridDim.x), &sh_flag))
+    final_scalars(a.B, a.beta, a.hdr, a.w, a.P, a.K, a.C, a.scalars, a.counts, a.status, sh_f64,
+                  sh_i64);
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(grpo_reduce_kernel, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Per-token objective from log-probs (float32), shared by nothing else: the
+// vocabulary kernel has its own copy in its epilogue.
+struct TokTerms {
+  float loss, k3, G;
+  bool clipped;
+};
+
+__device__ __forceinline__ TokTerms token_terms(float logp, float old, float ref, bool has_ref,
+                                                float adv, float wg, float lo, float hi,
+                                                float beta) {
+  TokTerms r;
+  const float rho = expf(logp - old);
+  const float d = has_ref ? ref - logp : 0.0f;
+  r.k3 = expm1f(d) - d;
+  r.clipped = (adv > 0.0f && rho > hi) || (adv < 0.0f && rho < lo);
+  const float unc = rho * adv;
+  const float clp = fminf(fmaxf(rho, lo), hi) * adv;
+  r.loss = -fminf(unc, clp);
+  const float dloss = r.clipped ? 0.0f : -adv * rho;
+  r.G = wg * (dloss + beta * -expm1f(d));
+  return r;
+}
+
+// One block per sequence: tokens -> dlogp, per-sequence totals; the last
+// block forms the scalars.  The grpo.cpp README's token-loss kernels (CUDA
+// section) compute the same loss from per-token log-probs.
+__global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
+#pragma clang fp contract(off)
+  __shared__ double sh_f64[kRedThreads / kWave];
+  __shared__ long long sh_i64[kRedThreads / kWave];
+  __shared__ int sh_flag;
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = i * a.T;
+  const float adv = a.A[i];
+  const float wg = float(a.w[i]) * (a.grad_scale ? *a.grad_scale : 1.0f);
+  const bool has_ref = a.ref != nullptr;
+  double p = 0.0, k = 0.0;
+  long long c = 0;
+  bool nonfinite = false;
+  const bool vec = (a.T & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.logp) |
+                                       reinterpret_cast<uintptr_t>(a.old) |
+                                       reinterpret_cast<uintptr_t>(a.ref) |
+                                       reinterpret_cast<uintptr_t>(a.dlogp) |
+                                       reinterpret_cast<uintptr_t>(a.out_loss) |
+                                       reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
+  if (vec) {
+    const int64_t n4 = a.T / 4;
+    for (int64_t q = tid; q < n4; q += kRedThreads) {
+      const int64_t t0 = base + 4 * q;
+      uint32_t m4 = 0x01010101u;
+      if (a.mask) m4 = *reinterpret_cast<const uint32_t*>(a.mask + t0);
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+      float tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
+      if (m4 != 0) {
+        const f32x4 lp = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
+        const f32x4 od = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
+        f32x4 rf = {0.f, 0.f, 0.f, 0.f};
+        if (has_ref) rf = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
+        const float lpv[4] = {lp.x, lp.y, lp.z, lp.w}, odv[4] = {od.x, od.y, od.z, od.w},
+                    rfv[4] = {rf.x, rf.y, rf.z, rf.w};
+        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if ((m4 >> (8 * j)) & 0xffu) {
+            const TokTerms r = token_terms(lpv[j], odv[j], rfv[j], has_ref, adv, wg, a.lo, a.hi,
+                                           a.beta);
+            gv[j] = r.G;
+            tl[j] = r.loss;
+            tk[j] = r.k3;
+            p = p + double(r.loss);
+            k = k + double(r.k3);
+            c += r.clipped ? 1 : 0;
+            nonfinite |= !(isfinite(r.loss) && isfinite(r.k3) && isfinite(r.G));
+          }
+        }
+        g = f32x4{gv[0], gv[1], gv[2], gv[3]};
+      }
+      if (a.dlogp) __builtin_nontemporal_store(g, reinterpret_cast<f32x4*>(a.dlogp + t0));
+      if (a.out_loss) *reinterpret_cast<f32x4*>(a.out_loss + t0) = f32x4{tl[0], tl[1], tl[2], tl[3]};
+      if (a.out_kl) *reinterpret_cast<f32x4*>(a.out_kl + t0) = f32x4{tk[0], tk[1], tk[2], tk[3]};
+    }
+  } else {
+    for (int64_t t = tid; t < a.T; t += kRedThreads) {
+      const int64_t s = base + t;
+      float g = 0.f, tl = 0.f, tk = 0.f;
+      if (a.mask == nullptr || a.mask[s] != 0) {
+        const TokTerms r = token_terms(a.logp[s], a.old[s], has_ref ? a.ref[s] : 0.0f, has_ref,
+                                       adv, wg, a.lo, a.hi, a.beta);
+        g = r.G;
+        tl = r.loss;
+        tk = r.k3;
+        p = p + double(r.loss);
+        k = k + double(r.k3);
+        c += r.clipped ? 1 : 0;
+        nonfinite |= !(isfinite(r.loss) && isfinite(r.k3) && isfinite(r.G));
+      }
+      if (a.dlogp) a.dlogp[s] = g;
+      if (a.out_loss) a.out_loss[s] = tl;
+      if (a.out_kl) a.out_kl[s] = tk;
+    }
+  }
+  if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
+  p = block_sum_f64<kRedThreads>(p, sh_f64);
+  k = block_sum_f64<kRedThreads>(k, sh_f64);
+  c = block_sum_i64<kRedThreads>(c, sh_i64);
+  if (tid == 0) {
+    a.P[i] = p;
+    a.K[i] = k;
+    a.C[i] = c;
+    if (a.seq_policy) a.seq_policy[i] = float(p);
+    if (a.seq_kl) a.seq_kl[i] = float(k);
+  }
+  if (last_block(&a.hdr->ticket_final, unsigned(gridDim.x), &sh_flag))
+    final_scalars(a.B, a.beta, a.hdr, a.w, a.P, a.K, a.C, a.scalars, a.counts, a.status, sh_f64,
+                  sh_i64);
+}
+
+hipError_t launch_token(const TokenArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(grpo_token_kernel, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace grpo

@@ -1,0 +1,353 @@
+"""Torch-facing binding of libgrpo.
+
+Argument marshalling only: tensors are checked for dtype/shape/layout, their
+device pointers are passed to the C ABI on torch's current stream, and output
+tensors are allocated with torch.  Every step of the loss runs in the HIP
+kernels; there is no fallback when the library or a GPU is missing.
+
+Semantics follow "GRPO Loss" (RL-Kernel docs): the entry point takes
+[B, T, V] policy and reference logits, action ids, cached behaviour
+log-probs, one reward per sequence and a completion mask, plus either uniform
+``samples_per_prompt`` or CSR ``group_boundaries``; the loss is
+policy_loss + beta * kl and its gradient flows into the policy logits only.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+from ._abi import GrpoCfg, GrpoGroups, GrpoOutputs, check, load_library
+
+_FDTYPE = {torch.float32: _abi.GRPO_F32, torch.bfloat16: _abi.GRPO_BF16}
+_IDTYPE = {torch.int64: _abi.GRPO_I64, torch.int32: _abi.GRPO_I32}
+
+# one zero-initialised workspace per (device, stream), grown on demand
+_WORKSPACES: dict = {}
+
+
+def _stream_ptr(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def workspace(B, T, num_groups, device, dedicated=False):
+    """A zero-filled workspace large enough for (B, T, num_groups).  The
+    shared one is reused across calls on the same device and stream (the
+    library leaves it clean after each call); ``dedicated`` returns a fresh
+    one (used when state must survive until a later backward call)."""
+    lib = load_library()
+    need = lib.grpo_workspace_bytes(int(B), int(T), int(num_groups))
+    if need == 0:
+        raise ValueError("invalid sizes for the workspace")
+    if dedicated:
+        return torch.zeros(need, dtype=torch.uint8, device=device), need
+    key = (torch.device(device).index, _stream_ptr(device))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws, ws.numel()
+
+
+def _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps):
+    if (samples_per_prompt is None) == (group_boundaries is None):
+        raise ValueError("give exactly one of samples_per_prompt / group_boundaries")
+    g = GrpoGroups()
+    keep = None
+    if samples_per_prompt is not None:
+        g.samples_per_prompt = int(samples_per_prompt)
+        g.num_groups = 0
+        g.group_boundaries = None
+        ng = 0
+    else:
+        off = [int(v) for v in group_boundaries]
+        keep = (C.c_int64 * len(off))(*off)
+        g.samples_per_prompt = 0
+        g.num_groups = len(off) - 1
+        g.group_boundaries = C.cast(keep, C.POINTER(C.c_int64))
+        ng = len(off) - 1
+    g.leave_one_out = 1 if leave_one_out else 0
+    g.scale_by_std = 1 if scale_by_std else 0
+    g.std_eps = float(std_eps)
+    return g, keep, ng
+
+
+def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
+    c = GrpoCfg()
+    c.eps_low = float(clip_eps if eps_low is None else eps_low)
+    c.eps_high = float(clip_eps if eps_high is None else eps_high)
+    c.beta = float(beta)
+    if reduction not in _abi.REDUCTION_CODES:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    c.reduction = _abi.REDUCTION_CODES[reduction]
+    c.alpha = float(alpha) if alpha is not None else 0.0
+    return c
+
+
+@dataclass
+class GRPOResult:
+    """Outputs of one call (device tensors).  ``loss``, ``policy_loss`` and
+    ``kl`` are 0-dim float32 views of ``scalars``."""
+    scalars: torch.Tensor
+    advantages: torch.Tensor
+    seq_policy: torch.Tensor
+    seq_kl: torch.Tensor
+    seq_weight: torch.Tensor
+    seq_tokens: torch.Tensor
+    counts: torch.Tensor
+    status: torch.Tensor
+    grad: torch.Tensor | None = None
+    tok_logp: torch.Tensor | None = None
+    tok_loss: torch.Tensor | None = None
+    tok_kl: torch.Tensor | None = None
+
+    @property
+    def loss(self):
+        return self.scalars[0]
+
+    @property
+    def policy_loss(self):
+        return self.scalars[1]
+
+    @property
+    def kl(self):
+        return self.scalars[2]
+
+
+def _outputs(B, T, device, per_token, want_logp):
+    f32 = dict(dtype=torch.float32, device=device)
+    res = GRPOResult(
+        scalars=torch.empty(3, **f32), advantages=torch.empty(B, **f32),
+        seq_policy=torch.empty(B, **f32), seq_kl=torch.empty(B, **f32),
+        seq_weight=torch.empty(B, **f32),
+        seq_tokens=torch.empty(B, dtype=torch.int32, device=device),
+        counts=torch.empty(2, dtype=torch.int64, device=device),
+        status=torch.empty(1, dtype=torch.int32, device=device))
+    if per_token:
+        res.tok_loss = torch.empty((B, T), **f32)
+        res.tok_kl = torch.empty((B, T), **f32)
+        if want_logp:
+            res.tok_logp = torch.empty((B, T), **f32)
+    o = GrpoOutputs()
+    o.scalars = res.scalars.data_ptr()
+    o.advantages = res.advantages.data_ptr()
+    o.seq_policy = res.seq_policy.data_ptr()
+    o.seq_kl = res.seq_kl.data_ptr()
+    o.seq_weight = res.seq_weight.data_ptr()
+    o.seq_tokens = res.seq_tokens.data_ptr()
+    o.counts = res.counts.data_ptr()
+    o.status = res.status.data_ptr()
+    o.tok_logp = _ptr(res.tok_logp)
+    o.tok_loss = _ptr(res.tok_loss)
+    o.tok_kl = _ptr(res.tok_kl)
+    return res, o
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _row_stride(t, name):
+    """Row stride (elements) of a [B, T, V] tensor whose (B, T) rows sit at a
+    uniform stride with contiguous vocabulary."""
+    _need(t.dim() == 3, f"{name} must be [B, T, V]")
+    B, T, V = t.shape
+    _need(t.stride(2) == 1, f"{name} needs a contiguous vocabulary dimension")
+    ld = t.stride(1) if T > 1 else (t.stride(0) if B > 1 else V)
+    _need(B == 1 or t.stride(0) == T * ld, f"{name} rows must sit at one uniform stride")
+    _need(ld >= V, f"{name} row stride must be >= V")
+    return ld
+
+
+def _mask_ptr(mask, B, T, device):
+    if mask is None:
+        return None, None
+    _need(tuple(mask.shape) == (B, T), "completion_mask must be [B, T]")
+    _need(mask.dtype in (torch.bool, torch.uint8), "completion_mask must be bool or uint8")
+    _need(mask.device == device and mask.is_contiguous(), "completion_mask: contiguous, same device")
+    return mask.data_ptr(), mask
+
+
+def grpo_advantages(rewards, *, samples_per_prompt=None, group_boundaries=None,
+                    leave_one_out=False, scale_by_std=True, std_eps=1e-6):
+    """Group-relative advantages [B] float32 ("GRPO Loss", Accuracy; dockyard_rl,
+    Advantage estimation)."""
+    lib = load_library()
+    _need(rewards.dtype == torch.float32 and rewards.dim() == 1 and rewards.is_cuda
+          and rewards.is_contiguous(), "rewards must be a contiguous float32 [B] GPU tensor")
+    B = rewards.shape[0]
+    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                          std_eps)
+    out = torch.empty(B, dtype=torch.float32, device=rewards.device)
+    ws, wsb = workspace(B, 1, ng, rewards.device)
+    check(lib.grpo_advantages(rewards.data_ptr(), B, C.byref(g), out.data_ptr(), ws.data_ptr(),
+                              wsb, _stream_ptr(rewards.device)), lib)
+    return out
+
+
+def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *,
+                    clip_eps=0.2, eps_low=None, eps_high=None, beta=0.04,
+                    samples_per_prompt=None, group_boundaries=None, leave_one_out=False,
+                    scale_by_std=True, std_eps=1e-6, reduction="token_mean", alpha=None,
+                    want_grad=True, grad_scale=None, per_token=False):
+    """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp."""
+    lib = load_library()
+    dev = logp.device
+    _need(logp.dim() == 2 and logp.is_cuda, "logp must be a [B, T] GPU tensor")
+    B, T = logp.shape
+    for name, t in (("logp", logp), ("old_logps", old_logps), ("ref_logps", ref_logps)):
+        if t is None:
+            continue
+        _need(t.dtype == torch.float32 and tuple(t.shape) == (B, T) and t.is_contiguous()
+              and t.device == dev, f"{name} must be contiguous float32 [B, T] on {dev}")
+    _need(rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,) and rewards.device == dev,
+          "rewards must be float32 [B]")
+    mptr, _ = _mask_ptr(completion_mask, B, T, dev)
+    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                          std_eps)
+    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+    res, o = _outputs(B, T, dev, per_token, want_logp=False)
+    if want_grad:
+        res.grad = torch.empty((B, T), dtype=torch.float32, device=dev)
+    ws, wsb = workspace(B, T, ng, dev)
+    check(lib.grpo_token_loss(logp.data_ptr(), old_logps.data_ptr(), _ptr(ref_logps), mptr,
+                              rewards.contiguous().data_ptr(), B, T, C.byref(g), C.byref(cfg),
+                              _ptr(res.grad), _ptr(grad_scale), C.byref(o), ws.data_ptr(), wsb,
+                              _stream_ptr(dev)), lib)
+    return res
+
+
+def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
+                      completion_mask=None, *, clip_eps=0.2, eps_low=None, eps_high=None,
+                      beta=0.04, samples_per_prompt=None, group_boundaries=None,
+                      leave_one_out=False, scale_by_std=True, std_eps=1e-6,
+                      reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
+                      grad_scale=None, per_token=False, _ws=None):
+    """Fused forward + analytic backward from [B, T, V] logits.
+
+    grad_out: None allocates a contiguous gradient (dtype ``grad_dtype``,
+    default the logits dtype); a tensor writes into it (it may be
+    ``policy_logits`` itself, in place); False runs the forward only.
+    """
+    lib = load_library()
+    dev = policy_logits.device
+    _need(policy_logits.is_cuda, "policy_logits must be on a GPU")
+    _need(policy_logits.dtype in _FDTYPE, "logits must be float32 or bfloat16")
+    ld = _row_stride(policy_logits, "policy_logits")
+    B, T, V = policy_logits.shape
+    if ref_logits is not None:
+        _need(ref_logits.dtype == policy_logits.dtype and tuple(ref_logits.shape) == (B, T, V)
+              and ref_logits.device == dev, "ref_logits must match policy_logits")
+        _need(_row_stride(ref_logits, "ref_logits") == ld, "ref_logits must share the row stride")
+    _need(action_ids.dtype in _IDTYPE and tuple(action_ids.shape) == (B, T)
+          and action_ids.is_contiguous() and action_ids.device == dev,
+          "action_ids must be contiguous int64/int32 [B, T]")
+    _need(old_logps.dtype == torch.float32 and tuple(old_logps.shape) == (B, T)
+          and old_logps.is_contiguous() and old_logps.device == dev,
+          "old_logps must be contiguous float32 [B, T]")
+    _need(rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,) and rewards.device == dev,
+          "rewards must be float32 [B]")
+    mptr, _ = _mask_ptr(completion_mask, B, T, dev)
+    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                          std_eps)
+    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+    res, o = _outputs(B, T, dev, per_token, want_logp=True)
+    if grad_out is None:
+        gdt = policy_logits.dtype if grad_dtype is None else grad_dtype
+        _need(gdt in _FDTYPE, "grad_dtype must be float32 or bfloat16")
+        grad_out = torch.empty((B, T, V), dtype=gdt, device=dev)
+    if grad_out is False:
+        gptr, gdt_code, gld = None, _abi.GRPO_F32, 0
+    else:
+        _need(grad_out.dtype in _FDTYPE and tuple(grad_out.shape) == (B, T, V)
+              and grad_out.device == dev, "grad_out must be float32/bfloat16 [B, T, V]")
+        gptr, gdt_code, gld = grad_out.data_ptr(), _FDTYPE[grad_out.dtype], _row_stride(grad_out, "grad_out")
+        res.grad = grad_out
+    if _ws is None:
+        ws, wsb = workspace(B, T, ng, dev)
+    else:
+        ws, wsb = _ws
+    check(lib.grpo_loss_fwd_bwd(policy_logits.data_ptr(), _ptr(ref_logits),
+                                _FDTYPE[policy_logits.dtype], ld, action_ids.data_ptr(),
+                                _IDTYPE[action_ids.dtype], old_logps.data_ptr(), mptr,
+                                rewards.contiguous().data_ptr(), B, T, V, C.byref(g), C.byref(cfg),
+                                gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o), ws.data_ptr(),
+                                wsb, _stream_ptr(dev)), lib)
+    return res
+
+
+def grpo_loss_bwd(policy_logits, action_ids, completion_mask, ws, *, grad_out=None,
+                  grad_dtype=None, grad_scale=None):
+    """Gradient pass after a forward-only grpo_loss_fwd_bwd(..., grad_out=False,
+    _ws=ws) on the same dedicated workspace ``ws`` = (tensor, bytes)."""
+    lib = load_library()
+    dev = policy_logits.device
+    ld = _row_stride(policy_logits, "policy_logits")
+    B, T, V = policy_logits.shape
+    if grad_out is None:
+        gdt = policy_logits.dtype if grad_dtype is None else grad_dtype
+        grad_out = torch.empty((B, T, V), dtype=gdt, device=dev)
+    mptr, _ = _mask_ptr(completion_mask, B, T, dev)
+    check(lib.grpo_loss_bwd(policy_logits.data_ptr(), _FDTYPE[policy_logits.dtype], ld,
+                            action_ids.data_ptr(), _IDTYPE[action_ids.dtype], mptr, B, T, V,
+                            grad_out.data_ptr(), _FDTYPE[grad_out.dtype],
+                            _row_stride(grad_out, "grad_out"), _ptr(grad_scale), ws[0].data_ptr(),
+                            ws[1], _stream_ptr(dev)), lib)
+    return grad_out
+
+
+class _GRPOLossFn(torch.autograd.Function):
+    """Autograd wrapper: the forward runs the vocabulary pass once and keeps the
+    per-row gradient weights in a dedicated workspace; the backward streams the
+    policy logits again and writes d loss / d logits scaled by the upstream
+    gradient."""
+
+    @staticmethod
+    def forward(ctx, policy_logits, ref_logits, action_ids, old_logps, rewards, mask, kw):
+        B, T, V = policy_logits.shape
+        ng = 0 if kw.get("group_boundaries") is None else len(kw["group_boundaries"]) - 1
+        ws = workspace(B, T, ng, policy_logits.device, dedicated=True)
+        res = grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards, mask,
+                                grad_out=False, _ws=ws, **kw)
+        ctx.save_for_backward(policy_logits, action_ids, mask if mask is not None else torch.empty(0))
+        ctx.has_mask = mask is not None
+        ctx.ws = ws
+        return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
+
+    @staticmethod
+    def backward(ctx, g_loss, g_pol, g_kl):
+        policy_logits, action_ids, mask = ctx.saved_tensors
+        scale = g_loss.reshape(1).to(torch.float32).contiguous()
+        grad = grpo_loss_bwd(policy_logits, action_ids, mask if ctx.has_mask else None, ctx.ws,
+                             grad_scale=scale)
+        ctx.ws = None
+        return grad, None, None, None, None, None, None
+
+
+def grpo_loss(policy_logits, ref_logits, action_ids, old_logps, rewards, completion_mask=None,
+              **kw):
+    """(loss, policy_loss, kl) with autograd into ``policy_logits`` (the call
+    signature of "GRPO Loss", Entry Point).  Gradients of policy_loss and kl
+    as separate outputs are not propagated: only ``loss`` is differentiable."""
+    return _GRPOLossFn.apply(policy_logits, ref_logits, action_ids, old_logps, rewards,
+                             completion_mask, kw)
+
+
+def set_timing_events(start, stop):
+    """Records the hipEvent_t handles ``start``/``stop`` (integers or
+    ctypes.c_void_p, created by the caller) around the vocabulary kernel of
+    the next logits calls; None turns it off."""
+    lib = load_library()
+    if start is None:
+        lib.grpo_set_timing_events(None, None)
+    else:
+        lib.grpo_set_timing_events(C.c_void_p(int(getattr(start, "value", start))),
+                                   C.c_void_p(int(getattr(stop, "value", stop))))

@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI that run without a GPU: the library loads,
+exports every function include/grpo.h declares, sizes its workspace, and
+rejects invalid arguments before launching anything."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+import rl_post_loss_amd as rpl
+from rl_post_loss_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grpo.h")
+
+# Argument-validation tests pass fake device addresses; they must never be able
+# to reach a kernel launch on a machine with a GPU, so they run on CPU hosts only.
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="host-validation tests use fake pointers")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"GRPO_API\s+[\w\s\*]*?\b(grpo_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("grpo_advantages", "grpo_token_loss", "grpo_loss_fwd_bwd", "grpo_loss_bwd",
+                 "grpo_workspace_bytes", "grpo_workspace_init", "grpo_status_str",
+                 "grpo_abi_version", "grpo_set_timing_events"):
+        assert name in fns
+    assert set(fns) == set(_abi.SIGNATURES), "binding and header disagree"
+
+
+def test_library_loads_and_exports_every_symbol():
+    lib = rpl.load_library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.grpo_abi_version() == _abi.GRPO_ABI_VERSION
+
+
+def test_status_strings():
+    lib = rpl.load_library()
+    for code in range(0, 9):
+        assert lib.grpo_status_str(code)
+    assert lib.grpo_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    lib = rpl.load_library()
+    a = lib.grpo_workspace_bytes(32, 2048, 0)
+    b = lib.grpo_workspace_bytes(32, 2048, 12)
+    assert a > 32 * 2048 * 24 and a % 256 == 0 and b >= a
+    assert lib.grpo_workspace_bytes(0, 10, 0) == 0
+    assert lib.grpo_workspace_bytes(10, -1, 0) == 0
+    assert lib.grpo_workspace_bytes(1 << 40, 1 << 40, 0) == 0
+
+
+def _groups(spp=4, bounds=None, loo=0, scale=1, eps=1e-6):
+    g = _abi.GrpoGroups()
+    g.samples_per_prompt = spp
+    keep = None
+    if bounds is not None:
+        keep = (C.c_int64 * len(bounds))(*bounds)
+        g.group_boundaries = C.cast(keep, C.POINTER(C.c_int64))
+        g.num_groups = len(bounds) - 1
+    g.leave_one_out, g.scale_by_std, g.std_eps = loo, scale, eps
+    return g, keep
+
+
+def _cfg(lo=0.2, hi=0.2, beta=0.04, red=0, alpha=0.0):
+    c = _abi.GrpoCfg()
+    c.eps_low, c.eps_high, c.beta, c.reduction, c.alpha = lo, hi, beta, red, alpha
+    return c
+
+
+FAKE = 0x10000000          # never dereferenced: every call below fails validation first
+FAKE_WS = 0x20000000
+
+
+def _fwd(lib, B=8, T=4, V=32, g=None, cfg=None, ref=FAKE, grad=FAKE + 0x4000000, ws=FAKE_WS,
+         ws_bytes=1 << 30, ld=None, gld=None, dtype=0, gdtype=0, ids_dtype=0, scalars=FAKE):
+    if g is None:
+        g, _ = _groups()
+    cfg = cfg or _cfg()
+    o = _abi.GrpoOutputs()
+    o.scalars = scalars
+    return lib.grpo_loss_fwd_bwd(FAKE, ref, dtype, ld or V, FAKE, ids_dtype, FAKE, None, FAKE,
+                                 B, T, V, C.byref(g), C.byref(cfg), grad, gdtype, gld or V, None,
+                                 C.byref(o), ws, ws_bytes, None)
+
+
+@cpu_only
+def test_fwd_bwd_argument_validation():
+    lib = rpl.load_library()
+    E = {v: k for k, v in _abi.STATUS_NAMES.items()}
+    assert _fwd(lib, scalars=None) == E["GRPO_ERR_NULL"]
+    assert _fwd(lib, B=0) == E["GRPO_ERR_SHAPE"]
+    assert _fwd(lib, V=0) == E["GRPO_ERR_SHAPE"]
+    assert _fwd(lib, ld=16) == E["GRPO_ERR_SHAPE"]          # row stride < V
+    assert _fwd(lib, gld=16) == E["GRPO_ERR_SHAPE"]
+    assert _fwd(lib, dtype=7) == E["GRPO_ERR_DTYPE"]
+    assert _fwd(lib, gdtype=9) == E["GRPO_ERR_DTYPE"]
+    assert _fwd(lib, ids_dtype=3) == E["GRPO_ERR_DTYPE"]
+    # groups: neither, both, B % spp, bad CSR, singleton
+    g, _ = _groups(spp=0)
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g, keep = _groups(spp=4, bounds=[0, 4, 8])
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g, _ = _groups(spp=3)
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    for bad in ([0, 4, 7], [1, 4, 8], [0, 5, 4, 8], [0, 1, 8], [0, 8, 8]):
+        g, keep = _groups(spp=0, bounds=bad)
+        assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"], bad
+    g, _ = _groups(spp=1)
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g, _ = _groups(eps=0.0)
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    # config
+    assert _fwd(lib, cfg=_cfg(lo=1.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(lo=-0.1)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(hi=-0.1)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(beta=-1.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(beta=float("nan"))) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(beta=0.1), ref=None) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(red=5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(red=2, alpha=1.5)) == E["GRPO_ERR_CONFIG"]
+    # aliasing: in place with another dtype or stride, partial overlap
+    assert _fwd(lib, grad=FAKE, gdtype=1) == E["GRPO_ERR_ALIAS"]
+    assert _fwd(lib, grad=FAKE + 64) == E["GRPO_ERR_ALIAS"]
+    assert _fwd(lib, grad=FAKE + 64, ref=FAKE + 0x4000000 + 64) == E["GRPO_ERR_ALIAS"]
+    # workspace: null, misaligned, too small
+    assert _fwd(lib, ws=None) == E["GRPO_ERR_WORKSPACE"]
+    assert _fwd(lib, ws=FAKE_WS + 8) == E["GRPO_ERR_WORKSPACE"]
+    assert _fwd(lib, ws_bytes=100) == E["GRPO_ERR_WORKSPACE"]
+
+
+@cpu_only
+def test_token_loss_and_advantages_validation():
+    lib = rpl.load_library()
+    E = {v: k for k, v in _abi.STATUS_NAMES.items()}
+    g, _ = _groups()
+    cfg = _cfg()
+    o = _abi.GrpoOutputs()
+    o.scalars = FAKE
+    call = lambda **k: lib.grpo_token_loss(
+        k.get("logp", FAKE), FAKE, k.get("ref", FAKE), None, FAKE, k.get("B", 8), k.get("T", 4),
+        C.byref(k.get("g", g)), C.byref(k.get("cfg", cfg)), FAKE, None, C.byref(o),
+        k.get("ws", FAKE_WS), k.get("wsb", 1 << 30), None)
+    assert call(logp=None) == E["GRPO_ERR_NULL"]
+    assert call(T=0) == E["GRPO_ERR_SHAPE"]
+    assert call(B=6) == E["GRPO_ERR_GROUPS"]
+    assert call(ref=None) == E["GRPO_ERR_CONFIG"]           # beta > 0 needs ref
+    assert call(wsb=10) == E["GRPO_ERR_WORKSPACE"]
+    assert lib.grpo_advantages(FAKE, 8, C.byref(_groups(spp=3)[0]), FAKE, FAKE_WS, 1 << 20,
+                               None) == E["GRPO_ERR_GROUPS"]
+    assert lib.grpo_advantages(None, 8, C.byref(g), FAKE, FAKE_WS, 1 << 20, None) == E["GRPO_ERR_NULL"]
+    assert lib.grpo_loss_bwd(FAKE, 0, 32, FAKE, 0, None, 8, 4, 32, None, 0, 32, None, FAKE_WS,
+                             1 << 30, None) == E["GRPO_ERR_NULL"]
+    assert lib.grpo_loss_bwd(FAKE, 0, 32, FAKE, 0, None, 8, 4, 32, FAKE + 4, 0, 32, None, FAKE_WS,
+                             1 << 30, None) == E["GRPO_ERR_ALIAS"]
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        _abi.load_library(str(tmp_path / "missing.so"))

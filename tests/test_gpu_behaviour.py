@@ -1,0 +1,215 @@
+"""Behaviour of the HIP path that parity alone does not show: bitwise
+reproducibility, masked-slot immunity, in-place gradients, the ref == policy
+identity, device-detected data faults, and the split forward/backward used by
+autograd."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import cfg_from, compare_logits_grad, gpu_kwargs, host_inputs, to_np
+from workloads import WORKLOADS, LogitsWorkload, make_logits_inputs, poison_masked
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _wl(V=5000, dtype="bf16", T=8, sizes=(4, 4), **kw):
+    base = dict(name=f"beh_V{V}", group_sizes=sizes, T=T, V=V, dtype=dtype, logit_std=2.0,
+                ref_noise_std=math.sqrt(0.1), old_noise_std=math.sqrt(0.05), reward_p=0.5,
+                len_range=(1, T))
+    base.update(kw)
+    return LogitsWorkload(**base)
+
+
+def _inputs(wl, seed=0):
+    cpu = make_logits_inputs(wl, device="cpu", seed=seed)
+    return cpu, {k: v.to(DEV) for k, v in cpu.items()}
+
+
+def _call(rpl, inp, wl, **extra):
+    kw = gpu_kwargs(wl)
+    kw.update(extra)
+    res = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
+                                inp["rewards"], inp["mask"], per_token=True, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.uint8) if a.dtype != torch.bool else a,
+                       b.view(torch.uint8) if b.dtype != torch.bool else b)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.uint8)
+
+
+@pytest.mark.parametrize("V,dtype", [(151936, "bf16"), (32, "f32"), (5000, "bf16")])
+def test_bitwise_reproducible(gpu_lib, V, dtype):
+    wl = _wl(V, dtype, T=16 if V > 10000 else 64)
+    announce(f"determinism V={V} {dtype}")
+    _, inp = _inputs(wl, seed=11)
+    first = _call(gpu_lib, inp, wl)
+    for k in range(10):
+        again = _call(gpu_lib, inp, wl)
+        assert torch.equal(_bits(first.scalars), _bits(again.scalars)), k
+        assert torch.equal(_bits(first.seq_policy), _bits(again.seq_policy)), k
+        assert torch.equal(_bits(first.seq_kl), _bits(again.seq_kl)), k
+        assert torch.equal(_bits(first.grad), _bits(again.grad)), k
+
+
+def test_masked_nan_inf_garbage_ids_do_not_leak(gpu_lib):
+    wl = _wl(3001, "bf16", T=12)
+    announce("masked poison")
+    cpu, inp = _inputs(wl, seed=12)
+    clean = _call(gpu_lib, inp, wl)
+    bad = poison_masked(inp, V=wl.V)
+    dirty = _call(gpu_lib, bad, wl)
+    assert torch.equal(_bits(clean.scalars), _bits(dirty.scalars))
+    assert torch.equal(_bits(clean.grad), _bits(dirty.grad))
+    assert int(dirty.status[0]) == 0
+
+
+def test_in_place_gradient_matches_out_of_place(gpu_lib):
+    wl = _wl(8192, "bf16", T=8)
+    announce("in place")
+    _, inp = _inputs(wl, seed=13)
+    out = _call(gpu_lib, inp, wl)
+    pol = inp["policy"].clone()
+    res = gpu_lib.grpo_loss_fwd_bwd(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                    inp["rewards"], inp["mask"], grad_out=pol, **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert res.grad.data_ptr() == pol.data_ptr()
+    assert torch.equal(_bits(out.scalars), _bits(res.scalars))
+    assert torch.equal(_bits(out.grad), _bits(pol))
+
+
+def test_identity_ref_is_policy_and_old_is_logp(gpu_lib):
+    """ref_logits is policy_logits and old_logps equals the kernel's own
+    log-probs: rho = 1 and k3 = 0 exactly, so the loss is -sum_i w_i L_i A_i."""
+    wl = _wl(20000, "bf16", T=10)
+    announce("identity")
+    _, inp = _inputs(wl, seed=14)
+    first = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["policy"], inp["action_ids"],
+                                      inp["old_logps"], inp["rewards"], inp["mask"],
+                                      per_token=True, **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    old = first.tok_logp.clone()
+    for eps in (0.1, 0.2, 0.45):
+        kw = gpu_kwargs(wl)
+        kw.update(eps_low=eps, eps_high=eps)
+        res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["policy"], inp["action_ids"], old,
+                                        inp["rewards"], inp["mask"], per_token=True, **kw)
+        torch.cuda.synchronize()
+        assert float(res.kl) == 0.0
+        assert torch.all(res.tok_kl == 0.0)
+        assert int(res.counts[1]) == 0
+        A = to_np(res.advantages)
+        w = to_np(res.seq_weight).astype(np.float64)
+        L = to_np(res.seq_tokens).astype(np.float64)
+        # per token the loss is -A exactly (rho == 1), so the sequence total is -L*A
+        assert np.array_equal(to_np(res.seq_policy), (-L * A).astype(np.float32).astype(np.float64))
+        h_old = first.tok_logp
+        assert torch.equal(res.tok_logp, h_old)
+        expect = -np.sum(w.astype(np.float32).astype(np.float64) * L * A)
+        assert abs(float(res.loss) - expect) <= 1e-6 * max(1.0, abs(expect))
+
+
+def test_bad_action_id_flags_and_zeroes_row(gpu_lib):
+    wl = _wl(1000, "f32", T=4, len_range=None)
+    announce("bad action id")
+    _, inp = _inputs(wl, seed=15)
+    ids = inp["action_ids"].clone()
+    ids[1, 2] = wl.V          # out of range at an active slot
+    ids[3, 0] = -3
+    res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], ids, inp["old_logps"],
+                                    inp["rewards"], inp["mask"], per_token=True, **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert int(res.status[0]) & gpu_lib.GRPO_FAULT_BAD_ACTION
+    assert torch.all(res.grad[1, 2] == 0) and torch.all(res.grad[3, 0] == 0)
+    assert float(res.tok_loss[1, 2]) == 0.0 and float(res.tok_kl[3, 0]) == 0.0
+    assert math.isfinite(float(res.loss))
+    # the next clean call reports no fault (status is per call)
+    clean = _call(gpu_lib, inp, wl)
+    assert int(clean.status[0]) == 0
+
+
+def test_no_active_tokens(gpu_lib):
+    wl = _wl(700, "bf16", T=5)
+    announce("no active tokens")
+    _, inp = _inputs(wl, seed=16)
+    mask = torch.zeros_like(inp["mask"])
+    for red in ("token_mean", "sequence_mean", "length_alpha"):
+        res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                        inp["old_logps"], inp["rewards"], mask,
+                                        **dict(gpu_kwargs(wl), reduction=red, alpha=0.5))
+        torch.cuda.synchronize()
+        assert int(res.status[0]) & gpu_lib.GRPO_FAULT_NO_TOKENS
+        assert float(res.loss) == 0.0 and float(res.kl) == 0.0
+        assert torch.all(res.grad == 0)
+        assert int(res.counts[0]) == 0
+
+
+def test_autograd_split_forward_backward(gpu_lib):
+    """grpo_loss() runs the forward pass, keeps per-row weights, and the
+    backward pass writes the same gradient as the fused call, scaled by the
+    upstream gradient."""
+    wl = _wl(12000, "bf16", T=6)
+    announce("autograd split")
+    _, inp = _inputs(wl, seed=17)
+    fused = _call(gpu_lib, inp, wl)
+    pol = inp["policy"].clone().requires_grad_(True)
+    loss, pl, kl = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                     inp["rewards"], inp["mask"], **gpu_kwargs(wl))
+    assert torch.equal(_bits(loss.detach().reshape(1)), _bits(fused.scalars[:1]))
+    loss.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(pol.grad), _bits(fused.grad))
+    pol.grad = None
+    loss2, _, _ = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                    inp["rewards"], inp["mask"], **gpu_kwargs(wl))
+    (2.0 * loss2).backward()
+    torch.cuda.synchronize()
+    scale = torch.tensor([2.0], device=DEV)
+    fused2 = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                       inp["old_logps"], inp["rewards"], inp["mask"],
+                                       grad_scale=scale, **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(pol.grad), _bits(fused2.grad))
+
+
+def test_confident_token_gradient_relative_accuracy(gpu_lib):
+    """p_a close to 1: 1 - p_a is formed without cancellation, so g_a keeps
+    its relative accuracy."""
+    V = 4096
+    wl = _wl(V, "f32", T=2, len_range=None, beta=0.0)
+    announce("confident tokens")
+    cpu, inp = _inputs(wl, seed=18)
+    ids = inp["action_ids"]
+    pol = inp["policy"].clone()
+    # the taken token dominates: 1 - p_a is about 4e-7
+    pol.scatter_(2, ids[..., None], 25.0)
+    res = gpu_lib.grpo_loss_fwd_bwd(pol, inp["ref"], ids, inp["old_logps"], inp["rewards"],
+                                    inp["mask"], per_token=True, **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    h = host_inputs(dict(cpu, policy=pol.cpu()))
+    ref = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
+                                   h["mask"], h["rewards"], groups=wl.groups_kwargs(),
+                                   cfg=cfg_from(wl))
+    g = to_np(res.grad)
+    r = ref.grad
+    idx = np.take_along_axis(r, h["action_ids"][..., None], -1)[..., 0]
+    gi = np.take_along_axis(g, h["action_ids"][..., None], -1)[..., 0]
+    nz = idx != 0
+    rel = np.abs(gi - idx)[nz] / np.abs(idx[nz])
+    assert np.all(rel < 1e-4), rel.max()
+    lp = to_np(res.tok_logp)
+    assert np.all(np.abs(lp - ref.tok["logp"]) <= 1e-6 * np.abs(ref.tok["logp"]) + 1e-12)

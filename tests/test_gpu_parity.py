@@ -1,0 +1,316 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes here let the oracle finish in seconds while still spanning several
+vector chunks per thread, ragged masks, vector tails and the scalar path.
+Full-size workloads are covered by tests/test_gpu_fullsize.py.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import (assert_bits_equal, cfg_from, compare_exact_parts, compare_logits_grad,
+                     compare_scalars, gpu_kwargs, host_inputs, to_np)
+from workloads import (TOKEN_WORKLOADS, WORKLOADS, LogitsWorkload, make_logits_inputs,
+                       make_token_inputs, poison_masked)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def run_logits(rpl, inp, wl, reduction=None, **extra):
+    kw = gpu_kwargs(wl, reduction)
+    kw.update(extra)
+    res = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
+                                inp["rewards"], inp["mask"], per_token=True, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_logits(h, wl, reduction=None, with_ref=True):
+    return oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"] if with_ref else None, h["action_ids"],
+                                    h["old_logps"], h["mask"], h["rewards"],
+                                    groups=wl.groups_kwargs(), cfg=cfg_from(wl, reduction))
+
+
+def check_logits_case(rpl, wl, seed=0, reduction=None):
+    announce(f"logits parity {wl.name} reduction={reduction or wl.reductions[0]} seed={seed}")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=seed)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = run_logits(rpl, inp, wl, reduction)
+    h = host_inputs(inp_cpu)
+    ref = oracle_logits(h, wl, reduction)
+    cfg = cfg_from(wl, reduction)
+    compare_exact_parts(res, ref, wl.name)
+    bf16 = wl.dtype == "bf16"
+    compare_scalars(res, ref, 1e-4 if bf16 else 1e-5, wl.name)
+    stats = compare_logits_grad(to_np(res.grad), ref, cfg, h["mask"], bf16, wl.name)
+    clipped = int(to_np(res.counts)[1])
+    assert abs(clipped - ref.clipped) <= stats["ambiguous"], (clipped, ref.clipped, stats)
+    st = int(to_np(res.status)[0])
+    assert st == 0, f"status bits {st}"
+    print(f"  stats {stats} clipped gpu={clipped} oracle={ref.clipped}", flush=True)
+    return res, ref
+
+
+def test_tiny_logits_workload(gpu_lib):
+    check_logits_case(gpu_lib, WORKLOADS["tiny_logits"])
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_logits_more_seeds(gpu_lib, seed):
+    check_logits_case(gpu_lib, WORKLOADS["tiny_logits"], seed=seed)
+
+
+def test_v32000_recipe_reduced(gpu_lib):
+    check_logits_case(gpu_lib, WORKLOADS["logits_v32000"].scaled(T=32, prompts=2))
+
+
+def test_v151936_recipe_reduced(gpu_lib):
+    check_logits_case(gpu_lib, WORKLOADS["logits_v151936"].scaled(T=12, prompts=1))
+
+
+@pytest.mark.parametrize("reduction", ["token_mean", "sequence_mean", "length_alpha"])
+def test_csr_v128256_recipe_reduced(gpu_lib, reduction):
+    check_logits_case(gpu_lib, WORKLOADS["logits_csr_v128256"].scaled(T=8, prompts=3),
+                      reduction=reduction)
+
+
+def _custom(V, dtype="bf16", T=6, sizes=(4, 4), **kw):
+    base = dict(name=f"custom_V{V}_{dtype}", group_sizes=sizes, T=T, V=V, dtype=dtype,
+                logit_std=2.0, ref_noise_std=math.sqrt(0.1), old_noise_std=math.sqrt(0.05),
+                reward_p=0.5, len_range=(1, T))
+    base.update(kw)
+    return LogitsWorkload(**base)
+
+
+@pytest.mark.parametrize("V,dtype", [
+    (1, "f32"), (2, "bf16"), (7, "f32"), (64, "bf16"), (1000, "bf16"), (1000, "f32"),
+    (2048, "f32"), (4097, "bf16"), (8200, "bf16"), (40000, "f32"), (70001, "bf16"),
+])
+def test_vocab_sizes_and_paths(gpu_lib, V, dtype):
+    """Wave-per-row, block-per-row, vector and scalar paths, ragged tails."""
+    check_logits_case(gpu_lib, _custom(V, dtype))
+
+
+def test_padded_row_stride_vector_tail(gpu_lib):
+    """Rows padded to a 16-byte multiple: the vector path with a scalar tail."""
+    rpl = gpu_lib
+    wl = _custom(4097, "bf16", T=5)
+    announce("padded stride V=4097 ld=4104")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=5)
+    B, T, V = wl.B, wl.T, wl.V
+    ld = 4104
+    pol = torch.full((B, T, ld), float("nan"), dtype=torch.bfloat16)
+    ref = torch.full((B, T, ld), float("inf"), dtype=torch.bfloat16)
+    pol[..., :V] = inp_cpu["policy"]
+    ref[..., :V] = inp_cpu["ref"]
+    polg, refg = pol.to(DEV)[..., :V], ref.to(DEV)[..., :V]
+    other = {k: v.to(DEV) for k, v in inp_cpu.items() if k not in ("policy", "ref")}
+    gbuf = torch.full((B, T, ld), 7.0, dtype=torch.bfloat16, device=DEV)
+    res = gpu_lib.grpo_loss_fwd_bwd(polg, refg, other["action_ids"], other["old_logps"],
+                                    other["rewards"], other["mask"], grad_out=gbuf[..., :V],
+                                    **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert torch.all(gbuf[..., V:] == 7.0), "padding of the gradient must stay untouched"
+    h = host_inputs(inp_cpu)
+    r = oracle_logits(h, wl)
+    compare_exact_parts(res, r)
+    compare_scalars(res, r, 1e-4)
+    compare_logits_grad(to_np(gbuf[..., :V]), r, cfg_from(wl), h["mask"], True)
+
+
+def test_int32_ids_and_f32_grad_from_bf16(gpu_lib):
+    wl = _custom(3000, "bf16", T=4)
+    announce("int32 ids, bf16 logits -> f32 grad")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=9)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    ids32 = inp["action_ids"].to(torch.int32)
+    res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], ids32, inp["old_logps"],
+                                    inp["rewards"], inp["mask"], grad_dtype=torch.float32,
+                                    **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert res.grad.dtype == torch.float32
+    h = host_inputs(inp_cpu)
+    r = oracle_logits(h, wl)
+    compare_scalars(res, r, 1e-4)
+    # float32 output: the tighter float32 criterion applies
+    compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], False)
+
+
+def test_no_reference_beta_zero(gpu_lib):
+    wl = _custom(513, "f32", T=4, beta=0.0)
+    announce("beta=0 without reference logits")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=4)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], None, inp["action_ids"], inp["old_logps"],
+                                    inp["rewards"], inp["mask"], **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    r = oracle_logits(h, wl, with_ref=False)
+    compare_scalars(res, r, 1e-5)
+    assert float(res.kl) == 0.0
+    compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], False)
+
+
+# ---------------------------------------------------------------------------
+# advantages and weights: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["bernoulli", "normal", "tiny_std"])
+@pytest.mark.parametrize("loo", [False, True])
+@pytest.mark.parametrize("scale", [True, False])
+def test_advantages_bit_exact(gpu_lib, kind, loo, scale):
+    announce(f"advantages {kind} loo={loo} scale={scale}")
+    rng = np.random.default_rng(zlib.crc32(f"{kind}{loo}{scale}".encode()))
+    sizes = [2, 3, 4, 5, 8, 16, 7, 64, 2, 31]
+    off = [0] + list(np.cumsum(sizes))
+    B = off[-1]
+    if kind == "bernoulli":
+        r = rng.integers(0, 2, B).astype(np.float32)
+    elif kind == "normal":
+        r = rng.normal(0.3, 1.7, B).astype(np.float32)
+    else:
+        r = (1.0 + rng.normal(0, 1e-7, B)).astype(np.float32)
+    rt = torch.tensor(r, device=DEV)
+    a = gpu_lib.grpo_advantages(rt, group_boundaries=off, leave_one_out=loo, scale_by_std=scale)
+    torch.cuda.synchronize()
+    ref = oracle.grpo_advantages(r, groups=dict(group_boundaries=off, leave_one_out=loo,
+                                                scale_by_std=scale))
+    assert_bits_equal(to_np(a), ref, "advantages")
+    # uniform groups
+    B2 = 8 * 16
+    r2 = rng.normal(0, 1, B2).astype(np.float32)
+    a2 = gpu_lib.grpo_advantages(torch.tensor(r2, device=DEV), samples_per_prompt=8,
+                                 leave_one_out=loo, scale_by_std=scale)
+    torch.cuda.synchronize()
+    ref2 = oracle.grpo_advantages(r2, groups=dict(samples_per_prompt=8, leave_one_out=loo,
+                                                  scale_by_std=scale))
+    assert_bits_equal(to_np(a2), ref2, "advantages uniform")
+
+
+def test_many_group_sqrt_and_division_bit_exact(gpu_lib):
+    """Thousands of groups with random real rewards: every binary64 sqrt and
+    division on the device must round exactly like numpy's."""
+    announce("advantages 4096 groups")
+    rng = np.random.default_rng(77)
+    sizes = rng.integers(2, 20, 4096)
+    off = [0] + list(np.cumsum(sizes))
+    r = (rng.standard_normal(off[-1]) * rng.uniform(1e-3, 1e3)).astype(np.float32)
+    a = gpu_lib.grpo_advantages(torch.tensor(r, device=DEV), group_boundaries=off)
+    torch.cuda.synchronize()
+    ref = oracle.grpo_advantages(r, groups=dict(group_boundaries=off))
+    assert_bits_equal(to_np(a), ref, "advantages")
+
+
+@pytest.mark.parametrize("reduction,alpha", [("token_mean", None), ("sequence_mean", None),
+                                             ("length_alpha", 0.5), ("length_alpha", 0.0),
+                                             ("length_alpha", 1.0)])
+def test_weights_bit_exact(gpu_lib, reduction, alpha):
+    announce(f"weights {reduction} alpha={alpha}")
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    inp_cpu = make_token_inputs(wl, device="cpu", seed=3, B=64, T=300)
+    inp_cpu["mask"][5] = False  # an empty sequence
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                                  inp["mask"], samples_per_prompt=16, reduction=reduction,
+                                  alpha=alpha)
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                                 groups=dict(samples_per_prompt=16),
+                                 cfg=oracle.LossConfig(reduction=reduction, alpha=alpha))
+    compare_exact_parts(res, ref)
+
+
+def test_weights_general_alpha_within_one_ulp(gpu_lib):
+    announce("weights alpha=0.3")
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    inp_cpu = make_token_inputs(wl, device="cpu", seed=4, B=32, T=500)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                                  inp["mask"], samples_per_prompt=16, reduction="length_alpha",
+                                  alpha=0.3)
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                                 groups=dict(samples_per_prompt=16),
+                                 cfg=oracle.LossConfig(reduction="length_alpha", alpha=0.3))
+    g = to_np(res.seq_weight).astype(np.float32).view(np.int32).astype(np.int64)
+    r = ref.seq_weight.astype(np.float32).view(np.int32).astype(np.int64)
+    assert np.max(np.abs(g - r)) <= 1
+
+
+# ---------------------------------------------------------------------------
+# logprob-level token loss
+# ---------------------------------------------------------------------------
+
+def check_token_case(rpl, wl, B, T, seed=0, reduction=None):
+    announce(f"token loss {wl.name} B={B} T={T} seed={seed}")
+    inp_cpu = make_token_inputs(wl, device="cpu", seed=seed, B=B, T=T)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    red = reduction or wl.reduction
+    res = rpl.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                              inp["mask"], eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
+                              samples_per_prompt=wl.group_size, reduction=red, per_token=True)
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    cfg = oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=red)
+    ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                                 groups=dict(samples_per_prompt=wl.group_size), cfg=cfg)
+    compare_exact_parts(res, ref)
+    compare_scalars(res, ref, 1e-5)
+    g = to_np(res.grad)
+    gmax = float(np.max(np.abs(ref.grad)))
+    err = np.abs(g - ref.grad)
+    # inputs are float32 log-probs: the only ambiguity is the float32 ratio at a clip bound
+    rho = ref.tok["rho"]
+    lo, hi = 1 - wl.eps_low, 1 + wl.eps_high
+    amb = (np.abs(rho - hi) <= 4e-7 * rho) | (np.abs(rho - lo) <= 4e-7 * rho)
+    bad = (err > 1e-5 * gmax) & ~amb
+    assert not bad.any(), f"{int(bad.sum())} dlogp values out of tolerance"
+    assert np.all(g[~h["mask"]] == 0.0)
+    return res, ref
+
+
+def test_token_loss_small_full(gpu_lib):
+    check_token_case(gpu_lib, TOKEN_WORKLOADS["token_loss_full"], B=64, T=257)
+
+
+def test_token_loss_small_ragged(gpu_lib):
+    check_token_case(gpu_lib, TOKEN_WORKLOADS["token_loss_ragged"], B=64, T=1000)
+
+
+@pytest.mark.parametrize("reduction", ["token_mean", "length_alpha"])
+def test_token_loss_other_reductions(gpu_lib, reduction):
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    if reduction == "length_alpha":
+        import dataclasses
+        announce("token loss alpha")
+        inp_cpu = make_token_inputs(wl, device="cpu", seed=8, B=32, T=128)
+        inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+        res = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"],
+                                      inp["rewards"], inp["mask"], samples_per_prompt=16,
+                                      reduction="length_alpha", alpha=0.5)
+        torch.cuda.synchronize()
+        h = host_inputs(inp_cpu)
+        ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"],
+                                     h["rewards"], groups=dict(samples_per_prompt=16),
+                                     cfg=oracle.LossConfig(reduction="length_alpha", alpha=0.5))
+        compare_exact_parts(res, ref)
+        compare_scalars(res, ref, 1e-5)
+    else:
+        check_token_case(gpu_lib, wl, B=32, T=130, reduction=reduction)
+
+
+def test_token_loss_unaligned_scalar_path(gpu_lib):
+    """T not a multiple of 4: the scalar path of the token kernel."""
+    check_token_case(gpu_lib, TOKEN_WORKLOADS["token_loss_ragged"], B=32, T=131)
