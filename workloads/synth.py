@@ -65,8 +65,9 @@ class LogitsWorkload:
         T2 = self.T if T is None else T
         lr = self.len_range
         if lr is not None and T is not None:
-            lo = max(1, min(lr[0], T2))
-            lr = (lo, T2)
+            # keep the same length mix relative to T
+            lo = max(1, int(round(lr[0] * T2 / self.T)))
+            lr = (min(lo, T2), T2)
         return replace(self, T=T2, V=self.V if V is None else V, group_sizes=gs,
                        len_range=lr, name=f"{self.name}[B{sum(gs)},T{T2},V{self.V if V is None else V}]")
 
