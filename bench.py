@@ -13,10 +13,13 @@ the vocabulary kernel (algorithmic bytes over its own HIP-event-timed
 duration, against 8 TB/s HBM), and the fp64 CPU oracle's rate on a bounded
 sample of the same workload.
 
-Auxiliary modes:
-  --calibrate            also run a plain device copy of known size (for the
-                         counter scaling of rocprofv3 --pmc runs)
-  --summarize-pmc DIR... write a profiles/ summary from rocprofv3 csv output
+Auxiliary modes (for the HBM-traffic counters, see profiles/):
+  --calibrate-only       run only a plain elementwise kernel over 2 GiB that
+                         reads and writes known bytes (counter scale)
+  --summarize-pmc F W CF CW
+                         write profiles/<kernel>_<workload>_pmc.json from four
+                         rocprofv3 --pmc csv runs: FETCH_SIZE and WRITE_SIZE of
+                         the bench, then of the calibration run
 """
 
 from __future__ import annotations
@@ -146,6 +149,50 @@ def load_traffic(workload):
     return d.get("traffic_bytes_per_launch")
 
 
+def run_token(args):
+    """Logprob-level token loss (no vocabulary).  The 71 MB working set fits
+    the memory-side cache, so the timed loop rotates over enough input copies
+    (each call reads a different one) to keep it from being served there."""
+    import torch
+    import rl_post_loss_amd as rpl
+    from workloads import TOKEN_WORKLOADS, make_token_inputs
+
+    rpl.load_library()
+    dev = torch.device("cuda:0")
+    wl = TOKEN_WORKLOADS[args.workload]
+    copies = [make_token_inputs(wl, device=dev, seed=args.seed + k) for k in range(args.copies)]
+    outs = [torch.empty((wl.B, wl.T), dtype=torch.float32, device=dev) for _ in range(args.copies)]
+    kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
+              samples_per_prompt=wl.group_size, reduction=wl.reduction)
+
+    def step(k):
+        c = copies[k % len(copies)]
+        return rpl.grpo_token_loss(c["logp"], c["old_logps"], c["ref_logp"], c["rewards"], c["mask"],
+                                   **kw)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    m = copies[0]["mask"]
+    active = int(m.sum())
+    rows = wl.B * wl.T
+    alg = active * 17 + (rows - active) * 5
+    out = {"metric": "tokens/s for the logprob-level GRPO token loss (forward + dlogp)",
+           "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{wl.name}: B={wl.B} ({wl.num_groups} groups of {wl.group_size}), "
+                                  f"T={wl.T}, {wl.reduction}, input copies rotated: {args.copies}",
+                      "active_tokens": active, "algorithmic_bytes": alg,
+                      "step_GBps": alg / (ms * 1e-3) / 1e9}}
+    print(json.dumps(out), flush=True)
+
+
 def run(args):
     import torch
     import rl_post_loss_amd as rpl
@@ -170,13 +217,6 @@ def run(args):
     def step():
         return rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
                                      inp["rewards"], inp["mask"], grad_out=grad, **kw)
-
-    if args.calibrate:
-        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for _ in range(args.warmup):
         res = step()
@@ -246,41 +286,69 @@ def run(args):
     print(json.dumps(out), flush=True)
 
 
-def summarize_pmc(dirs, workload, out_dir):
-    """Combine a FETCH_SIZE run and a WRITE_SIZE run (rocprofv3 csv output
-    under ``dirs``) into profiles/<kernel>_<workload>_pmc.json + .txt.  The
-    counters of the calibration copy (2 GiB read, 2 GiB written) give the
-    scale from counter units to bytes."""
+def calibrate_only():
+    """One elementwise kernel over CALIB_BYTES of float32: reads CALIB_BYTES,
+    writes CALIB_BYTES (torch.add with a scalar, out= a second buffer)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_bytes_read": CALIB_BYTES, "calibration_bytes_written": CALIB_BYTES,
+                      "check": float(dst[0])}))
+
+
+def _pmc_values(d, counter, name_part):
+    """Per-dispatch counter values (summed over the csv rows of a dispatch)
+    of kernels whose name contains ``name_part``."""
     import csv
-    vals = {"FETCH_SIZE": {}, "WRITE_SIZE": {}}
-    for d in dirs:
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(path) as f:
-                for row in csv.DictReader(f):
-                    name = row.get("Counter_Name")
-                    if name not in vals:
-                        continue
-                    kern = row.get("Kernel_Name", "")
-                    key = "copy" if ("copy" in kern.lower() or "elementwise" in kern.lower()) else \
-                          ("rows" if ROW_KERNEL in kern else None)
-                    if key is None:
-                        continue
-                    did = row.get("Dispatch_Id")
-                    vals[name].setdefault(key, {}).setdefault(did, 0.0)
-                    vals[name][key][did] += float(row["Counter_Value"])
+    per = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or name_part not in row.get("Kernel_Name", ""):
+                    continue
+                did = row.get("Dispatch_Id")
+                per[did] = per.get(did, 0.0) + float(row["Counter_Value"])
+    return list(per.values())
+
+
+def summarize_pmc(dirs, workload, out_dir):
+    """Combine the four rocprofv3 --pmc runs into profiles/<kernel>_<workload>_pmc.json.
+    The counters read over the calibration kernel, which moves a known number
+    of bytes each way, give the scale from counter units to bytes."""
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
     res = {}
-    for name, per in vals.items():
-        copy = max(per.get("copy", {}).values(), default=None)
-        rows = list(per.get("rows", {}).values())
-        if copy is None or not rows:
-            raise SystemExit(f"missing {name} data for the copy or the row kernel")
-        scale = CALIB_BYTES / copy          # bytes per counter unit
-        res[name] = dict(copy_counter=copy, scale_bytes_per_unit=scale,
-                         row_kernel_counter_avg=sum(rows) / len(rows),
-                         row_kernel_bytes_avg=sum(rows) / len(rows) * scale, dispatches=len(rows))
+    for counter, run_dir, cal_dir in (("FETCH_SIZE", fetch_dir, cal_fetch_dir),
+                                      ("WRITE_SIZE", write_dir, cal_write_dir)):
+        cal = _pmc_values(cal_dir, counter, "_add<float>")
+        rows = _pmc_values(run_dir, counter, ROW_KERNEL)
+        if not cal or not rows:
+            raise SystemExit(f"missing {counter} values (calibration {len(cal)}, row kernel {len(rows)})")
+        c = max(cal)
+        scale = CALIB_BYTES / c
+        res[counter] = dict(calibration_counter=c, calibration_bytes=CALIB_BYTES,
+                            scale_bytes_per_unit=scale,
+                            row_kernel_counter_per_dispatch=rows,
+                            row_kernel_bytes_avg=sum(rows) / len(rows) * scale)
     traffic = res["FETCH_SIZE"]["row_kernel_bytes_avg"] + res["WRITE_SIZE"]["row_kernel_bytes_avg"]
     summary = dict(kernel=ROW_KERNEL, workload=workload, kernel_source_hash=kernel_source_hash(),
-                   counters=res, traffic_bytes_per_launch=traffic)
+                   counters=res, traffic_bytes_per_launch=traffic,
+                   commands=["rocprofv3 --pmc FETCH_SIZE --kernel-include-regex grpo_rows -f csv "
+                             f"-d gpurun_out/pmc_fetch -o run -- python3 bench.py --workload {workload} "
+                             "--steps 3 --warmup 1 --no-cpu-baseline",
+                             "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex grpo_rows -f csv "
+                             f"-d gpurun_out/pmc_write -o run -- python3 bench.py --workload {workload} "
+                             "--steps 3 --warmup 1 --no-cpu-baseline",
+                             "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex elementwise -f csv "
+                             "-d gpurun_out/pmc_cal_fetch -o run -- python3 bench.py --calibrate-only",
+                             "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex elementwise -f csv "
+                             "-d gpurun_out/pmc_cal_write -o run -- python3 bench.py --calibrate-only",
+                             "python bench.py --workload " + workload + " --summarize-pmc "
+                             "gpurun_out/pmc_fetch gpurun_out/pmc_write gpurun_out/pmc_cal_fetch "
+                             "gpurun_out/pmc_cal_write"])
     os.makedirs(out_dir, exist_ok=True)
     base = os.path.join(out_dir, f"{ROW_KERNEL}_{workload}_pmc")
     with open(base + ".json", "w") as f:
@@ -297,9 +365,13 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--calibrate", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs="+", default=None)
+    ap.add_argument("--copies", type=int, default=6, help="input copies rotated by the token-loss bench")
+    ap.add_argument("--calibrate-only", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, default=None)
     args = ap.parse_args()
+    if args.calibrate_only:
+        calibrate_only()
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.workload, os.path.join(ROOT, "profiles"))
         return
@@ -308,7 +380,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    run(args)
+    if args.workload.startswith("token_loss"):
+        run_token(args)
+    else:
+        run(args)
 
 
 if __name__ == "__main__":
