@@ -16,6 +16,7 @@ hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream);
 hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
+bool resident_fits(int64_t V, int tin_bf16);
 }  // namespace grpo
 
 using namespace grpo;
@@ -131,11 +132,19 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
+#ifndef GRPO_RESIDENT
+#define GRPO_RESIDENT 1    // use the resident-row kernel where it fits
+#endif
+
+#ifndef GRPO_NT_LARGE
+#define GRPO_NT_LARGE 1024  // threads per row for rows above 64 KB
+#endif
+
 int choose_nt(int64_t V, int esize) {
   const int64_t bytes = V * esize;
   if (bytes <= 4096) return 64;
   if (bytes <= 65536) return 256;
-  return 512;
+  return GRPO_NT_LARGE;
 }
 
 }  // namespace
@@ -345,6 +354,12 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   l.nt = choose_nt(V, fdtype_size(logits_dtype));
   l.vec = rows_vectorizable(policy_logits, ref_logits, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);
+  // rows above 4 KB that fit in one block's registers keep the policy row
+  // resident between the two passes (fused mode only)
+  // rows above 4 KB that fit one block's registers keep the policy row
+  // resident between the passes (fused mode); longer rows stream
+  l.resident = GRPO_RESIDENT && grad_out && l.vec && V * fdtype_size(logits_dtype) > 4096 &&
+               resident_fits(V, l.tin_bf16);
   const bool timed = g_ev_start && g_ev_stop;
   if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
   if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;

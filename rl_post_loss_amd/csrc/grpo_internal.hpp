@@ -112,6 +112,7 @@ struct RowLaunch {
   int tg_bf16;   // gradient is bf16 (else f32)
   int nt;        // threads per row: 64, 256, 512 or 1024
   int vec;       // every row is 16-byte aligned: 16-byte chunks
+  int resident;  // fused mode with the policy row held in registers
 };
 
 // Per-sequence and scalar reduction.

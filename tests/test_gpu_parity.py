@@ -101,6 +101,14 @@ def test_vocab_sizes_and_paths(gpu_lib, V, dtype):
     check_logits_case(gpu_lib, _custom(V, dtype))
 
 
+@pytest.mark.parametrize("V,dtype", [(40000, "bf16"), (20001 * 4 // 4, "f32")])
+def test_many_rows_per_block(gpu_lib, V, dtype):
+    """More rows than compute units, ragged masks: each persistent block walks
+    several rows and skips (zero-fills) the masked ones between them."""
+    wl = _custom(V, dtype, T=64, sizes=(8, 8), len_range=(1, 64))
+    check_logits_case(gpu_lib, wl, seed=21)
+
+
 def test_padded_row_stride_vector_tail(gpu_lib):
     """Rows padded to a 16-byte multiple: the vector path with a scalar tail."""
     rpl = gpu_lib
