@@ -166,17 +166,41 @@ def run_token(args):
     kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
               samples_per_prompt=wl.group_size, reduction=wl.reduction)
 
-    def step(k):
-        c = copies[k % len(copies)]
-        return rpl.grpo_token_loss(c["logp"], c["old_logps"], c["ref_logp"], c["rewards"], c["mask"],
-                                   **kw)
+    results = [None] * len(copies)
 
-    for k in range(args.warmup):
+    def step(k):
+        j = k % len(copies)
+        c = copies[j]
+        results[j] = rpl.grpo_token_loss(c["logp"], c["old_logps"], c["ref_logp"], c["rewards"],
+                                         c["mask"], out=results[j], **kw)
+
+    for k in range(max(args.warmup, len(copies))):
         step(k)
     torch.cuda.synchronize()
+    # eager calls (Python binding overhead included)
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(k)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the same calls captured in HIP graphs, one per input copy: GPU time of the path
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(len(copies)):
+            step(j)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for j in range(len(copies)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(j)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % len(graphs)].replay()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     m = copies[0]["mask"]
@@ -190,7 +214,8 @@ def run_token(args):
            "config": {"workload": f"{wl.name}: B={wl.B} ({wl.num_groups} groups of {wl.group_size}), "
                                   f"T={wl.T}, {wl.reduction}, input copies rotated: {args.copies}",
                       "active_tokens": active, "algorithmic_bytes": alg,
-                      "step_GBps": alg / (ms * 1e-3) / 1e9}}
+                      "step_GBps": alg / (ms * 1e-3) / 1e9, "timing": "HIP graph replays",
+                      "ms_per_step_eager_python": ms_eager}}
     print(json.dumps(out), flush=True)
 
 

@@ -47,12 +47,10 @@
  * a fixed order, so repeated calls with the same inputs and sizes give
  * bit-identical outputs.
  *
- * Workspace: grpo_workspace_bytes() bytes of device memory, 256-byte aligned,
- * ZERO-FILLED before its first use (grpo_workspace_init() does that).  The
- * library keeps its internal completion counters at zero at the end of every
- * call, so a workspace can be reused without clearing it again.  A workspace
- * serves one call at a time: calls that share a workspace must be ordered on
- * one stream.  grpo_loss_fwd_bwd() with grad_out == NULL leaves per-row
+ * Workspace: grpo_workspace_bytes() bytes of device memory, 256-byte aligned.
+ * Its contents need no initialisation: every call writes each workspace value
+ * before reading it.  A workspace serves one call at a time: calls that share
+ * a workspace must be ordered on one stream.  grpo_loss_fwd_bwd() with grad_out == NULL leaves per-row
  * state in the workspace that grpo_loss_bwd() consumes; it stays valid until
  * the next call that uses the same workspace.
  *
@@ -174,7 +172,8 @@ GRPO_API const char *grpo_status_str(int status);
  * entry point below for these sizes. */
 GRPO_API size_t grpo_workspace_bytes(int64_t B, int64_t T, int32_t num_groups);
 
-/* Zero-fills a workspace (needed once, before its first use). */
+/* Zero-fills a workspace.  Optional (calls never read uninitialised
+ * workspace bytes); useful to make a fresh workspace's contents defined. */
 GRPO_API grpo_status grpo_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Group-relative advantages alone ([GRPO-LOSS] Accuracy; [DOCKYARD]

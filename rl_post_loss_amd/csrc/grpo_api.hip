@@ -15,6 +15,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream);
+hipError_t launch_final(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
 bool resident_fits(int64_t V, int tin_bf16);
 }  // namespace grpo
@@ -123,6 +124,22 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
   a.seq_weight_out = out ? out->seq_weight : nullptr;
   a.seq_tokens_out = out ? out->seq_tokens : nullptr;
   return launch_prep(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+grpo_status run_final(const Ws& w, int64_t B, double beta, const grpo_outputs* out,
+                      hipStream_t s) {
+  FinalArgs f{};
+  f.B = B;
+  f.beta = float(beta);
+  f.hdr = w.hdr();
+  f.w = w.at<double>(w.l.w);
+  f.P = w.at<double>(w.l.P);
+  f.K = w.at<double>(w.l.K);
+  f.C = w.at<int64_t>(w.l.C);
+  f.scalars = out->scalars;
+  f.counts = out->counts;
+  f.status = out->status;
+  return launch_final(f, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
 int fdtype_size(int32_t dt) { return dt == GRPO_F32 ? 4 : (dt == GRPO_BF16 ? 2 : 0); }
@@ -237,14 +254,12 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.P = w.at<double>(w.l.P);
   a.K = w.at<double>(w.l.K);
   a.C = w.at<int64_t>(w.l.C);
-  a.scalars = out->scalars;
   a.seq_policy = out->seq_policy;
   a.seq_kl = out->seq_kl;
-  a.counts = out->counts;
-  a.status = out->status;
   a.out_loss = out->tok_loss;
   a.out_kl = out->tok_kl;
-  return launch_token(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+  if (launch_token(a, s) != hipSuccess) return GRPO_ERR_HIP;
+  return run_final(w, B, cfg->beta, out, s);
 }
 
 static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype,
@@ -377,12 +392,10 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   r.P = w.at<double>(w.l.P);
   r.K = w.at<double>(w.l.K);
   r.C = w.at<int64_t>(w.l.C);
-  r.scalars = out->scalars;
   r.seq_policy = out->seq_policy;
   r.seq_kl = out->seq_kl;
-  r.counts = out->counts;
-  r.status = out->status;
-  return launch_reduce(r, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+  if (launch_reduce(r, s) != hipSuccess) return GRPO_ERR_HIP;
+  return run_final(w, B, cfg->beta, out, s);
 }
 
 grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64_t row_stride,

@@ -126,21 +126,4 @@ __device__ __forceinline__ long long block_sum_i64(long long v, long long* sh) {
   }
 }
 
-// "Last block done" ticket.  Every block publishes its results, fences, and
-// takes a ticket; the block that draws nblocks-1 sees all results and runs
-// the final fixed-order step.  atomicInc wraps the counter back to zero, so
-// it is zero again after every launch.  Must be called by all threads.
-__device__ __forceinline__ bool last_block(unsigned* counter, unsigned nblocks, int* sh_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned t = atomicInc(counter, nblocks - 1);
-    *sh_flag = (t == nblocks - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *sh_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
 }  // namespace grpo

@@ -11,10 +11,9 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace header (first 256 bytes).
+// Workspace header (first 256 bytes).  Every call writes what it later reads:
+// the prep kernel clears `status`, the weights kernel writes `num_tokens`.
 struct WsHeader {
-  uint32_t ticket_prep;   // completion counter of the prep kernel
-  uint32_t ticket_final;  // completion counter of the final reduction
   uint32_t status;        // GRPO_FAULT_* bits gathered during the call
   uint32_t pad0;
   int64_t num_tokens;     // N
@@ -115,7 +114,7 @@ struct RowLaunch {
   int resident;  // fused mode with the policy row held in registers
 };
 
-// Per-sequence and scalar reduction.
+// Per-sequence reduction (stage 1).
 struct ReduceArgs {
   int64_t B, T;
   float beta;
@@ -128,9 +127,20 @@ struct ReduceArgs {
   double* K;
   int64_t* C;
   // outputs
-  float* scalars;
   float* seq_policy;
   float* seq_kl;
+};
+
+// Scalar reduction (stage 2).
+struct FinalArgs {
+  int64_t B;
+  float beta;
+  WsHeader* hdr;
+  const double* w;
+  const double* P;
+  const double* K;
+  const int64_t* C;
+  float* scalars;
   int64_t* counts;
   uint32_t* status;
 };
@@ -153,11 +163,8 @@ struct TokenArgs {
   double* K;
   int64_t* C;
   // outputs
-  float* scalars;
   float* seq_policy;
   float* seq_kl;
-  int64_t* counts;
-  uint32_t* status;
   float* out_loss;
   float* out_kl;
 };

@@ -11,6 +11,10 @@
 // Everything here is binary64 with contraction off, in the same sequential
 // order as the defining formulas, so advantages and weights round to the
 // same float32 bits as any other correct binary64 evaluation of that order.
+//
+// Two kernels, so that no block ever waits on another: grpo_prep_kernel (one
+// block per sequence: L_i and A_i) and grpo_weights_kernel (one block: N and
+// every w_i).  The kernel boundary between them makes the counts visible.
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
@@ -19,32 +23,14 @@
 namespace grpo {
 
 constexpr int kPrepThreads = 256;
+constexpr int kWeightThreads = 1024;
+constexpr int kRewardStage = 1024;  // rewards of one group staged in LDS per round
 
 // Number of nonzero bytes in a 32-bit word.  For each byte b, bit 7 of
 // ((b & 0x7f) + 0x7f) | b is set exactly when b != 0 (no carry crosses bytes).
 __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
   uint32_t t = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
   return __popc(t);
-}
-
-__device__ double group_advantage(const float* __restrict__ r, int64_t s, int64_t e, int64_t i,
-                                  bool leave_one_out, bool scale_by_std, double std_eps) {
-#pragma clang fp contract(off)
-  const int64_t n = e - s;
-  double total = 0.0;
-  for (int64_t j = s; j < e; ++j) total = total + double(r[j]);
-  const double mean = total / double(n);
-  double sq = 0.0;
-  for (int64_t j = s; j < e; ++j) {
-    const double dev = double(r[j]) - mean;
-    sq = sq + dev * dev;
-  }
-  const double sd = sqrt(sq / double(n));
-  const double denom = sd >= std_eps ? sd : std_eps;
-  const double ri = double(r[i]);
-  const double base = leave_one_out ? (total - ri) / double(n - 1) : mean;
-  const double diff = ri - base;
-  return scale_by_std ? diff / denom : diff;
 }
 
 __device__ double sequence_weight(int32_t reduction, double alpha, int64_t B, int64_t L,
@@ -62,13 +48,18 @@ __device__ double sequence_weight(int32_t reduction, double alpha, int64_t B, in
   return num / (double(B) * Lf);
 }
 
+// One block per sequence i: L_i (active slots) and A_i.  The group's rewards
+// are staged in LDS by all threads; one thread then forms the binary64 sums
+// in index order.  Block 0 also clears the workspace fault word, which no
+// other kernel of the call writes before this one has finished.
 __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
+#pragma clang fp contract(off)
   __shared__ long long sh_i64[kPrepThreads / kWave];
-  __shared__ int sh_flag;
+  __shared__ float sh_r[kRewardStage];
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
+  if (i == 0 && tid == 0 && a.want_weights) a.hdr->status = 0;
 
-  // L_i: active slots of sequence i
   long long cnt = 0;
   if (a.T > 0) {
     if (a.mask == nullptr) {
@@ -85,52 +76,98 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
   }
   const long long L = block_sum_i64<kPrepThreads>(cnt, sh_i64);
 
-  if (tid == 0) {
-    int64_t s, e;
-    if (a.spp > 0) {
-      s = (i / a.spp) * a.spp;
-      e = s + a.spp;
-    } else {
-      int lo = 0, hi = a.num_groups;  // offsets[lo] <= i < offsets[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) / 2;
-        if (a.offsets[mid] <= i) lo = mid; else hi = mid;
-      }
-      s = a.offsets[lo];
-      e = a.offsets[lo + 1];
+  // group [s, e) of sequence i
+  int64_t s, e;
+  if (a.spp > 0) {
+    s = (i / a.spp) * a.spp;
+    e = s + a.spp;
+  } else {
+    int lo = 0, hi = a.num_groups;  // offsets[lo] <= i < offsets[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (a.offsets[mid] <= i) lo = mid; else hi = mid;
     }
-    const double adv = group_advantage(a.rewards, s, e, i, a.leave_one_out != 0,
-                                       a.scale_by_std != 0, a.std_eps);
-    const float advf = float(adv);
+    s = a.offsets[lo];
+    e = a.offsets[lo + 1];
+  }
+  const int64_t n = e - s;
+
+  // S = sum r (index order), then var = sum (r - mean)^2 / n; groups longer
+  // than the stage go through it in rounds, keeping the sequential order
+  double total = 0.0;
+  for (int64_t b = s; b < e; b += kRewardStage) {
+    const int64_t m = (e - b) < kRewardStage ? (e - b) : kRewardStage;
+    __syncthreads();
+    for (int64_t k = tid; k < m; k += kPrepThreads) sh_r[k] = a.rewards[b + k];
+    __syncthreads();
+    if (tid == 0)
+      for (int64_t k = 0; k < m; ++k) total = total + double(sh_r[k]);
+  }
+  double sq = 0.0;
+  if (n <= kRewardStage) {
+    // the stage still holds the whole group
+    if (tid == 0) {
+      const double mean = total / double(n);
+      for (int64_t k = 0; k < n; ++k) {
+        const double dev = double(sh_r[k]) - mean;
+        sq = sq + dev * dev;
+      }
+    }
+  } else {
+    const double mean_all = total / double(n);  // only thread 0's value is used
+    for (int64_t b = s; b < e; b += kRewardStage) {
+      const int64_t m = (e - b) < kRewardStage ? (e - b) : kRewardStage;
+      __syncthreads();
+      for (int64_t k = tid; k < m; k += kPrepThreads) sh_r[k] = a.rewards[b + k];
+      __syncthreads();
+      if (tid == 0)
+        for (int64_t k = 0; k < m; ++k) {
+          const double dev = double(sh_r[k]) - mean_all;
+          sq = sq + dev * dev;
+        }
+    }
+  }
+  if (tid == 0) {
+    const double mean = total / double(n);
+    const double sd = sqrt(sq / double(n));
+    const double denom = sd >= a.std_eps ? sd : a.std_eps;
+    const double ri = double(a.rewards[i]);
+    const double base = a.leave_one_out ? (total - ri) / double(n - 1) : mean;
+    const double diff = ri - base;
+    const float advf = float(a.scale_by_std ? diff / denom : diff);
     a.A[i] = advf;
     if (a.adv_out) a.adv_out[i] = advf;
     a.L[i] = int32_t(L);
     if (a.seq_tokens_out) a.seq_tokens_out[i] = int32_t(L);
   }
-  if (!a.want_weights) return;
+}
 
-  if (last_block(&a.hdr->ticket_prep, unsigned(gridDim.x), &sh_flag)) {
-    long long n = 0;
-    for (int64_t k = tid; k < a.B; k += kPrepThreads) n += a.L[k];
-    const long long N = block_sum_i64<kPrepThreads>(n, sh_i64);
-    for (int64_t k = tid; k < a.B; k += kPrepThreads) {
-      const double wk = sequence_weight(a.reduction, a.alpha, a.B, a.L[k], N);
-      a.w[k] = wk;
-      if (a.seq_weight_out) a.seq_weight_out[k] = float(wk);
-    }
-    if (tid == 0) {
-      a.hdr->num_tokens = N;
-      if (N == 0) atomicOr(&a.hdr->status, GRPO_FAULT_NO_TOKENS);
-    }
+// One block: N = sum L_i, then every w_i.
+__global__ __launch_bounds__(kWeightThreads) void grpo_weights_kernel(PrepArgs a) {
+  __shared__ long long sh_i64[kWeightThreads / kWave];
+  const int tid = threadIdx.x;
+  long long n = 0;
+  for (int64_t k = tid; k < a.B; k += kWeightThreads) n += a.L[k];
+  const long long N = block_sum_i64<kWeightThreads>(n, sh_i64);
+  for (int64_t k = tid; k < a.B; k += kWeightThreads) {
+    const double wk = sequence_weight(a.reduction, a.alpha, a.B, a.L[k], N);
+    a.w[k] = wk;
+    if (a.seq_weight_out) a.seq_weight_out[k] = float(wk);
+  }
+  if (tid == 0) {
+    a.hdr->num_tokens = N;
+    if (N == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
   }
 }
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(grpo_prep_kernel, dim3(unsigned(a.B)), dim3(kPrepThreads), 0, stream, a);
+  if (!a.want_weights) return hipGetLastError();
+  hipLaunchKernelGGL(grpo_weights_kernel, dim3(1), dim3(kWeightThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-// Workspace clearing (used once, before a workspace's first call).
+// Workspace clearing (optional: every call initialises what it reads).
 __global__ void grpo_zero_kernel(uint4* p, size_t n16) {
   for (size_t k = size_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n16;
        k += size_t(gridDim.x) * blockDim.x)

@@ -6,8 +6,9 @@
 // Both stages run in a fixed tree in binary64 without atomics, so results
 // are bit-identical from run to run.  The grpo.cpp README (CUDA section)
 // measures per-token atomics against block reduction for the same loss; here
-// no float atomic is used at all: the last block to finish (an integer
-// ticket) does the scalar stage.
+// no atomic is used at all: the per-sequence stage is one kernel (a block per
+// sequence) and the scalar stage a second, single-block kernel, so no block
+// ever waits on, or fences for, another.
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
@@ -17,38 +18,42 @@ namespace grpo {
 
 constexpr int kRedThreads = 256;
 
-// Scalar stage: policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i (binary64),
-// written as float32, plus the token and clip counts and the fault bits.
-// Run by every thread of the last block.
-__device__ void final_scalars(int64_t B, float beta, WsHeader* hdr, const double* w,
-                              const double* P, const double* K, const int64_t* C,
-                              float* scalars, int64_t* counts, uint32_t* status,
-                              double* sh_f64, long long* sh_i64) {
+// Scalar stage (one block): policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i in
+// binary64, written as float32, plus the token and clip counts and the fault
+// bits of the call.
+constexpr int kFinalThreads = 1024;
+
+__global__ __launch_bounds__(kFinalThreads) void grpo_final_kernel(FinalArgs a) {
 #pragma clang fp contract(off)
+  __shared__ double sh_f64[kFinalThreads / kWave];
+  __shared__ long long sh_i64[kFinalThreads / kWave];
   const int tid = threadIdx.x;
   double pl = 0.0, kl = 0.0;
   long long ct = 0;
-  for (int64_t j = tid; j < B; j += kRedThreads) {
-    pl = pl + w[j] * P[j];
-    kl = kl + w[j] * K[j];
-    ct += C[j];
+  for (int64_t j = tid; j < a.B; j += kFinalThreads) {
+    pl = pl + a.w[j] * a.P[j];
+    kl = kl + a.w[j] * a.K[j];
+    ct += a.C[j];
   }
-  pl = block_sum_f64<kRedThreads>(pl, sh_f64);
-  kl = block_sum_f64<kRedThreads>(kl, sh_f64);
-  ct = block_sum_i64<kRedThreads>(ct, sh_i64);
+  pl = block_sum_f64<kFinalThreads>(pl, sh_f64);
+  kl = block_sum_f64<kFinalThreads>(kl, sh_f64);
+  ct = block_sum_i64<kFinalThreads>(ct, sh_i64);
   if (tid == 0) {
-    const double loss = pl + double(beta) * kl;
-    scalars[0] = float(loss);
-    scalars[1] = float(pl);
-    scalars[2] = float(kl);
-    if (counts) {
-      counts[0] = hdr->num_tokens;
-      counts[1] = ct;
+    const double loss = pl + double(a.beta) * kl;
+    a.scalars[0] = float(loss);
+    a.scalars[1] = float(pl);
+    a.scalars[2] = float(kl);
+    if (a.counts) {
+      a.counts[0] = a.hdr->num_tokens;
+      a.counts[1] = ct;
     }
-    const uint32_t st = atomicOr(&hdr->status, 0u);
-    if (status) *status = st;
-    atomicAnd(&hdr->status, 0u);  // the workspace starts the next call clean
+    if (a.status) *a.status = a.hdr->status;
   }
+}
+
+hipError_t launch_final(const FinalArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(grpo_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 // Stage 1 over the per-token values the row kernel left in the workspace.
@@ -56,7 +61,6 @@ __global__ __launch_bounds__(kRedThreads) void grpo_reduce_kernel(ReduceArgs a) 
 #pragma clang fp contract(off)
   __shared__ double sh_f64[kRedThreads / kWave];
   __shared__ long long sh_i64[kRedThreads / kWave];
-  __shared__ int sh_flag;
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
@@ -77,9 +81,6 @@ __global__ __launch_bounds__(kRedThreads) void grpo_reduce_kernel(ReduceArgs a) 
     if (a.seq_policy) a.seq_policy[i] = float(p);
     if (a.seq_kl) a.seq_kl[i] = float(k);
   }
-  if (last_block(&a.hdr->ticket_final, unsigned(gridDim.x), &sh_flag))
-    final_scalars(a.B, a.beta, a.hdr, a.w, a.P, a.K, a.C, a.scalars, a.counts, a.status, sh_f64,
-                  sh_i64);
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
@@ -110,14 +111,12 @@ __device__ __forceinline__ TokTerms token_terms(float logp, float old, float ref
   return r;
 }
 
-// One block per sequence: tokens -> dlogp, per-sequence totals; the last
-// block forms the scalars.  The grpo.cpp README's token-loss kernels (CUDA
+// One block per sequence: tokens -> dlogp and the per-sequence totals.  The grpo.cpp README's token-loss kernels (CUDA
 // section) compute the same loss from per-token log-probs.
 __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma clang fp contract(off)
   __shared__ double sh_f64[kRedThreads / kWave];
   __shared__ long long sh_i64[kRedThreads / kWave];
-  __shared__ int sh_flag;
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
@@ -135,24 +134,43 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
                                        reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
   if (vec) {
+    // each thread takes QU quads of 4 tokens per round: their mask words
+    // first, then the log-prob loads of the active ones, then the arithmetic,
+    // so a round costs two memory round trips
+    constexpr int QU = 4;
     const int64_t n4 = a.T / 4;
-    for (int64_t q = tid; q < n4; q += kRedThreads) {
-      const int64_t t0 = base + 4 * q;
-      uint32_t m4 = 0x01010101u;
-      if (a.mask) m4 = *reinterpret_cast<const uint32_t*>(a.mask + t0);
-      f32x4 g = {0.f, 0.f, 0.f, 0.f};
-      float tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
-      if (m4 != 0) {
-        const f32x4 lp = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
-        const f32x4 od = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
-        f32x4 rf = {0.f, 0.f, 0.f, 0.f};
-        if (has_ref) rf = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
-        const float lpv[4] = {lp.x, lp.y, lp.z, lp.w}, odv[4] = {od.x, od.y, od.z, od.w},
-                    rfv[4] = {rf.x, rf.y, rf.z, rf.w};
-        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t q0 = tid; q0 < n4; q0 += QU * kRedThreads) {
+      uint32_t m4[QU];
+      f32x4 lp[QU], od[QU], rf[QU];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int64_t q = q0 + int64_t(u) * kRedThreads;
+        m4[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
+                                 : 0x01010101u)
+                       : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
+        lp[u] = od[u] = rf[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m4[u] != 0) {
+          lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
+          od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
+          if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int64_t q = q0 + int64_t(u) * kRedThreads;
+        if (q >= n4) continue;
+        const int64_t t0 = base + 4 * q;
+        const float lpv[4] = {lp[u].x, lp[u].y, lp[u].z, lp[u].w};
+        const float odv[4] = {od[u].x, od[u].y, od[u].z, od[u].w};
+        const float rfv[4] = {rf[u].x, rf[u].y, rf[u].z, rf[u].w};
+        float gv[4] = {0.f, 0.f, 0.f, 0.f}, tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if ((m4 >> (8 * j)) & 0xffu) {
+          if ((m4[u] >> (8 * j)) & 0xffu) {
             const TokTerms r = token_terms(lpv[j], odv[j], rfv[j], has_ref, adv, wg, a.lo, a.hi,
                                            a.beta);
             gv[j] = r.G;
@@ -164,11 +182,12 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
             nonfinite |= !(isfinite(r.loss) && isfinite(r.k3) && isfinite(r.G));
           }
         }
-        g = f32x4{gv[0], gv[1], gv[2], gv[3]};
+        if (a.dlogp)
+          __builtin_nontemporal_store(f32x4{gv[0], gv[1], gv[2], gv[3]},
+                                      reinterpret_cast<f32x4*>(a.dlogp + t0));
+        if (a.out_loss) *reinterpret_cast<f32x4*>(a.out_loss + t0) = f32x4{tl[0], tl[1], tl[2], tl[3]};
+        if (a.out_kl) *reinterpret_cast<f32x4*>(a.out_kl + t0) = f32x4{tk[0], tk[1], tk[2], tk[3]};
       }
-      if (a.dlogp) __builtin_nontemporal_store(g, reinterpret_cast<f32x4*>(a.dlogp + t0));
-      if (a.out_loss) *reinterpret_cast<f32x4*>(a.out_loss + t0) = f32x4{tl[0], tl[1], tl[2], tl[3]};
-      if (a.out_kl) *reinterpret_cast<f32x4*>(a.out_kl + t0) = f32x4{tk[0], tk[1], tk[2], tk[3]};
     }
   } else {
     for (int64_t t = tid; t < a.T; t += kRedThreads) {
@@ -201,9 +220,6 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     if (a.seq_policy) a.seq_policy[i] = float(p);
     if (a.seq_kl) a.seq_kl[i] = float(k);
   }
-  if (last_block(&a.hdr->ticket_final, unsigned(gridDim.x), &sh_flag))
-    final_scalars(a.B, a.beta, a.hdr, a.w, a.P, a.K, a.C, a.scalars, a.counts, a.status, sh_f64,
-                  sh_i64);
 }
 
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream) {

@@ -56,7 +56,25 @@ def workspace(B, T, num_groups, device, dedicated=False):
     return ws, ws.numel()
 
 
+_STRUCT_CACHE: dict = {}
+
+
 def _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps):
+    key = ("g", B, samples_per_prompt,
+           None if group_boundaries is None else tuple(int(v) for v in group_boundaries),
+           bool(leave_one_out), bool(scale_by_std), float(std_eps))
+    hit = _STRUCT_CACHE.get(key)
+    if hit is not None:
+        return hit
+    hit = _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                       std_eps)
+    if len(_STRUCT_CACHE) > 256:
+        _STRUCT_CACHE.clear()
+    _STRUCT_CACHE[key] = hit
+    return hit
+
+
+def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps):
     if (samples_per_prompt is None) == (group_boundaries is None):
         raise ValueError("give exactly one of samples_per_prompt / group_boundaries")
     g = GrpoGroups()
@@ -80,6 +98,15 @@ def _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std
 
 
 def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
+    key = ("c", clip_eps, eps_low, eps_high, beta, reduction, alpha)
+    hit = _STRUCT_CACHE.get(key)
+    if hit is None:
+        hit = _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+        _STRUCT_CACHE[key] = hit
+    return hit
+
+
+def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
     c = GrpoCfg()
     c.eps_low = float(clip_eps if eps_low is None else eps_low)
     c.eps_high = float(clip_eps if eps_high is None else eps_high)
@@ -107,6 +134,7 @@ class GRPOResult:
     tok_logp: torch.Tensor | None = None
     tok_loss: torch.Tensor | None = None
     tok_kl: torch.Tensor | None = None
+    _c_outputs: object = None   # the GrpoOutputs struct pointing at these tensors
 
     @property
     def loss(self):
@@ -147,7 +175,20 @@ def _outputs(B, T, device, per_token, want_logp):
     o.tok_logp = _ptr(res.tok_logp)
     o.tok_loss = _ptr(res.tok_loss)
     o.tok_kl = _ptr(res.tok_kl)
+    res._c_outputs = o
     return res, o
+
+
+def _reuse(out, B, T, device, per_token):
+    """Outputs of a previous call (same sizes and device) to be written again."""
+    if out is None:
+        return None
+    _need(isinstance(out, GRPOResult) and out._c_outputs is not None, "out must be a GRPOResult")
+    _need(out.advantages.shape[0] == B and out.scalars.device == device, "out has other sizes")
+    if per_token:
+        _need(out.tok_loss is not None and tuple(out.tok_loss.shape) == (B, T),
+              "out has no per-token buffers of this size")
+    return out
 
 
 def _need(cond, msg):
@@ -197,8 +238,9 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
                     clip_eps=0.2, eps_low=None, eps_high=None, beta=0.04,
                     samples_per_prompt=None, group_boundaries=None, leave_one_out=False,
                     scale_by_std=True, std_eps=1e-6, reduction="token_mean", alpha=None,
-                    want_grad=True, grad_scale=None, per_token=False):
-    """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp."""
+                    want_grad=True, grad_scale=None, per_token=False, out=None):
+    """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp.
+    ``out``: a previous result of the same sizes whose buffers are reused."""
     lib = load_library()
     dev = logp.device
     _need(logp.dim() == 2 and logp.is_cuda, "logp must be a [B, T] GPU tensor")
@@ -214,9 +256,15 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
     g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
                           std_eps)
     cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
-    res, o = _outputs(B, T, dev, per_token, want_logp=False)
-    if want_grad:
+    res = _reuse(out, B, T, dev, per_token)
+    if res is None:
+        res, o = _outputs(B, T, dev, per_token, want_logp=False)
+    else:
+        o = res._c_outputs
+    if want_grad and (res.grad is None or tuple(res.grad.shape) != (B, T)):
         res.grad = torch.empty((B, T), dtype=torch.float32, device=dev)
+    if not want_grad:
+        res.grad = None
     ws, wsb = workspace(B, T, ng, dev)
     check(lib.grpo_token_loss(logp.data_ptr(), old_logps.data_ptr(), _ptr(ref_logps), mptr,
                               rewards.contiguous().data_ptr(), B, T, C.byref(g), C.byref(cfg),
@@ -230,12 +278,13 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                       beta=0.04, samples_per_prompt=None, group_boundaries=None,
                       leave_one_out=False, scale_by_std=True, std_eps=1e-6,
                       reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
-                      grad_scale=None, per_token=False, _ws=None):
+                      grad_scale=None, per_token=False, out=None, _ws=None):
     """Fused forward + analytic backward from [B, T, V] logits.
 
     grad_out: None allocates a contiguous gradient (dtype ``grad_dtype``,
     default the logits dtype); a tensor writes into it (it may be
     ``policy_logits`` itself, in place); False runs the forward only.
+    out: a previous result of the same sizes whose output buffers are reused.
     """
     lib = load_library()
     dev = policy_logits.device
@@ -259,7 +308,11 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
                           std_eps)
     cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
-    res, o = _outputs(B, T, dev, per_token, want_logp=True)
+    res = _reuse(out, B, T, dev, per_token)
+    if res is None:
+        res, o = _outputs(B, T, dev, per_token, want_logp=True)
+    else:
+        o = res._c_outputs
     if grad_out is None:
         gdt = policy_logits.dtype if grad_dtype is None else grad_dtype
         _need(gdt in _FDTYPE, "grad_dtype must be float32 or bfloat16")
