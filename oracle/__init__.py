@@ -5,6 +5,8 @@ import this package; the HIP library never does.
 """
 
 from .grpo_oracle import (  # noqa: F401
+    KL_ESTIMATORS,
+    PG_LOSSES,
     REDUCTIONS,
     LossConfig,
     OracleInputError,
@@ -14,7 +16,9 @@ from .grpo_oracle import (  # noqa: F401
     grpo_advantages,
     grpo_loss_fwd_bwd,
     grpo_token_loss,
+    kl_terms,
     logits_rows,
+    policy_terms,
     row_logsumexp,
     sequence_weights,
     token_terms,

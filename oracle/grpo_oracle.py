@@ -44,10 +44,25 @@ repository design notes as well):
   flows (inclusive clamp, tie split of the minimum sums to the full gradient).
 * Masked slots are never read (boolean selection), so NaN/Inf or garbage ids
   stored there cannot reach any output.
+* Dual clip: for A < 0 the clipped objective is bounded below by c * A
+  (c > 1); below that bound the token carries no surrogate gradient.
+* CISPO: the clipped ratio multiplies -A logp as a constant (stop-gradient),
+  so the gradient is -A clip(rho) for every token, clipped or not.
+* SAPO: tau is chosen by the sign of A (tau_pos for A > 0, tau_neg
+  otherwise); f_tau(rho) = 4 sigmoid(tau (rho - 1)) / tau, so at rho = 1 the
+  gradient equals the unclipped surrogate's.
+* On-policy: the ratio is exp(logp - sg(logp)) = 1, so the value is -A and the
+  gradient -A (the clip band is inactive at rho = 1).
+* KL clamps clamp d = logp_ref - logp to [-v_in, v_in] before the estimator
+  and the estimator's value to [-v_out, v_out] after it; as with torch's
+  clamp, the gradient passes at an exact bound and is zero strictly outside.
+* Fixed-constant normaliser: every active token weighs 1 / C for a declared
+  C > 0, independent of the mask.
 
 Parity pins: every function here is pinned by CPU tests in
-``tests/test_oracle_pins.py`` (closed forms, library routines, finite
-differences, an independent autograd formulation, invariants).  The absolute
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_variants.py`` (closed
+forms, library routines, finite differences, an independent autograd
+formulation, invariants).  The absolute
 loss values of the synthetic workloads are not printed by the pages, so those
 are pinned only through the checks above.
 """
@@ -59,7 +74,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-REDUCTIONS = ("token_mean", "sequence_mean", "length_alpha")
+REDUCTIONS = ("token_mean", "sequence_mean", "length_alpha", "fixed_constant")
 
 
 class OracleInputError(ValueError):
@@ -136,7 +151,7 @@ def group_advantages(rewards, offsets, leave_one_out=False, scale_by_std=True,
 # [RPP] PPO and KL reduction; [GRPO-CPP] The length-normalization detail)
 # ---------------------------------------------------------------------------
 
-def sequence_weights(mask, reduction="token_mean", alpha=None):
+def sequence_weights(mask, reduction="token_mean", alpha=None, norm_constant=None):
     """Return (L [B] int64, N int, omega [B] float64).
 
     omega_i is the weight every active token of sequence i carries in the
@@ -144,6 +159,7 @@ def sequence_weights(mask, reduction="token_mean", alpha=None):
       token_mean     1 / max(N, 1)                 (global active-token mean)
       sequence_mean  1 / (B * max(L_i, 1))          (mean within, then over B)
       length_alpha   L_i**alpha / (B * L_i), 0 if L_i = 0
+      fixed_constant 1 / norm_constant            (a declared denominator)
     """
     m = np.asarray(mask).astype(bool)
     if m.ndim != 2:
@@ -168,6 +184,10 @@ def sequence_weights(mask, reduction="token_mean", alpha=None):
         else:
             num = np.power(Lf, float(alpha))
         w = np.where(L > 0, num / (float(B) * np.maximum(Lf, 1.0)), 0.0)
+    elif reduction == "fixed_constant":
+        if norm_constant is None or not norm_constant > 0:
+            raise OracleInputError("fixed_constant needs norm_constant > 0")
+        w = np.full(B, 1.0 / float(norm_constant), dtype=np.float64)
     else:
         raise OracleInputError(f"unknown reduction {reduction!r}")
     return L, N, w
@@ -178,44 +198,140 @@ def sequence_weights(mask, reduction="token_mean", alpha=None):
 # [DOCKYARD] One loss many algorithms, Reference-KL penalty)
 # ---------------------------------------------------------------------------
 
+PG_LOSSES = ("clip", "cispo", "sapo", "reinforce", "on_policy")
+KL_ESTIMATORS = ("k3", "k1", "k2")
+
+
 @dataclass
 class LossConfig:
-    """Objective settings.  A symmetric clip sets eps_low = eps_high."""
+    """Objective settings.  A symmetric clip sets eps_low = eps_high.
+
+    pg_loss ([DOCKYARD] One loss many algorithms, CISPO; [RPP] Formula-level
+    comparison for SAPO):
+      clip       -min(rho A, clip(rho) A), optionally dual-clipped for A < 0
+      cispo      -A sg(clip(rho)) logp       (the clipped ratio is a constant weight)
+      sapo       -f_tau(rho) A, f_tau(rho) = 4 sigmoid(tau (rho - 1)) / tau,
+                 tau = sapo_tau_pos for A > 0, sapo_tau_neg otherwise
+      reinforce  -A logp                     (the ratio dropped)
+      on_policy  the clip loss with the ratio pinned to 1 by a stop-gradient:
+                 value -A, gradient -A
+    kl_estimator ([DOCKYARD] Reference-KL penalty), with d = logp_ref - logp:
+      k3 = e^d - d - 1,  k1 = -d = logp - logp_ref,  k2 = d^2 / 2
+    kl_input_clamp / kl_output_clamp clamp d and the estimator to [-v, v].
+    reduction "fixed_constant" weights every token by 1 / norm_constant
+    ([GRPO-LOSS] Normalizer semantics).
+    """
     eps_low: float = 0.2
     eps_high: float = 0.2
     beta: float = 0.04
     reduction: str = "token_mean"
     alpha: float | None = None
+    pg_loss: str = "clip"
+    kl_estimator: str = "k3"
+    dual_clip_c: float | None = None
+    sapo_tau_pos: float = 1.0
+    sapo_tau_neg: float = 1.0
+    kl_input_clamp: float | None = None
+    kl_output_clamp: float | None = None
+    norm_constant: float | None = None
+
+
+def policy_terms(logp, old_logp, adv, cfg: LossConfig):
+    """Per-token policy loss l, its derivative dl/dlogp and the clip flag.
+
+    A flag marks a token whose surrogate gradient is cut by clipping (clip
+    loss, including the dual clip) or, for CISPO, whose ratio lies outside
+    the band (its weight is clipped).  At an exact bound the gradient flows:
+    torch's clamp passes the gradient there and a tie of the minimum splits it
+    in halves that sum to the full value.
+    """
+    logp = np.asarray(logp, dtype=np.float64)
+    A = np.asarray(adv, dtype=np.float64)
+    rho = np.exp(logp - np.asarray(old_logp, dtype=np.float64))
+    lo = 1.0 - cfg.eps_low
+    hi = 1.0 + cfg.eps_high
+    if cfg.pg_loss == "clip":
+        obj = np.minimum(rho * A, np.clip(rho, lo, hi) * A)
+        clipped = ((A > 0) & (rho > hi)) | ((A < 0) & (rho < lo))
+        dobj = np.where(clipped, 0.0, A * rho)
+        if cfg.dual_clip_c is not None:
+            # negative-advantage objective bounded below by c * A
+            dual = (A < 0) & (obj < cfg.dual_clip_c * A)
+            obj = np.where(dual, cfg.dual_clip_c * A, obj)
+            dobj = np.where(dual, 0.0, dobj)
+            clipped = clipped | dual
+        loss, dloss = -obj, -dobj
+    elif cfg.pg_loss == "cispo":
+        wgt = np.clip(rho, lo, hi)
+        loss = -A * wgt * logp
+        dloss = -A * wgt
+        clipped = (rho < lo) | (rho > hi)
+    elif cfg.pg_loss == "sapo":
+        tau = np.where(A > 0, cfg.sapo_tau_pos, cfg.sapo_tau_neg)
+        sig = 1.0 / (1.0 + np.exp(-tau * (rho - 1.0)))
+        loss = -(4.0 * sig / tau) * A
+        dloss = -A * 4.0 * sig * (1.0 - sig) * rho
+        clipped = np.zeros(np.shape(loss), dtype=bool)
+    elif cfg.pg_loss == "reinforce":
+        loss = -A * logp
+        dloss = -A * np.ones_like(logp)
+        clipped = np.zeros(np.shape(loss), dtype=bool)
+    elif cfg.pg_loss == "on_policy":
+        loss = -A * np.ones_like(logp)
+        dloss = -A * np.ones_like(logp)
+        clipped = np.zeros(np.shape(loss), dtype=bool)
+    else:
+        raise OracleInputError(f"unknown pg_loss {cfg.pg_loss!r}")
+    return rho, loss, dloss, clipped
+
+
+def kl_terms(d, cfg: LossConfig):
+    """Per-token KL estimator value and its derivative with respect to logp
+    (d = logp_ref - logp, so dd/dlogp = -1)."""
+    d = np.asarray(d, dtype=np.float64)
+    if cfg.kl_input_clamp is not None:
+        v = cfg.kl_input_clamp
+        pass_in = np.abs(d) <= v
+        dc = np.clip(d, -v, v)
+    else:
+        pass_in = np.ones(d.shape, dtype=bool)
+        dc = d
+    if cfg.kl_estimator == "k3":
+        val = np.expm1(dc) - dc
+        dval_dd = np.expm1(dc)
+    elif cfg.kl_estimator == "k1":
+        val = -dc
+        dval_dd = -np.ones_like(dc)
+    elif cfg.kl_estimator == "k2":
+        val = 0.5 * dc * dc
+        dval_dd = dc
+    else:
+        raise OracleInputError(f"unknown kl_estimator {cfg.kl_estimator!r}")
+    if cfg.kl_output_clamp is not None:
+        w = cfg.kl_output_clamp
+        pass_out = np.abs(val) <= w
+        val = np.clip(val, -w, w)
+    else:
+        pass_out = np.ones(d.shape, dtype=bool)
+    dkl = np.where(pass_in & pass_out, -dval_dd, 0.0)
+    return val, dkl
 
 
 def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig):
     """Per-token quantities, all float64 arrays of the broadcast shape.
 
-    rho   = exp(logp - old_logp)                          importance ratio
-    d     = logp_ref - logp,  k3 = exp(d) - d - 1         reference KL (k3)
-    loss  = -min(rho * A, clip(rho, 1 - eps_low, 1 + eps_high) * A)
-    clipped = (A > 0 and rho > 1 + eps_high) or (A < 0 and rho < 1 - eps_low)
-    dloss = d loss / d logp = -A * rho unless clipped, else 0
-    dkl   = d k3 / d logp   = 1 - exp(d)
+    rho, loss, dloss, clipped from policy_terms; d = logp_ref - logp (0
+    without a reference), kl and dkl = d kl / d logp from kl_terms.  With the
+    default settings: loss = -min(rho A, clip(rho) A), kl = k3 = e^d - d - 1.
     """
     logp = np.asarray(logp, dtype=np.float64)
-    old = np.asarray(old_logp, dtype=np.float64)
-    A = np.asarray(adv, dtype=np.float64)
-    rho = np.exp(logp - old)
+    rho, loss, dloss, clipped = policy_terms(logp, old_logp, adv, cfg)
     if logp_ref is None:
         d = np.zeros_like(logp)
     else:
         d = np.asarray(logp_ref, dtype=np.float64) - logp
-    k3 = np.expm1(d) - d
-    lo = 1.0 - cfg.eps_low
-    hi = 1.0 + cfg.eps_high
-    unclipped_obj = rho * A
-    clipped_obj = np.clip(rho, lo, hi) * A
-    loss = -np.minimum(unclipped_obj, clipped_obj)
-    clipped = ((A > 0) & (rho > hi)) | ((A < 0) & (rho < lo))
-    dloss = np.where(clipped, 0.0, -A * rho)
-    dkl = -np.expm1(d)
-    return dict(rho=rho, d=d, k3=k3, loss=loss, clipped=clipped, dloss=dloss, dkl=dkl)
+    kl, dkl = kl_terms(d, cfg)
+    return dict(rho=rho, d=d, kl=kl, loss=loss, clipped=clipped, dloss=dloss, dkl=dkl)
 
 
 def _check_cfg(cfg: LossConfig, have_ref: bool):
@@ -225,6 +341,17 @@ def _check_cfg(cfg: LossConfig, have_ref: bool):
         raise OracleInputError("beta > 0 needs reference log-probs")
     if cfg.reduction not in REDUCTIONS:
         raise OracleInputError("unknown reduction")
+    if cfg.reduction == "fixed_constant" and not (cfg.norm_constant and cfg.norm_constant > 0):
+        raise OracleInputError("fixed_constant needs norm_constant > 0")
+    if cfg.pg_loss not in PG_LOSSES or cfg.kl_estimator not in KL_ESTIMATORS:
+        raise OracleInputError("unknown pg_loss or kl_estimator")
+    if cfg.dual_clip_c is not None and (cfg.pg_loss != "clip" or not cfg.dual_clip_c > 1.0):
+        raise OracleInputError("dual clip needs the clip loss and c > 1")
+    if cfg.pg_loss == "sapo" and not (cfg.sapo_tau_pos > 0 and cfg.sapo_tau_neg > 0):
+        raise OracleInputError("SAPO temperatures must be positive")
+    for v in (cfg.kl_input_clamp, cfg.kl_output_clamp):
+        if v is not None and not v > 0:
+            raise OracleInputError("KL clamps must be positive")
 
 
 @dataclass
@@ -234,7 +361,7 @@ class OracleResult:
     kl: float
     advantages: np.ndarray          # [B] float64
     seq_policy: np.ndarray          # [B] sum over active tokens of the token loss
-    seq_kl: np.ndarray              # [B] sum over active tokens of k3
+    seq_kl: np.ndarray              # [B] sum over active tokens of the KL estimator
     seq_weight: np.ndarray          # [B] omega_i
     seq_tokens: np.ndarray          # [B] L_i
     num_tokens: int                 # N
@@ -272,7 +399,7 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
     A = group_advantages(rewards, off, groups.get("leave_one_out", False),
                          groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
-    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha)
+    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha, cfg.norm_constant)
 
     ii, tt = np.nonzero(m)                      # boolean selection: masked slots never read
     lp = np.asarray(logp, dtype=np.float64)[ii, tt]
@@ -293,12 +420,12 @@ def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_activ
     for i in range(B):
         s, e = int(bounds[i]), int(bounds[i + 1])
         P[i] = math.fsum(terms["loss"][s:e])
-        K[i] = math.fsum(terms["k3"][s:e])
+        K[i] = math.fsum(terms["kl"][s:e])
         C[i] = int(np.count_nonzero(terms["clipped"][s:e]))
     loss, policy_loss, kl = _reduce(P, K, w, cfg.beta)
     G = w[ii] * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
     tok = {}
-    for name in ("rho", "d", "k3", "loss", "dloss", "dkl"):
+    for name in ("rho", "d", "kl", "loss", "dloss", "dkl"):
         full = np.zeros((B, T))
         full[ii, tt] = terms[name]
         tok[name] = full
@@ -381,12 +508,12 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
     A = group_advantages(rewards, off, groups.get("leave_one_out", False),
                          groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
-    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha)
+    L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha, cfg.norm_constant)
     ii, tt = np.nonzero(m)
     ids = np.asarray(action_ids)[ii, tt].astype(np.int64)
     old = np.asarray(old_logps, dtype=np.float64)[ii, tt]
     grad = np.zeros((B, T, V)) if want_grad else None
-    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "k3", "loss", "dloss", "dkl", "logp")}
+    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "kl", "loss", "dloss", "dkl", "logp")}
     acc["clipped"] = np.zeros(len(ii), dtype=bool)
     for s in range(0, len(ii), row_chunk):
         sl = slice(s, s + row_chunk)

@@ -116,7 +116,7 @@ def compare_scalars(res, ref, loss_rtol, what=""):
     assert rel <= loss_rtol, f"{what} loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} kappa={kappa:.3g}"
     # policy_loss and kl: relative to the weighted absolute sums they are made of
     scale_p = float(np.sum(ref.seq_weight * np.abs(ref.tok["loss"]).sum(axis=1))) + 1e-30
-    scale_k = float(np.sum(ref.seq_weight * np.abs(ref.tok["k3"]).sum(axis=1))) + 1e-30
+    scale_k = float(np.sum(ref.seq_weight * np.abs(ref.tok["kl"]).sum(axis=1))) + 1e-30
     assert abs(float(res.policy_loss) - ref.policy_loss) <= loss_rtol * scale_p, what
     assert abs(float(res.kl) - ref.kl) <= loss_rtol * scale_k, what
     # per-sequence totals: the relative bound plus the float32 log-prob error
@@ -127,7 +127,7 @@ def compare_scalars(res, ref, loss_rtol, what=""):
     prop_p = (np.abs(A) * ref.tok["rho"] * (ref.tok["dloss"] != 0)).sum(axis=1) * LOGP_ABS_ERR
     prop_k = (np.abs(np.expm1(ref.tok["d"]))).sum(axis=1) * 2 * LOGP_ABS_ERR
     tp = loss_rtol * np.abs(ref.tok["loss"]).sum(axis=1) + prop_p + 1e-30
-    tk = loss_rtol * np.abs(ref.tok["k3"]).sum(axis=1) + prop_k + 1e-30
+    tk = loss_rtol * np.abs(ref.tok["kl"]).sum(axis=1) + prop_k + 1e-30
     ep = np.abs(sp - ref.seq_policy)
     ek = np.abs(sk - ref.seq_kl)
     assert np.all(ep <= tp), f"{what} seq_policy worst {np.max(ep / tp):.3g}x of bound"

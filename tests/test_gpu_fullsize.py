@@ -118,7 +118,7 @@ def test_fullsize_logits(gpu_lib, name, reduction):
             continue
         # token loss / k3 within the propagated float32 log-prob error
         assert abs(tl.reshape(-1)[r] - o["loss"][0]) <= 2 * LOGP_ABS_ERR * abs(A[i]) * rho + 1e-6
-        assert abs(tk.reshape(-1)[r] - o["k3"][0]) <= 2 * LOGP_ABS_ERR * abs(np.expm1(o["d"][0])) + 1e-7
+        assert abs(tk.reshape(-1)[r] - o["kl"][0]) <= 2 * LOGP_ABS_ERR * abs(np.expm1(o["d"][0])) + 1e-7
         # gradient row, bf16 criterion (with the ill-conditioned-G allowance)
         G = o["G"][0]
         dG = abs(w[i]) * (abs(A[i]) * rho + 2 * cfg.beta * np.exp(o["d"][0])) * 2 * LOGP_ABS_ERR

@@ -91,18 +91,18 @@ def test_k3_expectation_is_kl_divergence():
         terms = orc.token_terms(logp, np.zeros(V), logq, np.zeros(V), LossConfig())
         p = np.exp(logp)
         expect = np.sum(scipy.special.rel_entr(p, np.exp(logq)))
-        assert abs(np.sum(p * terms["k3"]) - expect) < 1e-12
+        assert abs(np.sum(p * terms["kl"]) - expect) < 1e-12
         # the opposite direction must NOT match (the test would catch a swapped d)
         wrong = np.sum(scipy.special.rel_entr(np.exp(logq), p))
-        assert abs(np.sum(p * terms["k3"]) - wrong) > 1e-6
+        assert abs(np.sum(p * terms["kl"]) - wrong) > 1e-6
 
 
 def test_k3_nonnegative_and_zero_at_zero():
     d = np.linspace(-5, 5, 101)
     t = orc.token_terms(np.zeros_like(d), np.zeros_like(d), d, np.zeros_like(d), LossConfig())
-    assert np.all(t["k3"] >= 0)
+    assert np.all(t["kl"] >= 0)
     t0 = orc.token_terms(np.array([0.3]), np.array([0.0]), np.array([0.3]), np.array([1.0]), LossConfig())
-    assert t0["k3"][0] == 0.0 and t0["dkl"][0] == 0.0
+    assert t0["kl"][0] == 0.0 and t0["dkl"][0] == 0.0
 
 
 # ---------------------------------------------------------------------------
@@ -514,7 +514,7 @@ def _torch_objective(x, y, ids, old, mask, r, offsets, cfg, loo, scale_std, std_
     klv = (w[:, None] * torch.where(mt, kl, zero)).sum()
     total = pol + cfg.beta * klv
     total.backward()
-    return float(total), float(pol), float(klv), xt.grad.numpy()
+    return total.item(), pol.item(), klv.item(), xt.grad.numpy()
 
 
 @pytest.mark.parametrize("seed", range(6))
