@@ -19,10 +19,13 @@
  *                and mask contract, PPO and KL reduction.
  *   [GRPO-CPP]   grpo.cpp README: The length-normalization detail, CUDA.
  *   [DOCKYARD]   dockyard_rl, "GRPO and the clipped policy-gradient loss":
- *                Advantage estimation, One loss many algorithms,
+ *                Advantage estimation, One loss many algorithms, CISPO,
  *                Reference-KL penalty.
+ *   [RPP-F]      Relax docs, "REINFORCE++ and REINFORCE++-baseline":
+ *                Formula-level comparison (SAPO's soft gate).
  *
- * Objective (per active token (i, t) of sequence i, action a = action_ids[i,t]):
+ * Objective (per active token (i, t) of sequence i, action a = action_ids[i,t]),
+ * in the default settings (GRPO_PG_CLIP, GRPO_KL_K3, no clamps):
  *   logp     = log softmax(policy_logits[i,t,:])[a]
  *   logp_ref = log softmax(ref_logits[i,t,:])[a]
  *   rho      = exp(logp - old_logps[i,t])
@@ -36,7 +39,9 @@
  *   G_it = w_i * grad_scale * ( (clipped ? 0 : -A_i * rho) + beta * (1 - exp(d)) )
  * A token is clipped when rho lies strictly outside [1 - eps_low, 1 + eps_high]
  * on the side that the sign of A_i selects; at the exact bound the gradient
- * flows.
+ * flows.  In general G_it = w_i * grad_scale * (dl/dlogp + beta * dkl/dlogp)
+ * for the policy loss and KL estimator that grpo_cfg selects (grpo_pg_loss,
+ * grpo_kl_estimator); "kl" then stands for the selected estimator.
  *
  * Masks: a nonzero byte marks an active slot ([GRPO-LOSS] Tensor Contract;
  * torch.bool and uint8 both work).  Selection is boolean ([RPP] Notation and
@@ -69,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 1
+#define GRPO_ABI_VERSION 2
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -81,7 +86,7 @@ typedef enum grpo_status {
   GRPO_ERR_SHAPE = 2,      /* B, T or V not positive, a row stride < V, or sizes overflow */
   GRPO_ERR_DTYPE = 3,      /* unknown dtype code */
   GRPO_ERR_GROUPS = 4,     /* group specification invalid ([GRPO-LOSS] Group specification) */
-  GRPO_ERR_CONFIG = 5,     /* eps/beta/reduction/alpha invalid, or beta > 0 without a reference */
+  GRPO_ERR_CONFIG = 5,     /* a grpo_cfg field invalid, or beta > 0 without a reference */
   GRPO_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or smaller than grpo_workspace_bytes() */
   GRPO_ERR_ALIAS = 7,      /* grad_out overlaps policy_logits without being exactly in place */
   GRPO_ERR_HIP = 8         /* a HIP runtime call or kernel launch failed */
@@ -99,13 +104,49 @@ typedef enum grpo_idtype { GRPO_I64 = 0, GRPO_I32 = 1 } grpo_idtype;
  *   GRPO_TOKEN_MEAN     w_i = 1 / max(N, 1)              (global token mean)
  *   GRPO_SEQUENCE_MEAN  w_i = 1 / (B * max(L_i, 1))      (mean in sequence, then over B)
  *   GRPO_LENGTH_ALPHA   w_i = L_i^alpha / (B * L_i), 0 when L_i = 0
+ *   GRPO_FIXED_CONSTANT w_i = 1 / norm_constant          (a declared denominator)
  * The weights are computed in binary64 and are bit-exact for alpha in
  * {0, 0.5, 1}; other alpha use pow() and may differ in the last bit. */
 typedef enum grpo_reduction {
   GRPO_TOKEN_MEAN = 0,
   GRPO_SEQUENCE_MEAN = 1,
-  GRPO_LENGTH_ALPHA = 2
+  GRPO_LENGTH_ALPHA = 2,
+  GRPO_FIXED_CONSTANT = 3
 } grpo_reduction;
+
+/* Per-token policy loss l(logp) and its derivative, rho = exp(logp - old),
+ * clip(.) = clip(., 1 - eps_low, 1 + eps_high) ([DOCKYARD] One loss many
+ * algorithms, CISPO; [RPP-F] Formula-level comparison):
+ *   GRPO_PG_CLIP       l = -min(rho A, clip(rho) A); with dual_clip_c = c > 1
+ *                      and A < 0 the objective is bounded below by c A, and
+ *                      below that bound the token has no surrogate gradient
+ *   GRPO_PG_CISPO      l = -A sg(clip(rho)) logp: dl/dlogp = -A clip(rho)
+ *                      (the clipped ratio is a constant weight)
+ *   GRPO_PG_SAPO       l = -A f(rho), f(rho) = 4 sigmoid(tau (rho - 1)) / tau,
+ *                      tau = sapo_tau_pos if A > 0 else sapo_tau_neg:
+ *                      dl/dlogp = -4 A s (1 - s) rho with s the sigmoid
+ *   GRPO_PG_REINFORCE  l = -A logp: dl/dlogp = -A
+ *   GRPO_PG_ON_POLICY  ratio pinned to 1 by a stop-gradient: l = -A,
+ *                      dl/dlogp = -A
+ * The clip count (outputs->counts[1]) counts clipped tokens for CLIP (dual
+ * clip included) and tokens whose ratio lies outside the band for CISPO. */
+typedef enum grpo_pg_loss {
+  GRPO_PG_CLIP = 0,
+  GRPO_PG_CISPO = 1,
+  GRPO_PG_SAPO = 2,
+  GRPO_PG_REINFORCE = 3,
+  GRPO_PG_ON_POLICY = 4
+} grpo_pg_loss;
+
+/* Reference-KL estimator of d = logp_ref - logp ([DOCKYARD] Reference-KL
+ * penalty), after the optional input clamp d -> clip(d, -kl_input_clamp,
+ * kl_input_clamp) and followed by the optional output clamp of its value to
+ * [-kl_output_clamp, kl_output_clamp].  A clamp passes the gradient at its
+ * exact bound and cuts it strictly outside.
+ *   GRPO_KL_K3  exp(d) - d - 1     dkl/dlogp = 1 - exp(d)
+ *   GRPO_KL_K1  -d                 dkl/dlogp = 1
+ *   GRPO_KL_K2  d^2 / 2            dkl/dlogp = -d */
+typedef enum grpo_kl_estimator { GRPO_KL_K3 = 0, GRPO_KL_K1 = 1, GRPO_KL_K2 = 2 } grpo_kl_estimator;
 
 /* Device-detected data faults, OR-ed into outputs->status (which each call
  * overwrites). */
@@ -134,13 +175,23 @@ typedef struct grpo_groups {
   double std_eps;                   /* floor of the std, > 0 (usually 1e-6) */
 } grpo_groups;
 
-/* Objective settings.  A symmetric clip sets eps_low == eps_high. */
+/* Objective settings.  A symmetric clip sets eps_low == eps_high.  Zero in
+ * pg_loss .. norm_constant selects the clipped surrogate with the k3
+ * estimator, no dual clip and no KL clamps. */
 typedef struct grpo_cfg {
-  double eps_low;     /* in [0, 1) */
-  double eps_high;    /* >= 0 */
-  double beta;        /* reference-KL coefficient, >= 0 */
-  int32_t reduction;  /* grpo_reduction */
-  double alpha;       /* in [0, 1]; used by GRPO_LENGTH_ALPHA only */
+  double eps_low;          /* in [0, 1) */
+  double eps_high;         /* >= 0 */
+  double beta;             /* reference-KL coefficient, >= 0 */
+  int32_t reduction;       /* grpo_reduction */
+  double alpha;            /* in [0, 1]; used by GRPO_LENGTH_ALPHA only */
+  int32_t pg_loss;         /* grpo_pg_loss (0: the clipped surrogate) */
+  int32_t kl_estimator;    /* grpo_kl_estimator (0: k3) */
+  double dual_clip_c;      /* 0: off; else > 1, GRPO_PG_CLIP only */
+  double sapo_tau_pos;     /* > 0, read by GRPO_PG_SAPO only */
+  double sapo_tau_neg;     /* > 0, read by GRPO_PG_SAPO only */
+  double kl_input_clamp;   /* 0: off; else > 0 and finite */
+  double kl_output_clamp;  /* 0: off; else > 0 and finite */
+  double norm_constant;    /* > 0 and finite, read by GRPO_FIXED_CONSTANT only */
 } grpo_cfg;
 
 /* Outputs (DEVICE pointers).  Only `scalars` is required; any other field may
@@ -150,14 +201,14 @@ typedef struct grpo_outputs {
   float *scalars;      /* [3] loss, policy_loss, kl (float32) */
   float *advantages;   /* [B] A_i */
   float *seq_policy;   /* [B] sum over the sequence's active tokens of l */
-  float *seq_kl;       /* [B] sum over the sequence's active tokens of k3 */
+  float *seq_kl;       /* [B] sum over the sequence's active tokens of the KL estimator */
   float *seq_weight;   /* [B] w_i */
   int32_t *seq_tokens; /* [B] L_i */
   int64_t *counts;     /* [2] N (active tokens), number of clipped active tokens */
   uint32_t *status;    /* [1] GRPO_FAULT_* bits of this call */
   float *tok_logp;     /* [B*T] logp of the taken token (logits entry points only) */
   float *tok_loss;     /* [B*T] token loss l */
-  float *tok_kl;       /* [B*T] k3 */
+  float *tok_kl;       /* [B*T] KL estimator */
 } grpo_outputs;
 
 /* ABI version of the loaded library (GRPO_ABI_VERSION it was built with). */

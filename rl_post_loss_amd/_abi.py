@@ -8,13 +8,15 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 1
+GRPO_ABI_VERSION = 2
 
 GRPO_F32, GRPO_BF16 = 0, 1
 GRPO_I64, GRPO_I32 = 0, 1
-GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA = 0, 1, 2
+GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA, GRPO_FIXED_CONSTANT = 0, 1, 2, 3
 REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE_MEAN,
-                   "length_alpha": GRPO_LENGTH_ALPHA}
+                   "length_alpha": GRPO_LENGTH_ALPHA, "fixed_constant": GRPO_FIXED_CONSTANT}
+PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 4}
+KL_ESTIMATOR_CODES = {"k3": 0, "k1": 1, "k2": 2}
 
 GRPO_FAULT_BAD_ACTION = 1
 GRPO_FAULT_NO_TOKENS = 2
@@ -37,7 +39,9 @@ class GrpoGroups(C.Structure):
 
 class GrpoCfg(C.Structure):
     _fields_ = [("eps_low", f64), ("eps_high", f64), ("beta", f64), ("reduction", i32),
-                ("alpha", f64)]
+                ("alpha", f64), ("pg_loss", i32), ("kl_estimator", i32), ("dual_clip_c", f64),
+                ("sapo_tau_pos", f64), ("sapo_tau_neg", f64), ("kl_input_clamp", f64),
+                ("kl_output_clamp", f64), ("norm_constant", f64)]
 
 
 class GrpoOutputs(C.Structure):

@@ -66,10 +66,44 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref) {
   if (!(c->eps_high >= 0.0) || !isfinite(c->eps_high)) return GRPO_ERR_CONFIG;
   if (!(c->beta >= 0.0) || !isfinite(c->beta)) return GRPO_ERR_CONFIG;
   if (c->beta > 0.0 && !has_ref) return GRPO_ERR_CONFIG;
-  if (c->reduction < GRPO_TOKEN_MEAN || c->reduction > GRPO_LENGTH_ALPHA) return GRPO_ERR_CONFIG;
+  if (c->reduction < GRPO_TOKEN_MEAN || c->reduction > GRPO_FIXED_CONSTANT) return GRPO_ERR_CONFIG;
   if (c->reduction == GRPO_LENGTH_ALPHA && !(c->alpha >= 0.0 && c->alpha <= 1.0))
     return GRPO_ERR_CONFIG;
+  if (c->reduction == GRPO_FIXED_CONSTANT && !(c->norm_constant > 0.0 && isfinite(c->norm_constant)))
+    return GRPO_ERR_CONFIG;
+  if (c->pg_loss < GRPO_PG_CLIP || c->pg_loss > GRPO_PG_ON_POLICY) return GRPO_ERR_CONFIG;
+  if (c->kl_estimator < GRPO_KL_K3 || c->kl_estimator > GRPO_KL_K2) return GRPO_ERR_CONFIG;
+  // dual clip: 0 (off) or a finite c > 1, with the clipped surrogate only
+  if (c->dual_clip_c != 0.0 &&
+      !(c->pg_loss == GRPO_PG_CLIP && c->dual_clip_c > 1.0 && isfinite(c->dual_clip_c)))
+    return GRPO_ERR_CONFIG;
+  if (c->pg_loss == GRPO_PG_SAPO &&
+      !(c->sapo_tau_pos > 0.0 && isfinite(c->sapo_tau_pos) && c->sapo_tau_neg > 0.0 &&
+        isfinite(c->sapo_tau_neg)))
+    return GRPO_ERR_CONFIG;
+  for (double v : {c->kl_input_clamp, c->kl_output_clamp})
+    if (v != 0.0 && !(v > 0.0 && isfinite(v))) return GRPO_ERR_CONFIG;
   return GRPO_OK;
+}
+
+// Objective parameters for the kernels (float32, as they compute).
+Objective make_objective(const grpo_cfg* c) {
+  Objective o{};
+  o.lo = float(1.0 - c->eps_low);
+  o.hi = float(1.0 + c->eps_high);
+  o.beta = float(c->beta);
+  o.pg = c->pg_loss;
+  o.kl = c->kl_estimator;
+  o.dual_c = float(c->dual_clip_c);
+  o.tau_pos = float(c->sapo_tau_pos);
+  o.tau_neg = float(c->sapo_tau_neg);
+  o.kl_in = float(c->kl_input_clamp);
+  o.kl_out = float(c->kl_output_clamp);
+  o.general = (o.pg != GRPO_PG_CLIP || o.kl != GRPO_KL_K3 || c->dual_clip_c != 0.0 ||
+               c->kl_input_clamp != 0.0 || c->kl_output_clamp != 0.0)
+                  ? 1
+                  : 0;
+  return o;
 }
 
 struct Ws {
@@ -115,6 +149,7 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
   a.std_eps = g->std_eps;
   a.reduction = cfg ? cfg->reduction : GRPO_TOKEN_MEAN;
   a.alpha = cfg ? cfg->alpha : 0.0;
+  a.norm_constant = cfg ? cfg->norm_constant : 0.0;
   a.want_weights = want_weights ? 1 : 0;
   a.hdr = w.hdr();
   a.L = w.at<int32_t>(w.l.L);
@@ -130,7 +165,7 @@ grpo_status run_final(const Ws& w, int64_t B, double beta, const grpo_outputs* o
                       hipStream_t s) {
   FinalArgs f{};
   f.B = B;
-  f.beta = float(beta);
+  f.beta = beta;
   f.hdr = w.hdr();
   f.w = w.at<double>(w.l.w);
   f.P = w.at<double>(w.l.P);
@@ -243,9 +278,7 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.mask = mask;
   a.B = B;
   a.T = T;
-  a.lo = float(1.0 - cfg->eps_low);
-  a.hi = float(1.0 + cfg->eps_high);
-  a.beta = float(cfg->beta);
+  a.obj = make_objective(cfg);
   a.grad_scale = grad_scale;
   a.dlogp = dlogp_out;
   a.hdr = w.hdr();
@@ -346,9 +379,7 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.T = T;
   a.V = V;
   a.rows = rows;
-  a.lo = float(1.0 - cfg->eps_low);
-  a.hi = float(1.0 + cfg->eps_high);
-  a.beta = float(cfg->beta);
+  a.obj = make_objective(cfg);
   a.grad_scale = grad_scale;
   a.g = grad_out;
   a.ldg = grad_out ? grad_row_stride : 0;
@@ -369,8 +400,6 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   l.nt = choose_nt(V, fdtype_size(logits_dtype));
   l.vec = rows_vectorizable(policy_logits, ref_logits, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);
-  // rows above 4 KB that fit in one block's registers keep the policy row
-  // resident between the two passes (fused mode only)
   // rows above 4 KB that fit one block's registers keep the policy row
   // resident between the passes (fused mode); longer rows stream
   l.resident = GRPO_RESIDENT && grad_out && l.vec && V * fdtype_size(logits_dtype) > 4096 &&
@@ -383,7 +412,6 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   ReduceArgs r{};
   r.B = B;
   r.T = T;
-  r.beta = float(cfg->beta);
   r.hdr = w.hdr();
   r.tok_loss = a.tok_loss;
   r.tok_kl = a.tok_kl;

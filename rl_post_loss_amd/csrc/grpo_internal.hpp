@@ -52,6 +52,20 @@ inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
   return l;
 }
 
+// Per-token objective parameters, in the precision the kernels compute in.
+// `general` is 0 exactly for the clipped surrogate with k3, no dual clip and
+// no KL clamps, which takes a shorter code path.
+struct Objective {
+  float lo, hi;       // clip band [1 - eps_low, 1 + eps_high]
+  float beta;         // KL coefficient
+  int32_t pg;         // grpo_pg_loss
+  int32_t kl;         // grpo_kl_estimator
+  int32_t general;
+  float dual_c;       // dual-clip bound; 0: off
+  float tau_pos, tau_neg;
+  float kl_in, kl_out;  // clamps; +inf: off
+};
+
 // Group / advantage / weight preparation.
 struct PrepArgs {
   const uint8_t* mask;      // [B, T] or null (all active)
@@ -64,6 +78,7 @@ struct PrepArgs {
   double std_eps;
   int32_t reduction;
   double alpha;
+  double norm_constant;     // GRPO_FIXED_CONSTANT
   int32_t want_weights;     // 0: advantages only
   // workspace
   WsHeader* hdr;
@@ -86,7 +101,7 @@ struct RowArgs {
   const float* old;
   const uint8_t* mask;
   int64_t T, V, rows;
-  float lo, hi, beta;       // clip band [lo, hi] and KL coefficient
+  Objective obj;
   const float* grad_scale;  // null = 1
   void* g;                  // gradient out (null in forward-only mode)
   int64_t ldg;
@@ -117,7 +132,6 @@ struct RowLaunch {
 // Per-sequence reduction (stage 1).
 struct ReduceArgs {
   int64_t B, T;
-  float beta;
   WsHeader* hdr;
   const float* tok_loss;
   const float* tok_kl;
@@ -134,7 +148,7 @@ struct ReduceArgs {
 // Scalar reduction (stage 2).
 struct FinalArgs {
   int64_t B;
-  float beta;
+  double beta;
   WsHeader* hdr;
   const double* w;
   const double* P;
@@ -152,7 +166,7 @@ struct TokenArgs {
   const float* ref;         // null when beta == 0
   const uint8_t* mask;
   int64_t B, T;
-  float lo, hi, beta;
+  Objective obj;
   const float* grad_scale;
   float* dlogp;
   // workspace

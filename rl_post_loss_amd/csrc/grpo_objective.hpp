@@ -1,0 +1,120 @@
+// Per-token objective: policy loss, reference-KL estimator and the token's
+// d loss / d logp, shared by the logits row kernels and the log-prob token
+// kernel.
+//
+// Policy-loss forms follow the dockyard_rl design doc (One loss many
+// algorithms: the clipped surrogate, its dual clip, REINFORCE and the
+// on-policy form; CISPO) and the Relax REINFORCE++ page (Formula-level
+// comparison: SAPO's soft sigmoid gate).  KL estimators follow dockyard_rl
+// (Reference-KL penalty).  Everything is float32, as the rest of the row
+// epilogue.
+#pragma once
+
+#include <math.h>
+
+#include "../../include/grpo.h"
+#include "grpo_internal.hpp"
+
+namespace grpo {
+
+struct TokObj {
+  float loss;    // policy loss l
+  float kl;      // KL estimator value
+  float g;       // dl/dlogp + beta * dkl/dlogp, before the token weight
+  bool clipped;  // counted in the clip statistic
+};
+
+// clip(x, -v, v) that keeps a NaN (fminf/fmaxf would replace it by a bound)
+__device__ __forceinline__ float clamp_sym(float x, float v) {
+  return x != x ? x : fminf(fmaxf(x, -v), v);
+}
+
+// kGeneral = false: the clipped surrogate with k3, no dual clip, no clamps.
+// kGeneral = true: every form the Objective selects.  For the default
+// settings both evaluate the same expressions in the same order.
+template <bool kGeneral>
+__device__ __forceinline__ TokObj token_objective(const Objective& o, float logp, float old,
+                                                  float d, float adv) {
+#pragma clang fp contract(off)
+  TokObj r;
+  const float rho = expf(logp - old);
+  if constexpr (!kGeneral) {
+    r.kl = expm1f(d) - d;
+    r.clipped = (adv > 0.0f && rho > o.hi) || (adv < 0.0f && rho < o.lo);
+    const float unc = rho * adv;
+    const float clp = fminf(fmaxf(rho, o.lo), o.hi) * adv;
+    r.loss = -fminf(unc, clp);
+    const float dloss = r.clipped ? 0.0f : -adv * rho;
+    r.g = dloss + o.beta * -expm1f(d);
+    return r;
+  } else {
+    float dloss;
+    r.clipped = false;
+    if (o.pg == GRPO_PG_CLIP) {
+      r.clipped = (adv > 0.0f && rho > o.hi) || (adv < 0.0f && rho < o.lo);
+      const float unc = rho * adv;
+      const float clp = fminf(fmaxf(rho, o.lo), o.hi) * adv;
+      float obj = fminf(unc, clp);
+      dloss = r.clipped ? 0.0f : -adv * rho;
+      // dual clip: for A < 0 the objective is bounded below by c A
+      if (o.dual_c > 0.0f && adv < 0.0f && obj < o.dual_c * adv) {
+        obj = o.dual_c * adv;
+        dloss = 0.0f;
+        r.clipped = true;
+      }
+      r.loss = -obj;
+    } else if (o.pg == GRPO_PG_CISPO) {
+      // the clipped ratio weights -A logp as a constant
+      const float wgt = fminf(fmaxf(rho, o.lo), o.hi);
+      r.clipped = rho < o.lo || rho > o.hi;
+      dloss = -adv * wgt;
+      r.loss = dloss * logp;
+    } else if (o.pg == GRPO_PG_SAPO) {
+      // f(rho) = 4 s / tau with s = sigmoid(tau (rho - 1)); f'(rho) = 4 s (1 - s).
+      // s and 1 - s both come from e = exp(-|x|), so neither cancels.
+      const float tau = adv > 0.0f ? o.tau_pos : o.tau_neg;
+      const float x = tau * (rho - 1.0f);
+      const float e = expf(-fabsf(x));
+      const float inv = 1.0f / (1.0f + e);
+      const float s = x >= 0.0f ? inv : e * inv;
+      const float sc = x >= 0.0f ? e * inv : inv;
+      r.loss = -(4.0f * s / tau) * adv;
+      dloss = -adv * 4.0f * s * sc * rho;
+    } else if (o.pg == GRPO_PG_REINFORCE) {
+      r.loss = -adv * logp;
+      dloss = -adv;
+    } else {  // GRPO_PG_ON_POLICY: rho = exp(logp - sg(logp)) = 1
+      r.loss = -adv;
+      dloss = -adv;
+    }
+
+    bool pass = true;
+    float dc = d;
+    if (o.kl_in > 0.0f) {
+      pass = fabsf(d) <= o.kl_in;
+      dc = clamp_sym(d, o.kl_in);
+    }
+    float val, dval;  // estimator and its derivative in d
+    if (o.kl == GRPO_KL_K1) {
+      val = -dc;
+      dval = -1.0f;
+    } else if (o.kl == GRPO_KL_K2) {
+      val = 0.5f * dc * dc;
+      dval = dc;
+    } else {
+      const float em = expm1f(dc);
+      val = em - dc;
+      dval = em;
+    }
+    if (o.kl_out > 0.0f) {
+      pass = pass && fabsf(val) <= o.kl_out;
+      val = clamp_sym(val, o.kl_out);
+    }
+    r.kl = val;
+    const float dkl = pass ? -dval : 0.0f;  // dd/dlogp = -1
+    r.g = dloss + o.beta * dkl;
+    return r;
+  }
+}
+
+}  // namespace grpo

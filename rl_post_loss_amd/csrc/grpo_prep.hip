@@ -6,7 +6,8 @@
 // follow "GRPO Loss" (Normalizer semantics), the Relax REINFORCE++ page
 // (PPO and KL reduction: mean within a response, then over responses) and
 // the grpo.cpp README (The length-normalization detail: total weight
-// L_i^alpha / B per response).
+// L_i^alpha / B per response); the fixed-constant normaliser divides by a
+// declared constant ("GRPO Loss", Normalizer semantics).
 //
 // Everything here is binary64 with contraction off, in the same sequential
 // order as the defining formulas, so advantages and weights round to the
@@ -33,10 +34,11 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
   return __popc(t);
 }
 
-__device__ double sequence_weight(int32_t reduction, double alpha, int64_t B, int64_t L,
-                                  int64_t N) {
+__device__ double sequence_weight(int32_t reduction, double alpha, double norm_constant,
+                                  int64_t B, int64_t L, int64_t N) {
 #pragma clang fp contract(off)
   if (reduction == GRPO_TOKEN_MEAN) return 1.0 / double(N > 0 ? N : 1);
+  if (reduction == GRPO_FIXED_CONSTANT) return 1.0 / norm_constant;
   if (reduction == GRPO_SEQUENCE_MEAN) return 1.0 / (double(B) * double(L > 0 ? L : 1));
   if (L == 0) return 0.0;
   const double Lf = double(L);
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kWeightThreads) void grpo_weights_kernel(PrepArgs a
   for (int64_t k = tid; k < a.B; k += kWeightThreads) n += a.L[k];
   const long long N = block_sum_i64<kWeightThreads>(n, sh_i64);
   for (int64_t k = tid; k < a.B; k += kWeightThreads) {
-    const double wk = sequence_weight(a.reduction, a.alpha, a.B, a.L[k], N);
+    const double wk = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[k], N);
     a.w[k] = wk;
     if (a.seq_weight_out) a.seq_weight_out[k] = float(wk);
   }

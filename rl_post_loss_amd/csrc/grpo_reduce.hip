@@ -13,6 +13,7 @@
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
 #include "grpo_internal.hpp"
+#include "grpo_objective.hpp"
 
 namespace grpo {
 
@@ -88,31 +89,11 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Per-token objective from log-probs (float32), shared by nothing else: the
-// vocabulary kernel has its own copy in its epilogue.
-struct TokTerms {
-  float loss, k3, G;
-  bool clipped;
-};
-
-__device__ __forceinline__ TokTerms token_terms(float logp, float old, float ref, bool has_ref,
-                                                float adv, float wg, float lo, float hi,
-                                                float beta) {
-  TokTerms r;
-  const float rho = expf(logp - old);
-  const float d = has_ref ? ref - logp : 0.0f;
-  r.k3 = expm1f(d) - d;
-  r.clipped = (adv > 0.0f && rho > hi) || (adv < 0.0f && rho < lo);
-  const float unc = rho * adv;
-  const float clp = fminf(fmaxf(rho, lo), hi) * adv;
-  r.loss = -fminf(unc, clp);
-  const float dloss = r.clipped ? 0.0f : -adv * rho;
-  r.G = wg * (dloss + beta * -expm1f(d));
-  return r;
-}
-
-// One block per sequence: tokens -> dlogp and the per-sequence totals.  The grpo.cpp README's token-loss kernels (CUDA
-// section) compute the same loss from per-token log-probs.
+// One block per sequence: tokens -> dlogp and the per-sequence totals.  The
+// grpo.cpp README's token-loss kernels (CUDA section) compute the same loss
+// from per-token log-probs.  kGeneral selects the objective code path (see
+// token_objective).
+template <bool kGeneral>
 __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma clang fp contract(off)
   __shared__ double sh_f64[kRedThreads / kWave];
@@ -171,15 +152,15 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if ((m4[u] >> (8 * j)) & 0xffu) {
-            const TokTerms r = token_terms(lpv[j], odv[j], rfv[j], has_ref, adv, wg, a.lo, a.hi,
-                                           a.beta);
-            gv[j] = r.G;
+            const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
+            const TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv);
+            gv[j] = wg * r.g;
             tl[j] = r.loss;
-            tk[j] = r.k3;
+            tk[j] = r.kl;
             p = p + double(r.loss);
-            k = k + double(r.k3);
+            k = k + double(r.kl);
             c += r.clipped ? 1 : 0;
-            nonfinite |= !(isfinite(r.loss) && isfinite(r.k3) && isfinite(r.G));
+            nonfinite |= !(isfinite(r.loss) && isfinite(r.kl) && isfinite(gv[j]));
           }
         }
         if (a.dlogp)
@@ -194,15 +175,16 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
       const int64_t s = base + t;
       float g = 0.f, tl = 0.f, tk = 0.f;
       if (a.mask == nullptr || a.mask[s] != 0) {
-        const TokTerms r = token_terms(a.logp[s], a.old[s], has_ref ? a.ref[s] : 0.0f, has_ref,
-                                       adv, wg, a.lo, a.hi, a.beta);
-        g = r.G;
+        const float lps = a.logp[s];
+        const float d = has_ref ? a.ref[s] - lps : 0.0f;
+        const TokObj r = token_objective<kGeneral>(a.obj, lps, a.old[s], d, adv);
+        g = wg * r.g;
         tl = r.loss;
-        tk = r.k3;
+        tk = r.kl;
         p = p + double(r.loss);
-        k = k + double(r.k3);
+        k = k + double(r.kl);
         c += r.clipped ? 1 : 0;
-        nonfinite |= !(isfinite(r.loss) && isfinite(r.k3) && isfinite(r.G));
+        nonfinite |= !(isfinite(r.loss) && isfinite(r.kl) && isfinite(g));
       }
       if (a.dlogp) a.dlogp[s] = g;
       if (a.out_loss) a.out_loss[s] = tl;
@@ -223,7 +205,10 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 }
 
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(grpo_token_kernel, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
+  if (a.obj.general)
+    hipLaunchKernelGGL(grpo_token_kernel<true>, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(grpo_token_kernel<false>, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
 #include "grpo_internal.hpp"
+#include "grpo_objective.hpp"
 
 namespace grpo {
 
@@ -228,22 +229,15 @@ __device__ __forceinline__ RowGrad row_epilogue(const RowArgs& a, int64_t row, L
                                                 float adv, float wgt, float gs) {
   const RowLogp px = finish_row(sx, xa);
   const float d = has_ref ? row_log_ratio(px, finish_row(sy, ya)) : 0.0f;
-  const float rho = expf(px.logp - old);
-  const float k3 = expm1f(d) - d;
-  const bool clipped = (adv > 0.0f && rho > a.hi) || (adv < 0.0f && rho < a.lo);
-  const float unc = rho * adv;
-  const float clp = fminf(fmaxf(rho, a.lo), a.hi) * adv;
-  const float tl = -fminf(unc, clp);
-  const float dloss = clipped ? 0.0f : -adv * rho;
-  const float dkl = -expm1f(d);
-  const float G = wgt * gs * (dloss + a.beta * dkl);
-  if (!(isfinite(tl) && isfinite(k3) && isfinite(G))) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
-  a.tok_loss[row] = tl;
-  a.tok_kl[row] = k3;
-  a.flags[row] = clipped ? 1 : 0;
+  const TokObj t = token_objective<true>(a.obj, px.logp, old, d, adv);
+  const float G = wgt * gs * t.g;
+  if (!(isfinite(t.loss) && isfinite(t.kl) && isfinite(G))) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
+  a.tok_loss[row] = t.loss;
+  a.tok_kl[row] = t.kl;
+  a.flags[row] = t.clipped ? 1 : 0;
   if (a.out_logp) a.out_logp[row] = px.logp;
-  if (a.out_loss) a.out_loss[row] = tl;
-  if (a.out_kl) a.out_kl[row] = k3;
+  if (a.out_loss) a.out_loss[row] = t.loss;
+  if (a.out_kl) a.out_kl[row] = t.kl;
   return RowGrad{G, px.c, px.omp};
 }
 

@@ -97,16 +97,37 @@ def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_b
     return g, keep, ng
 
 
-def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
-    key = ("c", clip_eps, eps_low, eps_high, beta, reduction, alpha)
+# Objective keywords shared by the loss entry points, with their defaults
+# (the clipped surrogate with the k3 estimator).
+OBJECTIVE_DEFAULTS = dict(pg_loss="clip", kl_estimator="k3", dual_clip_c=None, sapo_tau_pos=1.0,
+                          sapo_tau_neg=1.0, kl_input_clamp=None, kl_output_clamp=None,
+                          norm_constant=None)
+
+
+def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, objective):
+    extra = {k: objective.pop(k, v) for k, v in OBJECTIVE_DEFAULTS.items()}
+    if objective:
+        raise TypeError(f"unexpected keyword arguments {sorted(objective)}")
+    key = ("c", clip_eps, eps_low, eps_high, beta, reduction, alpha) + tuple(extra.values())
     hit = _STRUCT_CACHE.get(key)
     if hit is None:
-        hit = _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+        hit = _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, **extra)
         _STRUCT_CACHE[key] = hit
     return hit
 
 
-def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
+def _optional_positive(name, v):
+    # None turns the option off (0 in the C struct); an explicit value must be
+    # positive, so that 0 never silently means "off"
+    if v is None:
+        return 0.0
+    _need(float(v) > 0.0, f"{name} must be positive or None")
+    return float(v)
+
+
+def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, *, pg_loss, kl_estimator,
+              dual_clip_c, sapo_tau_pos, sapo_tau_neg, kl_input_clamp, kl_output_clamp,
+              norm_constant):
     c = GrpoCfg()
     c.eps_low = float(clip_eps if eps_low is None else eps_low)
     c.eps_high = float(clip_eps if eps_high is None else eps_high)
@@ -115,6 +136,18 @@ def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha):
         raise ValueError(f"unknown reduction {reduction!r}")
     c.reduction = _abi.REDUCTION_CODES[reduction]
     c.alpha = float(alpha) if alpha is not None else 0.0
+    if pg_loss not in _abi.PG_LOSS_CODES:
+        raise ValueError(f"unknown pg_loss {pg_loss!r}")
+    if kl_estimator not in _abi.KL_ESTIMATOR_CODES:
+        raise ValueError(f"unknown kl_estimator {kl_estimator!r}")
+    c.pg_loss = _abi.PG_LOSS_CODES[pg_loss]
+    c.kl_estimator = _abi.KL_ESTIMATOR_CODES[kl_estimator]
+    c.dual_clip_c = _optional_positive("dual_clip_c", dual_clip_c)
+    c.sapo_tau_pos = float(sapo_tau_pos)
+    c.sapo_tau_neg = float(sapo_tau_neg)
+    c.kl_input_clamp = _optional_positive("kl_input_clamp", kl_input_clamp)
+    c.kl_output_clamp = _optional_positive("kl_output_clamp", kl_output_clamp)
+    c.norm_constant = _optional_positive("norm_constant", norm_constant)
     return c
 
 
@@ -238,9 +271,11 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
                     clip_eps=0.2, eps_low=None, eps_high=None, beta=0.04,
                     samples_per_prompt=None, group_boundaries=None, leave_one_out=False,
                     scale_by_std=True, std_eps=1e-6, reduction="token_mean", alpha=None,
-                    want_grad=True, grad_scale=None, per_token=False, out=None):
+                    want_grad=True, grad_scale=None, per_token=False, out=None, **objective):
     """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp.
-    ``out``: a previous result of the same sizes whose buffers are reused."""
+    ``out``: a previous result of the same sizes whose buffers are reused.
+    ``objective``: the keywords of OBJECTIVE_DEFAULTS (policy-loss form, KL
+    estimator, dual clip, SAPO temperatures, KL clamps, fixed normaliser)."""
     lib = load_library()
     dev = logp.device
     _need(logp.dim() == 2 and logp.is_cuda, "logp must be a [B, T] GPU tensor")
@@ -255,7 +290,7 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
     mptr, _ = _mask_ptr(completion_mask, B, T, dev)
     g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
                           std_eps)
-    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, dict(objective))
     res = _reuse(out, B, T, dev, per_token)
     if res is None:
         res, o = _outputs(B, T, dev, per_token, want_logp=False)
@@ -278,13 +313,14 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                       beta=0.04, samples_per_prompt=None, group_boundaries=None,
                       leave_one_out=False, scale_by_std=True, std_eps=1e-6,
                       reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
-                      grad_scale=None, per_token=False, out=None, _ws=None):
+                      grad_scale=None, per_token=False, out=None, _ws=None, **objective):
     """Fused forward + analytic backward from [B, T, V] logits.
 
     grad_out: None allocates a contiguous gradient (dtype ``grad_dtype``,
     default the logits dtype); a tensor writes into it (it may be
     ``policy_logits`` itself, in place); False runs the forward only.
     out: a previous result of the same sizes whose output buffers are reused.
+    objective: the keywords of OBJECTIVE_DEFAULTS, as for grpo_token_loss.
     """
     lib = load_library()
     dev = policy_logits.device
@@ -307,7 +343,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     mptr, _ = _mask_ptr(completion_mask, B, T, dev)
     g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
                           std_eps)
-    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha)
+    cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, dict(objective))
     res = _reuse(out, B, T, dev, per_token)
     if res is None:
         res, o = _outputs(B, T, dev, per_token, want_logp=True)

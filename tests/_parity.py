@@ -8,14 +8,20 @@ Tolerances (stated by the loss path's acceptance criteria, made concrete):
   * bf16 logits (oracle fed the same bf16 values): loss relative error
     <= 1e-4, gradient |dg| <= 2^-7 |g| per element, with an absolute floor of
     2^-126 (below it bf16 has no relative precision).
-Two refinements follow from the arithmetic, and every use is counted:
-  * clip-ambiguous tokens: when the oracle's ratio lies within the float32
-    log-prob error of a clip bound, either side is a correct result, so the
-    row's gradient may match the clipped or the unclipped branch;
+Three refinements follow from the arithmetic, and every use is counted:
+  * branch-ambiguous tokens: when the oracle's log-prob or log-ratio lies
+    within the float32 error of a branch point of the objective (a clip or
+    dual-clip bound, a KL clamp), either side is a correct result, so the
+    row's gradient may match any branch reached within that error;
   * ill-conditioned rows: when G (d loss / d logp) cancels, e.g. A = 0 and
     d close to 0, float32 log-probs (absolute error about 1e-6 at |logp| ~ 12)
     cannot give G to 2^-7; such a row is compared at its propagated error
-    bound instead.
+    bound instead;
+  * objectives whose value depends on the log-prob itself (REINFORCE, CISPO)
+    carry the float32 log-prob error into the loss; where the relative bound
+    fails, the loss is compared at that propagated bound instead.
+Branch points and error bounds come from the oracle evaluated at perturbed
+inputs, so they hold for every objective variant.
 """
 
 from __future__ import annotations
@@ -47,17 +53,19 @@ def to_np(t):
     return t.detach().double().cpu().numpy() if t.dtype.is_floating_point else t.detach().cpu().numpy()
 
 
-def cfg_from(wl, reduction=None):
+def cfg_from(wl, reduction=None, **objective):
     red = reduction or wl.reductions[0]
     return oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
-                             reduction=red, alpha=wl.alpha if red == "length_alpha" else None)
+                             reduction=red, alpha=wl.alpha if red == "length_alpha" else None,
+                             **objective)
 
 
-def gpu_kwargs(wl, reduction=None):
+def gpu_kwargs(wl, reduction=None, **objective):
     red = reduction or wl.reductions[0]
     kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=red,
               alpha=wl.alpha if red == "length_alpha" else None)
     kw.update(wl.groups_kwargs())
+    kw.update(objective)
     return kw
 
 
@@ -76,63 +84,143 @@ def host_inputs(inp):
     return out
 
 
+# ---------------------------------------------------------------------------
+# Perturbation of the oracle's per-token inputs.  The GPU evaluates the
+# objective at a log-prob and a log-ratio d that carry float32 errors; the
+# oracle evaluated at logp +- e (d held fixed) and at d +- e (logp held fixed)
+# gives, for any objective variant, (a) which tokens sit close enough to a
+# branch point (clip bound, dual-clip bound, KL clamp) for either branch to be
+# a correct result, (b) the first-order error bound of values and of G.
+# ---------------------------------------------------------------------------
+
+def _active(ref):
+    # the oracle stores 0 at masked slots; an active slot's ratio is positive
+    return ref.tok["rho"] > 0
+
+
+def _terms_at(ref, cfg, dlogp=0.0, dd=0.0):
+    t = ref.tok
+    act = _active(ref)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        old = np.where(act, t["logp"] - np.log(np.where(act, t["rho"], 1.0)), 0.0)
+        lp = t["logp"] + dlogp
+        lref = t["logp"] + t["d"] + dlogp + dd
+        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg)
+    for k, v in out.items():
+        out[k] = np.where(act, v, np.zeros_like(v))
+    return out
+
+
+def _G_of(ref, cfg, t):
+    return ref.seq_weight[:, None] * (t["dloss"] + cfg.beta * t["dkl"])
+
+
+def _branch(t):
+    return np.stack([t["clipped"], t["dkl"] == 0, t["dloss"] == 0])
+
+
+def branch_ambiguity(ref, cfg, mask, e_logp=4 * LOGP_ABS_ERR, e_d=4 * LOGP_ABS_ERR):
+    """(clip-flag ambiguous [B, T], branch ambiguous [B, T], candidate G list)."""
+    center = _terms_at(ref, cfg)
+    bc = _branch(center)
+    flag = np.zeros(mask.shape, dtype=bool)
+    anyb = np.zeros(mask.shape, dtype=bool)
+    cands = [_G_of(ref, cfg, center)]
+    for a, b in ((e_logp, 0.0), (-e_logp, 0.0), (0.0, e_d), (0.0, -e_d)):
+        t = _terms_at(ref, cfg, a, b)
+        flag |= t["clipped"] != center["clipped"]
+        anyb |= np.any(_branch(t) != bc, axis=0)
+        cands.append(_G_of(ref, cfg, t))
+    return flag & mask, anyb & mask, cands
+
+
+def _propagated(ref, cfg, key_fn, e_logp, e_d):
+    """First-order error of key_fn(terms) from logp +- e_logp and d +- e_d,
+    leaving out perturbations that change the token's branch."""
+    center = _terms_at(ref, cfg)
+    c = key_fn(center)
+    bc = _branch(center)
+    tot = np.zeros_like(c)
+    for pair in (((e_logp, 0.0), (-e_logp, 0.0)), ((0.0, e_d), (0.0, -e_d))):
+        worst = np.zeros_like(c)
+        for a, b in pair:
+            t = _terms_at(ref, cfg, a, b)
+            same = np.all(_branch(t) == bc, axis=0)
+            with np.errstate(invalid="ignore"):
+                worst = np.maximum(worst, np.where(same, np.abs(key_fn(t) - c), 0.0))
+        tot = tot + worst
+    return tot
+
+
 def ambiguous_rows(ref, cfg, mask):
-    """Active slots whose oracle ratio is within float32 reach of a clip bound."""
-    rho = ref.tok["rho"]
-    band = rho * 4.0 * LOGP_ABS_ERR + 1e-7
-    lo, hi = 1.0 - cfg.eps_low, 1.0 + cfg.eps_high
-    A = ref.advantages[:, None]
-    amb = ((np.abs(rho - hi) <= band) & (A > 0)) | ((np.abs(rho - lo) <= band) & (A < 0))
-    return amb & mask
+    """Active slots where either branch of the objective is a correct result."""
+    return branch_ambiguity(ref, cfg, mask)[1]
 
 
 def g_rel_tolerance(ref, cfg, base):
     """Per-slot relative tolerance of G: max(base, propagated float32 error)."""
-    A = ref.advantages[:, None]
-    w = ref.seq_weight[:, None]
-    rho = ref.tok["rho"]
-    ed = np.exp(ref.tok["d"])
     G = ref.tok["G"]
-    dG = np.abs(w) * (np.abs(A) * rho + 2.0 * cfg.beta * ed) * LOGP_ABS_ERR * 2.0
+    dG = _propagated(ref, cfg, lambda t: _G_of(ref, cfg, t), 2 * LOGP_ABS_ERR, 4 * LOGP_ABS_ERR)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(G != 0, dG / np.abs(G), np.inf)
     return np.maximum(base, rel), rel > base
 
 
-def alt_G(ref, cfg):
-    """G with the clip decision flipped (for ambiguous slots)."""
-    A = ref.advantages[:, None]
-    w = ref.seq_weight[:, None]
-    rho = ref.tok["rho"]
-    clipped = ref.tok["clipped"]
-    dloss_alt = np.where(clipped, -A * rho, 0.0)
-    return w * (dloss_alt + cfg.beta * ref.tok["dkl"])
+def value_bounds(ref, cfg, e_logp=LOGP_ABS_ERR, e_d=2 * LOGP_ABS_ERR):
+    """Per-token propagated float32 error of the policy loss and KL values."""
+    pl = _propagated(ref, cfg, lambda t: t["loss"], e_logp, e_d)
+    kl = _propagated(ref, cfg, lambda t: t["kl"], e_logp, e_d)
+    return pl, kl
 
 
-def compare_scalars(res, ref, loss_rtol, what=""):
+def compare_scalars(res, ref, cfg, loss_rtol, what="", e_logp=LOGP_ABS_ERR,
+                    e_d=2 * LOGP_ABS_ERR):
+    """Scalars and per-sequence totals.  The loss must meet loss_rtol; when an
+    objective's value depends on the log-prob itself (REINFORCE, CISPO), the
+    float32 log-prob error propagated through it is added to the bound, and
+    the returned flag says so."""
     loss = float(res.loss)
     kappa = (np.sum(ref.seq_weight * np.abs(ref.seq_policy)) + 1e-300) / max(abs(ref.loss), 1e-300)
     rel = abs(loss - ref.loss) / max(abs(ref.loss), 1e-300)
-    assert rel <= loss_rtol, f"{what} loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} kappa={kappa:.3g}"
+    pp, pk = value_bounds(ref, cfg, e_logp, e_d)
+    prop_loss = float(np.sum(ref.seq_weight * (pp.sum(axis=1) + cfg.beta * pk.sum(axis=1))))
+    propagated = rel > loss_rtol
+    if propagated:
+        lim = loss_rtol * abs(ref.loss) + prop_loss
+        assert abs(loss - ref.loss) <= lim, (
+            f"{what} loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} kappa={kappa:.3g} "
+            f"propagated bound {prop_loss:.3g}")
     # policy_loss and kl: relative to the weighted absolute sums they are made of
     scale_p = float(np.sum(ref.seq_weight * np.abs(ref.tok["loss"]).sum(axis=1))) + 1e-30
     scale_k = float(np.sum(ref.seq_weight * np.abs(ref.tok["kl"]).sum(axis=1))) + 1e-30
-    assert abs(float(res.policy_loss) - ref.policy_loss) <= loss_rtol * scale_p, what
-    assert abs(float(res.kl) - ref.kl) <= loss_rtol * scale_k, what
-    # per-sequence totals: the relative bound plus the float32 log-prob error
-    # propagated through each token (d l/d logp = -A rho, d k3/d d = e^d - 1)
+    wp = float(np.sum(ref.seq_weight * pp.sum(axis=1)))
+    wk = float(np.sum(ref.seq_weight * pk.sum(axis=1)))
+    assert abs(float(res.policy_loss) - ref.policy_loss) <= loss_rtol * scale_p + wp, what
+    assert abs(float(res.kl) - ref.kl) <= loss_rtol * scale_k + wk, what
+    # per-sequence totals: the relative bound plus the propagated error
     sp = to_np(res.seq_policy)
     sk = to_np(res.seq_kl)
-    A = ref.advantages[:, None]
-    prop_p = (np.abs(A) * ref.tok["rho"] * (ref.tok["dloss"] != 0)).sum(axis=1) * LOGP_ABS_ERR
-    prop_k = (np.abs(np.expm1(ref.tok["d"]))).sum(axis=1) * 2 * LOGP_ABS_ERR
-    tp = loss_rtol * np.abs(ref.tok["loss"]).sum(axis=1) + prop_p + 1e-30
-    tk = loss_rtol * np.abs(ref.tok["kl"]).sum(axis=1) + prop_k + 1e-30
+    tp = loss_rtol * np.abs(ref.tok["loss"]).sum(axis=1) + pp.sum(axis=1) + 1e-30
+    tk = loss_rtol * np.abs(ref.tok["kl"]).sum(axis=1) + pk.sum(axis=1) + 1e-30
     ep = np.abs(sp - ref.seq_policy)
     ek = np.abs(sk - ref.seq_kl)
     assert np.all(ep <= tp), f"{what} seq_policy worst {np.max(ep / tp):.3g}x of bound"
     assert np.all(ek <= tk), f"{what} seq_kl worst {np.max(ek / tk):.3g}x of bound"
-    return rel, kappa
+    return rel, kappa, propagated
+
+
+def compare_token_values(res, ref, cfg, mask, rtol, e_logp=LOGP_ABS_ERR, e_d=2 * LOGP_ABS_ERR):
+    """Per-token loss and KL outputs: rtol plus the propagated error; 0 at
+    masked slots."""
+    pp, pk = value_bounds(ref, cfg, e_logp, e_d)
+    for name, bound in (("loss", pp), ("kl", pk)):
+        g = to_np(getattr(res, "tok_" + name))
+        r = ref.tok[name]
+        assert np.all(g[~mask] == 0.0), f"tok_{name} at masked slots"
+        lim = rtol * np.abs(r) + 2.0 * bound + 1e-30
+        bad = (np.abs(g - r) > lim) & mask
+        assert not bad.any(), (f"tok_{name}: {int(bad.sum())} values out of bound, first at "
+                               f"{np.argwhere(bad)[0]}: gpu={g[bad][0]!r} oracle={r[bad][0]!r}")
 
 
 def compare_exact_parts(res, ref, what=""):
@@ -144,42 +232,53 @@ def compare_exact_parts(res, ref, what=""):
     return counts
 
 
-def compare_logits_grad(grad_gpu, ref, cfg, mask, bf16, what=""):
-    """grad_gpu: float64 numpy [B, T, V]; ref: oracle result with grad."""
+def compare_logits_grad(grad_gpu, ref, cfg, mask, bf16, what="", policy=None, ids=None):
+    """grad_gpu: float64 numpy [B, T, V]; ref: oracle result with grad.
+    policy, ids: host policy logits and action ids, needed only to rebuild a
+    row whose oracle G is exactly zero when the GPU took the other branch."""
     g = grad_gpu
     r = ref.grad
-    amb = ambiguous_rows(ref, cfg, mask)
-    stats = dict(ambiguous=int(amb.sum()), illcond=0, rows=int(mask.sum()))
+    flag_amb, amb, cands = branch_ambiguity(ref, cfg, mask)
+    stats = dict(ambiguous=int(flag_amb.sum()), branch_ambiguous=int(amb.sum()), illcond=0,
+                 rows=int(mask.sum()))
     # masked rows: exactly zero
     assert np.all(g[~mask] == 0.0), what + " masked rows must be zero"
+    gmax = float(np.max(np.abs(r))) if r.size else 0.0
+
+    def row_ok(gi, ri, tol_rel):
+        if bf16:
+            with np.errstate(invalid="ignore"):
+                lim = np.where(np.abs(ri) > 0, tol_rel * np.abs(ri), 0.0) + 2.0 ** -126
+            return np.abs(gi - ri) <= lim
+        return np.abs(gi - ri) <= 1e-5 * gmax + 1e-30
+
     if bf16:
         tol, ill = g_rel_tolerance(ref, cfg, 2.0 ** -7)
         stats["illcond"] = int((ill & mask).sum())
-        floor = 2.0 ** -126
-        err = np.abs(g - r)
-        with np.errstate(invalid="ignore"):
-            lim = np.where(np.abs(r) > 0, tol[..., None] * np.abs(r), 0.0) + floor
-        ok = err <= lim
-        bad_rows = ~ok.all(axis=-1) & mask
+        ok = row_ok(g, r, tol[..., None])
     else:
-        gmax = float(np.max(np.abs(r))) if r.size else 0.0
-        err = np.abs(g - r)
-        ok = err <= 1e-5 * gmax + 1e-30
-        bad_rows = ~ok.all(axis=-1) & mask
-    # ambiguous rows may match the flipped branch instead
+        tol = np.full(mask.shape, 1e-5)
+        ok = row_ok(g, r, None)
+    bad_rows = ~ok.all(axis=-1) & mask
+    # rows at a branch point may match any candidate branch instead
     for (i, t) in zip(*np.nonzero(bad_rows & amb)):
         G = ref.tok["G"][i, t]
-        Ga = alt_G(ref, cfg)[i, t]
-        if G != 0:
-            alt = r[i, t] * (Ga / G)
-        else:
-            continue
-        if bf16:
-            ok_alt = np.all(np.abs(g[i, t] - alt) <= 2.0 ** -7 * np.abs(alt) + 2.0 ** -126)
-        else:
-            ok_alt = np.all(np.abs(g[i, t] - alt) <= 1e-5 * float(np.max(np.abs(r))) + 1e-30)
-        if ok_alt:
-            bad_rows[i, t] = False
+        for C in cands[1:]:
+            Gc = C[i, t]
+            if G != 0:
+                alt = r[i, t] * (Gc / G)
+            elif policy is not None and ids is not None:
+                x = policy[i, t].astype(np.float64)
+                p = np.exp(x - x.max())
+                p /= p.sum()
+                onehot = np.zeros_like(p)
+                onehot[int(ids[i, t])] = 1.0
+                alt = Gc * (onehot - p)
+            else:
+                continue
+            if np.all(row_ok(g[i, t], alt, 2.0 ** -7 if bf16 else None)):
+                bad_rows[i, t] = False
+                break
     nbad = int(bad_rows.sum())
     if nbad:
         i, t = [int(v[0]) for v in np.nonzero(bad_rows)]

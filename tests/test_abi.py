@@ -5,6 +5,7 @@ rejects invalid arguments before launching anything."""
 import ctypes as C
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -71,10 +72,35 @@ def _groups(spp=4, bounds=None, loo=0, scale=1, eps=1e-6):
     return g, keep
 
 
-def _cfg(lo=0.2, hi=0.2, beta=0.04, red=0, alpha=0.0):
+def _cfg(lo=0.2, hi=0.2, beta=0.04, red=0, alpha=0.0, **extra):
     c = _abi.GrpoCfg()
     c.eps_low, c.eps_high, c.beta, c.reduction, c.alpha = lo, hi, beta, red, alpha
+    c.sapo_tau_pos = c.sapo_tau_neg = 1.0
+    for k, v in extra.items():
+        setattr(c, k, v)
     return c
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors have the C compiler's sizes and field offsets."""
+    structs = {"grpo_groups": _abi.GrpoGroups, "grpo_cfg": _abi.GrpoCfg,
+               "grpo_outputs": _abi.GrpoOutputs}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-o", str(exe), str(src)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                        text=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(out[name]) == C.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(out[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
 
 
 FAKE = 0x10000000          # never dereferenced: every call below fails validation first
@@ -128,6 +154,16 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, cfg=_cfg(beta=0.1), ref=None) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(red=5)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(red=2, alpha=1.5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(red=3)) == E["GRPO_ERR_CONFIG"]             # no norm_constant
+    assert _fwd(lib, cfg=_cfg(red=3, norm_constant=float("inf"))) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=-1)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(kl_estimator=3)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(dual_clip_c=1.0)) == E["GRPO_ERR_CONFIG"]    # needs c > 1
+    assert _fwd(lib, cfg=_cfg(dual_clip_c=3.0, pg_loss=1)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=2, sapo_tau_neg=0.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(kl_input_clamp=-1.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(kl_output_clamp=float("nan"))) == E["GRPO_ERR_CONFIG"]
     # aliasing: in place with another dtype or stride, partial overlap
     assert _fwd(lib, grad=FAKE, gdtype=1) == E["GRPO_ERR_ALIAS"]
     assert _fwd(lib, grad=FAKE + 64) == E["GRPO_ERR_ALIAS"]

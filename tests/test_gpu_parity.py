@@ -51,7 +51,7 @@ def check_logits_case(rpl, wl, seed=0, reduction=None):
     cfg = cfg_from(wl, reduction)
     compare_exact_parts(res, ref, wl.name)
     bf16 = wl.dtype == "bf16"
-    compare_scalars(res, ref, 1e-4 if bf16 else 1e-5, wl.name)
+    compare_scalars(res, ref, cfg, 1e-4 if bf16 else 1e-5, wl.name)
     stats = compare_logits_grad(to_np(res.grad), ref, cfg, h["mask"], bf16, wl.name)
     clipped = int(to_np(res.counts)[1])
     assert abs(clipped - ref.clipped) <= stats["ambiguous"], (clipped, ref.clipped, stats)
@@ -132,7 +132,7 @@ def test_padded_row_stride_vector_tail(gpu_lib):
     h = host_inputs(inp_cpu)
     r = oracle_logits(h, wl)
     compare_exact_parts(res, r)
-    compare_scalars(res, r, 1e-4)
+    compare_scalars(res, r, cfg_from(wl), 1e-4)
     compare_logits_grad(to_np(gbuf[..., :V]), r, cfg_from(wl), h["mask"], True)
 
 
@@ -149,7 +149,7 @@ def test_int32_ids_and_f32_grad_from_bf16(gpu_lib):
     assert res.grad.dtype == torch.float32
     h = host_inputs(inp_cpu)
     r = oracle_logits(h, wl)
-    compare_scalars(res, r, 1e-4)
+    compare_scalars(res, r, cfg_from(wl), 1e-4)
     # float32 output: the tighter float32 criterion applies
     compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], False)
 
@@ -164,7 +164,7 @@ def test_no_reference_beta_zero(gpu_lib):
     torch.cuda.synchronize()
     h = host_inputs(inp_cpu)
     r = oracle_logits(h, wl, with_ref=False)
-    compare_scalars(res, r, 1e-5)
+    compare_scalars(res, r, cfg_from(wl), 1e-5)
     assert float(res.kl) == 0.0
     compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], False)
 
@@ -275,7 +275,7 @@ def check_token_case(rpl, wl, B, T, seed=0, reduction=None):
     ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
                                  groups=dict(samples_per_prompt=wl.group_size), cfg=cfg)
     compare_exact_parts(res, ref)
-    compare_scalars(res, ref, 1e-5)
+    compare_scalars(res, ref, cfg, 1e-5)
     g = to_np(res.grad)
     gmax = float(np.max(np.abs(ref.grad)))
     err = np.abs(g - ref.grad)
@@ -314,7 +314,7 @@ def test_token_loss_other_reductions(gpu_lib, reduction):
                                      h["rewards"], groups=dict(samples_per_prompt=16),
                                      cfg=oracle.LossConfig(reduction="length_alpha", alpha=0.5))
         compare_exact_parts(res, ref)
-        compare_scalars(res, ref, 1e-5)
+        compare_scalars(res, ref, oracle.LossConfig(reduction="length_alpha", alpha=0.5), 1e-5)
     else:
         check_token_case(gpu_lib, wl, B=32, T=130, reduction=reduction)
 
