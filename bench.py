@@ -41,7 +41,8 @@ METRIC = "tokens/s for fused GRPO fwd+bwd from [B,T,V] logits; % of MI355X peak 
 ROW_KERNEL = "grpo_rows_kernel"
 KERNEL_SOURCES = ["rl_post_loss_amd/csrc/grpo_rows.hip", "rl_post_loss_amd/csrc/grpo_rows_resident.hip",
                   "rl_post_loss_amd/csrc/grpo_rowcore.hpp", "rl_post_loss_amd/csrc/grpo_device.hpp",
-                  "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_api.hip"]
+                  "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_objective.hpp",
+                  "rl_post_loss_amd/csrc/grpo_api.hip"]
 CALIB_BYTES = 1 << 31   # 2 GiB copy for counter calibration
 
 
