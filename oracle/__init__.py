@@ -8,6 +8,7 @@ from .grpo_oracle import (  # noqa: F401
     KL_ESTIMATORS,
     PG_LOSSES,
     REDUCTIONS,
+    TIS_TYPES,
     LossConfig,
     OracleInputError,
     OracleResult,
@@ -16,6 +17,7 @@ from .grpo_oracle import (  # noqa: F401
     grpo_advantages,
     grpo_loss_fwd_bwd,
     grpo_token_loss,
+    is_weights,
     kl_terms,
     logits_rows,
     policy_terms,

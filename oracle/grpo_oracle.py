@@ -22,8 +22,8 @@ Sources, cited by page title and section:
 * [GRPO-CPP]   grpo.cpp README (sections: The length-normalization detail,
   CUDA).
 * [DOCKYARD]   dockyard_rl design doc, "GRPO and the clipped policy-gradient
-  loss" (sections: Advantage estimation, One loss many algorithms,
-  Reference-KL penalty).
+  loss" (sections: Advantage estimation, One loss many algorithms, CISPO,
+  Reference-KL penalty, Off-policy correction (async GRPO)).
 
 Readings taken where the pages are silent or ambiguous (each is listed in the
 repository design notes as well):
@@ -58,6 +58,12 @@ repository design notes as well):
   clamp, the gradient passes at an exact bound and is zero strictly outside.
 * Fixed-constant normaliser: every active token weighs 1 / C for a declared
   C > 0, independent of the mask.
+* Off-policy correction: the importance weight is the ratio of the current
+  policy (the old log-probs, which the trainer computes with its weights
+  before the update) to the generating policy, exp(old - gen).  It is a
+  constant (it depends on no trained parameter), multiplies the policy loss
+  and its gradient, and leaves the KL term alone.  tis and icepop both clamp
+  it to [min, max]; tis defaults min to 0, icepop requires it.
 
 Parity pins: every function here is pinned by CPU tests in
 ``tests/test_oracle_pins.py`` and ``tests/test_oracle_variants.py`` (closed
@@ -220,6 +226,9 @@ class LossConfig:
     kl_input_clamp / kl_output_clamp clamp d and the estimator to [-v, v].
     reduction "fixed_constant" weights every token by 1 / norm_constant
     ([GRPO-LOSS] Normalizer semantics).
+    tis_type (None | "tis" | "icepop") truncates the off-policy importance
+    weight to [tis_ratio_min, tis_ratio_max] ([DOCKYARD] Off-policy
+    correction (async GRPO)); it needs the generating policy's log-probs.
     """
     eps_low: float = 0.2
     eps_high: float = 0.2
@@ -234,6 +243,24 @@ class LossConfig:
     kl_input_clamp: float | None = None
     kl_output_clamp: float | None = None
     norm_constant: float | None = None
+    tis_type: str | None = None
+    tis_ratio_min: float | None = None
+    tis_ratio_max: float | None = None
+
+
+TIS_TYPES = ("tis", "icepop")
+
+
+def is_weights(old_logp, gen_logp, cfg: LossConfig):
+    """Off-policy importance weight per token ([DOCKYARD] Off-policy
+    correction (async GRPO)): exp(old - gen), truncated to [min, max] by tis
+    (min defaults to 0) or icepop (both bounds given).  A constant: no
+    gradient flows through it."""
+    wt = np.exp(np.asarray(old_logp, dtype=np.float64) - np.asarray(gen_logp, dtype=np.float64))
+    if cfg.tis_type is not None:
+        lo = 0.0 if cfg.tis_ratio_min is None else float(cfg.tis_ratio_min)
+        wt = np.clip(wt, lo, float(cfg.tis_ratio_max))
+    return wt
 
 
 def policy_terms(logp, old_logp, adv, cfg: LossConfig):
@@ -317,15 +344,21 @@ def kl_terms(d, cfg: LossConfig):
     return val, dkl
 
 
-def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig):
+def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig, gen_logp=None):
     """Per-token quantities, all float64 arrays of the broadcast shape.
 
     rho, loss, dloss, clipped from policy_terms; d = logp_ref - logp (0
     without a reference), kl and dkl = d kl / d logp from kl_terms.  With the
     default settings: loss = -min(rho A, clip(rho) A), kl = k3 = e^d - d - 1.
+    With the generating policy's log-probs, loss and dloss carry the
+    off-policy importance weight (is_weights).
     """
     logp = np.asarray(logp, dtype=np.float64)
     rho, loss, dloss, clipped = policy_terms(logp, old_logp, adv, cfg)
+    if gen_logp is not None:
+        wt = is_weights(old_logp, gen_logp, cfg)
+        loss = loss * wt
+        dloss = dloss * wt
     if logp_ref is None:
         d = np.zeros_like(logp)
     else:
@@ -334,7 +367,7 @@ def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig):
     return dict(rho=rho, d=d, kl=kl, loss=loss, clipped=clipped, dloss=dloss, dkl=dkl)
 
 
-def _check_cfg(cfg: LossConfig, have_ref: bool):
+def _check_cfg(cfg: LossConfig, have_ref: bool, have_gen: bool = False):
     if not (0.0 <= cfg.eps_low < 1.0) or cfg.eps_high < 0.0 or cfg.beta < 0.0:
         raise OracleInputError("bad clip range or beta")
     if cfg.beta > 0.0 and not have_ref:
@@ -352,6 +385,18 @@ def _check_cfg(cfg: LossConfig, have_ref: bool):
     for v in (cfg.kl_input_clamp, cfg.kl_output_clamp):
         if v is not None and not v > 0:
             raise OracleInputError("KL clamps must be positive")
+    if cfg.tis_type is not None:
+        if cfg.tis_type not in TIS_TYPES:
+            raise OracleInputError("unknown truncated-IS type")
+        if not have_gen:
+            raise OracleInputError("truncated IS needs the generating policy's log-probs")
+        if cfg.tis_ratio_max is None or not cfg.tis_ratio_max > 0:
+            raise OracleInputError("truncated IS needs a positive upper bound")
+        if cfg.tis_type == "icepop" and cfg.tis_ratio_min is None:
+            raise OracleInputError("icepop needs a lower bound")
+        lo = 0.0 if cfg.tis_ratio_min is None else cfg.tis_ratio_min
+        if not (0.0 <= lo <= cfg.tis_ratio_max):
+            raise OracleInputError("truncated IS bounds must satisfy 0 <= min <= max")
 
 
 @dataclass
@@ -386,7 +431,7 @@ def _reduce(P, K, w, beta):
 # ---------------------------------------------------------------------------
 
 def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: LossConfig,
-                    grad_scale=1.0):
+                    grad_scale=1.0, gen_logp=None):
     """GRPO loss from per-token log-probs.  ``grad`` is d loss / d logp [B, T].
 
     ``groups`` is a dict with keys samples_per_prompt | group_boundaries and
@@ -394,7 +439,7 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     """
     logp = np.asarray(logp)
     B, T = logp.shape
-    _check_cfg(cfg, ref_logp is not None)
+    _check_cfg(cfg, ref_logp is not None, gen_logp is not None)
     m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
     off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
     A = group_advantages(rewards, off, groups.get("leave_one_out", False),
@@ -405,7 +450,8 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     lp = np.asarray(logp, dtype=np.float64)[ii, tt]
     old = np.asarray(old_logp, dtype=np.float64)[ii, tt]
     ref = None if ref_logp is None else np.asarray(ref_logp, dtype=np.float64)[ii, tt]
-    terms = token_terms(lp, old, ref, A[ii], cfg)
+    gen = None if gen_logp is None else np.asarray(gen_logp, dtype=np.float64)[ii, tt]
+    terms = token_terms(lp, old, ref, A[ii], cfg, gen)
     return _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale,
                      grad=None, logp_active=lp)
 
@@ -458,7 +504,7 @@ def row_logsumexp(rows):
 
 
 def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.0,
-                want_grad=True):
+                want_grad=True, gen=None):
     """Forward + gradient for a set of active rows (each row one token slot).
 
     x_rows, y_rows: [n, V] policy / reference logits (y_rows may be None when
@@ -481,7 +527,7 @@ def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.
     else:
         lse_ref = None
         logp_ref = None
-    terms = token_terms(logp, old, logp_ref, adv, cfg)
+    terms = token_terms(logp, old, logp_ref, adv, cfg, gen)
     G = np.asarray(w, dtype=np.float64) * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
     out = dict(terms, lse=lse, lse_ref=lse_ref, logp=logp, logp_ref=logp_ref, G=G)
     if want_grad:
@@ -494,7 +540,7 @@ def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.
 
 def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, rewards, *,
                       groups, cfg: LossConfig, grad_scale=1.0, want_grad=True,
-                      row_chunk=4096):
+                      row_chunk=4096, gen_logps=None):
     """GRPO loss and d loss / d policy_logits from [B, T, V] logits.
 
     Masked rows get an all-zero gradient row and are never read.
@@ -503,7 +549,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     if x.ndim != 3:
         raise OracleInputError("policy_logits must be [B, T, V]")
     B, T, V = x.shape
-    _check_cfg(cfg, ref_logits is not None)
+    _check_cfg(cfg, ref_logits is not None, gen_logps is not None)
     m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
     off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
     A = group_advantages(rewards, off, groups.get("leave_one_out", False),
@@ -512,6 +558,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     ii, tt = np.nonzero(m)
     ids = np.asarray(action_ids)[ii, tt].astype(np.int64)
     old = np.asarray(old_logps, dtype=np.float64)[ii, tt]
+    gen = None if gen_logps is None else np.asarray(gen_logps, dtype=np.float64)[ii, tt]
     grad = np.zeros((B, T, V)) if want_grad else None
     acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "kl", "loss", "dloss", "dkl", "logp")}
     acc["clipped"] = np.zeros(len(ii), dtype=bool)
@@ -520,7 +567,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
         xr = x[ii[sl], tt[sl]]
         yr = None if ref_logits is None else np.asarray(ref_logits)[ii[sl], tt[sl]]
         out = logits_rows(xr, yr, ids[sl], old[sl], A[ii[sl]], w[ii[sl]], cfg,
-                          grad_scale, want_grad)
+                          grad_scale, want_grad, None if gen is None else gen[sl])
         for k in acc:
             acc[k][sl] = out[k]
         if want_grad:

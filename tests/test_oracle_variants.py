@@ -1,5 +1,6 @@
 """Pins for the oracle's objective variants (policy-loss forms, KL estimators,
-KL clamps, the fixed-constant normaliser), each against something other than
+KL clamps, the fixed-constant normaliser, the truncated off-policy importance
+weight), each against something other than
 the oracle: torch autograd of an independent formulation (stop-gradients as
 ``detach``), central finite differences where the loss value is the quantity
 being differentiated, library KL divergences, and closed forms."""
@@ -27,7 +28,7 @@ def _case(rng, B=4, T=4, V=6, ratio_noise=0.5):
     return x, y, ids, old, mask, r
 
 
-def _torch_loss(x, y, ids, old, mask, r, spp, cfg):
+def _torch_loss(x, y, ids, old, mask, r, spp, cfg, gen=None):
     """Independent formulation with torch autograd (float64, CPU)."""
     xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
     idt = torch.tensor(ids)[..., None]
@@ -55,6 +56,11 @@ def _torch_loss(x, y, ids, old, mask, r, spp, cfg):
     else:  # on_policy: the ratio pinned to one by a stop-gradient
         r1 = torch.exp(logp - logp.detach())
         pg = -torch.minimum(r1 * A, r1.clamp(lo, hi) * A)
+    if gen is not None:                  # constant off-policy weight
+        wis = torch.exp(oldt - torch.tensor(gen, dtype=torch.float64))
+        if cfg.tis_type is not None:
+            wis = wis.clamp(cfg.tis_ratio_min or 0.0, cfg.tis_ratio_max)
+        pg = pg * wis
     lr = logq - logp                     # log(pi_ref / pi_theta)
     if cfg.kl_input_clamp is not None:
         lr = lr.clamp(-cfg.kl_input_clamp, cfg.kl_input_clamp)
@@ -100,26 +106,34 @@ VARIANTS = [
     dict(kl_input_clamp=0.2, kl_output_clamp=0.01),
     dict(reduction="fixed_constant", norm_constant=37.0),
     dict(reduction="length_alpha", alpha=0.5, pg_loss="cispo"),
+    dict(tis_type="tis", tis_ratio_max=1.5),
+    dict(tis_type="icepop", tis_ratio_min=0.6, tis_ratio_max=1.4, pg_loss="cispo"),
+    dict(tis_type="tis", tis_ratio_min=0.2, tis_ratio_max=2.0, dual_clip_c=2.0),
+    dict(is_only=True),
 ]
 
 
 @pytest.mark.parametrize("kw", VARIANTS, ids=lambda d: "-".join(f"{k}={v}" for k, v in d.items()))
 def test_variants_against_independent_autograd(kw):
+    kw = dict(kw)
+    use_gen = kw.pop("is_only", False) or "tis_type" in kw
     cfg = LossConfig(beta=0.3, **kw)
     for seed in range(3):
         rng = np.random.default_rng(1000 + seed)
         x, y, ids, old, mask, r = _case(rng)
-        res = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2), cfg=cfg)
-        tot, pol, klv, grad = _torch_loss(x, y, ids, old, mask, r, 2, cfg)
+        gen = old + rng.normal(0, 0.6, old.shape) if use_gen else None
+        res = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2), cfg=cfg,
+                                    gen_logps=gen)
+        tot, pol, klv, grad = _torch_loss(x, y, ids, old, mask, r, 2, cfg, gen)
         assert abs(res.loss - tot) < 1e-12 * max(1, abs(tot))
         assert abs(res.policy_loss - pol) < 1e-12 * max(1, abs(pol))
         assert abs(res.kl - klv) < 1e-12 * max(1, abs(klv))
         np.testing.assert_allclose(res.grad, grad, atol=1e-14, rtol=1e-10)
 
 
-def _loss_value(x, y, ids, old, mask, r, cfg):
+def _loss_value(x, y, ids, old, mask, r, cfg, gen=None):
     return orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2), cfg=cfg,
-                                 want_grad=False).loss
+                                 want_grad=False, gen_logps=gen).loss
 
 
 @pytest.mark.parametrize("kw", [
@@ -233,3 +247,72 @@ def test_variant_validation():
                 dict(reduction="fixed_constant"), dict(pg_loss="nope"), dict(kl_estimator="k9")):
         with pytest.raises(orc.OracleInputError):
             orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=g, cfg=LossConfig(**bad))
+
+
+def test_is_weight_with_gen_equal_old_changes_nothing():
+    """exp(old - gen) = 1 exactly: every output is bit-identical to the call
+    without the correction (also under truncation bounds around 1)."""
+    rng = np.random.default_rng(21)
+    x, y, ids, old, mask, r = _case(rng)
+    g = dict(samples_per_prompt=2)
+    base = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=g, cfg=LossConfig(beta=0.2))
+    for extra in (dict(), dict(tis_type="tis", tis_ratio_max=1.0),
+                  dict(tis_type="icepop", tis_ratio_min=1.0, tis_ratio_max=3.0)):
+        res = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=g,
+                                    cfg=LossConfig(beta=0.2, **extra), gen_logps=old.copy())
+        assert res.loss == base.loss and np.array_equal(res.grad, base.grad)
+
+
+def test_is_weight_closed_forms():
+    old = np.log(np.array([5.0, 0.25, 1.0]))
+    gen = np.zeros(3)
+    np.testing.assert_allclose(orc.is_weights(old, gen, LossConfig()), [5.0, 0.25, 1.0], rtol=1e-15)
+    np.testing.assert_allclose(orc.is_weights(old, gen, LossConfig(tis_type="tis", tis_ratio_max=2.0)),
+                               [2.0, 0.25, 1.0], rtol=1e-15)
+    np.testing.assert_allclose(
+        orc.is_weights(old, gen, LossConfig(tis_type="icepop", tis_ratio_min=0.5, tis_ratio_max=2.0)),
+        [2.0, 0.5, 1.0], rtol=1e-15)
+    # the weight scales the policy loss and its gradient, not the KL
+    A = np.array([1.0, -1.0, 2.0])
+    logp = np.log(np.array([1.1, 0.9, 1.0])) + old
+    cfg = LossConfig(tis_type="tis", tis_ratio_max=2.0, beta=0.5)
+    t0 = orc.token_terms(logp, old, logp + 0.1, A, LossConfig(beta=0.5))
+    t1 = orc.token_terms(logp, old, logp + 0.1, A, cfg, gen)
+    np.testing.assert_allclose(t1["loss"], t0["loss"] * [2.0, 0.25, 1.0], rtol=1e-15)
+    np.testing.assert_allclose(t1["dloss"], t0["dloss"] * [2.0, 0.25, 1.0], rtol=1e-15)
+    assert np.array_equal(t1["kl"], t0["kl"]) and np.array_equal(t1["dkl"], t0["dkl"])
+
+
+def test_is_finite_differences():
+    """The weight depends on no logit, so the gradient is the derivative of
+    the loss value."""
+    cfg = LossConfig(beta=0.3, tis_type="icepop", tis_ratio_min=0.7, tis_ratio_max=1.3)
+    rng = np.random.default_rng(8)
+    x, y, ids, old, mask, r = _case(rng, B=2, T=3, V=4, ratio_noise=0.7)
+    gen = old + rng.normal(0, 0.5, old.shape)
+    res = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2), cfg=cfg,
+                                gen_logps=gen)
+    rho = res.tok["rho"][mask]
+    assert min(abs(rho[:, None] - np.array([0.8, 1.2])[None]).ravel()) > 1e-4
+    h = 1e-6
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (_loss_value(xp, y, ids, old, mask, r, cfg, gen)
+                   - _loss_value(xm, y, ids, old, mask, r, cfg, gen)) / (2 * h)
+    np.testing.assert_allclose(res.grad, fd, atol=3e-9)
+
+
+def test_is_validation():
+    x, y, ids, old, mask, r = _case(np.random.default_rng(0), B=2, T=2, V=3)
+    g = dict(samples_per_prompt=2)
+    bad = [(dict(tis_type="tis", tis_ratio_max=2.0), None),            # no generating log-probs
+           (dict(tis_type="icepop", tis_ratio_max=2.0), old),          # icepop without a minimum
+           (dict(tis_type="tis", tis_ratio_min=3.0, tis_ratio_max=2.0), old),
+           (dict(tis_type="tis"), old),
+           (dict(tis_type="clip", tis_ratio_max=2.0), old)]
+    for kw, gen in bad:
+        with pytest.raises(orc.OracleInputError):
+            orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=g, cfg=LossConfig(**kw), gen_logps=gen)
