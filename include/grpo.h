@@ -20,7 +20,7 @@
  *   [GRPO-CPP]   grpo.cpp README: The length-normalization detail, CUDA.
  *   [DOCKYARD]   dockyard_rl, "GRPO and the clipped policy-gradient loss":
  *                Advantage estimation, One loss many algorithms, CISPO,
- *                Reference-KL penalty.
+ *                Reference-KL penalty, Off-policy correction (async GRPO).
  *   [RPP-F]      Relax docs, "REINFORCE++ and REINFORCE++-baseline":
  *                Formula-level comparison (SAPO's soft gate).
  *
@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 2
+#define GRPO_ABI_VERSION 3
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -148,6 +148,19 @@ typedef enum grpo_pg_loss {
  *   GRPO_KL_K2  d^2 / 2            dkl/dlogp = -d */
 typedef enum grpo_kl_estimator { GRPO_KL_K3 = 0, GRPO_KL_K1 = 1, GRPO_KL_K2 = 2 } grpo_kl_estimator;
 
+/* Off-policy correction ([DOCKYARD] Off-policy correction (async GRPO)).
+ * When the caller passes the generating policy's log-probs gen_logps, every
+ * token's policy loss l and its gradient are multiplied by the importance
+ * weight of the current policy (old_logps) to the generating one,
+ *   omega = exp(old_logps - gen_logps),
+ * a constant (it depends on no logit); the KL term is not weighted.
+ *   GRPO_TIS_NONE    omega as is
+ *   GRPO_TIS_TIS     clip(omega, tis_ratio_min, tis_ratio_max), min usually 0
+ *   GRPO_TIS_ICEPOP  clip(omega, tis_ratio_min, tis_ratio_max), both bounds
+ *                    chosen by the caller
+ * Truncation needs gen_logps. */
+typedef enum grpo_tis { GRPO_TIS_NONE = 0, GRPO_TIS_TIS = 1, GRPO_TIS_ICEPOP = 2 } grpo_tis;
+
 /* Device-detected data faults, OR-ed into outputs->status (which each call
  * overwrites). */
 #define GRPO_FAULT_BAD_ACTION 1u  /* an active slot's action id is outside [0, V): that slot
@@ -176,8 +189,8 @@ typedef struct grpo_groups {
 } grpo_groups;
 
 /* Objective settings.  A symmetric clip sets eps_low == eps_high.  Zero in
- * pg_loss .. norm_constant selects the clipped surrogate with the k3
- * estimator, no dual clip and no KL clamps. */
+ * pg_loss .. tis_ratio_max selects the clipped surrogate with the k3
+ * estimator, no dual clip, no KL clamps and no truncation. */
 typedef struct grpo_cfg {
   double eps_low;          /* in [0, 1) */
   double eps_high;         /* >= 0 */
@@ -192,6 +205,9 @@ typedef struct grpo_cfg {
   double kl_input_clamp;   /* 0: off; else > 0 and finite */
   double kl_output_clamp;  /* 0: off; else > 0 and finite */
   double norm_constant;    /* > 0 and finite, read by GRPO_FIXED_CONSTANT only */
+  int32_t tis_type;        /* grpo_tis (0: no truncation) */
+  double tis_ratio_min;    /* >= 0, <= tis_ratio_max; read when tis_type != 0 */
+  double tis_ratio_max;    /* > 0 and finite; read when tis_type != 0 */
 } grpo_cfg;
 
 /* Outputs (DEVICE pointers).  Only `scalars` is required; any other field may
@@ -235,13 +251,15 @@ GRPO_API grpo_status grpo_advantages(const float *rewards, int64_t B, const grpo
 /* Logprob-level token loss ([GRPO-CPP] CUDA: token loss from per-token
  * log-probs, returning dlogp).  logp, old_logp, ref_logp: [B, T] float32,
  * contiguous; ref_logp may be NULL only when beta == 0 (then d = 0).
+ * gen_logp: [B, T] float32 log-probs of the generating policy, or NULL (no
+ * off-policy correction; see grpo_tis).
  * mask: [B, T] bytes or NULL (all active).  rewards: [B] float32.
  * dlogp_out: [B, T] float32, d loss / d logp (0 at masked slots), or NULL
  * for the forward only.  grad_scale: device float scalar multiplying every
  * gradient, or NULL for 1.  The per-token outputs tok_logp are not written
  * by this entry point. */
 GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, const float *ref_logp,
-                            const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
+                            const float *gen_logp, const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
                             const grpo_groups *groups, const grpo_cfg *cfg, float *dlogp_out,
                             const float *grad_scale, const grpo_outputs *out, void *ws,
                             size_t ws_bytes, void *stream);
@@ -253,7 +271,9 @@ GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, c
  *     at element (i*T + t) * row_stride, row_stride >= V.  ref_logits may be
  *     NULL only when beta == 0.  ref_logits may equal policy_logits.
  *   action_ids: [B, T] in ids_dtype, contiguous.
- *   old_logps: [B, T] float32.  mask: [B, T] bytes or NULL.  rewards: [B].
+ *   old_logps: [B, T] float32.  gen_logps: [B, T] float32 or NULL (the
+ *     generating policy's log-probs for the off-policy correction; see
+ *     grpo_tis).  mask: [B, T] bytes or NULL.  rewards: [B].
  *   grad_out: [B, T, V] in grad_dtype with row stride grad_row_stride >= V;
  *     masked rows are written with zeros.  grad_out may be policy_logits
  *     itself (in place; then grad_dtype, grad_row_stride must equal
@@ -265,9 +285,9 @@ GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, c
  * is 16-byte aligned; other layouts take a slower scalar path. */
 GRPO_API grpo_status grpo_loss_fwd_bwd(const void *policy_logits, const void *ref_logits,
                               int32_t logits_dtype, int64_t row_stride, const void *action_ids,
-                              int32_t ids_dtype, const float *old_logps, const uint8_t *mask,
-                              const float *rewards, int64_t B, int64_t T, int64_t V,
-                              const grpo_groups *groups, const grpo_cfg *cfg, void *grad_out,
+                              int32_t ids_dtype, const float *old_logps, const float *gen_logps,
+                              const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
+                              int64_t V, const grpo_groups *groups, const grpo_cfg *cfg, void *grad_out,
                               int32_t grad_dtype, int64_t grad_row_stride,
                               const float *grad_scale, const grpo_outputs *out, void *ws,
                               size_t ws_bytes, void *stream);

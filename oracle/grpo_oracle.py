@@ -453,10 +453,11 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     gen = None if gen_logp is None else np.asarray(gen_logp, dtype=np.float64)[ii, tt]
     terms = token_terms(lp, old, ref, A[ii], cfg, gen)
     return _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale,
-                     grad=None, logp_active=lp)
+                     grad=None, logp_active=lp, gen_active=gen)
 
 
-def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_active):
+def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_active,
+              gen_active=None):
     P = np.zeros(B)
     K = np.zeros(B)
     C = np.zeros(B, dtype=np.int64)
@@ -484,6 +485,10 @@ def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_activ
     lfull = np.zeros((B, T))
     lfull[ii, tt] = logp_active
     tok["logp"] = lfull
+    if gen_active is not None:        # the input itself, kept for callers that re-evaluate terms
+        gfull = np.zeros((B, T))
+        gfull[ii, tt] = gen_active
+        tok["gen"] = gfull
     if grad is None:
         grad = Gfull.copy()           # token-level: d loss / d logp = m * G
     return OracleResult(loss=loss, policy_loss=policy_loss, kl=kl, advantages=A,
@@ -573,7 +578,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
         if want_grad:
             grad[ii[sl], tt[sl]] = out["grad"]
     res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=grad,
-                    logp_active=acc["logp"])
+                    logp_active=acc["logp"], gen_active=gen)
     return res
 
 

@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 2
+GRPO_ABI_VERSION = 3
 
 GRPO_F32, GRPO_BF16 = 0, 1
 GRPO_I64, GRPO_I32 = 0, 1
@@ -17,6 +17,7 @@ REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE
                    "length_alpha": GRPO_LENGTH_ALPHA, "fixed_constant": GRPO_FIXED_CONSTANT}
 PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 4}
 KL_ESTIMATOR_CODES = {"k3": 0, "k1": 1, "k2": 2}
+TIS_CODES = {None: 0, "tis": 1, "icepop": 2}
 
 GRPO_FAULT_BAD_ACTION = 1
 GRPO_FAULT_NO_TOKENS = 2
@@ -41,7 +42,8 @@ class GrpoCfg(C.Structure):
     _fields_ = [("eps_low", f64), ("eps_high", f64), ("beta", f64), ("reduction", i32),
                 ("alpha", f64), ("pg_loss", i32), ("kl_estimator", i32), ("dual_clip_c", f64),
                 ("sapo_tau_pos", f64), ("sapo_tau_neg", f64), ("kl_input_clamp", f64),
-                ("kl_output_clamp", f64), ("norm_constant", f64)]
+                ("kl_output_clamp", f64), ("norm_constant", f64), ("tis_type", i32),
+                ("tis_ratio_min", f64), ("tis_ratio_max", f64)]
 
 
 class GrpoOutputs(C.Structure):
@@ -56,10 +58,10 @@ SIGNATURES = {
     "grpo_workspace_bytes": (sz, [i64, i64, i32]),
     "grpo_workspace_init": (C.c_int, [vp, sz, vp]),
     "grpo_advantages": (C.c_int, [vp, i64, C.POINTER(GrpoGroups), vp, vp, sz, vp]),
-    "grpo_token_loss": (C.c_int, [vp, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
+    "grpo_token_loss": (C.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
                                   C.POINTER(GrpoCfg), vp, vp, C.POINTER(GrpoOutputs), vp, sz,
                                   vp]),
-    "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, i64, i64, i64,
+    "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, vp, i64, i64, i64,
                                     C.POINTER(GrpoGroups), C.POINTER(GrpoCfg), vp, i32, i64, vp,
                                     C.POINTER(GrpoOutputs), vp, sz, vp]),
     "grpo_loss_bwd": (C.c_int, [vp, i32, i64, vp, i32, vp, i64, i64, i64, vp, i32, i64, vp, vp,

@@ -60,7 +60,7 @@ grpo_status check_groups(const grpo_groups* g, int64_t B) {
   return GRPO_OK;
 }
 
-grpo_status check_cfg(const grpo_cfg* c, bool has_ref) {
+grpo_status check_cfg(const grpo_cfg* c, bool has_ref, bool has_gen) {
   if (!c) return GRPO_ERR_NULL;
   if (!(c->eps_low >= 0.0 && c->eps_low < 1.0)) return GRPO_ERR_CONFIG;
   if (!(c->eps_high >= 0.0) || !isfinite(c->eps_high)) return GRPO_ERR_CONFIG;
@@ -83,11 +83,16 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref) {
     return GRPO_ERR_CONFIG;
   for (double v : {c->kl_input_clamp, c->kl_output_clamp})
     if (v != 0.0 && !(v > 0.0 && isfinite(v))) return GRPO_ERR_CONFIG;
+  if (c->tis_type < GRPO_TIS_NONE || c->tis_type > GRPO_TIS_ICEPOP) return GRPO_ERR_CONFIG;
+  if (c->tis_type != GRPO_TIS_NONE &&
+      !(has_gen && c->tis_ratio_max > 0.0 && isfinite(c->tis_ratio_max) &&
+        c->tis_ratio_min >= 0.0 && c->tis_ratio_min <= c->tis_ratio_max))
+    return GRPO_ERR_CONFIG;
   return GRPO_OK;
 }
 
 // Objective parameters for the kernels (float32, as they compute).
-Objective make_objective(const grpo_cfg* c) {
+Objective make_objective(const grpo_cfg* c, bool has_gen) {
   Objective o{};
   o.lo = float(1.0 - c->eps_low);
   o.hi = float(1.0 + c->eps_high);
@@ -99,8 +104,12 @@ Objective make_objective(const grpo_cfg* c) {
   o.tau_neg = float(c->sapo_tau_neg);
   o.kl_in = float(c->kl_input_clamp);
   o.kl_out = float(c->kl_output_clamp);
+  o.has_is = has_gen ? 1 : 0;
+  o.tis = c->tis_type != GRPO_TIS_NONE ? 1 : 0;
+  o.tis_lo = float(c->tis_ratio_min);
+  o.tis_hi = float(c->tis_ratio_max);
   o.general = (o.pg != GRPO_PG_CLIP || o.kl != GRPO_KL_K3 || c->dual_clip_c != 0.0 ||
-               c->kl_input_clamp != 0.0 || c->kl_output_clamp != 0.0)
+               c->kl_input_clamp != 0.0 || c->kl_output_clamp != 0.0 || has_gen)
                   ? 1
                   : 0;
   return o;
@@ -253,7 +262,7 @@ grpo_status grpo_advantages(const float* rewards, int64_t B, const grpo_groups* 
 }
 
 grpo_status grpo_token_loss(const float* logp, const float* old_logp, const float* ref_logp,
-                            const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
+                            const float* gen_logp, const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
                             const grpo_groups* groups, const grpo_cfg* cfg, float* dlogp_out,
                             const float* grad_scale, const grpo_outputs* out, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -262,7 +271,7 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   if (!mul_ok(B, T, kMaxElems, &rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
   grpo_status st = check_groups(groups, B);
   if (st != GRPO_OK) return st;
-  st = check_cfg(cfg, ref_logp != nullptr);
+  st = check_cfg(cfg, ref_logp != nullptr, gen_logp != nullptr);
   if (st != GRPO_OK) return st;
   const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
   Ws w;
@@ -275,10 +284,11 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.logp = logp;
   a.old = old_logp;
   a.ref = ref_logp;
+  a.gen = gen_logp;
   a.mask = mask;
   a.B = B;
   a.T = T;
-  a.obj = make_objective(cfg);
+  a.obj = make_objective(cfg, gen_logp != nullptr);
   a.grad_scale = grad_scale;
   a.dlogp = dlogp_out;
   a.hdr = w.hdr();
@@ -340,9 +350,9 @@ static bool rows_vectorizable(const void* x, const void* y, int64_t ld, int32_t 
 
 grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
                               int32_t logits_dtype, int64_t row_stride, const void* action_ids,
-                              int32_t ids_dtype, const float* old_logps, const uint8_t* mask,
-                              const float* rewards, int64_t B, int64_t T, int64_t V,
-                              const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
+                              int32_t ids_dtype, const float* old_logps, const float* gen_logps,
+                              const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
+                              int64_t V, const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
                               int32_t grad_dtype, int64_t grad_row_stride,
                               const float* grad_scale, const grpo_outputs* out, void* ws,
                               size_t ws_bytes, void* stream) {
@@ -354,7 +364,7 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   if (st != GRPO_OK) return st;
   st = check_groups(groups, B);
   if (st != GRPO_OK) return st;
-  st = check_cfg(cfg, ref_logits != nullptr);
+  st = check_cfg(cfg, ref_logits != nullptr, gen_logps != nullptr);
   if (st != GRPO_OK) return st;
   st = check_alias(policy_logits, ref_logits, logits_dtype, row_stride, rows, V, grad_out,
                    grad_dtype, grad_row_stride);
@@ -375,11 +385,12 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.ids = action_ids;
   a.ids_i32 = ids_dtype == GRPO_I32 ? 1 : 0;
   a.old = old_logps;
+  a.gen = gen_logps;
   a.mask = mask;
   a.T = T;
   a.V = V;
   a.rows = rows;
-  a.obj = make_objective(cfg);
+  a.obj = make_objective(cfg, gen_logps != nullptr);
   a.grad_scale = grad_scale;
   a.g = grad_out;
   a.ldg = grad_out ? grad_row_stride : 0;

@@ -63,7 +63,10 @@ struct Objective {
   int32_t general;
   float dual_c;       // dual-clip bound; 0: off
   float tau_pos, tau_neg;
-  float kl_in, kl_out;  // clamps; +inf: off
+  float kl_in, kl_out;  // clamps; 0: off
+  int32_t has_is;     // off-policy weight exp(old - gen) on the policy term
+  int32_t tis;        // truncate that weight to [tis_lo, tis_hi]
+  float tis_lo, tis_hi;
 };
 
 // Group / advantage / weight preparation.
@@ -99,6 +102,7 @@ struct RowArgs {
   const void* ids;
   int32_t ids_i32;
   const float* old;
+  const float* gen;         // generating policy's log-probs, or null
   const uint8_t* mask;
   int64_t T, V, rows;
   Objective obj;
@@ -164,6 +168,7 @@ struct TokenArgs {
   const float* logp;
   const float* old;
   const float* ref;         // null when beta == 0
+  const float* gen;         // null: no off-policy weight
   const uint8_t* mask;
   int64_t B, T;
   Objective obj;

@@ -6,8 +6,8 @@
 // algorithms: the clipped surrogate, its dual clip, REINFORCE and the
 // on-policy form; CISPO) and the Relax REINFORCE++ page (Formula-level
 // comparison: SAPO's soft sigmoid gate).  KL estimators follow dockyard_rl
-// (Reference-KL penalty).  Everything is float32, as the rest of the row
-// epilogue.
+// (Reference-KL penalty), the off-policy weight its Off-policy correction
+// section.  Everything is float32, as the rest of the row epilogue.
 #pragma once
 
 #include <math.h>
@@ -34,7 +34,7 @@ __device__ __forceinline__ float clamp_sym(float x, float v) {
 // settings both evaluate the same expressions in the same order.
 template <bool kGeneral>
 __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp, float old,
-                                                  float d, float adv) {
+                                                  float d, float adv, float gen) {
 #pragma clang fp contract(off)
   TokObj r;
   const float rho = expf(logp - old);
@@ -86,6 +86,13 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
     } else {  // GRPO_PG_ON_POLICY: rho = exp(logp - sg(logp)) = 1
       r.loss = -adv;
       dloss = -adv;
+    }
+    if (o.has_is) {
+      // constant weight of the current to the generating policy
+      float wi = expf(old - gen);
+      if (o.tis) wi = wi != wi ? wi : fminf(fmaxf(wi, o.tis_lo), o.tis_hi);
+      r.loss = r.loss * wi;
+      dloss = dloss * wi;
     }
 
     bool pass = true;

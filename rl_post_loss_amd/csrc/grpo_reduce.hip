@@ -104,12 +104,14 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   const float adv = a.A[i];
   const float wg = float(a.w[i]) * (a.grad_scale ? *a.grad_scale : 1.0f);
   const bool has_ref = a.ref != nullptr;
+  const bool has_gen = a.gen != nullptr;
   double p = 0.0, k = 0.0;
   long long c = 0;
   bool nonfinite = false;
   const bool vec = (a.T & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.logp) |
                                        reinterpret_cast<uintptr_t>(a.old) |
                                        reinterpret_cast<uintptr_t>(a.ref) |
+                                       reinterpret_cast<uintptr_t>(a.gen) |
                                        reinterpret_cast<uintptr_t>(a.dlogp) |
                                        reinterpret_cast<uintptr_t>(a.out_loss) |
                                        reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     const int64_t n4 = a.T / 4;
     for (int64_t q0 = tid; q0 < n4; q0 += QU * kRedThreads) {
       uint32_t m4[QU];
-      f32x4 lp[QU], od[QU], rf[QU];
+      f32x4 lp[QU], od[QU], rf[QU], gn[QU];
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
         const int64_t q = q0 + int64_t(u) * kRedThreads;
@@ -133,11 +135,12 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
         const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
-        lp[u] = od[u] = rf[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lp[u] = od[u] = rf[u] = gn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (m4[u] != 0) {
           lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
           od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
           if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
+          if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
         }
       }
 #pragma unroll
@@ -148,12 +151,13 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
         const float lpv[4] = {lp[u].x, lp[u].y, lp[u].z, lp[u].w};
         const float odv[4] = {od[u].x, od[u].y, od[u].z, od[u].w};
         const float rfv[4] = {rf[u].x, rf[u].y, rf[u].z, rf[u].w};
+        const float gnv[4] = {gn[u].x, gn[u].y, gn[u].z, gn[u].w};
         float gv[4] = {0.f, 0.f, 0.f, 0.f}, tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if ((m4[u] >> (8 * j)) & 0xffu) {
             const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
-            const TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv);
+            const TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv, gnv[j]);
             gv[j] = wg * r.g;
             tl[j] = r.loss;
             tk[j] = r.kl;
@@ -177,7 +181,8 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
       if (a.mask == nullptr || a.mask[s] != 0) {
         const float lps = a.logp[s];
         const float d = has_ref ? a.ref[s] - lps : 0.0f;
-        const TokObj r = token_objective<kGeneral>(a.obj, lps, a.old[s], d, adv);
+        const TokObj r = token_objective<kGeneral>(a.obj, lps, a.old[s], d, adv,
+                                                   has_gen ? a.gen[s] : 0.0f);
         g = wg * r.g;
         tl = r.loss;
         tk = r.kl;

@@ -226,10 +226,10 @@ struct RowGrad {
 
 __device__ __forceinline__ RowGrad row_epilogue(const RowArgs& a, int64_t row, Lse sx, Lse sy,
                                                 float xa, float ya, bool has_ref, float old,
-                                                float adv, float wgt, float gs) {
+                                                float gen, float adv, float wgt, float gs) {
   const RowLogp px = finish_row(sx, xa);
   const float d = has_ref ? row_log_ratio(px, finish_row(sy, ya)) : 0.0f;
-  const TokObj t = token_objective<true>(a.obj, px.logp, old, d, adv);
+  const TokObj t = token_objective<true>(a.obj, px.logp, old, d, adv, gen);
   const float G = wgt * gs * t.g;
   if (!(isfinite(t.loss) && isfinite(t.kl) && isfinite(G))) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
   a.tok_loss[row] = t.loss;

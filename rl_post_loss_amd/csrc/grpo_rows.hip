@@ -93,9 +93,10 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
                                : nullptr;
 
     // per-token side inputs, loaded early by the finishing lane
-    float old = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f;
+    float old = 0.0f, gen = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f;
     if (lid == 0) {
       old = a.old[row];
+      if (a.gen) gen = a.gen[row];
       const int64_t i = row / a.T;
       adv = a.A[i];
       wgt = float(a.w[i]);
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
 
     // ---- per-token epilogue -------------------------------------------------
     if (lid == 0) {
-      const RowGrad rg = row_epilogue(a, row, sx, sy, xa, ya, has_ref, old, adv, wgt, gs);
+      const RowGrad rg = row_epilogue(a, row, sx, sy, xa, ya, has_ref, old, gen, adv, wgt, gs);
       G = rg.G;
       c2 = rg.c2;
       omp = rg.omp;

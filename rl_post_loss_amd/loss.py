@@ -101,7 +101,8 @@ def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_b
 # (the clipped surrogate with the k3 estimator).
 OBJECTIVE_DEFAULTS = dict(pg_loss="clip", kl_estimator="k3", dual_clip_c=None, sapo_tau_pos=1.0,
                           sapo_tau_neg=1.0, kl_input_clamp=None, kl_output_clamp=None,
-                          norm_constant=None)
+                          norm_constant=None, tis_type=None, tis_ratio_min=None,
+                          tis_ratio_max=None)
 
 
 def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, objective):
@@ -127,7 +128,7 @@ def _optional_positive(name, v):
 
 def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, *, pg_loss, kl_estimator,
               dual_clip_c, sapo_tau_pos, sapo_tau_neg, kl_input_clamp, kl_output_clamp,
-              norm_constant):
+              norm_constant, tis_type, tis_ratio_min, tis_ratio_max):
     c = GrpoCfg()
     c.eps_low = float(clip_eps if eps_low is None else eps_low)
     c.eps_high = float(clip_eps if eps_high is None else eps_high)
@@ -148,6 +149,14 @@ def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, *, pg_loss, k
     c.kl_input_clamp = _optional_positive("kl_input_clamp", kl_input_clamp)
     c.kl_output_clamp = _optional_positive("kl_output_clamp", kl_output_clamp)
     c.norm_constant = _optional_positive("norm_constant", norm_constant)
+    if tis_type not in _abi.TIS_CODES:
+        raise ValueError(f"unknown tis_type {tis_type!r}")
+    c.tis_type = _abi.TIS_CODES[tis_type]
+    if tis_type is not None:
+        _need(tis_ratio_max is not None, "truncated IS needs tis_ratio_max")
+        _need(tis_type == "tis" or tis_ratio_min is not None, "icepop needs tis_ratio_min")
+        c.tis_ratio_min = 0.0 if tis_ratio_min is None else float(tis_ratio_min)
+        c.tis_ratio_max = float(tis_ratio_max)
     return c
 
 
@@ -267,20 +276,24 @@ def grpo_advantages(rewards, *, samples_per_prompt=None, group_boundaries=None,
     return out
 
 
-def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *,
+def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *, gen_logps=None,
                     clip_eps=0.2, eps_low=None, eps_high=None, beta=0.04,
                     samples_per_prompt=None, group_boundaries=None, leave_one_out=False,
                     scale_by_std=True, std_eps=1e-6, reduction="token_mean", alpha=None,
                     want_grad=True, grad_scale=None, per_token=False, out=None, **objective):
     """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp.
     ``out``: a previous result of the same sizes whose buffers are reused.
+    ``gen_logps``: the generating policy's log-probs [B, T] float32, for the
+    off-policy importance weight (None: no correction).
     ``objective``: the keywords of OBJECTIVE_DEFAULTS (policy-loss form, KL
-    estimator, dual clip, SAPO temperatures, KL clamps, fixed normaliser)."""
+    estimator, dual clip, SAPO temperatures, KL clamps, fixed normaliser,
+    truncation of the importance weight)."""
     lib = load_library()
     dev = logp.device
     _need(logp.dim() == 2 and logp.is_cuda, "logp must be a [B, T] GPU tensor")
     B, T = logp.shape
-    for name, t in (("logp", logp), ("old_logps", old_logps), ("ref_logps", ref_logps)):
+    for name, t in (("logp", logp), ("old_logps", old_logps), ("ref_logps", ref_logps),
+                    ("gen_logps", gen_logps)):
         if t is None:
             continue
         _need(t.dtype == torch.float32 and tuple(t.shape) == (B, T) and t.is_contiguous()
@@ -301,7 +314,8 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
     if not want_grad:
         res.grad = None
     ws, wsb = workspace(B, T, ng, dev)
-    check(lib.grpo_token_loss(logp.data_ptr(), old_logps.data_ptr(), _ptr(ref_logps), mptr,
+    check(lib.grpo_token_loss(logp.data_ptr(), old_logps.data_ptr(), _ptr(ref_logps),
+                              _ptr(gen_logps), mptr,
                               rewards.contiguous().data_ptr(), B, T, C.byref(g), C.byref(cfg),
                               _ptr(res.grad), _ptr(grad_scale), C.byref(o), ws.data_ptr(), wsb,
                               _stream_ptr(dev)), lib)
@@ -309,7 +323,7 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
 
 
 def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
-                      completion_mask=None, *, clip_eps=0.2, eps_low=None, eps_high=None,
+                      completion_mask=None, *, gen_logps=None, clip_eps=0.2, eps_low=None, eps_high=None,
                       beta=0.04, samples_per_prompt=None, group_boundaries=None,
                       leave_one_out=False, scale_by_std=True, std_eps=1e-6,
                       reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
@@ -320,7 +334,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     default the logits dtype); a tensor writes into it (it may be
     ``policy_logits`` itself, in place); False runs the forward only.
     out: a previous result of the same sizes whose output buffers are reused.
-    objective: the keywords of OBJECTIVE_DEFAULTS, as for grpo_token_loss.
+    gen_logps, objective: as for grpo_token_loss.
     """
     lib = load_library()
     dev = policy_logits.device
@@ -338,6 +352,10 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     _need(old_logps.dtype == torch.float32 and tuple(old_logps.shape) == (B, T)
           and old_logps.is_contiguous() and old_logps.device == dev,
           "old_logps must be contiguous float32 [B, T]")
+    if gen_logps is not None:
+        _need(gen_logps.dtype == torch.float32 and tuple(gen_logps.shape) == (B, T)
+              and gen_logps.is_contiguous() and gen_logps.device == dev,
+              "gen_logps must be contiguous float32 [B, T]")
     _need(rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,) and rewards.device == dev,
           "rewards must be float32 [B]")
     mptr, _ = _mask_ptr(completion_mask, B, T, dev)
@@ -366,7 +384,8 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
         ws, wsb = _ws
     check(lib.grpo_loss_fwd_bwd(policy_logits.data_ptr(), _ptr(ref_logits),
                                 _FDTYPE[policy_logits.dtype], ld, action_ids.data_ptr(),
-                                _IDTYPE[action_ids.dtype], old_logps.data_ptr(), mptr,
+                                _IDTYPE[action_ids.dtype], old_logps.data_ptr(),
+                                _ptr(gen_logps), mptr,
                                 rewards.contiguous().data_ptr(), B, T, V, C.byref(g), C.byref(cfg),
                                 gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o), ws.data_ptr(),
                                 wsb, _stream_ptr(dev)), lib)

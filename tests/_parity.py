@@ -105,7 +105,7 @@ def _terms_at(ref, cfg, dlogp=0.0, dd=0.0):
         old = np.where(act, t["logp"] - np.log(np.where(act, t["rho"], 1.0)), 0.0)
         lp = t["logp"] + dlogp
         lref = t["logp"] + t["d"] + dlogp + dd
-        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg)
+        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg, t.get("gen"))
     for k, v in out.items():
         out[k] = np.where(act, v, np.zeros_like(v))
     return out
@@ -163,7 +163,8 @@ def g_rel_tolerance(ref, cfg, base):
     dG = _propagated(ref, cfg, lambda t: _G_of(ref, cfg, t), 2 * LOGP_ABS_ERR, 4 * LOGP_ABS_ERR)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(G != 0, dG / np.abs(G), np.inf)
-    return np.maximum(base, rel), rel > base
+    # rows with G = 0 are compared at the absolute floor, not counted here
+    return np.maximum(base, rel), (rel > base) & (G != 0)
 
 
 def value_bounds(ref, cfg, e_logp=LOGP_ABS_ERR, e_d=2 * LOGP_ABS_ERR):

@@ -108,13 +108,14 @@ FAKE_WS = 0x20000000
 
 
 def _fwd(lib, B=8, T=4, V=32, g=None, cfg=None, ref=FAKE, grad=FAKE + 0x4000000, ws=FAKE_WS,
-         ws_bytes=1 << 30, ld=None, gld=None, dtype=0, gdtype=0, ids_dtype=0, scalars=FAKE):
+         ws_bytes=1 << 30, ld=None, gld=None, dtype=0, gdtype=0, ids_dtype=0, scalars=FAKE,
+         gen=None):
     if g is None:
         g, _ = _groups()
     cfg = cfg or _cfg()
     o = _abi.GrpoOutputs()
     o.scalars = scalars
-    return lib.grpo_loss_fwd_bwd(FAKE, ref, dtype, ld or V, FAKE, ids_dtype, FAKE, None, FAKE,
+    return lib.grpo_loss_fwd_bwd(FAKE, ref, dtype, ld or V, FAKE, ids_dtype, FAKE, gen, None, FAKE,
                                  B, T, V, C.byref(g), C.byref(cfg), grad, gdtype, gld or V, None,
                                  C.byref(o), ws, ws_bytes, None)
 
@@ -164,6 +165,13 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, cfg=_cfg(pg_loss=2, sapo_tau_neg=0.0)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(kl_input_clamp=-1.0)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(kl_output_clamp=float("nan"))) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=1, tis_ratio_max=2.0)) == E["GRPO_ERR_CONFIG"]  # no gen
+    assert _fwd(lib, cfg=_cfg(tis_type=3, tis_ratio_max=2.0), gen=FAKE) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=2, tis_ratio_max=0.0), gen=FAKE) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=2, tis_ratio_min=3.0, tis_ratio_max=2.0),
+                gen=FAKE) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=1, tis_ratio_min=-1.0, tis_ratio_max=2.0),
+                gen=FAKE) == E["GRPO_ERR_CONFIG"]
     # aliasing: in place with another dtype or stride, partial overlap
     assert _fwd(lib, grad=FAKE, gdtype=1) == E["GRPO_ERR_ALIAS"]
     assert _fwd(lib, grad=FAKE + 64) == E["GRPO_ERR_ALIAS"]
@@ -183,13 +191,15 @@ def test_token_loss_and_advantages_validation():
     o = _abi.GrpoOutputs()
     o.scalars = FAKE
     call = lambda **k: lib.grpo_token_loss(
-        k.get("logp", FAKE), FAKE, k.get("ref", FAKE), None, FAKE, k.get("B", 8), k.get("T", 4),
+        k.get("logp", FAKE), FAKE, k.get("ref", FAKE), k.get("gen"), None, FAKE, k.get("B", 8),
+        k.get("T", 4),
         C.byref(k.get("g", g)), C.byref(k.get("cfg", cfg)), FAKE, None, C.byref(o),
         k.get("ws", FAKE_WS), k.get("wsb", 1 << 30), None)
     assert call(logp=None) == E["GRPO_ERR_NULL"]
     assert call(T=0) == E["GRPO_ERR_SHAPE"]
     assert call(B=6) == E["GRPO_ERR_GROUPS"]
     assert call(ref=None) == E["GRPO_ERR_CONFIG"]           # beta > 0 needs ref
+    assert call(cfg=_cfg(tis_type=2, tis_ratio_min=0.5, tis_ratio_max=2.0)) == E["GRPO_ERR_CONFIG"]
     assert call(wsb=10) == E["GRPO_ERR_WORKSPACE"]
     assert lib.grpo_advantages(FAKE, 8, C.byref(_groups(spp=3)[0]), FAKE, FAKE_WS, 1 << 20,
                                None) == E["GRPO_ERR_GROUPS"]

@@ -1,5 +1,6 @@
 """Parity of the objective variants (policy-loss forms, KL estimators, KL
-clamps, the fixed-constant normaliser) on the HIP path, through the C ABI,
+clamps, the fixed-constant normaliser, the truncated off-policy importance
+weight) on the HIP path, through the C ABI,
 against the fp64 oracle: logits entry point on each row-kernel path (wave per
 row, resident row, streaming row) and the log-prob token entry point."""
 
@@ -13,7 +14,8 @@ import torch
 import oracle
 from _parity import (branch_ambiguity, cfg_from, compare_exact_parts, compare_logits_grad,
                      compare_scalars, compare_token_values, gpu_kwargs, host_inputs, to_np)
-from workloads import TOKEN_WORKLOADS, LogitsWorkload, make_logits_inputs, make_token_inputs
+from workloads import (TOKEN_WORKLOADS, LogitsWorkload, make_gen_logps, make_logits_inputs,
+                       make_token_inputs)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -35,6 +37,11 @@ VARIANTS = [
     dict(kl_input_clamp=0.3, kl_output_clamp=0.02),
     dict(reduction="fixed_constant", norm_constant=4096.0),
     dict(reduction="length_alpha", alpha=0.5, pg_loss="cispo"),
+    # off-policy importance weight (the generating policy's log-probs are an input)
+    dict(is_only=True),
+    dict(tis_type="tis", tis_ratio_max=1.3),
+    dict(tis_type="icepop", tis_ratio_min=0.8, tis_ratio_max=1.25, pg_loss="cispo"),
+    dict(tis_type="tis", tis_ratio_min=0.5, tis_ratio_max=2.0, dual_clip_c=1.5, kl_estimator="k2"),
 ]
 
 
@@ -55,27 +62,33 @@ def _wl(V, dtype, T=16, sizes=(4, 4, 4, 4), **kw):
 
 
 def _split(kw):
+    """(reduction, alpha, whether the case takes generating log-probs, objective keywords)"""
     kw = dict(kw)
     red = kw.pop("reduction", None)
     alpha = kw.pop("alpha", None)
-    return red, alpha, kw
+    use_gen = kw.pop("is_only", False) or "tis_type" in kw
+    return red, alpha, use_gen, kw
 
 
 def check_variant_logits(rpl, wl, kw, seed=0):
-    red, alpha, obj = _split(kw)
+    red, alpha, use_gen, obj = _split(kw)
     if alpha is not None:
         wl = dataclasses.replace(wl, alpha=alpha)
     announce(f"variant logits {wl.name} {_id(kw)} seed={seed}")
     inp_cpu = make_logits_inputs(wl, device="cpu", seed=seed)
+    if use_gen:
+        inp_cpu["gen_logps"] = make_gen_logps(inp_cpu["old_logps"], seed=seed)
     inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
     gkw = gpu_kwargs(wl, red, **obj)
     res = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
-                                inp["rewards"], inp["mask"], per_token=True, **gkw)
+                                inp["rewards"], inp["mask"], per_token=True,
+                                gen_logps=inp.get("gen_logps"), **gkw)
     torch.cuda.synchronize()
     h = host_inputs(inp_cpu)
     cfg = cfg_from(wl, red, **obj)
     ref = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
-                                   h["mask"], h["rewards"], groups=wl.groups_kwargs(), cfg=cfg)
+                                   h["mask"], h["rewards"], groups=wl.groups_kwargs(), cfg=cfg,
+                                   gen_logps=h.get("gen_logps"))
     bf16 = wl.dtype == "bf16"
     rtol = 1e-4 if bf16 else 1e-5
     compare_exact_parts(res, ref, wl.name)
@@ -98,7 +111,8 @@ def test_variant_logits_small_rows(gpu_lib, kw, V, dtype):
     check_variant_logits(gpu_lib, _wl(V, dtype), kw)
 
 
-@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[4], VARIANTS[11]], ids=_id)
+@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[4], VARIANTS[11], VARIANTS[16]],
+                         ids=_id)
 @pytest.mark.parametrize("V", [32000, 151936])
 def test_variant_logits_long_rows(gpu_lib, kw, V):
     """Resident-row kernel (V = 32000 bf16) and streaming kernel (V = 151936 bf16)."""
@@ -130,15 +144,18 @@ def test_variant_autograd_split_passes(gpu_lib):
 # ---------------------------------------------------------------------------
 
 def check_variant_tokens(rpl, kw, B=64, T=257, seed=0):
-    red, alpha, obj = _split(kw)
+    red, alpha, use_gen, obj = _split(kw)
     base = TOKEN_WORKLOADS["token_loss_ragged"]
     wl = dataclasses.replace(base, old_noise_std=0.7, beta=0.1)
     announce(f"variant tokens {_id(kw)} B={B} T={T}")
     inp_cpu = make_token_inputs(wl, device="cpu", seed=seed, B=B, T=T)
+    if use_gen:
+        inp_cpu["gen_logps"] = make_gen_logps(inp_cpu["old_logps"], seed=seed)
     inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
     red = red or wl.reduction
     res = rpl.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
-                              inp["mask"], eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
+                              inp["mask"], gen_logps=inp.get("gen_logps"), eps_low=wl.eps_low,
+                              eps_high=wl.eps_high, beta=wl.beta,
                               samples_per_prompt=wl.group_size, reduction=red, alpha=alpha,
                               per_token=True, **obj)
     torch.cuda.synchronize()
@@ -147,7 +164,7 @@ def check_variant_tokens(rpl, kw, B=64, T=257, seed=0):
                             reduction=red, alpha=alpha, **obj)
     ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"],
                                  h["rewards"], groups=dict(samples_per_prompt=wl.group_size),
-                                 cfg=cfg)
+                                 cfg=cfg, gen_logp=h.get("gen_logps"))
     # float32 inputs: only the float32 arithmetic of the kernel separates it
     # from the oracle (a few ulp in the ratio and in d)
     e = 2.0 ** -21
@@ -172,6 +189,6 @@ def test_variant_tokens_vector_path(gpu_lib, kw):
     check_variant_tokens(gpu_lib, kw, T=256)
 
 
-@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[3], VARIANTS[11]], ids=_id)
+@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[3], VARIANTS[11], VARIANTS[17]], ids=_id)
 def test_variant_tokens_scalar_path(gpu_lib, kw):
     check_variant_tokens(gpu_lib, kw, B=32, T=131, seed=1)

@@ -24,6 +24,7 @@ VARIANTS = [
     dict(pg_loss="on_policy"),
     dict(kl_input_clamp=0.2, kl_output_clamp=0.02),
     dict(reduction="fixed_constant", norm_constant=50.0),
+    dict(tis_type="icepop", tis_ratio_min=0.7, tis_ratio_max=1.4, pg_loss="cispo"),
 ]
 
 
@@ -53,8 +54,9 @@ def _as_result(ref, grad_dtype=torch.float32):
 def test_helpers_accept_rounded_oracle(kw):
     cfg = oracle.LossConfig(beta=0.1, **kw)
     x, y, ids, old, mask, r = _case(3)
+    gen = old + np.random.default_rng(9).normal(0, 0.4, old.shape) if "tis_type" in kw else None
     ref = oracle.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2),
-                                   cfg=cfg)
+                                   cfg=cfg, gen_logps=gen)
     for dt, bf16 in ((torch.float32, False), (torch.bfloat16, True)):
         res = _as_result(ref, dt)
         compare_scalars(res, ref, cfg, 1e-5)

@@ -6,6 +6,7 @@ from .synth import (  # noqa: F401
     LogitsWorkload,
     TokenWorkload,
     make_logits_inputs,
+    make_gen_logps,
     make_token_inputs,
     poison_masked,
 )

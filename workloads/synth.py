@@ -239,6 +239,14 @@ def make_token_inputs(wl: TokenWorkload, device="cpu", seed=0, B=None, T=None):
                 rewards=rewards, mask=mask)
 
 
+def make_gen_logps(old_logps, seed=0, std=0.3):
+    """Log-probs of a generating policy a little older than the one behind
+    old_logps: old + N(0, std^2) per token, seeded."""
+    g = _gen(old_logps.device, seed + 7919)
+    noise = torch.randn(old_logps.shape, generator=g, device=old_logps.device) * std
+    return (old_logps.float() + noise).contiguous()
+
+
 def poison_masked(inputs, V=None):
     """Write NaN/+-Inf into every masked slot's logits rows and old log-probs
     and out-of-range ids into masked action ids (masked slots must never be
