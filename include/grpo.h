@@ -92,8 +92,11 @@ typedef enum grpo_status {
   GRPO_ERR_HIP = 8         /* a HIP runtime call or kernel launch failed */
 } grpo_status;
 
-/* Floating-point storage of logits and gradients. */
-typedef enum grpo_fdtype { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_fdtype;
+/* Floating-point storage of logits and gradients.  Supported (logits ->
+ * gradient) pairs: F32 -> F32 | BF16, BF16 -> BF16 | F32, F16 -> F16 | F32;
+ * others return GRPO_ERR_DTYPE.  Arithmetic is float32 for every storage;
+ * 16-bit gradients round to nearest even. */
+typedef enum grpo_fdtype { GRPO_F32 = 0, GRPO_BF16 = 1, GRPO_F16 = 2 } grpo_fdtype;
 
 /* Integer storage of action ids. */
 typedef enum grpo_idtype { GRPO_I64 = 0, GRPO_I32 = 1 } grpo_idtype;

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
 GRPO_ABI_VERSION = 3
 
-GRPO_F32, GRPO_BF16 = 0, 1
+GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
 GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA, GRPO_FIXED_CONSTANT = 0, 1, 2, 3
 REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE_MEAN,

@@ -17,7 +17,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream);
 hipError_t launch_final(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
-bool resident_fits(int64_t V, int tin_bf16);
+bool resident_fits(int64_t V, int esize);
 }  // namespace grpo
 
 using namespace grpo;
@@ -186,7 +186,17 @@ grpo_status run_final(const Ws& w, int64_t B, double beta, const grpo_outputs* o
   return launch_final(f, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
-int fdtype_size(int32_t dt) { return dt == GRPO_F32 ? 4 : (dt == GRPO_BF16 ? 2 : 0); }
+int fdtype_size(int32_t dt) {
+  return dt == GRPO_F32 ? 4 : ((dt == GRPO_BF16 || dt == GRPO_F16) ? 2 : 0);
+}
+
+// Supported (logits, gradient) storage pairs: a float32 gradient from any
+// logits; a bf16 gradient from f32 or bf16 logits; an f16 gradient from f16.
+bool dtype_pair_ok(int32_t x, int32_t g) {
+  if (g == GRPO_F32) return true;
+  if (g == GRPO_BF16) return x == GRPO_F32 || x == GRPO_BF16;
+  return g == GRPO_F16 && x == GRPO_F16;
+}
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -313,7 +323,8 @@ static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype
   if (!policy || !action_ids) return GRPO_ERR_NULL;
   if (fdtype_size(logits_dtype) == 0 || (ids_dtype != GRPO_I64 && ids_dtype != GRPO_I32))
     return GRPO_ERR_DTYPE;
-  if (grad_out && fdtype_size(grad_dtype) == 0) return GRPO_ERR_DTYPE;
+  if (grad_out && (fdtype_size(grad_dtype) == 0 || !dtype_pair_ok(logits_dtype, grad_dtype)))
+    return GRPO_ERR_DTYPE;
   int64_t tmp;
   if (!mul_ok(B, T, kMaxElems, rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
   if (V <= 0 || row_stride < V || !mul_ok(*rows, row_stride, kMaxElems, &tmp))
@@ -406,15 +417,15 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.out_kl = out->tok_kl;
   RowLaunch l{};
   l.mode = grad_out ? 0 : 1;
-  l.tin_bf16 = logits_dtype == GRPO_BF16;
-  l.tg_bf16 = grad_out ? (grad_dtype == GRPO_BF16) : l.tin_bf16;
+  l.tin = logits_dtype;
+  l.tg = grad_out ? grad_dtype : logits_dtype;
   l.nt = choose_nt(V, fdtype_size(logits_dtype));
   l.vec = rows_vectorizable(policy_logits, ref_logits, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);
   // rows above 4 KB that fit one block's registers keep the policy row
   // resident between the passes (fused mode); longer rows stream
   l.resident = GRPO_RESIDENT && grad_out && l.vec && V * fdtype_size(logits_dtype) > 4096 &&
-               resident_fits(V, l.tin_bf16);
+               resident_fits(V, fdtype_size(logits_dtype));
   const bool timed = g_ev_start && g_ev_stop;
   if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
   if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;
@@ -472,8 +483,8 @@ grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64
   a.stash = w.at<RowStash>(w.l.stash);
   RowLaunch l{};
   l.mode = 2;
-  l.tin_bf16 = logits_dtype == GRPO_BF16;
-  l.tg_bf16 = grad_dtype == GRPO_BF16;
+  l.tin = logits_dtype;
+  l.tg = grad_dtype;
   l.nt = choose_nt(V, fdtype_size(logits_dtype));
   l.vec = rows_vectorizable(policy_logits, nullptr, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);

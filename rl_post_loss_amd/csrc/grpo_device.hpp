@@ -31,6 +31,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return uint16_t(pack_bf16x2(x, 0.0f) & 0xffffu);
 }
 
+// IEEE binary16: -> f32 is exact (v_cvt_f32_f16); f32 -> f16 rounds to
+// nearest even in the default rounding mode.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f2 f16x2_to_f32(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(h2, w), f2);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return float(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+  return __builtin_bit_cast(uint16_t, _Float16(x));
+}
+
 // Raw 2^x (v_exp_f32).  Results below the normal range flush to zero; every
 // caller only feeds it arguments whose tiny results do not matter.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

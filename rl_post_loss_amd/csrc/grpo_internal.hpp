@@ -126,8 +126,8 @@ struct RowArgs {
 // Row-kernel instantiation choice.
 struct RowLaunch {
   int mode;      // 0 fused forward+backward, 1 forward only, 2 backward only
-  int tin_bf16;  // logits are bf16 (else f32)
-  int tg_bf16;   // gradient is bf16 (else f32)
+  int tin;       // logits storage (grpo_fdtype)
+  int tg;        // gradient storage (grpo_fdtype)
   int nt;        // threads per row: 64, 256, 512 or 1024
   int vec;       // every row is 16-byte aligned: 16-byte chunks
   int resident;  // fused mode with the policy row held in registers

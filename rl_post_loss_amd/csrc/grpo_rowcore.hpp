@@ -48,6 +48,33 @@ template <> struct In<float, true> {  // f32, 4 per 16 bytes
   }
 };
 
+template <> struct In<_Float16, true> {  // f16, 8 per 16 bytes
+  static constexpr int N = 8;
+  typedef u32x4 raw_t;
+  __device__ static raw_t load(const void* row, int64_t c) {
+    return reinterpret_cast<const raw_t*>(row)[c];
+  }
+  __device__ static raw_t load_nt(const void* row, int64_t c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const raw_t*>(row) + c);
+  }
+  __device__ static void cvt(raw_t r, float (&f)[N]) {
+    const f2 a = f16x2_to_f32(r.x), b = f16x2_to_f32(r.y), c = f16x2_to_f32(r.z),
+             d = f16x2_to_f32(r.w);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+  }
+};
+
+template <> struct In<_Float16, false> {
+  static constexpr int N = 1;
+  typedef uint16_t raw_t;
+  __device__ static raw_t load(const void* row, int64_t c) {
+    return reinterpret_cast<const uint16_t*>(row)[c];
+  }
+  __device__ static raw_t load_nt(const void* row, int64_t c) { return load(row, c); }
+  __device__ static void cvt(raw_t r, float (&f)[N]) { f[0] = f16_to_f32(r); }
+};
+
 template <> struct In<uint16_t, false> {
   static constexpr int N = 1;
   typedef uint16_t raw_t;
@@ -73,6 +100,9 @@ __device__ __forceinline__ float load_one(const void* row, int64_t v, uint16_t*)
 }
 __device__ __forceinline__ float load_one(const void* row, int64_t v, float*) {
   return reinterpret_cast<const float*>(row)[v];
+}
+__device__ __forceinline__ float load_one(const void* row, int64_t v, _Float16*) {
+  return f16_to_f32(reinterpret_cast<const uint16_t*>(row)[v]);
 }
 
 // Store N gradient values of type TG at chunk c (N consecutive elements).
@@ -102,6 +132,22 @@ template <int N> struct Out<uint16_t, N> {
       reinterpret_cast<uint16_t*>(row)[c] = 0;
     }
   }
+};
+
+template <int N> struct Out<_Float16, N> {
+  __device__ static void store(void* row, int64_t c, const float (&g)[N]) {
+    if constexpr (N == 8) {
+      u32x4 v = {pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]), pack_f16x2(g[4], g[5]),
+                 pack_f16x2(g[6], g[7])};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(row) + c);
+    } else if constexpr (N == 4) {
+      u32x2 v = {pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3])};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(row) + c);
+    } else {
+      reinterpret_cast<uint16_t*>(row)[c] = f32_to_f16(g[0]);
+    }
+  }
+  __device__ static void zero(void* row, int64_t c) { Out<uint16_t, N>::zero(row, c); }
 };
 
 template <int N> struct Out<float, N> {
@@ -138,6 +184,9 @@ __device__ __forceinline__ void store_one(void* row, int64_t v, float g, uint16_
 }
 __device__ __forceinline__ void store_one(void* row, int64_t v, float g, float*) {
   reinterpret_cast<float*>(row)[v] = g;
+}
+__device__ __forceinline__ void store_one(void* row, int64_t v, float g, _Float16*) {
+  reinterpret_cast<uint16_t*>(row)[v] = f32_to_f16(g);
 }
 
 // --- per-thread online log-sum-exp over one chunk -----------------------------

@@ -305,14 +305,18 @@ static hipError_t launch_vec(const RowArgs& a, const RowLaunch& l, hipStream_t s
   return l.vec ? launch_nt<TI, TG, MODE, true>(a, l.nt, s) : launch_nt<TI, TG, MODE, false>(a, l.nt, s);
 }
 
+// Storage pairs (logits -> gradient): f32 -> f32 | bf16, bf16 -> bf16 | f32,
+// f16 -> f16 | f32 (the entry points reject the others).
 template <int MODE>
 static hipError_t launch_types(const RowArgs& a, const RowLaunch& l, hipStream_t s) {
-  if (l.tin_bf16) {
-    return l.tg_bf16 ? launch_vec<uint16_t, uint16_t, MODE>(a, l, s)
-                     : launch_vec<uint16_t, float, MODE>(a, l, s);
-  }
-  return l.tg_bf16 ? launch_vec<float, uint16_t, MODE>(a, l, s)
-                   : launch_vec<float, float, MODE>(a, l, s);
+  if (l.tin == GRPO_BF16)
+    return l.tg == GRPO_BF16 ? launch_vec<uint16_t, uint16_t, MODE>(a, l, s)
+                             : launch_vec<uint16_t, float, MODE>(a, l, s);
+  if (l.tin == GRPO_F16)
+    return l.tg == GRPO_F16 ? launch_vec<_Float16, _Float16, MODE>(a, l, s)
+                            : launch_vec<_Float16, float, MODE>(a, l, s);
+  return l.tg == GRPO_BF16 ? launch_vec<float, uint16_t, MODE>(a, l, s)
+                           : launch_vec<float, float, MODE>(a, l, s);
 }
 
 hipError_t launch_rows_resident(const RowArgs& a, const RowLaunch& l, hipStream_t s);

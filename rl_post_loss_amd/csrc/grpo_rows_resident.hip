@@ -248,18 +248,22 @@ static hipError_t launch_res_types(const RowArgs& a, int64_t nvec, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-bool resident_fits(int64_t V, int tin_bf16) {
-  const int64_t nvec = V / (tin_bf16 ? 8 : 4);
+// esize: bytes per logit (2 or 4); a 16-byte chunk holds 16 / esize logits
+bool resident_fits(int64_t V, int esize) {
+  const int64_t nvec = V / (16 / esize);
   return nvec <= int64_t(768) * 22;
 }
 
 hipError_t launch_rows_resident(const RowArgs& a, const RowLaunch& l, hipStream_t s) {
-  const int64_t nvec = a.V / (l.tin_bf16 ? 8 : 4);
-  if (l.tin_bf16)
-    return l.tg_bf16 ? launch_res_types<uint16_t, uint16_t>(a, nvec, s)
-                     : launch_res_types<uint16_t, float>(a, nvec, s);
-  return l.tg_bf16 ? launch_res_types<float, uint16_t>(a, nvec, s)
-                   : launch_res_types<float, float>(a, nvec, s);
+  const int64_t nvec = a.V / (l.tin == GRPO_F32 ? 4 : 8);
+  if (l.tin == GRPO_BF16)
+    return l.tg == GRPO_BF16 ? launch_res_types<uint16_t, uint16_t>(a, nvec, s)
+                             : launch_res_types<uint16_t, float>(a, nvec, s);
+  if (l.tin == GRPO_F16)
+    return l.tg == GRPO_F16 ? launch_res_types<_Float16, _Float16>(a, nvec, s)
+                            : launch_res_types<_Float16, float>(a, nvec, s);
+  return l.tg == GRPO_BF16 ? launch_res_types<float, uint16_t>(a, nvec, s)
+                           : launch_res_types<float, float>(a, nvec, s);
 }
 
 }  // namespace grpo

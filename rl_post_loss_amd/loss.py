@@ -22,7 +22,8 @@ import torch
 from . import _abi
 from ._abi import GrpoCfg, GrpoGroups, GrpoOutputs, check, load_library
 
-_FDTYPE = {torch.float32: _abi.GRPO_F32, torch.bfloat16: _abi.GRPO_BF16}
+_FDTYPE = {torch.float32: _abi.GRPO_F32, torch.bfloat16: _abi.GRPO_BF16,
+           torch.float16: _abi.GRPO_F16}
 _IDTYPE = {torch.int64: _abi.GRPO_I64, torch.int32: _abi.GRPO_I32}
 
 # one zero-initialised workspace per (device, stream), grown on demand
@@ -339,7 +340,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     lib = load_library()
     dev = policy_logits.device
     _need(policy_logits.is_cuda, "policy_logits must be on a GPU")
-    _need(policy_logits.dtype in _FDTYPE, "logits must be float32 or bfloat16")
+    _need(policy_logits.dtype in _FDTYPE, "logits must be float32, bfloat16 or float16")
     ld = _row_stride(policy_logits, "policy_logits")
     B, T, V = policy_logits.shape
     if ref_logits is not None:
@@ -369,13 +370,13 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
         o = res._c_outputs
     if grad_out is None:
         gdt = policy_logits.dtype if grad_dtype is None else grad_dtype
-        _need(gdt in _FDTYPE, "grad_dtype must be float32 or bfloat16")
+        _need(gdt in _FDTYPE, "grad_dtype must be float32, bfloat16 or float16")
         grad_out = torch.empty((B, T, V), dtype=gdt, device=dev)
     if grad_out is False:
         gptr, gdt_code, gld = None, _abi.GRPO_F32, 0
     else:
         _need(grad_out.dtype in _FDTYPE and tuple(grad_out.shape) == (B, T, V)
-              and grad_out.device == dev, "grad_out must be float32/bfloat16 [B, T, V]")
+              and grad_out.device == dev, "grad_out must be float32/bfloat16/float16 [B, T, V]")
         gptr, gdt_code, gld = grad_out.data_ptr(), _FDTYPE[grad_out.dtype], _row_stride(grad_out, "grad_out")
         res.grad = grad_out
     if _ws is None:

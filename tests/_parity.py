@@ -7,7 +7,11 @@ Tolerances (stated by the loss path's acceptance criteria, made concrete):
     max|dg| <= 1e-5 * max|g|;
   * bf16 logits (oracle fed the same bf16 values): loss relative error
     <= 1e-4, gradient |dg| <= 2^-7 |g| per element, with an absolute floor of
-    2^-126 (below it bf16 has no relative precision).
+    2^-126 (below it bf16 has no relative precision);
+  * f16 logits and gradient: the same loss bound as bf16 (16-bit storage),
+    gradient |dg| <= 2^-10 |g| per element (round to nearest even in an
+    11-bit significand, plus the float32 error of G), with an absolute floor
+    of 2^-24 (the f16 subnormal spacing).
 Three refinements follow from the arithmetic, and every use is counted:
   * branch-ambiguous tokens: when the oracle's log-prob or log-ratio lies
     within the float32 error of a branch point of the objective (a clip or
@@ -74,10 +78,10 @@ def oracle_groups(wl):
 
 
 def host_inputs(inp):
-    """Host float64 / int views of a batch (bf16 values exactly as the GPU sees them)."""
+    """Host float64 / int views of a batch (16-bit values exactly as the GPU sees them)."""
     out = {}
     for k, v in inp.items():
-        if v.dtype in (torch.bfloat16, torch.float32):
+        if v.dtype in (torch.bfloat16, torch.float16, torch.float32):
             out[k] = v.detach().float().cpu().numpy()
         else:
             out[k] = v.detach().cpu().numpy()
@@ -233,10 +237,20 @@ def compare_exact_parts(res, ref, what=""):
     return counts
 
 
-def compare_logits_grad(grad_gpu, ref, cfg, mask, bf16, what="", policy=None, ids=None):
+# per-element bar of 16-bit gradients: (relative bound, absolute floor)
+GRAD16_BAR = {"bf16": (2.0 ** -7, 2.0 ** -126), "f16": (2.0 ** -10, 2.0 ** -24)}
+
+
+def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids=None):
     """grad_gpu: float64 numpy [B, T, V]; ref: oracle result with grad.
+    gdt: the gradient's storage, "f32", "bf16" or "f16" (True means "bf16",
+    False "f32").
     policy, ids: host policy logits and action ids, needed only to rebuild a
     row whose oracle G is exactly zero when the GPU took the other branch."""
+    if gdt is True or gdt is False:
+        gdt = "bf16" if gdt else "f32"
+    bf16 = gdt != "f32"                         # a 16-bit per-element bar
+    base, floor = GRAD16_BAR.get(gdt, (None, None))
     g = grad_gpu
     r = ref.grad
     flag_amb, amb, cands = branch_ambiguity(ref, cfg, mask)
@@ -249,12 +263,12 @@ def compare_logits_grad(grad_gpu, ref, cfg, mask, bf16, what="", policy=None, id
     def row_ok(gi, ri, tol_rel):
         if bf16:
             with np.errstate(invalid="ignore"):
-                lim = np.where(np.abs(ri) > 0, tol_rel * np.abs(ri), 0.0) + 2.0 ** -126
+                lim = np.where(np.abs(ri) > 0, tol_rel * np.abs(ri), 0.0) + floor
             return np.abs(gi - ri) <= lim
         return np.abs(gi - ri) <= 1e-5 * gmax + 1e-30
 
     if bf16:
-        tol, ill = g_rel_tolerance(ref, cfg, 2.0 ** -7)
+        tol, ill = g_rel_tolerance(ref, cfg, base)
         stats["illcond"] = int((ill & mask).sum())
         ok = row_ok(g, r, tol[..., None])
     else:
@@ -277,7 +291,7 @@ def compare_logits_grad(grad_gpu, ref, cfg, mask, bf16, what="", policy=None, id
                 alt = Gc * (onehot - p)
             else:
                 continue
-            if np.all(row_ok(g[i, t], alt, 2.0 ** -7 if bf16 else None)):
+            if np.all(row_ok(g[i, t], alt, base)):
                 bad_rows[i, t] = False
                 break
     nbad = int(bad_rows.sum())

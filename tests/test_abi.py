@@ -132,6 +132,9 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, dtype=7) == E["GRPO_ERR_DTYPE"]
     assert _fwd(lib, gdtype=9) == E["GRPO_ERR_DTYPE"]
     assert _fwd(lib, ids_dtype=3) == E["GRPO_ERR_DTYPE"]
+    assert _fwd(lib, dtype=1, gdtype=2) == E["GRPO_ERR_DTYPE"]      # bf16 logits -> f16 grad
+    assert _fwd(lib, dtype=0, gdtype=2) == E["GRPO_ERR_DTYPE"]      # f32 logits -> f16 grad
+    assert _fwd(lib, dtype=2, gdtype=1) == E["GRPO_ERR_DTYPE"]      # f16 logits -> bf16 grad
     # groups: neither, both, B % spp, bad CSR, singleton
     g, _ = _groups(spp=0)
     assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]

@@ -50,9 +50,9 @@ def check_logits_case(rpl, wl, seed=0, reduction=None):
     ref = oracle_logits(h, wl, reduction)
     cfg = cfg_from(wl, reduction)
     compare_exact_parts(res, ref, wl.name)
-    bf16 = wl.dtype == "bf16"
-    compare_scalars(res, ref, cfg, 1e-4 if bf16 else 1e-5, wl.name)
-    stats = compare_logits_grad(to_np(res.grad), ref, cfg, h["mask"], bf16, wl.name)
+    half = wl.dtype != "f32"
+    compare_scalars(res, ref, cfg, 1e-4 if half else 1e-5, wl.name)
+    stats = compare_logits_grad(to_np(res.grad), ref, cfg, h["mask"], wl.dtype, wl.name)
     clipped = int(to_np(res.counts)[1])
     assert abs(clipped - ref.clipped) <= stats["ambiguous"], (clipped, ref.clipped, stats)
     st = int(to_np(res.status)[0])
@@ -107,6 +107,30 @@ def test_many_rows_per_block(gpu_lib, V, dtype):
     several rows and skips (zero-fills) the masked ones between them."""
     wl = _custom(V, dtype, T=64, sizes=(8, 8), len_range=(1, 64))
     check_logits_case(gpu_lib, wl, seed=21)
+
+
+@pytest.mark.parametrize("V", [1000, 4097, 40000, 151936])
+def test_f16_logits_and_gradient(gpu_lib, V):
+    """IEEE half logits and gradient on every row-kernel path: wave per row,
+    block per row with a scalar tail, resident, streaming."""
+    T = 6 if V > 100000 else 16
+    check_logits_case(gpu_lib, _custom(V, "f16", T=T), seed=3)
+
+
+def test_f16_logits_f32_gradient(gpu_lib):
+    wl = _custom(5000, "f16", T=8)
+    announce("f16 logits -> f32 grad")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=12)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
+                                    inp["rewards"], inp["mask"], grad_dtype=torch.float32,
+                                    **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert res.grad.dtype == torch.float32
+    h = host_inputs(inp_cpu)
+    r = oracle_logits(h, wl)
+    compare_scalars(res, r, cfg_from(wl), 1e-4)
+    compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], "f32")
 
 
 def test_padded_row_stride_vector_tail(gpu_lib):

@@ -57,11 +57,11 @@ def test_helpers_accept_rounded_oracle(kw):
     gen = old + np.random.default_rng(9).normal(0, 0.4, old.shape) if "tis_type" in kw else None
     ref = oracle.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2),
                                    cfg=cfg, gen_logps=gen)
-    for dt, bf16 in ((torch.float32, False), (torch.bfloat16, True)):
+    for dt, gdt in ((torch.float32, "f32"), (torch.bfloat16, "bf16"), (torch.float16, "f16")):
         res = _as_result(ref, dt)
         compare_scalars(res, ref, cfg, 1e-5)
         compare_token_values(res, ref, cfg, mask, 1e-5)
-        compare_logits_grad(res.grad.double().numpy(), ref, cfg, mask, bf16)
+        compare_logits_grad(res.grad.double().numpy(), ref, cfg, mask, gdt)
 
 
 def test_helpers_reject_a_wrong_loss():
@@ -79,7 +79,7 @@ def test_helpers_reject_a_wrong_loss():
         compare_scalars(res, ref, cfg, 1e-5)
 
 
-@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("bf16", ["f32", "bf16", "f16"])
 def test_helpers_reject_a_wrong_gradient_row(bf16):
     cfg = oracle.LossConfig(beta=0.1, pg_loss="cispo")
     x, y, ids, old, mask, r = _case(5)

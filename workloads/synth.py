@@ -37,7 +37,7 @@ class LogitsWorkload:
     group_sizes: tuple            # sizes of the reward groups, in order
     T: int
     V: int
-    dtype: str                    # "f32" | "bf16"
+    dtype: str                    # "f32" | "bf16" | "f16"
     logit_std: float
     ref_noise_std: float
     old_noise_std: float
@@ -178,12 +178,12 @@ def _rewards(group_sizes, p, degenerate, g, device):
 
 def make_logits_inputs(wl: LogitsWorkload, device="cpu", seed=0, row_chunk=None):
     """Draw one batch of inputs.  Returns a dict of tensors on ``device``:
-    policy, ref [B, T, V] (fp32 or bf16), action_ids [B, T] int64,
+    policy, ref [B, T, V] (fp32, bf16 or fp16), action_ids [B, T] int64,
     old_logps [B, T] fp32, rewards [B] fp32, mask [B, T] bool.
     Large batches are drawn in row chunks so no fp32 temporary exceeds about
     1 GiB."""
     B, T, V = wl.B, wl.T, wl.V
-    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
     g = _gen(device, seed)
     rows = B * T
     if row_chunk is None:
