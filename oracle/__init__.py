@@ -8,12 +8,14 @@ from .grpo_oracle import (  # noqa: F401
     KL_ESTIMATORS,
     PG_LOSSES,
     REDUCTIONS,
+    SEQUENCE_PG,
     TIS_TYPES,
     LossConfig,
     OracleInputError,
     OracleResult,
     group_advantages,
     group_offsets,
+    gspo_terms,
     grpo_advantages,
     grpo_loss_fwd_bwd,
     grpo_token_loss,
@@ -21,7 +23,12 @@ from .grpo_oracle import (  # noqa: F401
     kl_terms,
     logits_rows,
     policy_terms,
+    real_terms,
     row_logsumexp,
+    sequence_mask_keep,
+    sequence_mean,
+    sequence_terms,
     sequence_weights,
+    softmax_grad_rows,
     token_terms,
 )

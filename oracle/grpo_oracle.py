@@ -64,6 +64,28 @@ repository design notes as well):
   constant (it depends on no trained parameter), multiplies the policy loss
   and its gradient, and leaves the KL term alone.  tis and icepop both clamp
   it to [min, max]; tis defaults min to 0, icepop requires it.
+* Sequence-masked truncation (seq-mask-tis): a sequence's importance ratio
+  is the geometric mean of its tokens' weights, exp(mean over active tokens
+  of (old - gen)); when it lies outside [min, max] (inclusive bounds) the
+  whole sequence's policy term is masked (weight 0), otherwise every token
+  keeps its own untruncated weight.
+* GSPO: the sequence ratio rho_i = exp(s_i), s_i the mean over active tokens
+  of (logp - old), replaces the token ratio in the clipped surrogate; the
+  sequence's value l_i is broadcast to its active tokens, which the chosen
+  per-sequence weights then reduce (the global token mean is rejected:
+  sequence-level ratios exclude token-level reduction).  Its gradient is the
+  chain rule through s_i: every active token of sequence i gets
+  w_i * (sum_t omega_t / L_i) * dl_i/ds_i, with omega_t the off-policy
+  weights (1 without them).
+* REAL: the classification logit of sequence k is s_k (as for GSPO).  In a
+  group, sequences with at least one active token are positive when A_k > 0
+  and negative when A_k < 0; a group lacking either side contributes 0.  The
+  group loss is log(1 + sum_pos exp(-s/tau)) + log(1 + sum_neg exp(s/tau)),
+  the policy loss is the sum of group losses divided by the number of groups
+  in the batch, and the KL term is the global token mean (so REAL requires the
+  token_mean reduction).  Tokens carry no per-token policy loss (their token
+  loss reads 0); the gradient reaches token t of sequence k as
+  (d policy_loss / d s_k) / L_k.
 
 Parity pins: every function here is pinned by CPU tests in
 ``tests/test_oracle_pins.py`` and ``tests/test_oracle_variants.py`` (closed
@@ -204,7 +226,8 @@ def sequence_weights(mask, reduction="token_mean", alpha=None, norm_constant=Non
 # [DOCKYARD] One loss many algorithms, Reference-KL penalty)
 # ---------------------------------------------------------------------------
 
-PG_LOSSES = ("clip", "cispo", "sapo", "reinforce", "on_policy")
+PG_LOSSES = ("clip", "cispo", "sapo", "reinforce", "on_policy", "gspo", "real")
+SEQUENCE_PG = ("gspo", "real")
 KL_ESTIMATORS = ("k3", "k1", "k2")
 
 
@@ -221,14 +244,22 @@ class LossConfig:
       reinforce  -A logp                     (the ratio dropped)
       on_policy  the clip loss with the ratio pinned to 1 by a stop-gradient:
                  value -A, gradient -A
+      gspo       the clip loss on the sequence ratio exp(mean_t(logp - old))
+                 ([RPP] Formula-level comparison, GSPO row; [DOCKYARD] One
+                 loss many algorithms, sequence-level importance ratios)
+      real       in-group classification of sequences by the sign of A
+                 ([REAL-BLOG] REAL formalisation and source walkthrough),
+                 temperature real_tau
     kl_estimator ([DOCKYARD] Reference-KL penalty), with d = logp_ref - logp:
       k3 = e^d - d - 1,  k1 = -d = logp - logp_ref,  k2 = d^2 / 2
     kl_input_clamp / kl_output_clamp clamp d and the estimator to [-v, v].
     reduction "fixed_constant" weights every token by 1 / norm_constant
     ([GRPO-LOSS] Normalizer semantics).
     tis_type (None | "tis" | "icepop") truncates the off-policy importance
-    weight to [tis_ratio_min, tis_ratio_max] ([DOCKYARD] Off-policy
-    correction (async GRPO)); it needs the generating policy's log-probs.
+    weight to [tis_ratio_min, tis_ratio_max]; "seq_mask" instead masks the
+    sequences whose geometric-mean weight leaves that range ([DOCKYARD]
+    Off-policy correction (async GRPO)); each needs the generating policy's
+    log-probs.
     """
     eps_low: float = 0.2
     eps_high: float = 0.2
@@ -246,21 +277,104 @@ class LossConfig:
     tis_type: str | None = None
     tis_ratio_min: float | None = None
     tis_ratio_max: float | None = None
+    real_tau: float = 0.5
 
 
-TIS_TYPES = ("tis", "icepop")
+TIS_TYPES = ("tis", "icepop", "seq_mask")
 
 
-def is_weights(old_logp, gen_logp, cfg: LossConfig):
+def is_weights(old_logp, gen_logp, cfg: LossConfig, keep=None):
     """Off-policy importance weight per token ([DOCKYARD] Off-policy
     correction (async GRPO)): exp(old - gen), truncated to [min, max] by tis
-    (min defaults to 0) or icepop (both bounds given).  A constant: no
-    gradient flows through it."""
+    (min defaults to 0) or icepop (both bounds given).  For seq_mask the
+    weight stays untruncated and ``keep`` (per token: whether its sequence
+    passed sequence_mask_keep) multiplies it.  A constant: no gradient flows
+    through it."""
     wt = np.exp(np.asarray(old_logp, dtype=np.float64) - np.asarray(gen_logp, dtype=np.float64))
-    if cfg.tis_type is not None:
+    if cfg.tis_type in ("tis", "icepop"):
         lo = 0.0 if cfg.tis_ratio_min is None else float(cfg.tis_ratio_min)
         wt = np.clip(wt, lo, float(cfg.tis_ratio_max))
+    elif cfg.tis_type == "seq_mask":
+        wt = np.where(np.asarray(keep, dtype=bool), wt, 0.0)
     return wt
+
+
+def _seq_bounds(B, ii):
+    """Start/end of each sequence's run in the sorted active-token index ii."""
+    return np.searchsorted(ii, np.arange(B + 1))
+
+
+def sequence_mean(B, ii, values):
+    """Per sequence: (exactly rounded sum of ``values`` over its active
+    tokens) / max(L_i, 1); ii lists the active tokens' sequences in order."""
+    bounds = _seq_bounds(B, ii)
+    out = np.zeros(B, dtype=np.float64)
+    for i in range(B):
+        s0, e0 = int(bounds[i]), int(bounds[i + 1])
+        out[i] = math.fsum(values[s0:e0]) / max(e0 - s0, 1)
+    return out
+
+
+def sequence_mask_keep(B, ii, old_act, gen_act, lo, hi):
+    """seq-mask-tis ([DOCKYARD] Off-policy correction): sequence i is kept
+    when its geometric-mean importance ratio exp(mean_t(old - gen)) lies in
+    [lo, hi]."""
+    diff = np.asarray(old_act, dtype=np.float64) - np.asarray(gen_act, dtype=np.float64)
+    r = np.exp(sequence_mean(B, ii, diff))
+    return (r >= lo) & (r <= hi)
+
+
+def gspo_terms(s, adv, cfg: LossConfig):
+    """Sequence-level clipped surrogate ([RPP] Formula-level comparison, GSPO
+    row): rho_i = exp(s_i); l_i = -min(rho A, clip(rho) A); dl_i/ds_i =
+    -A rho unless clipped (then 0; drho/ds = rho).  Clipped as for the token
+    form: strictly outside the band on the side the sign of A selects."""
+    s = np.asarray(s, dtype=np.float64)
+    A = np.asarray(adv, dtype=np.float64)
+    rho = np.exp(s)
+    lo = 1.0 - cfg.eps_low
+    hi = 1.0 + cfg.eps_high
+    obj = np.minimum(rho * A, np.clip(rho, lo, hi) * A)
+    clipped = ((A > 0) & (rho > hi)) | ((A < 0) & (rho < lo))
+    dl_ds = np.where(clipped, 0.0, -A * rho)
+    return rho, -obj, dl_ds, clipped
+
+
+def _log1p_sum_exp(z):
+    """log(1 + sum exp(z)), float64, as a log-sum-exp with a zero appended
+    (the appended term is the 1)."""
+    vals = [0.0] + [float(v) for v in z]
+    M = max(vals)
+    return M + math.log(math.fsum(math.exp(v - M) for v in vals))
+
+
+def real_terms(s, adv, L, offsets, tau):
+    """REAL loss ([REAL-BLOG] REAL formalisation; source walkthrough steps
+    1-3).  Returns (group_loss [G], dpolicy/ds [B], policy_loss) with
+    policy_loss = sum_g group_loss_g / G."""
+    s = np.asarray(s, dtype=np.float64)
+    A = np.asarray(adv, dtype=np.float64)
+    B = s.shape[0]
+    G = len(offsets) - 1
+    group_loss = np.zeros(G, dtype=np.float64)
+    dpol = np.zeros(B, dtype=np.float64)
+    for g in range(G):
+        members = range(int(offsets[g]), int(offsets[g + 1]))
+        pos = [k for k in members if A[k] > 0 and L[k] > 0]
+        neg = [k for k in members if A[k] < 0 and L[k] > 0]
+        if not pos or not neg:
+            continue
+        lse_pos = _log1p_sum_exp([-s[k] / tau for k in pos])
+        lse_neg = _log1p_sum_exp([s[k] / tau for k in neg])
+        group_loss[g] = lse_pos + lse_neg
+        for k in pos:
+            dpol[k] = -(1.0 / tau) * math.exp(-s[k] / tau - lse_pos) / G
+        for k in neg:
+            dpol[k] = (1.0 / tau) * math.exp(s[k] / tau - lse_neg) / G
+    total = 0.0
+    for g in range(G):
+        total = total + group_loss[g]
+    return group_loss, dpol, total / G
 
 
 def policy_terms(logp, old_logp, adv, cfg: LossConfig):
@@ -307,6 +421,8 @@ def policy_terms(logp, old_logp, adv, cfg: LossConfig):
         loss = -A * np.ones_like(logp)
         dloss = -A * np.ones_like(logp)
         clipped = np.zeros(np.shape(loss), dtype=bool)
+    elif cfg.pg_loss in SEQUENCE_PG:
+        raise OracleInputError("sequence-level losses need whole sequences (sequence_terms)")
     else:
         raise OracleInputError(f"unknown pg_loss {cfg.pg_loss!r}")
     return rho, loss, dloss, clipped
@@ -344,27 +460,64 @@ def kl_terms(d, cfg: LossConfig):
     return val, dkl
 
 
-def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig, gen_logp=None):
+def token_terms(logp, old_logp, logp_ref, adv, cfg: LossConfig, gen_logp=None, keep=None):
     """Per-token quantities, all float64 arrays of the broadcast shape.
 
     rho, loss, dloss, clipped from policy_terms; d = logp_ref - logp (0
     without a reference), kl and dkl = d kl / d logp from kl_terms.  With the
     default settings: loss = -min(rho A, clip(rho) A), kl = k3 = e^d - d - 1.
     With the generating policy's log-probs, loss and dloss carry the
-    off-policy importance weight (is_weights).
+    off-policy importance weight (is_weights; ``keep`` per token for
+    seq_mask).  For the sequence-level losses (gspo, real) the policy part
+    needs whole sequences: here loss, dloss and clipped are 0 and
+    sequence_terms fills them in.
     """
     logp = np.asarray(logp, dtype=np.float64)
-    rho, loss, dloss, clipped = policy_terms(logp, old_logp, adv, cfg)
-    if gen_logp is not None:
-        wt = is_weights(old_logp, gen_logp, cfg)
-        loss = loss * wt
-        dloss = dloss * wt
+    if cfg.pg_loss in SEQUENCE_PG:
+        rho = np.exp(logp - np.asarray(old_logp, dtype=np.float64))
+        loss = np.zeros_like(logp)
+        dloss = np.zeros_like(logp)
+        clipped = np.zeros(logp.shape, dtype=bool)
+    else:
+        rho, loss, dloss, clipped = policy_terms(logp, old_logp, adv, cfg)
+        if gen_logp is not None:
+            wt = is_weights(old_logp, gen_logp, cfg, keep)
+            loss = loss * wt
+            dloss = dloss * wt
     if logp_ref is None:
         d = np.zeros_like(logp)
     else:
         d = np.asarray(logp_ref, dtype=np.float64) - logp
     kl, dkl = kl_terms(d, cfg)
     return dict(rho=rho, d=d, kl=kl, loss=loss, clipped=clipped, dloss=dloss, dkl=dkl)
+
+
+def sequence_terms(B, ii, logp_act, old_act, gen_act, A, L, w, offsets, cfg: LossConfig):
+    """Policy part of the sequence-level losses.  Returns per active token the
+    token loss, the clip flag and gpol = d policy_loss / d logp (weights
+    included), plus per sequence s_i (the mean log-ratio) and, for REAL, the
+    group losses and the policy loss.
+
+    GSPO: policy_loss = sum_i w_i sum_t omega_t l_i, so by the chain rule
+    through s_i = mean_t(logp - old), d/dlogp_t = w_i (sum_t omega_t / L_i) dl_i/ds_i.
+    REAL: d/dlogp_t = (d policy_loss / d s_i) / L_i.
+    """
+    diff = np.asarray(logp_act, dtype=np.float64) - np.asarray(old_act, dtype=np.float64)
+    s = sequence_mean(B, ii, diff)
+    n = len(ii)
+    Lc = np.maximum(np.asarray(L), 1).astype(np.float64)
+    if cfg.pg_loss == "gspo":
+        _, l_seq, dl_ds, clip_seq = gspo_terms(s, A, cfg)
+        om = np.ones(n) if gen_act is None else is_weights(old_act, gen_act, cfg)
+        om_mean = sequence_mean(B, ii, om)          # sum_t omega_t / max(L_i, 1)
+        loss = om * l_seq[ii]
+        gpol = np.asarray(w, dtype=np.float64)[ii] * om_mean[ii] * dl_ds[ii]
+        return dict(loss=loss, clipped=clip_seq[ii], gpol=gpol, seq_logratio=s,
+                    group_loss=None, policy_loss=None)
+    group_loss, dpol, policy_loss = real_terms(s, A, L, offsets, cfg.real_tau)
+    gpol = dpol[ii] / Lc[ii]
+    return dict(loss=np.zeros(n), clipped=np.zeros(n, dtype=bool), gpol=gpol, seq_logratio=s,
+                group_loss=group_loss, policy_loss=policy_loss)
 
 
 def _check_cfg(cfg: LossConfig, have_ref: bool, have_gen: bool = False):
@@ -385,6 +538,15 @@ def _check_cfg(cfg: LossConfig, have_ref: bool, have_gen: bool = False):
     for v in (cfg.kl_input_clamp, cfg.kl_output_clamp):
         if v is not None and not v > 0:
             raise OracleInputError("KL clamps must be positive")
+    if cfg.pg_loss == "gspo" and cfg.reduction == "token_mean":
+        raise OracleInputError("sequence-level ratios exclude the token-mean reduction")
+    if cfg.pg_loss == "real":
+        if cfg.reduction != "token_mean":
+            raise OracleInputError("REAL takes its KL term as the global token mean")
+        if have_gen:
+            raise OracleInputError("REAL takes no off-policy weights")
+        if not (cfg.real_tau > 0 and math.isfinite(cfg.real_tau)):
+            raise OracleInputError("REAL needs a positive temperature")
     if cfg.tis_type is not None:
         if cfg.tis_type not in TIS_TYPES:
             raise OracleInputError("unknown truncated-IS type")
@@ -392,8 +554,10 @@ def _check_cfg(cfg: LossConfig, have_ref: bool, have_gen: bool = False):
             raise OracleInputError("truncated IS needs the generating policy's log-probs")
         if cfg.tis_ratio_max is None or not cfg.tis_ratio_max > 0:
             raise OracleInputError("truncated IS needs a positive upper bound")
-        if cfg.tis_type == "icepop" and cfg.tis_ratio_min is None:
-            raise OracleInputError("icepop needs a lower bound")
+        if cfg.tis_type in ("icepop", "seq_mask") and cfg.tis_ratio_min is None:
+            raise OracleInputError("icepop and seq_mask need a lower bound")
+        if cfg.tis_type == "seq_mask" and cfg.pg_loss in SEQUENCE_PG:
+            raise OracleInputError("seq_mask is not combined with sequence-level losses")
         lo = 0.0 if cfg.tis_ratio_min is None else cfg.tis_ratio_min
         if not (0.0 <= lo <= cfg.tis_ratio_max):
             raise OracleInputError("truncated IS bounds must satisfy 0 <= min <= max")
@@ -413,6 +577,9 @@ class OracleResult:
     clipped: int                    # number of clipped active tokens
     tok: dict = field(default_factory=dict)   # per-token arrays [B, T] (0 at masked slots)
     grad: np.ndarray | None = None  # d loss / d logits [B, T, V] or d loss / d logp [B, T]
+    seq_logratio: np.ndarray | None = None  # [B] s_i (sequence-level losses only)
+    group_loss: np.ndarray | None = None    # [G] REAL group losses
+    seq_keep: np.ndarray | None = None      # [B] seq_mask: sequence kept
 
 
 def _reduce(P, K, w, beta):
@@ -451,13 +618,41 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     old = np.asarray(old_logp, dtype=np.float64)[ii, tt]
     ref = None if ref_logp is None else np.asarray(ref_logp, dtype=np.float64)[ii, tt]
     gen = None if gen_logp is None else np.asarray(gen_logp, dtype=np.float64)[ii, tt]
-    terms = token_terms(lp, old, ref, A[ii], cfg, gen)
+    keep = _keep(B, ii, old, gen, cfg)
+    terms = token_terms(lp, old, ref, A[ii], cfg, gen, None if keep is None else keep[ii])
+    _add_sequence_terms(terms, B, ii, lp, old, gen, A, L, w, off, cfg)
     return _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale,
-                     grad=None, logp_active=lp, gen_active=gen)
+                     grad=None, logp_active=lp, gen_active=gen, keep=keep)
+
+
+def _keep(B, ii, old, gen, cfg):
+    """Per-sequence keep flags of seq_mask (None otherwise)."""
+    if cfg.tis_type != "seq_mask":
+        return None
+    return sequence_mask_keep(B, ii, old, gen, float(cfg.tis_ratio_min), float(cfg.tis_ratio_max))
+
+
+def _add_sequence_terms(terms, B, ii, lp, old, gen, A, L, w, off, cfg):
+    """For gspo / real: fill in the policy part once every log-prob is known."""
+    if cfg.pg_loss not in SEQUENCE_PG:
+        return
+    sq = sequence_terms(B, ii, lp, old, gen, A, L, w, off, cfg)
+    terms["loss"] = sq["loss"]
+    terms["clipped"] = sq["clipped"]
+    terms["gpol"] = sq["gpol"]
+    terms["seq"] = sq
+
+
+def _token_G(terms, w, ii, cfg, grad_scale):
+    """G = d loss / d logp per active token: w_i (dl/dlogp + beta dkl/dlogp),
+    or, for the sequence-level losses, gpol + w_i beta dkl/dlogp."""
+    if "gpol" in terms:
+        return (terms["gpol"] + w[ii] * (cfg.beta * terms["dkl"])) * grad_scale
+    return w[ii] * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
 
 
 def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_active,
-              gen_active=None):
+              gen_active=None, keep=None):
     P = np.zeros(B)
     K = np.zeros(B)
     C = np.zeros(B, dtype=np.int64)
@@ -470,7 +665,11 @@ def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_activ
         K[i] = math.fsum(terms["kl"][s:e])
         C[i] = int(np.count_nonzero(terms["clipped"][s:e]))
     loss, policy_loss, kl = _reduce(P, K, w, cfg.beta)
-    G = w[ii] * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
+    seq = terms.get("seq")
+    if seq is not None and seq["policy_loss"] is not None:
+        policy_loss = seq["policy_loss"]        # REAL: its own group normalisation
+        loss = policy_loss + cfg.beta * kl
+    G = _token_G(terms, w, ii, cfg, grad_scale)
     tok = {}
     for name in ("rho", "d", "kl", "loss", "dloss", "dkl"):
         full = np.zeros((B, T))
@@ -493,7 +692,10 @@ def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_activ
         grad = Gfull.copy()           # token-level: d loss / d logp = m * G
     return OracleResult(loss=loss, policy_loss=policy_loss, kl=kl, advantages=A,
                         seq_policy=P, seq_kl=K, seq_weight=w, seq_tokens=L,
-                        num_tokens=N, clipped=int(C.sum()), tok=tok, grad=grad)
+                        num_tokens=N, clipped=int(C.sum()), tok=tok, grad=grad,
+                        seq_logratio=None if seq is None else seq["seq_logratio"],
+                        group_loss=None if seq is None else seq["group_loss"],
+                        seq_keep=keep)
 
 
 # ---------------------------------------------------------------------------
@@ -509,13 +711,15 @@ def row_logsumexp(rows):
 
 
 def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.0,
-                want_grad=True, gen=None):
+                want_grad=True, gen=None, keep=None):
     """Forward + gradient for a set of active rows (each row one token slot).
 
     x_rows, y_rows: [n, V] policy / reference logits (y_rows may be None when
     beta == 0); ids [n]; old [n]; adv [n] = A of the row's sequence; w [n] =
-    omega of the row's sequence.  Returns the per-row terms, LSEs, G and the
-    gradient rows g_v = G * (onehot(a)_v - softmax(x)_v).
+    omega of the row's sequence; keep [n] the seq_mask flag of the row's
+    sequence.  Returns the per-row terms, LSEs, G and the gradient rows
+    g_v = G * (onehot(a)_v - softmax(x)_v).  For the sequence-level losses G
+    here holds only the KL part (the policy part needs whole sequences).
     """
     x = np.asarray(x_rows, dtype=np.float64)
     n, V = x.shape
@@ -532,15 +736,23 @@ def logits_rows(x_rows, y_rows, ids, old, adv, w, cfg: LossConfig, grad_scale=1.
     else:
         lse_ref = None
         logp_ref = None
-    terms = token_terms(logp, old, logp_ref, adv, cfg, gen)
+    terms = token_terms(logp, old, logp_ref, adv, cfg, gen, keep)
     G = np.asarray(w, dtype=np.float64) * (terms["dloss"] + cfg.beta * terms["dkl"]) * grad_scale
     out = dict(terms, lse=lse, lse_ref=lse_ref, logp=logp, logp_ref=logp_ref, G=G)
     if want_grad:
-        p = np.exp(x - lse[:, None])
-        g = -G[:, None] * p
-        g[r, ids] = G * (1.0 - p[r, ids])
-        out["grad"] = g
+        out["grad"] = softmax_grad_rows(x, ids, lse, G)
     return out
+
+
+def softmax_grad_rows(x_rows, ids, lse, G):
+    """g_v = G * (onehot(a)_v - softmax(x)_v) for each row, softmax from the
+    row's log-sum-exp."""
+    x = np.asarray(x_rows, dtype=np.float64)
+    r = np.arange(x.shape[0])
+    p = np.exp(x - np.asarray(lse, dtype=np.float64)[:, None])
+    g = -G[:, None] * p
+    g[r, ids] = G * (1.0 - p[r, ids])
+    return g
 
 
 def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, rewards, *,
@@ -564,21 +776,35 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     ids = np.asarray(action_ids)[ii, tt].astype(np.int64)
     old = np.asarray(old_logps, dtype=np.float64)[ii, tt]
     gen = None if gen_logps is None else np.asarray(gen_logps, dtype=np.float64)[ii, tt]
+    keep = _keep(B, ii, old, gen, cfg)
+    seq_level = cfg.pg_loss in SEQUENCE_PG
     grad = np.zeros((B, T, V)) if want_grad else None
-    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "kl", "loss", "dloss", "dkl", "logp")}
+    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "kl", "loss", "dloss", "dkl", "logp", "lse")}
     acc["clipped"] = np.zeros(len(ii), dtype=bool)
     for s in range(0, len(ii), row_chunk):
         sl = slice(s, s + row_chunk)
         xr = x[ii[sl], tt[sl]]
         yr = None if ref_logits is None else np.asarray(ref_logits)[ii[sl], tt[sl]]
         out = logits_rows(xr, yr, ids[sl], old[sl], A[ii[sl]], w[ii[sl]], cfg,
-                          grad_scale, want_grad, None if gen is None else gen[sl])
+                          grad_scale, want_grad and not seq_level,
+                          None if gen is None else gen[sl],
+                          None if keep is None else keep[ii[sl]])
         for k in acc:
             acc[k][sl] = out[k]
-        if want_grad:
+        if want_grad and not seq_level:
             grad[ii[sl], tt[sl]] = out["grad"]
+    if seq_level:
+        # the policy part needs every log-prob of a sequence: a second pass
+        # over the rows writes the gradient once G is known
+        _add_sequence_terms(acc, B, ii, acc["logp"], old, gen, A, L, w, off, cfg)
+        if want_grad:
+            G = _token_G(acc, w, ii, cfg, grad_scale)
+            for s in range(0, len(ii), row_chunk):
+                sl = slice(s, s + row_chunk)
+                grad[ii[sl], tt[sl]] = softmax_grad_rows(x[ii[sl], tt[sl]], ids[sl],
+                                                         acc["lse"][sl], G[sl])
     res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=grad,
-                    logp_active=acc["logp"], gen_active=gen)
+                    logp_active=acc["logp"], gen_active=gen, keep=keep)
     return res
 
 
