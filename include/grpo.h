@@ -22,7 +22,10 @@
  *                Advantage estimation, One loss many algorithms, CISPO,
  *                Reference-KL penalty, Off-policy correction (async GRPO).
  *   [RPP-F]      Relax docs, "REINFORCE++ and REINFORCE++-baseline":
- *                Formula-level comparison (SAPO's soft gate).
+ *                Formula-level comparison (SAPO's soft gate, GSPO's sequence
+ *                ratio).
+ *   [REAL]       ms-swift blog on the REAL loss: REAL formalisation and the
+ *                source walkthrough (in-group classification of sequences).
  *
  * Objective (per active token (i, t) of sequence i, action a = action_ids[i,t]),
  * in the default settings (GRPO_PG_CLIP, GRPO_KL_K3, no clamps):
@@ -74,7 +77,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 3
+#define GRPO_ABI_VERSION 4
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -131,14 +134,38 @@ typedef enum grpo_reduction {
  *   GRPO_PG_REINFORCE  l = -A logp: dl/dlogp = -A
  *   GRPO_PG_ON_POLICY  ratio pinned to 1 by a stop-gradient: l = -A,
  *                      dl/dlogp = -A
+ * Sequence-level forms ([RPP-F] GSPO row; [DOCKYARD] sequence-level
+ * importance ratios; [REAL]) use s_i, the mean over sequence i's active
+ * tokens of (logp - old_logps):
+ *   GRPO_PG_GSPO       rho_i = exp(s_i) replaces the token ratio in the
+ *                      clipped surrogate; l_i = -min(rho_i A, clip(rho_i) A)
+ *                      is every active token's loss, so d loss / d logp_t =
+ *                      w_i * (mean of the tokens' off-policy weights, 1
+ *                      without them) * (clipped ? 0 : -A rho_i).  Not with
+ *                      GRPO_TOKEN_MEAN (sequence ratios exclude token-level
+ *                      reduction) nor the dual clip.
+ *   GRPO_PG_REAL       in-group classification: in group g, sequences with
+ *                      at least one active token are positive when A > 0 and
+ *                      negative when A < 0; a group lacking either side adds
+ *                      0; group loss log(1 + sum_pos exp(-s/tau)) +
+ *                      log(1 + sum_neg exp(s/tau)) with tau = real_tau;
+ *                      policy_loss = (sum of group losses) / (number of
+ *                      groups); token t of sequence k gets d policy_loss /
+ *                      d s_k / L_k.  Tokens carry no per-token policy loss
+ *                      (their token loss and seq_policy read 0).  Needs
+ *                      GRPO_TOKEN_MEAN (the KL term is the global token mean)
+ *                      and no gen_logps.
  * The clip count (outputs->counts[1]) counts clipped tokens for CLIP (dual
- * clip included) and tokens whose ratio lies outside the band for CISPO. */
+ * clip included), tokens whose ratio lies outside the band for CISPO and the
+ * active tokens of clipped sequences for GSPO. */
 typedef enum grpo_pg_loss {
   GRPO_PG_CLIP = 0,
   GRPO_PG_CISPO = 1,
   GRPO_PG_SAPO = 2,
   GRPO_PG_REINFORCE = 3,
-  GRPO_PG_ON_POLICY = 4
+  GRPO_PG_ON_POLICY = 4,
+  GRPO_PG_GSPO = 5,
+  GRPO_PG_REAL = 6
 } grpo_pg_loss;
 
 /* Reference-KL estimator of d = logp_ref - logp ([DOCKYARD] Reference-KL
@@ -157,12 +184,23 @@ typedef enum grpo_kl_estimator { GRPO_KL_K3 = 0, GRPO_KL_K1 = 1, GRPO_KL_K2 = 2 
  * weight of the current policy (old_logps) to the generating one,
  *   omega = exp(old_logps - gen_logps),
  * a constant (it depends on no logit); the KL term is not weighted.
- *   GRPO_TIS_NONE    omega as is
- *   GRPO_TIS_TIS     clip(omega, tis_ratio_min, tis_ratio_max), min usually 0
- *   GRPO_TIS_ICEPOP  clip(omega, tis_ratio_min, tis_ratio_max), both bounds
- *                    chosen by the caller
+ *   GRPO_TIS_NONE      omega as is
+ *   GRPO_TIS_TIS       clip(omega, tis_ratio_min, tis_ratio_max), min usually 0
+ *   GRPO_TIS_ICEPOP    clip(omega, tis_ratio_min, tis_ratio_max), both bounds
+ *                      chosen by the caller
+ *   GRPO_TIS_SEQ_MASK  sequence masking: a sequence whose geometric-mean
+ *                      weight exp(mean over its active tokens of (old_logps -
+ *                      gen_logps)) lies outside [tis_ratio_min,
+ *                      tis_ratio_max] has omega = 0 on every token; the other
+ *                      sequences keep their untruncated omega.  Not with the
+ *                      sequence-level policy losses.
  * Truncation needs gen_logps. */
-typedef enum grpo_tis { GRPO_TIS_NONE = 0, GRPO_TIS_TIS = 1, GRPO_TIS_ICEPOP = 2 } grpo_tis;
+typedef enum grpo_tis {
+  GRPO_TIS_NONE = 0,
+  GRPO_TIS_TIS = 1,
+  GRPO_TIS_ICEPOP = 2,
+  GRPO_TIS_SEQ_MASK = 3
+} grpo_tis;
 
 /* Device-detected data faults, OR-ed into outputs->status (which each call
  * overwrites). */
@@ -211,6 +249,7 @@ typedef struct grpo_cfg {
   int32_t tis_type;        /* grpo_tis (0: no truncation) */
   double tis_ratio_min;    /* >= 0, <= tis_ratio_max; read when tis_type != 0 */
   double tis_ratio_max;    /* > 0 and finite; read when tis_type != 0 */
+  double real_tau;         /* > 0 and finite, read by GRPO_PG_REAL only (usually 0.5) */
 } grpo_cfg;
 
 /* Outputs (DEVICE pointers).  Only `scalars` is required; any other field may
@@ -228,6 +267,8 @@ typedef struct grpo_outputs {
   float *tok_logp;     /* [B*T] logp of the taken token (logits entry points only) */
   float *tok_loss;     /* [B*T] token loss l */
   float *tok_kl;       /* [B*T] KL estimator */
+  float *seq_logratio; /* [B] s_i, the mean log-ratio of sequence i (written by the
+                          sequence-level policy losses only) */
 } grpo_outputs;
 
 /* ABI version of the loaded library (GRPO_ABI_VERSION it was built with). */

@@ -295,6 +295,8 @@ def is_weights(old_logp, gen_logp, cfg: LossConfig, keep=None):
         lo = 0.0 if cfg.tis_ratio_min is None else float(cfg.tis_ratio_min)
         wt = np.clip(wt, lo, float(cfg.tis_ratio_max))
     elif cfg.tis_type == "seq_mask":
+        if keep is None:
+            raise OracleInputError("seq_mask needs each token's sequence keep flag")
         wt = np.where(np.asarray(keep, dtype=bool), wt, 0.0)
     return wt
 

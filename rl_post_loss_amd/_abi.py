@@ -8,16 +8,17 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 3
+GRPO_ABI_VERSION = 4
 
 GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
 GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA, GRPO_FIXED_CONSTANT = 0, 1, 2, 3
 REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE_MEAN,
                    "length_alpha": GRPO_LENGTH_ALPHA, "fixed_constant": GRPO_FIXED_CONSTANT}
-PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 4}
+PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 4, "gspo": 5,
+                 "real": 6}
 KL_ESTIMATOR_CODES = {"k3": 0, "k1": 1, "k2": 2}
-TIS_CODES = {None: 0, "tis": 1, "icepop": 2}
+TIS_CODES = {None: 0, "tis": 1, "icepop": 2, "seq_mask": 3}
 
 GRPO_FAULT_BAD_ACTION = 1
 GRPO_FAULT_NO_TOKENS = 2
@@ -43,13 +44,13 @@ class GrpoCfg(C.Structure):
                 ("alpha", f64), ("pg_loss", i32), ("kl_estimator", i32), ("dual_clip_c", f64),
                 ("sapo_tau_pos", f64), ("sapo_tau_neg", f64), ("kl_input_clamp", f64),
                 ("kl_output_clamp", f64), ("norm_constant", f64), ("tis_type", i32),
-                ("tis_ratio_min", f64), ("tis_ratio_max", f64)]
+                ("tis_ratio_min", f64), ("tis_ratio_max", f64), ("real_tau", f64)]
 
 
 class GrpoOutputs(C.Structure):
     _fields_ = [("scalars", vp), ("advantages", vp), ("seq_policy", vp), ("seq_kl", vp),
                 ("seq_weight", vp), ("seq_tokens", vp), ("counts", vp), ("status", vp),
-                ("tok_logp", vp), ("tok_loss", vp), ("tok_kl", vp)]
+                ("tok_logp", vp), ("tok_loss", vp), ("tok_kl", vp), ("seq_logratio", vp)]
 
 
 SIGNATURES = {

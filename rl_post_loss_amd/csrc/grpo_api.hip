@@ -17,6 +17,8 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream);
 hipError_t launch_final(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
+hipError_t launch_seq(const SeqArgs& a, hipStream_t stream);
+hipError_t launch_real(const RealArgs& a, hipStream_t stream);
 bool resident_fits(int64_t V, int esize);
 }  // namespace grpo
 
@@ -71,7 +73,13 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref, bool has_gen) {
     return GRPO_ERR_CONFIG;
   if (c->reduction == GRPO_FIXED_CONSTANT && !(c->norm_constant > 0.0 && isfinite(c->norm_constant)))
     return GRPO_ERR_CONFIG;
-  if (c->pg_loss < GRPO_PG_CLIP || c->pg_loss > GRPO_PG_ON_POLICY) return GRPO_ERR_CONFIG;
+  if (c->pg_loss < GRPO_PG_CLIP || c->pg_loss > GRPO_PG_REAL) return GRPO_ERR_CONFIG;
+  // sequence-level ratios exclude the token-level reduction; REAL takes its
+  // KL term as the global token mean and no off-policy weights
+  if (c->pg_loss == GRPO_PG_GSPO && c->reduction == GRPO_TOKEN_MEAN) return GRPO_ERR_CONFIG;
+  if (c->pg_loss == GRPO_PG_REAL &&
+      (c->reduction != GRPO_TOKEN_MEAN || has_gen || !(c->real_tau > 0.0 && isfinite(c->real_tau))))
+    return GRPO_ERR_CONFIG;
   if (c->kl_estimator < GRPO_KL_K3 || c->kl_estimator > GRPO_KL_K2) return GRPO_ERR_CONFIG;
   // dual clip: 0 (off) or a finite c > 1, with the clipped surrogate only
   if (c->dual_clip_c != 0.0 &&
@@ -83,12 +91,24 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref, bool has_gen) {
     return GRPO_ERR_CONFIG;
   for (double v : {c->kl_input_clamp, c->kl_output_clamp})
     if (v != 0.0 && !(v > 0.0 && isfinite(v))) return GRPO_ERR_CONFIG;
-  if (c->tis_type < GRPO_TIS_NONE || c->tis_type > GRPO_TIS_ICEPOP) return GRPO_ERR_CONFIG;
+  if (c->tis_type < GRPO_TIS_NONE || c->tis_type > GRPO_TIS_SEQ_MASK) return GRPO_ERR_CONFIG;
+  if (c->tis_type == GRPO_TIS_SEQ_MASK &&
+      (c->pg_loss == GRPO_PG_GSPO || c->pg_loss == GRPO_PG_REAL))
+    return GRPO_ERR_CONFIG;
   if (c->tis_type != GRPO_TIS_NONE &&
       !(has_gen && c->tis_ratio_max > 0.0 && isfinite(c->tis_ratio_max) &&
         c->tis_ratio_min >= 0.0 && c->tis_ratio_min <= c->tis_ratio_max))
     return GRPO_ERR_CONFIG;
   return GRPO_OK;
+}
+
+bool is_sequence_level(const grpo_cfg* c) {
+  return c->pg_loss == GRPO_PG_GSPO || c->pg_loss == GRPO_PG_REAL;
+}
+
+// Number of reward groups of a validated group description.
+int64_t group_count(const grpo_groups* g, int64_t B) {
+  return g->samples_per_prompt > 0 ? B / g->samples_per_prompt : int64_t(g->num_groups);
 }
 
 // Objective parameters for the kernels (float32, as they compute).
@@ -105,9 +125,11 @@ Objective make_objective(const grpo_cfg* c, bool has_gen) {
   o.kl_in = float(c->kl_input_clamp);
   o.kl_out = float(c->kl_output_clamp);
   o.has_is = has_gen ? 1 : 0;
-  o.tis = c->tis_type != GRPO_TIS_NONE ? 1 : 0;
+  o.tis = (c->tis_type == GRPO_TIS_TIS || c->tis_type == GRPO_TIS_ICEPOP) ? 1 : 0;
   o.tis_lo = float(c->tis_ratio_min);
   o.tis_hi = float(c->tis_ratio_max);
+  o.seq = is_sequence_level(c) ? 1 : 0;
+  o.seq_mask = c->tis_type == GRPO_TIS_SEQ_MASK ? 1 : 0;
   o.general = (o.pg != GRPO_PG_CLIP || o.kl != GRPO_KL_K3 || c->dual_clip_c != 0.0 ||
                c->kl_input_clamp != 0.0 || c->kl_output_clamp != 0.0 || has_gen)
                   ? 1
@@ -137,8 +159,21 @@ grpo_status check_ws(void* ws, size_t ws_bytes, int64_t B, int64_t T, int32_t nu
 // advantages and (optionally) weights.
 grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int64_t B, int64_t T,
                      const grpo_groups* g, const grpo_cfg* cfg, bool want_weights,
-                     const grpo_outputs* out, float* adv_out, hipStream_t s) {
+                     const grpo_outputs* out, float* adv_out, hipStream_t s,
+                     const float* old = nullptr, const float* gen = nullptr) {
   PrepArgs a{};
+  a.iw_mode = kIwNone;
+  if (cfg && gen) {
+    if (cfg->tis_type == GRPO_TIS_SEQ_MASK) a.iw_mode = kIwSeqMask;
+    else if (cfg->pg_loss == GRPO_PG_GSPO) a.iw_mode = kIwMean;
+  }
+  a.old = old;
+  a.gen = gen;
+  if (cfg) a.obj = make_objective(cfg, gen != nullptr);
+  a.seq_lo = cfg ? cfg->tis_ratio_min : 0.0;
+  a.seq_hi = cfg ? cfg->tis_ratio_max : 0.0;
+  a.iwseq = w.at<double>(w.l.iwseq);
+  a.useq = want_weights ? w.at<float>(w.l.useq) : nullptr;
   a.mask = mask;
   a.rewards = rewards;
   a.B = B;
@@ -171,10 +206,12 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
 }
 
 grpo_status run_final(const Ws& w, int64_t B, double beta, const grpo_outputs* out,
-                      hipStream_t s) {
+                      hipStream_t s, int64_t real_groups = 0) {
   FinalArgs f{};
   f.B = B;
   f.beta = beta;
+  f.gloss = real_groups > 0 ? w.at<double>(w.l.gloss) : nullptr;
+  f.num_groups = real_groups;
   f.hdr = w.hdr();
   f.w = w.at<double>(w.l.w);
   f.P = w.at<double>(w.l.P);
@@ -216,6 +253,64 @@ int choose_nt(int64_t V, int esize) {
   if (bytes <= 4096) return 64;
   if (bytes <= 65536) return 256;
   return GRPO_NT_LARGE;
+}
+
+// Sequence phase of GSPO / REAL: per-sequence s_i (and the GSPO loss and
+// coefficient), then for REAL the group kernel.  `fill` (logits path) also
+// writes the token losses and per-sequence totals over the row pass's KL.
+grpo_status run_sequence_phase(const Ws& w, const grpo_cfg* cfg, const grpo_groups* g,
+                               const float* logp, const float* old, const float* gen,
+                               const uint8_t* mask, int64_t B, int64_t T,
+                               const float* grad_scale, bool fill, const grpo_outputs* out,
+                               hipStream_t s) {
+  SeqArgs q{};
+  q.B = B;
+  q.T = T;
+  q.pg = cfg->pg_loss;
+  q.lo = 1.0 - cfg->eps_low;
+  q.hi = 1.0 + cfg->eps_high;
+  q.obj = make_objective(cfg, gen != nullptr);
+  q.logp = logp;
+  q.old = old;
+  q.gen = gen;
+  q.mask = mask;
+  q.grad_scale = grad_scale;
+  q.stash = fill ? w.at<RowStash>(w.l.stash) : nullptr;
+  q.fill = fill ? 1 : 0;
+  q.hdr = w.hdr();
+  q.L = w.at<int32_t>(w.l.L);
+  q.A = w.at<float>(w.l.A);
+  q.w = w.at<double>(w.l.w);
+  q.iwseq = (gen && cfg->pg_loss == GRPO_PG_GSPO) ? w.at<double>(w.l.iwseq) : nullptr;
+  q.tok_kl = w.at<float>(w.l.tok_kl);
+  q.slogr = w.at<double>(w.l.slogr);
+  q.useq = w.at<float>(w.l.useq);
+  q.lseq = w.at<double>(w.l.lseq);
+  q.cseq = w.at<int32_t>(w.l.cseq);
+  q.tok_loss = w.at<float>(w.l.tok_loss);
+  q.flags = w.at<uint8_t>(w.l.flags);
+  q.P = w.at<double>(w.l.P);
+  q.K = w.at<double>(w.l.K);
+  q.C = w.at<int64_t>(w.l.C);
+  q.seq_logratio = out->seq_logratio;
+  q.seq_policy = out->seq_policy;
+  q.seq_kl = out->seq_kl;
+  q.out_loss = out->tok_loss;
+  if (launch_seq(q, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (cfg->pg_loss != GRPO_PG_REAL) return GRPO_OK;
+  RealArgs r{};
+  r.B = B;
+  r.spp = g->samples_per_prompt;
+  r.num_groups = g->samples_per_prompt > 0 ? 0 : g->num_groups;
+  r.offsets = r.num_groups > 0 ? w.at<int64_t>(w.l.offsets) : nullptr;
+  r.tau = cfg->real_tau;
+  r.grad_scale = grad_scale;
+  r.L = q.L;
+  r.A = q.A;
+  r.slogr = q.slogr;
+  r.useq = q.useq;
+  r.gloss = w.at<double>(w.l.gloss);
+  return launch_real(r, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
 }  // namespace
@@ -288,8 +383,14 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   st = check_ws(ws, ws_bytes, B, T, ng, &w);
   if (st != GRPO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s);
+  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s, old_logp, gen_logp);
   if (st != GRPO_OK) return st;
+  const bool seqlv = is_sequence_level(cfg);
+  if (seqlv) {
+    st = run_sequence_phase(w, cfg, groups, logp, old_logp, gen_logp, mask, B, T, grad_scale,
+                            false, out, s);
+    if (st != GRPO_OK) return st;
+  }
   TokenArgs a{};
   a.logp = logp;
   a.old = old_logp;
@@ -307,12 +408,17 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.P = w.at<double>(w.l.P);
   a.K = w.at<double>(w.l.K);
   a.C = w.at<int64_t>(w.l.C);
+  a.iwseq = cfg->tis_type == GRPO_TIS_SEQ_MASK ? w.at<double>(w.l.iwseq) : nullptr;
+  a.useq = w.at<float>(w.l.useq);
+  a.lseq = w.at<double>(w.l.lseq);
+  a.cseq = w.at<int32_t>(w.l.cseq);
   a.seq_policy = out->seq_policy;
   a.seq_kl = out->seq_kl;
   a.out_loss = out->tok_loss;
   a.out_kl = out->tok_kl;
   if (launch_token(a, s) != hipSuccess) return GRPO_ERR_HIP;
-  return run_final(w, B, cfg->beta, out, s);
+  return run_final(w, B, cfg->beta, out, s,
+                   cfg->pg_loss == GRPO_PG_REAL ? group_count(groups, B) : 0);
 }
 
 static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype,
@@ -386,8 +492,9 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   if (st != GRPO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s);
+  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s, old_logps, gen_logps);
   if (st != GRPO_OK) return st;
+  const bool seqlv = is_sequence_level(cfg);
 
   RowArgs a{};
   a.x = policy_logits;
@@ -403,8 +510,8 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.rows = rows;
   a.obj = make_objective(cfg, gen_logps != nullptr);
   a.grad_scale = grad_scale;
-  a.g = grad_out;
-  a.ldg = grad_out ? grad_row_stride : 0;
+  a.g = seqlv ? nullptr : grad_out;
+  a.ldg = (grad_out && !seqlv) ? grad_row_stride : 0;
   a.hdr = w.hdr();
   a.A = w.at<float>(w.l.A);
   a.w = w.at<double>(w.l.w);
@@ -412,11 +519,14 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.tok_kl = w.at<float>(w.l.tok_kl);
   a.flags = w.at<uint8_t>(w.l.flags);
   a.stash = w.at<RowStash>(w.l.stash);
+  a.tok_logp = seqlv ? w.at<float>(w.l.tok_logp) : nullptr;
+  a.iwseq = cfg->tis_type == GRPO_TIS_SEQ_MASK ? w.at<double>(w.l.iwseq) : nullptr;
+  a.useq = w.at<float>(w.l.useq);
   a.out_logp = out->tok_logp;
   a.out_loss = out->tok_loss;
   a.out_kl = out->tok_kl;
   RowLaunch l{};
-  l.mode = grad_out ? 0 : 1;
+  l.mode = (grad_out && !seqlv) ? 0 : 1;
   l.tin = logits_dtype;
   l.tg = grad_out ? grad_dtype : logits_dtype;
   l.nt = choose_nt(V, fdtype_size(logits_dtype));
@@ -424,11 +534,33 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
                             grad_row_stride, grad_dtype);
   // rows above 4 KB that fit one block's registers keep the policy row
   // resident between the passes (fused mode); longer rows stream
-  l.resident = GRPO_RESIDENT && grad_out && l.vec && V * fdtype_size(logits_dtype) > 4096 &&
+  l.resident = GRPO_RESIDENT && l.mode == 0 && l.vec && V * fdtype_size(logits_dtype) > 4096 &&
                resident_fits(V, fdtype_size(logits_dtype));
   const bool timed = g_ev_start && g_ev_stop;
   if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
   if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;
+
+  if (seqlv) {
+    // the sequence phase needs every log-prob of a sequence; the gradient
+    // pass then re-reads the policy rows
+    st = run_sequence_phase(w, cfg, groups, a.tok_logp, old_logps, gen_logps, mask, B, T,
+                            grad_scale, true, out, s);
+    if (st != GRPO_OK) return st;
+    if (grad_out) {
+      RowArgs b = a;
+      b.y = nullptr;
+      b.g = grad_out;
+      b.ldg = grad_row_stride;
+      b.grad_scale = nullptr;  // the row and sequence passes folded it in
+      RowLaunch lb = l;
+      lb.mode = 2;
+      lb.resident = 0;
+      if (launch_rows(b, lb, s) != hipSuccess) return GRPO_ERR_HIP;
+    }
+    if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
+    return run_final(w, B, cfg->beta, out, s,
+                     cfg->pg_loss == GRPO_PG_REAL ? group_count(groups, B) : 0);
+  }
   if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
 
   ReduceArgs r{};
@@ -481,6 +613,7 @@ grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64
   a.ldg = grad_row_stride;
   a.hdr = w.hdr();
   a.stash = w.at<RowStash>(w.l.stash);
+  a.useq = w.at<float>(w.l.useq);
   RowLaunch l{};
   l.mode = 2;
   l.tin = logits_dtype;

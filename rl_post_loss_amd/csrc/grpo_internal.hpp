@@ -21,14 +21,17 @@ struct WsHeader {
 
 // Per-row state handed from the forward pass to the gradient pass.
 struct RowStash {
-  float G;     // d loss / d logp of the row (0: masked, bad id, or no gradient)
+  float G;     // d loss / d logp of the row known after the row pass (0: masked,
+               // bad id, or no gradient); the sequence-level policy part is
+               // added from the per-sequence coefficient
   float c;     // base-2 log-normaliser: p_v = 2^(x_v * log2e - c)
   float omp;   // 1 - p_a, computed without cancellation
-  float pad;
+  float act;   // 1: an active row with a valid action id; 0 otherwise
 };
 
 struct WsLayout {
-  size_t hdr, L, A, w, P, K, C, offsets, tok_loss, tok_kl, flags, stash, total;
+  size_t hdr, L, A, w, P, K, C, slogr, useq, lseq, cseq, iwseq, gloss, offsets, tok_loss, tok_kl,
+      tok_logp, flags, stash, total;
 };
 
 inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
@@ -42,8 +45,15 @@ inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
   l.P = o; o = align_up(o + size_t(B) * 8);
   l.K = o; o = align_up(o + size_t(B) * 8);
   l.C = o; o = align_up(o + size_t(B) * 8);
+  l.slogr = o; o = align_up(o + size_t(B) * 8);   // s_i (sequence-level losses)
+  l.useq = o; o = align_up(o + size_t(B) * 4);    // per-sequence gradient coefficient
+  l.lseq = o; o = align_up(o + size_t(B) * 8);    // GSPO sequence loss l_i
+  l.cseq = o; o = align_up(o + size_t(B) * 4);    // GSPO sequence clipped flag
+  l.iwseq = o; o = align_up(o + size_t(B) * 8);   // seq-mask keep flag or GSPO mean weight
+  l.gloss = o; o = align_up(o + size_t(B) * 8);   // REAL group losses (<= B groups)
   l.tok_loss = o; o = align_up(o + rows * 4);
   l.tok_kl = o; o = align_up(o + rows * 4);
+  l.tok_logp = o; o = align_up(o + rows * 4);
   l.flags = o; o = align_up(o + rows);
   l.stash = o; o = align_up(o + rows * sizeof(RowStash));
   // last, so that every other offset is independent of the group count
@@ -65,9 +75,15 @@ struct Objective {
   float tau_pos, tau_neg;
   float kl_in, kl_out;  // clamps; 0: off
   int32_t has_is;     // off-policy weight exp(old - gen) on the policy term
-  int32_t tis;        // truncate that weight to [tis_lo, tis_hi]
+  int32_t tis;        // truncate that weight to [tis_lo, tis_hi] (tis, icepop)
   float tis_lo, tis_hi;
+  int32_t seq;        // 1: sequence-level policy loss (GSPO, REAL): the row and
+                      // token passes compute the KL part only
+  int32_t seq_mask;   // 1: the weight is multiplied by the sequence's keep flag
 };
+
+// Importance-weight statistics per sequence, computed by the prep kernel.
+enum IwMode { kIwNone = 0, kIwSeqMask = 1, kIwMean = 2 };
 
 // Group / advantage / weight preparation.
 struct PrepArgs {
@@ -83,11 +99,19 @@ struct PrepArgs {
   double alpha;
   double norm_constant;     // GRPO_FIXED_CONSTANT
   int32_t want_weights;     // 0: advantages only
+  // per-sequence importance-weight statistic (IwMode) over the active tokens
+  int32_t iw_mode;
+  const float* old;
+  const float* gen;
+  Objective obj;            // token-weight truncation (kIwMean)
+  double seq_lo, seq_hi;    // sequence-ratio bounds (kIwSeqMask)
   // workspace
   WsHeader* hdr;
   int32_t* L;
   float* A;
   double* w;
+  double* iwseq;            // kIwSeqMask: keep flag (0 or 1); kIwMean: mean token weight
+  float* useq;              // cleared to 0 (token-level losses) when non-null
   // outputs (nullable)
   float* adv_out;
   float* seq_weight_out;
@@ -117,6 +141,9 @@ struct RowArgs {
   float* tok_kl;
   uint8_t* flags;
   RowStash* stash;
+  float* tok_logp;          // workspace copy of logp (sequence-level losses), or null
+  const double* iwseq;      // seq-mask keep flags, or null
+  const float* useq;        // backward: per-sequence gradient coefficient
   // per-token outputs (nullable)
   float* out_logp;
   float* out_loss;
@@ -149,6 +176,58 @@ struct ReduceArgs {
   float* seq_kl;
 };
 
+// Sequence phase of the sequence-level losses (one block per sequence):
+// s_i, and for GSPO the sequence loss, clip flag and gradient coefficient.
+struct SeqArgs {
+  int64_t B, T;
+  int32_t pg;               // GRPO_PG_GSPO or GRPO_PG_REAL
+  double lo, hi;            // GSPO clip band (binary64)
+  Objective obj;            // token-weight settings (has_is, tis bounds)
+  const float* logp;        // [B, T]: the caller's log-probs or the row pass's copy
+  const float* old;
+  const float* gen;         // or null
+  const uint8_t* mask;      // or null
+  const float* grad_scale;  // or null
+  const RowStash* stash;    // logits path: skips slots with an out-of-range id; else null
+  int32_t fill;             // 1: also write token losses, clip flags and P, K, C
+  // workspace
+  WsHeader* hdr;
+  const int32_t* L;
+  const float* A;
+  const double* w;
+  const double* iwseq;      // GSPO mean token weight (null without gen)
+  const float* tok_kl;      // fill: the row pass's KL values
+  double* slogr;
+  float* useq;
+  double* lseq;
+  int32_t* cseq;
+  float* tok_loss;
+  uint8_t* flags;
+  double* P;
+  double* K;
+  int64_t* C;
+  // outputs (nullable)
+  float* seq_logratio;
+  float* seq_policy;
+  float* seq_kl;
+  float* out_loss;
+};
+
+// REAL group phase (one block over all groups).
+struct RealArgs {
+  int64_t B;
+  int32_t spp;              // uniform group size, or 0 for CSR
+  int32_t num_groups;
+  const int64_t* offsets;   // device CSR offsets (num_groups + 1) or null
+  double tau;
+  const float* grad_scale;
+  const int32_t* L;
+  const float* A;
+  const double* slogr;
+  float* useq;
+  double* gloss;
+};
+
 // Scalar reduction (stage 2).
 struct FinalArgs {
   int64_t B;
@@ -158,6 +237,8 @@ struct FinalArgs {
   const double* P;
   const double* K;
   const int64_t* C;
+  const double* gloss;      // REAL: group losses; null otherwise
+  int64_t num_groups;       // REAL: number of groups
   float* scalars;
   int64_t* counts;
   uint32_t* status;
@@ -181,6 +262,10 @@ struct TokenArgs {
   double* P;
   double* K;
   int64_t* C;
+  const double* iwseq;      // seq-mask keep flags, or null
+  const float* useq;        // sequence-level: per-sequence gradient coefficient
+  const double* lseq;       // GSPO: sequence loss
+  const int32_t* cseq;      // GSPO: sequence clipped flag
   // outputs
   float* seq_policy;
   float* seq_kl;

@@ -7,7 +7,9 @@
 // on-policy form; CISPO) and the Relax REINFORCE++ page (Formula-level
 // comparison: SAPO's soft sigmoid gate).  KL estimators follow dockyard_rl
 // (Reference-KL penalty), the off-policy weight its Off-policy correction
-// section.  Everything is float32, as the rest of the row epilogue.
+// section.  Everything is float32, as the rest of the row epilogue.  The
+// sequence-level losses (GSPO, REAL) need whole sequences: here they
+// contribute only their KL part, and the sequence kernels add the rest.
 #pragma once
 
 #include <math.h>
@@ -29,12 +31,21 @@ __device__ __forceinline__ float clamp_sym(float x, float v) {
   return x != x ? x : fminf(fmaxf(x, -v), v);
 }
 
+// Off-policy weight of one token: exp(old - gen), truncated for tis/icepop.
+__device__ __forceinline__ float token_is_weight(const Objective& o, float old, float gen) {
+  float wi = expf(old - gen);
+  if (o.tis) wi = wi != wi ? wi : fminf(fmaxf(wi, o.tis_lo), o.tis_hi);
+  return wi;
+}
+
 // kGeneral = false: the clipped surrogate with k3, no dual clip, no clamps.
 // kGeneral = true: every form the Objective selects.  For the default
-// settings both evaluate the same expressions in the same order.
+// settings both evaluate the same expressions in the same order.  `keep` is
+// the sequence's seq-mask flag (read only with o.seq_mask).
 template <bool kGeneral>
 __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp, float old,
-                                                  float d, float adv, float gen) {
+                                                  float d, float adv, float gen,
+                                                  float keep = 1.0f) {
 #pragma clang fp contract(off)
   TokObj r;
   const float rho = expf(logp - old);
@@ -50,7 +61,11 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
   } else {
     float dloss;
     r.clipped = false;
-    if (o.pg == GRPO_PG_CLIP) {
+    if (o.seq) {
+      // GSPO / REAL: the policy part is formed per sequence
+      r.loss = 0.0f;
+      dloss = 0.0f;
+    } else if (o.pg == GRPO_PG_CLIP) {
       r.clipped = (adv > 0.0f && rho > o.hi) || (adv < 0.0f && rho < o.lo);
       const float unc = rho * adv;
       const float clp = fminf(fmaxf(rho, o.lo), o.hi) * adv;
@@ -87,10 +102,11 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
       r.loss = -adv;
       dloss = -adv;
     }
-    if (o.has_is) {
-      // constant weight of the current to the generating policy
-      float wi = expf(old - gen);
-      if (o.tis) wi = wi != wi ? wi : fminf(fmaxf(wi, o.tis_lo), o.tis_hi);
+    if (o.has_is && !o.seq) {
+      // constant weight of the current to the generating policy; a masked
+      // sequence (seq-mask) has weight 0 whatever the token's ratio
+      float wi = token_is_weight(o, old, gen);
+      if (o.seq_mask) wi = keep != 0.0f ? wi : 0.0f;
       r.loss = r.loss * wi;
       dloss = dloss * wi;
     }

@@ -20,6 +20,7 @@
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
 #include "grpo_internal.hpp"
+#include "grpo_objective.hpp"
 
 namespace grpo {
 
@@ -57,6 +58,7 @@ __device__ double sequence_weight(int32_t reduction, double alpha, double norm_c
 __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
 #pragma clang fp contract(off)
   __shared__ long long sh_i64[kPrepThreads / kWave];
+  __shared__ double sh_f64[kPrepThreads / kWave];
   __shared__ float sh_r[kRewardStage];
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -77,6 +79,31 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
     }
   }
   const long long L = block_sum_i64<kPrepThreads>(cnt, sh_i64);
+
+  // importance-weight statistic over the active tokens, in binary64 and a
+  // fixed tree: the sum of (old - gen) for sequence masking, the sum of the
+  // (truncated) token weights for the sequence ratio's mean weight
+  if (a.iw_mode != kIwNone) {
+    const int64_t base = i * a.T;
+    double acc = 0.0;
+    for (int64_t t = tid; t < a.T; t += kPrepThreads) {
+      if (a.mask != nullptr && a.mask[base + t] == 0) continue;
+      const float o = a.old[base + t], g = a.gen[base + t];
+      if (a.iw_mode == kIwSeqMask) acc = acc + (double(o) - double(g));
+      else acc = acc + double(token_is_weight(a.obj, o, g));
+    }
+    acc = block_sum_f64<kPrepThreads>(acc, sh_f64);
+    if (tid == 0) {
+      const double mean = acc / double(L > 0 ? L : 1);
+      if (a.iw_mode == kIwSeqMask) {
+        const double r = exp(mean);
+        a.iwseq[i] = (r >= a.seq_lo && r <= a.seq_hi) ? 1.0 : 0.0;
+      } else {
+        a.iwseq[i] = mean;
+      }
+    }
+  }
+  if (tid == 0 && a.useq) a.useq[i] = 0.0f;
 
   // group [s, e) of sequence i
   int64_t s, e;

@@ -21,7 +21,8 @@ constexpr int kRedThreads = 256;
 
 // Scalar stage (one block): policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i in
 // binary64, written as float32, plus the token and clip counts and the fault
-// bits of the call.
+// bits of the call.  For REAL the policy loss is instead the sum of the group
+// losses over the number of groups (ms-swift REAL blog, source walkthrough).
 constexpr int kFinalThreads = 1024;
 
 __global__ __launch_bounds__(kFinalThreads) void grpo_final_kernel(FinalArgs a) {
@@ -39,6 +40,12 @@ __global__ __launch_bounds__(kFinalThreads) void grpo_final_kernel(FinalArgs a) 
   pl = block_sum_f64<kFinalThreads>(pl, sh_f64);
   kl = block_sum_f64<kFinalThreads>(kl, sh_f64);
   ct = block_sum_i64<kFinalThreads>(ct, sh_i64);
+  if (a.gloss) {
+    double gl = 0.0;
+    for (int64_t g = tid; g < a.num_groups; g += kFinalThreads) gl = gl + a.gloss[g];
+    gl = block_sum_f64<kFinalThreads>(gl, sh_f64);
+    pl = gl / double(a.num_groups);
+  }
   if (tid == 0) {
     const double loss = pl + double(a.beta) * kl;
     a.scalars[0] = float(loss);
@@ -89,6 +96,17 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Sequence-level losses: a token's policy loss from its sequence's (GSPO:
+// omega_t * l_i, counted as clipped with its sequence; REAL: 0).
+__device__ __forceinline__ void seq_token(const Objective& o, TokObj& r, bool gspo, double lseq,
+                                          bool cseq, float old, float gen, bool has_gen) {
+  if (gspo) {
+    const float om = has_gen ? token_is_weight(o, old, gen) : 1.0f;
+    r.loss = float(double(om) * lseq);
+    r.clipped = cseq;
+  }
+}
+
 // One block per sequence: tokens -> dlogp and the per-sequence totals.  The
 // grpo.cpp README's token-loss kernels (CUDA section) compute the same loss
 // from per-token log-probs.  kGeneral selects the objective code path (see
@@ -105,6 +123,14 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   const float wg = float(a.w[i]) * (a.grad_scale ? *a.grad_scale : 1.0f);
   const bool has_ref = a.ref != nullptr;
   const bool has_gen = a.gen != nullptr;
+  const float keep = a.iwseq ? float(a.iwseq[i]) : 1.0f;
+  // sequence-level losses: the sequence kernels' loss, clip flag and
+  // gradient coefficient (grad_scale included) of this sequence
+  const bool seqlv = kGeneral && a.obj.seq;
+  const bool gspo = seqlv && a.obj.pg == GRPO_PG_GSPO;
+  const double lseq = gspo ? a.lseq[i] : 0.0;
+  const bool cseq = gspo && a.cseq[i] != 0;
+  const float useq = seqlv ? a.useq[i] : 0.0f;
   double p = 0.0, k = 0.0;
   long long c = 0;
   bool nonfinite = false;
@@ -157,8 +183,9 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
         for (int j = 0; j < 4; ++j) {
           if ((m4[u] >> (8 * j)) & 0xffu) {
             const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
-            const TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv, gnv[j]);
-            gv[j] = wg * r.g;
+            TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv, gnv[j], keep);
+            if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, odv[j], gnv[j], has_gen);
+            gv[j] = seqlv ? wg * r.g + useq : wg * r.g;
             tl[j] = r.loss;
             tk[j] = r.kl;
             p = p + double(r.loss);
@@ -181,9 +208,10 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
       if (a.mask == nullptr || a.mask[s] != 0) {
         const float lps = a.logp[s];
         const float d = has_ref ? a.ref[s] - lps : 0.0f;
-        const TokObj r = token_objective<kGeneral>(a.obj, lps, a.old[s], d, adv,
-                                                   has_gen ? a.gen[s] : 0.0f);
-        g = wg * r.g;
+        const float ods = a.old[s], gns = has_gen ? a.gen[s] : 0.0f;
+        TokObj r = token_objective<kGeneral>(a.obj, lps, ods, d, adv, gns, keep);
+        if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, ods, gns, has_gen);
+        g = seqlv ? wg * r.g + useq : wg * r.g;
         tl = r.loss;
         tk = r.kl;
         p = p + double(r.loss);

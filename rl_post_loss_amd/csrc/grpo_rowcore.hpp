@@ -275,15 +275,17 @@ struct RowGrad {
 
 __device__ __forceinline__ RowGrad row_epilogue(const RowArgs& a, int64_t row, Lse sx, Lse sy,
                                                 float xa, float ya, bool has_ref, float old,
-                                                float gen, float adv, float wgt, float gs) {
+                                                float gen, float adv, float wgt, float gs,
+                                                float keep) {
   const RowLogp px = finish_row(sx, xa);
   const float d = has_ref ? row_log_ratio(px, finish_row(sy, ya)) : 0.0f;
-  const TokObj t = token_objective<true>(a.obj, px.logp, old, d, adv, gen);
+  const TokObj t = token_objective<true>(a.obj, px.logp, old, d, adv, gen, keep);
   const float G = wgt * gs * t.g;
   if (!(isfinite(t.loss) && isfinite(t.kl) && isfinite(G))) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
   a.tok_loss[row] = t.loss;
   a.tok_kl[row] = t.kl;
   a.flags[row] = t.clipped ? 1 : 0;
+  if (a.tok_logp) a.tok_logp[row] = px.logp;
   if (a.out_logp) a.out_logp[row] = px.logp;
   if (a.out_loss) a.out_loss[row] = t.loss;
   if (a.out_kl) a.out_kl[row] = t.kl;
@@ -297,6 +299,7 @@ __device__ __forceinline__ void row_inactive(const RowArgs& a, int64_t row, bool
   a.tok_kl[row] = 0.0f;
   a.flags[row] = 0;
   a.stash[row] = RowStash{0.0f, 0.0f, 0.0f, 0.0f};
+  if (a.tok_logp) a.tok_logp[row] = 0.0f;
   if (a.out_logp) a.out_logp[row] = 0.0f;
   if (a.out_loss) a.out_loss[row] = 0.0f;
   if (a.out_kl) a.out_kl[row] = 0.0f;

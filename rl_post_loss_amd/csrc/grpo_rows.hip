@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
                                : nullptr;
 
     // per-token side inputs, loaded early by the finishing lane
-    float old = 0.0f, gen = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f;
+    float old = 0.0f, gen = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f, keep = 1.0f;
     if (lid == 0) {
       old = a.old[row];
       if (a.gen) gen = a.gen[row];
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       adv = a.A[i];
       wgt = float(a.w[i]);
       if (a.grad_scale) gs = *a.grad_scale;
+      if (a.iwseq) keep = float(a.iwseq[i]);
     }
 
     // ---- pass 1 ----------------------------------------------------------
@@ -188,11 +189,12 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
 
     // ---- per-token epilogue -------------------------------------------------
     if (lid == 0) {
-      const RowGrad rg = row_epilogue(a, row, sx, sy, xa, ya, has_ref, old, gen, adv, wgt, gs);
+      const RowGrad rg = row_epilogue(a, row, sx, sy, xa, ya, has_ref, old, gen, adv, wgt, gs,
+                                      keep);
       G = rg.G;
       c2 = rg.c2;
       omp = rg.omp;
-      if constexpr (!kPass2) a.stash[row] = RowStash{G, c2, omp, 0.0f};
+      if constexpr (!kPass2) a.stash[row] = RowStash{G, c2, omp, 1.0f};
     }
     if constexpr (!kPass2) return;
     // broadcast G, c2, omp to the row's threads
@@ -212,9 +214,11 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       omp = __shfl(omp, 0);
     }
   } else {
-    // backward only: per-row state from the forward pass
+    // backward only: per-row state from the forward pass, plus the policy
+    // part of the sequence-level losses (0 for the token-level ones)
     const RowStash st = a.stash[row];
-    G = st.G * (a.grad_scale ? *a.grad_scale : 1.0f);
+    G = st.act != 0.0f ? (st.G + a.useq[row / a.T]) * (a.grad_scale ? *a.grad_scale : 1.0f)
+                       : 0.0f;
     c2 = st.c;
     omp = st.omp;
     if (G != 0.0f) aid = load_action(a, row);

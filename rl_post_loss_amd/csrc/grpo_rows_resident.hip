@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
                              : nullptr;
   const raw_t* yp = reinterpret_cast<const raw_t*>(yrow) + lid;
 
-  float old = 0.0f, gen = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f;
+  float old = 0.0f, gen = 0.0f, adv = 0.0f, wgt = 0.0f, gs = 1.0f, keep = 1.0f;
   if (lid == 0) {
     old = a.old[row];
     if (a.gen) gen = a.gen[row];
@@ -75,6 +75,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
     adv = a.A[i];
     wgt = float(a.w[i]);
     if (a.grad_scale) gs = *a.grad_scale;
+    if (a.iwseq) keep = float(a.iwseq[i]);
   }
 
   // ---- issue the loads -----------------------------------------------------
@@ -174,7 +175,8 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
       sx = lse_merge(sx, sh_lse[0][k]);
       if (has_ref) sy = lse_merge(sy, sh_lse[1][k]);
     }
-    const RowGrad rg = row_epilogue(a, row, sx, sy, sh_xa[0], sh_xa[1], has_ref, old, gen, adv, wgt, gs);
+    const RowGrad rg = row_epilogue(a, row, sx, sy, sh_xa[0], sh_xa[1], has_ref, old, gen, adv, wgt, gs,
+                                    keep);
     sh_bcast[0] = rg.G;
     sh_bcast[1] = rg.c2;
     sh_bcast[2] = rg.omp;

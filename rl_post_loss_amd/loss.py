@@ -103,7 +103,7 @@ def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_b
 OBJECTIVE_DEFAULTS = dict(pg_loss="clip", kl_estimator="k3", dual_clip_c=None, sapo_tau_pos=1.0,
                           sapo_tau_neg=1.0, kl_input_clamp=None, kl_output_clamp=None,
                           norm_constant=None, tis_type=None, tis_ratio_min=None,
-                          tis_ratio_max=None)
+                          tis_ratio_max=None, real_tau=0.5)
 
 
 def _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, objective):
@@ -129,7 +129,7 @@ def _optional_positive(name, v):
 
 def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, *, pg_loss, kl_estimator,
               dual_clip_c, sapo_tau_pos, sapo_tau_neg, kl_input_clamp, kl_output_clamp,
-              norm_constant, tis_type, tis_ratio_min, tis_ratio_max):
+              norm_constant, tis_type, tis_ratio_min, tis_ratio_max, real_tau):
     c = GrpoCfg()
     c.eps_low = float(clip_eps if eps_low is None else eps_low)
     c.eps_high = float(clip_eps if eps_high is None else eps_high)
@@ -155,9 +155,11 @@ def _make_cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, *, pg_loss, k
     c.tis_type = _abi.TIS_CODES[tis_type]
     if tis_type is not None:
         _need(tis_ratio_max is not None, "truncated IS needs tis_ratio_max")
-        _need(tis_type == "tis" or tis_ratio_min is not None, "icepop needs tis_ratio_min")
+        _need(tis_type == "tis" or tis_ratio_min is not None,
+              "icepop and seq_mask need tis_ratio_min")
         c.tis_ratio_min = 0.0 if tis_ratio_min is None else float(tis_ratio_min)
         c.tis_ratio_max = float(tis_ratio_max)
+    c.real_tau = float(real_tau)
     return c
 
 
@@ -177,6 +179,7 @@ class GRPOResult:
     tok_logp: torch.Tensor | None = None
     tok_loss: torch.Tensor | None = None
     tok_kl: torch.Tensor | None = None
+    seq_logratio: torch.Tensor | None = None   # [B] s_i (GSPO and REAL only)
     _c_outputs: object = None   # the GrpoOutputs struct pointing at these tensors
 
     @property
@@ -198,6 +201,7 @@ def _outputs(B, T, device, per_token, want_logp):
         scalars=torch.empty(3, **f32), advantages=torch.empty(B, **f32),
         seq_policy=torch.empty(B, **f32), seq_kl=torch.empty(B, **f32),
         seq_weight=torch.empty(B, **f32),
+        seq_logratio=torch.zeros(B, **f32),
         seq_tokens=torch.empty(B, dtype=torch.int32, device=device),
         counts=torch.empty(2, dtype=torch.int64, device=device),
         status=torch.empty(1, dtype=torch.int32, device=device))
@@ -218,6 +222,7 @@ def _outputs(B, T, device, per_token, want_logp):
     o.tok_logp = _ptr(res.tok_logp)
     o.tok_loss = _ptr(res.tok_loss)
     o.tok_kl = _ptr(res.tok_kl)
+    o.seq_logratio = res.seq_logratio.data_ptr()
     res._c_outputs = o
     return res, o
 
@@ -288,7 +293,10 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
     off-policy importance weight (None: no correction).
     ``objective``: the keywords of OBJECTIVE_DEFAULTS (policy-loss form, KL
     estimator, dual clip, SAPO temperatures, KL clamps, fixed normaliser,
-    truncation of the importance weight)."""
+    truncation of the importance weight, REAL temperature).  pg_loss "gspo"
+    (sequence ratio) and "real" (in-group classification) are the
+    sequence-level forms; their per-sequence mean log-ratio lands in
+    ``seq_logratio``."""
     lib = load_library()
     dev = logp.device
     _need(logp.dim() == 2 and logp.is_cuda, "logp must be a [B, T] GPU tensor")

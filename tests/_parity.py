@@ -109,7 +109,8 @@ def _terms_at(ref, cfg, dlogp=0.0, dd=0.0):
         old = np.where(act, t["logp"] - np.log(np.where(act, t["rho"], 1.0)), 0.0)
         lp = t["logp"] + dlogp
         lref = t["logp"] + t["d"] + dlogp + dd
-        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg, t.get("gen"))
+        keep = None if ref.seq_keep is None else np.broadcast_to(ref.seq_keep[:, None], lp.shape)
+        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg, t.get("gen"), keep)
     for k, v in out.items():
         out[k] = np.where(act, v, np.zeros_like(v))
     return out
@@ -241,19 +242,26 @@ def compare_exact_parts(res, ref, what=""):
 GRAD16_BAR = {"bf16": (2.0 ** -7, 2.0 ** -126), "f16": (2.0 ** -10, 2.0 ** -24)}
 
 
-def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids=None):
+def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids=None,
+                        branches=None):
     """grad_gpu: float64 numpy [B, T, V]; ref: oracle result with grad.
     gdt: the gradient's storage, "f32", "bf16" or "f16" (True means "bf16",
     False "f32").
     policy, ids: host policy logits and action ids, needed only to rebuild a
-    row whose oracle G is exactly zero when the GPU took the other branch."""
+    row whose oracle G is exactly zero when the GPU took the other branch.
+    branches: precomputed (flag-ambiguous, branch-ambiguous, candidate G
+    list, relative G tolerance, ill-conditioned) for the sequence-level
+    losses (seq_branches); None derives them per token."""
     if gdt is True or gdt is False:
         gdt = "bf16" if gdt else "f32"
     bf16 = gdt != "f32"                         # a 16-bit per-element bar
     base, floor = GRAD16_BAR.get(gdt, (None, None))
     g = grad_gpu
     r = ref.grad
-    flag_amb, amb, cands = branch_ambiguity(ref, cfg, mask)
+    if branches is None:
+        flag_amb, amb, cands = branch_ambiguity(ref, cfg, mask)
+    else:
+        flag_amb, amb, cands = branches[:3]
     stats = dict(ambiguous=int(flag_amb.sum()), branch_ambiguous=int(amb.sum()), illcond=0,
                  rows=int(mask.sum()))
     # masked rows: exactly zero
@@ -268,7 +276,7 @@ def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids
         return np.abs(gi - ri) <= 1e-5 * gmax + 1e-30
 
     if bf16:
-        tol, ill = g_rel_tolerance(ref, cfg, base)
+        tol, ill = g_rel_tolerance(ref, cfg, base) if branches is None else branches[3:5]
         stats["illcond"] = int((ill & mask).sum())
         ok = row_ok(g, r, tol[..., None])
     else:
@@ -304,3 +312,133 @@ def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids
             f"gpu={g[i, t, k]!r} oracle={r[i, t, k]!r} G={ref.tok['G'][i, t]!r} "
             f"rho={ref.tok['rho'][i, t]!r} A={ref.advantages[i]!r} d={ref.tok['d'][i, t]!r}")
     return stats
+
+
+# ---------------------------------------------------------------------------
+# Sequence-level losses (GSPO, REAL).  Their policy part depends on s_i, the
+# mean log-ratio of a sequence, which the GPU forms from float32 log-probs:
+# its error is at most the log-prob error.  As for the token-level helpers,
+# the oracle evaluated at s +- e (and at d +- e for the KL part) gives the
+# candidate G of a sequence at a branch point (a GSPO sequence at its clip
+# bound) and the propagated error of G and of the values elsewhere.
+# ---------------------------------------------------------------------------
+
+SEQ_ABS_ERR = 2 * LOGP_ABS_ERR
+
+
+def _active_index(mask):
+    ii, tt = np.nonzero(mask)
+    return ii, tt
+
+
+def _token_is_weights(cfg, h, mask):
+    """Off-policy weight of every slot (1 without generating log-probs; 0 at
+    masked slots)."""
+    if h.get("gen_logps") is None:
+        return mask.astype(np.float64)
+    om = oracle.is_weights(h["old_logps"], h["gen_logps"], cfg)
+    return np.where(mask, om, 0.0)
+
+
+def _seq_policy_part(ref, cfg, s, h, mask, groups):
+    """Per sequence (gpol coefficient, policy value l_i or group losses) at
+    log-ratios s, via the oracle's own sequence functions."""
+    B = mask.shape[0]
+    A = ref.advantages
+    L = ref.seq_tokens
+    w = ref.seq_weight
+    if cfg.pg_loss == "gspo":
+        _, l_seq, dl_ds, clipped = oracle.gspo_terms(s, A, cfg)
+        om_mean = _token_is_weights(cfg, h, mask).sum(axis=1) / np.maximum(L, 1)
+        return dict(coef=w * om_mean * dl_ds, value=l_seq, branch=clipped, om_mean=om_mean)
+    off = oracle.group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    gl, dpol, pol = oracle.real_terms(s, A, L, off, cfg.real_tau)
+    return dict(coef=dpol / np.maximum(L, 1), value=gl, policy_loss=pol,
+                branch=np.zeros(B, dtype=bool), dpol=dpol)
+
+
+def _seq_G(ref, cfg, part, dkl):
+    return part["coef"][:, None] + ref.seq_weight[:, None] * (cfg.beta * dkl)
+
+
+def seq_branches(ref, cfg, mask, h, groups, base, e_s=SEQ_ABS_ERR, e_d=4 * LOGP_ABS_ERR):
+    """(flag-ambiguous, branch-ambiguous [B, T], candidate G list, relative G
+    tolerance [B, T], ill-conditioned [B, T]) for a sequence-level loss."""
+    s = ref.seq_logratio
+    center = _seq_policy_part(ref, cfg, s, h, mask, groups)
+    dkl0 = ref.tok["dkl"]
+    G0 = _seq_G(ref, cfg, center, dkl0)
+    cands = [G0]
+    flag = np.zeros(mask.shape, dtype=bool)
+    anyb = np.zeros(mask.shape, dtype=bool)
+    dG = np.zeros(mask.shape)
+    for ds in (e_s, -e_s):
+        part = _seq_policy_part(ref, cfg, s + ds, h, mask, groups)
+        Gp = _seq_G(ref, cfg, part, dkl0)
+        cands.append(Gp)
+        chg = (part["branch"] != center["branch"])[:, None] & mask
+        flag |= chg
+        anyb |= chg
+        dG = np.maximum(dG, np.where(chg, 0.0, np.abs(Gp - G0)))
+    dGd = np.zeros(mask.shape)
+    for dd in (e_d, -e_d):
+        _, dkl = oracle.kl_terms(ref.tok["d"] + dd, cfg)
+        dkl = np.where(mask, dkl, 0.0)
+        Gp = _seq_G(ref, cfg, center, dkl)
+        cands.append(Gp)
+        chg = ((dkl == 0) != (dkl0 == 0)) & mask
+        anyb |= chg
+        dGd = np.maximum(dGd, np.where(chg, 0.0, np.abs(Gp - G0)))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(G0 != 0, (dG + dGd) / np.abs(G0), np.inf)
+    return flag & mask, anyb & mask, cands, np.maximum(base, rel), (rel > base) & (G0 != 0) & mask
+
+
+def compare_seq_outputs(res, ref, cfg, mask, h, groups, rtol, what=""):
+    """Scalars, per-sequence and per-token values of a sequence-level loss.
+    Returns the number of sequences at a clip bound (either branch correct)."""
+    B = mask.shape[0]
+    s = ref.seq_logratio
+    gs = to_np(res.seq_logratio)
+    lim_s = SEQ_ABS_ERR + 2.0 ** -23 * np.abs(s)
+    assert np.all(np.abs(gs - s) <= lim_s), (
+        f"{what} seq_logratio worst {np.max(np.abs(gs - s) / lim_s):.3g}x of bound")
+    center = _seq_policy_part(ref, cfg, s, h, mask, groups)
+    _, pk = value_bounds(ref, cfg)
+    kl_prop = float(np.sum(ref.seq_weight * pk.sum(axis=1)))
+    ambiguous_seq = np.zeros(B, dtype=bool)
+    if cfg.pg_loss == "gspo":
+        # error of l_i from s +- e (a sequence at its clip bound may take either branch)
+        dval = np.zeros(B)
+        for ds in (SEQ_ABS_ERR, -SEQ_ABS_ERR):
+            part = _seq_policy_part(ref, cfg, s + ds, h, mask, groups)
+            ambiguous_seq |= part["branch"] != center["branch"]
+            dval = np.maximum(dval, np.abs(part["value"] - center["value"]))
+        dval = dval + rtol * np.abs(center["value"])
+        om = _token_is_weights(cfg, h, mask)
+        tok_bound = om * dval[:, None] + rtol * np.abs(ref.tok["loss"]) + 1e-30
+        tl = to_np(res.tok_loss)
+        bad = (np.abs(tl - ref.tok["loss"]) > tok_bound) & mask
+        assert not bad.any(), f"{what} tok_loss: {int(bad.sum())} values out of bound"
+        assert np.all(tl[~mask] == 0.0), f"{what} tok_loss at masked slots"
+        seq_bound = tok_bound.sum(axis=1)
+        sp = to_np(res.seq_policy)
+        assert np.all(np.abs(sp - ref.seq_policy) <= seq_bound), f"{what} seq_policy"
+        pol_prop = float(np.sum(ref.seq_weight * seq_bound))
+        pol_scale = float(np.sum(ref.seq_weight * np.abs(ref.seq_policy)))
+    else:
+        pol_prop = float(np.sum(np.abs(center["dpol"]))) * SEQ_ABS_ERR
+        pol_scale = float(np.sum(np.abs(center["value"]))) / max(len(center["value"]), 1)
+        assert np.all(to_np(res.seq_policy) == 0.0), f"{what} REAL seq_policy must be 0"
+        assert np.all(to_np(res.tok_loss) == 0.0), f"{what} REAL token losses must be 0"
+    loss = float(res.loss)
+    lim = rtol * abs(ref.loss) + pol_prop + cfg.beta * kl_prop + 1e-30
+    assert abs(loss - ref.loss) <= lim, (
+        f"{what} loss gpu={loss!r} oracle={ref.loss!r} bound {lim:.3g}")
+    assert abs(float(res.policy_loss) - ref.policy_loss) <= rtol * pol_scale + pol_prop + 1e-30, (
+        f"{what} policy_loss gpu={float(res.policy_loss)!r} oracle={ref.policy_loss!r}")
+    scale_k = float(np.sum(ref.seq_weight * np.abs(ref.tok["kl"]).sum(axis=1))) + 1e-30
+    assert abs(float(res.kl) - ref.kl) <= rtol * scale_k + kl_prop, f"{what} kl"
+    tk = rtol * np.abs(ref.tok["kl"]).sum(axis=1) + pk.sum(axis=1) + 1e-30
+    assert np.all(np.abs(to_np(res.seq_kl) - ref.seq_kl) <= tk), f"{what} seq_kl"
+    return int(ambiguous_seq.sum())

@@ -160,8 +160,16 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, cfg=_cfg(red=2, alpha=1.5)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(red=3)) == E["GRPO_ERR_CONFIG"]             # no norm_constant
     assert _fwd(lib, cfg=_cfg(red=3, norm_constant=float("inf"))) == E["GRPO_ERR_CONFIG"]
-    assert _fwd(lib, cfg=_cfg(pg_loss=5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=7)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(pg_loss=-1)) == E["GRPO_ERR_CONFIG"]
+    # sequence-level losses: GSPO excludes the token mean and the dual clip;
+    # REAL needs the token mean, a positive temperature and no gen_logps
+    assert _fwd(lib, cfg=_cfg(pg_loss=5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=5, red=1, dual_clip_c=3.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=6, red=1, real_tau=0.5)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=6, real_tau=0.0)) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=6, real_tau=float("inf"))) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(pg_loss=6, real_tau=0.5), gen=FAKE) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(kl_estimator=3)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(dual_clip_c=1.0)) == E["GRPO_ERR_CONFIG"]    # needs c > 1
     assert _fwd(lib, cfg=_cfg(dual_clip_c=3.0, pg_loss=1)) == E["GRPO_ERR_CONFIG"]
@@ -169,7 +177,10 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, cfg=_cfg(kl_input_clamp=-1.0)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(kl_output_clamp=float("nan"))) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(tis_type=1, tis_ratio_max=2.0)) == E["GRPO_ERR_CONFIG"]  # no gen
-    assert _fwd(lib, cfg=_cfg(tis_type=3, tis_ratio_max=2.0), gen=FAKE) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=4, tis_ratio_max=2.0), gen=FAKE) == E["GRPO_ERR_CONFIG"]
+    assert _fwd(lib, cfg=_cfg(tis_type=3, tis_ratio_max=2.0)) == E["GRPO_ERR_CONFIG"]   # no gen
+    assert _fwd(lib, cfg=_cfg(tis_type=3, tis_ratio_min=0.5, tis_ratio_max=2.0, pg_loss=5, red=1),
+                gen=FAKE) == E["GRPO_ERR_CONFIG"]                   # not with sequence ratios
     assert _fwd(lib, cfg=_cfg(tis_type=2, tis_ratio_max=0.0), gen=FAKE) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(tis_type=2, tis_ratio_min=3.0, tis_ratio_max=2.0),
                 gen=FAKE) == E["GRPO_ERR_CONFIG"]

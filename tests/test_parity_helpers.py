@@ -25,6 +25,7 @@ VARIANTS = [
     dict(kl_input_clamp=0.2, kl_output_clamp=0.02),
     dict(reduction="fixed_constant", norm_constant=50.0),
     dict(tis_type="icepop", tis_ratio_min=0.7, tis_ratio_max=1.4, pg_loss="cispo"),
+    dict(tis_type="seq_mask", tis_ratio_min=0.8, tis_ratio_max=1.25),
 ]
 
 
@@ -129,4 +130,121 @@ def test_branch_flip_rejected_away_from_bounds_accepted_at_a_bound():
     g = ref2.grad.copy()
     g[i, t] = G_un * (onehot - p)
     stats = compare_logits_grad(g, ref2, cfg, mask, False, policy=x, ids=ids)
+    assert stats["ambiguous"] >= 1
+
+
+# --- sequence-level losses ----------------------------------------------------
+
+SEQ_VARIANTS = [
+    dict(pg_loss="gspo", reduction="sequence_mean"),
+    dict(pg_loss="gspo", reduction="length_alpha", alpha=0.5, kl_estimator="k2"),
+    dict(pg_loss="gspo", reduction="sequence_mean", tis_type="tis", tis_ratio_max=1.3),
+    dict(pg_loss="real"),
+    dict(pg_loss="real", real_tau=0.2, kl_input_clamp=0.2),
+]
+
+
+def _seq_case(seed, shift=0.4):
+    x, y, ids, old, mask, r = _case(seed, old_std=0.3)
+    old = old + np.random.default_rng(seed + 100).uniform(-shift, shift, (old.shape[0], 1))
+    return x, y, ids, old, mask, r
+
+
+def _seq_as_result(ref, grad_dtype=torch.float32):
+    res = _as_result(ref, grad_dtype)
+    res.seq_logratio = torch.tensor(ref.seq_logratio, dtype=torch.float32)
+    return res
+
+
+def _seq_run(kw, seed):
+    from _parity import compare_seq_outputs, seq_branches  # noqa: F401
+    cfg = oracle.LossConfig(beta=0.1, **kw)
+    x, y, ids, old, mask, r = _seq_case(seed)
+    gen = old + np.random.default_rng(seed + 9).normal(0, 0.4, old.shape) if "tis_type" in kw else None
+    groups = dict(samples_per_prompt=2)
+    ref = oracle.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=groups, cfg=cfg, gen_logps=gen)
+    h = dict(old_logps=old, gen_logps=gen)
+    return cfg, x, ids, mask, ref, h, groups
+
+
+@pytest.mark.parametrize("kw", SEQ_VARIANTS, ids=str)
+def test_seq_helpers_accept_rounded_oracle(kw):
+    from _parity import GRAD16_BAR, compare_seq_outputs, seq_branches
+    cfg, x, ids, mask, ref, h, groups = _seq_run(kw, 11)
+    if kw["pg_loss"] == "gspo":
+        assert ref.clipped > 0
+    for dt, gdt in ((torch.float32, "f32"), (torch.bfloat16, "bf16"), (torch.float16, "f16")):
+        res = _seq_as_result(ref, dt)
+        compare_seq_outputs(res, ref, cfg, mask, h, groups, 1e-5)
+        base = GRAD16_BAR.get(gdt, (1e-5, 0))[0]
+        br = seq_branches(ref, cfg, mask, h, groups, base)
+        compare_logits_grad(res.grad.double().numpy(), ref, cfg, mask, gdt, branches=br)
+
+
+@pytest.mark.parametrize("kw", [SEQ_VARIANTS[0], SEQ_VARIANTS[3]], ids=str)
+def test_seq_helpers_reject_planted_mistakes(kw):
+    from _parity import compare_seq_outputs, seq_branches
+    cfg, x, ids, mask, ref, h, groups = _seq_run(kw, 12)
+    res = _seq_as_result(ref)
+    res.loss = torch.tensor(ref.loss * (1 + 1e-3) + 1e-6, dtype=torch.float32)
+    with pytest.raises(AssertionError):
+        compare_seq_outputs(res, ref, cfg, mask, h, groups, 1e-5)
+    res = _seq_as_result(ref)
+    res.seq_logratio = res.seq_logratio + 1e-4
+    with pytest.raises(AssertionError):
+        compare_seq_outputs(res, ref, cfg, mask, h, groups, 1e-5)
+    res = _seq_as_result(ref)
+    res.policy_loss = torch.tensor(ref.policy_loss * 1.01 + 1e-6, dtype=torch.float32)
+    with pytest.raises(AssertionError):
+        compare_seq_outputs(res, ref, cfg, mask, h, groups, 1e-5)
+    # one gradient row off by 5 %
+    i, t = [int(v[0]) for v in np.nonzero(mask & (np.abs(ref.tok["G"]) > 1e-3))]
+    g = ref.grad.copy()
+    g[i, t] *= 1.05
+    br = seq_branches(ref, cfg, mask, h, groups, 2.0 ** -7)
+    with pytest.raises(AssertionError):
+        compare_logits_grad(g, ref, cfg, mask, "bf16", branches=br)
+
+
+def test_seq_branch_flip_rejected_away_from_bounds_accepted_at_a_bound():
+    from _parity import SEQ_ABS_ERR, seq_branches
+    kw = dict(pg_loss="gspo", reduction="sequence_mean")
+    cfg = oracle.LossConfig(beta=0.0, **kw)
+    x, _, ids, _, mask, _ = _seq_case(13)
+    groups = dict(samples_per_prompt=2)
+    r = np.tile([0.0, 1.0], 4)
+    lse = scipy.special.logsumexp(x, axis=-1)
+    logp = np.take_along_axis(x, ids[..., None], -1)[..., 0] - lse
+    A = oracle.group_advantages(r, oracle.group_offsets(8, 2))
+    k = int(np.nonzero(A > 0)[0][0])
+
+    def run(shift_k):
+        old = logp.copy()
+        old[k] = logp[k] - shift_k               # sequence k's log-ratio is shift_k exactly
+        ref = oracle.grpo_loss_fwd_bwd(x, None, ids, old, mask, r, groups=groups, cfg=cfg)
+        return ref, dict(old_logps=old, gen_logps=None)
+
+    def unclipped_rows(ref, g):
+        rho = np.exp(ref.seq_logratio[k])
+        for t in np.nonzero(mask[k])[0]:
+            p = scipy.special.softmax(x[k, t])
+            onehot = np.zeros_like(p)
+            onehot[ids[k, t]] = 1.0
+            g[k, t] = -ref.seq_weight[k] * A[k] * rho * (onehot - p)
+        return g
+
+    # far above the band (rho = e^0.5): flipping the sequence to unclipped is caught
+    ref, h = run(0.5)
+    assert ref.clipped == ref.seq_tokens[k]
+    br = seq_branches(ref, cfg, mask, h, groups, 1e-5)
+    with pytest.raises(AssertionError):
+        compare_logits_grad(unclipped_rows(ref, ref.grad.copy()), ref, cfg, mask, "f32", policy=x,
+                            ids=ids, branches=br)
+    # a hair above the upper bound: either branch is right
+    ref2, h2 = run(np.log(1.2) + SEQ_ABS_ERR / 4)
+    assert ref2.clipped == ref2.seq_tokens[k]
+    br2 = seq_branches(ref2, cfg, mask, h2, groups, 1e-5)
+    assert br2[0][k][mask[k]].all()
+    stats = compare_logits_grad(unclipped_rows(ref2, ref2.grad.copy()), ref2, cfg, mask, "f32",
+                                policy=x, ids=ids, branches=br2)
     assert stats["ambiguous"] >= 1

@@ -9,4 +9,5 @@ from .synth import (  # noqa: F401
     make_gen_logps,
     make_token_inputs,
     poison_masked,
+    shift_by_sequence,
 )

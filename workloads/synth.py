@@ -247,6 +247,14 @@ def make_gen_logps(old_logps, seed=0, std=0.3):
     return (old_logps.float() + noise).contiguous()
 
 
+def shift_by_sequence(t, seed=0, spread=0.4):
+    """t [B, T] plus one offset per sequence drawn from U(-spread, spread),
+    seeded: moves whole sequences' log-ratios across a clip band."""
+    g = _gen(t.device, seed + 104729)
+    off = (torch.rand((t.shape[0], 1), generator=g, device=t.device) * 2.0 - 1.0) * spread
+    return (t.float() + off).contiguous()
+
+
 def poison_masked(inputs, V=None):
     """Write NaN/+-Inf into every masked slot's logits rows and old log-probs
     and out-of-range ids into masked action ids (masked slots must never be
