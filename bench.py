@@ -1,6 +1,6 @@
 """Benchmark of the GRPO loss hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--objective NAME]
 
 One step is one grpo_loss_fwd_bwd call (advantages and weights, the fused
 vocabulary pass with the analytic gradient, the fixed-order reductions) over
@@ -12,6 +12,13 @@ Prints one JSON line with tokens/s (all B*T slots per second), the roofline of
 the vocabulary kernel (algorithmic bytes over its own HIP-event-timed
 duration, against 8 TB/s HBM), and the fp64 CPU oracle's rate on a bounded
 sample of the same workload.
+
+--objective selects another per-token or sequence-level objective on the same
+workload (default: the clipped surrogate with k3 the workload names).  The
+sequence-level ones (gspo, real) run a forward row pass, the per-sequence
+phase and a gradient pass; the timed "vocabulary kernel" then spans all three
+and the byte model is unchanged (policy read twice, reference once, gradient
+written once).
 
 Auxiliary modes (for the HBM-traffic counters, see profiles/):
   --calibrate-only       run only a plain elementwise kernel over 2 GiB that
@@ -44,6 +51,15 @@ KERNEL_SOURCES = ["rl_post_loss_amd/csrc/grpo_rows.hip", "rl_post_loss_amd/csrc/
                   "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_objective.hpp",
                   "rl_post_loss_amd/csrc/grpo_api.hip"]
 CALIB_BYTES = 1 << 31   # 2 GiB copy for counter calibration
+
+# objective presets: (keyword overrides, needs generating log-probs)
+OBJECTIVES = {
+    "default": ({}, False),
+    "cispo": (dict(pg_loss="cispo"), False),
+    "gspo": (dict(pg_loss="gspo", reduction="sequence_mean"), False),
+    "real": (dict(pg_loss="real", reduction="token_mean"), False),
+    "seq_mask": (dict(tis_type="seq_mask", tis_ratio_min=0.8, tis_ratio_max=1.25), True),
+}
 
 
 def kernel_source_hash():
@@ -223,7 +239,7 @@ def run_token(args):
 def run(args):
     import torch
     import rl_post_loss_amd as rpl
-    from workloads import WORKLOADS, make_logits_inputs
+    from workloads import WORKLOADS, make_gen_logps, make_logits_inputs
 
     rpl.load_library()
     dev = torch.device("cuda:0")
@@ -240,10 +256,13 @@ def run(args):
     kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=wl.reductions[0],
               alpha=wl.alpha)
     kw.update(wl.groups_kwargs())
+    obj, needs_gen = OBJECTIVES[args.objective]
+    kw.update(obj)
+    gen = make_gen_logps(inp["old_logps"], seed=args.seed) if needs_gen else None
 
     def step():
         return rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
-                                     inp["rewards"], inp["mask"], grad_out=grad, **kw)
+                                     inp["rewards"], inp["mask"], grad_out=grad, gen_logps=gen, **kw)
 
     for _ in range(args.warmup):
         res = step()
@@ -270,7 +289,7 @@ def run(args):
     rows = B * T
     alg_bytes = byte_model(wl, active, rows)
     achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name) if args.objective == "default" else None
     value = rows / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC,
@@ -287,8 +306,10 @@ def run(args):
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: B={B} ({len(wl.group_sizes)} groups), T={T}, V={V}, "
-                        f"{wl.dtype} logits and gradient, {wl.reductions[0]}, "
-                        f"{'full mask' if wl.len_range is None else 'ragged lengths %d..%d' % wl.len_range}",
+                        f"{wl.dtype} logits and gradient, {kw['reduction']}, "
+                        f"{'full mask' if wl.len_range is None else 'ragged lengths %d..%d' % wl.len_range}"
+                        + ("" if args.objective == "default" else f", objective {args.objective}"),
+            "objective": {k: v for k, v in obj.items()},
             "B": B, "T": T, "V": V, "storage": wl.dtype, "active_slots": active,
             "hbm_fraction_of_step": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "bit_reproducible": bool(repro),
@@ -305,7 +326,7 @@ def run(args):
             "algorithmic_bytes": alg_bytes,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.objective == "default":
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, inp, target_s=args.cpu_seconds)
     else:
@@ -389,6 +410,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="logits_v151936")
+    ap.add_argument("--objective", default="default", choices=sorted(OBJECTIVES))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -52,17 +52,22 @@ def _run(cmd):
     return p.returncode, out
 
 
-def build_library(verbose=False, jobs=None):
+def build_library(verbose=False, jobs=None, extra_flags=(), lib_path=None, build_dir=None):
     """Compiles every csrc/*.hip for gfx950 and links libgrpo.so.  Always
-    rebuilds.  Raises RuntimeError with the compiler output on failure."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    rebuilds.  Raises RuntimeError with the compiler output on failure.
+    extra_flags (e.g. a -D tuning knob), lib_path and build_dir serve
+    side-by-side builds of variants; the defaults build the library the
+    package loads."""
+    lib = lib_path or LIB
+    bdir = build_dir or BUILD_DIR
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(bdir, os.path.basename(s) + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), 8)
 
     def compile_one(pair):
         src, obj = pair
-        return src, _run([HIPCC, *FLAGS, "-c", src, "-o", obj])
+        return src, _run([HIPCC, *FLAGS, *extra_flags, "-c", src, "-o", obj])
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(compile_one, zip(srcs, objs)))
@@ -71,12 +76,12 @@ def build_library(verbose=False, jobs=None):
             print(out)
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{out}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     rc, out = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def clean():

@@ -245,12 +245,19 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 #endif
 
 #ifndef GRPO_NT_LARGE
-#define GRPO_NT_LARGE 1024  // threads per row for rows above 64 KB
+#define GRPO_NT_LARGE 1024  // threads per row for rows above 64 KB (fused kernel)
+#endif
+#ifndef GRPO_NT_SPLIT
+#define GRPO_NT_SPLIT 256   // threads per row above 4 KB for the forward-only and
+                            // gradient-only kernels (several rows per CU, measured best)
 #endif
 
-int choose_nt(int64_t V, int esize) {
+// Threads per row.  The fused kernel gives a long row a whole block; the
+// split kernels (one pass each) run better with several rows per CU.
+int choose_nt(int64_t V, int esize, int mode) {
   const int64_t bytes = V * esize;
   if (bytes <= 4096) return 64;
+  if (mode != 0) return GRPO_NT_SPLIT;
   if (bytes <= 65536) return 256;
   return GRPO_NT_LARGE;
 }
@@ -529,7 +536,7 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   l.mode = (grad_out && !seqlv) ? 0 : 1;
   l.tin = logits_dtype;
   l.tg = grad_out ? grad_dtype : logits_dtype;
-  l.nt = choose_nt(V, fdtype_size(logits_dtype));
+  l.nt = choose_nt(V, fdtype_size(logits_dtype), l.mode);
   l.vec = rows_vectorizable(policy_logits, ref_logits, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);
   // rows above 4 KB that fit one block's registers keep the policy row
@@ -554,6 +561,7 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
       b.grad_scale = nullptr;  // the row and sequence passes folded it in
       RowLaunch lb = l;
       lb.mode = 2;
+      lb.nt = choose_nt(V, fdtype_size(logits_dtype), lb.mode);
       lb.resident = 0;
       if (launch_rows(b, lb, s) != hipSuccess) return GRPO_ERR_HIP;
     }
@@ -618,7 +626,7 @@ grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64
   l.mode = 2;
   l.tin = logits_dtype;
   l.tg = grad_dtype;
-  l.nt = choose_nt(V, fdtype_size(logits_dtype));
+  l.nt = choose_nt(V, fdtype_size(logits_dtype), l.mode);
   l.vec = rows_vectorizable(policy_logits, nullptr, row_stride, logits_dtype, grad_out,
                             grad_row_stride, grad_dtype);
   const bool timed = g_ev_start && g_ev_stop;

@@ -39,6 +39,10 @@
 #ifndef GRPO_Y_NONTEMPORAL
 #define GRPO_Y_NONTEMPORAL 1   // the reference row is read once: non-temporal loads
 #endif
+#ifndef GRPO_PASS1_PIPELINE
+#define GRPO_PASS1_PIPELINE 1  // pass 1 in two register stages: the next stage's loads are
+                               // in flight while the current one is summed
+#endif
 
 namespace grpo {
 
@@ -108,9 +112,66 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
     Lse sx = lse_init(), sy = lse_init();
     float xa = 0.0f, ya = 0.0f;
     bool own = false;
+    typedef typename IN::raw_t raw_t;
+    // one chunk of x (and y) into the running sums; the owner of the taken
+    // token's chunk lifts it out first
+    auto consume = [&](const raw_t* px, const raw_t* py, int u, int64_t cc) {
+      float fx[N], fy[N];
+      IN::cvt(px[u], fx);
+      if (has_ref) IN::cvt(py[u], fy);
+      if (cc == ca) {
+        own = true;
+        take_out(fx, ja, xa);
+        if (has_ref) take_out(fy, ja, ya);
+      }
+      lse_add(sx, fx);
+      if (has_ref) lse_add(sy, fy);
+    };
     int64_t c = lid;
+#if GRPO_PASS1_PIPELINE
+    // stages of P chunks each for x and y, in two register sets: while one
+    // stage is summed the next one's loads are in flight
+    constexpr int P = U / 2;
+    if (c + (P - 1) * NT < nvec) {
+      raw_t ax[P], ay[P], bx[P], by[P];
+      auto load_stage = [&](raw_t* dx, raw_t* dy, int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) dx[u] = IN::load(xrow, c0 + u * NT);
+        if (has_ref) {
+#pragma unroll
+          for (int u = 0; u < P; ++u)
+            dy[u] = GRPO_Y_NONTEMPORAL ? IN::load_nt(yrow, c0 + u * NT) : IN::load(yrow, c0 + u * NT);
+        }
+      };
+      auto sum_stage = [&](const raw_t* dx, const raw_t* dy, int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) consume(dx, dy, u, c0 + u * NT);
+      };
+      load_stage(ax, ay, c);
+      while (true) {
+        int64_t cn = c + P * NT;
+        if (cn + (P - 1) * NT >= nvec) {
+          sum_stage(ax, ay, c);
+          c = cn;
+          break;
+        }
+        load_stage(bx, by, cn);
+        sum_stage(ax, ay, c);
+        c = cn;
+        cn = c + P * NT;
+        if (cn + (P - 1) * NT >= nvec) {
+          sum_stage(bx, by, c);
+          c = cn;
+          break;
+        }
+        load_stage(ax, ay, cn);
+        sum_stage(bx, by, c);
+        c = cn;
+      }
+    }
+#else
     for (; c + (U - 1) * NT < nvec; c += U * NT) {
-      typename IN::raw_t rx[U], ry[U];
+      raw_t rx[U], ry[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) rx[u] = IN::load(xrow, c + u * NT);
       if (has_ref) {
@@ -119,19 +180,9 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
           ry[u] = GRPO_Y_NONTEMPORAL ? IN::load_nt(yrow, c + u * NT) : IN::load(yrow, c + u * NT);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float fx[N], fy[N];
-        IN::cvt(rx[u], fx);
-        if (has_ref) IN::cvt(ry[u], fy);
-        if (c + u * NT == ca) {
-          own = true;
-          take_out(fx, ja, xa);
-          if (has_ref) take_out(fy, ja, ya);
-        }
-        lse_add(sx, fx);
-        if (has_ref) lse_add(sy, fy);
-      }
+      for (int u = 0; u < U; ++u) consume(rx, ry, u, c + u * NT);
     }
+#endif
     for (; c < nvec; c += NT) {
       float fx[N], fy[N];
       IN::cvt(IN::load(xrow, c), fx);
