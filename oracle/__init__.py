@@ -5,6 +5,7 @@ import this package; the HIP library never does.
 """
 
 from .grpo_oracle import (  # noqa: F401
+    ADV_ESTIMATORS,
     KL_ESTIMATORS,
     PG_LOSSES,
     REDUCTIONS,
@@ -13,6 +14,10 @@ from .grpo_oracle import (  # noqa: F401
     LossConfig,
     OracleInputError,
     OracleResult,
+    clamp_advantages,
+    discounted_returns,
+    gdpo_advantages,
+    global_masked_normalize,
     group_advantages,
     group_offsets,
     gspo_terms,
@@ -24,11 +29,14 @@ from .grpo_oracle import (  # noqa: F401
     logits_rows,
     policy_terms,
     real_terms,
+    reinforce_pp_baseline_raw,
+    reinforce_pp_token_rewards,
     row_logsumexp,
     sequence_mask_keep,
     sequence_mean,
     sequence_terms,
     sequence_weights,
     softmax_grad_rows,
+    token_advantages,
     token_terms,
 )

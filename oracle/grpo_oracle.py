@@ -174,6 +174,38 @@ def group_advantages(rewards, offsets, leave_one_out=False, scale_by_std=True,
     return A
 
 
+def _advantages_of(rewards, B, groups):
+    """(A [B], CSR offsets) from rewards and a group specification, with the
+    optional clamp of [DOCKYARD] Advantage estimation (groups keys
+    adv_clip_low / adv_clip_high)."""
+    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    A = group_advantages(rewards, off, groups.get("leave_one_out", False),
+                         groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    if groups.get("adv_clip_low") is not None:
+        lo, hi = float(groups["adv_clip_low"]), float(groups["adv_clip_high"])
+        if not lo <= hi:
+            raise OracleInputError("advantage clamp needs low <= high")
+        A = np.clip(A, lo, hi)
+    return A, off
+
+
+def _advantage_source(rewards, groups, advantages, B, T, cfg):
+    """Advantages of every slot: from rewards and groups ([B], broadcast) or
+    given per token ([B, T]).  Returns (A [B] or None, offsets or None,
+    A per slot [B, T])."""
+    if advantages is None:
+        A, off = _advantages_of(rewards, B, groups)
+        return A, off, np.broadcast_to(A[:, None], (B, T))
+    if rewards is not None:
+        raise OracleInputError("give rewards or token advantages, not both")
+    if cfg.pg_loss in SEQUENCE_PG:
+        raise OracleInputError("sequence-level losses take per-sequence advantages")
+    At = np.asarray(advantages, dtype=np.float64)
+    if At.shape != (B, T):
+        raise OracleInputError("token advantages must be [B, T]")
+    return None, None, At
+
+
 # ---------------------------------------------------------------------------
 # Token counts and per-sequence weights  ([GRPO-LOSS] Normalizer semantics;
 # [RPP] PPO and KL reduction; [GRPO-CPP] The length-normalization detail)
@@ -600,19 +632,19 @@ def _reduce(P, K, w, beta):
 # ---------------------------------------------------------------------------
 
 def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: LossConfig,
-                    grad_scale=1.0, gen_logp=None):
+                    grad_scale=1.0, gen_logp=None, advantages=None):
     """GRPO loss from per-token log-probs.  ``grad`` is d loss / d logp [B, T].
 
     ``groups`` is a dict with keys samples_per_prompt | group_boundaries and
-    optional leave_one_out, scale_by_std, std_eps.
+    optional leave_one_out, scale_by_std, std_eps, adv_clip_low/high.
+    ``advantages``: precomputed token advantages [B, T] (then rewards and
+    groups are None), e.g. from token_advantages.
     """
     logp = np.asarray(logp)
     B, T = logp.shape
     _check_cfg(cfg, ref_logp is not None, gen_logp is not None)
     m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
-    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
-    A = group_advantages(rewards, off, groups.get("leave_one_out", False),
-                         groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    A, off, A_slot = _advantage_source(rewards, groups, advantages, B, T, cfg)
     L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha, cfg.norm_constant)
 
     ii, tt = np.nonzero(m)                      # boolean selection: masked slots never read
@@ -621,7 +653,9 @@ def grpo_token_loss(logp, old_logp, ref_logp, mask, rewards, *, groups, cfg: Los
     ref = None if ref_logp is None else np.asarray(ref_logp, dtype=np.float64)[ii, tt]
     gen = None if gen_logp is None else np.asarray(gen_logp, dtype=np.float64)[ii, tt]
     keep = _keep(B, ii, old, gen, cfg)
-    terms = token_terms(lp, old, ref, A[ii], cfg, gen, None if keep is None else keep[ii])
+    adv = A_slot[ii, tt]
+    terms = token_terms(lp, old, ref, adv, cfg, gen, None if keep is None else keep[ii])
+    terms["adv"] = adv
     _add_sequence_terms(terms, B, ii, lp, old, gen, A, L, w, off, cfg)
     return _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale,
                      grad=None, logp_active=lp, gen_active=gen, keep=keep)
@@ -673,7 +707,7 @@ def _assemble(B, T, ii, tt, terms, A, L, N, w, cfg, grad_scale, grad, logp_activ
         loss = policy_loss + cfg.beta * kl
     G = _token_G(terms, w, ii, cfg, grad_scale)
     tok = {}
-    for name in ("rho", "d", "kl", "loss", "dloss", "dkl"):
+    for name in ("rho", "d", "kl", "loss", "dloss", "dkl", "adv"):
         full = np.zeros((B, T))
         full[ii, tt] = terms[name]
         tok[name] = full
@@ -759,10 +793,11 @@ def softmax_grad_rows(x_rows, ids, lse, G):
 
 def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, rewards, *,
                       groups, cfg: LossConfig, grad_scale=1.0, want_grad=True,
-                      row_chunk=4096, gen_logps=None):
+                      row_chunk=4096, gen_logps=None, advantages=None):
     """GRPO loss and d loss / d policy_logits from [B, T, V] logits.
 
     Masked rows get an all-zero gradient row and are never read.
+    ``advantages``: precomputed token advantages [B, T], as for grpo_token_loss.
     """
     x = np.asarray(policy_logits)
     if x.ndim != 3:
@@ -770,11 +805,10 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     B, T, V = x.shape
     _check_cfg(cfg, ref_logits is not None, gen_logps is not None)
     m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
-    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
-    A = group_advantages(rewards, off, groups.get("leave_one_out", False),
-                         groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    A, off, A_slot = _advantage_source(rewards, groups, advantages, B, T, cfg)
     L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha, cfg.norm_constant)
     ii, tt = np.nonzero(m)
+    adv = A_slot[ii, tt]
     ids = np.asarray(action_ids)[ii, tt].astype(np.int64)
     old = np.asarray(old_logps, dtype=np.float64)[ii, tt]
     gen = None if gen_logps is None else np.asarray(gen_logps, dtype=np.float64)[ii, tt]
@@ -787,7 +821,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
         sl = slice(s, s + row_chunk)
         xr = x[ii[sl], tt[sl]]
         yr = None if ref_logits is None else np.asarray(ref_logits)[ii[sl], tt[sl]]
-        out = logits_rows(xr, yr, ids[sl], old[sl], A[ii[sl]], w[ii[sl]], cfg,
+        out = logits_rows(xr, yr, ids[sl], old[sl], adv[sl], w[ii[sl]], cfg,
                           grad_scale, want_grad and not seq_level,
                           None if gen is None else gen[sl],
                           None if keep is None else keep[ii[sl]])
@@ -805,14 +839,150 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
                 sl = slice(s, s + row_chunk)
                 grad[ii[sl], tt[sl]] = softmax_grad_rows(x[ii[sl], tt[sl]], ids[sl],
                                                          acc["lse"][sl], G[sl])
+    acc["adv"] = adv
     res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=grad,
                     logp_active=acc["logp"], gen_active=gen, keep=keep)
     return res
 
 
 def grpo_advantages(rewards, *, groups):
-    """Advantages alone, as the boundary's advantage entry point returns them."""
+    """Advantages alone, as the boundary's advantage entry point returns them
+    (with the group specification's clamp, if any)."""
     r = np.asarray(rewards)
-    off = group_offsets(r.shape[0], groups.get("samples_per_prompt"), groups.get("group_boundaries"))
-    return group_advantages(r, off, groups.get("leave_one_out", False),
-                            groups.get("scale_by_std", True), groups.get("std_eps", 1e-6))
+    return _advantages_of(r, r.shape[0], groups)[0]
+
+
+# ---------------------------------------------------------------------------
+# Token-level advantage estimators  ([RPP] REINFORCE++, REINFORCE++-baseline,
+# Global masked normalization; [DOCKYARD] Advantage estimation (clamp), GDPO)
+# ---------------------------------------------------------------------------
+
+ADV_ESTIMATORS = ("reinforce_pp", "reinforce_pp_baseline")
+
+
+def reinforce_pp_token_rewards(rewards, old_logp, ref_logp, mask, kl_coef):
+    """[RPP] REINFORCE++: r_{i,t} = m_{i,t} (-kl_coef * d_{i,t} + 1(t = T_i) R_i)
+    with the signed k1 estimator d = log pi_old - log pi_ref and T_i the last
+    valid position of response i.  Masked slots are never read."""
+    m = np.asarray(mask).astype(bool)
+    B, T = m.shape
+    R = np.asarray(rewards, dtype=np.float64)
+    old = np.asarray(old_logp, dtype=np.float64)
+    ref = np.asarray(ref_logp, dtype=np.float64)
+    r = np.zeros((B, T))
+    for i in range(B):
+        valid = np.nonzero(m[i])[0]
+        for t in valid:
+            r[i, t] = -kl_coef * (old[i, t] - ref[i, t])
+        if valid.size:
+            r[i, valid[-1]] = r[i, valid[-1]] + R[i]
+    return r
+
+
+def discounted_returns(r, mask, gamma):
+    """G_{i,t} = m_{i,t} sum_{u >= t} gamma^(u - t) r_{i,u}, accumulated
+    backwards over positions (r is 0 at masked slots)."""
+    m = np.asarray(mask).astype(bool)
+    B, T = m.shape
+    G = np.zeros((B, T))
+    for i in range(B):
+        acc = 0.0
+        for t in range(T - 1, -1, -1):
+            acc = float(r[i, t]) + gamma * acc
+            G[i, t] = acc if m[i, t] else 0.0
+    return G
+
+
+def reinforce_pp_baseline_raw(rewards, offsets, mask):
+    """[RPP] REINFORCE++-baseline: C_i = R_i - (mean of the group, the sample
+    itself included; no std division), broadcast to the valid tokens."""
+    m = np.asarray(mask).astype(bool)
+    R = [float(v) for v in np.asarray(rewards, dtype=np.float64).ravel()]
+    C = np.zeros(len(R))
+    for g in range(len(offsets) - 1):
+        s, e = int(offsets[g]), int(offsets[g + 1])
+        total = 0.0
+        for j in range(s, e):
+            total = total + R[j]
+        b = total / (e - s)
+        for j in range(s, e):
+            C[j] = R[j] - b
+    return np.where(m, C[:, None], 0.0)
+
+
+def global_masked_normalize(A, mask, var_floor=1e-8):
+    """[RPP] Global masked normalization: over every valid token,
+    mu = mean, var = population variance (ddof 0), and
+    A_hat = m (A - mu) / sqrt(max(var, var_floor)).  An empty mask gives zeros."""
+    m = np.asarray(mask).astype(bool)
+    vals = np.asarray(A, dtype=np.float64)[m]
+    N = vals.size
+    if N == 0:
+        return np.zeros(m.shape)
+    mu = math.fsum(vals) / N
+    var = math.fsum((v - mu) * (v - mu) for v in vals) / N
+    return np.where(m, (np.asarray(A, dtype=np.float64) - mu) / math.sqrt(max(var, var_floor)), 0.0)
+
+
+def clamp_advantages(A, low, high):
+    """[DOCKYARD] Advantage estimation: clamp to [advantage_clip_low,
+    advantage_clip_high]."""
+    return np.clip(np.asarray(A, dtype=np.float64), low, high)
+
+
+def token_advantages(estimator, rewards, old_logp, ref_logp, mask, *, groups=None, kl_coef=0.0,
+                     gamma=1.0, normalize=True):
+    """[B, T] advantages of a token-level estimator, float64.
+
+    reinforce_pp: returns of the k1-shaped token rewards (KL-to-go plus the
+    terminal reward); reinforce_pp_baseline: the inclusive group-mean
+    difference broadcast to the valid tokens.  Then, optionally, the global
+    masked normalization, and the group specification's clamp if it has one
+    (``groups`` keys adv_clip_low / adv_clip_high)."""
+    m = np.asarray(mask).astype(bool)
+    B, T = m.shape
+    if estimator not in ADV_ESTIMATORS:
+        raise OracleInputError(f"unknown estimator {estimator!r}")
+    if not (0.0 < gamma <= 1.0):
+        raise OracleInputError("gamma must lie in (0, 1]")
+    if estimator == "reinforce_pp":
+        if ref_logp is None and kl_coef != 0.0:
+            raise OracleInputError("KL shaping needs the reference log-probs")
+        ref = old_logp if ref_logp is None else ref_logp
+        r = reinforce_pp_token_rewards(rewards, old_logp, ref, m, kl_coef)
+        A = discounted_returns(r, m, gamma)
+    else:
+        if groups is None:
+            raise OracleInputError("the baseline estimator needs reward groups")
+        off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+        A = reinforce_pp_baseline_raw(rewards, off, m)
+    if normalize:
+        A = global_masked_normalize(A, m)
+    if groups is not None and groups.get("adv_clip_low") is not None:
+        A = np.where(m, clamp_advantages(A, groups["adv_clip_low"], groups["adv_clip_high"]), 0.0)
+    return A
+
+
+def gdpo_advantages(component_rewards, *, groups, std_eps=1e-6):
+    """[DOCKYARD] GDPO: for each reward component a per-group baseline (the
+    group's leave_one_out flag; the page's GDPO uses leave-one-out),
+    optionally divided by the component's group std (scale_by_std), summed
+    over components, then renormalized over the batch to zero mean and unit
+    population std (floored at std_eps); finally the optional clamp."""
+    Rc = np.asarray(component_rewards, dtype=np.float64)
+    if Rc.ndim != 2 or Rc.shape[0] < 2:
+        raise OracleInputError("GDPO needs at least two reward components [C, B]")
+    C, B = Rc.shape
+    off = group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    total = np.zeros(B)
+    for c in range(C):
+        total = total + group_advantages(Rc[c], off, groups.get("leave_one_out", True),
+                                         groups.get("scale_by_std", True),
+                                         groups.get("std_eps", std_eps))
+    vals = [float(v) for v in total]
+    mu = math.fsum(vals) / B
+    sd = math.sqrt(math.fsum((v - mu) * (v - mu) for v in vals) / B)
+    A = (total - mu) / max(sd, groups.get("std_eps", std_eps))
+    if groups.get("adv_clip_low") is not None:
+        A = clamp_advantages(A, groups["adv_clip_low"], groups["adv_clip_high"])
+    return A

@@ -110,7 +110,8 @@ def _terms_at(ref, cfg, dlogp=0.0, dd=0.0):
         lp = t["logp"] + dlogp
         lref = t["logp"] + t["d"] + dlogp + dd
         keep = None if ref.seq_keep is None else np.broadcast_to(ref.seq_keep[:, None], lp.shape)
-        out = oracle.token_terms(lp, old, lref, ref.advantages[:, None], cfg, t.get("gen"), keep)
+        adv = t["adv"] if "adv" in t else ref.advantages[:, None]
+        out = oracle.token_terms(lp, old, lref, adv, cfg, t.get("gen"), keep)
     for k, v in out.items():
         out[k] = np.where(act, v, np.zeros_like(v))
     return out
