@@ -26,6 +26,11 @@
  *                ratio).
  *   [REAL]       ms-swift blog on the REAL loss: REAL formalisation and the
  *                source walkthrough (in-group classification of sequences).
+ *   [RPP-A]      Relax docs, "REINFORCE++ and REINFORCE++-baseline":
+ *                REINFORCE++, REINFORCE++-baseline, Global masked
+ *                normalization (token-level advantages).
+ *   [GDPO]       dockyard_rl, "GRPO and the clipped policy-gradient loss":
+ *                GDPO multi-reward advantage.
  *
  * Objective (per active token (i, t) of sequence i, action a = action_ids[i,t]),
  * in the default settings (GRPO_PG_CLIP, GRPO_KL_K3, no clamps):
@@ -77,7 +82,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 4
+#define GRPO_ABI_VERSION 5
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -219,7 +224,9 @@ typedef enum grpo_tis {
  *   baseline b_i = mean, or (S - r_i) / (n - 1) with leave_one_out
  *   A_i = (r_i - b_i) / max(std, std_eps) if scale_by_std, else r_i - b_i
  * rounded once to float.  With leave_one_out the difference is divided by
- * the whole group's population std. */
+ * the whole group's population std.  With clip_advantages the binary64 value
+ * is clamped to [adv_clip_low, adv_clip_high] before the rounding ([DOCKYARD]
+ * Advantage estimation). */
 typedef struct grpo_groups {
   int32_t samples_per_prompt;       /* > 1, or 0 when group_boundaries is given */
   int32_t num_groups;               /* CSR: number of groups; ignored for uniform groups */
@@ -227,7 +234,22 @@ typedef struct grpo_groups {
   int32_t leave_one_out;            /* 0 or 1 */
   int32_t scale_by_std;             /* 0 or 1 (the usual GRPO setting is 1) */
   double std_eps;                   /* floor of the std, > 0 (usually 1e-6) */
+  int32_t clip_advantages;          /* 0 or 1 */
+  double adv_clip_low;              /* finite, <= adv_clip_high; read when clip_advantages */
+  double adv_clip_high;             /* finite; read when clip_advantages */
 } grpo_groups;
+
+/* Token-level advantage estimators ([RPP-A] below), for grpo_token_advantages().
+ *   GRPO_ADV_REINFORCE_PP           r_t = m_t (-kl_coef * (old_logp_t - ref_logp_t)
+ *                                   + [t = T_i] R_i), T_i the last active slot of
+ *                                   sequence i; A_t = m_t sum_{u >= t} gamma^(u-t) r_u
+ *                                   (the discount counts slot positions)
+ *   GRPO_ADV_REINFORCE_PP_BASELINE  A_t = m_t (R_i - mean of R over i's group, i
+ *                                   included; no std division) */
+typedef enum grpo_adv_estimator {
+  GRPO_ADV_REINFORCE_PP = 0,
+  GRPO_ADV_REINFORCE_PP_BASELINE = 1
+} grpo_adv_estimator;
 
 /* Objective settings.  A symmetric clip sets eps_low == eps_high.  Zero in
  * pg_loss .. tis_ratio_max selects the clipped surrogate with the k3
@@ -292,18 +314,60 @@ GRPO_API grpo_status grpo_workspace_init(void *ws, size_t ws_bytes, void *stream
 GRPO_API grpo_status grpo_advantages(const float *rewards, int64_t B, const grpo_groups *groups,
                             float *adv_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Token-level advantages [B, T] ([RPP-A]), computed in binary64 and rounded
+ * once to float32 (0 at masked slots).
+ *   estimator: grpo_adv_estimator.  rewards: [B] float32 (R_i).
+ *   old_logp, ref_logp: [B, T] float32 (GRPO_ADV_REINFORCE_PP only; ref_logp
+ *     may be NULL when kl_coef == 0, old_logp may then be NULL too).
+ *   mask: [B, T] bytes or NULL (all active).
+ *   groups: the reward groups, required by GRPO_ADV_REINFORCE_PP_BASELINE
+ *     (whose leave_one_out / scale_by_std must be 0: the baseline is the
+ *     inclusive mean without std division); optional for GRPO_ADV_REINFORCE_PP.
+ *     Its clamp, if set, is applied last.
+ *   kl_coef >= 0 and finite; gamma in (0, 1].
+ *   normalize: 1 applies the global masked normalization over every active
+ *     slot of the batch: A <- (A - mu) / sqrt(max(var, 1e-8)), population
+ *     moments (an empty mask gives zeros and GRPO_FAULT_NO_TOKENS).
+ *   adv_out: [B, T] float32.  status: device uint32 for GRPO_FAULT_* bits, or NULL.
+ * Errors as for the loss entry points (GRPO_ERR_CONFIG for a bad estimator,
+ * kl_coef or gamma, or a missing input it needs). */
+GRPO_API grpo_status grpo_token_advantages(int32_t estimator, const float *rewards,
+                                           const float *old_logp, const float *ref_logp,
+                                           const uint8_t *mask, int64_t B, int64_t T,
+                                           const grpo_groups *groups, double kl_coef,
+                                           double gamma, int32_t normalize, float *adv_out,
+                                           uint32_t *status, void *ws, size_t ws_bytes,
+                                           void *stream);
+
+/* Multi-reward advantages [B] ([GDPO]).  rewards: [num_components, B]
+ * float32 (component c of sample i at c * B + i), num_components >= 2.  For
+ * each component the group baseline and std scaling follow `groups` exactly
+ * as grpo_advantages does (GDPO uses leave_one_out = 1); the per-component
+ * advantages are summed in binary64, the sum is renormalised over the batch
+ * to zero mean and unit population std (floored at groups->std_eps), then
+ * clamped if the groups ask for it, and rounded once to float32.
+ * adv_out: [B] float32. */
+GRPO_API grpo_status grpo_gdpo_advantages(const float *rewards, int32_t num_components, int64_t B,
+                                          const grpo_groups *groups, float *adv_out, void *ws,
+                                          size_t ws_bytes, void *stream);
+
 /* Logprob-level token loss ([GRPO-CPP] CUDA: token loss from per-token
  * log-probs, returning dlogp).  logp, old_logp, ref_logp: [B, T] float32,
  * contiguous; ref_logp may be NULL only when beta == 0 (then d = 0).
  * gen_logp: [B, T] float32 log-probs of the generating policy, or NULL (no
  * off-policy correction; see grpo_tis).
  * mask: [B, T] bytes or NULL (all active).  rewards: [B] float32.
+ * token_advantages: [B, T] float32 precomputed advantages (e.g. from
+ *   grpo_token_advantages), or NULL.  When given, rewards and groups must be
+ *   NULL, out->advantages is not written, and the sequence-level policy
+ *   losses are rejected (they take one advantage per sequence).
  * dlogp_out: [B, T] float32, d loss / d logp (0 at masked slots), or NULL
  * for the forward only.  grad_scale: device float scalar multiplying every
  * gradient, or NULL for 1.  The per-token outputs tok_logp are not written
  * by this entry point. */
 GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, const float *ref_logp,
-                            const float *gen_logp, const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
+                            const float *gen_logp, const uint8_t *mask, const float *rewards,
+                            const float *token_advantages, int64_t B, int64_t T,
                             const grpo_groups *groups, const grpo_cfg *cfg, float *dlogp_out,
                             const float *grad_scale, const grpo_outputs *out, void *ws,
                             size_t ws_bytes, void *stream);
@@ -318,6 +382,7 @@ GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, c
  *   old_logps: [B, T] float32.  gen_logps: [B, T] float32 or NULL (the
  *     generating policy's log-probs for the off-policy correction; see
  *     grpo_tis).  mask: [B, T] bytes or NULL.  rewards: [B].
+ *   token_advantages: [B, T] float32 or NULL, as for grpo_token_loss.
  *   grad_out: [B, T, V] in grad_dtype with row stride grad_row_stride >= V;
  *     masked rows are written with zeros.  grad_out may be policy_logits
  *     itself (in place; then grad_dtype, grad_row_stride must equal
@@ -330,7 +395,8 @@ GRPO_API grpo_status grpo_token_loss(const float *logp, const float *old_logp, c
 GRPO_API grpo_status grpo_loss_fwd_bwd(const void *policy_logits, const void *ref_logits,
                               int32_t logits_dtype, int64_t row_stride, const void *action_ids,
                               int32_t ids_dtype, const float *old_logps, const float *gen_logps,
-                              const uint8_t *mask, const float *rewards, int64_t B, int64_t T,
+                              const uint8_t *mask, const float *rewards,
+                              const float *token_advantages, int64_t B, int64_t T,
                               int64_t V, const grpo_groups *groups, const grpo_cfg *cfg, void *grad_out,
                               int32_t grad_dtype, int64_t grad_row_stride,
                               const float *grad_scale, const grpo_outputs *out, void *ws,

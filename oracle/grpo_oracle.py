@@ -867,13 +867,15 @@ def reinforce_pp_token_rewards(rewards, old_logp, ref_logp, mask, kl_coef):
     m = np.asarray(mask).astype(bool)
     B, T = m.shape
     R = np.asarray(rewards, dtype=np.float64)
-    old = np.asarray(old_logp, dtype=np.float64)
-    ref = np.asarray(ref_logp, dtype=np.float64)
+    shaped = kl_coef != 0.0            # without the KL term the log-probs are not needed
+    old = np.asarray(old_logp, dtype=np.float64) if shaped else None
+    ref = np.asarray(ref_logp, dtype=np.float64) if shaped else None
     r = np.zeros((B, T))
     for i in range(B):
         valid = np.nonzero(m[i])[0]
-        for t in valid:
-            r[i, t] = -kl_coef * (old[i, t] - ref[i, t])
+        if shaped:
+            for t in valid:
+                r[i, t] = -kl_coef * (old[i, t] - ref[i, t])
         if valid.size:
             r[i, valid[-1]] = r[i, valid[-1]] + R[i]
     return r
@@ -946,10 +948,9 @@ def token_advantages(estimator, rewards, old_logp, ref_logp, mask, *, groups=Non
     if not (0.0 < gamma <= 1.0):
         raise OracleInputError("gamma must lie in (0, 1]")
     if estimator == "reinforce_pp":
-        if ref_logp is None and kl_coef != 0.0:
-            raise OracleInputError("KL shaping needs the reference log-probs")
-        ref = old_logp if ref_logp is None else ref_logp
-        r = reinforce_pp_token_rewards(rewards, old_logp, ref, m, kl_coef)
+        if (ref_logp is None or old_logp is None) and kl_coef != 0.0:
+            raise OracleInputError("KL shaping needs the old and reference log-probs")
+        r = reinforce_pp_token_rewards(rewards, old_logp, ref_logp, m, kl_coef)
         A = discounted_returns(r, m, gamma)
     else:
         if groups is None:

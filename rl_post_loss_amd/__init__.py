@@ -15,9 +15,11 @@ from ._abi import (  # noqa: F401
 from .loss import (  # noqa: F401
     GRPOResult,
     grpo_advantages,
+    grpo_gdpo_advantages,
     grpo_loss,
     grpo_loss_bwd,
     grpo_loss_fwd_bwd,
+    grpo_token_advantages,
     grpo_token_loss,
     set_timing_events,
     workspace,

@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 4
+GRPO_ABI_VERSION = 5
 
 GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
@@ -19,6 +19,7 @@ PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 
                  "real": 6}
 KL_ESTIMATOR_CODES = {"k3": 0, "k1": 1, "k2": 2}
 TIS_CODES = {None: 0, "tis": 1, "icepop": 2, "seq_mask": 3}
+ADV_ESTIMATOR_CODES = {"reinforce_pp": 0, "reinforce_pp_baseline": 1}
 
 GRPO_FAULT_BAD_ACTION = 1
 GRPO_FAULT_NO_TOKENS = 2
@@ -36,7 +37,8 @@ i32, i64, sz, f64 = C.c_int32, C.c_int64, C.c_size_t, C.c_double
 class GrpoGroups(C.Structure):
     _fields_ = [("samples_per_prompt", i32), ("num_groups", i32),
                 ("group_boundaries", C.POINTER(C.c_int64)), ("leave_one_out", i32),
-                ("scale_by_std", i32), ("std_eps", f64)]
+                ("scale_by_std", i32), ("std_eps", f64), ("clip_advantages", i32),
+                ("adv_clip_low", f64), ("adv_clip_high", f64)]
 
 
 class GrpoCfg(C.Structure):
@@ -59,10 +61,13 @@ SIGNATURES = {
     "grpo_workspace_bytes": (sz, [i64, i64, i32]),
     "grpo_workspace_init": (C.c_int, [vp, sz, vp]),
     "grpo_advantages": (C.c_int, [vp, i64, C.POINTER(GrpoGroups), vp, vp, sz, vp]),
-    "grpo_token_loss": (C.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
+    "grpo_token_advantages": (C.c_int, [i32, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
+                                        f64, f64, i32, vp, vp, vp, sz, vp]),
+    "grpo_gdpo_advantages": (C.c_int, [vp, i32, i64, C.POINTER(GrpoGroups), vp, vp, sz, vp]),
+    "grpo_token_loss": (C.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, i64, C.POINTER(GrpoGroups),
                                   C.POINTER(GrpoCfg), vp, vp, C.POINTER(GrpoOutputs), vp, sz,
                                   vp]),
-    "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, vp, i64, i64, i64,
+    "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64,
                                     C.POINTER(GrpoGroups), C.POINTER(GrpoCfg), vp, i32, i64, vp,
                                     C.POINTER(GrpoOutputs), vp, sz, vp]),
     "grpo_loss_bwd": (C.c_int, [vp, i32, i64, vp, i32, vp, i64, i64, i64, vp, i32, i64, vp, vp,

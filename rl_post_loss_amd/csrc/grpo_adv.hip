@@ -1,0 +1,289 @@
+// Token-level and multi-reward advantage estimators.
+//
+// REINFORCE++ and REINFORCE++-baseline follow the Relax docs page
+// "REINFORCE++ and REINFORCE++-baseline" (sections REINFORCE++,
+// REINFORCE++-baseline, Global masked normalization):
+//   REINFORCE++  token reward r_t = m_t (-kl_coef (old_t - ref_t) + [t = T_i] R_i),
+//                return A_t = m_t sum_{u >= t} gamma^(u - t) r_u;
+//   baseline     A_t = m_t (R_i - mean of R over i's group, i included);
+// then optionally A <- (A - mu) / sqrt(max(var, 1e-8)) with the population
+// moments of every active slot of the batch.  GDPO follows the dockyard_rl
+// design doc (GDPO multi-reward advantage): a per-component group baseline,
+// summed over components, renormalised over the batch.
+//
+// Everything is binary64 with contraction off and rounded once to float32.
+// The returns run as a chunked backward scan: thread j of the sequence's
+// block owns slots [j K, (j + 1) K); each chunk's partial return and
+// gamma^length are combined right to left by one thread, then every chunk
+// replays its slots from the carry it receives.  Sums over slots are fixed
+// trees, sums over sequences a single block, so results repeat bit for bit.
+
+#include "../../include/grpo.h"
+#include "grpo_device.hpp"
+#include "grpo_internal.hpp"
+
+namespace grpo {
+
+constexpr int kAdvThreads = 256;
+constexpr int kMomentThreads = 1024;
+constexpr int kGdpoThreads = 1024;
+
+struct AdvShared {
+  double h[kAdvThreads];      // chunk's return at its first slot, from its own slots
+  double g[kAdvThreads];      // gamma^(chunk length)
+  double carry[kAdvThreads];  // return at the slot after the chunk
+  double red[kAdvThreads / kWave];
+  long long red_i[kAdvThreads / kWave];
+  double cval;                // baseline difference of the sequence
+  long long last;             // last active slot (-1: none)
+};
+
+__device__ __forceinline__ bool adv_active(const TokAdvArgs& a, int64_t r) {
+  return a.mask == nullptr || a.mask[r] != 0;
+}
+
+__device__ __forceinline__ double clamp_adv(const TokAdvArgs& a, double v) {
+  if (!a.clip) return v;
+  return v < a.clip_lo ? a.clip_lo : (v > a.clip_hi ? a.clip_hi : v);  // keeps a NaN
+}
+
+// Token reward of REINFORCE++ at slot t (0 at masked slots).
+__device__ __forceinline__ double rpp_reward(const TokAdvArgs& a, int64_t base, int64_t t,
+                                             long long last, double R) {
+#pragma clang fp contract(off)
+  const int64_t r = base + t;
+  if (!adv_active(a, r)) return 0.0;
+  double v = 0.0;
+  if (a.kl_coef != 0.0) v = -a.kl_coef * (double(a.old[r]) - double(a.ref[r]));
+  if (t == last) v = v + R;
+  return v;
+}
+
+// Calls f(t, active, A_t) for every slot of this thread's chunk of sequence
+// i, in backward order (A_t is the raw advantage, 0 at masked slots).  All
+// threads of the block must call it.
+template <typename F>
+__device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& f) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x;
+  const int64_t T = a.T, base = i * a.T;
+  const int64_t K = (T + kAdvThreads - 1) / kAdvThreads;
+  const int64_t t0 = tid * K < T ? tid * K : T;
+  const int64_t t1 = t0 + K < T ? t0 + K : T;
+  if (a.estimator == GRPO_ADV_REINFORCE_PP_BASELINE) {
+    const double c = sh.cval;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      const bool act = adv_active(a, base + t);
+      f(t, act, act ? c : 0.0);
+    }
+    return;
+  }
+  const double R = double(a.rewards[i]);
+  const long long last = sh.last;
+  double acc = 0.0, gl = 1.0;
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    acc = rpp_reward(a, base, t, last, R) + a.gamma * acc;
+    gl = gl * a.gamma;
+  }
+  __syncthreads();  // sh.h / sh.g may still be read by a previous call
+  sh.h[tid] = acc;
+  sh.g[tid] = gl;
+  __syncthreads();
+  if (tid == 0) {
+    double c = 0.0;
+    for (int j = kAdvThreads - 1; j >= 0; --j) {
+      sh.carry[j] = c;
+      c = sh.h[j] + sh.g[j] * c;
+    }
+  }
+  __syncthreads();
+  acc = sh.carry[tid];
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    acc = rpp_reward(a, base, t, last, R) + a.gamma * acc;
+    const bool act = adv_active(a, base + t);
+    f(t, act, act ? acc : 0.0);
+  }
+}
+
+// One block per sequence; a.pass selects the work (see TokAdvArgs).
+__global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) {
+#pragma clang fp contract(off)
+  __shared__ AdvShared sh;
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = i * a.T;
+  if (i == 0 && tid == 0 && a.pass == 0) a.hdr->status = 0;
+
+  if (a.estimator == GRPO_ADV_REINFORCE_PP) {
+    // last active slot of the sequence
+    const int64_t K = (a.T + kAdvThreads - 1) / kAdvThreads;
+    const int64_t t0 = tid * K < a.T ? tid * K : a.T;
+    const int64_t t1 = t0 + K < a.T ? t0 + K : a.T;
+    long long mx = -1;
+    for (int64_t t = t0; t < t1; ++t)
+      if (adv_active(a, base + t)) mx = t;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const long long o = __shfl_xor(mx, off);
+      mx = o > mx ? o : mx;
+    }
+    if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      long long m = -1;
+      for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
+      sh.last = m;
+    }
+  } else if (tid == 0) {
+    // group mean (the sample itself included), summed in index order
+    int64_t s, e;
+    if (a.spp > 0) {
+      s = (i / a.spp) * a.spp;
+      e = s + a.spp;
+    } else {
+      int lo = 0, hi = a.num_groups;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (a.offsets[mid] <= i) lo = mid; else hi = mid;
+      }
+      s = a.offsets[lo];
+      e = a.offsets[lo + 1];
+    }
+    double total = 0.0;
+    for (int64_t j = s; j < e; ++j) total = total + double(a.rewards[j]);
+    sh.cval = double(a.rewards[i]) - total / double(e - s);
+  }
+  __syncthreads();
+
+  if (a.pass == 0 && !a.normalize) {
+    for_each_raw(a, i, sh, [&](int64_t t, bool, double v) { a.out[base + t] = float(clamp_adv(a, v)); });
+    if (i == 0 && tid == 0 && a.status) *a.status = 0u;
+    return;
+  }
+  if (a.pass == 2) {
+    const double mu = a.hdr->mu, sd = a.hdr->sd;
+    for_each_raw(a, i, sh, [&](int64_t t, bool act, double v) {
+      a.out[base + t] = act ? float(clamp_adv(a, (v - mu) / sd)) : 0.0f;
+    });
+    if (i == 0 && tid == 0 && a.status) *a.status = a.hdr->status;
+    return;
+  }
+  // pass 0: sum and count; pass 1: squared deviations from the mean
+  const double mu = a.pass == 1 ? a.hdr->mu : 0.0;
+  double sum = 0.0;
+  long long cnt = 0;
+  for_each_raw(a, i, sh, [&](int64_t, bool act, double v) {
+    if (!act) return;
+    if (a.pass == 0) {
+      sum = sum + v;
+      ++cnt;
+    } else {
+      const double dv = v - mu;
+      sum = sum + dv * dv;
+    }
+  });
+  sum = block_sum_f64<kAdvThreads>(sum, sh.red);
+  cnt = block_sum_i64<kAdvThreads>(cnt, sh.red_i);
+  if (tid == 0) {
+    a.S[i] = sum;
+    if (a.pass == 0) a.L[i] = int32_t(cnt);
+  }
+}
+
+// One block: pass 0 -> N and the mean; pass 1 -> the floored std.
+__global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(TokAdvArgs a) {
+#pragma clang fp contract(off)
+  __shared__ double sh_f64[kMomentThreads / kWave];
+  __shared__ long long sh_i64[kMomentThreads / kWave];
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  long long n = 0;
+  for (int64_t k = tid; k < a.B; k += kMomentThreads) {
+    s = s + a.S[k];
+    n += a.L[k];
+  }
+  s = block_sum_f64<kMomentThreads>(s, sh_f64);
+  n = block_sum_i64<kMomentThreads>(n, sh_i64);
+  if (tid != 0) return;
+  if (a.pass == 0) {
+    a.hdr->num_tokens = n;
+    a.hdr->mu = n > 0 ? s / double(n) : 0.0;
+    if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
+  } else {
+    const double var = n > 0 ? s / double(n) : 0.0;
+    a.hdr->sd = sqrt(var > 1e-8 ? var : 1e-8);
+  }
+}
+
+hipError_t launch_token_advantages(const TokAdvArgs& base, hipStream_t s) {
+  TokAdvArgs a = base;
+  const dim3 grid(unsigned(a.B));
+  a.pass = 0;
+  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
+  if (!a.normalize) return hipGetLastError();
+  hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
+  a.pass = 1;
+  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
+  hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
+  a.pass = 2;
+  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// GDPO: thread g forms group g's per-component advantages (sums in member
+// order, as the group-relative advantages do) and adds them up in component
+// order; then the block renormalises the totals over the batch.
+__global__ __launch_bounds__(kGdpoThreads) void grpo_gdpo_kernel(GdpoArgs a) {
+#pragma clang fp contract(off)
+  __shared__ double sh_f64[kGdpoThreads / kWave];
+  const int tid = threadIdx.x;
+  const int64_t G = a.spp > 0 ? a.B / a.spp : int64_t(a.num_groups);
+  for (int64_t g = tid; g < G; g += kGdpoThreads) {
+    const int64_t s0 = a.spp > 0 ? g * a.spp : a.offsets[g];
+    const int64_t e0 = a.spp > 0 ? s0 + a.spp : a.offsets[g + 1];
+    const int64_t n = e0 - s0;
+    for (int64_t j = s0; j < e0; ++j) a.total[j] = 0.0;
+    for (int c = 0; c < a.C; ++c) {
+      const float* r = a.rewards + int64_t(c) * a.B;
+      double S = 0.0;
+      for (int64_t j = s0; j < e0; ++j) S = S + double(r[j]);
+      const double mean = S / double(n);
+      double sq = 0.0;
+      for (int64_t j = s0; j < e0; ++j) {
+        const double dev = double(r[j]) - mean;
+        sq = sq + dev * dev;
+      }
+      const double sd = sqrt(sq / double(n));
+      const double denom = sd >= a.std_eps ? sd : a.std_eps;
+      for (int64_t j = s0; j < e0; ++j) {
+        const double rj = double(r[j]);
+        const double b = a.leave_one_out ? (S - rj) / double(n - 1) : mean;
+        const double diff = rj - b;
+        a.total[j] = a.total[j] + (a.scale_by_std ? diff / denom : diff);
+      }
+    }
+  }
+  __syncthreads();
+  double s = 0.0;
+  for (int64_t j = tid; j < a.B; j += kGdpoThreads) s = s + a.total[j];
+  const double mu = block_sum_f64<kGdpoThreads>(s, sh_f64) / double(a.B);
+  double q = 0.0;
+  for (int64_t j = tid; j < a.B; j += kGdpoThreads) {
+    const double dv = a.total[j] - mu;
+    q = q + dv * dv;
+  }
+  const double sd = sqrt(block_sum_f64<kGdpoThreads>(q, sh_f64) / double(a.B));
+  const double denom = sd >= a.std_eps ? sd : a.std_eps;
+  for (int64_t j = tid; j < a.B; j += kGdpoThreads) {
+    double v = (a.total[j] - mu) / denom;
+    if (a.clip) v = v < a.clip_lo ? a.clip_lo : (v > a.clip_hi ? a.clip_hi : v);
+    a.out[j] = float(v);
+  }
+}
+
+hipError_t launch_gdpo(const GdpoArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(grpo_gdpo_kernel, dim3(1), dim3(kGdpoThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace grpo

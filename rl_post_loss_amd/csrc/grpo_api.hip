@@ -19,6 +19,8 @@ hipError_t launch_final(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
 hipError_t launch_seq(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_real(const RealArgs& a, hipStream_t stream);
+hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s);
+hipError_t launch_gdpo(const GdpoArgs& a, hipStream_t s);
 bool resident_fits(int64_t V, int esize);
 }  // namespace grpo
 
@@ -50,6 +52,10 @@ grpo_status check_groups(const grpo_groups* g, int64_t B) {
   if (g->leave_one_out != 0 && g->leave_one_out != 1) return GRPO_ERR_GROUPS;
   if (g->scale_by_std != 0 && g->scale_by_std != 1) return GRPO_ERR_GROUPS;
   if (!(g->std_eps > 0.0) || !isfinite(g->std_eps)) return GRPO_ERR_GROUPS;
+  if (g->clip_advantages != 0 && g->clip_advantages != 1) return GRPO_ERR_GROUPS;
+  if (g->clip_advantages &&
+      !(isfinite(g->adv_clip_low) && isfinite(g->adv_clip_high) && g->adv_clip_low <= g->adv_clip_high))
+    return GRPO_ERR_GROUPS;
   if (uniform) {
     if (g->samples_per_prompt < 2 || B % g->samples_per_prompt != 0) return GRPO_ERR_GROUPS;
     return GRPO_OK;
@@ -100,6 +106,20 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref, bool has_gen) {
         c->tis_ratio_min >= 0.0 && c->tis_ratio_min <= c->tis_ratio_max))
     return GRPO_ERR_CONFIG;
   return GRPO_OK;
+}
+
+// The advantages come from exactly one source: rewards with their groups,
+// or the caller's token advantages (then neither rewards nor groups).
+grpo_status check_advantage_source(const float* rewards, const float* token_advantages,
+                                   const grpo_groups* groups, int64_t B) {
+  if (token_advantages) return (rewards || groups) ? GRPO_ERR_CONFIG : GRPO_OK;
+  if (!rewards) return GRPO_ERR_NULL;
+  return check_groups(groups, B);
+}
+
+// CSR group count of a (possibly absent) group description, 0 for uniform.
+int32_t group_count_csr(const grpo_groups* g) {
+  return (!g || g->samples_per_prompt > 0) ? 0 : g->num_groups;
 }
 
 bool is_sequence_level(const grpo_cfg* c) {
@@ -175,11 +195,11 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
   a.iwseq = w.at<double>(w.l.iwseq);
   a.useq = want_weights ? w.at<float>(w.l.useq) : nullptr;
   a.mask = mask;
-  a.rewards = rewards;
+  a.rewards = g ? rewards : nullptr;  // no groups: the caller gives token advantages
   a.B = B;
   a.T = T;
-  a.spp = g->samples_per_prompt;
-  a.num_groups = g->samples_per_prompt > 0 ? 0 : g->num_groups;
+  a.spp = g ? g->samples_per_prompt : 0;
+  a.num_groups = (!g || g->samples_per_prompt > 0) ? 0 : g->num_groups;
   a.offsets = nullptr;
   if (a.num_groups > 0) {
     int64_t* dev = w.at<int64_t>(w.l.offsets);
@@ -188,9 +208,14 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
       return GRPO_ERR_HIP;
     a.offsets = dev;
   }
-  a.leave_one_out = g->leave_one_out;
-  a.scale_by_std = g->scale_by_std;
-  a.std_eps = g->std_eps;
+  if (g) {
+    a.leave_one_out = g->leave_one_out;
+    a.scale_by_std = g->scale_by_std;
+    a.std_eps = g->std_eps;
+    a.clip = g->clip_advantages;
+    a.clip_lo = g->adv_clip_low;
+    a.clip_hi = g->adv_clip_high;
+  }
   a.reduction = cfg ? cfg->reduction : GRPO_TOKEN_MEAN;
   a.alpha = cfg ? cfg->alpha : 0.0;
   a.norm_constant = cfg ? cfg->norm_constant : 0.0;
@@ -374,18 +399,20 @@ grpo_status grpo_advantages(const float* rewards, int64_t B, const grpo_groups* 
 }
 
 grpo_status grpo_token_loss(const float* logp, const float* old_logp, const float* ref_logp,
-                            const float* gen_logp, const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
+                            const float* gen_logp, const uint8_t* mask, const float* rewards,
+                            const float* token_advantages, int64_t B, int64_t T,
                             const grpo_groups* groups, const grpo_cfg* cfg, float* dlogp_out,
                             const float* grad_scale, const grpo_outputs* out, void* ws,
                             size_t ws_bytes, void* stream) {
-  if (!logp || !old_logp || !rewards || !out || !out->scalars) return GRPO_ERR_NULL;
+  if (!logp || !old_logp || !out || !out->scalars) return GRPO_ERR_NULL;
   int64_t rows;
   if (!mul_ok(B, T, kMaxElems, &rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
-  grpo_status st = check_groups(groups, B);
+  grpo_status st = check_advantage_source(rewards, token_advantages, groups, B);
   if (st != GRPO_OK) return st;
   st = check_cfg(cfg, ref_logp != nullptr, gen_logp != nullptr);
   if (st != GRPO_OK) return st;
-  const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
+  if (token_advantages && is_sequence_level(cfg)) return GRPO_ERR_CONFIG;
+  const int32_t ng = group_count_csr(groups);
   Ws w;
   st = check_ws(ws, ws_bytes, B, T, ng, &w);
   if (st != GRPO_OK) return st;
@@ -403,6 +430,7 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.old = old_logp;
   a.ref = ref_logp;
   a.gen = gen_logp;
+  a.adv_tok = token_advantages;
   a.mask = mask;
   a.B = B;
   a.T = T;
@@ -475,25 +503,27 @@ static bool rows_vectorizable(const void* x, const void* y, int64_t ld, int32_t 
 grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
                               int32_t logits_dtype, int64_t row_stride, const void* action_ids,
                               int32_t ids_dtype, const float* old_logps, const float* gen_logps,
-                              const uint8_t* mask, const float* rewards, int64_t B, int64_t T,
+                              const uint8_t* mask, const float* rewards,
+                              const float* token_advantages, int64_t B, int64_t T,
                               int64_t V, const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
                               int32_t grad_dtype, int64_t grad_row_stride,
                               const float* grad_scale, const grpo_outputs* out, void* ws,
                               size_t ws_bytes, void* stream) {
-  if (!old_logps || !rewards || !out || !out->scalars) return GRPO_ERR_NULL;
+  if (!old_logps || !out || !out->scalars) return GRPO_ERR_NULL;
   int64_t rows = 0;
   grpo_status st = logits_common_checks(policy_logits, logits_dtype, row_stride, action_ids,
                                         ids_dtype, B, T, V, grad_out, grad_dtype,
                                         grad_row_stride, &rows);
   if (st != GRPO_OK) return st;
-  st = check_groups(groups, B);
+  st = check_advantage_source(rewards, token_advantages, groups, B);
   if (st != GRPO_OK) return st;
   st = check_cfg(cfg, ref_logits != nullptr, gen_logps != nullptr);
   if (st != GRPO_OK) return st;
+  if (token_advantages && is_sequence_level(cfg)) return GRPO_ERR_CONFIG;
   st = check_alias(policy_logits, ref_logits, logits_dtype, row_stride, rows, V, grad_out,
                    grad_dtype, grad_row_stride);
   if (st != GRPO_OK) return st;
-  const int32_t ng = groups->samples_per_prompt > 0 ? 0 : groups->num_groups;
+  const int32_t ng = group_count_csr(groups);
   Ws w;
   st = check_ws(ws, ws_bytes, B, T, ng, &w);
   if (st != GRPO_OK) return st;
@@ -511,6 +541,7 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   a.ids_i32 = ids_dtype == GRPO_I32 ? 1 : 0;
   a.old = old_logps;
   a.gen = gen_logps;
+  a.adv_tok = token_advantages;
   a.mask = mask;
   a.T = T;
   a.V = V;
@@ -634,6 +665,105 @@ grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64
   if (launch_rows(a, l, s) != hipSuccess) return GRPO_ERR_HIP;
   if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
   return GRPO_OK;
+}
+
+grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const float* old_logp,
+                                  const float* ref_logp, const uint8_t* mask, int64_t B, int64_t T,
+                                  const grpo_groups* groups, double kl_coef, double gamma,
+                                  int32_t normalize, float* adv_out, uint32_t* status, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (!rewards || !adv_out) return GRPO_ERR_NULL;
+  int64_t rows;
+  if (!mul_ok(B, T, kMaxElems, &rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if (estimator != GRPO_ADV_REINFORCE_PP && estimator != GRPO_ADV_REINFORCE_PP_BASELINE)
+    return GRPO_ERR_CONFIG;
+  if (!(kl_coef >= 0.0 && isfinite(kl_coef)) || !(gamma > 0.0 && gamma <= 1.0))
+    return GRPO_ERR_CONFIG;
+  if (normalize != 0 && normalize != 1) return GRPO_ERR_CONFIG;
+  if (estimator == GRPO_ADV_REINFORCE_PP && kl_coef != 0.0 && (!old_logp || !ref_logp))
+    return GRPO_ERR_NULL;
+  if (groups) {
+    grpo_status st = check_groups(groups, B);
+    if (st != GRPO_OK) return st;
+  }
+  if (estimator == GRPO_ADV_REINFORCE_PP_BASELINE) {
+    // the inclusive group mean without std division
+    if (!groups) return GRPO_ERR_NULL;
+    if (groups->leave_one_out || groups->scale_by_std) return GRPO_ERR_GROUPS;
+  }
+  const int32_t ng = group_count_csr(groups);
+  Ws w;
+  grpo_status st = check_ws(ws, ws_bytes, B, T, ng, &w);
+  if (st != GRPO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TokAdvArgs a{};
+  a.estimator = estimator;
+  a.rewards = rewards;
+  a.old = old_logp;
+  a.ref = ref_logp;
+  a.mask = mask;
+  a.B = B;
+  a.T = T;
+  a.spp = groups ? groups->samples_per_prompt : 0;
+  a.num_groups = ng;
+  if (ng > 0) {
+    int64_t* dev = w.at<int64_t>(w.l.offsets);
+    if (hipMemcpyAsync(dev, groups->group_boundaries, size_t(ng + 1) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return GRPO_ERR_HIP;
+    a.offsets = dev;
+  }
+  a.kl_coef = kl_coef;
+  a.gamma = gamma;
+  a.normalize = normalize;
+  a.clip = groups ? groups->clip_advantages : 0;
+  a.clip_lo = groups ? groups->adv_clip_low : 0.0;
+  a.clip_hi = groups ? groups->adv_clip_high : 0.0;
+  a.hdr = w.hdr();
+  a.S = w.at<double>(w.l.P);
+  a.L = w.at<int32_t>(w.l.L);
+  a.out = adv_out;
+  a.status = status;
+  return launch_token_advantages(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+grpo_status grpo_gdpo_advantages(const float* rewards, int32_t num_components, int64_t B,
+                                 const grpo_groups* groups, float* adv_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!rewards || !adv_out) return GRPO_ERR_NULL;
+  if (B <= 0 || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if (num_components < 2) return GRPO_ERR_CONFIG;
+  int64_t tmp;
+  if (!mul_ok(B, num_components, kMaxElems, &tmp)) return GRPO_ERR_SHAPE;
+  grpo_status st = check_groups(groups, B);
+  if (st != GRPO_OK) return st;
+  const int32_t ng = group_count_csr(groups);
+  Ws w;
+  st = check_ws(ws, ws_bytes, B, 1, ng, &w);
+  if (st != GRPO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GdpoArgs a{};
+  a.rewards = rewards;
+  a.C = num_components;
+  a.B = B;
+  a.spp = groups->samples_per_prompt;
+  a.num_groups = ng;
+  if (ng > 0) {
+    int64_t* dev = w.at<int64_t>(w.l.offsets);
+    if (hipMemcpyAsync(dev, groups->group_boundaries, size_t(ng + 1) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return GRPO_ERR_HIP;
+    a.offsets = dev;
+  }
+  a.leave_one_out = groups->leave_one_out;
+  a.scale_by_std = groups->scale_by_std;
+  a.std_eps = groups->std_eps;
+  a.clip = groups->clip_advantages;
+  a.clip_lo = groups->adv_clip_low;
+  a.clip_hi = groups->adv_clip_high;
+  a.total = w.at<double>(w.l.P);
+  a.out = adv_out;
+  return launch_gdpo(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
 }  // extern "C"

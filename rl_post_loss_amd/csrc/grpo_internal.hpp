@@ -17,6 +17,7 @@ struct WsHeader {
   uint32_t status;        // GRPO_FAULT_* bits gathered during the call
   uint32_t pad0;
   int64_t num_tokens;     // N
+  double mu, sd;          // moments of the global masked normalization
 };
 
 // Per-row state handed from the forward pass to the gradient pass.
@@ -95,6 +96,8 @@ struct PrepArgs {
   const int64_t* offsets;   // device copy of the CSR offsets (num_groups + 1)
   int32_t leave_one_out, scale_by_std;
   double std_eps;
+  int32_t clip;             // clamp the advantages to [clip_lo, clip_hi]
+  double clip_lo, clip_hi;
   int32_t reduction;
   double alpha;
   double norm_constant;     // GRPO_FIXED_CONSTANT
@@ -127,6 +130,7 @@ struct RowArgs {
   int32_t ids_i32;
   const float* old;
   const float* gen;         // generating policy's log-probs, or null
+  const float* adv_tok;     // [B, T] token advantages, or null (per-sequence A)
   const uint8_t* mask;
   int64_t T, V, rows;
   Objective obj;
@@ -228,6 +232,45 @@ struct RealArgs {
   double* gloss;
 };
 
+// Token-level advantage estimators (REINFORCE++, -baseline) and the global
+// masked normalization, in passes over the sequences.
+struct TokAdvArgs {
+  int32_t estimator;        // grpo_adv_estimator
+  const float* rewards;
+  const float* old;         // or null (no KL shaping)
+  const float* ref;         // or null (no KL shaping)
+  const uint8_t* mask;
+  int64_t B, T;
+  int32_t spp, num_groups;
+  const int64_t* offsets;
+  double kl_coef, gamma;
+  int32_t normalize;
+  int32_t clip;
+  double clip_lo, clip_hi;
+  int32_t pass;             // 0: sums (or the output when not normalizing), 1: squared
+                            // deviations, 2: the normalized output
+  WsHeader* hdr;
+  double* S;                // [B] per-sequence sums of the pass
+  int32_t* L;               // [B] active slots
+  float* out;               // [B, T]
+  uint32_t* status;         // or null
+};
+
+// GDPO multi-reward advantages (one block).
+struct GdpoArgs {
+  const float* rewards;     // [C, B]
+  int32_t C;
+  int64_t B;
+  int32_t spp, num_groups;
+  const int64_t* offsets;
+  int32_t leave_one_out, scale_by_std;
+  double std_eps;
+  int32_t clip;
+  double clip_lo, clip_hi;
+  double* total;            // [B] workspace
+  float* out;               // [B]
+};
+
 // Scalar reduction (stage 2).
 struct FinalArgs {
   int64_t B;
@@ -250,6 +293,7 @@ struct TokenArgs {
   const float* old;
   const float* ref;         // null when beta == 0
   const float* gen;         // null: no off-policy weight
+  const float* adv_tok;     // [B, T] token advantages, or null (per-sequence A)
   const uint8_t* mask;
   int64_t B, T;
   Objective obj;

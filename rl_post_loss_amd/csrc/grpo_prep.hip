@@ -105,6 +105,16 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
   }
   if (tid == 0 && a.useq) a.useq[i] = 0.0f;
 
+  if (a.rewards == nullptr) {
+    // token advantages come from the caller: only the counts are needed
+    if (tid == 0) {
+      a.A[i] = 0.0f;
+      a.L[i] = int32_t(L);
+      if (a.seq_tokens_out) a.seq_tokens_out[i] = int32_t(L);
+    }
+    return;
+  }
+
   // group [s, e) of sequence i
   int64_t s, e;
   if (a.spp > 0) {
@@ -163,7 +173,11 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
     const double ri = double(a.rewards[i]);
     const double base = a.leave_one_out ? (total - ri) / double(n - 1) : mean;
     const double diff = ri - base;
-    const float advf = float(a.scale_by_std ? diff / denom : diff);
+    double adv = a.scale_by_std ? diff / denom : diff;
+    // optional clamp (dockyard_rl, Advantage estimation), before the one
+    // rounding; comparisons keep a NaN
+    if (a.clip) adv = adv < a.clip_lo ? a.clip_lo : (adv > a.clip_hi ? a.clip_hi : adv);
+    const float advf = float(adv);
     a.A[i] = advf;
     if (a.adv_out) a.adv_out[i] = advf;
     a.L[i] = int32_t(L);

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   const float wg = float(a.w[i]) * (a.grad_scale ? *a.grad_scale : 1.0f);
   const bool has_ref = a.ref != nullptr;
   const bool has_gen = a.gen != nullptr;
+  const bool has_atok = a.adv_tok != nullptr;
   const float keep = a.iwseq ? float(a.iwseq[i]) : 1.0f;
   // sequence-level losses: the sequence kernels' loss, clip flag and
   // gradient coefficient (grad_scale included) of this sequence
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
                                        reinterpret_cast<uintptr_t>(a.old) |
                                        reinterpret_cast<uintptr_t>(a.ref) |
                                        reinterpret_cast<uintptr_t>(a.gen) |
+                                       reinterpret_cast<uintptr_t>(a.adv_tok) |
                                        reinterpret_cast<uintptr_t>(a.dlogp) |
                                        reinterpret_cast<uintptr_t>(a.out_loss) |
                                        reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     const int64_t n4 = a.T / 4;
     for (int64_t q0 = tid; q0 < n4; q0 += QU * kRedThreads) {
       uint32_t m4[QU];
-      f32x4 lp[QU], od[QU], rf[QU], gn[QU];
+      f32x4 lp[QU], od[QU], rf[QU], gn[QU], av[QU];
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
         const int64_t q = q0 + int64_t(u) * kRedThreads;
@@ -161,12 +163,13 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
         const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
-        lp[u] = od[u] = rf[u] = gn[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lp[u] = od[u] = rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (m4[u] != 0) {
           lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
           od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
           if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
           if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
+          if (has_atok) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.adv_tok + t0));
         }
       }
 #pragma unroll
@@ -178,12 +181,14 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
         const float odv[4] = {od[u].x, od[u].y, od[u].z, od[u].w};
         const float rfv[4] = {rf[u].x, rf[u].y, rf[u].z, rf[u].w};
         const float gnv[4] = {gn[u].x, gn[u].y, gn[u].z, gn[u].w};
+        const float avv[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
         float gv[4] = {0.f, 0.f, 0.f, 0.f}, tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if ((m4[u] >> (8 * j)) & 0xffu) {
             const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
-            TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, adv, gnv[j], keep);
+            TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, has_atok ? avv[j] : adv,
+                                                 gnv[j], keep);
             if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, odv[j], gnv[j], has_gen);
             gv[j] = seqlv ? wg * r.g + useq : wg * r.g;
             tl[j] = r.loss;
@@ -209,7 +214,8 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
         const float lps = a.logp[s];
         const float d = has_ref ? a.ref[s] - lps : 0.0f;
         const float ods = a.old[s], gns = has_gen ? a.gen[s] : 0.0f;
-        TokObj r = token_objective<kGeneral>(a.obj, lps, ods, d, adv, gns, keep);
+        TokObj r = token_objective<kGeneral>(a.obj, lps, ods, d, has_atok ? a.adv_tok[s] : adv, gns,
+                                             keep);
         if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, ods, gns, has_gen);
         g = seqlv ? wg * r.g + useq : wg * r.g;
         tl = r.loss;

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       old = a.old[row];
       if (a.gen) gen = a.gen[row];
       const int64_t i = row / a.T;
-      adv = a.A[i];
+      adv = a.adv_tok ? a.adv_tok[row] : a.A[i];
       wgt = float(a.w[i]);
       if (a.grad_scale) gs = *a.grad_scale;
       if (a.iwseq) keep = float(a.iwseq[i]);

@@ -60,22 +60,25 @@ def workspace(B, T, num_groups, device, dedicated=False):
 _STRUCT_CACHE: dict = {}
 
 
-def _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps):
+def _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps,
+            adv_clip=None):
     key = ("g", B, samples_per_prompt,
            None if group_boundaries is None else tuple(int(v) for v in group_boundaries),
-           bool(leave_one_out), bool(scale_by_std), float(std_eps))
+           bool(leave_one_out), bool(scale_by_std), float(std_eps),
+           None if adv_clip is None else tuple(float(v) for v in adv_clip))
     hit = _STRUCT_CACHE.get(key)
     if hit is not None:
         return hit
     hit = _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
-                       std_eps)
+                       std_eps, adv_clip)
     if len(_STRUCT_CACHE) > 256:
         _STRUCT_CACHE.clear()
     _STRUCT_CACHE[key] = hit
     return hit
 
 
-def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps):
+def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std, std_eps,
+                 adv_clip=None):
     if (samples_per_prompt is None) == (group_boundaries is None):
         raise ValueError("give exactly one of samples_per_prompt / group_boundaries")
     g = GrpoGroups()
@@ -95,6 +98,9 @@ def _make_groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_b
     g.leave_one_out = 1 if leave_one_out else 0
     g.scale_by_std = 1 if scale_by_std else 0
     g.std_eps = float(std_eps)
+    if adv_clip is not None:
+        g.clip_advantages = 1
+        g.adv_clip_low, g.adv_clip_high = float(adv_clip[0]), float(adv_clip[1])
     return g, keep, ng
 
 
@@ -266,15 +272,15 @@ def _mask_ptr(mask, B, T, device):
 
 
 def grpo_advantages(rewards, *, samples_per_prompt=None, group_boundaries=None,
-                    leave_one_out=False, scale_by_std=True, std_eps=1e-6):
+                    leave_one_out=False, scale_by_std=True, std_eps=1e-6, adv_clip=None):
     """Group-relative advantages [B] float32 ("GRPO Loss", Accuracy; dockyard_rl,
-    Advantage estimation)."""
+    Advantage estimation).  adv_clip: (low, high) clamp, or None."""
     lib = load_library()
     _need(rewards.dtype == torch.float32 and rewards.dim() == 1 and rewards.is_cuda
           and rewards.is_contiguous(), "rewards must be a contiguous float32 [B] GPU tensor")
     B = rewards.shape[0]
     g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
-                          std_eps)
+                          std_eps, adv_clip)
     out = torch.empty(B, dtype=torch.float32, device=rewards.device)
     ws, wsb = workspace(B, 1, ng, rewards.device)
     check(lib.grpo_advantages(rewards.data_ptr(), B, C.byref(g), out.data_ptr(), ws.data_ptr(),
@@ -282,15 +288,98 @@ def grpo_advantages(rewards, *, samples_per_prompt=None, group_boundaries=None,
     return out
 
 
+def grpo_token_advantages(estimator, rewards, completion_mask=None, *, old_logps=None,
+                          ref_logps=None, samples_per_prompt=None, group_boundaries=None,
+                          kl_coef=0.0, gamma=1.0, normalize=True, adv_clip=None, status=None):
+    """Token-level advantages [B, T] float32 (Relax REINFORCE++ page):
+    ``reinforce_pp`` (k1-shaped token rewards from old_logps and ref_logps
+    with coefficient kl_coef, the terminal reward on the last active slot,
+    discounted returns with gamma) or ``reinforce_pp_baseline`` (reward
+    minus the inclusive group mean), then the global masked normalization
+    when ``normalize``; adv_clip (low, high) clamps the result.  ``status``:
+    an int32 [1] tensor for the fault bits, or None."""
+    lib = load_library()
+    _need(estimator in _abi.ADV_ESTIMATOR_CODES, f"unknown estimator {estimator!r}")
+    _need(rewards.dtype == torch.float32 and rewards.dim() == 1 and rewards.is_cuda
+          and rewards.is_contiguous(), "rewards must be a contiguous float32 [B] GPU tensor")
+    dev = rewards.device
+    B = rewards.shape[0]
+    ref = completion_mask if completion_mask is not None else old_logps
+    _need(ref is not None, "give completion_mask or old_logps to fix T")
+    T = ref.shape[1]
+    for name, t in (("old_logps", old_logps), ("ref_logps", ref_logps)):
+        if t is not None:
+            _need(t.dtype == torch.float32 and tuple(t.shape) == (B, T) and t.is_contiguous()
+                  and t.device == dev, f"{name} must be contiguous float32 [B, T] on {dev}")
+    mptr, _ = _mask_ptr(completion_mask, B, T, dev)
+    gptr = None
+    ng = 0
+    if samples_per_prompt is not None or group_boundaries is not None:
+        g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, False, False, 1e-6, adv_clip)
+        gptr = C.byref(g)
+    elif adv_clip is not None:
+        # the clamp travels in the group description: a dummy of one group of B
+        g, keep, ng = _groups(B, None, [0, B], False, False, 1e-6, adv_clip)
+        gptr = C.byref(g)
+    out = torch.empty((B, T), dtype=torch.float32, device=dev)
+    ws, wsb = workspace(B, T, ng, dev)
+    check(lib.grpo_token_advantages(_abi.ADV_ESTIMATOR_CODES[estimator], rewards.data_ptr(),
+                                    _ptr(old_logps), _ptr(ref_logps), mptr, B, T, gptr,
+                                    float(kl_coef), float(gamma), 1 if normalize else 0,
+                                    out.data_ptr(), _ptr(status), ws.data_ptr(), wsb,
+                                    _stream_ptr(dev)), lib)
+    return out
+
+
+def grpo_gdpo_advantages(component_rewards, *, samples_per_prompt=None, group_boundaries=None,
+                         leave_one_out=True, scale_by_std=True, std_eps=1e-6, adv_clip=None):
+    """Multi-reward advantages [B] float32 (dockyard_rl, GDPO): a group
+    baseline per reward component ([C, B] float32, C >= 2), summed, then
+    renormalised over the batch."""
+    lib = load_library()
+    R = component_rewards
+    _need(R.dtype == torch.float32 and R.dim() == 2 and R.is_cuda and R.is_contiguous(),
+          "component_rewards must be a contiguous float32 [C, B] GPU tensor")
+    Cn, B = R.shape
+    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                          std_eps, adv_clip)
+    out = torch.empty(B, dtype=torch.float32, device=R.device)
+    ws, wsb = workspace(B, 1, ng, R.device)
+    check(lib.grpo_gdpo_advantages(R.data_ptr(), Cn, B, C.byref(g), out.data_ptr(), ws.data_ptr(),
+                                   wsb, _stream_ptr(R.device)), lib)
+    return out
+
+
+def _advantage_args(rewards, token_advantages, B, T, dev, samples_per_prompt, group_boundaries,
+                    leave_one_out, scale_by_std, std_eps, adv_clip):
+    """(rewards pointer, token-advantage pointer, groups struct or None, CSR count)."""
+    if token_advantages is not None:
+        _need(rewards is None and samples_per_prompt is None and group_boundaries is None,
+              "token_advantages replace rewards and groups")
+        _need(token_advantages.dtype == torch.float32 and tuple(token_advantages.shape) == (B, T)
+              and token_advantages.is_contiguous() and token_advantages.device == dev,
+              "token_advantages must be contiguous float32 [B, T]")
+        return None, token_advantages.data_ptr(), None, 0
+    _need(rewards is not None and rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,)
+          and rewards.device == dev, "rewards must be float32 [B]")
+    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
+                          std_eps, adv_clip)
+    return rewards.contiguous().data_ptr(), None, g, ng
+
+
 def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *, gen_logps=None,
                     clip_eps=0.2, eps_low=None, eps_high=None, beta=0.04,
                     samples_per_prompt=None, group_boundaries=None, leave_one_out=False,
                     scale_by_std=True, std_eps=1e-6, reduction="token_mean", alpha=None,
-                    want_grad=True, grad_scale=None, per_token=False, out=None, **objective):
+                    want_grad=True, grad_scale=None, per_token=False, out=None,
+                    token_advantages=None, adv_clip=None, **objective):
     """Loss from per-token log-probs ([B, T] float32); ``grad`` is d loss / d logp.
     ``out``: a previous result of the same sizes whose buffers are reused.
     ``gen_logps``: the generating policy's log-probs [B, T] float32, for the
     off-policy importance weight (None: no correction).
+    ``token_advantages``: precomputed [B, T] float32 advantages (then rewards
+    is None and no groups are given); ``adv_clip``: (low, high) clamp of the
+    group advantages.
     ``objective``: the keywords of OBJECTIVE_DEFAULTS (policy-loss form, KL
     estimator, dual clip, SAPO temperatures, KL clamps, fixed normaliser,
     truncation of the importance weight, REAL temperature).  pg_loss "gspo"
@@ -307,11 +396,10 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
             continue
         _need(t.dtype == torch.float32 and tuple(t.shape) == (B, T) and t.is_contiguous()
               and t.device == dev, f"{name} must be contiguous float32 [B, T] on {dev}")
-    _need(rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,) and rewards.device == dev,
-          "rewards must be float32 [B]")
     mptr, _ = _mask_ptr(completion_mask, B, T, dev)
-    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
-                          std_eps)
+    rptr, aptr, g, ng = _advantage_args(rewards, token_advantages, B, T, dev, samples_per_prompt,
+                                        group_boundaries, leave_one_out, scale_by_std, std_eps,
+                                        adv_clip)
     cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, dict(objective))
     res = _reuse(out, B, T, dev, per_token)
     if res is None:
@@ -324,8 +412,8 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
         res.grad = None
     ws, wsb = workspace(B, T, ng, dev)
     check(lib.grpo_token_loss(logp.data_ptr(), old_logps.data_ptr(), _ptr(ref_logps),
-                              _ptr(gen_logps), mptr,
-                              rewards.contiguous().data_ptr(), B, T, C.byref(g), C.byref(cfg),
+                              _ptr(gen_logps), mptr, rptr, aptr, B, T,
+                              None if g is None else C.byref(g), C.byref(cfg),
                               _ptr(res.grad), _ptr(grad_scale), C.byref(o), ws.data_ptr(), wsb,
                               _stream_ptr(dev)), lib)
     return res
@@ -336,14 +424,15 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                       beta=0.04, samples_per_prompt=None, group_boundaries=None,
                       leave_one_out=False, scale_by_std=True, std_eps=1e-6,
                       reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
-                      grad_scale=None, per_token=False, out=None, _ws=None, **objective):
+                      grad_scale=None, per_token=False, out=None, _ws=None,
+                      token_advantages=None, adv_clip=None, **objective):
     """Fused forward + analytic backward from [B, T, V] logits.
 
     grad_out: None allocates a contiguous gradient (dtype ``grad_dtype``,
     default the logits dtype); a tensor writes into it (it may be
     ``policy_logits`` itself, in place); False runs the forward only.
     out: a previous result of the same sizes whose output buffers are reused.
-    gen_logps, objective: as for grpo_token_loss.
+    gen_logps, token_advantages, adv_clip, objective: as for grpo_token_loss.
     """
     lib = load_library()
     dev = policy_logits.device
@@ -365,11 +454,10 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
         _need(gen_logps.dtype == torch.float32 and tuple(gen_logps.shape) == (B, T)
               and gen_logps.is_contiguous() and gen_logps.device == dev,
               "gen_logps must be contiguous float32 [B, T]")
-    _need(rewards.dtype == torch.float32 and tuple(rewards.shape) == (B,) and rewards.device == dev,
-          "rewards must be float32 [B]")
     mptr, _ = _mask_ptr(completion_mask, B, T, dev)
-    g, keep, ng = _groups(B, samples_per_prompt, group_boundaries, leave_one_out, scale_by_std,
-                          std_eps)
+    rptr, aptr, g, ng = _advantage_args(rewards, token_advantages, B, T, dev, samples_per_prompt,
+                                        group_boundaries, leave_one_out, scale_by_std, std_eps,
+                                        adv_clip)
     cfg = _cfg(clip_eps, eps_low, eps_high, beta, reduction, alpha, dict(objective))
     res = _reuse(out, B, T, dev, per_token)
     if res is None:
@@ -394,8 +482,8 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
     check(lib.grpo_loss_fwd_bwd(policy_logits.data_ptr(), _ptr(ref_logits),
                                 _FDTYPE[policy_logits.dtype], ld, action_ids.data_ptr(),
                                 _IDTYPE[action_ids.dtype], old_logps.data_ptr(),
-                                _ptr(gen_logps), mptr,
-                                rewards.contiguous().data_ptr(), B, T, V, C.byref(g), C.byref(cfg),
+                                _ptr(gen_logps), mptr, rptr, aptr, B, T, V,
+                                None if g is None else C.byref(g), C.byref(cfg),
                                 gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o), ws.data_ptr(),
                                 wsb, _stream_ptr(dev)), lib)
     return res

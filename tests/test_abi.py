@@ -30,6 +30,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("grpo_advantages", "grpo_token_loss", "grpo_loss_fwd_bwd", "grpo_loss_bwd",
+                 "grpo_token_advantages", "grpo_gdpo_advantages",
                  "grpo_workspace_bytes", "grpo_workspace_init", "grpo_status_str",
                  "grpo_abi_version", "grpo_set_timing_events"):
         assert name in fns
@@ -109,14 +110,15 @@ FAKE_WS = 0x20000000
 
 def _fwd(lib, B=8, T=4, V=32, g=None, cfg=None, ref=FAKE, grad=FAKE + 0x4000000, ws=FAKE_WS,
          ws_bytes=1 << 30, ld=None, gld=None, dtype=0, gdtype=0, ids_dtype=0, scalars=FAKE,
-         gen=None):
+         gen=None, rewards=FAKE, tadv=None, no_groups=False):
     if g is None:
         g, _ = _groups()
     cfg = cfg or _cfg()
     o = _abi.GrpoOutputs()
     o.scalars = scalars
-    return lib.grpo_loss_fwd_bwd(FAKE, ref, dtype, ld or V, FAKE, ids_dtype, FAKE, gen, None, FAKE,
-                                 B, T, V, C.byref(g), C.byref(cfg), grad, gdtype, gld or V, None,
+    return lib.grpo_loss_fwd_bwd(FAKE, ref, dtype, ld or V, FAKE, ids_dtype, FAKE, gen, None,
+                                 rewards, tadv, B, T, V, None if no_groups else C.byref(g),
+                                 C.byref(cfg), grad, gdtype, gld or V, None,
                                  C.byref(o), ws, ws_bytes, None)
 
 
@@ -149,6 +151,19 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
     g, _ = _groups(eps=0.0)
     assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g, _ = _groups()
+    g.clip_advantages, g.adv_clip_low, g.adv_clip_high = 1, 1.0, -1.0    # low > high
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g.clip_advantages, g.adv_clip_low, g.adv_clip_high = 1, -float("inf"), 1.0
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    g.clip_advantages = 2
+    assert _fwd(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    # advantage source: exactly one of rewards (with groups) or token advantages
+    assert _fwd(lib, rewards=None) == E["GRPO_ERR_NULL"]
+    assert _fwd(lib, tadv=FAKE) == E["GRPO_ERR_CONFIG"]                       # and rewards
+    assert _fwd(lib, tadv=FAKE, rewards=None) == E["GRPO_ERR_CONFIG"]         # and groups
+    assert _fwd(lib, tadv=FAKE, rewards=None, no_groups=True,
+                cfg=_cfg(pg_loss=5, red=1)) == E["GRPO_ERR_CONFIG"]          # sequence-level
     # config
     assert _fwd(lib, cfg=_cfg(lo=1.0)) == E["GRPO_ERR_CONFIG"]
     assert _fwd(lib, cfg=_cfg(lo=-0.1)) == E["GRPO_ERR_CONFIG"]
@@ -205,7 +220,7 @@ def test_token_loss_and_advantages_validation():
     o = _abi.GrpoOutputs()
     o.scalars = FAKE
     call = lambda **k: lib.grpo_token_loss(
-        k.get("logp", FAKE), FAKE, k.get("ref", FAKE), k.get("gen"), None, FAKE, k.get("B", 8),
+        k.get("logp", FAKE), FAKE, k.get("ref", FAKE), k.get("gen"), None, FAKE, None, k.get("B", 8),
         k.get("T", 4),
         C.byref(k.get("g", g)), C.byref(k.get("cfg", cfg)), FAKE, None, C.byref(o),
         k.get("ws", FAKE_WS), k.get("wsb", 1 << 30), None)
@@ -222,6 +237,31 @@ def test_token_loss_and_advantages_validation():
                              1 << 30, None) == E["GRPO_ERR_NULL"]
     assert lib.grpo_loss_bwd(FAKE, 0, 32, FAKE, 0, None, 8, 4, 32, FAKE + 4, 0, 32, None, FAKE_WS,
                              1 << 30, None) == E["GRPO_ERR_ALIAS"]
+    # token advantages
+    tok = lambda est=0, r=FAKE, old=FAKE, ref=FAKE, g=None, kl=0.1, gamma=1.0, norm=1, out=FAKE, \
+        wsb=1 << 30: lib.grpo_token_advantages(est, r, old, ref, None, 8, 4,
+                                               None if g is None else C.byref(g), kl, gamma, norm,
+                                               out, None, FAKE_WS, wsb, None)
+    assert tok(r=None) == E["GRPO_ERR_NULL"]
+    assert tok(out=None) == E["GRPO_ERR_NULL"]
+    assert tok(est=2) == E["GRPO_ERR_CONFIG"]
+    assert tok(kl=-1.0) == E["GRPO_ERR_CONFIG"]
+    assert tok(gamma=0.0) == E["GRPO_ERR_CONFIG"]
+    assert tok(gamma=1.5) == E["GRPO_ERR_CONFIG"]
+    assert tok(norm=2) == E["GRPO_ERR_CONFIG"]
+    assert tok(ref=None) == E["GRPO_ERR_NULL"]                     # KL shaping needs ref
+    assert tok(est=1) == E["GRPO_ERR_NULL"]                        # baseline needs groups
+    gb, _ = _groups(scale=1)
+    assert tok(est=1, g=gb) == E["GRPO_ERR_GROUPS"]                # inclusive mean, no std
+    gb, _ = _groups(spp=3, scale=0)
+    assert tok(est=1, g=gb) == E["GRPO_ERR_GROUPS"]
+    assert tok(wsb=10) == E["GRPO_ERR_WORKSPACE"]
+    # GDPO
+    gd = lambda r=FAKE, c=2, g=g, out=FAKE: lib.grpo_gdpo_advantages(r, c, 8, C.byref(g), out,
+                                                                     FAKE_WS, 1 << 20, None)
+    assert gd(r=None) == E["GRPO_ERR_NULL"]
+    assert gd(c=1) == E["GRPO_ERR_CONFIG"]
+    assert gd(g=_groups(spp=3)[0]) == E["GRPO_ERR_GROUPS"]
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
