@@ -236,6 +236,72 @@ def run_token(args):
     print(json.dumps(out), flush=True)
 
 
+ADV_WORKLOADS = {"adv_reinforce_pp": "reinforce_pp", "adv_reinforce_pp_baseline": "reinforce_pp_baseline"}
+
+
+def run_adv(args):
+    """Token-level advantage estimator over the log-prob workload's shape
+    (B = 1024 in groups of 16, T = 4096, ragged lengths): REINFORCE++
+    returns (k1 shaping 0.01, gamma 1) or the inclusive group baseline, with
+    the global masked normalization.  Input copies are rotated as for the
+    token loss; timed as HIP graph replays."""
+    import torch
+    import rl_post_loss_amd as rpl
+    from workloads import TOKEN_WORKLOADS, make_token_inputs
+
+    rpl.load_library()
+    dev = torch.device("cuda:0")
+    est = ADV_WORKLOADS[args.workload]
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    copies = [make_token_inputs(wl, device=dev, seed=args.seed + k) for k in range(args.copies)]
+    kw = dict(kl_coef=0.01, gamma=1.0, normalize=True)
+    if est == "reinforce_pp_baseline":
+        kw = dict(samples_per_prompt=wl.group_size, normalize=True)
+    outs = [None] * len(copies)
+
+    def step(k):
+        j = k % len(copies)
+        c = copies[j]
+        extra = dict(old_logps=c["old_logps"], ref_logps=c["ref_logp"]) if est == "reinforce_pp" else {}
+        outs[j] = rpl.grpo_token_advantages(est, c["rewards"], c["mask"], **extra, **kw)
+
+    for k in range(max(args.warmup, len(copies))):
+        step(k)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(len(copies)):
+            step(j)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for j in range(len(copies)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(j)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows = wl.B * wl.T
+    # minimum bytes: old, ref f32 and the mask read once (REINFORCE++), the output written once
+    per_slot = (4 + 4 + 1 + 4) if est == "reinforce_pp" else (1 + 4)
+    alg = rows * per_slot
+    out = {"metric": "tokens/s for the token-level advantage estimator (returns + global normalization)",
+           "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+           "config": {"workload": f"{args.workload}: B={wl.B} (groups of {wl.group_size}), T={wl.T}, "
+                                  f"ragged lengths, {est}, normalized; input copies rotated: {args.copies}",
+                      "algorithmic_bytes": alg, "step_GBps": alg / (ms * 1e-3) / 1e9,
+                      "timing": "HIP graph replays"}}
+    print(json.dumps(out), flush=True)
+
+
 def run(args):
     import torch
     import rl_post_loss_amd as rpl
@@ -431,6 +497,8 @@ def main():
         sys.exit(2)
     if args.workload.startswith("token_loss"):
         run_token(args)
+    elif args.workload in ADV_WORKLOADS:
+        run_adv(args)
     else:
         run(args)
 
