@@ -12,11 +12,14 @@
 // summed over components, renormalised over the batch.
 //
 // Everything is binary64 with contraction off and rounded once to float32.
-// The returns run as a chunked backward scan: thread j of the sequence's
-// block owns slots [j K, (j + 1) K); each chunk's partial return and
-// gamma^length are combined right to left by one thread, then every chunk
-// replays its slots from the carry it receives.  Sums over slots are fixed
-// trees, sums over sequences a single block, so results repeat bit for bit.
+// The returns run as a tiled backward scan: a sequence's block walks tiles of
+// kAdvTile slots from the right end; a tile's token rewards are staged in LDS
+// with coalesced loads, thread j folds its kAdvChunk consecutive slots into
+// an affine map x -> h + g x of the return after the chunk, a suffix scan of
+// those maps (wave shuffles, then the waves in order) gives every chunk its
+// carry and the carry into the next tile, every chunk replays its slots from
+// its carry, and the returns leave LDS with coalesced accesses again.  Sums over slots are fixed trees, sums over
+// sequences a single block, so results repeat bit for bit.
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
@@ -25,18 +28,25 @@
 namespace grpo {
 
 constexpr int kAdvThreads = 256;
+constexpr int kAdvChunk = 8;                           // consecutive slots per thread in a tile
+constexpr int kAdvTile = kAdvThreads * kAdvChunk;      // slots per tile
+constexpr int kAdvPad = kAdvChunk + 1;                 // LDS row per thread (bank spread)
 constexpr int kMomentThreads = 1024;
 constexpr int kGdpoThreads = 1024;
 
 struct AdvShared {
-  double h[kAdvThreads];      // chunk's return at its first slot, from its own slots
-  double g[kAdvThreads];      // gamma^(chunk length)
-  double carry[kAdvThreads];  // return at the slot after the chunk
+  double v[kAdvThreads * kAdvPad];  // a tile's token rewards, then its returns
+  uint8_t act[kAdvTile];            // a tile's mask
+  double wh[kAdvThreads / kWave];  // per wave: its chunks' composed map (h + g x)
+  double wg[kAdvThreads / kWave];
   double red[kAdvThreads / kWave];
   long long red_i[kAdvThreads / kWave];
   double cval;                // baseline difference of the sequence
   long long last;             // last active slot (-1: none)
 };
+
+// LDS index of tile slot q (thread q / kAdvChunk owns kAdvChunk consecutive slots)
+__device__ __forceinline__ int adv_lds(int q) { return (q / kAdvChunk) * kAdvPad + q % kAdvChunk; }
 
 __device__ __forceinline__ bool adv_active(const TokAdvArgs& a, int64_t r) {
   return a.mask == nullptr || a.mask[r] != 0;
@@ -47,61 +57,122 @@ __device__ __forceinline__ double clamp_adv(const TokAdvArgs& a, double v) {
   return v < a.clip_lo ? a.clip_lo : (v > a.clip_hi ? a.clip_hi : v);  // keeps a NaN
 }
 
-// Token reward of REINFORCE++ at slot t (0 at masked slots).
-__device__ __forceinline__ double rpp_reward(const TokAdvArgs& a, int64_t base, int64_t t,
-                                             long long last, double R) {
-#pragma clang fp contract(off)
-  const int64_t r = base + t;
-  if (!adv_active(a, r)) return 0.0;
-  double v = 0.0;
-  if (a.kl_coef != 0.0) v = -a.kl_coef * (double(a.old[r]) - double(a.ref[r]));
-  if (t == last) v = v + R;
-  return v;
-}
-
-// Calls f(t, active, A_t) for every slot of this thread's chunk of sequence
-// i, in backward order (A_t is the raw advantage, 0 at masked slots).  All
-// threads of the block must call it.
+// Calls f(t, active, A_t) once for every slot t of sequence i (A_t the raw
+// advantage, 0 at masked slots); each thread visits slots t = tile start +
+// threadIdx.x + k * blockDim.x, tiles from the right end.  All threads of
+// the block must call it.
 template <typename F>
 __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& f) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int64_t T = a.T, base = i * a.T;
-  const int64_t K = (T + kAdvThreads - 1) / kAdvThreads;
-  const int64_t t0 = tid * K < T ? tid * K : T;
-  const int64_t t1 = t0 + K < T ? t0 + K : T;
   if (a.estimator == GRPO_ADV_REINFORCE_PP_BASELINE) {
     const double c = sh.cval;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-      const bool act = adv_active(a, base + t);
-      f(t, act, act ? c : 0.0);
+    constexpr int U = 8;
+    for (int64_t t0 = tid; t0 < T; t0 += int64_t(U) * kAdvThreads) {
+      bool act[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t t = t0 + int64_t(k) * kAdvThreads;
+        act[k] = t < T && adv_active(a, base + t);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t t = t0 + int64_t(k) * kAdvThreads;
+        if (t < T) f(t, act[k], act[k] ? c : 0.0);
+      }
     }
     return;
   }
   const double R = double(a.rewards[i]);
   const long long last = sh.last;
-  double acc = 0.0, gl = 1.0;
-  for (int64_t t = t1 - 1; t >= t0; --t) {
-    acc = rpp_reward(a, base, t, last, R) + a.gamma * acc;
-    gl = gl * a.gamma;
-  }
-  __syncthreads();  // sh.h / sh.g may still be read by a previous call
-  sh.h[tid] = acc;
-  sh.g[tid] = gl;
-  __syncthreads();
-  if (tid == 0) {
-    double c = 0.0;
-    for (int j = kAdvThreads - 1; j >= 0; --j) {
-      sh.carry[j] = c;
-      c = sh.h[j] + sh.g[j] * c;
+  const bool shaped = a.kl_coef != 0.0;
+  constexpr int kPer = kAdvTile / kAdvThreads;
+  constexpr int NW = kAdvThreads / kWave;
+  const int lane = tid % kWave, wv = tid / kWave;
+  double tile_carry = 0.0;  // return at the slot after the current tile (same in every thread)
+  for (int64_t end = T; end > 0; end -= kAdvTile) {
+    const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
+    const int n = int(end - start);
+    __syncthreads();  // the previous tile's values are consumed
+    // token rewards r_t = m_t (-kl_coef (old - ref) + [t = T_i] R): every load of
+    // the tile is issued before any is used; masked values are discarded by selection
+    uint8_t mk[kPer];
+    float ov[kPer], rv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = tid + k * kAdvThreads;
+      mk[k] = 0;
+      ov[k] = rv[k] = 0.0f;
+      if (q < n) {
+        mk[k] = a.mask ? a.mask[base + start + q] : 1;
+        if (shaped) {
+          ov[k] = a.old[base + start + q];
+          rv[k] = a.ref[base + start + q];
+        }
+      }
     }
-  }
-  __syncthreads();
-  acc = sh.carry[tid];
-  for (int64_t t = t1 - 1; t >= t0; --t) {
-    acc = rpp_reward(a, base, t, last, R) + a.gamma * acc;
-    const bool act = adv_active(a, base + t);
-    f(t, act, act ? acc : 0.0);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = tid + k * kAdvThreads;
+      if (q >= n) continue;
+      const bool act = mk[k] != 0;
+      double v = 0.0;
+      if (act) {
+        if (shaped) v = -a.kl_coef * (double(ov[k]) - double(rv[k]));
+        if (start + q == last) v = v + R;
+      }
+      sh.v[adv_lds(q)] = v;
+      sh.act[q] = act ? 1 : 0;
+    }
+    __syncthreads();
+    // this thread's chunk as an affine map x -> h + g x of the return after it
+    const int q0 = tid * kAdvChunk < n ? tid * kAdvChunk : n;
+    const int q1 = q0 + kAdvChunk < n ? q0 + kAdvChunk : n;
+    double h = 0.0, g = 1.0;
+    for (int q = q1 - 1; q >= q0; --q) {
+      h = sh.v[adv_lds(q)] + a.gamma * h;
+      g = g * a.gamma;
+    }
+    // suffix scan of the maps (chunk j composed with chunks j+1 ...): in the
+    // wave, then across waves, in a fixed tree
+    double sh_ = h, sg = g;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const double oh = __shfl_down(sh_, off), og = __shfl_down(sg, off);
+      if (lane + off < kWave) {
+        sh_ = sh_ + sg * oh;
+        sg = sg * og;
+      }
+    }
+    if (lane == 0) {
+      sh.wh[wv] = sh_;
+      sh.wg[wv] = sg;
+    }
+    __syncthreads();
+    // the map of the waves after this one, applied to the tile's carry
+    double x = tile_carry;
+    for (int w = NW - 1; w > wv; --w) x = sh.wh[w] + sh.wg[w] * x;
+    // exclusive suffix in the wave: the next lane's inclusive map
+    double nh = __shfl_down(sh_, 1), ng = __shfl_down(sg, 1);
+    if (lane == kWave - 1) {
+      nh = 0.0;
+      ng = 1.0;
+    }
+    double acc = nh + ng * x;  // return at the slot after this chunk
+    // the carry into the next tile: the whole tile's map applied to tile_carry
+    double tc = tile_carry;
+    for (int w = NW - 1; w >= 0; --w) tc = sh.wh[w] + sh.wg[w] * tc;
+    tile_carry = tc;
+    for (int q = q1 - 1; q >= q0; --q) {
+      acc = sh.v[adv_lds(q)] + a.gamma * acc;
+      sh.v[adv_lds(q)] = acc;
+    }
+    __syncthreads();
+    for (int q = tid; q < n; q += kAdvThreads) {
+      const bool act = sh.act[q] != 0;
+      f(start + q, act, act ? sh.v[adv_lds(q)] : 0.0);
+    }
   }
 }
 
@@ -115,24 +186,36 @@ __global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) 
   if (i == 0 && tid == 0 && a.pass == 0) a.hdr->status = 0;
 
   if (a.estimator == GRPO_ADV_REINFORCE_PP) {
-    // last active slot of the sequence
-    const int64_t K = (a.T + kAdvThreads - 1) / kAdvThreads;
-    const int64_t t0 = tid * K < a.T ? tid * K : a.T;
-    const int64_t t1 = t0 + K < a.T ? t0 + K : a.T;
-    long long mx = -1;
-    for (int64_t t = t0; t < t1; ++t)
-      if (adv_active(a, base + t)) mx = t;
+    if (a.pass == 0) {
+      // last active slot of the sequence, kept for the later passes
+      long long mx = -1;
+      constexpr int U = 8;
+      for (int64_t t0 = tid; t0 < a.T; t0 += int64_t(U) * kAdvThreads) {
+        bool act[U];
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const long long o = __shfl_xor(mx, off);
-      mx = o > mx ? o : mx;
-    }
-    if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
-    __syncthreads();
-    if (tid == 0) {
-      long long m = -1;
-      for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
-      sh.last = m;
+        for (int k = 0; k < U; ++k) {
+          const int64_t t = t0 + int64_t(k) * kAdvThreads;
+          act[k] = t < a.T && adv_active(a, base + t);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+          if (act[k]) mx = t0 + int64_t(k) * kAdvThreads;
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const long long o = __shfl_xor(mx, off);
+        mx = o > mx ? o : mx;
+      }
+      if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
+      __syncthreads();
+      if (tid == 0) {
+        long long m = -1;
+        for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
+        sh.last = m;
+        a.last[i] = m;
+      }
+    } else if (tid == 0) {
+      sh.last = a.last[i];
     }
   } else if (tid == 0) {
     // group mean (the sample itself included), summed in index order

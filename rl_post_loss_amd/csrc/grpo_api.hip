@@ -722,6 +722,7 @@ grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const
   a.hdr = w.hdr();
   a.S = w.at<double>(w.l.P);
   a.L = w.at<int32_t>(w.l.L);
+  a.last = w.at<int64_t>(w.l.C);
   a.out = adv_out;
   a.status = status;
   return launch_token_advantages(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;

@@ -252,6 +252,7 @@ struct TokAdvArgs {
   WsHeader* hdr;
   double* S;                // [B] per-sequence sums of the pass
   int32_t* L;               // [B] active slots
+  int64_t* last;            // [B] last active slot (REINFORCE++), from pass 0
   float* out;               // [B, T]
   uint32_t* status;         // or null
 };
