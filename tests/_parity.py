@@ -315,6 +315,71 @@ def compare_logits_grad(grad_gpu, ref, cfg, mask, gdt, what="", policy=None, ids
     return stats
 
 
+def token_branches(ref, cfg, mask, base):
+    """The branch tuple of seq_branches for a token-level objective:
+    (flag-ambiguous, branch-ambiguous, candidate G list, relative G
+    tolerance, ill-conditioned), all [B, T]."""
+    flag, amb, cands = branch_ambiguity(ref, cfg, mask)
+    tol, ill = g_rel_tolerance(ref, cfg, base)
+    return flag, amb, cands, tol, ill
+
+
+def check_grad_row(g, x, a, key, branches, gdt, what=""):
+    """One 16-bit gradient row ``g`` (float64 [V]) against the oracle's row
+    G (onehot(a) - softmax(x)) for logits ``x`` and taken id ``a``, with G
+    the oracle's value at slot ``key`` = (i, t) of ``branches`` (token_branches
+    or seq_branches).  At a branch point a row that matches any candidate
+    G passes (at the plain 16-bit bar)."""
+    base, floor = GRAD16_BAR[gdt]
+    _, amb, cands, tol, _ = branches
+    i, t = key
+    xr = np.asarray(x, dtype=np.float64)[None]
+    lse = oracle.row_logsumexp(xr)
+    ids = np.array([int(a)])
+    worst = None
+    for k, C in enumerate(cands):
+        if k > 0 and not amb[i, t]:
+            break
+        r = oracle.softmax_grad_rows(xr, ids, lse, np.array([C[i, t]]))[0]
+        rel = tol[i, t] if k == 0 else base
+        with np.errstate(invalid="ignore"):
+            lim = np.where(np.abs(r) > 0, rel * np.abs(r), 0.0) + floor
+        err = np.abs(g - r)
+        if np.all(err <= lim):
+            return
+        if worst is None:
+            v = int(np.argmax(err / lim))
+            worst = (float(err[v] / lim[v]), v, float(g[v]), float(r[v]), float(C[i, t]))
+    raise AssertionError(f"{what} gradient row {key}: worst element {worst[1]} at {worst[0]:.3g}x "
+                         f"of its bound (gpu {worst[2]!r}, oracle {worst[3]!r}, G {worst[4]!r})")
+
+
+def sample_rows(B, T, mask, rng, n=24):
+    """Flat slot indices to check one by one: the first and last slot, one
+    active slot per sequence, the last slot of every ragged sequence (a
+    masked one) and ``n`` uniform draws."""
+    rows = {0, B * T - 1}
+    for i in range(B):
+        act = np.nonzero(mask[i])[0]
+        if act.size:
+            rows.add(i * T + int(act[rng.integers(0, act.size)]))
+        if act.size < T:
+            rows.add(i * T + T - 1)
+    rows |= set(int(v) for v in rng.integers(0, B * T, n))
+    return sorted(rows)
+
+
+def assert_grad_rows_sum_to_zero(grad2d, chunk=2048):
+    """Every gradient row is G (onehot - softmax), so it sums to G (1 - sum p)
+    = 0 up to the storage rounding of its elements."""
+    n = grad2d.shape[0]
+    for s in range(0, n, chunk):
+        blk = grad2d[s:s + chunk].double()
+        rs = blk.sum(dim=1)
+        ra = blk.abs().sum(dim=1)
+        assert bool(torch.all(rs.abs() <= 2.0 ** -7 * ra + 1e-30)), f"row sums, rows {s}..{s + chunk}"
+
+
 # ---------------------------------------------------------------------------
 # Sequence-level losses (GSPO, REAL).  Their policy part depends on s_i, the
 # mean log-ratio of a sequence, which the GPU forms from float32 log-probs:

@@ -20,7 +20,7 @@ import torch
 import oracle
 from _parity import (assert_bits_equal, cfg_from, compare_exact_parts, compare_logits_grad,
                      compare_scalars, compare_token_values, gpu_kwargs, host_inputs, to_np)
-from workloads import LogitsWorkload, make_logits_inputs
+from workloads import TOKEN_WORKLOADS, LogitsWorkload, make_logits_inputs, make_token_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -174,6 +174,69 @@ def test_gdpo_advantages(gpu_lib, kw):
     want = oracle.gdpo_advantages(comps.numpy(), groups=og)
     exact, n = _within_ulp(A.cpu().numpy(), want, "GDPO")
     print(f"  bit-exact {exact}/{n}", flush=True)
+
+
+@pytest.mark.parametrize("estimator", ["reinforce_pp", "reinforce_pp_baseline"])
+def test_token_advantages_fullsize(gpu_lib, estimator):
+    """The benchmarked configuration, compared whole: B = 1024 in groups of
+    16, T = 4096, ragged lengths, normalized (REINFORCE++: k1 shaping 0.01,
+    gamma 1).  Then the same call captured in a HIP graph and replayed,
+    with eager calls on other inputs in between: every replay bit-identical
+    to the eager result."""
+    rpl = gpu_lib
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    announce(f"token advantages full size {estimator}: generating")
+    a = make_token_inputs(wl, device=DEV, seed=0)
+    b = make_token_inputs(wl, device=DEV, seed=1)
+    if estimator == "reinforce_pp":
+        kw = dict(kl_coef=0.01, gamma=1.0, normalize=True)
+        extra = lambda c: dict(old_logps=c["old_logps"], ref_logps=c["ref_logp"])  # noqa: E731
+        groups = None
+    else:
+        kw = dict(samples_per_prompt=wl.group_size, normalize=True)
+        extra = lambda c: {}  # noqa: E731
+        groups = dict(samples_per_prompt=wl.group_size)
+    got = rpl.grpo_token_advantages(estimator, a["rewards"], a["mask"], **extra(a), **kw)
+    torch.cuda.synchronize()
+    announce(f"token advantages full size {estimator}: oracle")
+    h = {k: v.cpu().numpy() for k, v in a.items()}
+    want = oracle.token_advantages(estimator, h["rewards"], h["old_logps"], h["ref_logp"],
+                                   h["mask"], groups=groups, kl_coef=kw.get("kl_coef", 0.0),
+                                   gamma=kw.get("gamma", 1.0), normalize=True)
+    g = got.cpu().numpy()
+    assert np.all(g[~h["mask"]] == 0.0)
+    exact, n = _within_ulp(g, want, f"full size {estimator}")
+    print(f"  bit-exact {exact}/{n}", flush=True)
+
+    announce(f"token advantages full size {estimator}: graph replays")
+    static = {k: v.clone() for k, v in a.items()}
+    box = {}
+
+    def call():
+        box["A"] = rpl.grpo_token_advantages(estimator, static["rewards"], static["mask"],
+                                             **extra(static), **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    eager_b = rpl.grpo_token_advantages(estimator, b["rewards"], b["mask"], **extra(b), **kw)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src, ref = (a, got) if rep % 2 == 0 else (b, eager_b)
+        for k in static:
+            static[k].copy_(src[k])
+        graph.replay()
+        junk = rpl.grpo_token_advantages(estimator, b["rewards"], a["mask"], **extra(b), **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(box["A"].view(torch.int32), ref.view(torch.int32)), rep
+        del junk
 
 
 def test_group_advantage_clamp_bit_exact(gpu_lib):

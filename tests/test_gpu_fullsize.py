@@ -18,8 +18,8 @@ import pytest
 import torch
 
 import oracle
-from _parity import (LOGP_ABS_ERR, cfg_from, compare_exact_parts, compare_scalars, g_rel_tolerance,
-                     gpu_kwargs, to_np)
+from _parity import (LOGP_ABS_ERR, assert_grad_rows_sum_to_zero, cfg_from, compare_exact_parts,
+                     compare_scalars, gpu_kwargs, sample_rows, to_np)
 from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs, make_token_inputs
 
 pytestmark = pytest.mark.gpu
@@ -28,18 +28,6 @@ DEV = "cuda:0"
 
 def announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
-
-
-def _sample_rows(B, T, mask, rng, n=24):
-    rows = {0, B * T - 1}
-    for i in range(B):
-        act = np.nonzero(mask[i])[0]
-        if act.size:
-            rows.add(i * T + int(act[rng.integers(0, act.size)]))
-        if act.size < T:
-            rows.add(i * T + T - 1)     # a masked slot
-    rows |= set(int(v) for v in rng.integers(0, B * T, n))
-    return sorted(rows)
 
 
 @pytest.mark.parametrize("name,reduction", [
@@ -92,7 +80,7 @@ def test_fullsize_logits(gpu_lib, name, reduction):
 
     # sampled rows against the oracle
     rng = np.random.default_rng(1)
-    rows = _sample_rows(B, T, mask, rng)
+    rows = sample_rows(B, T, mask, rng)
     announce(f"full size {name} {red}: {len(rows)} sampled rows")
     pol = inp["policy"].view(B * T, V)
     ref = inp["ref"].view(B * T, V)
@@ -129,13 +117,7 @@ def test_fullsize_logits(gpu_lib, name, reduction):
 
     # every gradient row sums to ~0: G * (1 - sum p); bf16 rounding bounds the rest
     announce(f"full size {name} {red}: row sums")
-    rs = torch.zeros(B * T, dtype=torch.float64, device=DEV)
-    ra = torch.zeros(B * T, dtype=torch.float64, device=DEV)
-    for s in range(0, B * T, 2048):
-        blk = g2[s:s + 2048].double()
-        rs[s:s + 2048] = blk.sum(dim=1)
-        ra[s:s + 2048] = blk.abs().sum(dim=1)
-    assert bool(torch.all(rs.abs() <= 2.0 ** -7 * ra + 1e-30))
+    assert_grad_rows_sum_to_zero(g2)
 
     # bit-identical second run
     announce(f"full size {name} {red}: run 2")
