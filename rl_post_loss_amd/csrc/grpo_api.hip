@@ -175,12 +175,36 @@ grpo_status check_ws(void* ws, size_t ws_bytes, int64_t B, int64_t T, int32_t nu
   return GRPO_OK;
 }
 
+// The device view of a group specification; CSR offsets are copied into the
+// workspace (the one host array of the boundary).  No groups: a zero spec.
+grpo_status copy_offsets(const Ws& w, const grpo_groups* g, hipStream_t s, GroupSpec* out) {
+  *out = GroupSpec{};
+  if (!g) return GRPO_OK;
+  out->spp = g->samples_per_prompt;
+  out->num_groups = g->samples_per_prompt > 0 ? 0 : g->num_groups;
+  if (out->num_groups > 0) {
+    int64_t* dev = w.at<int64_t>(w.l.offsets);
+    if (hipMemcpyAsync(dev, g->group_boundaries, size_t(out->num_groups + 1) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return GRPO_ERR_HIP;
+    out->offsets = dev;
+  }
+  out->leave_one_out = g->leave_one_out;
+  out->scale_by_std = g->scale_by_std;
+  out->std_eps = g->std_eps;
+  out->clip = g->clip_advantages;
+  out->clip_lo = g->adv_clip_low;
+  out->clip_hi = g->adv_clip_high;
+  return GRPO_OK;
+}
+
 // Prep launch shared by every entry point: copies CSR offsets, then counts,
 // advantages and (optionally) weights.
 grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int64_t B, int64_t T,
                      const grpo_groups* g, const grpo_cfg* cfg, bool want_weights,
                      const grpo_outputs* out, float* adv_out, hipStream_t s,
-                     const float* old = nullptr, const float* gen = nullptr) {
+                     const float* old = nullptr, const float* gen = nullptr,
+                     bool weights_kernel = true) {
   PrepArgs a{};
   a.iw_mode = kIwNone;
   if (cfg && gen) {
@@ -220,6 +244,7 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
   a.alpha = cfg ? cfg->alpha : 0.0;
   a.norm_constant = cfg ? cfg->norm_constant : 0.0;
   a.want_weights = want_weights ? 1 : 0;
+  a.weights_kernel = weights_kernel ? 1 : 0;
   a.hdr = w.hdr();
   a.L = w.at<int32_t>(w.l.L);
   a.A = w.at<float>(w.l.A);
@@ -231,8 +256,11 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
 }
 
 grpo_status run_final(const Ws& w, int64_t B, double beta, const grpo_outputs* out,
-                      hipStream_t s, int64_t real_groups = 0) {
+                      hipStream_t s, int64_t real_groups = 0, bool count_tokens = false,
+                      bool fault_words = false) {
   FinalArgs f{};
+  f.L = count_tokens ? w.at<int32_t>(w.l.L) : nullptr;
+  f.fault = fault_words ? w.at<uint32_t>(w.l.fault) : nullptr;
   f.B = B;
   f.beta = beta;
   f.gloss = real_groups > 0 ? w.at<double>(w.l.gloss) : nullptr;
@@ -417,9 +445,21 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   st = check_ws(ws, ws_bytes, B, T, ng, &w);
   if (st != GRPO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s, old_logp, gen_logp);
-  if (st != GRPO_OK) return st;
+  // token-level objectives: the token kernel forms the weights itself (no
+  // weights kernel), and where no weight needs N and no sequence statistic
+  // is needed beforehand, the counts and advantages too (no prep kernel);
+  // the sequence-level losses need everything before their sequence phase
   const bool seqlv = is_sequence_level(cfg);
+  const bool seq_stat = gen_logp != nullptr && cfg->tis_type == GRPO_TIS_SEQ_MASK;
+  const int weights_mode = seqlv ? 0 : ((cfg->reduction != GRPO_TOKEN_MEAN && !seq_stat) ? 2 : 1);
+  GroupSpec grp{};
+  if (weights_mode == 2) {
+    st = copy_offsets(w, groups, s, &grp);
+  } else {
+    st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s, old_logp, gen_logp,
+                  seqlv);
+  }
+  if (st != GRPO_OK) return st;
   if (seqlv) {
     st = run_sequence_phase(w, cfg, groups, logp, old_logp, gen_logp, mask, B, T, grad_scale,
                             false, out, s);
@@ -451,9 +491,22 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.seq_kl = out->seq_kl;
   a.out_loss = out->tok_loss;
   a.out_kl = out->tok_kl;
+  a.weights_mode = weights_mode;
+  a.L = w.at<int32_t>(w.l.L);
+  a.reduction = cfg->reduction;
+  a.alpha = cfg->alpha;
+  a.norm_constant = cfg->norm_constant;
+  a.w_out = w.at<double>(w.l.w);
+  a.seq_weight_out = out->seq_weight;
+  a.rewards = groups ? rewards : nullptr;
+  a.grp = grp;
+  a.adv_out = out->advantages;
+  a.seq_tokens_out = out->seq_tokens;
+  a.fault = w.at<uint32_t>(w.l.fault);
   if (launch_token(a, s) != hipSuccess) return GRPO_ERR_HIP;
   return run_final(w, B, cfg->beta, out, s,
-                   cfg->pg_loss == GRPO_PG_REAL ? group_count(groups, B) : 0);
+                   cfg->pg_loss == GRPO_PG_REAL ? group_count(groups, B) : 0, !seqlv,
+                   weights_mode == 2);
 }
 
 static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype,

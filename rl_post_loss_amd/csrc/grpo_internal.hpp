@@ -31,8 +31,8 @@ struct RowStash {
 };
 
 struct WsLayout {
-  size_t hdr, L, A, w, P, K, C, slogr, useq, lseq, cseq, iwseq, gloss, offsets, tok_loss, tok_kl,
-      tok_logp, flags, stash, total;
+  size_t hdr, L, A, w, P, K, C, slogr, useq, lseq, cseq, iwseq, gloss, fault, offsets, tok_loss,
+      tok_kl, tok_logp, flags, stash, total;
 };
 
 inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
@@ -52,6 +52,7 @@ inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
   l.cseq = o; o = align_up(o + size_t(B) * 4);    // GSPO sequence clipped flag
   l.iwseq = o; o = align_up(o + size_t(B) * 8);   // seq-mask keep flag or GSPO mean weight
   l.gloss = o; o = align_up(o + size_t(B) * 8);   // REAL group losses (<= B groups)
+  l.fault = o; o = align_up(o + size_t(B) * 4);   // per-sequence fault bits (token kernel)
   l.tok_loss = o; o = align_up(o + rows * 4);
   l.tok_kl = o; o = align_up(o + rows * 4);
   l.tok_logp = o; o = align_up(o + rows * 4);
@@ -86,6 +87,17 @@ struct Objective {
 // Importance-weight statistics per sequence, computed by the prep kernel.
 enum IwMode { kIwNone = 0, kIwSeqMask = 1, kIwMean = 2 };
 
+// Device view of a group specification (grpo_groups).
+struct GroupSpec {
+  int32_t spp;              // uniform group size, or 0 for CSR
+  int32_t num_groups;
+  const int64_t* offsets;   // device copy of the CSR offsets (num_groups + 1)
+  int32_t leave_one_out, scale_by_std;
+  double std_eps;
+  int32_t clip;             // clamp the advantages to [clip_lo, clip_hi]
+  double clip_lo, clip_hi;
+};
+
 // Group / advantage / weight preparation.
 struct PrepArgs {
   const uint8_t* mask;      // [B, T] or null (all active)
@@ -102,6 +114,7 @@ struct PrepArgs {
   double alpha;
   double norm_constant;     // GRPO_FIXED_CONSTANT
   int32_t want_weights;     // 0: advantages only
+  int32_t weights_kernel;   // with want_weights: also launch the weights kernel
   // per-sequence importance-weight statistic (IwMode) over the active tokens
   int32_t iw_mode;
   const float* old;
@@ -283,6 +296,8 @@ struct FinalArgs {
   const int64_t* C;
   const double* gloss;      // REAL: group losses; null otherwise
   int64_t num_groups;       // REAL: number of groups
+  const int32_t* L;         // non-null: form N (and its fault bit) from these counts
+  const uint32_t* fault;    // non-null: the call's fault bits are the OR of these
   float* scalars;
   int64_t* counts;
   uint32_t* status;
@@ -316,6 +331,21 @@ struct TokenArgs {
   float* seq_kl;
   float* out_loss;
   float* out_kl;
+  // token-level objectives: each block forms its own w_i (weights mode 1:
+  // from the prep kernel's counts; mode 2: from its own count of the mask,
+  // with its own group advantage); the scalar kernel then forms N
+  int32_t weights_mode;     // 0: w from the workspace
+  int32_t* L;
+  int32_t reduction;
+  double alpha, norm_constant;
+  double* w_out;
+  float* seq_weight_out;
+  // weights mode 2
+  const float* rewards;     // null with token advantages
+  GroupSpec grp;
+  float* adv_out;
+  int32_t* seq_tokens_out;
+  uint32_t* fault;
 };
 
 }  // namespace grpo

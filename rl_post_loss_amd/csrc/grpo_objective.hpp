@@ -31,6 +31,28 @@ __device__ __forceinline__ float clamp_sym(float x, float v) {
   return x != x ? x : fminf(fmaxf(x, -v), v);
 }
 
+// Per-sequence token weight w_i of the reduction (binary64, contraction
+// off): token mean 1/N ("GRPO Loss", Normalizer semantics), sequence mean
+// 1/(B L_i) (Relax REINFORCE++ page, PPO and KL reduction), length weighting
+// L_i^alpha / (B L_i) (grpo.cpp README, The length-normalization detail), or a
+// declared constant.  Shared by the weights kernel and the token kernel so
+// both give the same bits.
+__device__ inline double sequence_weight(int32_t reduction, double alpha, double norm_constant,
+                                  int64_t B, int64_t L, int64_t N) {
+#pragma clang fp contract(off)
+  if (reduction == GRPO_TOKEN_MEAN) return 1.0 / double(N > 0 ? N : 1);
+  if (reduction == GRPO_FIXED_CONSTANT) return 1.0 / norm_constant;
+  if (reduction == GRPO_SEQUENCE_MEAN) return 1.0 / (double(B) * double(L > 0 ? L : 1));
+  if (L == 0) return 0.0;
+  const double Lf = double(L);
+  double num;
+  if (alpha == 0.0) num = 1.0;
+  else if (alpha == 0.5) num = sqrt(Lf);
+  else if (alpha == 1.0) num = Lf;
+  else num = pow(Lf, alpha);
+  return num / (double(B) * Lf);
+}
+
 // Off-policy weight of one token: exp(old - gen), truncated for tis/icepop.
 __device__ __forceinline__ float token_is_weight(const Objective& o, float old, float gen) {
   float wi = expf(old - gen);

@@ -16,9 +16,11 @@
 // Two kernels, so that no block ever waits on another: grpo_prep_kernel (one
 // block per sequence: L_i and A_i) and grpo_weights_kernel (one block: N and
 // every w_i).  The kernel boundary between them makes the counts visible.
+// The log-prob token loss skips the second: its token kernel forms w_i itself.
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
+#include "grpo_groupadv.hpp"
 #include "grpo_internal.hpp"
 #include "grpo_objective.hpp"
 
@@ -26,30 +28,7 @@ namespace grpo {
 
 constexpr int kPrepThreads = 256;
 constexpr int kWeightThreads = 1024;
-constexpr int kRewardStage = 1024;  // rewards of one group staged in LDS per round
 
-// Number of nonzero bytes in a 32-bit word.  For each byte b, bit 7 of
-// ((b & 0x7f) + 0x7f) | b is set exactly when b != 0 (no carry crosses bytes).
-__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
-  uint32_t t = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
-  return __popc(t);
-}
-
-__device__ double sequence_weight(int32_t reduction, double alpha, double norm_constant,
-                                  int64_t B, int64_t L, int64_t N) {
-#pragma clang fp contract(off)
-  if (reduction == GRPO_TOKEN_MEAN) return 1.0 / double(N > 0 ? N : 1);
-  if (reduction == GRPO_FIXED_CONSTANT) return 1.0 / norm_constant;
-  if (reduction == GRPO_SEQUENCE_MEAN) return 1.0 / (double(B) * double(L > 0 ? L : 1));
-  if (L == 0) return 0.0;
-  const double Lf = double(L);
-  double num;
-  if (alpha == 0.0) num = 1.0;
-  else if (alpha == 0.5) num = sqrt(Lf);
-  else if (alpha == 1.0) num = Lf;
-  else num = pow(Lf, alpha);
-  return num / (double(B) * Lf);
-}
 
 // One block per sequence i: L_i (active slots) and A_i.  The group's rewards
 // are staged in LDS by all threads; one thread then forms the binary64 sums
@@ -115,69 +94,18 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
     return;
   }
 
-  // group [s, e) of sequence i
-  int64_t s, e;
-  if (a.spp > 0) {
-    s = (i / a.spp) * a.spp;
-    e = s + a.spp;
-  } else {
-    int lo = 0, hi = a.num_groups;  // offsets[lo] <= i < offsets[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) / 2;
-      if (a.offsets[mid] <= i) lo = mid; else hi = mid;
-    }
-    s = a.offsets[lo];
-    e = a.offsets[lo + 1];
-  }
-  const int64_t n = e - s;
-
-  // S = sum r (index order), then var = sum (r - mean)^2 / n; groups longer
-  // than the stage go through it in rounds, keeping the sequential order
-  double total = 0.0;
-  for (int64_t b = s; b < e; b += kRewardStage) {
-    const int64_t m = (e - b) < kRewardStage ? (e - b) : kRewardStage;
-    __syncthreads();
-    for (int64_t k = tid; k < m; k += kPrepThreads) sh_r[k] = a.rewards[b + k];
-    __syncthreads();
-    if (tid == 0)
-      for (int64_t k = 0; k < m; ++k) total = total + double(sh_r[k]);
-  }
-  double sq = 0.0;
-  if (n <= kRewardStage) {
-    // the stage still holds the whole group
-    if (tid == 0) {
-      const double mean = total / double(n);
-      for (int64_t k = 0; k < n; ++k) {
-        const double dev = double(sh_r[k]) - mean;
-        sq = sq + dev * dev;
-      }
-    }
-  } else {
-    const double mean_all = total / double(n);  // only thread 0's value is used
-    for (int64_t b = s; b < e; b += kRewardStage) {
-      const int64_t m = (e - b) < kRewardStage ? (e - b) : kRewardStage;
-      __syncthreads();
-      for (int64_t k = tid; k < m; k += kPrepThreads) sh_r[k] = a.rewards[b + k];
-      __syncthreads();
-      if (tid == 0)
-        for (int64_t k = 0; k < m; ++k) {
-          const double dev = double(sh_r[k]) - mean_all;
-          sq = sq + dev * dev;
-        }
-    }
-  }
+  GroupSpec g{};
+  g.spp = a.spp;
+  g.num_groups = a.num_groups;
+  g.offsets = a.offsets;
+  g.leave_one_out = a.leave_one_out;
+  g.scale_by_std = a.scale_by_std;
+  g.std_eps = a.std_eps;
+  g.clip = a.clip;
+  g.clip_lo = a.clip_lo;
+  g.clip_hi = a.clip_hi;
+  const float advf = group_advantage<kPrepThreads>(g, a.rewards, i, sh_r);
   if (tid == 0) {
-    const double mean = total / double(n);
-    const double sd = sqrt(sq / double(n));
-    const double denom = sd >= a.std_eps ? sd : a.std_eps;
-    const double ri = double(a.rewards[i]);
-    const double base = a.leave_one_out ? (total - ri) / double(n - 1) : mean;
-    const double diff = ri - base;
-    double adv = a.scale_by_std ? diff / denom : diff;
-    // optional clamp (dockyard_rl, Advantage estimation), before the one
-    // rounding; comparisons keep a NaN
-    if (a.clip) adv = adv < a.clip_lo ? a.clip_lo : (adv > a.clip_hi ? a.clip_hi : adv);
-    const float advf = float(adv);
     a.A[i] = advf;
     if (a.adv_out) a.adv_out[i] = advf;
     a.L[i] = int32_t(L);
@@ -205,7 +133,7 @@ __global__ __launch_bounds__(kWeightThreads) void grpo_weights_kernel(PrepArgs a
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(grpo_prep_kernel, dim3(unsigned(a.B)), dim3(kPrepThreads), 0, stream, a);
-  if (!a.want_weights) return hipGetLastError();
+  if (!a.want_weights || !a.weights_kernel) return hipGetLastError();
   hipLaunchKernelGGL(grpo_weights_kernel, dim3(1), dim3(kWeightThreads), 0, stream, a);
   return hipGetLastError();
 }

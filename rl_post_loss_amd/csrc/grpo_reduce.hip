@@ -6,12 +6,16 @@
 // Both stages run in a fixed tree in binary64 without atomics, so results
 // are bit-identical from run to run.  The grpo.cpp README (CUDA section)
 // measures per-token atomics against block reduction for the same loss; here
-// no atomic is used at all: the per-sequence stage is one kernel (a block per
-// sequence) and the scalar stage a second, single-block kernel, so no block
-// ever waits on, or fences for, another.
+// no atomic is used for values at all: the per-sequence stage is one kernel
+// (a block per sequence) and the scalar stage a second, single-block kernel,
+// so no block ever waits on, or fences for, another.  (A single kernel whose
+// last block forms the scalars needs a device-scope release fence per block;
+// on gfx950 that writes back the XCD's L2 and cost more than the launch it
+// saves.)
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
+#include "grpo_groupadv.hpp"
 #include "grpo_internal.hpp"
 #include "grpo_objective.hpp"
 
@@ -27,36 +31,77 @@ constexpr int kFinalThreads = 1024;
 
 __global__ __launch_bounds__(kFinalThreads) void grpo_final_kernel(FinalArgs a) {
 #pragma clang fp contract(off)
-  __shared__ double sh_f64[kFinalThreads / kWave];
-  __shared__ long long sh_i64[kFinalThreads / kWave];
-  const int tid = threadIdx.x;
-  double pl = 0.0, kl = 0.0;
-  long long ct = 0;
+  // every sum in the tree of block_sum_* (butterfly in each wave, then the
+  // wave partials in wave order), all of them through one LDS exchange
+  constexpr int NW = kFinalThreads / kWave;
+  __shared__ double sh_pl[NW], sh_kl[NW], sh_gl[NW];
+  __shared__ long long sh_ct[NW], sh_n[NW];
+  __shared__ uint32_t sh_f[NW];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  double pl = 0.0, kl = 0.0, gl = 0.0;
+  long long ct = 0, n = 0;
+  uint32_t f = 0;
+#pragma unroll 1
   for (int64_t j = tid; j < a.B; j += kFinalThreads) {
     pl = pl + a.w[j] * a.P[j];
     kl = kl + a.w[j] * a.K[j];
     ct += a.C[j];
+    if (a.L) n += a.L[j];
+    if (a.fault) f |= a.fault[j];
   }
-  pl = block_sum_f64<kFinalThreads>(pl, sh_f64);
-  kl = block_sum_f64<kFinalThreads>(kl, sh_f64);
-  ct = block_sum_i64<kFinalThreads>(ct, sh_i64);
   if (a.gloss) {
-    double gl = 0.0;
+#pragma unroll 1
     for (int64_t g = tid; g < a.num_groups; g += kFinalThreads) gl = gl + a.gloss[g];
-    gl = block_sum_f64<kFinalThreads>(gl, sh_f64);
-    pl = gl / double(a.num_groups);
   }
-  if (tid == 0) {
-    const double loss = pl + double(a.beta) * kl;
-    a.scalars[0] = float(loss);
-    a.scalars[1] = float(pl);
-    a.scalars[2] = float(kl);
-    if (a.counts) {
-      a.counts[0] = a.hdr->num_tokens;
-      a.counts[1] = ct;
-    }
-    if (a.status) *a.status = a.hdr->status;
+  pl = wave_sum_f64<kWave>(pl);
+  kl = wave_sum_f64<kWave>(kl);
+  gl = wave_sum_f64<kWave>(gl);
+  ct = wave_sum_i64<kWave>(ct);
+  n = wave_sum_i64<kWave>(n);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) f |= uint32_t(__shfl_xor(int(f), off));
+  if (lane == 0) {
+    sh_pl[wv] = pl;
+    sh_kl[wv] = kl;
+    sh_gl[wv] = gl;
+    sh_ct[wv] = ct;
+    sh_n[wv] = n;
+    sh_f[wv] = f;
   }
+  __syncthreads();
+  if (tid != 0) return;
+  double tpl = 0.0, tkl = 0.0, tgl = 0.0;
+  long long tct = 0, tn = 0;
+  uint32_t tf = 0;
+#pragma unroll 4
+  for (int k = 0; k < NW; ++k) {
+    tpl += sh_pl[k];
+    tkl += sh_kl[k];
+    tgl += sh_gl[k];
+    tct += sh_ct[k];
+    tn += sh_n[k];
+    tf |= sh_f[k];
+  }
+  // REAL: the policy loss is the sum of the group losses over the number of
+  // groups (ms-swift REAL blog, source walkthrough)
+  if (a.gloss) tpl = tgl / double(a.num_groups);
+  // with the token kernel's own weights, N and its fault bit are formed
+  // here; without a prep kernel the call's faults are the per-sequence words
+  uint32_t st = a.fault ? (tf & GRPO_FAULT_NONFINITE) : a.hdr->status;
+  if (a.L) {
+    a.hdr->num_tokens = tn;
+    if (tn == 0) st |= GRPO_FAULT_NO_TOKENS;
+    a.hdr->status = st;
+  }
+  const double loss = tpl + double(a.beta) * tkl;
+  a.scalars[0] = float(loss);
+  a.scalars[1] = float(tpl);
+  a.scalars[2] = float(tkl);
+  if (a.counts) {
+    a.counts[0] = a.L ? tn : a.hdr->num_tokens;
+    a.counts[1] = tct;
+  }
+  if (a.status) *a.status = st;
 }
 
 hipError_t launch_final(const FinalArgs& a, hipStream_t stream) {
@@ -110,20 +155,125 @@ __device__ __forceinline__ void seq_token(const Objective& o, TokObj& r, bool gs
 // One block per sequence: tokens -> dlogp and the per-sequence totals.  The
 // grpo.cpp README's token-loss kernels (CUDA section) compute the same loss
 // from per-token log-probs.  kGeneral selects the objective code path (see
-// token_objective).
-template <bool kGeneral>
+// token_objective).  kWeights: 0 takes w_i from the workspace; 1 forms it
+// from the prep kernel's counts; 2 also counts the sequence's own mask and
+// forms its group advantage (no prep kernel: reductions that do not need N).
+template <bool kGeneral, int kWeights>
 __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma clang fp contract(off)
   __shared__ double sh_f64[kRedThreads / kWave];
   __shared__ long long sh_i64[kRedThreads / kWave];
+  __shared__ float sh_r[kWeights == 2 ? kRewardStage : 1];
+  __shared__ float sh_adv;
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
-  const float adv = a.A[i];
-  const float wg = float(a.w[i]) * (a.grad_scale ? *a.grad_scale : 1.0f);
+  const bool vec = (a.T & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.logp) |
+                                       reinterpret_cast<uintptr_t>(a.old) |
+                                       reinterpret_cast<uintptr_t>(a.ref) |
+                                       reinterpret_cast<uintptr_t>(a.gen) |
+                                       reinterpret_cast<uintptr_t>(a.adv_tok) |
+                                       reinterpret_cast<uintptr_t>(a.dlogp) |
+                                       reinterpret_cast<uintptr_t>(a.out_loss) |
+                                       reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
   const bool has_ref = a.ref != nullptr;
   const bool has_gen = a.gen != nullptr;
   const bool has_atok = a.adv_tok != nullptr;
+  // vector path: each thread takes QU quads of 4 tokens per round: their mask
+  // words, then the log-prob loads of the active ones, then the arithmetic.
+  // The first round's loads are issued before the prologue below (counts,
+  // weights, advantage) waits on anything but the mask words.
+  constexpr int QU = 4;
+  const int64_t n4 = a.T / 4;
+  uint32_t m4[QU];
+  f32x4 lp[QU], od[QU], rf[QU], gn[QU], av[QU];
+  auto load_masks = [&](int64_t q0) {
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t q = q0 + int64_t(u) * kRedThreads;
+      m4[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
+                               : 0x01010101u)
+                     : 0u;
+    }
+  };
+  auto load_data = [&](int64_t q0) {
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
+      lp[u] = od[u] = rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m4[u] != 0) {
+        lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
+        od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
+        if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
+        if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
+        if (has_atok) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.adv_tok + t0));
+      }
+    }
+  };
+  // weights mode 2: the group's rewards are requested with the mask words
+  // (one per thread when the group fits the block); the load is issued
+  // unconditionally, from a valid address, so that nothing waits on it early
+  int64_t g_s = 0, g_n = 0;
+  float r_pre = 0.0f;
+  if constexpr (kWeights == 2) {
+    if (a.rewards) {
+      int64_t g_e;
+      group_bounds(a.grp, i, &g_s, &g_e);
+      g_n = g_e - g_s;
+    }
+    const float* rsrc = a.rewards ? a.rewards : a.logp;
+    r_pre = rsrc[g_s + (tid < g_n ? tid : 0)];
+  }
+  const bool staged = kWeights == 2 && a.rewards != nullptr && g_n <= kRedThreads;
+  if (vec) load_masks(tid);
+  // stage the rewards before any data load is issued, so that waiting for
+  // them never waits for those loads
+  if (staged && tid < g_n) sh_r[tid] = r_pre;
+  if (vec) load_data(tid);
+  float adv;
+  long long Li = 0;
+  double wi;
+  if constexpr (kWeights == 2) {
+    // L_i from this block's own mask words, and A_i: the count's wave
+    // partials and the staged rewards share one barrier
+    long long cnt = 0;
+    if (vec) {
+#pragma unroll
+      for (int u = 0; u < QU; ++u) cnt += nonzero_bytes(m4[u]);
+      for (int64_t q = tid + QU * kRedThreads; q < n4; q += kRedThreads)
+        cnt += a.mask ? nonzero_bytes(*reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)) : 4;
+    } else {
+      for (int64_t t = tid; t < a.T; t += kRedThreads) cnt += (a.mask == nullptr || a.mask[base + t] != 0);
+    }
+    cnt = wave_sum_i64<kWave>(cnt);
+    if (tid % kWave == 0) sh_i64[tid / kWave] = cnt;
+    __syncthreads();
+    for (int w = 0; w < kRedThreads / kWave; ++w) Li += sh_i64[w];
+    if (staged) {
+      if (tid == 0) sh_adv = group_advantage_staged(a.grp, sh_r, g_n, i - g_s);
+    } else if (a.rewards) {
+      const float v = group_advantage<kRedThreads>(a.grp, a.rewards, i, sh_r);
+      if (tid == 0) sh_adv = v;
+    }
+    __syncthreads();
+    adv = a.rewards ? sh_adv : 0.0f;
+    wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, Li, 0);
+  } else if constexpr (kWeights == 1) {
+    adv = a.A[i];
+    // token mean needs N = sum_j L_j (the prep kernel's counts, fixed tree)
+    long long N = 0;
+    if (a.reduction == GRPO_TOKEN_MEAN) {
+      long long n = 0;
+      for (int64_t j = tid; j < a.B; j += kRedThreads) n += a.L[j];
+      N = block_sum_i64<kRedThreads>(n, sh_i64);
+    }
+    wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[i], N);
+  } else {
+    adv = a.A[i];
+    wi = a.w[i];
+  }
+  const float wg = float(wi) * (a.grad_scale ? *a.grad_scale : 1.0f);
   const float keep = a.iwseq ? float(a.iwseq[i]) : 1.0f;
   // sequence-level losses: the sequence kernels' loss, clip flag and
   // gradient coefficient (grad_scale included) of this sequence
@@ -135,42 +285,11 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   double p = 0.0, k = 0.0;
   long long c = 0;
   bool nonfinite = false;
-  const bool vec = (a.T & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.logp) |
-                                       reinterpret_cast<uintptr_t>(a.old) |
-                                       reinterpret_cast<uintptr_t>(a.ref) |
-                                       reinterpret_cast<uintptr_t>(a.gen) |
-                                       reinterpret_cast<uintptr_t>(a.adv_tok) |
-                                       reinterpret_cast<uintptr_t>(a.dlogp) |
-                                       reinterpret_cast<uintptr_t>(a.out_loss) |
-                                       reinterpret_cast<uintptr_t>(a.out_kl)) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
   if (vec) {
-    // each thread takes QU quads of 4 tokens per round: their mask words
-    // first, then the log-prob loads of the active ones, then the arithmetic,
-    // so a round costs two memory round trips
-    constexpr int QU = 4;
-    const int64_t n4 = a.T / 4;
     for (int64_t q0 = tid; q0 < n4; q0 += QU * kRedThreads) {
-      uint32_t m4[QU];
-      f32x4 lp[QU], od[QU], rf[QU], gn[QU], av[QU];
-#pragma unroll
-      for (int u = 0; u < QU; ++u) {
-        const int64_t q = q0 + int64_t(u) * kRedThreads;
-        m4[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
-                                 : 0x01010101u)
-                       : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < QU; ++u) {
-        const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
-        lp[u] = od[u] = rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (m4[u] != 0) {
-          lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
-          od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
-          if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
-          if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
-          if (has_atok) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.adv_tok + t0));
-        }
+      if (q0 != tid) {
+        load_masks(q0);
+        load_data(q0);
       }
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
@@ -230,24 +349,49 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
       if (a.out_kl) a.out_kl[s] = tk;
     }
   }
-  if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
+  if constexpr (kWeights != 2) {
+    if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
+  }
   p = block_sum_f64<kRedThreads>(p, sh_f64);
   k = block_sum_f64<kRedThreads>(k, sh_f64);
   c = block_sum_i64<kRedThreads>(c, sh_i64);
+  bool bad = false;
+  if constexpr (kWeights == 2) bad = __syncthreads_or(nonfinite ? 1 : 0) != 0;
   if (tid == 0) {
     a.P[i] = p;
     a.K[i] = k;
     a.C[i] = c;
     if (a.seq_policy) a.seq_policy[i] = float(p);
     if (a.seq_kl) a.seq_kl[i] = float(k);
+    if constexpr (kWeights != 0) {
+      a.w_out[i] = wi;
+      if (a.seq_weight_out) a.seq_weight_out[i] = float(wi);
+    }
+    if constexpr (kWeights == 2) {
+      // what the prep kernel would have written, and this sequence's faults
+      a.L[i] = int32_t(Li);
+      if (a.seq_tokens_out) a.seq_tokens_out[i] = int32_t(Li);
+      if (a.rewards && a.adv_out) a.adv_out[i] = adv;
+      a.fault[i] = bad ? GRPO_FAULT_NONFINITE : 0u;
+    }
   }
 }
 
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream) {
-  if (a.obj.general)
-    hipLaunchKernelGGL(grpo_token_kernel<true>, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(grpo_token_kernel<false>, dim3(unsigned(a.B)), dim3(kRedThreads), 0, stream, a);
+  const dim3 grid(unsigned(a.B)), block(kRedThreads);
+#define GRPO_TOKEN_LAUNCH(W)                                                              \
+  if (a.obj.general)                                                                      \
+    hipLaunchKernelGGL((grpo_token_kernel<true, W>), grid, block, 0, stream, a);          \
+  else                                                                                    \
+    hipLaunchKernelGGL((grpo_token_kernel<false, W>), grid, block, 0, stream, a);
+  if (a.weights_mode == 2) {
+    GRPO_TOKEN_LAUNCH(2)
+  } else if (a.weights_mode == 1) {
+    GRPO_TOKEN_LAUNCH(1)
+  } else {
+    GRPO_TOKEN_LAUNCH(0)
+  }
+#undef GRPO_TOKEN_LAUNCH
   return hipGetLastError();
 }
 
