@@ -22,6 +22,13 @@
 namespace grpo {
 
 constexpr int kRedThreads = 256;
+// Token kernel: threads per sequence block, and quads of 4 tokens each thread
+// takes per round (kTokThreads * kTokQuads * 4 tokens per round).
+#ifndef GRPO_TOK_THREADS
+#define GRPO_TOK_THREADS 256
+#endif
+constexpr int kTokThreads = GRPO_TOK_THREADS;
+constexpr int kTokQuads = 1024 / kTokThreads > 0 ? 1024 / kTokThreads : 1;
 
 // Scalar stage (one block): policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i in
 // binary64, written as float32, plus the token and clip counts and the fault
@@ -159,10 +166,10 @@ __device__ __forceinline__ void seq_token(const Objective& o, TokObj& r, bool gs
 // from the prep kernel's counts; 2 also counts the sequence's own mask and
 // forms its group advantage (no prep kernel: reductions that do not need N).
 template <bool kGeneral, int kWeights>
-__global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
+__global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
 #pragma clang fp contract(off)
-  __shared__ double sh_f64[kRedThreads / kWave];
-  __shared__ long long sh_i64[kRedThreads / kWave];
+  __shared__ double sh_f64[kTokThreads / kWave];
+  __shared__ long long sh_i64[kTokThreads / kWave];
   __shared__ float sh_r[kWeights == 2 ? kRewardStage : 1];
   __shared__ float sh_adv;
   const int64_t i = blockIdx.x;
@@ -184,31 +191,35 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   // words, then the log-prob loads of the active ones, then the arithmetic.
   // The first round's loads are issued before the prologue below (counts,
   // weights, advantage) waits on anything but the mask words.
-  constexpr int QU = 4;
+  constexpr int QU = kTokQuads;
   const int64_t n4 = a.T / 4;
   uint32_t m4[QU];
   f32x4 lp[QU], od[QU], rf[QU], gn[QU], av[QU];
   auto load_masks = [&](int64_t q0) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
-      const int64_t q = q0 + int64_t(u) * kRedThreads;
+      const int64_t q = q0 + int64_t(u) * kTokThreads;
       m4[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
                                : 0x01010101u)
                      : 0u;
     }
   };
+  // Branch-free: a quad with no active token (or past the row's end) reads the
+  // row's first quad instead, an in-bounds line that every thread of the row
+  // touches anyway, and its values are never used.  Without per-quad branches
+  // the compiler can wait for each quad's own loads alone rather than for
+  // every outstanding load and store.
   auto load_data = [&](int64_t q0) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
-      const int64_t t0 = base + 4 * (q0 + int64_t(u) * kRedThreads);
-      lp[u] = od[u] = rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (m4[u] != 0) {
-        lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
-        od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
-        if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
-        if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
-        if (has_atok) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.adv_tok + t0));
-      }
+      const int64_t q = q0 + int64_t(u) * kTokThreads;
+      const int64_t t0 = base + (m4[u] != 0 ? 4 * q : 0);
+      lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
+      od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
+      rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (has_ref) rf[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ref + t0));
+      if (has_gen) gn[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.gen + t0));
+      if (has_atok) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.adv_tok + t0));
     }
   };
   // weights mode 2: the group's rewards are requested with the mask words
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     const float* rsrc = a.rewards ? a.rewards : a.logp;
     r_pre = rsrc[g_s + (tid < g_n ? tid : 0)];
   }
-  const bool staged = kWeights == 2 && a.rewards != nullptr && g_n <= kRedThreads;
+  const bool staged = kWeights == 2 && a.rewards != nullptr && g_n <= kTokThreads;
   if (vec) load_masks(tid);
   // stage the rewards before any data load is issued, so that waiting for
   // them never waits for those loads
@@ -241,19 +252,19 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     if (vec) {
 #pragma unroll
       for (int u = 0; u < QU; ++u) cnt += nonzero_bytes(m4[u]);
-      for (int64_t q = tid + QU * kRedThreads; q < n4; q += kRedThreads)
+      for (int64_t q = tid + QU * kTokThreads; q < n4; q += kTokThreads)
         cnt += a.mask ? nonzero_bytes(*reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)) : 4;
     } else {
-      for (int64_t t = tid; t < a.T; t += kRedThreads) cnt += (a.mask == nullptr || a.mask[base + t] != 0);
+      for (int64_t t = tid; t < a.T; t += kTokThreads) cnt += (a.mask == nullptr || a.mask[base + t] != 0);
     }
     cnt = wave_sum_i64<kWave>(cnt);
     if (tid % kWave == 0) sh_i64[tid / kWave] = cnt;
     __syncthreads();
-    for (int w = 0; w < kRedThreads / kWave; ++w) Li += sh_i64[w];
+    for (int w = 0; w < kTokThreads / kWave; ++w) Li += sh_i64[w];
     if (staged) {
       if (tid == 0) sh_adv = group_advantage_staged(a.grp, sh_r, g_n, i - g_s);
     } else if (a.rewards) {
-      const float v = group_advantage<kRedThreads>(a.grp, a.rewards, i, sh_r);
+      const float v = group_advantage<kTokThreads>(a.grp, a.rewards, i, sh_r);
       if (tid == 0) sh_adv = v;
     }
     __syncthreads();
@@ -265,8 +276,8 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
     long long N = 0;
     if (a.reduction == GRPO_TOKEN_MEAN) {
       long long n = 0;
-      for (int64_t j = tid; j < a.B; j += kRedThreads) n += a.L[j];
-      N = block_sum_i64<kRedThreads>(n, sh_i64);
+      for (int64_t j = tid; j < a.B; j += kTokThreads) n += a.L[j];
+      N = block_sum_i64<kTokThreads>(n, sh_i64);
     }
     wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[i], N);
   } else {
@@ -286,14 +297,14 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   long long c = 0;
   bool nonfinite = false;
   if (vec) {
-    for (int64_t q0 = tid; q0 < n4; q0 += QU * kRedThreads) {
+    for (int64_t q0 = tid; q0 < n4; q0 += QU * kTokThreads) {
       if (q0 != tid) {
         load_masks(q0);
         load_data(q0);
       }
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
-        const int64_t q = q0 + int64_t(u) * kRedThreads;
+        const int64_t q = q0 + int64_t(u) * kTokThreads;
         if (q >= n4) continue;
         const int64_t t0 = base + 4 * q;
         const float lpv[4] = {lp[u].x, lp[u].y, lp[u].z, lp[u].w};
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
       }
     }
   } else {
-    for (int64_t t = tid; t < a.T; t += kRedThreads) {
+    for (int64_t t = tid; t < a.T; t += kTokThreads) {
       const int64_t s = base + t;
       float g = 0.f, tl = 0.f, tk = 0.f;
       if (a.mask == nullptr || a.mask[s] != 0) {
@@ -352,9 +363,9 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
   if constexpr (kWeights != 2) {
     if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
   }
-  p = block_sum_f64<kRedThreads>(p, sh_f64);
-  k = block_sum_f64<kRedThreads>(k, sh_f64);
-  c = block_sum_i64<kRedThreads>(c, sh_i64);
+  p = block_sum_f64<kTokThreads>(p, sh_f64);
+  k = block_sum_f64<kTokThreads>(k, sh_f64);
+  c = block_sum_i64<kTokThreads>(c, sh_i64);
   bool bad = false;
   if constexpr (kWeights == 2) bad = __syncthreads_or(nonfinite ? 1 : 0) != 0;
   if (tid == 0) {
@@ -378,7 +389,7 @@ __global__ __launch_bounds__(kRedThreads) void grpo_token_kernel(TokenArgs a) {
 }
 
 hipError_t launch_token(const TokenArgs& a, hipStream_t stream) {
-  const dim3 grid(unsigned(a.B)), block(kRedThreads);
+  const dim3 grid(unsigned(a.B)), block(kTokThreads);
 #define GRPO_TOKEN_LAUNCH(W)                                                              \
   if (a.obj.general)                                                                      \
     hipLaunchKernelGGL((grpo_token_kernel<true, W>), grid, block, 0, stream, a);          \
