@@ -18,11 +18,19 @@
 // an affine map x -> h + g x of the return after the chunk, a suffix scan of
 // those maps (wave shuffles, then the waves in order) gives every chunk its
 // carry and the carry into the next tile, every chunk replays its slots from
-// its carry, and the returns leave LDS with coalesced accesses again.  Sums over slots are fixed trees, sums over
-// sequences a single block, so results repeat bit for bit.
+// its carry, and the returns leave LDS with coalesced accesses again.
+//
+// With the global normalization the returns are kept in binary64 in the
+// workspace and each sequence leaves the moments (count, mean, sum of squared
+// deviations) of its active values: per thread from sums of deviations
+// from its first value, merged across the block, and one block merges the
+// sequences' moments with Chan et al.'s pairwise update in a
+// fixed tree, so results repeat bit for bit; a flat pass over the slots then
+// writes (A - mu) / sd.  Three launches in all.
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
+#include "grpo_groupadv.hpp"
 #include "grpo_internal.hpp"
 
 namespace grpo {
@@ -91,14 +99,13 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
   constexpr int NW = kAdvThreads / kWave;
   const int lane = tid % kWave, wv = tid / kWave;
   double tile_carry = 0.0;  // return at the slot after the current tile (same in every thread)
-  for (int64_t end = T; end > 0; end -= kAdvTile) {
+  // a tile's inputs in registers: every load of the tile is issued before any
+  // is used (loading the next tile during this one's scan measured slower)
+  uint8_t mk[kPer];
+  float ov[kPer], rv[kPer];
+  auto load_tile = [&](int64_t end) {
     const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
     const int n = int(end - start);
-    __syncthreads();  // the previous tile's values are consumed
-    // token rewards r_t = m_t (-kl_coef (old - ref) + [t = T_i] R): every load of
-    // the tile is issued before any is used; masked values are discarded by selection
-    uint8_t mk[kPer];
-    float ov[kPer], rv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = tid + k * kAdvThreads;
@@ -112,6 +119,15 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
         }
       }
     }
+  };
+  if (T > 0) load_tile(T);
+  for (int64_t end = T; end > 0; end -= kAdvTile) {
+    const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
+    const int n = int(end - start);
+    if (end != T) load_tile(end);
+    __syncthreads();  // the previous tile's values are consumed
+    // token rewards r_t = m_t (-kl_coef (old - ref) + [t = T_i] R); masked
+    // values are discarded by selection
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = tid + k * kAdvThreads;
@@ -176,140 +192,267 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
   }
 }
 
-// One block per sequence; a.pass selects the work (see TokAdvArgs).
+// Moments (count, mean, sum of squared deviations) of a set of values.
+struct Moments {
+  double n, m, M2;
+};
+
+// Chan et al.'s merge of two disjoint sets' moments (a first).
+__device__ __forceinline__ Moments moments_merge(Moments a, Moments b) {
+#pragma clang fp contract(off)
+  if (b.n == 0.0) return a;
+  if (a.n == 0.0) return b;
+  const double n = a.n + b.n;
+  const double d = b.m - a.m;
+  Moments r;
+  r.n = n;
+  r.m = a.m + d * (b.n / n);
+  r.M2 = a.M2 + b.M2 + d * d * (a.n * (b.n / n));
+  return r;
+}
+
+// Block-wide merge in a fixed tree: lane pairs down the wave, then the waves
+// in order; the result is valid in thread 0.
+template <int NT>
+__device__ Moments block_moments(Moments v, double* sh) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    Moments o;
+    o.n = __shfl_down(v.n, off);
+    o.m = __shfl_down(v.m, off);
+    o.M2 = __shfl_down(v.M2, off);
+    if (lane % (2 * off) == 0 && lane + off < kWave) v = moments_merge(v, o);
+  }
+  constexpr int NW = NT / kWave;
+  __syncthreads();
+  if (lane == 0) {
+    sh[3 * w] = v.n;
+    sh[3 * w + 1] = v.m;
+    sh[3 * w + 2] = v.M2;
+  }
+  __syncthreads();
+  Moments t{0.0, 0.0, 0.0};
+  if (threadIdx.x == 0)
+    for (int k = 0; k < NW; ++k) t = moments_merge(t, Moments{sh[3 * k], sh[3 * k + 1], sh[3 * k + 2]});
+  return t;
+}
+
+// One block per sequence: the raw advantages.  Without normalization they are
+// the output; with it, REINFORCE++'s returns go to the workspace and every
+// sequence leaves the moments of its active slots' values (the baseline's
+// value is the same at every active slot: L_i copies of R_i - group mean).
 __global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) {
 #pragma clang fp contract(off)
   __shared__ AdvShared sh;
+  __shared__ double sh_mom[3 * (kAdvThreads / kWave)];
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
-  if (i == 0 && tid == 0 && a.pass == 0) a.hdr->status = 0;
+  if (i == 0 && tid == 0) a.hdr->status = 0;
 
   if (a.estimator == GRPO_ADV_REINFORCE_PP) {
-    if (a.pass == 0) {
-      // last active slot of the sequence, kept for the later passes
-      long long mx = -1;
-      constexpr int U = 8;
-      for (int64_t t0 = tid; t0 < a.T; t0 += int64_t(U) * kAdvThreads) {
-        bool act[U];
+    // last active slot of the sequence (the terminal reward goes there)
+    long long mx = -1;
+    constexpr int U = 8;
+    for (int64_t t0 = tid; t0 < a.T; t0 += int64_t(U) * kAdvThreads) {
+      bool act[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-          const int64_t t = t0 + int64_t(k) * kAdvThreads;
-          act[k] = t < a.T && adv_active(a, base + t);
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k)
-          if (act[k]) mx = t0 + int64_t(k) * kAdvThreads;
+      for (int k = 0; k < U; ++k) {
+        const int64_t t = t0 + int64_t(k) * kAdvThreads;
+        act[k] = t < a.T && adv_active(a, base + t);
       }
 #pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const long long o = __shfl_xor(mx, off);
-        mx = o > mx ? o : mx;
-      }
-      if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
-      __syncthreads();
-      if (tid == 0) {
-        long long m = -1;
-        for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
-        sh.last = m;
-        a.last[i] = m;
-      }
-    } else if (tid == 0) {
-      sh.last = a.last[i];
+      for (int k = 0; k < U; ++k)
+        if (act[k]) mx = t0 + int64_t(k) * kAdvThreads;
     }
-  } else if (tid == 0) {
-    // group mean (the sample itself included), summed in index order
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const long long o = __shfl_xor(mx, off);
+      mx = o > mx ? o : mx;
+    }
+    if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      long long m = -1;
+      for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
+      sh.last = m;
+    }
+  } else {
+    // group mean (the sample itself included), summed in index order by one
+    // thread from rewards the whole block stages in LDS (rounds of kAdvTile)
+    GroupSpec g{};
+    g.spp = a.spp;
+    g.num_groups = a.num_groups;
+    g.offsets = a.offsets;
     int64_t s, e;
-    if (a.spp > 0) {
-      s = (i / a.spp) * a.spp;
-      e = s + a.spp;
-    } else {
-      int lo = 0, hi = a.num_groups;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) / 2;
-        if (a.offsets[mid] <= i) lo = mid; else hi = mid;
-      }
-      s = a.offsets[lo];
-      e = a.offsets[lo + 1];
-    }
+    group_bounds(g, i, &s, &e);
+    float* stage = reinterpret_cast<float*>(sh.v);
     double total = 0.0;
-    for (int64_t j = s; j < e; ++j) total = total + double(a.rewards[j]);
-    sh.cval = double(a.rewards[i]) - total / double(e - s);
+    for (int64_t b = s; b < e; b += kAdvTile) {
+      const int64_t m = (e - b) < kAdvTile ? (e - b) : kAdvTile;
+      __syncthreads();
+      for (int64_t k = tid; k < m; k += kAdvThreads) stage[k] = a.rewards[b + k];
+      __syncthreads();
+      if (tid == 0)
+        for (int64_t k = 0; k < m; ++k) total = total + double(stage[k]);
+    }
+    if (tid == 0) sh.cval = double(a.rewards[i]) - total / double(e - s);
   }
   __syncthreads();
 
-  if (a.pass == 0 && !a.normalize) {
+  if (!a.normalize) {
     for_each_raw(a, i, sh, [&](int64_t t, bool, double v) { a.out[base + t] = float(clamp_adv(a, v)); });
     if (i == 0 && tid == 0 && a.status) *a.status = 0u;
     return;
   }
-  if (a.pass == 2) {
-    const double mu = a.hdr->mu, sd = a.hdr->sd;
+  if (a.estimator == GRPO_ADV_REINFORCE_PP) {
+    // per thread, sums of the deviations from its first value (no division
+    // per value, and no cancellation unless that value is an outlier many
+    // spreads away); the threads' moments then merge in a fixed tree
+    double c = 0.0, s1 = 0.0, s2 = 0.0, n = 0.0;
     for_each_raw(a, i, sh, [&](int64_t t, bool act, double v) {
-      a.out[base + t] = act ? float(clamp_adv(a, (v - mu) / sd)) : 0.0f;
+      if (!act) return;
+      a.V[base + t] = v;
+      if (n == 0.0) c = v;
+      const double d = v - c;
+      s1 = s1 + d;
+      s2 = s2 + d * d;
+      n = n + 1.0;
     });
-    if (i == 0 && tid == 0 && a.status) *a.status = a.hdr->status;
-    return;
-  }
-  // pass 0: sum and count; pass 1: squared deviations from the mean
-  const double mu = a.pass == 1 ? a.hdr->mu : 0.0;
-  double sum = 0.0;
-  long long cnt = 0;
-  for_each_raw(a, i, sh, [&](int64_t, bool act, double v) {
-    if (!act) return;
-    if (a.pass == 0) {
-      sum = sum + v;
-      ++cnt;
-    } else {
-      const double dv = v - mu;
-      sum = sum + dv * dv;
+    Moments mo{0.0, 0.0, 0.0};
+    if (n > 0.0) {
+      const double dm = s1 / n;
+      const double m2 = s2 - s1 * dm;
+      mo = Moments{n, c + dm, m2 > 0.0 ? m2 : 0.0};
     }
-  });
-  sum = block_sum_f64<kAdvThreads>(sum, sh.red);
-  cnt = block_sum_i64<kAdvThreads>(cnt, sh.red_i);
-  if (tid == 0) {
-    a.S[i] = sum;
-    if (a.pass == 0) a.L[i] = int32_t(cnt);
+    mo = block_moments<kAdvThreads>(mo, sh_mom);
+    if (tid == 0) {
+      a.L[i] = int32_t(mo.n);
+      a.mean[i] = mo.m;
+      a.M2[i] = mo.M2;
+    }
+  } else {
+    long long cnt = 0;
+    if (a.mask == nullptr) {
+      cnt = tid == 0 ? a.T : 0;
+    } else if (a.T % 4 == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
+      const uint32_t* w4 = reinterpret_cast<const uint32_t*>(a.mask + base);
+      for (int64_t k = tid; k < a.T / 4; k += kAdvThreads) cnt += nonzero_bytes(w4[k]);
+    } else {
+      for (int64_t t = tid; t < a.T; t += kAdvThreads) cnt += a.mask[base + t] != 0 ? 1 : 0;
+    }
+    cnt = block_sum_i64<kAdvThreads>(cnt, sh.red_i);
+    if (tid == 0) {
+      a.L[i] = int32_t(cnt);
+      a.mean[i] = sh.cval;
+      a.M2[i] = 0.0;
+    }
   }
 }
 
-// One block: pass 0 -> N and the mean; pass 1 -> the floored std.
+// One block: the moments of every active slot of the batch, merged over the
+// sequences in a fixed tree; mu and the floored std for the output pass.
 __global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(TokAdvArgs a) {
 #pragma clang fp contract(off)
-  __shared__ double sh_f64[kMomentThreads / kWave];
-  __shared__ long long sh_i64[kMomentThreads / kWave];
+  __shared__ double sh_mom[3 * (kMomentThreads / kWave)];
   const int tid = threadIdx.x;
-  double s = 0.0;
-  long long n = 0;
+  Moments mo{0.0, 0.0, 0.0};
   for (int64_t k = tid; k < a.B; k += kMomentThreads) {
-    s = s + a.S[k];
-    n += a.L[k];
+    const int32_t n = a.L[k];
+    if (n > 0) {
+      // L_i copies of the baseline value enter as one set of n equal values
+      mo = moments_merge(mo, Moments{double(n), a.mean[k], a.M2[k]});
+    }
   }
-  s = block_sum_f64<kMomentThreads>(s, sh_f64);
-  n = block_sum_i64<kMomentThreads>(n, sh_i64);
+  mo = block_moments<kMomentThreads>(mo, sh_mom);
   if (tid != 0) return;
-  if (a.pass == 0) {
-    a.hdr->num_tokens = n;
-    a.hdr->mu = n > 0 ? s / double(n) : 0.0;
-    if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
+  const long long n = (long long)mo.n;
+  a.hdr->num_tokens = n;
+  a.hdr->mu = n > 0 ? mo.m : 0.0;
+  const double var = n > 0 ? mo.M2 / mo.n : 0.0;
+  a.hdr->sd = sqrt(var > 1e-8 ? var : 1e-8);
+  if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
+}
+
+constexpr int kNormThreads = 256;
+constexpr int kNormQuads = 1;   // quads of 4 slots per thread (4 measured slower: fewer waves)
+
+// Output pass over the slots: (A - mu) / sd at active slots, 0 elsewhere;
+// kNormQuads quads of four slots per thread when the rows allow 16-byte
+// accesses, else one slot per thread.
+__global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvArgs a, int vec) {
+#pragma clang fp contract(off)
+  const double mu = a.hdr->mu, sd = a.hdr->sd;
+  const bool rpp = a.estimator == GRPO_ADV_REINFORCE_PP;
+  const int64_t rows = a.B * a.T;
+  if (vec) {
+    const int64_t nq = rows / 4;
+    const int64_t q0 = int64_t(blockIdx.x) * (kNormThreads * kNormQuads) + threadIdx.x;
+    uint32_t m4[kNormQuads];
+    f32x4 lo[kNormQuads], hi[kNormQuads];
+#pragma unroll
+    for (int u = 0; u < kNormQuads; ++u) {
+      const int64_t q = q0 + int64_t(u) * kNormThreads;
+      m4[u] = q < nq ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + 4 * q) : 0x01010101u) : 0u;
+    }
+    if (rpp) {
+      // a quad with no active slot reads the first slot's line instead (its
+      // values are not used), so that the loads need no branch
+#pragma unroll
+      for (int u = 0; u < kNormQuads; ++u) {
+        const int64_t src = m4[u] != 0 ? 4 * (q0 + int64_t(u) * kNormThreads) : 0;
+        lo[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.V + src));
+        hi[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.V + src + 2));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kNormQuads; ++u) {
+      const int64_t q = q0 + int64_t(u) * kNormThreads;
+      if (q >= nq) continue;
+      double v[4];
+      if (rpp) {
+        v[0] = __builtin_bit_cast(double, f2{lo[u].x, lo[u].y});
+        v[1] = __builtin_bit_cast(double, f2{lo[u].z, lo[u].w});
+        v[2] = __builtin_bit_cast(double, f2{hi[u].x, hi[u].y});
+        v[3] = __builtin_bit_cast(double, f2{hi[u].z, hi[u].w});
+      } else {
+        v[0] = v[1] = v[2] = v[3] = a.mean[(4 * q) / a.T];
+      }
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = ((m4[u] >> (8 * j)) & 0xffu) ? float(clamp_adv(a, (v[j] - mu) / sd)) : 0.0f;
+      __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(a.out + 4 * q));
+    }
+    if (q0 == 0 && a.status) *a.status = a.hdr->status;
   } else {
-    const double var = n > 0 ? s / double(n) : 0.0;
-    a.hdr->sd = sqrt(var > 1e-8 ? var : 1e-8);
+    const int64_t gid = int64_t(blockIdx.x) * kNormThreads + threadIdx.x;
+    if (gid >= rows) return;
+    const bool act = adv_active(a, gid);
+    float o = 0.0f;
+    if (act) {
+      const double v = rpp ? a.V[gid] : a.mean[gid / a.T];
+      o = float(clamp_adv(a, (v - mu) / sd));
+    }
+    a.out[gid] = o;
+    if (gid == 0 && a.status) *a.status = a.hdr->status;
   }
 }
 
-hipError_t launch_token_advantages(const TokAdvArgs& base, hipStream_t s) {
-  TokAdvArgs a = base;
-  const dim3 grid(unsigned(a.B));
-  a.pass = 0;
-  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
+hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(grpo_tokadv_kernel, dim3(unsigned(a.B)), dim3(kAdvThreads), 0, s, a);
   if (!a.normalize) return hipGetLastError();
   hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
-  a.pass = 1;
-  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
-  hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
-  a.pass = 2;
-  hipLaunchKernelGGL(grpo_tokadv_kernel, grid, dim3(kAdvThreads), 0, s, a);
+  const int64_t rows = a.B * a.T;
+  const int vec = (a.T % 4 == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.V) & 15) == 0) ? 1 : 0;
+  const int64_t per_block = vec ? int64_t(kNormThreads) * kNormQuads : int64_t(kNormThreads);
+  const int64_t items = vec ? rows / 4 : rows;
+  const int64_t blocks = (items + per_block - 1) / per_block;
+  hipLaunchKernelGGL(grpo_tokadv_norm_kernel, dim3(unsigned(blocks)), dim3(kNormThreads), 0, s, a,
+                     vec);
   return hipGetLastError();
 }
 

@@ -773,9 +773,10 @@ grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const
   a.clip_lo = groups ? groups->adv_clip_low : 0.0;
   a.clip_hi = groups ? groups->adv_clip_high : 0.0;
   a.hdr = w.hdr();
-  a.S = w.at<double>(w.l.P);
   a.L = w.at<int32_t>(w.l.L);
-  a.last = w.at<int64_t>(w.l.C);
+  a.mean = w.at<double>(w.l.P);
+  a.M2 = w.at<double>(w.l.K);
+  a.V = w.at<double>(w.l.stash);  // the row stash (16 bytes per slot) holds one double per slot
   a.out = adv_out;
   a.status = status;
   return launch_token_advantages(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;

@@ -35,6 +35,9 @@ struct WsLayout {
       tok_kl, tok_logp, flags, stash, total;
 };
 
+// The token-advantage estimators keep one binary64 value per slot in the stash.
+static_assert(sizeof(RowStash) >= sizeof(double), "stash slot too small for a double");
+
 inline WsLayout ws_layout(int64_t B, int64_t T, int32_t num_groups) {
   WsLayout l{};
   size_t o = 0;
@@ -260,12 +263,13 @@ struct TokAdvArgs {
   int32_t normalize;
   int32_t clip;
   double clip_lo, clip_hi;
-  int32_t pass;             // 0: sums (or the output when not normalizing), 1: squared
-                            // deviations, 2: the normalized output
   WsHeader* hdr;
-  double* S;                // [B] per-sequence sums of the pass
-  int32_t* L;               // [B] active slots
-  int64_t* last;            // [B] last active slot (REINFORCE++), from pass 0
+  // per sequence: active slots, mean and sum of squared deviations of its
+  // raw advantages (the moments the global normalization merges)
+  int32_t* L;
+  double* mean;
+  double* M2;
+  double* V;                // [B, T] raw REINFORCE++ returns (normalizing only)
   float* out;               // [B, T]
   uint32_t* status;         // or null
 };
