@@ -213,3 +213,44 @@ def test_confident_token_gradient_relative_accuracy(gpu_lib):
     assert np.all(rel < 1e-4), rel.max()
     lp = to_np(res.tok_logp)
     assert np.all(np.abs(lp - ref.tok["logp"]) <= 1e-6 * np.abs(ref.tok["logp"]) + 1e-12)
+
+
+@pytest.mark.parametrize("reduction", ["token_mean", "sequence_mean", "length_alpha",
+                                       "fixed_constant"])
+def test_token_loss_fault_bits(gpu_lib, reduction):
+    """The log-prob entry point's fault bits, on both of its launch
+    structures (token mean: counts, token and scalar kernels; the others: the
+    token kernel forms its own counts and reports faults per sequence): no
+    active token gives NO_TOKENS with zero loss and gradient; a non-finite
+    per-token value at an active slot gives NONFINITE; the next clean call
+    on the same workspace reports no fault (status is per call)."""
+    from workloads import TOKEN_WORKLOADS, make_token_inputs
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    announce(f"token loss fault bits {reduction}")
+    inp = make_token_inputs(wl, device=DEV, seed=21, B=32, T=256)
+    kw = dict(eps_low=0.2, eps_high=0.2, beta=0.04, samples_per_prompt=16, reduction=reduction,
+              alpha=0.5 if reduction == "length_alpha" else None)
+    if reduction == "fixed_constant":
+        kw["norm_constant"] = 500.0
+
+    def call(mask, old):
+        res = gpu_lib.grpo_token_loss(inp["logp"], old, inp["ref_logp"], inp["rewards"], mask, **kw)
+        torch.cuda.synchronize()
+        return res
+
+    none = call(torch.zeros_like(inp["mask"]), inp["old_logps"])
+    assert int(none.status[0]) & gpu_lib.GRPO_FAULT_NO_TOKENS
+    assert float(none.loss) == 0.0 and float(none.kl) == 0.0 and int(none.counts[0]) == 0
+    assert torch.all(none.grad == 0)
+
+    # an old log-prob of -inf at an active slot makes the ratio infinite
+    old = inp["old_logps"].clone()
+    act = torch.nonzero(inp["mask"][3])
+    old[3, int(act[0])] = float("-inf")
+    bad = call(inp["mask"], old)
+    assert int(bad.status[0]) & gpu_lib.GRPO_FAULT_NONFINITE
+    assert not int(bad.status[0]) & gpu_lib.GRPO_FAULT_NO_TOKENS
+
+    clean = call(inp["mask"], inp["old_logps"])
+    assert int(clean.status[0]) == 0
+    assert int(clean.counts[0]) == int(inp["mask"].sum())
