@@ -43,6 +43,9 @@
 #define GRPO_PASS1_PIPELINE 1  // pass 1 in two register stages: the next stage's loads are
                                // in flight while the current one is summed
 #endif
+#ifndef GRPO_LOAD_PRIO
+#define GRPO_LOAD_PRIO 0       // wave priority while a stage's loads are issued (s_setprio)
+#endif
 
 namespace grpo {
 
@@ -135,6 +138,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
     if (c + (P - 1) * NT < nvec) {
       raw_t ax[P], ay[P], bx[P], by[P];
       auto load_stage = [&](raw_t* dx, raw_t* dy, int64_t c0) {
+        if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(GRPO_LOAD_PRIO);
 #pragma unroll
         for (int u = 0; u < P; ++u) dx[u] = IN::load(xrow, c0 + u * NT);
         if (has_ref) {
@@ -142,6 +146,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
           for (int u = 0; u < P; ++u)
             dy[u] = GRPO_Y_NONTEMPORAL ? IN::load_nt(yrow, c0 + u * NT) : IN::load(yrow, c0 + u * NT);
         }
+        if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(0);
       };
       auto sum_stage = [&](const raw_t* dx, const raw_t* dy, int64_t c0) {
 #pragma unroll
@@ -300,8 +305,10 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       auto more = [&](int64_t cc) { return GRPO_PASS2_REVERSE ? cc >= 0 : cc <= last; };
       for (; more(c + (U - 1) * step); c += U * step) {
         typename IN::raw_t rx[U];
+        if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(GRPO_LOAD_PRIO);
 #pragma unroll
         for (int u = 0; u < U; ++u) rx[u] = IN::load(xrow, c + u * step);
+        if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float f[N], g[N];
