@@ -176,6 +176,31 @@ def test_seq_split_backward_and_grad_scale(gpu_lib, kw):
     assert float(loss.detach()) == float(fused.loss)
 
 
+@pytest.mark.parametrize("kw", [SEQ_CASES[0], SEQ_CASES[4]], ids=_id)
+@pytest.mark.parametrize("V,dtype,T", [(1000, "f32", 2048), (2600, "bf16", 1400)])
+def test_seq_large_csr_split_bitwise(gpu_lib, kw, V, dtype, T):
+    """Sequence-level losses over a larger batch of unequal CSR groups
+    (4, 8, 2, 6, 4) with T = 2048 (64 threads and four rows per block) and
+    T = 1400 (256 threads per row): against the oracle, and bitwise against
+    the autograd split (the forward pass alone, then the backward pass)."""
+    rpl = gpu_lib
+    wl = _wl(V, dtype, T=T, sizes=(4, 8, 2, 6, 4), csr=True)
+    res, _, inp = check_seq_logits(rpl, wl, kw, seed=6)
+    red, _, _, obj = _split(kw)
+    gkw = gpu_kwargs(wl, red, **obj)
+    args = (inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"], inp["rewards"],
+            inp["mask"])
+    fused = rpl.grpo_loss_fwd_bwd(*args, **gkw)
+    pol = inp["policy"].clone().requires_grad_(True)
+    loss, _, _ = rpl.grpo_loss(pol, *args[1:], **gkw)
+    loss.backward(torch.tensor(1.0, device=DEV))
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(pol.grad.view(bits), fused.grad.view(bits))
+    assert torch.equal(fused.grad.view(bits), res.grad.view(bits))
+    assert float(loss.detach()) == float(fused.loss)
+
+
 @pytest.mark.parametrize("kw", [SEQ_CASES[0], SEQ_CASES[4], SEQ_CASES[6]], ids=_id)
 def test_seq_masked_slots_never_read(gpu_lib, kw):
     rpl = gpu_lib
