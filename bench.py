@@ -345,14 +345,18 @@ def run(args):
         res = step()
     torch.cuda.synchronize()
     ref_scalars = res.scalars.clone() if args.warmup else None
+    ref_grad_sum = int(grad.view(torch.int16 if grad.element_size() == 2 else torch.int32)
+                       .sum(dtype=torch.int64)) if args.warmup else None
 
     ev = HipEvents(args.steps)
     lib = rpl.load_library()
+    step_scalars = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         lib.grpo_set_timing_events(ev.pairs[k][0], ev.pairs[k][1])
         res = step()
+        step_scalars.append(res.scalars)  # each call returns its own scalar tensor
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lib.grpo_set_timing_events(None, None)
@@ -360,7 +364,13 @@ def run(args):
     kern_ms = [ev.elapsed_ms(k) for k in range(args.steps)]
     ev.close()
     kern_avg = sum(kern_ms) / len(kern_ms)
-    repro = ref_scalars is None or torch.equal(ref_scalars.view(torch.int32), res.scalars.view(torch.int32))
+    kern_median = sorted(kern_ms)[len(kern_ms) // 2]
+    # bit reproducibility: every timed step's scalars equal the warm-up's, and
+    # the gradient left by the last step has the warm-up gradient's checksum
+    repro = ref_scalars is None or (
+        all(torch.equal(ref_scalars.view(torch.int32), sc.view(torch.int32)) for sc in step_scalars)
+        and int(grad.view(torch.int16 if grad.element_size() == 2 else torch.int32)
+                .sum(dtype=torch.int64)) == ref_grad_sum)
 
     active = int(inp["mask"].sum())
     rows = B * T
@@ -388,6 +398,7 @@ def run(args):
                         + ("" if args.objective == "default" else f", objective {args.objective}"),
             "objective": {k: v for k, v in obj.items()},
             "B": B, "T": T, "V": V, "storage": wl.dtype, "active_slots": active,
+            "active_tokens_per_s": active / (ms_per_step * 1e-3),
             "hbm_fraction_of_step": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "bit_reproducible": bool(repro),
         },
@@ -400,6 +411,7 @@ def run(args):
             "traffic": traffic,
             "kernel": ROW_KERNEL,
             "kernel_ms": kern_avg,
+            "kernel_ms_median": kern_median,
             "algorithmic_bytes": alg_bytes,
         },
     }
