@@ -73,7 +73,7 @@ def _case_id(kw):
 
 
 @pytest.mark.parametrize("kw", TOKEN_CASES, ids=_case_id)
-@pytest.mark.parametrize("T", [203, 4096, 5000])
+@pytest.mark.parametrize("T", [203, 4096, 5000, 5008])
 def test_token_advantages(gpu_lib, kw, T):
     rpl = gpu_lib
     kw = dict(kw)
