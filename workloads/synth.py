@@ -101,14 +101,14 @@ class TokenWorkload:
         return self.group_size * self.num_groups
 
 
-def _csr_sizes(total, choices, seed):
+def _csr_sizes(total, choices, count, seed):
+    """`count` group sizes drawn i.i.d. from `choices`, all redrawn until they
+    sum to `total` (seeded)."""
     rng = np.random.default_rng([seed, 7])
     while True:
-        sizes = []
-        while sum(sizes) < total:
-            sizes.append(int(rng.choice(choices)))
+        sizes = tuple(int(v) for v in rng.choice(choices, size=count))
         if sum(sizes) == total:
-            return tuple(sizes)
+            return sizes
 
 
 WORKLOADS = {
@@ -125,7 +125,7 @@ WORKLOADS = {
         logit_std=3.0, ref_noise_std=math.sqrt(0.1), old_noise_std=math.sqrt(0.05),
         reward_p=0.5, len_range=None, ids="softmax", spike=8.0),
     "logits_csr_v128256": LogitsWorkload(
-        name="logits_csr_v128256", group_sizes=_csr_sizes(96, (4, 8, 16), 0), T=1024,
+        name="logits_csr_v128256", group_sizes=_csr_sizes(96, (4, 8, 16), 12, 0), T=1024,
         V=128256, dtype="bf16", logit_std=2.0, ref_noise_std=math.sqrt(0.1),
         old_noise_std=math.sqrt(0.05), reward_p=0.5, len_range=(1, 1024), csr=True,
         degenerate_groups=1, eps_low=0.2, eps_high=0.28, beta=0.01,
