@@ -62,10 +62,12 @@
  *
  * Workspace: grpo_workspace_bytes() bytes of device memory, 256-byte aligned.
  * Its contents need no initialisation: every call writes each workspace value
- * before reading it.  A workspace serves one call at a time: calls that share
- * a workspace must be ordered on one stream.  grpo_loss_fwd_bwd() with grad_out == NULL leaves per-row
- * state in the workspace that grpo_loss_bwd() consumes; it stays valid until
- * the next call that uses the same workspace.
+ * before it uses it (a 16-byte access may also fetch neighbouring slots the
+ * call leaves unused, whose values are discarded).  A workspace serves one
+ * call at a time: calls that share a workspace must be ordered on one stream.
+ * grpo_loss_fwd_bwd() with grad_out == NULL leaves per-row state in the
+ * workspace that grpo_loss_bwd() consumes; it stays valid until the next
+ * call that uses the same workspace.
  *
  * Errors: every entry point validates its arguments on the host and returns a
  * grpo_status without launching anything when they are wrong.  Faults that
@@ -305,8 +307,9 @@ GRPO_API const char *grpo_status_str(int status);
  * entry point below for these sizes. */
 GRPO_API size_t grpo_workspace_bytes(int64_t B, int64_t T, int32_t num_groups);
 
-/* Zero-fills a workspace.  Optional (calls never read uninitialised
- * workspace bytes); useful to make a fresh workspace's contents defined. */
+/* Zero-fills a workspace.  Optional (no result depends on a workspace value
+ * the call did not write); useful to make a fresh workspace's contents
+ * defined. */
 GRPO_API grpo_status grpo_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Group-relative advantages alone ([GRPO-LOSS] Accuracy; [DOCKYARD]
