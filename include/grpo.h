@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 5
+#define GRPO_ABI_VERSION 6
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -414,6 +414,18 @@ GRPO_API grpo_status grpo_loss_bwd(const void *policy_logits, int32_t logits_dty
                           int64_t B, int64_t T, int64_t V, void *grad_out, int32_t grad_dtype,
                           int64_t grad_row_stride, const float *grad_scale, void *ws,
                           size_t ws_bytes, void *stream);
+
+/* Multiplies rows x V gradient elements (row stride row_stride >= V
+ * elements, storage grad_dtype) in place by the device float *scale, and
+ * returns without touching them when *scale == 1.  For an autograd wrapper
+ * whose forward call already wrote d loss / d policy_logits with an upstream
+ * gradient of 1 ([GRPO-LOSS] Entry Point: the gradient lands in the logits
+ * buffer): its backward scales by the true upstream gradient.  One rounding
+ * per element (float32 product, then round to nearest even to the storage).
+ * Errors: NULL pointers, unknown dtype, non-positive or overflowing sizes,
+ * row_stride < V. */
+GRPO_API grpo_status grpo_scale_grad(void *grad, int32_t grad_dtype, int64_t rows, int64_t V,
+                                     int64_t row_stride, const float *scale, void *stream);
 
 /* Optional timing hook for profiling tools: when both are non-NULL, the
  * logits entry points record `start` right before and `stop` right after

@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 5
+GRPO_ABI_VERSION = 6
 
 GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
@@ -72,6 +72,7 @@ SIGNATURES = {
                                     C.POINTER(GrpoOutputs), vp, sz, vp]),
     "grpo_loss_bwd": (C.c_int, [vp, i32, i64, vp, i32, vp, i64, i64, i64, vp, i32, i64, vp, vp,
                                 sz, vp]),
+    "grpo_scale_grad": (C.c_int, [vp, i32, i64, i64, i64, vp, vp]),
     "grpo_set_timing_events": (None, [vp, vp]),
 }
 

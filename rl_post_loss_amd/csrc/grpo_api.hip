@@ -20,6 +20,7 @@ hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s);
 hipError_t launch_seq(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_real(const RealArgs& a, hipStream_t stream);
 hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s);
+hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_gdpo(const GdpoArgs& a, hipStream_t s);
 bool resident_fits(int64_t V, int esize);
 }  // namespace grpo
@@ -819,6 +820,23 @@ grpo_status grpo_gdpo_advantages(const float* rewards, int32_t num_components, i
   a.total = w.at<double>(w.l.P);
   a.out = adv_out;
   return launch_gdpo(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+}
+
+grpo_status grpo_scale_grad(void* grad, int32_t grad_dtype, int64_t rows, int64_t V,
+                            int64_t row_stride, const float* scale, void* stream) {
+  if (!grad || !scale) return GRPO_ERR_NULL;
+  if (fdtype_size(grad_dtype) == 0) return GRPO_ERR_DTYPE;
+  int64_t tmp;
+  if (rows <= 0 || V <= 0 || row_stride < V || !mul_ok(rows, row_stride, kMaxElems, &tmp))
+    return GRPO_ERR_SHAPE;
+  ScaleArgs a{};
+  a.g = grad;
+  a.dtype = grad_dtype;
+  a.rows = rows;
+  a.V = V;
+  a.ld = row_stride;
+  a.scale = scale;
+  return launch_scale(a, static_cast<hipStream_t>(stream)) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
 }  // extern "C"

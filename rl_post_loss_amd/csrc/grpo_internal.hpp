@@ -274,6 +274,14 @@ struct TokAdvArgs {
   uint32_t* status;         // or null
 };
 
+// In-place scaling of gradient rows by a device scalar.
+struct ScaleArgs {
+  void* g;
+  int32_t dtype;            // grpo_fdtype
+  int64_t rows, V, ld;      // ld: row stride, elements
+  const float* scale;       // device scalar; 1 skips the work
+};
+
 // GDPO multi-reward advantages (one block).
 struct GdpoArgs {
   const float* rewards;     // [C, B]

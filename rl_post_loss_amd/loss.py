@@ -509,15 +509,45 @@ def grpo_loss_bwd(policy_logits, action_ids, completion_mask, ws, *, grad_out=No
     return grad_out
 
 
+def grpo_scale_grad(grad, scale):
+    """Multiplies ``grad`` ([B, T, V] or [rows, V], float32/bfloat16/float16,
+    unit stride along V) in place by the device scalar ``scale`` (float32
+    [1]); nothing is touched when it is 1."""
+    lib = load_library()
+    _need(grad.dtype in _FDTYPE and grad.is_cuda and grad.dim() >= 2 and grad.stride(-1) == 1,
+          "grad must be a float32/bfloat16/float16 GPU tensor with unit stride along V")
+    _need(scale.dtype == torch.float32 and scale.numel() == 1 and scale.device == grad.device,
+          "scale must be a float32 scalar on the gradient's device")
+    V = grad.shape[-1]
+    rows = grad.numel() // V
+    ld = grad.stride(-2)
+    _need(all(grad.stride(k) == grad.stride(k + 1) * grad.shape[k + 1]
+              for k in range(grad.dim() - 2)), "grad rows must be evenly spaced")
+    check(lib.grpo_scale_grad(grad.data_ptr(), _FDTYPE[grad.dtype], rows, V, ld,
+                              scale.contiguous().data_ptr(), _stream_ptr(grad.device)), lib)
+    return grad
+
+
 class _GRPOLossFn(torch.autograd.Function):
-    """Autograd wrapper: the forward runs the vocabulary pass once and keeps the
-    per-row gradient weights in a dedicated workspace; the backward streams the
-    policy logits again and writes d loss / d logits scaled by the upstream
-    gradient."""
+    """Autograd wrapper.  By default the forward runs the vocabulary pass once
+    and keeps the per-row gradient weights in a dedicated workspace; the
+    backward streams the policy logits again and writes d loss / d logits
+    scaled by the upstream gradient (no [B, T, V] buffer is held in between).
+    With ``precompute_grad`` the forward runs the fused kernel and keeps its
+    gradient; the backward only scales it by the upstream gradient in place
+    (nothing to do for the usual upstream gradient of 1)."""
 
     @staticmethod
     def forward(ctx, policy_logits, ref_logits, action_ids, old_logps, rewards, mask, kw):
+        kw = dict(kw)
+        precompute = kw.pop("precompute_grad", False)
         B, T, V = policy_logits.shape
+        ctx.precompute = precompute
+        if precompute:
+            res = grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
+                                    mask, **kw)
+            ctx.grad = res.grad
+            return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
         ng = 0 if kw.get("group_boundaries") is None else len(kw["group_boundaries"]) - 1
         ws = workspace(B, T, ng, policy_logits.device, dedicated=True)
         res = grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards, mask,
@@ -529,8 +559,12 @@ class _GRPOLossFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, g_loss, g_pol, g_kl):
-        policy_logits, action_ids, mask = ctx.saved_tensors
         scale = g_loss.reshape(1).to(torch.float32).contiguous()
+        if ctx.precompute:
+            grad = grpo_scale_grad(ctx.grad, scale)
+            ctx.grad = None
+            return grad, None, None, None, None, None, None
+        policy_logits, action_ids, mask = ctx.saved_tensors
         grad = grpo_loss_bwd(policy_logits, action_ids, mask if ctx.has_mask else None, ctx.ws,
                              grad_scale=scale)
         ctx.ws = None
@@ -538,10 +572,18 @@ class _GRPOLossFn(torch.autograd.Function):
 
 
 def grpo_loss(policy_logits, ref_logits, action_ids, old_logps, rewards, completion_mask=None,
-              **kw):
+              precompute_grad=False, **kw):
     """(loss, policy_loss, kl) with autograd into ``policy_logits`` (the call
     signature of "GRPO Loss", Entry Point).  Gradients of policy_loss and kl
-    as separate outputs are not propagated: only ``loss`` is differentiable."""
+    as separate outputs are not propagated: only ``loss`` is differentiable.
+    ``precompute_grad``: compute d loss / d logits in the forward call with
+    the fused kernel (one read of the policy logits fewer than a separate
+    backward pass, at the cost of holding a [B, T, V] gradient until the
+    backward); the backward then multiplies it by the upstream gradient."""
+    if precompute_grad:
+        _need("grad_scale" not in kw and "grad_out" not in kw,
+              "precompute_grad takes its scale from the backward pass")
+    kw = dict(kw, precompute_grad=precompute_grad)
     return _GRPOLossFn.apply(policy_logits, ref_logits, action_ids, old_logps, rewards,
                              completion_mask, kw)
 

@@ -267,3 +267,17 @@ def test_token_loss_and_advantages_validation():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         _abi.load_library(str(tmp_path / "missing.so"))
+
+
+@cpu_only
+def test_scale_grad_argument_validation():
+    lib = rpl.load_library()
+    E = {v: k for k, v in _abi.STATUS_NAMES.items()}
+    scale = C.c_void_p(FAKE)
+    assert lib.grpo_scale_grad(None, 1, 4, 8, 8, scale, None) == E["GRPO_ERR_NULL"]
+    assert lib.grpo_scale_grad(FAKE, 1, 4, 8, 8, None, None) == E["GRPO_ERR_NULL"]
+    assert lib.grpo_scale_grad(FAKE, 5, 4, 8, 8, scale, None) == E["GRPO_ERR_DTYPE"]
+    assert lib.grpo_scale_grad(FAKE, 1, 0, 8, 8, scale, None) == E["GRPO_ERR_SHAPE"]
+    assert lib.grpo_scale_grad(FAKE, 1, 4, 0, 8, scale, None) == E["GRPO_ERR_SHAPE"]
+    assert lib.grpo_scale_grad(FAKE, 1, 4, 8, 7, scale, None) == E["GRPO_ERR_SHAPE"]   # stride < V
+    assert lib.grpo_scale_grad(FAKE, 1, 1 << 40, 1 << 30, 1 << 30, scale, None) == E["GRPO_ERR_SHAPE"]

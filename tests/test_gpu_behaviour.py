@@ -254,3 +254,84 @@ def test_token_loss_fault_bits(gpu_lib, reduction):
     clean = call(inp["mask"], inp["old_logps"])
     assert int(clean.status[0]) == 0
     assert int(clean.counts[0]) == int(inp["mask"].sum())
+
+
+@pytest.mark.parametrize("V,dtype", [(5000, "bf16"), (1000, "f32"), (4097, "f16")])
+def test_autograd_precompute_grad(gpu_lib, V, dtype):
+    """grpo_loss(..., precompute_grad=True): the forward call writes the fused
+    kernel's gradient and the backward multiplies it by the upstream
+    gradient in place (grpo_scale_grad).  Upstream 1 leaves the fused
+    gradient untouched (bitwise); other upstream values give exactly the
+    float32 product rounded once to the storage, as torch's own multiply
+    and conversion do; the split autograd path agrees within the storage's
+    rounding."""
+    wl = _wl(V, dtype, T=6)
+    announce(f"autograd precompute_grad V={V} {dtype}")
+    _, inp = _inputs(wl, seed=23)
+    fused = _call(gpu_lib, inp, wl)
+    for upstream in (1.0, 0.5, 0.37):
+        pol = inp["policy"].clone().requires_grad_(True)
+        loss, _, _ = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                       inp["rewards"], inp["mask"], precompute_grad=True,
+                                       **gpu_kwargs(wl))
+        loss.backward(torch.tensor(upstream, device=DEV))
+        torch.cuda.synchronize()
+        assert float(loss.detach()) == float(fused.loss)
+        want = fused.grad if upstream == 1.0 else (fused.grad.float() * upstream).to(fused.grad.dtype)
+        assert torch.equal(_bits(pol.grad), _bits(want)), upstream
+    # the split path (forward pass, then a backward stream with the scale inside G)
+    pol = inp["policy"].clone().requires_grad_(True)
+    loss, _, _ = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                   inp["rewards"], inp["mask"], **gpu_kwargs(wl))
+    loss.backward(torch.tensor(0.37, device=DEV))
+    torch.cuda.synchronize()
+    # Both gradients are rounded to the storage once (the fused one before
+    # the scale, the split one after it), each within unit roundoff u of its
+    # value, so they differ by at most 2u/(1-u) relative to ref, plus the
+    # float32 arithmetic of the two orders (2^-20).  Below the smallest normal
+    # the spacing is fixed: each rounding is off by at most half of it.
+    u, tiny = {"bf16": (2.0 ** -8, 2.0 ** -133), "f16": (2.0 ** -11, 2.0 ** -24),
+               "f32": (0.0, 2.0 ** -149)}[dtype]
+    rel = 2 * u / (1 - u) + 2.0 ** -20
+    ref = fused.grad.double() * 0.37
+    err = (pol.grad.double() - ref).abs()
+    excess = (err - tiny) / ref.abs().clamp_min(1e-300)
+    assert bool(torch.all(err <= rel * ref.abs() + tiny)), (float(err.max()), float(excess.max()), rel)
+
+
+def test_scale_grad_layouts(gpu_lib):
+    """grpo_scale_grad on a padded row stride (scalar path) and on aligned
+    rows (vector path) in every storage: the rows scale exactly as torch's
+    float32 multiply and conversion do, the padding is never touched, and a
+    scale of 1 leaves every bit as it was."""
+    announce("scale_grad layouts")
+    g = torch.Generator(device=DEV).manual_seed(3)
+    s = torch.tensor([0.73], dtype=torch.float32, device=DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    for dt in (torch.float32, torch.bfloat16, torch.float16):
+        for V, ld in ((1000, 1000), (1001, 1008), (4096, 4100)):
+            buf = torch.randn((37, ld), generator=g, device=DEV).to(dt)
+            view = buf[:, :V]
+            before = buf.clone()
+            gpu_lib.grpo_scale_grad(view, one)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(buf), _bits(before))
+            gpu_lib.grpo_scale_grad(view, s)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(view.contiguous()),
+                               _bits((before[:, :V].float() * 0.73).to(dt)))
+            assert torch.equal(_bits(buf[:, V:].contiguous()), _bits(before[:, V:].contiguous()))
+    # every finite 16-bit pattern (both zeros, subnormals, the largest values),
+    # through the scalar path (7-element rows) and the vector path (8)
+    pat = torch.arange(-(1 << 15), 1 << 15, dtype=torch.int32).to(torch.int16)
+    for dt in (torch.bfloat16, torch.float16):
+        x = pat.view(dt).to(DEV)
+        x = x[torch.isfinite(x)]
+        for V in (7, 8):
+            n = (x.numel() // V) * V
+            rows = x[:n].reshape(-1, V).contiguous()
+            for scale in (0.5, 0.73, 1.75):
+                got = rows.clone()
+                gpu_lib.grpo_scale_grad(got, torch.tensor([scale], dtype=torch.float32, device=DEV))
+                torch.cuda.synchronize()
+                assert torch.equal(_bits(got), _bits((rows.float() * scale).to(dt))), (dt, V, scale)
