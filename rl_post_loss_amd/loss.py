@@ -588,6 +588,37 @@ def grpo_loss(policy_logits, ref_logits, action_ids, old_logps, rewards, complet
                              completion_mask, kw)
 
 
+class _GRPOLogpLossFn(torch.autograd.Function):
+    """Autograd wrapper of the log-prob-level loss.  The forward call writes
+    d loss / d logp (for an upstream gradient of 1) beside the loss; the
+    backward multiplies that [B, T] float32 gradient in place by the upstream
+    gradient (grpo_scale_grad, nothing to do when it is 1)."""
+
+    @staticmethod
+    def forward(ctx, logp, old_logps, ref_logps, rewards, mask, kw):
+        res = grpo_token_loss(logp, old_logps, ref_logps, rewards, mask, want_grad=True, **kw)
+        ctx.grad = res.grad
+        return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
+
+    @staticmethod
+    def backward(ctx, g_loss, g_pol, g_kl):
+        scale = g_loss.reshape(1).to(torch.float32).contiguous()
+        grad = grpo_scale_grad(ctx.grad, scale)
+        ctx.grad = None
+        return grad, None, None, None, None, None
+
+
+def grpo_logp_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, **kw):
+    """(loss, policy_loss, kl) from per-token log-probs, with autograd into
+    ``logp`` ([B, T] float32): the loss of grpo_token_loss for a caller that
+    computes the log-probs of the taken tokens itself, e.g. as a gather from
+    its own log-softmax.  Only ``loss`` is differentiable.  The keywords are
+    those of grpo_token_loss, without the output and gradient controls."""
+    _need(not ({"want_grad", "grad_scale", "out", "per_token"} & set(kw)),
+          "grpo_logp_loss takes the gradient's scale from the backward pass and returns scalars only")
+    return _GRPOLogpLossFn.apply(logp, old_logps, ref_logps, rewards, completion_mask, dict(kw))
+
+
 def set_timing_events(start, stop):
     """Records the hipEvent_t handles ``start``/``stop`` (integers or
     ctypes.c_void_p, created by the caller) around the vocabulary kernel of

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from _parity import cfg_from, compare_logits_grad, gpu_kwargs, host_inputs, to_np
+from _parity import cfg_from, compare_logits_grad, compare_scalars, gpu_kwargs, host_inputs, to_np
 from workloads import WORKLOADS, LogitsWorkload, make_logits_inputs, poison_masked
 
 pytestmark = pytest.mark.gpu
@@ -297,6 +297,61 @@ def test_autograd_precompute_grad(gpu_lib, V, dtype):
     err = (pol.grad.double() - ref).abs()
     excess = (err - tiny) / ref.abs().clamp_min(1e-300)
     assert bool(torch.all(err <= rel * ref.abs() + tiny)), (float(err.max()), float(excess.max()), rel)
+
+
+@pytest.mark.parametrize("reduction", ["token_mean", "sequence_mean"])
+def test_autograd_logp_loss(gpu_lib, reduction):
+    """grpo_logp_loss: the same loss as grpo_token_loss, and logp.grad is
+    that call's d loss / d logp (upstream 1, bitwise) or its float32 product
+    with the upstream gradient (0.5, 0.37, exactly as torch multiplies)."""
+    from workloads import TOKEN_WORKLOADS, make_token_inputs
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    announce(f"autograd logp loss {reduction}")
+    inp = make_token_inputs(wl, device=DEV, seed=29, B=32, T=258)
+    kw = dict(eps_low=0.2, eps_high=0.28, beta=0.04, samples_per_prompt=8, reduction=reduction)
+    direct = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                                     inp["mask"], **kw)
+    torch.cuda.synchronize()
+    for upstream in (1.0, 0.5, 0.37):
+        lp = inp["logp"].clone().requires_grad_(True)
+        loss, pol, kl = gpu_lib.grpo_logp_loss(lp, inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                                               inp["mask"], **kw)
+        loss.backward(torch.tensor(upstream, device=DEV))
+        torch.cuda.synchronize()
+        assert float(loss.detach()) == float(direct.loss)
+        assert float(pol.detach()) == float(direct.policy_loss)
+        assert float(kl.detach()) == float(direct.kl)
+        want = direct.grad if upstream == 1.0 else direct.grad * upstream
+        assert torch.equal(_bits(lp.grad), _bits(want)), upstream
+
+
+def test_logp_loss_chain_against_oracle(gpu_lib):
+    """d loss / d logits through torch's log-softmax and gather into
+    grpo_logp_loss (the token kernel's gradient, chained by torch's
+    backward) against the oracle's fused gradient, at the float32 bar of the
+    logits path: an end-to-end check of the token path that shares no kernel
+    with the vocabulary kernel."""
+    wl = _wl(V=1000, dtype="f32", T=12, sizes=(4, 4, 4), len_range=(1, 12))
+    announce("logp loss chain vs oracle V=1000 f32")
+    cpu, inp = _inputs(wl, seed=31)
+    logits = inp["policy"].clone().requires_grad_(True)
+    ids = inp["action_ids"][..., None]
+    logp = torch.log_softmax(logits, dim=-1).gather(-1, ids).squeeze(-1)
+    with torch.no_grad():
+        ref_logp = torch.log_softmax(inp["ref"], dim=-1).gather(-1, ids).squeeze(-1).contiguous()
+    loss, _, _ = gpu_lib.grpo_logp_loss(logp.contiguous(), inp["old_logps"], ref_logp, inp["rewards"],
+                                        inp["mask"], **gpu_kwargs(wl))
+    loss.backward()
+    # the same call without autograd, for its per-sequence totals
+    direct = gpu_lib.grpo_token_loss(logp.detach().contiguous(), inp["old_logps"], ref_logp,
+                                     inp["rewards"], inp["mask"], **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert float(loss.detach()) == float(direct.loss)
+    h = host_inputs(cpu)
+    ref = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"], h["mask"],
+                                   h["rewards"], groups=wl.groups_kwargs(), cfg=cfg_from(wl))
+    compare_scalars(direct, ref, cfg_from(wl), 1e-5, "logp chain")
+    compare_logits_grad(to_np(logits.grad), ref, cfg_from(wl), h["mask"], "f32", "logp chain")
 
 
 def test_scale_grad_layouts(gpu_lib):
