@@ -158,12 +158,14 @@ def test_no_active_tokens(gpu_lib):
         assert int(res.counts[0]) == 0
 
 
-def test_autograd_split_forward_backward(gpu_lib):
+@pytest.mark.parametrize("V", [12000, 20000])
+def test_autograd_split_forward_backward(gpu_lib, V):
     """grpo_loss() runs the forward pass, keeps per-row weights, and the
     backward pass writes the same gradient as the fused call, scaled by the
-    upstream gradient."""
-    wl = _wl(12000, "bf16", T=6)
-    announce("autograd split")
+    upstream gradient (24 KB rows: 256 threads per row in both split
+    kernels; 40 KB rows: the gradient-only kernel at 1024 threads)."""
+    wl = _wl(V, "bf16", T=6)
+    announce(f"autograd split V={V}")
     _, inp = _inputs(wl, seed=17)
     fused = _call(gpu_lib, inp, wl)
     pol = inp["policy"].clone().requires_grad_(True)
