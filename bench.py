@@ -122,6 +122,32 @@ def cpu_baseline(wl, inp, target_s=12.0, rows_per_chunk=32):
                        f"float64 numpy, single thread, {compute:.1f} s of compute; host copies excluded")
 
 
+def cpu_baseline_groups(wl, inp, call, target_s=12.0, groups_per_chunk=16):
+    """The fp64 oracle as it stands on a [B, T] log-prob batch: ``call`` runs
+    it on host arrays of whole groups, a chunk at a time in batch order and
+    starting over at the end of the batch, until about ``target_s`` seconds
+    of host compute have run.  Each chunk is its own oracle call, so its
+    sequence weights and any global statistic are the chunk's; the work per
+    slot is the same."""
+    h = {k: v.cpu().numpy() for k, v in inp.items()}
+    B, T = h["mask"].shape
+    size = wl.group_size * groups_per_chunk
+    compute = 0.0
+    done = 0                      # sequences processed, over all passes
+    while compute < target_s:
+        start = done % B
+        sl = slice(start, min(B, start + size))
+        part = {k: v[sl] for k, v in h.items()}
+        t0 = time.perf_counter()
+        call(part)
+        compute += time.perf_counter() - t0
+        done += sl.stop - sl.start
+    return dict(value=done * T / compute, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} sequences ({done * T} slots, {done / B:.2f} passes over the batch of "
+                       f"{B}) in chunks of {size} sequences, float64 numpy, single thread, "
+                       f"{compute:.1f} s of compute; host copies excluded")
+
+
 class HipEvents:
     """hipEvent_t pairs created through the HIP runtime (the vocabulary kernel
     is launched by the library on torch's current stream; the library records
@@ -262,6 +288,17 @@ def run_token(args):
                       "step_GBps": alg / (ms * 1e-3) / 1e9, "timing": GRAPH_TIMING,
                       "ms_per_step_graph_per_call": ms_graph_per_call,
                       "ms_per_step_eager_python": ms_eager}}
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cfg = oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
+                                reduction=wl.reduction)
+        out["cpu_baseline"] = cpu_baseline_groups(
+            wl, copies[0], lambda h: oracle.grpo_token_loss(
+                h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                groups=dict(samples_per_prompt=wl.group_size), cfg=cfg),
+            target_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
@@ -310,6 +347,18 @@ def run_adv(args):
                                   f"ragged lengths, {est}, normalized; input copies rotated: {args.copies}",
                       "algorithmic_bytes": alg, "step_GBps": alg / (ms * 1e-3) / 1e9,
                       "timing": GRAPH_TIMING, "ms_per_step_graph_per_call": ms_graph_per_call}}
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        if est == "reinforce_pp":
+            call = lambda h: oracle.token_advantages(est, h["rewards"], h["old_logps"], h["ref_logp"],
+                                                     h["mask"], **kw)
+        else:
+            call = lambda h: oracle.token_advantages(est, h["rewards"], None, None, h["mask"],
+                                                     groups=dict(samples_per_prompt=wl.group_size),
+                                                     normalize=True)
+        out["cpu_baseline"] = cpu_baseline_groups(wl, copies[0], call, target_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
