@@ -142,6 +142,16 @@ def test_seq_real_csr_leave_one_out(gpu_lib):
     check_seq_logits(gpu_lib, wl, dict(pg_loss="real"), seed=3)
 
 
+@pytest.mark.parametrize("kw", [SEQ_CASES[0], SEQ_CASES[4], SEQ_CASES[6]], ids=_id)
+@pytest.mark.parametrize("V", [4097, 20000])
+def test_seq_logits_f16(gpu_lib, V, kw):
+    """IEEE half logits and gradient through the sequence-level losses (the
+    forward-only kernel, then the gradient-only kernel: 256 threads per row
+    with a scalar tail at V = 4097, 1024 at V = 20000) and the
+    sequence-masked truncated IS (the fused kernel)."""
+    check_seq_logits(gpu_lib, _wl(V, "f16", T=8), kw, seed=6)
+
+
 def test_seq_gspo_f32_gradient_from_bf16(gpu_lib):
     check_seq_logits(gpu_lib, _wl(4097, "bf16"), SEQ_CASES[0], seed=4, grad_dtype=torch.float32)
 
