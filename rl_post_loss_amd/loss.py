@@ -528,6 +528,15 @@ def grpo_scale_grad(grad, scale):
     return grad
 
 
+def _scalar_outputs(ctx, res):
+    """(loss, policy_loss, kl) of an autograd wrapper; the last two are
+    detached reporting values ("GRPO Loss", Tensor Contract), so calling
+    backward on them raises instead of giving a zero gradient."""
+    loss, pol, kl = (res.scalars[k].clone() for k in range(3))
+    ctx.mark_non_differentiable(pol, kl)
+    return loss, pol, kl
+
+
 class _GRPOLossFn(torch.autograd.Function):
     """Autograd wrapper.  By default the forward runs the vocabulary pass once
     and keeps the per-row gradient weights in a dedicated workspace; the
@@ -547,7 +556,7 @@ class _GRPOLossFn(torch.autograd.Function):
             res = grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                                     mask, **kw)
             ctx.grad = res.grad
-            return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
+            return _scalar_outputs(ctx, res)
         ng = 0 if kw.get("group_boundaries") is None else len(kw["group_boundaries"]) - 1
         ws = workspace(B, T, ng, policy_logits.device, dedicated=True)
         res = grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards, mask,
@@ -555,7 +564,7 @@ class _GRPOLossFn(torch.autograd.Function):
         ctx.save_for_backward(policy_logits, action_ids, mask if mask is not None else torch.empty(0))
         ctx.has_mask = mask is not None
         ctx.ws = ws
-        return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
+        return _scalar_outputs(ctx, res)
 
     @staticmethod
     def backward(ctx, g_loss, g_pol, g_kl):
@@ -574,8 +583,8 @@ class _GRPOLossFn(torch.autograd.Function):
 def grpo_loss(policy_logits, ref_logits, action_ids, old_logps, rewards, completion_mask=None,
               precompute_grad=False, **kw):
     """(loss, policy_loss, kl) with autograd into ``policy_logits`` (the call
-    signature of "GRPO Loss", Entry Point).  Gradients of policy_loss and kl
-    as separate outputs are not propagated: only ``loss`` is differentiable.
+    signature of "GRPO Loss", Entry Point).  policy_loss and kl are detached
+    reporting values: only ``loss`` is differentiable.
     ``precompute_grad``: compute d loss / d logits in the forward call with
     the fused kernel (one read of the policy logits fewer than a separate
     backward pass, at the cost of holding a [B, T, V] gradient until the
@@ -598,7 +607,7 @@ class _GRPOLogpLossFn(torch.autograd.Function):
     def forward(ctx, logp, old_logps, ref_logps, rewards, mask, kw):
         res = grpo_token_loss(logp, old_logps, ref_logps, rewards, mask, want_grad=True, **kw)
         ctx.grad = res.grad
-        return res.scalars[0].clone(), res.scalars[1].clone(), res.scalars[2].clone()
+        return _scalar_outputs(ctx, res)
 
     @staticmethod
     def backward(ctx, g_loss, g_pol, g_kl):
@@ -612,7 +621,8 @@ def grpo_logp_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, **
     """(loss, policy_loss, kl) from per-token log-probs, with autograd into
     ``logp`` ([B, T] float32): the loss of grpo_token_loss for a caller that
     computes the log-probs of the taken tokens itself, e.g. as a gather from
-    its own log-softmax.  Only ``loss`` is differentiable.  The keywords are
+    its own log-softmax.  Only ``loss`` is differentiable (policy_loss and
+    kl are detached reporting values).  The keywords are
     those of grpo_token_loss, without the output and gradient controls."""
     _need(not ({"want_grad", "grad_scale", "out", "per_token"} & set(kw)),
           "grpo_logp_loss takes the gradient's scale from the backward pass and returns scalars only")

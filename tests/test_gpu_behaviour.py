@@ -172,6 +172,10 @@ def test_autograd_split_forward_backward(gpu_lib, V):
     loss, pl, kl = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
                                      inp["rewards"], inp["mask"], **gpu_kwargs(wl))
     assert torch.equal(_bits(loss.detach().reshape(1)), _bits(fused.scalars[:1]))
+    # policy_loss and kl are detached reporting values
+    assert loss.requires_grad and not pl.requires_grad and not kl.requires_grad
+    with pytest.raises(RuntimeError):
+        kl.backward()
     loss.backward()
     torch.cuda.synchronize()
     assert torch.equal(_bits(pol.grad), _bits(fused.grad))
@@ -318,6 +322,7 @@ def test_autograd_logp_loss(gpu_lib, reduction):
         lp = inp["logp"].clone().requires_grad_(True)
         loss, pol, kl = gpu_lib.grpo_logp_loss(lp, inp["old_logps"], inp["ref_logp"], inp["rewards"],
                                                inp["mask"], **kw)
+        assert loss.requires_grad and not pol.requires_grad and not kl.requires_grad
         loss.backward(torch.tensor(upstream, device=DEV))
         torch.cuda.synchronize()
         assert float(loss.detach()) == float(direct.loss)
