@@ -15,6 +15,8 @@ policy_loss + beta * kl and its gradient flows into the policy logits only.
 from __future__ import annotations
 
 import ctypes as C
+import hashlib
+import json
 from dataclasses import dataclass
 
 import torch
@@ -187,6 +189,19 @@ class GRPOResult:
     tok_kl: torch.Tensor | None = None
     seq_logratio: torch.Tensor | None = None   # [B] s_i (GSPO and REAL only)
     _c_outputs: object = None   # the GrpoOutputs struct pointing at these tensors
+    _prov: object = None        # the call's settings, turned into ``provenance`` when read
+
+    @property
+    def provenance(self):
+        """What produced these outputs: the entry point, the library's ABI
+        version, the sizes and storage types, the objective and group settings
+        as the library received them, which optional inputs were given, the
+        device, and ``fingerprint``, a hash of the settings that fix the
+        numbers (entry point, storage types, objective, groups), for telling
+        runs of the same configuration from others."""
+        if self._prov is not None and not isinstance(self._prov, dict):
+            self._prov = _provenance(*self._prov)
+        return self._prov
 
     @property
     def loss(self):
@@ -199,6 +214,23 @@ class GRPOResult:
     @property
     def kl(self):
         return self.scalars[2]
+
+
+def _struct_fields(st):
+    return {name: getattr(st, name) for name, _ in st._fields_ if name != "group_boundaries"}
+
+
+def _provenance(entry, sizes, dtypes, cfg, groups, boundaries, inputs, device):
+    g = None
+    if groups is not None:
+        g = _struct_fields(groups)
+        g["group_boundaries"] = None if boundaries is None else [int(v) for v in boundaries]
+    d = dict(entry=entry, abi_version=int(load_library().grpo_abi_version()), sizes=sizes,
+             dtypes=dtypes, config=_struct_fields(cfg), groups=g, inputs=inputs,
+             device=torch.cuda.get_device_name(device))
+    ident = json.dumps({k: d[k] for k in ("entry", "dtypes", "config", "groups")}, sort_keys=True)
+    d["fingerprint"] = hashlib.sha256(ident.encode()).hexdigest()[:16]
+    return d
 
 
 def _outputs(B, T, device, per_token, want_logp):
@@ -416,6 +448,13 @@ def grpo_token_loss(logp, old_logps, ref_logps, rewards, completion_mask=None, *
                               None if g is None else C.byref(g), C.byref(cfg),
                               _ptr(res.grad), _ptr(grad_scale), C.byref(o), ws.data_ptr(), wsb,
                               _stream_ptr(dev)), lib)
+    res._prov = ("grpo_token_loss", dict(B=B, T=T), dict(logp="torch.float32"), cfg, g,
+                 group_boundaries,
+                 dict(ref_logps=ref_logps is not None, gen_logps=gen_logps is not None,
+                      token_advantages=token_advantages is not None,
+                      grad_scale=grad_scale is not None, mask=completion_mask is not None,
+                      grad=want_grad),
+                 dev)
     return res
 
 
@@ -486,6 +525,14 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                                 None if g is None else C.byref(g), C.byref(cfg),
                                 gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o), ws.data_ptr(),
                                 wsb, _stream_ptr(dev)), lib)
+    res._prov = ("grpo_loss_fwd_bwd", dict(B=B, T=T, V=V),
+                 dict(logits=str(policy_logits.dtype), action_ids=str(action_ids.dtype),
+                      grad=None if grad_out is False else str(grad_out.dtype)),
+                 cfg, g, group_boundaries,
+                 dict(ref_logits=ref_logits is not None, gen_logps=gen_logps is not None,
+                      token_advantages=token_advantages is not None,
+                      grad_scale=grad_scale is not None, mask=completion_mask is not None),
+                 dev)
     return res
 
 

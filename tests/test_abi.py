@@ -281,3 +281,29 @@ def test_scale_grad_argument_validation():
     assert lib.grpo_scale_grad(FAKE, 1, 4, 0, 8, scale, None) == E["GRPO_ERR_SHAPE"]
     assert lib.grpo_scale_grad(FAKE, 1, 4, 8, 7, scale, None) == E["GRPO_ERR_SHAPE"]   # stride < V
     assert lib.grpo_scale_grad(FAKE, 1, 1 << 40, 1 << 30, 1 << 30, scale, None) == E["GRPO_ERR_SHAPE"]
+
+
+def test_provenance_fingerprint(monkeypatch):
+    """The fingerprint of a result's provenance follows the settings that fix
+    the numbers (entry point, storage types, objective, groups) and nothing
+    else: not the sizes, the optional-input flags or the device."""
+    import torch
+    from rl_post_loss_amd import loss as L
+    monkeypatch.setattr(torch.cuda, "get_device_name", lambda d=None: "gpu")
+
+    def fp(entry="grpo_loss_fwd_bwd", eps=0.2, red="token_mean", spp=8, bounds=None, B=16,
+           logits="torch.bfloat16", inputs=None):
+        cfg = L._make_cfg(eps, None, None, 0.04, red, None, **L.OBJECTIVE_DEFAULTS)
+        g, _, _ = L._make_groups(B, spp, bounds, False, True, 1e-6)
+        d = L._provenance(entry, dict(B=B, T=4, V=32), dict(logits=logits), cfg, g, bounds,
+                          inputs or {}, "cuda:0")
+        assert d["config"]["eps_low"] == eps and d["groups"]["group_boundaries"] == (
+            None if bounds is None else list(bounds))
+        return d["fingerprint"]
+
+    base = fp()
+    assert fp(B=32, inputs=dict(mask=True)) == base
+    for other in (fp(entry="grpo_token_loss"), fp(eps=0.25), fp(red="sequence_mean"), fp(spp=4),
+                  fp(logits="torch.float32"), fp(spp=None, bounds=[0, 8, 16])):
+        assert other != base
+    assert fp(spp=None, bounds=[0, 8, 16]) != fp(spp=None, bounds=[0, 4, 16])

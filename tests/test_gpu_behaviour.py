@@ -361,6 +361,28 @@ def test_logp_loss_chain_against_oracle(gpu_lib):
     compare_logits_grad(to_np(logits.grad), ref, cfg_from(wl), h["mask"], "f32", "logp chain")
 
 
+def test_result_provenance(gpu_lib):
+    """GRPOResult.provenance records the call; its fingerprint is the same
+    for the same settings on other data and sizes, and differs when a setting
+    that changes the numbers differs."""
+    wl = _wl(1000, "f32", T=4)
+    announce("provenance")
+    _, inp = _inputs(wl, seed=41)
+    a = _call(gpu_lib, inp, wl).provenance
+    assert a["entry"] == "grpo_loss_fwd_bwd" and a["abi_version"] == 6
+    assert a["sizes"] == dict(B=wl.B, T=4, V=1000) and a["dtypes"]["logits"] == "torch.float32"
+    assert a["groups"]["samples_per_prompt"] == 4 and a["device"]
+    _, inp2 = _inputs(_wl(1000, "f32", T=9), seed=42)
+    assert _call(gpu_lib, inp2, _wl(1000, "f32", T=9)).provenance["fingerprint"] == a["fingerprint"]
+    other = _call(gpu_lib, inp, wl, eps_high=0.3).provenance
+    assert other["fingerprint"] != a["fingerprint"] and other["config"]["eps_high"] == 0.3
+    lp = torch.log_softmax(inp["policy"], -1).gather(-1, inp["action_ids"][..., None])[..., 0]
+    t = gpu_lib.grpo_token_loss(lp.contiguous(), inp["old_logps"], lp.contiguous(), inp["rewards"],
+                                inp["mask"], **gpu_kwargs(wl))
+    torch.cuda.synchronize()
+    assert t.provenance["entry"] == "grpo_token_loss" and t.provenance["inputs"]["grad"]
+
+
 def test_scale_grad_layouts(gpu_lib):
     """grpo_scale_grad on a padded row stride (scalar path) and on aligned
     rows (vector path) in every storage: the rows scale exactly as torch's
