@@ -17,7 +17,55 @@
 #include "../../include/grpo.h"
 #include "grpo_internal.hpp"
 
+// 1: the per-token exponentials use the hardware base-2 exponential and the
+// KL estimator a short series (exp_hw, k3_expm1 below); 0: the math
+// library's expf and expm1f.
+#ifndef GRPO_FAST_TOKEN_MATH
+#define GRPO_FAST_TOKEN_MATH 1
+#endif
+
 namespace grpo {
+
+// e^x as 2^(fl(x log2 e)) on the hardware exponential: about 2 ulp for
+// |x| up to ~10 (the rounding of x log2 e adds |x| 2^-24 relative), exactly
+// 1 at x = 0; results below 2^-126 flush to zero.
+__device__ __forceinline__ float exp_hw(float x) {
+#if GRPO_FAST_TOKEN_MATH
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+#else
+  return expf(x);
+#endif
+}
+
+// The k3 estimator e^d - 1 - d and e^d - 1 together.  For |d| < 1/2,
+// k3 = d^2 (1/2 + d/3! + ... + d^7/9!): the next term is below 2^-28 of k3,
+// and nothing cancels, where e^d - 1 - d loses the leading digits for small
+// d; e^d - 1 = d + k3.  Otherwise both come from the hardware exponential,
+// where |e^d - 1| > 0.39 keeps the subtraction benign.  NaN and +-inf give
+// what expm1f gives: k3(NaN) = NaN, k3(+inf) = NaN, k3(-inf) = +inf.
+struct K3Pair {
+  float k3, em1;
+};
+__device__ __forceinline__ K3Pair k3_expm1(float d) {
+#pragma clang fp contract(off)
+#if GRPO_FAST_TOKEN_MATH
+  float p = 1.0f / 362880.0f;
+  p = fmaf(p, d, 1.0f / 40320.0f);
+  p = fmaf(p, d, 1.0f / 5040.0f);
+  p = fmaf(p, d, 1.0f / 720.0f);
+  p = fmaf(p, d, 1.0f / 120.0f);
+  p = fmaf(p, d, 1.0f / 24.0f);
+  p = fmaf(p, d, 1.0f / 6.0f);
+  p = fmaf(p, d, 0.5f);
+  const float ks = (d * d) * p;
+  const float e = exp_hw(d) - 1.0f;
+  const bool small = fabsf(d) < 0.5f;
+  return K3Pair{small ? ks : e - d, small ? d + ks : e};
+#else
+  const float em = expm1f(d);
+  return K3Pair{em - d, em};
+#endif
+}
 
 struct TokObj {
   float loss;    // policy loss l
@@ -55,7 +103,7 @@ __device__ inline double sequence_weight(int32_t reduction, double alpha, double
 
 // Off-policy weight of one token: exp(old - gen), truncated for tis/icepop.
 __device__ __forceinline__ float token_is_weight(const Objective& o, float old, float gen) {
-  float wi = expf(old - gen);
+  float wi = exp_hw(old - gen);
   if (o.tis) wi = wi != wi ? wi : fminf(fmaxf(wi, o.tis_lo), o.tis_hi);
   return wi;
 }
@@ -70,15 +118,16 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
                                                   float keep = 1.0f) {
 #pragma clang fp contract(off)
   TokObj r;
-  const float rho = expf(logp - old);
+  const float rho = exp_hw(logp - old);
   if constexpr (!kGeneral) {
-    r.kl = expm1f(d) - d;
+    const K3Pair k = k3_expm1(d);
+    r.kl = k.k3;
     r.clipped = (adv > 0.0f && rho > o.hi) || (adv < 0.0f && rho < o.lo);
     const float unc = rho * adv;
     const float clp = fminf(fmaxf(rho, o.lo), o.hi) * adv;
     r.loss = -fminf(unc, clp);
     const float dloss = r.clipped ? 0.0f : -adv * rho;
-    r.g = dloss + o.beta * -expm1f(d);
+    r.g = dloss + o.beta * -k.em1;
     return r;
   } else {
     float dloss;
@@ -111,7 +160,7 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
       // s and 1 - s both come from e = exp(-|x|), so neither cancels.
       const float tau = adv > 0.0f ? o.tau_pos : o.tau_neg;
       const float x = tau * (rho - 1.0f);
-      const float e = expf(-fabsf(x));
+      const float e = exp_hw(-fabsf(x));
       const float inv = 1.0f / (1.0f + e);
       const float s = x >= 0.0f ? inv : e * inv;
       const float sc = x >= 0.0f ? e * inv : inv;
@@ -147,9 +196,9 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
       val = 0.5f * dc * dc;
       dval = dc;
     } else {
-      const float em = expm1f(dc);
-      val = em - dc;
-      dval = em;
+      const K3Pair k = k3_expm1(dc);
+      val = k.k3;
+      dval = k.em1;
     }
     if (o.kl_out > 0.0f) {
       pass = pass && fabsf(val) <= o.kl_out;
