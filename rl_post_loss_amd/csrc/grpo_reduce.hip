@@ -295,7 +295,11 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
   const float useq = seqlv ? a.useq[i] : 0.0f;
   double p = 0.0, k = 0.0;
   long long c = 0;
-  bool nonfinite = false;
+  // A non-finite token loss or KL carries into p or k (float values cannot
+  // overflow a binary64 sum), and a non-finite gradient value into gz, which
+  // gains g * 0: 0 for every finite g, NaN otherwise.  One test after the
+  // loop then flags exactly the sequences with a non-finite value.
+  float gz = 0.0f;
   if (vec) {
     for (int64_t q0 = tid; q0 < n4; q0 += QU * kTokThreads) {
       if (q0 != tid) {
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
             p = p + double(r.loss);
             k = k + double(r.kl);
             c += r.clipped ? 1 : 0;
-            nonfinite |= !(isfinite(r.loss) && isfinite(r.kl) && isfinite(gv[j]));
+            gz = fmaf(gv[j], 0.0f, gz);
           }
         }
         if (a.dlogp)
@@ -353,13 +357,14 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
         p = p + double(r.loss);
         k = k + double(r.kl);
         c += r.clipped ? 1 : 0;
-        nonfinite |= !(isfinite(r.loss) && isfinite(r.kl) && isfinite(g));
+        gz = fmaf(g, 0.0f, gz);
       }
       if (a.dlogp) a.dlogp[s] = g;
       if (a.out_loss) a.out_loss[s] = tl;
       if (a.out_kl) a.out_kl[s] = tk;
     }
   }
+  const bool nonfinite = !(isfinite(p) && isfinite(k) && isfinite(gz));
   if constexpr (kWeights != 2) {
     if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
   }
