@@ -419,3 +419,48 @@ def test_scale_grad_layouts(gpu_lib):
                 gpu_lib.grpo_scale_grad(got, torch.tensor([scale], dtype=torch.float32, device=DEV))
                 torch.cuda.synchronize()
                 assert torch.equal(_bits(got), _bits((rows.float() * scale).to(dt))), (dt, V, scale)
+
+
+@pytest.mark.parametrize("general", [False, True])
+def test_kl_estimator_accuracy(gpu_lib, general):
+    """The k3 estimator e^d - 1 - d and its derivative e^d - 1 as the kernels
+    evaluate them, against binary64, over d in [-40, 40] (dense near 0).
+    With logp = old (ratio 1), equal rewards (A = 0), beta = 1 and a fixed
+    normaliser of 1, the token's KL output is k3(d) and its gradient is
+    -(e^d - 1) with no other rounding.  For |d| < 1 (the series) both are
+    within 4 ulp; beyond, within 4 ulp of the hardware exponential's error
+    e^d (|d| + 1) 2^-24.  general: the objective's general code path (an
+    input clamp no value reaches)."""
+    announce(f"KL estimator accuracy general={general}")
+    B, T = 16, 4096
+    rng = np.random.default_rng(5)
+    tiny = np.logspace(-8, 0, 6000)
+    d_want = np.concatenate([tiny, -tiny, np.linspace(-1.5, 1.5, 20000), rng.uniform(-40, 40, 20000),
+                             [0.0, 1.0, -1.0, 0.9999999, -0.9999999]])
+    d_want = np.resize(d_want, B * T).reshape(B, T)
+    logp = np.full((B, T), -1.25, dtype=np.float32)
+    ref = (logp.astype(np.float64) + d_want).astype(np.float32)
+    d = (ref - logp).astype(np.float64)                 # the float32 difference the kernel forms
+    kw = dict(samples_per_prompt=8, beta=1.0, reduction="fixed_constant", norm_constant=1.0,
+              per_token=True)
+    if general:
+        kw["kl_input_clamp"] = 1000.0
+    lp = torch.from_numpy(logp).to(DEV)
+    res = gpu_lib.grpo_token_loss(lp, lp.clone(), torch.from_numpy(ref).to(DEV),
+                                  torch.ones(B, device=DEV), torch.ones((B, T), dtype=torch.bool, device=DEV),
+                                  **kw)
+    torch.cuda.synchronize()
+    k3 = to_np(res.tok_kl)
+    em1 = -to_np(res.grad)
+    em1_x = np.expm1(d)
+    k3_x = np.where(np.abs(d) < 1e-3, d * d * (0.5 + d / 6 + d * d / 24 + d ** 3 / 120), em1_x - d)
+    u = 2.0 ** -24
+    small = np.abs(d) < 1.0
+    assert np.all(np.abs(k3 - k3_x)[small] <= 4 * u * k3_x[small]), float(np.max(np.abs(k3 - k3_x)[small] / k3_x[small]))
+    assert np.all(np.abs(em1 - em1_x)[small] <= 4 * u * np.abs(em1_x)[small])
+    big = ~small
+    lim = 4 * u * (np.exp(d) * (np.abs(d) + 1) + np.abs(em1_x) + np.abs(k3_x))
+    assert np.all(np.abs(k3 - k3_x)[big] <= lim[big])
+    assert np.all(np.abs(em1 - em1_x)[big] <= lim[big])
+    assert np.all(k3[d == 0] == 0) and np.all(em1[d == 0] == 0)
+    assert np.all(k3 >= 0)
