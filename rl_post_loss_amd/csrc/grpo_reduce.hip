@@ -368,11 +368,41 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
   if constexpr (kWeights != 2) {
     if (nonfinite) atomicOr(&a.hdr->status, GRPO_FAULT_NONFINITE);
   }
-  p = block_sum_f64<kTokThreads>(p, sh_f64);
-  k = block_sum_f64<kTokThreads>(k, sh_f64);
-  c = block_sum_i64<kTokThreads>(c, sh_i64);
+  // the sequence's totals: the tree of block_sum_* (butterfly in each wave,
+  // then the wave partials in wave order), all four through one exchange
+  constexpr int NW = kTokThreads / kWave;
+  __shared__ double sh_pk[2][NW];
+  __shared__ long long sh_c[NW];
+  __shared__ int sh_bad[NW];
+  p = wave_sum_f64<kWave>(p);
+  k = wave_sum_f64<kWave>(k);
+  c = wave_sum_i64<kWave>(c);
+  const bool wbad = __ballot(nonfinite ? 1 : 0) != 0;
+  const int lane = tid % kWave, wv = tid / kWave;
+  __syncthreads();  // earlier readers of shared memory are done
+  if (lane == 0) {
+    sh_pk[0][wv] = p;
+    sh_pk[1][wv] = k;
+    sh_c[wv] = c;
+    sh_bad[wv] = wbad ? 1 : 0;
+  }
+  __syncthreads();
   bool bad = false;
-  if constexpr (kWeights == 2) bad = __syncthreads_or(nonfinite ? 1 : 0) != 0;
+  if (tid == 0) {
+    double tp = 0.0, tk = 0.0;
+    long long tc = 0;
+    int tb = 0;
+    for (int w = 0; w < NW; ++w) {
+      tp += sh_pk[0][w];
+      tk += sh_pk[1][w];
+      tc += sh_c[w];
+      tb |= sh_bad[w];
+    }
+    p = tp;
+    k = tk;
+    c = tc;
+    bad = tb != 0;
+  }
   if (tid == 0) {
     a.P[i] = p;
     a.K[i] = k;
