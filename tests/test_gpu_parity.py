@@ -101,6 +101,19 @@ def test_vocab_sizes_and_paths(gpu_lib, V, dtype):
     check_logits_case(gpu_lib, _custom(V, dtype))
 
 
+@pytest.mark.parametrize("V,dtype", [
+    (2048, "bf16"), (2056, "bf16"),        # 4 KB rows: wave per row, then a resident block
+    (32768, "bf16"), (32776, "bf16"),      # 64 KB: resident at 256 threads (16 chunks), then 768
+    (135168, "bf16"), (135176, "bf16"),    # 264 KB: the largest resident row, then streaming
+    (16384, "f32"), (16388, "f32"),        # the same limits for float32 rows
+    (67584, "f32"), (67588, "f32"),
+])
+def test_kernel_variant_boundaries(gpu_lib, V, dtype):
+    """Row sizes exactly at each kernel variant's limit and one chunk past
+    it, so that both sides of every switch in the row-kernel choice run."""
+    check_logits_case(gpu_lib, _custom(V, dtype, T=4, sizes=(4, 4)), seed=9)
+
+
 @pytest.mark.parametrize("V,dtype", [(40000, "bf16"), (20001 * 4 // 4, "f32")])
 def test_many_rows_per_block(gpu_lib, V, dtype):
     """More rows than compute units, ragged masks: each persistent block walks
