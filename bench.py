@@ -523,18 +523,17 @@ def summarize_pmc(dirs, workload, out_dir):
     summary = dict(kernel=ROW_KERNEL, workload=workload, kernel_source_hash=kernel_source_hash(),
                    counters=res, traffic_bytes_per_launch=traffic,
                    commands=["rocprofv3 --pmc FETCH_SIZE --kernel-include-regex grpo_rows -f csv "
-                             f"-d gpurun_out/pmc_fetch -o run -- python3 bench.py --workload {workload} "
+                             f"-d {fetch_dir} -o run -- python3 bench.py --workload {workload} "
                              "--steps 3 --warmup 1 --no-cpu-baseline",
                              "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex grpo_rows -f csv "
-                             f"-d gpurun_out/pmc_write -o run -- python3 bench.py --workload {workload} "
+                             f"-d {write_dir} -o run -- python3 bench.py --workload {workload} "
                              "--steps 3 --warmup 1 --no-cpu-baseline",
                              "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex elementwise -f csv "
-                             "-d gpurun_out/pmc_cal_fetch -o run -- python3 bench.py --calibrate-only",
+                             f"-d {cal_fetch_dir} -o run -- python3 bench.py --calibrate-only",
                              "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex elementwise -f csv "
-                             "-d gpurun_out/pmc_cal_write -o run -- python3 bench.py --calibrate-only",
-                             "python bench.py --workload " + workload + " --summarize-pmc "
-                             "gpurun_out/pmc_fetch gpurun_out/pmc_write gpurun_out/pmc_cal_fetch "
-                             "gpurun_out/pmc_cal_write"])
+                             f"-d {cal_write_dir} -o run -- python3 bench.py --calibrate-only",
+                             f"python bench.py --workload {workload} --summarize-pmc "
+                             f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"])
     os.makedirs(out_dir, exist_ok=True)
     base = os.path.join(out_dir, f"{ROW_KERNEL}_{workload}_pmc")
     with open(base + ".json", "w") as f:
