@@ -464,3 +464,40 @@ def test_kl_estimator_accuracy(gpu_lib, general):
     assert np.all(np.abs(em1 - em1_x)[big] <= lim[big])
     assert np.all(k3[d == 0] == 0) and np.all(em1[d == 0] == 0)
     assert np.all(k3 >= 0)
+
+
+def test_two_streams_at_once(gpu_lib):
+    """Calls on two streams with no synchronisation between them each get
+    their own workspace (the binding keys it by stream), so both results
+    equal the single-stream ones bit for bit: the fused logits call and the
+    log-prob token loss."""
+    wl = _wl(6000, "bf16", T=32, sizes=(4, 4, 4, 4))
+    announce("two streams")
+    _, a = _inputs(wl, seed=51)
+    _, b = _inputs(wl, seed=52)
+    ref_a, ref_b = _call(gpu_lib, a, wl), _call(gpu_lib, b, wl)
+    lp = {k: torch.log_softmax(v["policy"].float(), -1).gather(-1, v["action_ids"][..., None])[..., 0]
+          .contiguous() for k, v in (("a", a), ("b", b))}
+    tok = {k: gpu_lib.grpo_token_loss(lp[k], v["old_logps"], lp[k], v["rewards"], v["mask"],
+                                      **gpu_kwargs(wl)) for k, v in (("a", a), ("b", b))}
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    out = {"a": [], "b": []}
+    for _ in range(4):
+        for key, inp, s in (("a", a, s1), ("b", b, s2)):
+            with torch.cuda.stream(s):
+                r = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                              inp["old_logps"], inp["rewards"], inp["mask"],
+                                              **gpu_kwargs(wl))
+                t = gpu_lib.grpo_token_loss(lp[key], inp["old_logps"], lp[key], inp["rewards"],
+                                            inp["mask"], **gpu_kwargs(wl))
+                out[key].append((r, t))
+    torch.cuda.synchronize()
+    for key, ref, rt in (("a", ref_a, tok["a"]), ("b", ref_b, tok["b"])):
+        for r, t in out[key]:
+            assert torch.equal(_bits(r.scalars), _bits(ref.scalars)), key
+            assert torch.equal(_bits(r.grad), _bits(ref.grad)), key
+            assert torch.equal(_bits(t.scalars), _bits(rt.scalars)), key
+            assert torch.equal(_bits(t.grad), _bits(rt.grad)), key
