@@ -334,6 +334,15 @@ def test_token_loss_small_ragged(gpu_lib):
     check_token_case(gpu_lib, TOKEN_WORKLOADS["token_loss_ragged"], B=64, T=1000)
 
 
+@pytest.mark.parametrize("T", [65536, 65537])
+@pytest.mark.parametrize("name", ["token_loss_full", "token_loss_ragged"])
+def test_token_loss_long_sequences(gpu_lib, name, T):
+    """Sequences 16 times the benchmark's length: each block walks 16 rounds
+    of its loads (vector path) or 257 strided steps (scalar path, odd T)
+    before the sequence's reductions."""
+    check_token_case(gpu_lib, TOKEN_WORKLOADS[name], B=16, T=T, seed=13)
+
+
 @pytest.mark.parametrize("reduction", ["token_mean", "length_alpha"])
 def test_token_loss_other_reductions(gpu_lib, reduction):
     wl = TOKEN_WORKLOADS["token_loss_ragged"]
