@@ -307,3 +307,19 @@ def test_provenance_fingerprint(monkeypatch):
                   fp(logits="torch.float32"), fp(spp=None, bounds=[0, 8, 16])):
         assert other != base
     assert fp(spp=None, bounds=[0, 8, 16]) != fp(spp=None, bounds=[0, 4, 16])
+
+
+def test_autograd_wrappers_reject_conflicting_arguments():
+    """The autograd entry points take the gradient's scale from the backward
+    pass and return scalars only, so the keywords that would contradict that
+    are rejected before any work is done."""
+    import torch
+    import rl_post_loss_amd as rpl
+    x = torch.zeros((2, 3))
+    for kw in (dict(want_grad=False), dict(grad_scale=x), dict(out=None), dict(per_token=True)):
+        with pytest.raises(ValueError):
+            rpl.grpo_logp_loss(x, x, x, None, None, **kw)
+    with pytest.raises(ValueError):
+        rpl.grpo_loss(x, x, x, x, x, None, precompute_grad=True, grad_scale=x)
+    with pytest.raises(ValueError):
+        rpl.grpo_loss(x, x, x, x, x, None, precompute_grad=True, grad_out=x)
