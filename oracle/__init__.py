@@ -23,6 +23,7 @@ from .grpo_oracle import (  # noqa: F401
     gspo_terms,
     grpo_advantages,
     grpo_loss_fwd_bwd,
+    grpo_loss_rows,
     grpo_token_loss,
     is_weights,
     kl_terms,

@@ -803,7 +803,39 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     if x.ndim != 3:
         raise OracleInputError("policy_logits must be [B, T, V]")
     B, T, V = x.shape
-    _check_cfg(cfg, ref_logits is not None, gen_logps is not None)
+    y = None if ref_logits is None else np.asarray(ref_logits)
+    grad = np.zeros((B, T, V)) if want_grad else None
+
+    def fetch(ii, tt):
+        return x[ii, tt], (None if y is None else y[ii, tt])
+
+    def sink(ii, tt, rows):
+        grad[ii, tt] = rows
+
+    res = grpo_loss_rows(fetch, (B, T, V), action_ids, old_logps, mask, rewards, groups=groups,
+                         cfg=cfg, have_ref=y is not None, grad_scale=grad_scale,
+                         row_chunk=row_chunk, gen_logps=gen_logps, advantages=advantages,
+                         grad_sink=sink if want_grad else None)
+    res.grad = grad
+    return res
+
+
+def grpo_loss_rows(fetch_rows, shape, action_ids, old_logps, mask, rewards, *, groups,
+                   cfg: LossConfig, have_ref=True, grad_scale=1.0, row_chunk=4096,
+                   gen_logps=None, advantages=None, grad_sink=None, map_chunks=map):
+    """The computation of grpo_loss_fwd_bwd over logits that are not held
+    whole: ``fetch_rows(ii, tt)`` returns the policy and reference rows
+    ([n, V] each; the reference None without one) of the active slots
+    (ii, tt), and ``grad_sink(ii, tt, grad_rows)``, if given, receives the
+    gradient rows of those slots instead of a [B, T, V] array.  Chunks of
+    ``row_chunk`` active slots are independent, so ``map_chunks`` (the
+    builtin ``map`` or a thread pool's ``map``) may evaluate them in any
+    order; the per-token values land at their slots and every sum runs in
+    _assemble, so the result does not depend on it.  The returned result's
+    ``grad`` is None; its ``tok`` also holds each active row's policy
+    log-sum-exp (``lse``)."""
+    B, T, V = shape
+    _check_cfg(cfg, have_ref, gen_logps is not None)
     m = np.ones((B, T), dtype=bool) if mask is None else np.asarray(mask).astype(bool)
     A, off, A_slot = _advantage_source(rewards, groups, advantages, B, T, cfg)
     L, N, w = sequence_weights(m, cfg.reduction, cfg.alpha, cfg.norm_constant)
@@ -814,34 +846,47 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, mask, re
     gen = None if gen_logps is None else np.asarray(gen_logps, dtype=np.float64)[ii, tt]
     keep = _keep(B, ii, old, gen, cfg)
     seq_level = cfg.pg_loss in SEQUENCE_PG
-    grad = np.zeros((B, T, V)) if want_grad else None
-    acc = {k: np.zeros(len(ii)) for k in ("rho", "d", "kl", "loss", "dloss", "dkl", "logp", "lse")}
+    keys = ("rho", "d", "kl", "loss", "dloss", "dkl", "logp", "lse", "clipped")
+    acc = {k: np.zeros(len(ii)) for k in keys[:-1]}
     acc["clipped"] = np.zeros(len(ii), dtype=bool)
-    for s in range(0, len(ii), row_chunk):
+    starts = range(0, len(ii), row_chunk)
+
+    def forward_chunk(s):
         sl = slice(s, s + row_chunk)
-        xr = x[ii[sl], tt[sl]]
-        yr = None if ref_logits is None else np.asarray(ref_logits)[ii[sl], tt[sl]]
-        out = logits_rows(xr, yr, ids[sl], old[sl], adv[sl], w[ii[sl]], cfg,
-                          grad_scale, want_grad and not seq_level,
-                          None if gen is None else gen[sl],
+        xr, yr = fetch_rows(ii[sl], tt[sl])
+        rows_grad = grad_sink is not None and not seq_level
+        out = logits_rows(xr, yr, ids[sl], old[sl], adv[sl], w[ii[sl]], cfg, grad_scale,
+                          rows_grad, None if gen is None else gen[sl],
                           None if keep is None else keep[ii[sl]])
-        for k in acc:
-            acc[k][sl] = out[k]
-        if want_grad and not seq_level:
-            grad[ii[sl], tt[sl]] = out["grad"]
+        if rows_grad:
+            grad_sink(ii[sl], tt[sl], out["grad"])
+        return sl, {k: out[k] for k in keys}
+
+    for sl, part in map_chunks(forward_chunk, starts):
+        for k in keys:
+            acc[k][sl] = part[k]
     if seq_level:
         # the policy part needs every log-prob of a sequence: a second pass
         # over the rows writes the gradient once G is known
         _add_sequence_terms(acc, B, ii, acc["logp"], old, gen, A, L, w, off, cfg)
-        if want_grad:
+        if grad_sink is not None:
             G = _token_G(acc, w, ii, cfg, grad_scale)
-            for s in range(0, len(ii), row_chunk):
+
+            def gradient_chunk(s):
                 sl = slice(s, s + row_chunk)
-                grad[ii[sl], tt[sl]] = softmax_grad_rows(x[ii[sl], tt[sl]], ids[sl],
-                                                         acc["lse"][sl], G[sl])
+                xr, _ = fetch_rows(ii[sl], tt[sl])
+                grad_sink(ii[sl], tt[sl], softmax_grad_rows(xr, ids[sl], acc["lse"][sl], G[sl]))
+                return sl
+
+            for _ in map_chunks(gradient_chunk, starts):
+                pass
     acc["adv"] = adv
-    res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=grad,
+    res = _assemble(B, T, ii, tt, acc, A, L, N, w, cfg, grad_scale, grad=None,
                     logp_active=acc["logp"], gen_active=gen, keep=keep)
+    res.grad = None
+    lse = np.zeros((B, T))
+    lse[ii, tt] = acc["lse"]
+    res.tok["lse"] = lse
     return res
 
 

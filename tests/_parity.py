@@ -21,9 +21,12 @@ Three refinements follow from the arithmetic, and every use is counted:
     d close to 0, float32 log-probs (absolute error about 1e-6 at |logp| ~ 12)
     cannot give G to 2^-7; such a row is compared at its propagated error
     bound instead;
-  * objectives whose value depends on the log-prob itself (REINFORCE, CISPO)
-    carry the float32 log-prob error into the loss; where the relative bound
-    fails, the loss is compared at that propagated bound instead.
+  * objectives whose value is linear in the log-prob itself (REINFORCE:
+    -A logp; CISPO: -A sg(clip(rho)) logp) carry the float32 log-prob error
+    (about 2^-19 absolute) into every token's loss at full size, so their
+    summed loss is compared at rtol |loss| plus that propagated error.  For
+    every other objective, the default clipped surrogate with k3 included,
+    the relative bound is enforced outright.
 Branch points and error bounds come from the oracle evaluated at perturbed
 inputs, so they hold for every objective variant.
 """
@@ -180,19 +183,36 @@ def value_bounds(ref, cfg, e_logp=LOGP_ABS_ERR, e_d=2 * LOGP_ABS_ERR):
     return pl, kl
 
 
+# objectives whose per-token value is linear in logp itself, so the float32
+# log-prob error enters the loss value undamped: only these may fall back to
+# the propagated bound (the value of every other objective depends on logp
+# through the ratio or d only)
+VALUE_LINEAR_IN_LOGP = ("reinforce", "cispo")
+
+
 def compare_scalars(res, ref, cfg, loss_rtol, what="", e_logp=LOGP_ABS_ERR,
-                    e_d=2 * LOGP_ABS_ERR):
-    """Scalars and per-sequence totals.  The loss must meet loss_rtol; when an
-    objective's value depends on the log-prob itself (REINFORCE, CISPO), the
-    float32 log-prob error propagated through it is added to the bound, and
-    the returned flag says so."""
+                    e_d=2 * LOGP_ABS_ERR, allow_propagated=None):
+    """Scalars and per-sequence totals.  The loss must meet loss_rtol
+    relative to the oracle's loss.  Only when ``allow_propagated`` (default:
+    the objective is one of VALUE_LINEAR_IN_LOGP) may a loss outside that
+    bound pass at rtol |loss| plus the float32 log-prob error propagated
+    through every token; the returned flag and the printed line say when it
+    did.  Returns (rel, kappa, propagated)."""
+    if allow_propagated is None:
+        allow_propagated = cfg.pg_loss in VALUE_LINEAR_IN_LOGP
     loss = float(res.loss)
     kappa = (np.sum(ref.seq_weight * np.abs(ref.seq_policy)) + 1e-300) / max(abs(ref.loss), 1e-300)
     rel = abs(loss - ref.loss) / max(abs(ref.loss), 1e-300)
     pp, pk = value_bounds(ref, cfg, e_logp, e_d)
     prop_loss = float(np.sum(ref.seq_weight * (pp.sum(axis=1) + cfg.beta * pk.sum(axis=1))))
     propagated = rel > loss_rtol
+    print(f"  [{what}] loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} (bar {loss_rtol:g}) "
+          f"kappa={kappa:.3g} propagated-bound={prop_loss:.3g} "
+          f"{'FALLBACK' if propagated else 'strict'}", flush=True)
     if propagated:
+        assert allow_propagated, (
+            f"{what} loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} > {loss_rtol:g} "
+            f"(kappa={kappa:.3g}; objective {cfg.pg_loss}/{cfg.kl_estimator} has no fallback)")
         lim = loss_rtol * abs(ref.loss) + prop_loss
         assert abs(loss - ref.loss) <= lim, (
             f"{what} loss gpu={loss!r} oracle={ref.loss!r} rel={rel:.3g} kappa={kappa:.3g} "

@@ -1,16 +1,18 @@
-"""Full-size workloads, in the launch configuration bench.py times.
+"""Full-size workloads, in the launch configuration bench.py times, compared
+whole against the fp64 oracle.
 
-The logits workloads are far too large for the fp64 oracle to redo whole
-(10^10 vocabulary entries), so each check uses what the oracle can compute
-one row at a time plus properties that hold at any size:
+The logits workloads (10^10 vocabulary entries) are streamed through the
+oracle a chunk of rows at a time on the host's cores (tests/_fullsize.py):
   * advantages, weights, token counts: bit-exact against the oracle;
-  * sampled rows (first, last, every group, random): log-prob, token loss,
-    k3 and the whole gradient row against the oracle;
-  * the scalars against the fp64 fixed-order sum of the kernel's own
-    per-token outputs (checks the two reduction stages at full size);
-  * every gradient row sums to ~0 (softmax rows sum to one);
+  * the three scalars against the oracle's own scalars at the stated bar
+    (bf16 logits: loss relative error <= 1e-4), per-sequence totals, every
+    active token's log-prob, loss and k3;
+  * every active gradient row against the oracle's row at 2^-7 per element
+    (rows at a clip bound may match either branch, ill-conditioned rows
+    their propagated bound; both are counted and printed);
+  * every masked gradient row is exactly zero, every row sums to ~0;
   * a second call is bit-identical.
-The token-loss workload (4,194,304 tokens) is compared whole.
+The token-loss workload (4,194,304 tokens) is compared whole as well.
 """
 
 import numpy as np
@@ -18,8 +20,9 @@ import pytest
 import torch
 
 import oracle
-from _parity import (LOGP_ABS_ERR, assert_grad_rows_sum_to_zero, cfg_from, compare_exact_parts,
-                     compare_scalars, gpu_kwargs, sample_rows, to_np)
+from _fullsize import masked_rows_zero, stream_oracle
+from _parity import (LOGP_ABS_ERR, assert_grad_rows_sum_to_zero, branch_ambiguity, cfg_from,
+                     compare_exact_parts, compare_scalars, compare_token_values, gpu_kwargs, to_np)
 from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs, make_token_inputs
 
 pytestmark = pytest.mark.gpu
@@ -41,86 +44,40 @@ def test_fullsize_logits(gpu_lib, name, reduction):
     rpl = gpu_lib
     wl = WORKLOADS[name]
     red = reduction or wl.reductions[0]
-    announce(f"full size {name} {red}: generating")
+    what = f"{name} {red}"
+    announce(f"full size {what}: generating")
     inp = make_logits_inputs(wl, device=DEV, seed=0)
     B, T, V = wl.B, wl.T, wl.V
     kw = gpu_kwargs(wl, red)
     grad = torch.empty((B, T, V), dtype=inp["policy"].dtype, device=DEV)
-    announce(f"full size {name} {red}: run 1")
+    announce(f"full size {what}: run 1")
     res = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
                                 inp["rewards"], inp["mask"], grad_out=grad, per_token=True, **kw)
     torch.cuda.synchronize()
     assert int(res.status[0]) == 0
 
-    mask = inp["mask"].cpu().numpy()
-    rewards = inp["rewards"].cpu().numpy()
     cfg = cfg_from(wl, red)
-    groups = wl.groups_kwargs()
-    off = oracle.group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
-    A = oracle.group_advantages(rewards, off, wl.leave_one_out, wl.scale_by_std)
-    L, N, w = oracle.sequence_weights(mask, cfg.reduction, cfg.alpha)
-    gA = to_np(res.advantages)
-    assert np.array_equal(gA.astype(np.float32).view(np.uint32), A.astype(np.float32).view(np.uint32))
-    assert np.array_equal(to_np(res.seq_weight).astype(np.float32).view(np.uint32),
-                          w.astype(np.float32).view(np.uint32))
-    assert np.array_equal(to_np(res.seq_tokens), L) and int(res.counts[0]) == N
+    mask = inp["mask"].cpu().numpy().astype(bool)
+    ref, st = stream_oracle(inp, grad, wl, cfg, wl.groups_kwargs(), announce=announce)
+    announce(f"full size {what}: oracle done, {st}")
+    compare_exact_parts(res, ref, what)
+    compare_scalars(res, ref, cfg, 1e-4, what)
+    compare_token_values(res, ref, cfg, mask, 1e-4)
+    glp = to_np(res.tok_logp)
+    assert np.all(np.abs(glp - ref.tok["logp"])[mask] <= LOGP_ABS_ERR), what
+    flag, _, _ = branch_ambiguity(ref, cfg, mask)
+    clipped = int(res.counts[1])
+    assert abs(clipped - ref.clipped) <= int(flag.sum()), (clipped, ref.clipped, int(flag.sum()))
+    announce(f"full size {what}: clipped gpu={clipped} oracle={ref.clipped} "
+             f"ambiguous={int(flag.sum())}")
 
-    # scalars against the fixed-order fp64 sum of the kernel's per-token values
-    tl = to_np(res.tok_loss)
-    tk = to_np(res.tok_kl)
-    P = tl.sum(axis=1)
-    K = tk.sum(axis=1)
-    pl = float(np.sum(w * P))
-    kl = float(np.sum(w * K))
-    for got, want in ((float(res.policy_loss), pl), (float(res.kl), kl),
-                      (float(res.loss), pl + wl.beta * kl)):
-        assert abs(got - want) <= 2e-7 * max(abs(want), 1e-30) + 1e-12, (got, want)
-    assert np.allclose(to_np(res.seq_policy), P, rtol=1e-6, atol=1e-9)
-    assert np.allclose(to_np(res.seq_kl), K, rtol=1e-6, atol=1e-9)
-
-    # sampled rows against the oracle
-    rng = np.random.default_rng(1)
-    rows = sample_rows(B, T, mask, rng)
-    announce(f"full size {name} {red}: {len(rows)} sampled rows")
-    pol = inp["policy"].view(B * T, V)
-    ref = inp["ref"].view(B * T, V)
-    ids = inp["action_ids"].view(-1).cpu().numpy()
-    old = inp["old_logps"].view(-1).cpu().numpy()
-    g2 = grad.view(B * T, V)
-    mflat = mask.reshape(-1)
-    glp = to_np(res.tok_logp).reshape(-1)
-    for r in rows:
-        i = r // T
-        g_row = g2[r].double().cpu().numpy()
-        if not mflat[r]:
-            assert np.all(g_row == 0.0) and tl.reshape(-1)[r] == 0.0
-            continue
-        x = pol[r].float().cpu().numpy()[None]
-        y = ref[r].float().cpu().numpy()[None]
-        o = oracle.logits_rows(x, y, ids[r:r + 1], old[r:r + 1], A[i:i + 1], w[i:i + 1], cfg)
-        assert abs(glp[r] - o["logp"][0]) <= LOGP_ABS_ERR, (r, glp[r], o["logp"][0])
-        lo, hi = 1 - cfg.eps_low, 1 + cfg.eps_high
-        rho = o["rho"][0]
-        ambiguous = min(abs(rho - lo), abs(rho - hi)) <= rho * 4 * LOGP_ABS_ERR
-        if ambiguous:
-            continue
-        # token loss / k3 within the propagated float32 log-prob error
-        assert abs(tl.reshape(-1)[r] - o["loss"][0]) <= 2 * LOGP_ABS_ERR * abs(A[i]) * rho + 1e-6
-        assert abs(tk.reshape(-1)[r] - o["kl"][0]) <= 2 * LOGP_ABS_ERR * abs(np.expm1(o["d"][0])) + 1e-7
-        # gradient row, bf16 criterion (with the ill-conditioned-G allowance)
-        G = o["G"][0]
-        dG = abs(w[i]) * (abs(A[i]) * rho + 2 * cfg.beta * np.exp(o["d"][0])) * 2 * LOGP_ABS_ERR
-        tol = max(2.0 ** -7, dG / abs(G)) if G != 0 else 0.0
-        gr = o["grad"][0]
-        err = np.abs(g_row - gr)
-        assert np.all(err <= tol * np.abs(gr) + 2.0 ** -126), (r, float(np.max(err / (np.abs(gr) + 1e-300))))
-
+    assert masked_rows_zero(grad, inp["mask"]), what
     # every gradient row sums to ~0: G * (1 - sum p); bf16 rounding bounds the rest
-    announce(f"full size {name} {red}: row sums")
-    assert_grad_rows_sum_to_zero(g2)
+    announce(f"full size {what}: row sums")
+    assert_grad_rows_sum_to_zero(grad.view(B * T, V))
 
     # bit-identical second run
-    announce(f"full size {name} {red}: run 2")
+    announce(f"full size {what}: run 2")
     grad2 = torch.empty_like(grad)
     res2 = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
                                  inp["rewards"], inp["mask"], grad_out=grad2, **kw)
@@ -148,6 +105,7 @@ def test_fullsize_token_loss(gpu_lib, name):
                                  groups=dict(samples_per_prompt=wl.group_size), cfg=cfg)
     compare_exact_parts(res, ref, name)
     compare_scalars(res, ref, cfg, 1e-5, name)
+    compare_token_values(res, ref, cfg, h["mask"].astype(bool), 1e-5)
     g = to_np(res.grad)
     rho = ref.tok["rho"]
     lo, hi = 1 - wl.eps_low, 1 + wl.eps_high

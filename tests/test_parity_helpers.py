@@ -248,3 +248,60 @@ def test_seq_branch_flip_rejected_away_from_bounds_accepted_at_a_bound():
     stats = compare_logits_grad(unclipped_rows(ref2, ref2.grad.copy()), ref2, cfg, mask, "f32",
                                 policy=x, ids=ids, branches=br2)
     assert stats["ambiguous"] >= 1
+
+
+def _bf16_case(seed=5):
+    """A small bf16 batch in the shape of the full-size inputs (torch tensors)."""
+    x, y, ids, old, mask, r = _case(seed, B=8, T=10, V=300)
+    t = dict(policy=torch.tensor(x, dtype=torch.bfloat16), ref=torch.tensor(y, dtype=torch.bfloat16),
+             action_ids=torch.tensor(ids), old_logps=torch.tensor(old, dtype=torch.float32),
+             mask=torch.tensor(mask), rewards=torch.tensor(r, dtype=torch.float32))
+    return t
+
+
+def test_stream_oracle_accepts_rounded_oracle_and_rejects_a_bad_row():
+    """The whole-batch streaming comparison (tests/_fullsize.py) equals the
+    in-memory oracle, accepts the oracle's own gradient rounded to bf16 and
+    rejects one row off by 5 %."""
+    from _fullsize import masked_rows_zero, stream_oracle
+    t = _bf16_case()
+    cfg = oracle.LossConfig(eps_low=0.2, eps_high=0.28, beta=0.04)
+    groups = dict(samples_per_prompt=4)
+    h = {k: (v.float().numpy() if v.is_floating_point() else v.numpy()) for k, v in t.items()}
+    want = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
+                                    h["mask"], h["rewards"], groups=groups, cfg=cfg)
+    grad = torch.tensor(want.grad).to(torch.bfloat16)
+    wl = SimpleNamespace()
+    got, st = stream_oracle(t, grad, wl, cfg, groups, chunk=3, workers=3, announce=lambda m: None)
+    assert got.loss == want.loss and np.array_equal(got.tok["G"], want.tok["G"])
+    assert st["rows"] == int(h["mask"].sum())
+    assert masked_rows_zero(grad, t["mask"])
+    i, tt = np.argwhere(h["mask"])[len(np.argwhere(h["mask"])) // 2]
+    bad = grad.clone()
+    bad[i, tt] = (bad[i, tt].float() * 1.05).to(torch.bfloat16)
+    with pytest.raises(AssertionError):
+        stream_oracle(t, bad, wl, cfg, groups, chunk=3, workers=3, announce=lambda m: None)
+    # a nonzero masked row is caught
+    mi, mt = np.argwhere(~h["mask"])[0]
+    bad = grad.clone()
+    bad[mi, mt, 0] = 1.0
+    assert not masked_rows_zero(bad, t["mask"])
+
+
+def test_loss_bar_is_strict_for_the_clipped_surrogate():
+    """A loss 2e-4 off in relative terms fails the bf16 bar of the default
+    objective, however large the propagated log-prob error would be; CISPO
+    (value linear in logp) may still fall back to that propagated bound."""
+    x, y, ids, old, mask, r = _case(4)
+    for pg, ok in (("clip", False), ("cispo", True)):
+        cfg = oracle.LossConfig(beta=0.1, pg_loss=pg)
+        ref = oracle.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=dict(samples_per_prompt=2),
+                                       cfg=cfg)
+        res = _as_result(ref)
+        res.loss = torch.tensor(ref.loss * (1 + 2e-4), dtype=torch.float32)
+        # a huge log-prob error budget would cover the 2e-4 for either objective
+        if ok:
+            compare_scalars(res, ref, cfg, 1e-4, e_logp=1e-2, e_d=1e-2)
+        else:
+            with pytest.raises(AssertionError):
+                compare_scalars(res, ref, cfg, 1e-4, e_logp=1e-2, e_d=1e-2)
