@@ -7,7 +7,9 @@
  * `void *stream`, a hipStream_t; NULL selects the default stream) and never
  * synchronises the host; results are valid once the stream reaches them.
  * The library never allocates or frees memory: the caller owns every buffer,
- * including the workspace sized by grpo_workspace_bytes().
+ * including the workspace sized by grpo_workspace_bytes().  (The one entry
+ * point without a workspace argument, grpo_loss_fwd_bwd_noalloc, uses a
+ * fixed array that the library's code object holds on each GPU.)
  *
  * What is computed follows these pages (cited by title and section):
  *   [GRPO-LOSS]  RL-Kernel docs, "GRPO Loss": Entry Point, Group
@@ -84,7 +86,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 6
+#define GRPO_ABI_VERSION 7
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -407,6 +409,39 @@ GRPO_API grpo_status grpo_loss_fwd_bwd(const void *policy_logits, const void *re
                               int32_t grad_dtype, int64_t grad_row_stride,
                               const float *grad_scale, const grpo_outputs *out, void *ws,
                               size_t ws_bytes, void *stream);
+
+/* Size of the library's own scratch array that grpo_loss_fwd_bwd_noalloc
+ * uses as its workspace: 8 MiB on every GPU the library runs on, held until
+ * the process ends.  It covers grpo_workspace_bytes(B, T, num_groups) up to
+ * that size, about 280,000 token slots (B * T). */
+#define GRPO_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* grpo_loss_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing (no hipMalloc, no
+ * allocating library routine); the workspace is the library's static scratch
+ * array of GRPO_NOALLOC_SCRATCH_BYTES on the GPU that runs `stream` (the
+ * current GPU for the null stream), whose device address is looked up once
+ * per GPU on the first call there.  Every other argument, output and error is
+ * as for grpo_loss_fwd_bwd; in addition it returns GRPO_ERR_WORKSPACE,
+ * without launching anything, when grpo_workspace_bytes(B, T, num_groups)
+ * exceeds GRPO_NOALLOC_SCRATCH_BYTES.  The scratch array keeps the last
+ * call's contents; no result depends on them (every value is written before
+ * it is read).  All calls on one GPU share that one array: calls that can
+ * overlap on a GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  With grad_out == NULL it runs the forward only;
+ * grpo_loss_bwd cannot follow it (that takes a caller's workspace). */
+GRPO_API grpo_status grpo_loss_fwd_bwd_noalloc(const void *policy_logits, const void *ref_logits,
+                                               int32_t logits_dtype, int64_t row_stride,
+                                               const void *action_ids, int32_t ids_dtype,
+                                               const float *old_logps, const float *gen_logps,
+                                               const uint8_t *mask, const float *rewards,
+                                               const float *token_advantages, int64_t B, int64_t T,
+                                               int64_t V, const grpo_groups *groups,
+                                               const grpo_cfg *cfg, void *grad_out,
+                                               int32_t grad_dtype, int64_t grad_row_stride,
+                                               const float *grad_scale, const grpo_outputs *out,
+                                               void *stream);
 
 /* Backward of a preceding grpo_loss_fwd_bwd(..., grad_out = NULL, ...) call on
  * the same workspace and the same policy_logits/action_ids/mask/sizes:

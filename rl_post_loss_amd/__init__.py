@@ -19,6 +19,7 @@ from .loss import (  # noqa: F401
     grpo_loss,
     grpo_loss_bwd,
     grpo_loss_fwd_bwd,
+    grpo_loss_fwd_bwd_noalloc,
     grpo_logp_loss,
     grpo_scale_grad,
     grpo_token_advantages,

@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 6
+GRPO_ABI_VERSION = 7
 
 GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
@@ -24,6 +24,9 @@ ADV_ESTIMATOR_CODES = {"reinforce_pp": 0, "reinforce_pp_baseline": 1}
 GRPO_FAULT_BAD_ACTION = 1
 GRPO_FAULT_NO_TOKENS = 2
 GRPO_FAULT_NONFINITE = 4
+
+# bytes of the library's scratch array (GRPO_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 STATUS_NAMES = {0: "GRPO_OK", 1: "GRPO_ERR_NULL", 2: "GRPO_ERR_SHAPE", 3: "GRPO_ERR_DTYPE",
                 4: "GRPO_ERR_GROUPS", 5: "GRPO_ERR_CONFIG", 6: "GRPO_ERR_WORKSPACE",
@@ -70,6 +73,9 @@ SIGNATURES = {
     "grpo_loss_fwd_bwd": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64,
                                     C.POINTER(GrpoGroups), C.POINTER(GrpoCfg), vp, i32, i64, vp,
                                     C.POINTER(GrpoOutputs), vp, sz, vp]),
+    "grpo_loss_fwd_bwd_noalloc": (C.c_int, [vp, vp, i32, i64, vp, i32, vp, vp, vp, vp, vp, i64,
+                                            i64, i64, C.POINTER(GrpoGroups), C.POINTER(GrpoCfg),
+                                            vp, i32, i64, vp, C.POINTER(GrpoOutputs), vp]),
     "grpo_loss_bwd": (C.c_int, [vp, i32, i64, vp, i32, vp, i64, i64, i64, vp, i32, i64, vp, vp,
                                 sz, vp]),
     "grpo_scale_grad": (C.c_int, [vp, i32, i64, i64, i64, vp, vp]),

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/grpo.h"
@@ -380,6 +382,42 @@ grpo_status run_sequence_phase(const Ws& w, const grpo_cfg* cfg, const grpo_grou
   return launch_real(r, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
 }
 
+// Workspace of grpo_loss_fwd_bwd_noalloc, for callers that cannot allocate:
+// one array per GPU, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: host code uses only
+// the per-device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[GRPO_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+grpo_status scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return GRPO_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return GRPO_ERR_HIP;
+    dev = int(d);
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return GRPO_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return GRPO_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return GRPO_ERR_HIP;
+    if (e != hipSuccess || !p) return GRPO_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GRPO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -560,15 +598,17 @@ static bool rows_vectorizable(const void* x, const void* y, int64_t ld, int32_t 
   return true;
 }
 
-grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
-                              int32_t logits_dtype, int64_t row_stride, const void* action_ids,
-                              int32_t ids_dtype, const float* old_logps, const float* gen_logps,
-                              const uint8_t* mask, const float* rewards,
-                              const float* token_advantages, int64_t B, int64_t T,
-                              int64_t V, const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
-                              int32_t grad_dtype, int64_t grad_row_stride,
-                              const float* grad_scale, const grpo_outputs* out, void* ws,
-                              size_t ws_bytes, void* stream) {
+// Both logits entry points: validates everything, then (ws == NULL) takes
+// the library's scratch array as the workspace, then launches.
+static grpo_status loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
+                                int32_t logits_dtype, int64_t row_stride, const void* action_ids,
+                                int32_t ids_dtype, const float* old_logps, const float* gen_logps,
+                                const uint8_t* mask, const float* rewards,
+                                const float* token_advantages, int64_t B, int64_t T, int64_t V,
+                                const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
+                                int32_t grad_dtype, int64_t grad_row_stride,
+                                const float* grad_scale, const grpo_outputs* out, void* ws,
+                                size_t ws_bytes, bool use_scratch, void* stream) {
   if (!old_logps || !out || !out->scalars) return GRPO_ERR_NULL;
   int64_t rows = 0;
   grpo_status st = logits_common_checks(policy_logits, logits_dtype, row_stride, action_ids,
@@ -584,10 +624,20 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
                    grad_dtype, grad_row_stride);
   if (st != GRPO_OK) return st;
   const int32_t ng = group_count_csr(groups);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_scratch) {
+    // every argument is valid: refuse sizes beyond the scratch array before
+    // touching the device, then take this device's copy of it
+    const size_t need = grpo_workspace_bytes(B, T, ng);
+    if (need == 0) return GRPO_ERR_SHAPE;
+    if (need > GRPO_NOALLOC_SCRATCH_BYTES) return GRPO_ERR_WORKSPACE;
+    st = scratch_for_stream(s, &ws);
+    if (st != GRPO_OK) return st;
+    ws_bytes = GRPO_NOALLOC_SCRATCH_BYTES;
+  }
   Ws w;
   st = check_ws(ws, ws_bytes, B, T, ng, &w);
   if (st != GRPO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   st = run_prep(w, rewards, mask, B, T, groups, cfg, true, out, nullptr, s, old_logps, gen_logps);
   if (st != GRPO_OK) return st;
@@ -677,6 +727,37 @@ grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
   r.seq_kl = out->seq_kl;
   if (launch_reduce(r, s) != hipSuccess) return GRPO_ERR_HIP;
   return run_final(w, B, cfg->beta, out, s);
+}
+
+grpo_status grpo_loss_fwd_bwd(const void* policy_logits, const void* ref_logits,
+                              int32_t logits_dtype, int64_t row_stride, const void* action_ids,
+                              int32_t ids_dtype, const float* old_logps, const float* gen_logps,
+                              const uint8_t* mask, const float* rewards,
+                              const float* token_advantages, int64_t B, int64_t T,
+                              int64_t V, const grpo_groups* groups, const grpo_cfg* cfg, void* grad_out,
+                              int32_t grad_dtype, int64_t grad_row_stride,
+                              const float* grad_scale, const grpo_outputs* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return loss_fwd_bwd(policy_logits, ref_logits, logits_dtype, row_stride, action_ids, ids_dtype,
+                      old_logps, gen_logps, mask, rewards, token_advantages, B, T, V, groups, cfg,
+                      grad_out, grad_dtype, grad_row_stride, grad_scale, out, ws, ws_bytes, false,
+                      stream);
+}
+
+grpo_status grpo_loss_fwd_bwd_noalloc(const void* policy_logits, const void* ref_logits,
+                                      int32_t logits_dtype, int64_t row_stride,
+                                      const void* action_ids, int32_t ids_dtype,
+                                      const float* old_logps, const float* gen_logps,
+                                      const uint8_t* mask, const float* rewards,
+                                      const float* token_advantages, int64_t B, int64_t T,
+                                      int64_t V, const grpo_groups* groups, const grpo_cfg* cfg,
+                                      void* grad_out, int32_t grad_dtype, int64_t grad_row_stride,
+                                      const float* grad_scale, const grpo_outputs* out,
+                                      void* stream) {
+  return loss_fwd_bwd(policy_logits, ref_logits, logits_dtype, row_stride, action_ids, ids_dtype,
+                      old_logps, gen_logps, mask, rewards, token_advantages, B, T, V, groups, cfg,
+                      grad_out, grad_dtype, grad_row_stride, grad_scale, out, nullptr, 0, true,
+                      stream);
 }
 
 grpo_status grpo_loss_bwd(const void* policy_logits, int32_t logits_dtype, int64_t row_stride,

@@ -464,7 +464,7 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                       leave_one_out=False, scale_by_std=True, std_eps=1e-6,
                       reduction="token_mean", alpha=None, grad_out=None, grad_dtype=None,
                       grad_scale=None, per_token=False, out=None, _ws=None,
-                      token_advantages=None, adv_clip=None, **objective):
+                      token_advantages=None, adv_clip=None, _noalloc=False, **objective):
     """Fused forward + analytic backward from [B, T, V] logits.
 
     grad_out: None allocates a contiguous gradient (dtype ``grad_dtype``,
@@ -514,18 +514,22 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
               and grad_out.device == dev, "grad_out must be float32/bfloat16/float16 [B, T, V]")
         gptr, gdt_code, gld = grad_out.data_ptr(), _FDTYPE[grad_out.dtype], _row_stride(grad_out, "grad_out")
         res.grad = grad_out
-    if _ws is None:
-        ws, wsb = workspace(B, T, ng, dev)
+    args = (policy_logits.data_ptr(), _ptr(ref_logits), _FDTYPE[policy_logits.dtype], ld,
+            action_ids.data_ptr(), _IDTYPE[action_ids.dtype], old_logps.data_ptr(),
+            _ptr(gen_logps), mptr, rptr, aptr, B, T, V, None if g is None else C.byref(g),
+            C.byref(cfg), gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o))
+    if _noalloc:
+        entry = "grpo_loss_fwd_bwd_noalloc"
+        with torch.cuda.device(dev):
+            check(lib.grpo_loss_fwd_bwd_noalloc(*args, _stream_ptr(dev)), lib)
     else:
-        ws, wsb = _ws
-    check(lib.grpo_loss_fwd_bwd(policy_logits.data_ptr(), _ptr(ref_logits),
-                                _FDTYPE[policy_logits.dtype], ld, action_ids.data_ptr(),
-                                _IDTYPE[action_ids.dtype], old_logps.data_ptr(),
-                                _ptr(gen_logps), mptr, rptr, aptr, B, T, V,
-                                None if g is None else C.byref(g), C.byref(cfg),
-                                gptr, gdt_code, gld, _ptr(grad_scale), C.byref(o), ws.data_ptr(),
-                                wsb, _stream_ptr(dev)), lib)
-    res._prov = ("grpo_loss_fwd_bwd", dict(B=B, T=T, V=V),
+        entry = "grpo_loss_fwd_bwd"
+        if _ws is None:
+            ws, wsb = workspace(B, T, ng, dev)
+        else:
+            ws, wsb = _ws
+        check(lib.grpo_loss_fwd_bwd(*args, ws.data_ptr(), wsb, _stream_ptr(dev)), lib)
+    res._prov = (entry, dict(B=B, T=T, V=V),
                  dict(logits=str(policy_logits.dtype), action_ids=str(action_ids.dtype),
                       grad=None if grad_out is False else str(grad_out.dtype)),
                  cfg, g, group_boundaries,
@@ -534,6 +538,21 @@ def grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
                       grad_scale=grad_scale is not None, mask=completion_mask is not None),
                  dev)
     return res
+
+
+def grpo_loss_fwd_bwd_noalloc(policy_logits, ref_logits, action_ids, old_logps, rewards,
+                              completion_mask=None, **kw):
+    """grpo_loss_fwd_bwd through the C entry point that takes no workspace
+    (for callers that cannot allocate device memory): the library's static
+    scratch array on the tensors' GPU serves as the workspace, so nothing is
+    allocated beyond the outputs; pass ``grad_out`` and ``out`` (a previous
+    result of the same sizes) to allocate nothing at all.  Calls that may
+    overlap on one GPU share that array and must be ordered by the caller.
+    Sizes beyond the array (rl_post_loss_amd._abi.NOALLOC_SCRATCH_BYTES of
+    workspace) raise GrpoError (GRPO_ERR_WORKSPACE)."""
+    _need("_ws" not in kw, "the no-allocation entry point takes no workspace")
+    return grpo_loss_fwd_bwd(policy_logits, ref_logits, action_ids, old_logps, rewards,
+                             completion_mask, _noalloc=True, **kw)
 
 
 def grpo_loss_bwd(policy_logits, action_ids, completion_mask, ws, *, grad_out=None,

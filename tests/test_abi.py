@@ -323,3 +323,39 @@ def test_autograd_wrappers_reject_conflicting_arguments():
         rpl.grpo_loss(x, x, x, x, x, None, precompute_grad=True, grad_scale=x)
     with pytest.raises(ValueError):
         rpl.grpo_loss(x, x, x, x, x, None, precompute_grad=True, grad_out=x)
+
+
+def _fwd_noalloc(lib, B=8, T=4, V=32, g=None, cfg=None, scalars=FAKE, grad=FAKE + 0x4000000,
+                 ld=None):
+    if g is None:
+        g, _ = _groups()
+    cfg = cfg or _cfg()
+    o = _abi.GrpoOutputs()
+    o.scalars = scalars
+    return lib.grpo_loss_fwd_bwd_noalloc(FAKE, FAKE, 0, ld or V, FAKE, 0, FAKE, None, None, FAKE,
+                                         None, B, T, V, C.byref(g), C.byref(cfg), grad, 0, V,
+                                         None, C.byref(o), None)
+
+
+@cpu_only
+def test_noalloc_argument_validation():
+    """The entry point without a workspace validates every argument as
+    grpo_loss_fwd_bwd does and refuses sizes whose workspace exceeds the
+    library's scratch array, all before touching a device."""
+    lib = rpl.load_library()
+    E = {v: k for k, v in _abi.STATUS_NAMES.items()}
+    assert _fwd_noalloc(lib, scalars=None) == E["GRPO_ERR_NULL"]
+    assert _fwd_noalloc(lib, B=0) == E["GRPO_ERR_SHAPE"]
+    assert _fwd_noalloc(lib, ld=16) == E["GRPO_ERR_SHAPE"]
+    assert _fwd_noalloc(lib, cfg=_cfg(lo=1.0)) == E["GRPO_ERR_CONFIG"]
+    g, _ = _groups(spp=3)
+    assert _fwd_noalloc(lib, g=g) == E["GRPO_ERR_GROUPS"]
+    # the largest T whose workspace fits, and one past it
+    B = 8
+    fits = max(t for t in (1 << k for k in range(10, 24))
+               if lib.grpo_workspace_bytes(B, t, 0) <= _abi.NOALLOC_SCRATCH_BYTES)
+    assert lib.grpo_workspace_bytes(B, 2 * fits, 0) > _abi.NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(lib, B=B, T=2 * fits, V=1) == E["GRPO_ERR_WORKSPACE"]
+    assert _fwd_noalloc(lib, B=1024, T=4096, V=1) == E["GRPO_ERR_WORKSPACE"]
+    # the stated capacity: about 280,000 slots
+    assert 200_000 <= B * fits * 2 and lib.grpo_workspace_bytes(1, 280_000, 0) <= 8 << 20

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from _parity import cfg_from, compare_logits_grad, compare_scalars, gpu_kwargs, host_inputs, to_np
+from rl_post_loss_amd._abi import GRPO_ABI_VERSION
 from workloads import WORKLOADS, LogitsWorkload, make_logits_inputs, poison_masked
 
 pytestmark = pytest.mark.gpu
@@ -373,7 +374,7 @@ def test_result_provenance(gpu_lib):
     announce("provenance")
     _, inp = _inputs(wl, seed=41)
     a = _call(gpu_lib, inp, wl).provenance
-    assert a["entry"] == "grpo_loss_fwd_bwd" and a["abi_version"] == 6
+    assert a["entry"] == "grpo_loss_fwd_bwd" and a["abi_version"] == GRPO_ABI_VERSION
     assert a["sizes"] == dict(B=wl.B, T=4, V=1000) and a["dtypes"]["logits"] == "torch.float32"
     assert a["groups"]["samples_per_prompt"] == 4 and a["device"]
     _, inp2 = _inputs(_wl(1000, "f32", T=9), seed=42)
