@@ -1,30 +1,35 @@
 """Benchmark of the GRPO loss hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--objective NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--objective NAME]
 
-One step is one grpo_loss_fwd_bwd call (advantages and weights, the fused
-vocabulary pass with the analytic gradient, the fixed-order reductions) over
-one batch of synthetic inputs already resident in HBM.  The default workload
-is the Qwen-size vocabulary: B = 32 (4 prompts x 8 samples), T = 2048,
-V = 151,936, bf16 logits, full mask, token-mean reduction.
+One step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: advantages and weights, the fused vocabulary pass
+with the analytic gradient, the fixed-order reductions
+(grpo_loss_fwd_bwd); for the log-prob workloads one grpo_token_loss call.
 
-Prints one JSON line with tokens/s (all B*T slots per second), the roofline of
-the vocabulary kernel (algorithmic bytes over its own HIP-event-timed
-duration, against 8 TB/s HBM), and the fp64 CPU oracle's rate on a bounded
-sample of the same workload.
+The default (``--workload all``) prints ONE JSON line whose headline is the
+Qwen-size vocabulary (B = 32 as 4 prompts x 8 samples, T = 2048,
+V = 151,936, bf16 logits, full mask, token mean) and whose ``configs`` holds
+one record per other workload: the tiny f32 batch, the 4,194,304-token loss
+(full and ragged masks), the V = 32,000 batch and the CSR V = 128,256 batch
+under the token mean, the sequence mean and length^0.5.  Every record has
+tokens/s, a ``roofline`` block for its dominant kernel (algorithmic bytes
+over that kernel's own HIP-event-timed duration, against 8 TB/s HBM, plus
+HBM traffic from committed rocprofv3 counter summaries when they match the
+current sources) and a ``cpu_baseline``: the fp64 oracle, as it stands, on
+a bounded sample of the same batch over the host's cores (worker processes
+started before the GPU is touched).
 
---objective selects another per-token or sequence-level objective on the same
-workload (default: the clipped surrogate with k3 the workload names).  The
-sequence-level ones (gspo, real) run a forward row pass, the per-sequence
-phase and a gradient pass; the timed "vocabulary kernel" then spans all three
-and the byte model is unchanged (policy read twice, reference once, gradient
-written once).
+--workload NAME runs one workload alone (one line); --objective selects
+another objective on a logits workload.  The sequence-level objectives
+(gspo, real) run a forward row pass, the per-sequence phase and a gradient
+pass; the timed kernel then spans all three.
 
 Auxiliary modes (for the HBM-traffic counters, see profiles/):
   --calibrate-only       run only a plain elementwise kernel over 2 GiB that
                          reads and writes known bytes (counter scale)
-  --summarize-pmc F W CF CW
-                         write profiles/<kernel>_<workload>_pmc.json from four
+  --summarize-pmc F W CF CW --kernel K
+                         write profiles/<K>_<workload>_pmc.json from four
                          rocprofv3 --pmc csv runs: FETCH_SIZE and WRITE_SIZE of
                          the bench, then of the calibration run
 """
@@ -37,6 +42,7 @@ import hashlib
 import json
 import os
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -45,12 +51,13 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "tokens/s for fused GRPO fwd+bwd from [B,T,V] logits; % of MI355X peak HBM GB/s"
-ROW_KERNEL = "grpo_rows_kernel"
 KERNEL_SOURCES = ["rl_post_loss_amd/csrc/grpo_rows.hip", "rl_post_loss_amd/csrc/grpo_rows_resident.hip",
                   "rl_post_loss_amd/csrc/grpo_rowcore.hpp", "rl_post_loss_amd/csrc/grpo_device.hpp",
                   "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_objective.hpp",
+                  "rl_post_loss_amd/csrc/grpo_reduce.hip", "rl_post_loss_amd/csrc/grpo_adv.hip",
                   "rl_post_loss_amd/csrc/grpo_api.hip"]
 CALIB_BYTES = 1 << 31   # 2 GiB copy for counter calibration
+MAX_WORKERS = 16        # host processes for the oracle (the machine's CPU share per GPU)
 
 # objective presets: (keyword overrides, needs generating log-probs)
 OBJECTIVES = {
@@ -70,88 +77,213 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def byte_model(wl, mask_active_rows, rows):
-    """Algorithmic HBM bytes of one vocabulary-kernel launch: every active row
-    reads the policy row twice and the reference row once and writes the
-    gradient row once; a masked row only writes its zero gradient; plus the
-    per-slot side inputs (action id, old log-prob, mask byte)."""
+# ---------------------------------------------------------------------------
+# Byte models (algorithmic bytes per launch of the dominant kernel)
+# ---------------------------------------------------------------------------
+
+def byte_model(wl, active, rows):
+    """The stated model of the fused logits call: every active row reads the
+    policy row twice and the reference row once and writes the gradient row
+    once; a masked row only writes its zero gradient; plus the per-slot side
+    inputs (int64 action id, float32 old log-prob, mask byte)."""
     bx = 4 if wl.dtype == "f32" else 2
     bg = bx
     V = wl.V
-    ids_bytes = 8
-    side = rows * (ids_bytes + 4 + 1)
-    return mask_active_rows * V * (3 * bx + bg) + (rows - mask_active_rows) * V * bg + side
+    return active * V * (3 * bx + bg) + (rows - active) * V * bg + rows * (8 + 4 + 1)
 
 
-def cpu_baseline(wl, inp, target_s=12.0, rows_per_chunk=32):
-    """The fp64 oracle as it stands, on successive row chunks of this batch
-    until about ``target_s`` seconds of host compute have run."""
+def min_bytes(wl, active, rows, resident):
+    """The bytes the chosen row kernel must move at least: the resident kernel
+    reads each active policy row once (policy + reference + gradient), the
+    streaming kernel twice (the byte model itself)."""
+    if not resident:
+        return byte_model(wl, active, rows)
+    bx = 4 if wl.dtype == "f32" else 2
+    V = wl.V
+    return active * V * (2 * bx + bx) + (rows - active) * V * bx + rows * (8 + 4 + 1)
+
+
+def token_bytes(active, rows):
+    """Log-prob token loss: an active token reads logp, old and ref (f32) and
+    the mask byte and writes dlogp (17 B); a masked one reads its mask byte
+    and writes a zero (5 B)."""
+    return active * 17 + (rows - active) * 5
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on a bounded sample of the same
+# batch, spread over worker processes (started before the GPU is touched).
+# ---------------------------------------------------------------------------
+
+def host_workers():
+    return max(1, min(MAX_WORKERS, len(os.sched_getaffinity(0))))
+
+
+def under_profiler():
+    """True when a profiler's library is preloaded into this process (it may
+    have initialised the GPU before main, so no worker process is started)."""
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return True
+    return "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
+def start_pool(workers):
+    """Worker processes for the oracle, spawned before this process touches
+    the GPU (the children never do)."""
+    import multiprocessing
+    ctx = multiprocessing.get_context("spawn")
+    pool = ctx.Pool(workers)
+    pool.map(_worker_warm, range(workers))   # imports done before anything is timed
+    return pool
+
+
+def _worker_warm(_):
+    import numpy  # noqa: F401
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def _cfg_of(d):
+    import oracle
+    return oracle.LossConfig(**d)
+
+
+def _rows_job(job):
+    """Worker: the oracle's forward and gradient over one chunk of active rows
+    (policy and reference rows read from the shared float32 sample files)."""
     import numpy as np
     import oracle
-    h_mask = inp["mask"].cpu().numpy()
+    xpath, ypath, shape, s, e, ids, old, adv, w, cfg = job
+    x = np.load(xpath, mmap_mode="r")[s:e]
+    y = np.load(ypath, mmap_mode="r")[s:e]
+    oracle.logits_rows(x, y, ids, old, adv, w, _cfg_of(cfg))
+    return e - s
+
+
+def _token_job(job):
+    """Worker: the oracle's log-prob token loss over whole groups."""
+    import oracle
+    h, spp, cfg = job
+    oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                           groups=dict(samples_per_prompt=spp), cfg=_cfg_of(cfg))
+    return h["mask"].size
+
+
+def _cfg_dict(wl, reduction, obj):
+    d = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=reduction,
+             alpha=wl.alpha if reduction == "length_alpha" else None)
+    d.update(obj)
+    return d
+
+
+def _timed_passes(pool, jobs, target_s):
+    """Runs the jobs over the pool, again and again, until target_s of wall
+    time have passed; returns (units done, seconds)."""
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        done += sum(pool.map(_run_job, jobs, chunksize=1))
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            return done, el
+
+
+def _run_job(job):
+    kind, payload = job
+    return _rows_job(payload) if kind == "rows" else _token_job(payload)
+
+
+def cpu_baseline_logits(pool, workers, wl, inp, reduction, obj, target_s, sample_rows):
+    """The oracle over the first ``sample_rows`` slots of this batch (its active
+    rows: masked rows are never read), chunks of 16 rows spread over the
+    worker processes, repeated until target_s of wall time.  Rows reach the
+    workers through float32 files written before timing starts."""
+    import numpy as np
+    import torch
+
+    import oracle
+    B, T, V = wl.B, wl.T, wl.V
+    h_mask = inp["mask"].cpu().numpy().astype(bool)
     h_rew = inp["rewards"].cpu().numpy()
     groups = wl.groups_kwargs()
-    off = oracle.group_offsets(wl.B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
+    off = oracle.group_offsets(B, groups.get("samples_per_prompt"), groups.get("group_boundaries"))
     A = oracle.group_advantages(h_rew, off, groups.get("leave_one_out", False),
                                 groups.get("scale_by_std", True))
-    cfg = oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
-                            reduction=wl.reductions[0], alpha=wl.alpha)
-    _, _, w = oracle.sequence_weights(h_mask, cfg.reduction, cfg.alpha)
-    B, T, V = wl.B, wl.T, wl.V
-    pol = inp["policy"].view(B * T, V)
-    ref = inp["ref"].view(B * T, V)
-    ids = inp["action_ids"].view(-1).cpu().numpy()
-    old = inp["old_logps"].view(-1).cpu().numpy()
-    mflat = h_mask.reshape(-1)
-    rows_done = 0
-    compute = 0.0
-    r0 = 0
-    while compute < target_s and r0 < B * T:
-        r1 = min(B * T, r0 + rows_per_chunk)
-        sel = np.nonzero(mflat[r0:r1])[0] + r0
-        x = pol[r0:r1].float().cpu().numpy()[sel - r0]
-        y = ref[r0:r1].float().cpu().numpy()[sel - r0]
-        seq = sel // T
-        t0 = time.perf_counter()
-        oracle.logits_rows(x, y, ids[sel], old[sel], A[seq], w[seq], cfg)
-        compute += time.perf_counter() - t0
-        rows_done += r1 - r0
-        r0 = r1
-    return dict(value=rows_done / compute, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{rows_done} of {B * T} slots (rows {0}..{r0 - 1}) of the same batch, "
-                       f"float64 numpy, single thread, {compute:.1f} s of compute; host copies excluded")
+    cfg = _cfg_dict(wl, reduction, obj)
+    _, _, w = oracle.sequence_weights(h_mask, reduction, cfg["alpha"])
+    n = min(B * T, sample_rows)
+    sel = np.nonzero(h_mask.reshape(-1)[:n])[0]
+    ids = inp["action_ids"].reshape(-1).cpu().numpy()[sel]
+    old = inp["old_logps"].reshape(-1).cpu().numpy()[sel]
+    seq = sel // T
+    tmp = _sample_dir()
+    try:
+        xpath = os.path.join(tmp, "x.npy")
+        ypath = os.path.join(tmp, "y.npy")
+        idx = torch.from_numpy(sel.astype(np.int64)).to(inp["policy"].device)
+        for path, t in ((xpath, inp["policy"]), (ypath, inp["ref"])):
+            rows = t.reshape(B * T, V).index_select(0, idx).float().cpu().numpy()
+            np.save(path, rows)
+            del rows
+        jobs = []
+        for s in range(0, len(sel), 16):
+            e = min(len(sel), s + 16)
+            jobs.append(("rows", (xpath, ypath, (len(sel), V), s, e, ids[s:e], old[s:e], A[seq[s:e]],
+                                  w[seq[s:e]], cfg)))
+        rows_done, el = _timed_passes(pool, jobs, target_s)
+    finally:
+        _rmtree(tmp)
+    passes = rows_done / max(len(sel), 1)
+    slots = passes * n
+    return dict(value=slots / el, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"slots 0..{n - 1} of {B * T} ({len(sel)} active rows; masked rows are never "
+                       f"read) of the same batch, {passes:.2f} passes, float64 numpy on {workers} worker "
+                       f"processes, {el:.1f} s wall; GPU-to-host copies excluded")
 
 
-def cpu_baseline_groups(wl, inp, call, target_s=12.0, groups_per_chunk=16):
-    """The fp64 oracle as it stands on a [B, T] log-prob batch: ``call`` runs
-    it on host arrays of whole groups, a chunk at a time in batch order and
-    starting over at the end of the batch, until about ``target_s`` seconds
-    of host compute have run.  Each chunk is its own oracle call, so its
-    sequence weights and any global statistic are the chunk's; the work per
-    slot is the same."""
+def cpu_baseline_tokens(pool, workers, wl, inp, target_s, groups_per_job=1):
+    """The oracle's log-prob token loss over whole groups of this batch, one
+    job per group spread over the worker processes, repeated until target_s
+    of wall time."""
     h = {k: v.cpu().numpy() for k, v in inp.items()}
     B, T = h["mask"].shape
-    size = wl.group_size * groups_per_chunk
-    compute = 0.0
-    done = 0                      # sequences processed, over all passes
-    while compute < target_s:
-        start = done % B
-        sl = slice(start, min(B, start + size))
-        part = {k: v[sl] for k, v in h.items()}
-        t0 = time.perf_counter()
-        call(part)
-        compute += time.perf_counter() - t0
-        done += sl.stop - sl.start
-    return dict(value=done * T / compute, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} sequences ({done * T} slots, {done / B:.2f} passes over the batch of "
-                       f"{B}) in chunks of {size} sequences, float64 numpy, single thread, "
-                       f"{compute:.1f} s of compute; host copies excluded")
+    size = wl.group_size * groups_per_job
+    cfg = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=wl.reduction)
+    jobs = [("tok", ({k: v[s:s + size] for k, v in h.items()}, wl.group_size, cfg))
+            for s in range(0, B, size)]
+    slots, el = _timed_passes(pool, jobs, target_s)
+    return dict(value=slots / el, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"the whole batch in jobs of {size} sequences ({groups_per_job} group(s) each), "
+                       f"{slots / (B * T):.2f} passes, float64 numpy on {workers} worker processes, "
+                       f"{el:.1f} s wall")
 
+
+def _sample_dir():
+    """A scratch directory for the oracle's sample: /dev/shm when it has room,
+    else the temporary directory."""
+    import shutil
+    for base in ("/dev/shm", tempfile.gettempdir()):
+        try:
+            if shutil.disk_usage(base).free > (24 << 30):
+                return tempfile.mkdtemp(prefix="grpo_oracle_", dir=base)
+        except OSError:
+            pass
+    return tempfile.mkdtemp(prefix="grpo_oracle_")
+
+
+def _rmtree(path):
+    import shutil
+    shutil.rmtree(path, ignore_errors=True)
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
 
 class HipEvents:
-    """hipEvent_t pairs created through the HIP runtime (the vocabulary kernel
-    is launched by the library on torch's current stream; the library records
-    these events right around that launch)."""
+    """hipEvent_t pairs created through the HIP runtime (the kernel is launched
+    by the library on torch's current stream; the library records these
+    events right around that launch)."""
 
     def __init__(self, n):
         import ctypes as C
@@ -180,10 +312,35 @@ class HipEvents:
             self.hip.hipEventDestroy(b)
 
 
-def load_traffic(workload):
-    """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{ROW_KERNEL}_{workload}_pmc.json")
+def timed_kernel(lib, steps, step):
+    """Runs ``step(k)`` ``steps`` times with the library's timing hook set
+    around the dominant kernel of each call; returns (host ms per step, list
+    of kernel ms)."""
+    import torch
+    ev = HipEvents(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        lib.grpo_set_timing_events(ev.pairs[k][0], ev.pairs[k][1])
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.grpo_set_timing_events(None, None)
+    kern = [ev.elapsed_ms(k) for k in range(steps)]
+    ev.close()
+    return (t1 - t0) * 1e3 / steps, kern
+
+
+def _median(v):
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch (bytes) from the committed counter summary of
+    ``kernel`` on ``workload``, if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -191,6 +348,19 @@ def load_traffic(workload):
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def roofline(kernel, workload, alg_bytes, kern_ms, extra=None):
+    kavg = sum(kern_ms) / len(kern_ms)
+    achieved = alg_bytes / (kavg * 1e-3) / 1e9
+    traffic = load_traffic(kernel, workload)
+    r = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": kernel,
+         "kernel_ms": kavg, "kernel_ms_median": _median(kern_ms), "algorithmic_bytes": alg_bytes,
+         "physical_frac": None if traffic is None else traffic / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if extra:
+        r.update(extra)
+    return r
 
 
 GRAPH_TIMING = ("GPU time per call: the calls captured in one HIP graph per replay (each input "
@@ -240,66 +410,160 @@ def _graph_times(step, ncopies, steps, per_graph=30):
     return ms, ms_single
 
 
-def run_token(args):
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Workload runners: each returns one record
+# ---------------------------------------------------------------------------
+
+def _row_kernel_name(wl, resident):
+    return "grpo_rows_resident_kernel" if resident else "grpo_rows_kernel"
+
+
+def _resident(wl):
+    """Whether the fused call takes the resident-row kernel: rows above 4 KB
+    and up to 264 KB, 16-byte aligned (the library's own choice, restated
+    for labelling the record; the kernel trace names the kernel that ran)."""
+    b = wl.V * (4 if wl.dtype == "f32" else 2)
+    return 4096 < b <= 270336 and b % 16 == 0
+
+
+def run_logits_record(args, wl, inp, reduction, objective="default", pool=None, workers=1,
+                      cpu_seconds=None, sample_rows=None):
+    import torch
+    import rl_post_loss_amd as rpl
+    from workloads import make_gen_logps
+
+    lib = rpl.load_library()
+    B, T, V = wl.B, wl.T, wl.V
+    grad = torch.empty((B, T, V), dtype=inp["policy"].dtype, device=inp["policy"].device)
+    kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=reduction,
+              alpha=wl.alpha if reduction == "length_alpha" else None)
+    kw.update(wl.groups_kwargs())
+    obj, needs_gen = OBJECTIVES[objective]
+    kw.update(obj)
+    gen = make_gen_logps(inp["old_logps"], seed=args.seed) if needs_gen else None
+    out = [None]
+
+    def step(k=0):
+        out[0] = rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                       inp["old_logps"], inp["rewards"], inp["mask"],
+                                       grad_out=grad, gen_logps=gen, out=out[0], **kw)
+        return out[0]
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    ref_scalars = out[0].scalars.clone()
+    gview = grad.view(torch.int16 if grad.element_size() == 2 else torch.int32)
+    ref_grad_sum = int(gview.sum(dtype=torch.int64))
+    step_scalars = []
+
+    def timed_step(k):
+        step()
+        step_scalars.append(out[0].scalars.clone())
+
+    ms_per_step, kern = timed_kernel(lib, args.steps, timed_step)
+    repro = (all(torch.equal(ref_scalars.view(torch.int32), sc.view(torch.int32)) for sc in step_scalars)
+             and int(gview.sum(dtype=torch.int64)) == ref_grad_sum)
+    active = int(inp["mask"].sum())
+    rows = B * T
+    resident = _resident(wl) and objective in ("default", "cispo", "seq_mask")
+    kname = _row_kernel_name(wl, resident)
+    key = wl.name if reduction == wl.reductions[0] else f"{wl.name}_{reduction}"
+    alg = byte_model(wl, active, rows)
+    mb = min_bytes(wl, active, rows, resident)
+    kavg = sum(kern) / len(kern)
+    rec = {
+        "workload": f"{wl.name}: B={B} ({len(wl.group_sizes)} groups{', CSR' if wl.csr else ''}), "
+                    f"T={T}, V={V}, {wl.dtype} logits and gradient, {reduction}, "
+                    + ("full mask" if wl.len_range is None else "ragged lengths %d..%d" % wl.len_range)
+                    + ("" if objective == "default" else f", objective {objective}"),
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": rows / (ms_per_step * 1e-3),
+        "active_tokens_per_s": active / (ms_per_step * 1e-3),
+        "B": B, "T": T, "V": V, "storage": wl.dtype, "active_slots": active,
+        "hbm_fraction_of_step": alg / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "bit_reproducible": bool(repro),
+        "roofline": roofline(kname, key, alg, kern, {
+            "byte_model": "policy row read twice, reference once, gradient written once per active "
+                          "row; zero gradient per masked row; 13 B of side inputs per slot",
+            "kernel_min_bytes": mb,
+            "kernel_min_frac": mb / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS}),
+    }
+    if objective != "default":
+        rec["objective"] = obj
+    if pool is not None and objective == "default":
+        _log(f"oracle baseline {key}")
+        rec["cpu_baseline"] = cpu_baseline_logits(pool, workers, wl, inp, reduction, obj,
+                                                  cpu_seconds or args.cpu_seconds,
+                                                  sample_rows or 4096)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def run_token_record(args, wl, pool=None, workers=1, copies=None):
     """Logprob-level token loss (no vocabulary).  The 71 MB working set fits
-    the memory-side cache, so the timed loop rotates over enough input copies
+    the memory-side cache, so the timed calls rotate over enough input copies
     (each call reads a different one) to keep it from being served there."""
     import torch
     import rl_post_loss_amd as rpl
-    from workloads import TOKEN_WORKLOADS, make_token_inputs
+    from workloads import make_token_inputs
 
-    rpl.load_library()
+    lib = rpl.load_library()
     dev = torch.device("cuda:0")
-    wl = TOKEN_WORKLOADS[args.workload]
-    copies = [make_token_inputs(wl, device=dev, seed=args.seed + k) for k in range(args.copies)]
-    outs = [torch.empty((wl.B, wl.T), dtype=torch.float32, device=dev) for _ in range(args.copies)]
+    ncop = copies or args.copies
+    cps = [make_token_inputs(wl, device=dev, seed=args.seed + k) for k in range(ncop)]
     kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
               samples_per_prompt=wl.group_size, reduction=wl.reduction)
-
-    results = [None] * len(copies)
+    results = [None] * ncop
 
     def step(k):
-        j = k % len(copies)
-        c = copies[j]
+        j = k % ncop
+        c = cps[j]
         results[j] = rpl.grpo_token_loss(c["logp"], c["old_logps"], c["ref_logp"], c["rewards"],
                                          c["mask"], out=results[j], **kw)
 
-    for k in range(max(args.warmup, len(copies))):
+    for k in range(max(args.warmup, ncop)):
         step(k)
     torch.cuda.synchronize()
-    # eager calls (Python binding overhead included)
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
+    ref_scalars = [r.scalars.clone() for r in results]
+    ref_grads = [r.grad.clone() for r in results]
+    ms_eager, kern = timed_kernel(lib, max(args.steps, 30), step)
+    ms, ms_graph_per_call = _graph_times(step, ncop, max(args.steps, 30))
     torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms, ms_graph_per_call = _graph_times(step, len(copies), args.steps)
-    m = copies[0]["mask"]
-    active = int(m.sum())
+    repro = all(torch.equal(a.view(torch.int32), r.scalars.view(torch.int32)) and
+                torch.equal(g.view(torch.int32), r.grad.view(torch.int32))
+                for a, g, r in zip(ref_scalars, ref_grads, results))
+    active = int(cps[0]["mask"].sum())
     rows = wl.B * wl.T
-    alg = active * 17 + (rows - active) * 5
-    out = {"metric": "tokens/s for the logprob-level GRPO token loss (forward + dlogp)",
-           "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": f"{wl.name}: B={wl.B} ({wl.num_groups} groups of {wl.group_size}), "
-                                  f"T={wl.T}, {wl.reduction}, input copies rotated: {args.copies}",
-                      "active_tokens": active, "algorithmic_bytes": alg,
-                      "step_GBps": alg / (ms * 1e-3) / 1e9, "timing": GRAPH_TIMING,
-                      "ms_per_step_graph_per_call": ms_graph_per_call,
-                      "ms_per_step_eager_python": ms_eager}}
-    out["cpu_baseline"] = None
-    if not args.no_cpu_baseline:
-        import oracle
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cfg = oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
-                                reduction=wl.reduction)
-        out["cpu_baseline"] = cpu_baseline_groups(
-            wl, copies[0], lambda h: oracle.grpo_token_loss(
-                h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
-                groups=dict(samples_per_prompt=wl.group_size), cfg=cfg),
-            target_s=args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    alg = token_bytes(active, rows)
+    rec = {
+        "workload": f"{wl.name}: B={wl.B} ({wl.num_groups} groups of {wl.group_size}), T={wl.T}, "
+                    f"f32 log-probs, {wl.reduction}, "
+                    + ("full mask" if wl.len_range is None else "ragged lengths %d..%d" % wl.len_range)
+                    + f"; input copies rotated: {ncop}",
+        "ms_per_step": ms, "timing": GRAPH_TIMING,
+        "tokens_per_s": rows / (ms * 1e-3), "active_tokens_per_s": active / (ms * 1e-3),
+        "active_slots": active, "algorithmic_bytes": alg,
+        "hbm_fraction_of_step": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "ms_per_step_graph_per_call": ms_graph_per_call, "ms_per_step_eager_python": ms_eager,
+        "bit_reproducible": bool(repro),
+        "roofline": roofline("grpo_token_kernel", wl.name, alg, kern, {
+            "byte_model": "17 B per active token (logp, old, ref f32 + mask in, dlogp out), 5 B per "
+                          "masked token (mask in, zero out)",
+            "timing": "the token kernel alone, HIP events around its launch in eager calls"}),
+    }
+    if pool is not None:
+        _log(f"oracle baseline {wl.name}")
+        rec["cpu_baseline"] = cpu_baseline_tokens(pool, workers, wl, cps[0], args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    del cps, results
+    return rec
 
 
 ADV_WORKLOADS = {"adv_reinforce_pp": "reinforce_pp", "adv_reinforce_pp_baseline": "reinforce_pp_baseline"}
@@ -310,12 +574,12 @@ def run_adv(args):
     (B = 1024 in groups of 16, T = 4096, ragged lengths): REINFORCE++
     returns (k1 shaping 0.01, gamma 1) or the inclusive group baseline, with
     the global masked normalization.  Input copies are rotated as for the
-    token loss; timed as the token loss is."""
+    token loss."""
     import torch
     import rl_post_loss_amd as rpl
     from workloads import TOKEN_WORKLOADS, make_token_inputs
 
-    rpl.load_library()
+    lib = rpl.load_library()
     dev = torch.device("cuda:0")
     est = ADV_WORKLOADS[args.workload]
     wl = TOKEN_WORKLOADS["token_loss_ragged"]
@@ -334,6 +598,7 @@ def run_adv(args):
     for k in range(max(args.warmup, len(copies))):
         step(k)
     torch.cuda.synchronize()
+    _, kern = timed_kernel(lib, max(args.steps, 30), step)
     ms, ms_graph_per_call = _graph_times(step, len(copies), args.steps)
     rows = wl.B * wl.T
     # minimum bytes: old, ref f32 and the mask read once (REINFORCE++), the output written once
@@ -346,131 +611,93 @@ def run_adv(args):
            "config": {"workload": f"{args.workload}: B={wl.B} (groups of {wl.group_size}), T={wl.T}, "
                                   f"ragged lengths, {est}, normalized; input copies rotated: {args.copies}",
                       "algorithmic_bytes": alg, "step_GBps": alg / (ms * 1e-3) / 1e9,
-                      "timing": GRAPH_TIMING, "ms_per_step_graph_per_call": ms_graph_per_call}}
+                      "timing": GRAPH_TIMING, "ms_per_step_graph_per_call": ms_graph_per_call},
+           "roofline": roofline("grpo_tokadv_kernels", args.workload, alg, kern,
+                                {"timing": "the estimator's three kernels, HIP events around them"})}
     out["cpu_baseline"] = None
-    if not args.no_cpu_baseline:
-        import oracle
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        if est == "reinforce_pp":
-            call = lambda h: oracle.token_advantages(est, h["rewards"], h["old_logps"], h["ref_logp"],
-                                                     h["mask"], **kw)
-        else:
-            call = lambda h: oracle.token_advantages(est, h["rewards"], None, None, h["mask"],
-                                                     groups=dict(samples_per_prompt=wl.group_size),
-                                                     normalize=True)
-        out["cpu_baseline"] = cpu_baseline_groups(wl, copies[0], call, target_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def run(args):
+def _line(rec, args, wl_key):
+    """The bench line around one record."""
+    return {
+        "metric": METRIC if not wl_key.startswith("token_loss") else
+        "tokens/s for the logprob-level GRPO token loss (forward + dlogp)",
+        "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {k: v for k, v in rec.items() if k not in ("roofline", "cpu_baseline", "ms_per_step",
+                                                              "tokens_per_s")},
+        "roofline": rec["roofline"], "cpu_baseline": rec["cpu_baseline"],
+    }
+
+
+def run_single(args, pool, workers):
     import torch
     import rl_post_loss_amd as rpl
-    from workloads import WORKLOADS, make_gen_logps, make_logits_inputs
+    from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs
+
+    rpl.load_library()
+    if args.workload in TOKEN_WORKLOADS:
+        rec = run_token_record(args, TOKEN_WORKLOADS[args.workload], pool, workers)
+        print(json.dumps(_line(rec, args, args.workload)), flush=True)
+        return
+    name, _, red = args.workload.partition(":")
+    wl = WORKLOADS[name]
+    red = red or (OBJECTIVES[args.objective][0].get("reduction") or wl.reductions[0])
+    _log(f"generating {wl.name}: B={wl.B} T={wl.T} V={wl.V} {wl.dtype}")
+    inp = make_logits_inputs(wl, device=torch.device("cuda:0"), seed=args.seed)
+    torch.cuda.synchronize()
+    rec = run_logits_record(args, wl, inp, red, args.objective, pool, workers)
+    print(json.dumps(_line(rec, args, name)), flush=True)
+
+
+# sample of slots the CPU baseline takes from each logits workload (about
+# 2-3 s of oracle work over 16 processes)
+SAMPLE_ROWS = {"tiny_logits": 128, "logits_v32000": 16384, "logits_v151936": 2048,
+               "logits_csr_v128256": 6144}
+
+
+def run_all(args, pool, workers):
+    """The headline (V = 151,936) and one record per other workload, in one line."""
+    import torch
+    import rl_post_loss_amd as rpl
+    from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs
 
     rpl.load_library()
     dev = torch.device("cuda:0")
-    wl = WORKLOADS[args.workload]
-    print(f"[bench] generating {wl.name}: B={wl.B} T={wl.T} V={wl.V} {wl.dtype}", file=sys.stderr,
-          flush=True)
-    t_gen = time.perf_counter()
-    inp = make_logits_inputs(wl, device=dev, seed=args.seed)
-    torch.cuda.synchronize()
-    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-    B, T, V = wl.B, wl.T, wl.V
-    gdt = inp["policy"].dtype
-    grad = torch.empty((B, T, V), dtype=gdt, device=dev)
-    kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=wl.reductions[0],
-              alpha=wl.alpha)
-    kw.update(wl.groups_kwargs())
-    obj, needs_gen = OBJECTIVES[args.objective]
-    kw.update(obj)
-    gen = make_gen_logps(inp["old_logps"], seed=args.seed) if needs_gen else None
+    subs = {}
+    head = None
+    for name in ("logits_v151936", "tiny_logits", "logits_v32000", "logits_csr_v128256"):
+        wl = WORKLOADS[name]
+        _log(f"generating {wl.name}: B={wl.B} T={wl.T} V={wl.V} {wl.dtype}")
+        t0 = time.perf_counter()
+        inp = make_logits_inputs(wl, device=dev, seed=args.seed)
+        torch.cuda.synchronize()
+        _log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+        for red in wl.reductions:
+            key = name if red == wl.reductions[0] else f"{name}:{red}"
+            _log(f"timing {key}")
+            rec = run_logits_record(args, wl, inp, red, pool=pool, workers=workers,
+                                    sample_rows=SAMPLE_ROWS[name])
+            if name == "logits_v151936":
+                head = rec
+            else:
+                subs[key] = rec
+        del inp
+        torch.cuda.empty_cache()
+    for name in ("token_loss_full", "token_loss_ragged"):
+        _log(f"timing {name}")
+        subs[name] = run_token_record(args, TOKEN_WORKLOADS[name], pool, workers)
+        torch.cuda.empty_cache()
+    line = _line(head, args, "logits_v151936")
+    line["configs"] = subs
+    print(json.dumps(line), flush=True)
 
-    def step():
-        return rpl.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"], inp["old_logps"],
-                                     inp["rewards"], inp["mask"], grad_out=grad, gen_logps=gen, **kw)
 
-    for _ in range(args.warmup):
-        res = step()
-    torch.cuda.synchronize()
-    ref_scalars = res.scalars.clone() if args.warmup else None
-    ref_grad_sum = int(grad.view(torch.int16 if grad.element_size() == 2 else torch.int32)
-                       .sum(dtype=torch.int64)) if args.warmup else None
-
-    ev = HipEvents(args.steps)
-    lib = rpl.load_library()
-    step_scalars = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        lib.grpo_set_timing_events(ev.pairs[k][0], ev.pairs[k][1])
-        res = step()
-        step_scalars.append(res.scalars)  # each call returns its own scalar tensor
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    lib.grpo_set_timing_events(None, None)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [ev.elapsed_ms(k) for k in range(args.steps)]
-    ev.close()
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    kern_median = sorted(kern_ms)[len(kern_ms) // 2]
-    # bit reproducibility: every timed step's scalars equal the warm-up's, and
-    # the gradient left by the last step has the warm-up gradient's checksum
-    repro = ref_scalars is None or (
-        all(torch.equal(ref_scalars.view(torch.int32), sc.view(torch.int32)) for sc in step_scalars)
-        and int(grad.view(torch.int16 if grad.element_size() == 2 else torch.int32)
-                .sum(dtype=torch.int64)) == ref_grad_sum)
-
-    active = int(inp["mask"].sum())
-    rows = B * T
-    alg_bytes = byte_model(wl, active, rows)
-    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
-    traffic = load_traffic(wl.name) if args.objective == "default" else None
-    value = rows / (ms_per_step * 1e-3)
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{wl.name}: B={B} ({len(wl.group_sizes)} groups), T={T}, V={V}, "
-                        f"{wl.dtype} logits and gradient, {kw['reduction']}, "
-                        f"{'full mask' if wl.len_range is None else 'ragged lengths %d..%d' % wl.len_range}"
-                        + ("" if args.objective == "default" else f", objective {args.objective}"),
-            "objective": {k: v for k, v in obj.items()},
-            "B": B, "T": T, "V": V, "storage": wl.dtype, "active_slots": active,
-            "active_tokens_per_s": active / (ms_per_step * 1e-3),
-            "hbm_fraction_of_step": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "bit_reproducible": bool(repro),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic,
-            "kernel": ROW_KERNEL,
-            "kernel_ms": kern_avg,
-            "kernel_ms_median": kern_median,
-            "algorithmic_bytes": alg_bytes,
-        },
-    }
-    if not args.no_cpu_baseline and args.objective == "default":
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, inp, target_s=args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
-
+# ---------------------------------------------------------------------------
+# Counter calibration and summaries
+# ---------------------------------------------------------------------------
 
 def calibrate_only():
     """One elementwise kernel over CALIB_BYTES of float32: reads CALIB_BYTES,
@@ -498,44 +725,47 @@ def _pmc_values(d, counter, name_part):
                     continue
                 did = row.get("Dispatch_Id")
                 per[did] = per.get(did, 0.0) + float(row["Counter_Value"])
-    return list(per.values())
+    return [per[k] for k in sorted(per, key=lambda v: int(v))]
 
 
-def summarize_pmc(dirs, workload, out_dir):
+def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1):
     """Combine the four rocprofv3 --pmc runs into profiles/<kernel>_<workload>_pmc.json.
     The counters read over the calibration kernel, which moves a known number
-    of bytes each way, give the scale from counter units to bytes."""
+    of bytes each way, give the scale from counter units to bytes.  The first
+    ``skip_first`` dispatches (warm-up) are left out of the average."""
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
     res = {}
     for counter, run_dir, cal_dir in (("FETCH_SIZE", fetch_dir, cal_fetch_dir),
                                       ("WRITE_SIZE", write_dir, cal_write_dir)):
         cal = _pmc_values(cal_dir, counter, "_add<float>")
-        rows = _pmc_values(run_dir, counter, ROW_KERNEL)
+        rows = _pmc_values(run_dir, counter, kernel)
         if not cal or not rows:
-            raise SystemExit(f"missing {counter} values (calibration {len(cal)}, row kernel {len(rows)})")
+            raise SystemExit(f"missing {counter} values (calibration {len(cal)}, kernel {len(rows)})")
+        used = rows[skip_first:] if len(rows) > skip_first else rows
         c = max(cal)
         scale = CALIB_BYTES / c
         res[counter] = dict(calibration_counter=c, calibration_bytes=CALIB_BYTES,
-                            scale_bytes_per_unit=scale,
-                            row_kernel_counter_per_dispatch=rows,
-                            row_kernel_bytes_avg=sum(rows) / len(rows) * scale)
-    traffic = res["FETCH_SIZE"]["row_kernel_bytes_avg"] + res["WRITE_SIZE"]["row_kernel_bytes_avg"]
-    summary = dict(kernel=ROW_KERNEL, workload=workload, kernel_source_hash=kernel_source_hash(),
+                            scale_bytes_per_unit=scale, kernel_counter_per_dispatch=rows,
+                            dispatches_averaged=len(used),
+                            kernel_bytes_avg=sum(used) / len(used) * scale)
+    traffic = res["FETCH_SIZE"]["kernel_bytes_avg"] + res["WRITE_SIZE"]["kernel_bytes_avg"]
+    wl_arg = workload.replace("_sequence_mean", ":sequence_mean").replace("_length_alpha", ":length_alpha")
+    summary = dict(kernel=kernel, workload=workload, kernel_source_hash=kernel_source_hash(),
                    counters=res, traffic_bytes_per_launch=traffic,
-                   commands=["rocprofv3 --pmc FETCH_SIZE --kernel-include-regex grpo_rows -f csv "
-                             f"-d {fetch_dir} -o run -- python3 bench.py --workload {workload} "
+                   commands=[f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {kernel} -f csv "
+                             f"-d {fetch_dir} -o run -- python3 bench.py --workload {wl_arg} "
                              "--steps 3 --warmup 1 --no-cpu-baseline",
-                             "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex grpo_rows -f csv "
-                             f"-d {write_dir} -o run -- python3 bench.py --workload {workload} "
+                             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {kernel} -f csv "
+                             f"-d {write_dir} -o run -- python3 bench.py --workload {wl_arg} "
                              "--steps 3 --warmup 1 --no-cpu-baseline",
                              "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex elementwise -f csv "
                              f"-d {cal_fetch_dir} -o run -- python3 bench.py --calibrate-only",
                              "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex elementwise -f csv "
                              f"-d {cal_write_dir} -o run -- python3 bench.py --calibrate-only",
-                             f"python bench.py --workload {workload} --summarize-pmc "
+                             f"python bench.py --workload {wl_arg} --kernel {kernel} --summarize-pmc "
                              f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"])
     os.makedirs(out_dir, exist_ok=True)
-    base = os.path.join(out_dir, f"{ROW_KERNEL}_{workload}_pmc")
+    base = os.path.join(out_dir, f"{kernel}_{workload}_pmc")
     with open(base + ".json", "w") as f:
         json.dump(summary, f, indent=1)
     print(json.dumps(summary, indent=1))
@@ -546,32 +776,50 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="logits_v151936")
+    ap.add_argument("--workload", default="all",
+                    help="all | a logits workload (optionally name:reduction) | token_loss_full | "
+                         "token_loss_ragged | adv_reinforce_pp | adv_reinforce_pp_baseline")
     ap.add_argument("--objective", default="default", choices=sorted(OBJECTIVES))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.5,
+                    help="wall seconds of oracle work per workload over the worker processes")
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated by the token-loss bench")
     ap.add_argument("--calibrate-only", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, default=None)
+    ap.add_argument("--kernel", default="grpo_rows_kernel", help="kernel named by --summarize-pmc")
     args = ap.parse_args()
     if args.calibrate_only:
         calibrate_only()
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.workload, os.path.join(ROOT, "profiles"))
+        key = args.workload.replace(":", "_")
+        summarize_pmc(args.summarize_pmc, key, args.kernel, os.path.join(ROOT, "profiles"))
         return
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    if args.workload.startswith("token_loss"):
-        run_token(args)
-    elif args.workload in ADV_WORKLOADS:
+    if args.workload in ADV_WORKLOADS:
         run_adv(args)
-    else:
-        run(args)
+        return
+    pool = None
+    workers = host_workers()
+    if not args.no_cpu_baseline and args.objective == "default":
+        if under_profiler():
+            _log("under a profiler: no oracle worker processes, cpu_baseline left out")
+        else:
+            _log(f"starting {workers} oracle worker processes")
+            pool = start_pool(workers)
+    try:
+        if args.workload == "all":
+            run_all(args, pool, workers)
+        else:
+            run_single(args, pool, workers)
+    finally:
+        if pool is not None:
+            pool.terminate()
 
 
 if __name__ == "__main__":

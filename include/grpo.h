@@ -467,7 +467,9 @@ GRPO_API grpo_status grpo_scale_grad(void *grad, int32_t grad_dtype, int64_t row
 
 /* Optional timing hook for profiling tools: when both are non-NULL, the
  * logits entry points record `start` right before and `stop` right after
- * the launch of their vocabulary-streaming kernel, on the call's stream.
+ * the launch of their vocabulary-streaming kernel, grpo_token_loss around
+ * its token kernel and grpo_token_advantages around its kernels, on the
+ * call's stream.
  * The events are hipEvent_t handles owned by the caller; pass NULLs to turn
  * the hook off.  Not thread-safe: set it from the thread that launches. */
 GRPO_API void grpo_set_timing_events(void *start, void *stop);

@@ -548,7 +548,10 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   a.adv_out = out->advantages;
   a.seq_tokens_out = out->seq_tokens;
   a.fault = w.at<uint32_t>(w.l.fault);
+  const bool timed = g_ev_start && g_ev_stop;
+  if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
   if (launch_token(a, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
   return run_final(w, B, cfg->beta, out, s,
                    cfg->pg_loss == GRPO_PG_REAL ? group_count(groups, B) : 0, !seqlv,
                    weights_mode == 2);
@@ -867,7 +870,11 @@ grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const
   a.V = w.at<double>(w.l.stash);  // the row stash (16 bytes per slot) holds one double per slot
   a.out = adv_out;
   a.status = status;
-  return launch_token_advantages(a, s) == hipSuccess ? GRPO_OK : GRPO_ERR_HIP;
+  const bool timed = g_ev_start && g_ev_stop;
+  if (timed && hipEventRecord(g_ev_start, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (launch_token_advantages(a, s) != hipSuccess) return GRPO_ERR_HIP;
+  if (timed && hipEventRecord(g_ev_stop, s) != hipSuccess) return GRPO_ERR_HIP;
+  return GRPO_OK;
 }
 
 grpo_status grpo_gdpo_advantages(const float* rewards, int32_t num_components, int64_t B,

@@ -1,7 +1,7 @@
 """Host logic of bench.py, without a GPU: the refusal of more than one GPU,
-the byte model of the vocabulary kernel, the counter summary's scaling from
-counter units to bytes, the tie of the reported traffic to the kernel
-sources, and the CPU-oracle baseline over whole groups."""
+the byte models of the vocabulary and token kernels, the counter summary's
+scaling from counter units to bytes, the tie of the reported traffic to the
+kernel sources, and the CPU-oracle baselines over worker processes."""
 
 import csv
 import json
@@ -10,7 +10,7 @@ import subprocess
 import sys
 
 import bench
-from workloads import TOKEN_WORKLOADS, WORKLOADS, make_token_inputs
+from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs, make_token_inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -35,6 +35,16 @@ def test_byte_model():
     tiny = WORKLOADS["tiny_logits"]   # float32
     n = tiny.B * tiny.T
     assert bench.byte_model(tiny, 10, n) == 10 * tiny.V * 16 + (n - 10) * tiny.V * 4 + n * 13
+    # the resident kernel reads an active policy row once: one policy pass fewer
+    v32 = WORKLOADS["logits_v32000"]
+    n = v32.B * v32.T
+    assert bench.byte_model(v32, 100, n) - bench.min_bytes(v32, 100, n, True) == 100 * v32.V * 2
+    assert bench.min_bytes(wl, rows, rows, False) == bench.byte_model(wl, rows, rows)
+    assert bench._resident(v32) and bench._resident(WORKLOADS["logits_csr_v128256"])
+    assert not bench._resident(wl) and not bench._resident(tiny)
+    # token loss: 17 B per active token, 5 B per masked one
+    assert bench.token_bytes(4_194_304, 4_194_304) == 71_303_168
+    assert bench.token_bytes(10, 30) == 10 * 17 + 20 * 5
 
 
 def _counter_csv(d, kernel, counter, values):
@@ -50,19 +60,21 @@ def _counter_csv(d, kernel, counter, values):
 
 
 def test_summarize_pmc_scales_by_the_calibration_kernel(tmp_path):
-    row = f"void grpo::{bench.ROW_KERNEL}<unsigned short>(grpo::RowArgs)"
+    row = "void grpo::grpo_rows_kernel<unsigned short>(grpo::RowArgs)"
     cal = "void at::native::elementwise_kernel<_add<float>>(...)"
     dirs = [str(tmp_path / n) for n in ("f", "w", "cf", "cw")]
-    _counter_csv(dirs[0], row, "FETCH_SIZE", [[10.0, 20.0], [40.0, 20.0]])   # 30, 60 per dispatch
-    _counter_csv(dirs[1], row, "WRITE_SIZE", [[5.0], [7.0]])
+    # dispatch 0 is the warm-up, left out of the average
+    _counter_csv(dirs[0], row, "FETCH_SIZE", [[1.0], [10.0, 20.0], [40.0, 20.0]])   # 30, 60
+    _counter_csv(dirs[1], row, "WRITE_SIZE", [[1.0], [5.0], [7.0]])
     _counter_csv(dirs[2], cal, "FETCH_SIZE", [[1000.0, 24.0]])             # 1024 units
     _counter_csv(dirs[3], cal, "WRITE_SIZE", [[2048.0]])
     out = tmp_path / "profiles"
-    bench.summarize_pmc(dirs, "wl", str(out))
-    d = json.load(open(out / f"{bench.ROW_KERNEL}_wl_pmc.json"))
+    bench.summarize_pmc(dirs, "wl", "grpo_rows_kernel", str(out))
+    d = json.load(open(out / "grpo_rows_kernel_wl_pmc.json"))
     fetch = 45.0 * bench.CALIB_BYTES / 1024.0
     write = 6.0 * bench.CALIB_BYTES / 2048.0
-    assert d["counters"]["FETCH_SIZE"]["row_kernel_counter_per_dispatch"] == [30.0, 60.0]
+    assert d["counters"]["FETCH_SIZE"]["kernel_counter_per_dispatch"] == [1.0, 30.0, 60.0]
+    assert d["counters"]["FETCH_SIZE"]["dispatches_averaged"] == 2
     assert abs(d["traffic_bytes_per_launch"] - (fetch + write)) <= 1e-9 * (fetch + write)
     assert d["kernel_source_hash"] == bench.kernel_source_hash()
 
@@ -70,27 +82,40 @@ def test_summarize_pmc_scales_by_the_calibration_kernel(tmp_path):
 def test_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    path = prof / f"{bench.ROW_KERNEL}_wl_pmc.json"
+    path = prof / "grpo_token_kernel_wl_pmc.json"
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
-    assert bench.load_traffic("wl") is None
+    assert bench.load_traffic("grpo_token_kernel", "wl") is None
     path.write_text(json.dumps(dict(kernel_source_hash="abc", traffic_bytes_per_launch=123.0)))
-    assert bench.load_traffic("wl") == 123.0
+    assert bench.load_traffic("grpo_token_kernel", "wl") == 123.0
     path.write_text(json.dumps(dict(kernel_source_hash="old", traffic_bytes_per_launch=123.0)))
-    assert bench.load_traffic("wl") is None
+    assert bench.load_traffic("grpo_token_kernel", "wl") is None
 
 
-def test_cpu_baseline_over_whole_groups():
-    wl = TOKEN_WORKLOADS["token_loss_ragged"]
-    inp = make_token_inputs(wl, device="cpu", seed=0, B=48, T=32)
-    sizes = []
+def test_cpu_baselines_over_worker_processes():
+    """The oracle baselines run on spawned worker processes: the token loss
+    over whole groups, the logits rows from float32 sample files."""
+    import torch
+    pool = bench.start_pool(2)
+    try:
+        wl = TOKEN_WORKLOADS["token_loss_ragged"]
+        inp = make_token_inputs(wl, device="cpu", seed=0, B=48, T=32)
+        res = bench.cpu_baseline_tokens(pool, 2, wl, inp, target_s=0.05)
+        assert res["kind"] == "oracle" and res["cores"] == 2 and res["value"] > 0
+        assert "jobs of 16 sequences" in res["sample"]
+        lw = WORKLOADS["logits_v32000"].scaled(T=8, V=300, prompts=2)
+        linp = make_logits_inputs(lw, device="cpu", seed=1)
+        res = bench.cpu_baseline_logits(pool, 2, lw, linp, "token_mean", {}, 0.05, 64)
+        assert res["value"] > 0 and res["cores"] == 2 and "slots 0..63" in res["sample"]
+    finally:
+        pool.terminate()
 
-    def call(h):
-        sizes.append(h["mask"].shape[0])
-        assert all(v.shape[0] == h["mask"].shape[0] for v in h.values())
-        sum(float(v.sum()) for v in h.values())   # some host work to time
 
-    res = bench.cpu_baseline_groups(wl, inp, call, target_s=0.01, groups_per_chunk=2)
-    assert sizes and all(n % wl.group_size == 0 for n in sizes)
-    assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
-    assert f"{sum(sizes)} sequences" in res["sample"]
+def test_profiler_guard(monkeypatch):
+    monkeypatch.delenv("LD_PRELOAD", raising=False)
+    for k in list(os.environ):
+        if k.startswith("ROCPROF"):
+            monkeypatch.delenv(k)
+    assert not bench.under_profiler()
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/librocprofiler-sdk-tool.so")
+    assert bench.under_profiler()
