@@ -73,38 +73,142 @@ __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
   return a;
 }
 
-__device__ __forceinline__ Lse shfl_xor_lse(Lse v, int mask) {
-  return Lse{__shfl_xor(v.m, mask), __shfl_xor(v.mL, mask), __shfl_xor(v.s, mask)};
+// --- wave64 reductions without LDS traffic -----------------------------------
+// A wave-wide reduction runs six exchange steps; after step k every lane holds
+// the combination of a group of 2^(k+1) lanes.  Steps 0-3 stay inside a row
+// of 16 lanes and use DPP lane selection on a v_mov (quad permutation
+// 1,0,3,2, quad permutation 2,3,0,1, the half-row mirror 7 - l, the row mirror
+// 15 - l); steps 4 and 5 cross rows with gfx950's v_permlane16_swap (rows
+// 0 <-> 1, 2 <-> 3) and v_permlane32_swap (lanes 0-31 <-> 32-63).  Each step
+// pairs lanes symmetrically and combines the two values with a commutative
+// operation, so both lanes of a pair, and at the end every lane, hold the
+// same bits; the tree is fixed, so the result is the same from run to run.
+// Every lane of the wave must be active.
+struct Pair32 {
+  uint32_t a, b;
+};
+
+template <int STEP>
+__device__ __forceinline__ Pair32 wave_step_u32(uint32_t v) {
+  static_assert(STEP >= 0 && STEP < 6, "six steps cover 64 lanes");
+  if constexpr (STEP < 4) {
+    constexpr int ctrl = STEP == 0 ? 0xB1 : (STEP == 1 ? 0x4E : (STEP == 2 ? 0x141 : 0x140));
+    const uint32_t p = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), ctrl, 0xF, 0xF, true));
+    return Pair32{v, p};
+  } else if constexpr (STEP == 4) {
+    // with both operands v, the pair comes back as (even row's value, odd
+    // row's value) in every lane of the two rows: the same operands, in the
+    // same order, on both sides
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return Pair32{r[0], r[1]};
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return Pair32{r[0], r[1]};
+  }
 }
 
-// Butterfly over `width` lanes (power of two <= 64); every lane ends with the
-// same merged state, independent of lane order.
+template <int STEP>
+__device__ __forceinline__ void wave_step_f32(float v, float& a, float& b) {
+  const Pair32 p = wave_step_u32<STEP>(__float_as_uint(v));
+  a = __uint_as_float(p.a);
+  b = __uint_as_float(p.b);
+}
+
+template <int STEP>
+__device__ __forceinline__ void wave_step_u64(uint64_t v, uint64_t& a, uint64_t& b) {
+  const Pair32 lo = wave_step_u32<STEP>(uint32_t(v));
+  const Pair32 hi = wave_step_u32<STEP>(uint32_t(v >> 32));
+  a = uint64_t(lo.a) | (uint64_t(hi.a) << 32);
+  b = uint64_t(lo.b) | (uint64_t(hi.b) << 32);
+}
+
+template <int STEP>
+__device__ __forceinline__ Lse wave_step_lse(Lse v) {
+  Lse a, b;
+  wave_step_f32<STEP>(v.m, a.m, b.m);
+  wave_step_f32<STEP>(v.mL, a.mL, b.mL);
+  wave_step_f32<STEP>(v.s, a.s, b.s);
+  return lse_merge(a, b);
+}
+
+template <int STEP>
+__device__ __forceinline__ double wave_step_f64(double v) {
+  uint64_t a, b;
+  wave_step_u64<STEP>(uint64_t(__double_as_longlong(v)), a, b);
+  return __longlong_as_double((long long)a) + __longlong_as_double((long long)b);
+}
+
+template <int STEP>
+__device__ __forceinline__ long long wave_step_i64(long long v) {
+  uint64_t a, b;
+  wave_step_u64<STEP>(uint64_t(v), a, b);
+  return (long long)(a + b);
+}
+
+template <int STEP>
+__device__ __forceinline__ uint32_t wave_step_or(uint32_t v) {
+  const Pair32 p = wave_step_u32<STEP>(v);
+  return p.a | p.b;
+}
+
+template <int STEP>
+__device__ __forceinline__ int wave_step_i32(int v) {
+  const Pair32 p = wave_step_u32<STEP>(uint32_t(v));
+  return int(p.a + p.b);
+}
+
+// Every lane ends with the merged state of the whole wave.
 template <int width>
 __device__ __forceinline__ Lse wave_lse(Lse v) {
-#pragma unroll
-  for (int off = width / 2; off > 0; off >>= 1) v = lse_merge(v, shfl_xor_lse(v, off));
-  return v;
+  static_assert(width == kWave, "whole waves");
+  v = wave_step_lse<0>(v);
+  v = wave_step_lse<1>(v);
+  v = wave_step_lse<2>(v);
+  v = wave_step_lse<3>(v);
+  v = wave_step_lse<4>(v);
+  return wave_step_lse<5>(v);
 }
 
 template <int width>
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  static_assert(width == kWave, "whole waves");
+  v = wave_step_f64<0>(v);
+  v = wave_step_f64<1>(v);
+  v = wave_step_f64<2>(v);
+  v = wave_step_f64<3>(v);
+  v = wave_step_f64<4>(v);
+  return wave_step_f64<5>(v);
 }
 
 template <int width>
 __device__ __forceinline__ long long wave_sum_i64(long long v) {
-#pragma unroll
-  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  static_assert(width == kWave, "whole waves");
+  v = wave_step_i64<0>(v);
+  v = wave_step_i64<1>(v);
+  v = wave_step_i64<2>(v);
+  v = wave_step_i64<3>(v);
+  v = wave_step_i64<4>(v);
+  return wave_step_i64<5>(v);
 }
 
 template <int width>
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  static_assert(width == kWave, "whole waves");
+  v = wave_step_i32<0>(v);
+  v = wave_step_i32<1>(v);
+  v = wave_step_i32<2>(v);
+  v = wave_step_i32<3>(v);
+  v = wave_step_i32<4>(v);
+  return wave_step_i32<5>(v);
+}
+
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+  v = wave_step_or<0>(v);
+  v = wave_step_or<1>(v);
+  v = wave_step_or<2>(v);
+  v = wave_step_or<3>(v);
+  v = wave_step_or<4>(v);
+  return wave_step_or<5>(v);
 }
 
 // Block-wide sums in a fixed tree (butterfly in each wave, then the per-wave

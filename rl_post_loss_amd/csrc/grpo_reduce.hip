@@ -65,8 +65,7 @@ __global__ __launch_bounds__(kFinalThreads) void grpo_final_kernel(FinalArgs a) 
   gl = wave_sum_f64<kWave>(gl);
   ct = wave_sum_i64<kWave>(ct);
   n = wave_sum_i64<kWave>(n);
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) f |= uint32_t(__shfl_xor(int(f), off));
+  f = wave_or_u32(f);
   if (lane == 0) {
     sh_pl[wv] = pl;
     sh_kl[wv] = kl;

@@ -239,8 +239,8 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
     } else {
       // the owner lane of the taken token inside this wave
       const int owner = ca < nvec ? int(ca % NT) : int((aid - tail0) % NT);
-      xa = __shfl(xa, owner);
-      ya = __shfl(ya, owner);
+      xa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xa), owner));
+      ya = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ya), owner));
     }
 
     // ---- per-token epilogue -------------------------------------------------
@@ -265,9 +265,9 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       c2 = sh_bcast[1];
       omp = sh_bcast[2];
     } else {
-      G = __shfl(G, 0);
-      c2 = __shfl(c2, 0);
-      omp = __shfl(omp, 0);
+      G = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 0));
+      c2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c2), 0));
+      omp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(omp), 0));
     }
   } else {
     // backward only: per-row state from the forward pass, plus the policy
