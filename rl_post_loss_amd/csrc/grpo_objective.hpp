@@ -125,7 +125,8 @@ __device__ __forceinline__ TokObj token_objective(const Objective& o, float logp
   if constexpr (!kGeneral) {
     const K3Pair k = k3_expm1(d);
     r.kl = k.k3;
-    r.clipped = (adv > 0.0f && rho > o.hi) || (adv < 0.0f && rho < o.lo);
+    // bitwise, not short-circuit: no branch per token
+    r.clipped = ((adv > 0.0f) & (rho > o.hi)) | ((adv < 0.0f) & (rho < o.lo));
     const float unc = rho * adv;
     const float clp = fminf(fmaxf(rho, o.lo), o.hi) * adv;
     r.loss = -fminf(unc, clp);

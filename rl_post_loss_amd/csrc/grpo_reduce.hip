@@ -28,7 +28,20 @@ constexpr int kRedThreads = 256;
 #define GRPO_TOK_THREADS 256
 #endif
 constexpr int kTokThreads = GRPO_TOK_THREADS;
-constexpr int kTokQuads = 1024 / kTokThreads > 0 ? 1024 / kTokThreads : 1;
+#ifndef GRPO_TOK_QUADS
+#define GRPO_TOK_QUADS (1024 / GRPO_TOK_THREADS > 0 ? 1024 / GRPO_TOK_THREADS : 1)
+#endif
+constexpr int kTokQuads = GRPO_TOK_QUADS;
+// GRPO_TOK_PIPE: issue the next round's loads before the current round's
+// arithmetic and stores (mask words two rounds ahead).  GRPO_TOK_SPEC: data
+// loads that do not wait for the mask words (1: the first round, 2: every
+// round); a masked quad's values are then read but never used.
+#ifndef GRPO_TOK_PIPE
+#define GRPO_TOK_PIPE 0
+#endif
+#ifndef GRPO_TOK_SPEC
+#define GRPO_TOK_SPEC 0
+#endif
 
 // Scalar stage (one block): policy_loss = sum_i w_i P_i, kl = sum_i w_i K_i in
 // binary64, written as float32, plus the token and clip counts and the fault
@@ -191,28 +204,31 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
   // The first round's loads are issued before the prologue below (counts,
   // weights, advantage) waits on anything but the mask words.
   constexpr int QU = kTokQuads;
+  constexpr bool kPipe = GRPO_TOK_PIPE != 0;
   const int64_t n4 = a.T / 4;
-  uint32_t m4[QU];
+  const int64_t step = int64_t(QU) * kTokThreads;
+  uint32_t m4[QU], mn[QU];
   f32x4 lp[QU], od[QU], rf[QU], gn[QU], av[QU];
-  auto load_masks = [&](int64_t q0) {
+  auto load_masks_to = [&](int64_t q0, uint32_t (&m)[QU]) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const int64_t q = q0 + int64_t(u) * kTokThreads;
-      m4[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
-                               : 0x01010101u)
-                     : 0u;
+      m[u] = q < n4 ? (a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + base + 4 * q)
+                              : 0x01010101u)
+                    : 0u;
     }
   };
+  auto load_masks = [&](int64_t q0) { load_masks_to(q0, m4); };
   // Branch-free: a quad with no active token (or past the row's end) reads the
   // row's first quad instead, an in-bounds line that every thread of the row
   // touches anyway, and its values are never used.  Without per-quad branches
   // the compiler can wait for each quad's own loads alone rather than for
   // every outstanding load and store.
-  auto load_data = [&](int64_t q0) {
+  auto load_data = [&](int64_t q0, bool spec) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const int64_t q = q0 + int64_t(u) * kTokThreads;
-      const int64_t t0 = base + (m4[u] != 0 ? 4 * q : 0);
+      const int64_t t0 = base + ((spec ? q < n4 : m4[u] != 0) ? 4 * q : 0);
       lp[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.logp + t0));
       od[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.old + t0));
       rf[u] = gn[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -236,11 +252,14 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
     r_pre = rsrc[g_s + (tid < g_n ? tid : 0)];
   }
   const bool staged = kWeights == 2 && a.rewards != nullptr && g_n <= kTokThreads;
-  if (vec) load_masks(tid);
+  if (vec) {
+    load_masks(tid);
+    if (kPipe && tid + step < n4) load_masks_to(tid + step, mn);
+  }
   // stage the rewards before any data load is issued, so that waiting for
   // them never waits for those loads
   if (staged && tid < g_n) sh_r[tid] = r_pre;
-  if (vec) load_data(tid);
+  if (vec) load_data(tid, GRPO_TOK_SPEC >= 1);
   float adv;
   long long Li = 0;
   double wi;
@@ -299,38 +318,65 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
   // gains g * 0: 0 for every finite g, NaN otherwise.  One test after the
   // loop then flags exactly the sequences with a non-finite value.
   float gz = 0.0f;
+  // the clip bounds as kernel constants in canonical form, so that the
+  // per-token clamp needs no canonicalisation of them
+  Objective obj = a.obj;
+  obj.lo = __builtin_canonicalizef(obj.lo);
+  obj.hi = __builtin_canonicalizef(obj.hi);
   if (vec) {
-    for (int64_t q0 = tid; q0 < n4; q0 += QU * kTokThreads) {
-      if (q0 != tid) {
+    int cn = 0;
+    for (int64_t q0 = tid; q0 < n4; q0 += step) {
+      if (!kPipe && q0 != tid) {
         load_masks(q0);
-        load_data(q0);
+        load_data(q0, GRPO_TOK_SPEC >= 2);
+      }
+      // this round's values; with kPipe the next round's loads go out now
+      uint32_t cm[QU];
+      f32x4 clp[QU], cod[QU], crf[QU], cgn[QU], cav[QU];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        cm[u] = m4[u];
+        clp[u] = lp[u];
+        cod[u] = od[u];
+        crf[u] = rf[u];
+        cgn[u] = gn[u];
+        cav[u] = av[u];
+      }
+      if (kPipe && q0 + step < n4) {
+#pragma unroll
+        for (int u = 0; u < QU; ++u) m4[u] = mn[u];
+        load_data(q0 + step, GRPO_TOK_SPEC >= 2);
+        if (q0 + 2 * step < n4) load_masks_to(q0 + 2 * step, mn);
       }
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
         const int64_t q = q0 + int64_t(u) * kTokThreads;
         if (q >= n4) continue;
         const int64_t t0 = base + 4 * q;
-        const float lpv[4] = {lp[u].x, lp[u].y, lp[u].z, lp[u].w};
-        const float odv[4] = {od[u].x, od[u].y, od[u].z, od[u].w};
-        const float rfv[4] = {rf[u].x, rf[u].y, rf[u].z, rf[u].w};
-        const float gnv[4] = {gn[u].x, gn[u].y, gn[u].z, gn[u].w};
-        const float avv[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+        const float lpv[4] = {clp[u].x, clp[u].y, clp[u].z, clp[u].w};
+        const float odv[4] = {cod[u].x, cod[u].y, cod[u].z, cod[u].w};
+        const float rfv[4] = {crf[u].x, crf[u].y, crf[u].z, crf[u].w};
+        const float gnv[4] = {cgn[u].x, cgn[u].y, cgn[u].z, cgn[u].w};
+        const float avv[4] = {cav[u].x, cav[u].y, cav[u].z, cav[u].w};
         float gv[4] = {0.f, 0.f, 0.f, 0.f}, tl[4] = {0.f, 0.f, 0.f, 0.f}, tk[4] = {0.f, 0.f, 0.f, 0.f};
+        // every token of the quad is evaluated and the mask selects the
+        // results: straight-line code for all tokens of the round, so their
+        // independent chains interleave (a masked token's inputs may be any
+        // bits, its values are discarded by the selects)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if ((m4[u] >> (8 * j)) & 0xffu) {
-            const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
-            TokObj r = token_objective<kGeneral>(a.obj, lpv[j], odv[j], d, has_atok ? avv[j] : adv,
-                                                 gnv[j], keep);
-            if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, odv[j], gnv[j], has_gen);
-            gv[j] = seqlv ? wg * r.g + useq : wg * r.g;
-            tl[j] = r.loss;
-            tk[j] = r.kl;
-            p = p + double(r.loss);
-            k = k + double(r.kl);
-            c += r.clipped ? 1 : 0;
-            gz = fmaf(gv[j], 0.0f, gz);
-          }
+          const bool on = ((cm[u] >> (8 * j)) & 0xffu) != 0;
+          const float d = has_ref ? rfv[j] - lpv[j] : 0.0f;
+          TokObj r = token_objective<kGeneral>(obj, lpv[j], odv[j], d, has_atok ? avv[j] : adv,
+                                               gnv[j], keep);
+          if (seqlv) seq_token(obj, r, gspo, lseq, cseq, odv[j], gnv[j], has_gen);
+          gv[j] = on ? (seqlv ? wg * r.g + useq : wg * r.g) : 0.0f;
+          tl[j] = on ? r.loss : 0.0f;
+          tk[j] = on ? r.kl : 0.0f;
+          p = p + double(tl[j]);
+          k = k + double(tk[j]);
+          cn += (on & r.clipped) ? 1 : 0;
+          gz = fmaf(gv[j], 0.0f, gz);
         }
         if (a.dlogp)
           __builtin_nontemporal_store(f32x4{gv[0], gv[1], gv[2], gv[3]},
@@ -339,6 +385,7 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
         if (a.out_kl) *reinterpret_cast<f32x4*>(a.out_kl + t0) = f32x4{tk[0], tk[1], tk[2], tk[3]};
       }
     }
+    c += cn;
   } else {
     for (int64_t t = tid; t < a.T; t += kTokThreads) {
       const int64_t s = base + t;
@@ -347,9 +394,9 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
         const float lps = a.logp[s];
         const float d = has_ref ? a.ref[s] - lps : 0.0f;
         const float ods = a.old[s], gns = has_gen ? a.gen[s] : 0.0f;
-        TokObj r = token_objective<kGeneral>(a.obj, lps, ods, d, has_atok ? a.adv_tok[s] : adv, gns,
+        TokObj r = token_objective<kGeneral>(obj, lps, ods, d, has_atok ? a.adv_tok[s] : adv, gns,
                                              keep);
-        if (seqlv) seq_token(a.obj, r, gspo, lseq, cseq, ods, gns, has_gen);
+        if (seqlv) seq_token(obj, r, gspo, lseq, cseq, ods, gns, has_gen);
         g = seqlv ? wg * r.g + useq : wg * r.g;
         tl = r.loss;
         tk = r.kl;
