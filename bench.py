@@ -506,6 +506,66 @@ def run_logits_record(args, wl, inp, reduction, objective="default", pool=None, 
     return rec
 
 
+def run_autograd_record(args, wl, inp, precompute, upstream=1.0):
+    """The autograd entry ("GRPO Loss", Entry Point: loss.backward() puts
+    d loss / d logits into the policy's .grad): one step is grpo_loss(...)
+    then loss.backward() on a leaf policy tensor whose .grad is cleared
+    first, so autograd hands over the gradient without accumulating.
+    precompute=False (default): forward-only kernel, then a gradient pass
+    that streams the policy again; precompute=True: the fused kernel in the
+    forward (its [B, T, V] gradient held until the backward), then an
+    in-place scale by the upstream gradient (a no-op for 1)."""
+    import torch
+    import rl_post_loss_amd as rpl
+
+    B, T, V = wl.B, wl.T, wl.V
+    red = wl.reductions[0]
+    kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta, reduction=red,
+              alpha=wl.alpha if red == "length_alpha" else None)
+    kw.update(wl.groups_kwargs())
+    pol = inp["policy"].detach().requires_grad_(True)
+
+    def step():
+        pol.grad = None
+        loss, _, _ = rpl.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                   inp["rewards"], inp["mask"], precompute_grad=precompute, **kw)
+        (loss if upstream == 1.0 else loss * upstream).backward()
+        return loss
+
+    for _ in range(max(1, args.warmup)):
+        ref_loss = step().detach().clone()
+    torch.cuda.synchronize()
+    gview = pol.grad.view(torch.int16 if pol.grad.element_size() == 2 else torch.int32)
+    ref_sum = int(gview.sum(dtype=torch.int64))
+    losses = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        losses.append(step().detach())
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gview = pol.grad.view(torch.int16 if pol.grad.element_size() == 2 else torch.int32)
+    repro = (all(torch.equal(l.view(torch.int32), ref_loss.view(torch.int32)) for l in losses)
+             and int(gview.sum(dtype=torch.int64)) == ref_sum)
+    rows = B * T
+    active = int(inp["mask"].sum())
+    alg = byte_model(wl, active, rows)
+    rec = {
+        "workload": f"{wl.name} through grpo_loss(...).backward() "
+                    + ("with precompute_grad=True (fused kernel in the forward, gradient held "
+                       "until the backward)" if precompute else
+                       "(forward-only pass, then a gradient pass that re-reads the policy)")
+                    + ("" if upstream == 1.0 else f", upstream gradient {upstream}"),
+        "ms_per_step": ms, "tokens_per_s": rows / (ms * 1e-3),
+        "hbm_fraction_of_step": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes": alg, "bit_reproducible": bool(repro),
+        "extra_memory_bytes_held": rows * V * pol.element_size() if precompute else 16 * rows,
+        "timing": "host wall clock over the timed steps, synchronized at both ends",
+    }
+    pol.grad = None
+    return rec
+
+
 def run_token_record(args, wl, pool=None, workers=1, copies=None):
     """Logprob-level token loss (no vocabulary).  The 71 MB working set fits
     the memory-side cache, so the timed calls rotate over enough input copies
@@ -687,6 +747,12 @@ def run_all(args, pool, workers):
                                     sample_rows=SAMPLE_ROWS[name])
             if name == "logits_v151936":
                 head = rec
+                for pre, up in ((False, 1.0), (True, 1.0), (False, 0.5), (True, 0.5)):
+                    akey = ("autograd_precompute" if pre else "autograd_split") + \
+                        ("" if up == 1.0 else "_upstream_0.5")
+                    _log(f"timing {name} {akey}")
+                    subs[f"{name}:{akey}"] = run_autograd_record(args, wl, inp, pre, up)
+                    torch.cuda.empty_cache()
             else:
                 subs[key] = rec
         del inp
