@@ -234,10 +234,12 @@ typedef enum grpo_tis {
 typedef struct grpo_groups {
   int32_t samples_per_prompt;       /* > 1, or 0 when group_boundaries is given */
   int32_t num_groups;               /* CSR: number of groups; ignored for uniform groups */
-  const int64_t *group_boundaries;  /* HOST pointer or NULL; copied during the call (a
-                                       host-to-device copy on the call's stream: the only
-                                       operation other than kernel launches that any
-                                       entry point enqueues) */
+  const int64_t *group_boundaries;  /* HOST pointer or NULL; read during the call and
+                                       passed to the device as kernel arguments (240
+                                       offsets per launch of a small copy kernel), so
+                                       every entry point enqueues kernel launches only
+                                       and may be captured in a HIP graph; the array is
+                                       not read after the call returns */
   int32_t leave_one_out;            /* 0 or 1 */
   int32_t scale_by_std;             /* 0 or 1 (the usual GRPO setting is 1) */
   double std_eps;                   /* floor of the std, > 0 (usually 1e-6) */

@@ -24,6 +24,7 @@ hipError_t launch_real(const RealArgs& a, hipStream_t stream);
 hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_gdpo(const GdpoArgs& a, hipStream_t s);
+hipError_t launch_copy_offsets(const int64_t* host, int64_t n, int64_t* dev, hipStream_t s);
 bool resident_fits(int64_t V, int esize);
 }  // namespace grpo
 
@@ -187,8 +188,7 @@ grpo_status copy_offsets(const Ws& w, const grpo_groups* g, hipStream_t s, Group
   out->num_groups = g->samples_per_prompt > 0 ? 0 : g->num_groups;
   if (out->num_groups > 0) {
     int64_t* dev = w.at<int64_t>(w.l.offsets);
-    if (hipMemcpyAsync(dev, g->group_boundaries, size_t(out->num_groups + 1) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+    if (launch_copy_offsets(g->group_boundaries, int64_t(out->num_groups) + 1, dev, s) != hipSuccess)
       return GRPO_ERR_HIP;
     out->offsets = dev;
   }
@@ -230,8 +230,7 @@ grpo_status run_prep(const Ws& w, const float* rewards, const uint8_t* mask, int
   a.offsets = nullptr;
   if (a.num_groups > 0) {
     int64_t* dev = w.at<int64_t>(w.l.offsets);
-    if (hipMemcpyAsync(dev, g->group_boundaries, size_t(a.num_groups + 1) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+    if (launch_copy_offsets(g->group_boundaries, int64_t(a.num_groups) + 1, dev, s) != hipSuccess)
       return GRPO_ERR_HIP;
     a.offsets = dev;
   }
@@ -852,8 +851,7 @@ grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const
   a.num_groups = ng;
   if (ng > 0) {
     int64_t* dev = w.at<int64_t>(w.l.offsets);
-    if (hipMemcpyAsync(dev, groups->group_boundaries, size_t(ng + 1) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+    if (launch_copy_offsets(groups->group_boundaries, int64_t(ng) + 1, dev, s) != hipSuccess)
       return GRPO_ERR_HIP;
     a.offsets = dev;
   }
@@ -900,8 +898,7 @@ grpo_status grpo_gdpo_advantages(const float* rewards, int32_t num_components, i
   a.num_groups = ng;
   if (ng > 0) {
     int64_t* dev = w.at<int64_t>(w.l.offsets);
-    if (hipMemcpyAsync(dev, groups->group_boundaries, size_t(ng + 1) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+    if (launch_copy_offsets(groups->group_boundaries, int64_t(ng) + 1, dev, s) != hipSuccess)
       return GRPO_ERR_HIP;
     a.offsets = dev;
   }

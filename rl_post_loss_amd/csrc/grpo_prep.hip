@@ -138,6 +138,33 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// CSR group offsets reach the device as kernel arguments, kOffsetChunk
+// values per launch: a call enqueues kernel launches only (no host-to-device
+// copy), so calls with CSR groups can be captured in a HIP graph, and the
+// host array is no longer read once the call returns.
+constexpr int kOffsetChunk = 240;
+struct OffsetChunk {
+  int64_t v[kOffsetChunk];
+  int32_t n;
+};
+
+__global__ __launch_bounds__(256) void grpo_offsets_kernel(OffsetChunk c, int64_t* dst) {
+  if (int(threadIdx.x) < c.n) dst[threadIdx.x] = c.v[threadIdx.x];
+}
+
+hipError_t launch_copy_offsets(const int64_t* host, int64_t n, int64_t* dev, hipStream_t stream) {
+  for (int64_t k0 = 0; k0 < n; k0 += kOffsetChunk) {
+    OffsetChunk c;
+    c.n = int32_t(n - k0 < kOffsetChunk ? n - k0 : kOffsetChunk);
+    for (int32_t j = 0; j < c.n; ++j) c.v[j] = host[k0 + j];
+    for (int32_t j = c.n; j < kOffsetChunk; ++j) c.v[j] = 0;
+    hipLaunchKernelGGL(grpo_offsets_kernel, dim3(1), dim3(256), 0, stream, c, dev + k0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // Workspace clearing (optional: every call initialises what it reads).
 __global__ void grpo_zero_kernel(uint4* p, size_t n16) {
   for (size_t k = size_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n16;

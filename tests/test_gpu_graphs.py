@@ -1,7 +1,8 @@
-"""The entry points are capturable in a HIP graph (uniform groups: no host
-copy, no memset, no synchronisation inside a call).  Every replay is checked
-bitwise against the eager result, with eager work, synchronisations and input
-updates between replays."""
+"""The entry points are capturable in a HIP graph: a call enqueues kernel
+launches only (no host copy, no memset, no synchronisation), with uniform
+or CSR groups (CSR offsets travel as kernel arguments).  Every replay is
+checked bitwise against the eager result, with eager work,
+synchronisations and input updates between replays."""
 
 import math
 
@@ -37,13 +38,20 @@ def _capture(fn):
     return g
 
 
-def test_token_loss_graph_replays(gpu_lib):
+@pytest.mark.parametrize("groups", ["uniform", "csr"])
+def test_token_loss_graph_replays(gpu_lib, groups):
     rpl = gpu_lib
     wl = TOKEN_WORKLOADS["token_loss_ragged"]
-    announce("graph token loss")
+    announce(f"graph token loss {groups}")
     a = make_token_inputs(wl, device=DEV, seed=31, B=64, T=512)
     b = make_token_inputs(wl, device=DEV, seed=32, B=64, T=512)
     kw = dict(samples_per_prompt=16, reduction="sequence_mean", per_token=True)
+    if groups == "csr":
+        # 30 CSR groups of 2 and 4 samples summing to B = 64
+        sizes = [2] * 27 + [4] * 2 + [2]
+        kw = dict(group_boundaries=[0] + [int(v) for v in torch.tensor(sizes).cumsum(0)],
+                  reduction="sequence_mean", per_token=True, leave_one_out=True)
+        assert kw["group_boundaries"][-1] == 64
     static = {k: v.clone() for k, v in a.items()}
     box = {}
 
@@ -71,12 +79,20 @@ def test_token_loss_graph_replays(gpu_lib):
         del junk
 
 
-def test_logits_graph_replays(gpu_lib):
+@pytest.mark.parametrize("mode", ["uniform", "csr", "csr_noalloc"])
+def test_logits_graph_replays(gpu_lib, mode):
     rpl = gpu_lib
-    wl = LogitsWorkload(name="graph", group_sizes=(4, 4), T=24, V=12000, dtype="bf16", logit_std=2.0,
-                        ref_noise_std=math.sqrt(0.1), old_noise_std=math.sqrt(0.05), reward_p=0.5,
-                        len_range=(1, 24))
-    announce("graph logits")
+    if mode == "uniform":
+        wl = LogitsWorkload(name="graph", group_sizes=(4, 4), T=24, V=12000, dtype="bf16",
+                            logit_std=2.0, ref_noise_std=math.sqrt(0.1),
+                            old_noise_std=math.sqrt(0.05), reward_p=0.5, len_range=(1, 24))
+    else:
+        wl = LogitsWorkload(name="graph_csr", group_sizes=(4, 2, 6, 2, 2), T=24, V=12000,
+                            dtype="bf16", logit_std=2.0, ref_noise_std=math.sqrt(0.1),
+                            old_noise_std=math.sqrt(0.05), reward_p=0.5, len_range=(1, 24),
+                            csr=True, leave_one_out=True, reductions=("sequence_mean",))
+    entry = rpl.grpo_loss_fwd_bwd_noalloc if mode == "csr_noalloc" else rpl.grpo_loss_fwd_bwd
+    announce(f"graph logits {mode}")
     a = make_logits_inputs(wl, device=DEV, seed=41)
     b = make_logits_inputs(wl, device=DEV, seed=42)
     kw = gpu_kwargs(wl)
@@ -85,9 +101,9 @@ def test_logits_graph_replays(gpu_lib):
     box = {}
 
     def call():
-        box["res"] = rpl.grpo_loss_fwd_bwd(static["policy"], static["ref"], static["action_ids"],
-                                           static["old_logps"], static["rewards"], static["mask"],
-                                           grad_out=grad, per_token=True, out=box.get("res"), **kw)
+        box["res"] = entry(static["policy"], static["ref"], static["action_ids"],
+                           static["old_logps"], static["rewards"], static["mask"],
+                           grad_out=grad, per_token=True, out=box.get("res"), **kw)
 
     g = _capture(call)
     res = box["res"]
