@@ -21,3 +21,13 @@ def gpu_lib():
     import rl_post_loss_amd as rpl
     rpl.load_library()  # raises if the shared library was not built
     return rpl
+
+
+def pytest_sessionstart(session):
+    # GRPO_TEST_LIB: run the tests against another build of libgrpo (the
+    # host-sanitized build of tests/test_host_sanitizers.py); unset on every
+    # ordinary run
+    path = os.environ.get("GRPO_TEST_LIB")
+    if path:
+        from rl_post_loss_amd import _abi
+        _abi._lib = _abi.load_library(path)
