@@ -23,10 +23,12 @@
 // With the global normalization the returns are kept in binary64 in the
 // workspace and each sequence leaves the moments (count, mean, sum of squared
 // deviations) of its active values: per thread from sums of deviations
-// from its first value, merged across the block, and one block merges the
-// sequences' moments with Chan et al.'s pairwise update in a
-// fixed tree, so results repeat bit for bit; a flat pass over the slots then
-// writes (A - mu) / sd.  Three launches in all.
+// from its first value, merged across the block.  The output pass then
+// writes (A - mu) / sd; each of its blocks first issues its loads, then
+// merges the sequences' moments with Chan et al.'s pairwise update in one
+// fixed tree (the same bits in every block, so results repeat bit for bit).
+// Two launches in all (three beyond kFusedMomentsMaxB sequences, where one
+// block merges the moments once).
 
 #include "../../include/grpo.h"
 #include "grpo_device.hpp"
@@ -376,14 +378,62 @@ __global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(Tok
 }
 
 constexpr int kNormThreads = 256;
-constexpr int kNormQuads = 1;   // quads of 4 slots per thread (4 measured slower: fewer waves)
+#ifndef GRPO_NORM_QUADS
+#define GRPO_NORM_QUADS 4
+#endif
+constexpr int kNormQuads = GRPO_NORM_QUADS;  // quads of 4 slots per thread
+// Up to this many sequences every block of the output pass merges the
+// sequences' moments itself (no separate one-block kernel and launch);
+// beyond it the merge runs once in grpo_tokadv_moments_kernel.
+constexpr int64_t kFusedMomentsMaxB = 4096;
+
+// mu and the floored sd of the global masked normalization, from the
+// sequences' moments merged in one fixed tree: thread t merges sequences
+// t, t + NT, ... in order, then the block tree of block_moments.  Every block
+// that runs it holds the same bits; with `publish` it also stores the count,
+// the moments and the no-token fault in the header.
+template <int NT>
+__device__ void merge_global_moments(const TokAdvArgs& a, double* sh_mom, double* sh_out,
+                                     bool publish) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x;
+  Moments mo{0.0, 0.0, 0.0};
+  for (int64_t k = tid; k < a.B; k += NT) {
+    const int32_t n = a.L[k];
+    if (n > 0) mo = moments_merge(mo, Moments{double(n), a.mean[k], a.M2[k]});
+  }
+  mo = block_moments<NT>(mo, sh_mom);
+  if (tid == 0) {
+    const long long n = (long long)mo.n;
+    const double mu = n > 0 ? mo.m : 0.0;
+    const double var = n > 0 ? mo.M2 / mo.n : 0.0;
+    const double sd = sqrt(var > 1e-8 ? var : 1e-8);
+    sh_out[0] = mu;
+    sh_out[1] = sd;
+    if (publish) {
+      a.hdr->num_tokens = n;
+      a.hdr->mu = mu;
+      a.hdr->sd = sd;
+      if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
+    }
+  }
+  __syncthreads();
+}
 
 // Output pass over the slots: (A - mu) / sd at active slots, 0 elsewhere;
 // kNormQuads quads of four slots per thread when the rows allow 16-byte
-// accesses, else one slot per thread.
+// accesses, else one slot per thread.  kFused: mu and sd from the
+// sequences' moments, merged by every block (block 0 publishes them).
+template <bool kFused>
 __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvArgs a, int vec) {
 #pragma clang fp contract(off)
-  const double mu = a.hdr->mu, sd = a.hdr->sd;
+  __shared__ double sh_mom[3 * (kNormThreads / kWave)];
+  __shared__ double sh_musd[2];
+  double mu = 0.0, sd = 1.0;
+  if constexpr (!kFused) {
+    mu = a.hdr->mu;
+    sd = a.hdr->sd;
+  }
   const bool rpp = a.estimator == GRPO_ADV_REINFORCE_PP;
   const int64_t rows = a.B * a.T;
   if (vec) {
@@ -406,6 +456,12 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
         hi[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.V + src + 2));
       }
     }
+    if constexpr (kFused) {
+      // the merge runs while this block's loads are in flight
+      merge_global_moments<kNormThreads>(a, sh_mom, sh_musd, blockIdx.x == 0);
+      mu = sh_musd[0];
+      sd = sh_musd[1];
+    }
 #pragma unroll
     for (int u = 0; u < kNormQuads; ++u) {
       const int64_t q = q0 + int64_t(u) * kNormThreads;
@@ -425,8 +481,13 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
         o[j] = ((m4[u] >> (8 * j)) & 0xffu) ? float(clamp_adv(a, (v[j] - mu) / sd)) : 0.0f;
       __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(a.out + 4 * q));
     }
-    if (q0 == 0 && a.status) *a.status = a.hdr->status;
+    if (q0 == 0 && a.status) *a.status = a.hdr->status;  // block 0, after it published
   } else {
+    if constexpr (kFused) {
+      merge_global_moments<kNormThreads>(a, sh_mom, sh_musd, blockIdx.x == 0);
+      mu = sh_musd[0];
+      sd = sh_musd[1];
+    }
     const int64_t gid = int64_t(blockIdx.x) * kNormThreads + threadIdx.x;
     if (gid >= rows) return;
     const bool act = adv_active(a, gid);
@@ -443,7 +504,8 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
 hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(grpo_tokadv_kernel, dim3(unsigned(a.B)), dim3(kAdvThreads), 0, s, a);
   if (!a.normalize) return hipGetLastError();
-  hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
+  const bool fused = a.B <= kFusedMomentsMaxB;
+  if (!fused) hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
   const int64_t rows = a.B * a.T;
   const int vec = (a.T % 4 == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 &&
@@ -451,8 +513,12 @@ hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s) {
   const int64_t per_block = vec ? int64_t(kNormThreads) * kNormQuads : int64_t(kNormThreads);
   const int64_t items = vec ? rows / 4 : rows;
   const int64_t blocks = (items + per_block - 1) / per_block;
-  hipLaunchKernelGGL(grpo_tokadv_norm_kernel, dim3(unsigned(blocks)), dim3(kNormThreads), 0, s, a,
-                     vec);
+  if (fused)
+    hipLaunchKernelGGL(grpo_tokadv_norm_kernel<true>, dim3(unsigned(blocks)), dim3(kNormThreads),
+                       0, s, a, vec);
+  else
+    hipLaunchKernelGGL(grpo_tokadv_norm_kernel<false>, dim3(unsigned(blocks)), dim3(kNormThreads),
+                       0, s, a, vec);
   return hipGetLastError();
 }
 
