@@ -717,6 +717,39 @@ def run_single(args, pool, workers):
     print(json.dumps(_line(rec, args, name)), flush=True)
 
 
+def memory_ceiling(gib=8):
+    """The box's own streaming rates, for reading the fractions of 8 TB/s in
+    context: torch's sum over a bf16 tensor (read), its zero fill (write) and
+    its copy (half read, half write), GIB GiB each way, median of 5 after a
+    warm-up, HIP events on the current stream."""
+    import torch
+    n = (gib << 30) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("read", lambda: x.sum(dtype=torch.float32), n * 2),
+                             ("write", lambda: y.zero_(), n * 2),
+                             ("copy", lambda: y.copy_(x), n * 4)):
+        fn()
+        ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        t = _median(ms)
+        out[f"{name}_GBps"] = nbytes / (t * 1e-3) / 1e9
+        out[f"{name}_frac_of_peak"] = out[f"{name}_GBps"] / PEAK_HBM_GBS
+    out["method"] = (f"torch sum (read), zero_ (write) and copy_ (read + write) over {gib} GiB of "
+                     "bf16, median of 5 timed with events; context for the fractions of 8 TB/s, "
+                     "not a limit the kernels are held to")
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 # sample of slots the CPU baseline takes from each logits workload (about
 # 2-3 s of oracle work over 16 processes)
 SAMPLE_ROWS = {"tiny_logits": 128, "logits_v32000": 16384, "logits_v151936": 2048,
@@ -763,6 +796,8 @@ def run_all(args, pool, workers):
         torch.cuda.empty_cache()
     line = _line(head, args, "logits_v151936")
     line["configs"] = subs
+    _log("timing the box's own streaming rates")
+    line["memory_ceiling"] = memory_ceiling()
     print(json.dumps(line), flush=True)
 
 

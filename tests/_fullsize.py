@@ -22,7 +22,7 @@ import numpy as np
 import torch
 
 import oracle
-from _parity import GRAD16_BAR, check_grad_row, token_branches
+from _parity import GRAD16_BAR, check_grad_row, seq_branches, token_branches
 
 
 def host_workers():
@@ -47,7 +47,10 @@ def stream_oracle(inp, grad, wl, cfg, groups, *, chunk=32, workers=None, announc
                   gen_logps=None):
     """Runs the oracle over the whole batch and compares every active gradient
     row.  Returns (oracle result without grad, stats).  ``grad`` is the GPU
-    gradient [B, T, V] (or None to skip the gradient)."""
+    gradient [B, T, V] (or None to skip the gradient); ``gen_logps`` the
+    host [B, T] generating log-probs of the off-policy weight, if any.  For
+    the sequence-level losses the gradient rows come from the oracle's second
+    pass, once every sequence's log-ratio is known."""
     B, T, V = inp["policy"].shape
     dev = inp["policy"].device
     pol = inp["policy"].reshape(B * T, V)
@@ -106,7 +109,11 @@ def stream_oracle(inp, grad, wl, cfg, groups, *, chunk=32, workers=None, announc
         return res, stats
     # rows that missed the plain bar: branch candidates and propagated bounds
     if state["failed"]:
-        branches = token_branches(res, cfg, mask, base)
+        if cfg.pg_loss in oracle.SEQUENCE_PG:
+            h = dict(old_logps=h_old, gen_logps=gen_logps)
+            branches = seq_branches(res, cfg, mask, h, groups, base)
+        else:
+            branches = token_branches(res, cfg, mask, base)
         for (i, t) in state["failed"]:
             r = i * T + t
             x = _to_host_f32(pol[r:r + 1])[0]

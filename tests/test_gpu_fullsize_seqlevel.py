@@ -3,21 +3,22 @@ in-group classification) and of sequence-masked truncated importance
 sampling, through the C ABI, in the launch configuration bench.py times
 (forward pass, sequence phase, gradient pass).
 
-logits_v32000 (B = 64 in 8 groups of 8, T = 1024, V = 32,000 bf16, ragged
-lengths 64..1024: about 35 K active rows) is small enough for the fp64
-oracle's forward pass over every active row, so every per-token and
-per-sequence value, the scalars and the REAL coupling within groups are
-compared whole; gradient rows are compared on a sample (the oracle's whole
-gradient would be 10^9 values).
+Both full-size batches are compared whole: the fp64 oracle streams every
+active row a chunk at a time on the host's cores (tests/_fullsize.py), its
+second pass forming every gradient row once the sequences' log-ratios are
+known, and each is compared with the GPU's row as it is formed.
 
-logits_v151936 (B = 32, T = 2048, V = 151,936 bf16, full mask: 65,536 rows)
-is too large for the oracle whole.  There GSPO is checked on whole
-sequences (first, last, one clipped) that the oracle recomputes row by row (s_i, every
-token's log-prob, loss and KL, sampled gradient rows), and on every sequence
-by properties: s_i is the mean of the sequence's own per-token log-ratios,
-the token loss is constant along a sequence, the scalars are the
-fixed-order sums of the per-token outputs, every gradient row sums to ~0 and
-a second call is bit-identical.
+logits_v32000 (B = 64 in 8 groups of 8, T = 1024, V = 32,000 bf16, ragged
+lengths 64..1024: about 35 K active rows): GSPO, REAL and seq-mask-tis;
+every per-token and per-sequence value, the scalars, the REAL coupling
+within groups and every gradient row.
+
+logits_v151936 (B = 32, T = 2048, V = 151,936 bf16, full mask: 65,536
+rows): GSPO and REAL compared whole in the same way; GSPO is also checked
+on every sequence by properties (s_i is the mean of the sequence's own
+per-token log-ratios, the token loss is constant along a sequence), on three
+sequences the oracle recomputes alone, every gradient row sums to ~0 and a
+second call is bit-identical.
 
 Old log-probs are shifted per sequence so that GSPO clips some sequences on
 both sides of the band and seq-mask drops some sequences.
@@ -35,6 +36,7 @@ from _parity import (GRAD16_BAR, LOGP_ABS_ERR, SEQ_ABS_ERR, assert_grad_rows_sum
                      cfg_from, check_grad_row, compare_exact_parts, compare_scalars,
                      compare_seq_outputs, compare_token_values, gpu_kwargs, host_inputs,
                      sample_rows, seq_branches, to_np, token_branches)
+from _fullsize import masked_rows_zero, stream_oracle
 from workloads import WORKLOADS, make_gen_logps, make_logits_inputs, shift_by_sequence
 
 pytestmark = pytest.mark.gpu
@@ -102,10 +104,10 @@ def test_fullsize_v32000_whole(gpu_lib, v32k, kw):
     mask = h["mask"].astype(bool)
     cfg = cfg_from(wl, red, **obj)
     groups = wl.groups_kwargs()
-    announce(f"{name}: oracle forward over {int(mask.sum())} active rows")
-    ref = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"], mask,
-                                   h["rewards"], groups=groups, cfg=cfg, want_grad=False,
-                                   gen_logps=h.get("gen_logps"))
+    announce(f"{name}: oracle over {int(mask.sum())} active rows, every gradient row compared")
+    ref, st = stream_oracle(inp, grad, wl, cfg, groups, announce=announce,
+                            gen_logps=h.get("gen_logps"))
+    announce(f"{name}: oracle done, {st}")
     compare_exact_parts(res, ref, name)
     glp = to_np(res.tok_logp)
     assert np.all(np.abs(glp - ref.tok["logp"])[mask] <= LOGP_ABS_ERR), name + " tok_logp"
@@ -125,19 +127,9 @@ def test_fullsize_v32000_whole(gpu_lib, v32k, kw):
     clipped = int(res.counts[1])
     assert abs(clipped - ref.clipped) <= int(br[0].sum()), (clipped, ref.clipped)
 
-    rows = sample_rows(B, T, mask, np.random.default_rng(3), n=48)
-    announce(f"{name}: {len(rows)} sampled gradient rows (sequences at a clip bound: {amb_seq})")
-    for r in rows:
-        i, t = divmod(r, T)
-        g = grad[i, t].double().cpu().numpy()
-        if not mask[i, t]:
-            assert np.all(g == 0.0), (name, i, t)
-            continue
-        check_grad_row(g, h["policy"][i, t], h["action_ids"][i, t], (i, t), br, "bf16", name)
-
-    announce(f"{name}: masked rows, row sums")
+    announce(f"{name}: masked rows, row sums (sequences at a clip bound: {amb_seq})")
     g2 = grad.view(B * T, V)
-    assert int(torch.count_nonzero(g2[~inp["mask"].view(-1)])) == 0
+    assert masked_rows_zero(grad, inp["mask"]), name
     assert_grad_rows_sum_to_zero(g2)
     announce(f"{name}: run 2")
     _rerun_bitwise(gpu_lib, inp, grad, res, gkw, gen)
@@ -260,3 +252,41 @@ def test_fullsize_gspo_headline(gpu_lib):
     assert_grad_rows_sum_to_zero(grad.view(B * T, V))
     announce(f"{name}: run 2")
     _rerun_bitwise(gpu_lib, inp, grad, res, gkw, None)
+
+
+@pytest.mark.parametrize("kw", [dict(pg_loss="gspo", reduction="sequence_mean"),
+                                dict(pg_loss="real")], ids=_id)
+def test_fullsize_headline_seqlevel_whole(gpu_lib, kw):
+    """GSPO and REAL at V = 151,936 compared whole: every token's log-prob,
+    loss and KL, every s_i and per-sequence total, the scalars and every
+    gradient row, against the oracle streamed over all 65,536 rows."""
+    wl = WORKLOADS["logits_v151936"]
+    obj = dict(kw)
+    red = obj.pop("reduction", None)
+    name = f"full size logits_v151936 {_id(kw)} whole"
+    B, T, V = wl.B, wl.T, wl.V
+    announce(f"{name}: generating")
+    inp = make_logits_inputs(wl, device=DEV, seed=0)
+    inp["old_logps"] = shift_by_sequence(inp["old_logps"], seed=0, spread=0.4)
+    gkw = gpu_kwargs(wl, red, **obj)
+    grad = torch.empty((B, T, V), dtype=torch.bfloat16, device=DEV)
+    announce(f"{name}: run")
+    res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                    inp["old_logps"], inp["rewards"], inp["mask"], grad_out=grad,
+                                    per_token=True, **gkw)
+    torch.cuda.synchronize()
+    assert int(res.status[0]) == 0
+    cfg = cfg_from(wl, red, **obj)
+    groups = wl.groups_kwargs()
+    mask = inp["mask"].cpu().numpy().astype(bool)
+    ref, st = stream_oracle(inp, grad, wl, cfg, groups, announce=announce)
+    announce(f"{name}: oracle done, {st}")
+    h = dict(old_logps=inp["old_logps"].cpu().numpy())
+    compare_exact_parts(res, ref, name)
+    glp = to_np(res.tok_logp)
+    assert np.all(np.abs(glp - ref.tok["logp"])[mask] <= LOGP_ABS_ERR), name + " tok_logp"
+    amb_seq = compare_seq_outputs(res, ref, cfg, mask, h, groups, 1e-4, name)
+    br = seq_branches(ref, cfg, mask, h, groups, BF16_BASE)
+    clipped = int(res.counts[1])
+    assert abs(clipped - ref.clipped) <= int(br[0].sum()), (clipped, ref.clipped)
+    announce(f"{name}: clipped gpu={clipped} oracle={ref.clipped}, sequences at a bound {amb_seq}")

@@ -305,3 +305,24 @@ def test_loss_bar_is_strict_for_the_clipped_surrogate():
         else:
             with pytest.raises(AssertionError):
                 compare_scalars(res, ref, cfg, 1e-4, e_logp=1e-2, e_d=1e-2)
+
+
+def test_stream_oracle_sequence_level():
+    """The streaming comparison of a sequence-level loss (GSPO): the second
+    pass's gradient rows, rounded to bf16, pass; one row off by 5 % fails."""
+    from _fullsize import stream_oracle
+    t = _bf16_case(seed=6)
+    cfg = oracle.LossConfig(eps_low=0.2, eps_high=0.2, beta=0.04, pg_loss="gspo",
+                            reduction="sequence_mean")
+    groups = dict(samples_per_prompt=4)
+    h = {k: (v.float().numpy() if v.is_floating_point() else v.numpy()) for k, v in t.items()}
+    want = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
+                                    h["mask"], h["rewards"], groups=groups, cfg=cfg)
+    grad = torch.tensor(want.grad).to(torch.bfloat16)
+    got, st = stream_oracle(t, grad, None, cfg, groups, chunk=5, workers=2, announce=lambda m: None)
+    assert got.loss == want.loss and np.array_equal(got.seq_logratio, want.seq_logratio)
+    i, tt = np.argwhere(h["mask"])[3]
+    bad = grad.clone()
+    bad[i, tt] = (bad[i, tt].float() * 1.05).to(torch.bfloat16)
+    with pytest.raises(AssertionError):
+        stream_oracle(t, bad, None, cfg, groups, chunk=5, workers=2, announce=lambda m: None)
