@@ -719,15 +719,16 @@ def run_single(args, pool, workers):
 
 def memory_ceiling(gib=8):
     """The box's own streaming rates, for reading the fractions of 8 TB/s in
-    context: torch's sum over a bf16 tensor (read), its zero fill (write) and
-    its copy (half read, half write), GIB GiB each way, median of 5 after a
-    warm-up, HIP events on the current stream."""
+    context: torch's row sums over a bf16 tensor (read), its zero fill
+    (write) and its copy (half read, half write), GIB GiB each way, median of
+    5 after a warm-up, HIP events on the current stream."""
     import torch
     n = (gib << 30) // 2
     x = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
     y = torch.empty_like(x)
     out = {}
-    for name, fn, nbytes in (("read", lambda: x.sum(dtype=torch.float32), n * 2),
+    xr = x.view(-1, 4096)
+    for name, fn, nbytes in (("read", lambda: xr.sum(dim=1, dtype=torch.float32), n * 2),
                              ("write", lambda: y.zero_(), n * 2),
                              ("copy", lambda: y.copy_(x), n * 4)):
         fn()
@@ -742,9 +743,9 @@ def memory_ceiling(gib=8):
         t = _median(ms)
         out[f"{name}_GBps"] = nbytes / (t * 1e-3) / 1e9
         out[f"{name}_frac_of_peak"] = out[f"{name}_GBps"] / PEAK_HBM_GBS
-    out["method"] = (f"torch sum (read), zero_ (write) and copy_ (read + write) over {gib} GiB of "
-                     "bf16, median of 5 timed with events; context for the fractions of 8 TB/s, "
-                     "not a limit the kernels are held to")
+    out["method"] = (f"torch row sums of 4,096 values (read), zero_ (write) and copy_ (read + "
+                     f"write) over {gib} GiB of bf16, median of 5 timed with events; context for "
+                     "the fractions of 8 TB/s, not a limit the kernels are held to")
     del x, y
     torch.cuda.empty_cache()
     return out
