@@ -159,38 +159,62 @@ def test_no_active_tokens(gpu_lib):
         assert int(res.counts[0]) == 0
 
 
-@pytest.mark.parametrize("V", [12000, 20000])
+@pytest.mark.parametrize("V", [6000, 12000, 20000])
 def test_autograd_split_forward_backward(gpu_lib, V):
     """grpo_loss() runs the forward pass, keeps per-row weights, and the
-    backward pass writes the same gradient as the fused call, scaled by the
-    upstream gradient (24 KB rows: 256 threads per row in both split
-    kernels; 40 KB rows: the gradient-only kernel at 1024 threads)."""
+    backward pass writes the gradient scaled by the upstream gradient.
+    12 KB rows: the fused kernel and both split kernels give a row 256
+    threads, so the split path carries the fused call's bits.  24 KB and
+    40 KB rows: the fused kernel holds a row at 512 threads (and the
+    gradient-only kernel runs 1024 on 40 KB rows), so the log-sum-exp trees
+    differ and both paths are held to the oracle instead."""
     wl = _wl(V, "bf16", T=6)
-    announce(f"autograd split V={V}")
-    _, inp = _inputs(wl, seed=17)
+    bitwise = V * 2 <= 16384
+    announce(f"autograd split V={V} ({'bitwise against the fused call' if bitwise else 'oracle'})")
+    cpu, inp = _inputs(wl, seed=17)
     fused = _call(gpu_lib, inp, wl)
     pol = inp["policy"].clone().requires_grad_(True)
     loss, pl, kl = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
                                      inp["rewards"], inp["mask"], **gpu_kwargs(wl))
-    assert torch.equal(_bits(loss.detach().reshape(1)), _bits(fused.scalars[:1]))
+    if bitwise:
+        assert torch.equal(_bits(loss.detach().reshape(1)), _bits(fused.scalars[:1]))
     # policy_loss and kl are detached reporting values
     assert loss.requires_grad and not pl.requires_grad and not kl.requires_grad
     with pytest.raises(RuntimeError):
         kl.backward()
     loss.backward()
     torch.cuda.synchronize()
-    assert torch.equal(_bits(pol.grad), _bits(fused.grad))
+    h = host_inputs(cpu)
+    cfg = cfg_from(wl)
+
+    def oracle_ref(scale):
+        return oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
+                                        h["mask"], h["rewards"], groups=wl.groups_kwargs(),
+                                        cfg=cfg, grad_scale=scale)
+
+    if bitwise:
+        assert torch.equal(_bits(pol.grad), _bits(fused.grad))
+    else:
+        ref = oracle_ref(1.0)
+        rel = abs(float(loss) - ref.loss) / abs(ref.loss)
+        print(f"  split loss rel {rel:.3g} against the oracle (bar 1e-4)", flush=True)
+        assert rel <= 1e-4
+        compare_logits_grad(to_np(pol.grad), ref, cfg, h["mask"], "bf16", "split backward")
     pol.grad = None
     loss2, _, _ = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
                                     inp["rewards"], inp["mask"], **gpu_kwargs(wl))
     (2.0 * loss2).backward()
     torch.cuda.synchronize()
-    scale = torch.tensor([2.0], device=DEV)
-    fused2 = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
-                                       inp["old_logps"], inp["rewards"], inp["mask"],
-                                       grad_scale=scale, **gpu_kwargs(wl))
-    torch.cuda.synchronize()
-    assert torch.equal(_bits(pol.grad), _bits(fused2.grad))
+    if bitwise:
+        scale = torch.tensor([2.0], device=DEV)
+        fused2 = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
+                                           inp["old_logps"], inp["rewards"], inp["mask"],
+                                           grad_scale=scale, **gpu_kwargs(wl))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(pol.grad), _bits(fused2.grad))
+    else:
+        compare_logits_grad(to_np(pol.grad), oracle_ref(2.0), cfg, h["mask"], "bf16",
+                            "split backward, upstream 2")
 
 
 def test_confident_token_gradient_relative_accuracy(gpu_lib):
