@@ -191,9 +191,22 @@ def _timed_passes(pool, jobs, target_s):
             return done, el
 
 
+def _adv_job(job):
+    """Worker: the oracle's token-level advantage estimator over whole groups
+    (normalised over the job's sequences: the same work per slot as the
+    batch-wide normalization)."""
+    import oracle
+    h, est, kw = job
+    oracle.token_advantages(est, h["rewards"], h.get("old_logps"), h.get("ref_logp"), h["mask"],
+                            **kw)
+    return h["mask"].size
+
+
 def _run_job(job):
     kind, payload = job
-    return _rows_job(payload) if kind == "rows" else _token_job(payload)
+    if kind == "rows":
+        return _rows_job(payload)
+    return _adv_job(payload) if kind == "adv" else _token_job(payload)
 
 
 def cpu_baseline_logits(pool, workers, wl, inp, reduction, obj, target_s, sample_rows):
@@ -637,7 +650,32 @@ def run_token_record(args, wl, pool=None, workers=1, copies=None):
 ADV_WORKLOADS = {"adv_reinforce_pp": "reinforce_pp", "adv_reinforce_pp_baseline": "reinforce_pp_baseline"}
 
 
-def run_adv(args):
+def _adv_kwargs(est, wl):
+    if est == "reinforce_pp":
+        return dict(kl_coef=0.01, gamma=1.0, normalize=True)
+    return dict(samples_per_prompt=wl.group_size, normalize=True)
+
+
+def cpu_baseline_adv(pool, workers, wl, est, inp, target_s):
+    """The oracle's estimator over the whole batch in jobs of one group each,
+    repeated until target_s of wall time."""
+    keys = ("rewards", "mask") + (("old_logps", "ref_logp") if est == "reinforce_pp" else ())
+    h = {k: inp[k].cpu().numpy() for k in keys}
+    B, T = h["mask"].shape
+    size = wl.group_size
+    kw = dict(_adv_kwargs(est, wl))
+    spp = kw.pop("samples_per_prompt", None)
+    if spp is not None:
+        kw["groups"] = dict(samples_per_prompt=spp)
+    jobs = [("adv", ({k: v[s:s + size] for k, v in h.items()}, est, kw)) for s in range(0, B, size)]
+    slots, el = _timed_passes(pool, jobs, target_s)
+    return dict(value=slots / el, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"the whole batch in jobs of one group ({size} sequences) each, normalised over "
+                       f"the job's sequences, {slots / (B * T):.2f} passes, float64 numpy on {workers} "
+                       f"worker processes, {el:.1f} s wall")
+
+
+def run_adv_record(args, name, pool=None, workers=1):
     """Token-level advantage estimator over the log-prob workload's shape
     (B = 1024 in groups of 16, T = 4096, ragged lengths): REINFORCE++
     returns (k1 shaping 0.01, gamma 1) or the inclusive group baseline, with
@@ -649,12 +687,10 @@ def run_adv(args):
 
     lib = rpl.load_library()
     dev = torch.device("cuda:0")
-    est = ADV_WORKLOADS[args.workload]
+    est = ADV_WORKLOADS[name]
     wl = TOKEN_WORKLOADS["token_loss_ragged"]
     copies = [make_token_inputs(wl, device=dev, seed=args.seed + k) for k in range(args.copies)]
-    kw = dict(kl_coef=0.01, gamma=1.0, normalize=True)
-    if est == "reinforce_pp_baseline":
-        kw = dict(samples_per_prompt=wl.group_size, normalize=True)
+    kw = _adv_kwargs(est, wl)
     outs = [None] * len(copies)
 
     def step(k):
@@ -666,34 +702,47 @@ def run_adv(args):
     for k in range(max(args.warmup, len(copies))):
         step(k)
     torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
     _, kern = timed_kernel(lib, max(args.steps, 30), step)
-    ms, ms_graph_per_call = _graph_times(step, len(copies), args.steps)
+    meas = [_graph_times(step, len(copies), 120) for _ in range(5)]
+    ms = _median([m[0] for m in meas])
+    ms_graph_per_call = _median([m[1] for m in meas])
+    torch.cuda.synchronize()
+    repro = all(torch.equal(a.view(torch.int32), o.view(torch.int32)) for a, o in zip(ref, outs))
     rows = wl.B * wl.T
     # minimum bytes: old, ref f32 and the mask read once (REINFORCE++), the output written once
     per_slot = (4 + 4 + 1 + 4) if est == "reinforce_pp" else (1 + 4)
     alg = rows * per_slot
-    out = {"metric": "tokens/s for the token-level advantage estimator (returns + global normalization)",
-           "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-           "config": {"workload": f"{args.workload}: B={wl.B} (groups of {wl.group_size}), T={wl.T}, "
-                                  f"ragged lengths, {est}, normalized; input copies rotated: {args.copies}",
-                      "algorithmic_bytes": alg, "step_GBps": alg / (ms * 1e-3) / 1e9,
-                      "timing": GRAPH_TIMING, "ms_per_step_graph_per_call": ms_graph_per_call},
-           "roofline": roofline("grpo_tokadv_kernels", args.workload, alg, kern,
-                                {"timing": "the estimator's three kernels, HIP events around them"})}
-    out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    rec = {"workload": f"{name}: B={wl.B} (groups of {wl.group_size}), T={wl.T}, ragged lengths, "
+                       f"{est}, normalized; input copies rotated: {args.copies}",
+           "ms_per_step": ms, "timing": GRAPH_TIMING, "tokens_per_s": rows / (ms * 1e-3),
+           "algorithmic_bytes": alg, "hbm_fraction_of_step": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "ms_per_step_graph_per_call": ms_graph_per_call, "bit_reproducible": bool(repro),
+           "roofline": roofline("grpo_tokadv_kernels", name, alg, kern, {
+               "byte_model": f"{per_slot} B per slot: "
+                             + ("old, ref f32 and the mask read, the advantage written"
+                                if est == "reinforce_pp" else "the mask read, the advantage written"),
+               "timing": "the estimator's kernels together, HIP events around them in eager calls"})}
+    if pool is not None:
+        _log(f"oracle baseline {name}")
+        rec["cpu_baseline"] = cpu_baseline_adv(pool, workers, wl, est, copies[0], args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    del copies, outs
+    return rec
 
 
 def _line(rec, args, wl_key):
     """The bench line around one record."""
     return {
-        "metric": METRIC if not wl_key.startswith("token_loss") else
-        "tokens/s for the logprob-level GRPO token loss (forward + dlogp)",
+        "metric": ("tokens/s for the logprob-level GRPO token loss (forward + dlogp)"
+                   if wl_key.startswith("token_loss") else
+                   "tokens/s for the token-level advantage estimator (returns + global normalization)"
+                   if wl_key in ADV_WORKLOADS else METRIC),
         "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64" if wl_key in ADV_WORKLOADS else "f32", "data": "synthetic",
         "config": {k: v for k, v in rec.items() if k not in ("roofline", "cpu_baseline", "ms_per_step",
                                                               "tokens_per_s")},
         "roofline": rec["roofline"], "cpu_baseline": rec["cpu_baseline"],
@@ -706,6 +755,10 @@ def run_single(args, pool, workers):
     from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs
 
     rpl.load_library()
+    if args.workload in ADV_WORKLOADS:
+        rec = run_adv_record(args, args.workload, pool, workers)
+        print(json.dumps(_line(rec, args, args.workload)), flush=True)
+        return
     if args.workload in TOKEN_WORKLOADS:
         rec = run_token_record(args, TOKEN_WORKLOADS[args.workload], pool, workers)
         print(json.dumps(_line(rec, args, args.workload)), flush=True)
@@ -798,6 +851,10 @@ def run_all(args, pool, workers):
         _log(f"timing {name}")
         subs[name] = run_token_record(args, TOKEN_WORKLOADS[name], pool, workers)
         torch.cuda.empty_cache()
+    for name in ADV_WORKLOADS:
+        _log(f"timing {name}")
+        subs[name] = run_adv_record(args, name, pool, workers)
+        torch.cuda.empty_cache()
     line = _line(head, args, "logits_v151936")
     line["configs"] = subs
     _log("timing the box's own streaming rates")
@@ -823,62 +880,159 @@ def calibrate_only():
                       "check": float(dst[0])}))
 
 
-def _pmc_values(d, counter, name_part):
-    """Per-dispatch counter values (summed over the csv rows of a dispatch)
-    of kernels whose name contains ``name_part``."""
+# the dominant "kernel" of a record that launches several kernels per call
+KERNEL_FAMILIES = {"grpo_tokadv_kernels": ("grpo_tokadv_kernel(", "grpo_tokadv_norm_kernel")}
+
+
+def _family(kernel):
+    return KERNEL_FAMILIES.get(kernel, (kernel,))
+
+
+def _csv_rows(d, suffix):
     import csv
-    per = {}
-    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
         with open(path) as f:
-            for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter or name_part not in row.get("Kernel_Name", ""):
-                    continue
-                did = row.get("Dispatch_Id")
-                per[did] = per.get(did, 0.0) + float(row["Counter_Value"])
-    return [per[k] for k in sorted(per, key=lambda v: int(v))]
+            yield from csv.DictReader(f)
 
 
-def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1):
-    """Combine the four rocprofv3 --pmc runs into profiles/<kernel>_<workload>_pmc.json.
-    The counters read over the calibration kernel, which moves a known number
-    of bytes each way, give the scale from counter units to bytes.  The first
-    ``skip_first`` dispatches (warm-up) are left out of the average."""
+def _pmc_by_kernel(d, counter):
+    """{kernel name: [per-dispatch counter value in dispatch order]} (a
+    dispatch's csv rows summed)."""
+    per = {}
+    for row in _csv_rows(d, "counter_collection.csv"):
+        if row.get("Counter_Name") != counter:
+            continue
+        key = (row.get("Kernel_Name", ""), int(row.get("Dispatch_Id")))
+        per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in sorted(per.items(), key=lambda kv: kv[0][1]):
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _matching(by_name, part):
+    vals = []
+    for name, v in by_name.items():
+        if part in name:
+            vals.extend(v)
+    return vals
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("grpo::", "")
+
+
+def pmc_commands(workload, regex, dirs):
+    wl_arg = workload.replace("_sequence_mean", ":sequence_mean").replace("_length_alpha", ":length_alpha")
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
-    res = {}
+    run = f"-- python3 bench.py --workload {wl_arg} --steps 3 --warmup 1 --no-cpu-baseline"
+    return [f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {regex} -f csv -d {fetch_dir} -o run {run}",
+            f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {regex} -f csv -d {write_dir} -o run {run}",
+            "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex elementwise -f csv "
+            f"-d {cal_fetch_dir} -o run -- python3 bench.py --calibrate-only",
+            "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex elementwise -f csv "
+            f"-d {cal_write_dir} -o run -- python3 bench.py --calibrate-only"]
+
+
+def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
+    """Combine the four rocprofv3 --pmc runs into
+    profiles/<kernel>_<workload>_pmc.json and .md.  The counters read over
+    the calibration kernel, which moves a known number of bytes each way,
+    give the scale from counter units to bytes.  The first ``skip_first``
+    dispatches of each kernel (warm-up) are left out of its average.  A
+    kernel family's traffic per call is the sum of its kernels' averages."""
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
+    regex = regex or kernel
+    res, per_kernel = {}, {}
     for counter, run_dir, cal_dir in (("FETCH_SIZE", fetch_dir, cal_fetch_dir),
                                       ("WRITE_SIZE", write_dir, cal_write_dir)):
-        cal = _pmc_values(cal_dir, counter, "_add<float>")
-        rows = _pmc_values(run_dir, counter, kernel)
-        if not cal or not rows:
-            raise SystemExit(f"missing {counter} values (calibration {len(cal)}, kernel {len(rows)})")
-        used = rows[skip_first:] if len(rows) > skip_first else rows
+        cal = _matching(_pmc_by_kernel(cal_dir, counter), "_add<float>")
+        by_name = _pmc_by_kernel(run_dir, counter)
+        if not cal or not by_name:
+            raise SystemExit(f"missing {counter} values (calibration {len(cal)}, kernels {len(by_name)})")
         c = max(cal)
         scale = CALIB_BYTES / c
+        total = 0.0
+        for part in _family(kernel):
+            rows = _matching(by_name, part)
+            if not rows:
+                raise SystemExit(f"no {counter} dispatches of {part}")
+            used = rows[skip_first:] if len(rows) > skip_first else rows
+            total += sum(used) / len(used) * scale
+        for name, rows in by_name.items():
+            used = rows[skip_first:] if len(rows) > skip_first else rows
+            per_kernel.setdefault(_short(name), {})[counter] = dict(
+                counter_per_dispatch=rows, dispatches_averaged=len(used),
+                bytes_avg=sum(used) / len(used) * scale)
         res[counter] = dict(calibration_counter=c, calibration_bytes=CALIB_BYTES,
-                            scale_bytes_per_unit=scale, kernel_counter_per_dispatch=rows,
-                            dispatches_averaged=len(used),
-                            kernel_bytes_avg=sum(used) / len(used) * scale)
+                            scale_bytes_per_unit=scale, kernel_bytes_avg=total)
     traffic = res["FETCH_SIZE"]["kernel_bytes_avg"] + res["WRITE_SIZE"]["kernel_bytes_avg"]
-    wl_arg = workload.replace("_sequence_mean", ":sequence_mean").replace("_length_alpha", ":length_alpha")
-    summary = dict(kernel=kernel, workload=workload, kernel_source_hash=kernel_source_hash(),
-                   counters=res, traffic_bytes_per_launch=traffic,
-                   commands=[f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {kernel} -f csv "
-                             f"-d {fetch_dir} -o run -- python3 bench.py --workload {wl_arg} "
-                             "--steps 3 --warmup 1 --no-cpu-baseline",
-                             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {kernel} -f csv "
-                             f"-d {write_dir} -o run -- python3 bench.py --workload {wl_arg} "
-                             "--steps 3 --warmup 1 --no-cpu-baseline",
-                             "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex elementwise -f csv "
-                             f"-d {cal_fetch_dir} -o run -- python3 bench.py --calibrate-only",
-                             "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex elementwise -f csv "
-                             f"-d {cal_write_dir} -o run -- python3 bench.py --calibrate-only",
-                             f"python bench.py --workload {wl_arg} --kernel {kernel} --summarize-pmc "
-                             f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"])
+    cmds = pmc_commands(workload, regex, dirs) + [
+        f"python bench.py --workload {workload} --kernel {kernel} --regex {regex} --summarize-pmc "
+        f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"]
+    summary = dict(kernel=kernel, members=list(_family(kernel)), workload=workload,
+                   kernel_source_hash=kernel_source_hash(), counters=res, per_kernel=per_kernel,
+                   traffic_bytes_per_launch=traffic, warmup_dispatches_skipped=skip_first,
+                   commands=cmds)
     os.makedirs(out_dir, exist_ok=True)
     base = os.path.join(out_dir, f"{kernel}_{workload}_pmc")
     with open(base + ".json", "w") as f:
         json.dump(summary, f, indent=1)
-    print(json.dumps(summary, indent=1))
+    lines = [f"# {kernel} on {workload}: HBM traffic counters (FETCH_SIZE, WRITE_SIZE)", "",
+             f"Kernel sources hash {summary['kernel_source_hash']} (bench.py reports `traffic` only "
+             "while the sources match).  Each counter in a run of its own; the calibration kernel "
+             f"(torch's float32 add, {CALIB_BYTES} B read and {CALIB_BYTES} B written) gives the "
+             "bytes per counter unit.  The first dispatch of each kernel (warm-up) is left out.", "",
+             "Commands (repository root, one MI355X):", ""] + ["    " + c for c in cmds] + [
+             "", "| counter | calibration reading | bytes per unit |", "|---|---|---|"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[counter]
+        lines.append(f"| {counter} | {r['calibration_counter']:.1f} | {r['scale_bytes_per_unit']:.2f} |")
+    lines += ["", "| kernel | dispatches | read (MB, avg) | written (MB, avg) |", "|---|---|---|---|"]
+    for name, d in sorted(per_kernel.items()):
+        f_, w_ = d.get("FETCH_SIZE", {}), d.get("WRITE_SIZE", {})
+        lines.append(f"| {name} | {len(f_.get('counter_per_dispatch', []))} | "
+                     f"{f_.get('bytes_avg', 0) / 1e6:.3f} | {w_.get('bytes_avg', 0) / 1e6:.3f} |")
+    lines += ["", f"Traffic per launch of {kernel}"
+              + (" (" + " + ".join(_family(kernel)) + ")" if kernel in KERNEL_FAMILIES else "")
+              + f": {traffic / 1e6:.3f} MB (read {res['FETCH_SIZE']['kernel_bytes_avg'] / 1e6:.3f}, "
+              f"written {res['WRITE_SIZE']['kernel_bytes_avg'] / 1e6:.3f})."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(dict(kernel=kernel, workload=workload, traffic=traffic)), flush=True)
+
+
+def summarize_trace(run_dir, workload, kernel, out_dir, command, skip_first):
+    """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3
+    --kernel-trace --stats run: per libgrpo kernel, the dispatch count and
+    the average, median, minimum and maximum duration over every dispatch
+    but the first ``skip_first`` (warm-up), and the average over all."""
+    per = {}
+    for row in _csv_rows(run_dir, "kernel_trace.csv"):
+        name = row.get("Kernel_Name", "")
+        if "grpo" not in name:
+            continue
+        dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3  # us
+        per.setdefault(name, []).append((int(row.get("Dispatch_Id", 0)), dur))
+    if not per:
+        raise SystemExit(f"no libgrpo dispatches under {run_dir}")
+    lines = [f"# {kernel} on {workload}: kernel trace", "",
+             f"Kernel sources hash {kernel_source_hash()}.  Durations in microseconds from the "
+             f"trace's start and end timestamps; the first {skip_first} dispatches of each kernel "
+             "(warm-up) are left out of the average, median, minimum and maximum.", "",
+             "Command (repository root, one MI355X):", "", "    " + command, "",
+             "| kernel | dispatches | avg us | median us | min us | max us | avg us, all dispatches |",
+             "|---|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = [x for _, x in sorted(v)]
+        used = d[skip_first:] if len(d) > skip_first else d
+        lines.append(f"| {_short(name)} | {len(d)} | {sum(used) / len(used):.1f} | "
+                     f"{_median(used):.1f} | {min(used):.1f} | {max(used):.1f} | "
+                     f"{sum(d) / len(d):.1f} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{kernel}_{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[-len(per):]), flush=True)
 
 
 def main():
@@ -897,23 +1051,32 @@ def main():
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated by the token-loss bench")
     ap.add_argument("--calibrate-only", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, default=None)
-    ap.add_argument("--kernel", default="grpo_rows_kernel", help="kernel named by --summarize-pmc")
+    ap.add_argument("--kernel", default="grpo_rows_kernel",
+                    help="kernel (or family) named by --summarize-pmc / --summarize-trace")
+    ap.add_argument("--regex", default=None, help="the --kernel-include-regex the counter runs used")
+    ap.add_argument("--summarize-trace", nargs=1, default=None,
+                    help="rocprofv3 --kernel-trace output directory to summarise")
+    ap.add_argument("--trace-command", default="", help="the command that made --summarize-trace's run")
+    ap.add_argument("--skip-first", type=int, default=1, help="warm-up dispatches left out")
     args = ap.parse_args()
     if args.calibrate_only:
         calibrate_only()
         return
     if args.summarize_pmc:
         key = args.workload.replace(":", "_")
-        summarize_pmc(args.summarize_pmc, key, args.kernel, os.path.join(ROOT, "profiles"))
+        summarize_pmc(args.summarize_pmc, key, args.kernel, os.path.join(ROOT, "profiles"),
+                      args.skip_first, args.regex)
+        return
+    if args.summarize_trace:
+        key = args.workload.replace(":", "_")
+        summarize_trace(args.summarize_trace[0], key, args.kernel, os.path.join(ROOT, "profiles"),
+                        args.trace_command, args.skip_first)
         return
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    if args.workload in ADV_WORKLOADS:
-        run_adv(args)
-        return
     pool = None
     workers = host_workers()
     if not args.no_cpu_baseline and args.objective == "default":

@@ -339,6 +339,120 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
   }
 }
 
+// --- gradient-only pass as a flat map ------------------------------------------
+// The gradient pass needs no reduction: g_v = G (onehot(a)_v - p_v) with the
+// row's G, c and 1 - p_a from the forward pass's stash.  Here every block of
+// kFlatThreads threads writes kFlatThreads 16-byte chunks (4 KB) of one row
+// (row = block / blocks per row), so a launch is millions of short blocks
+// with a small address footprint each.  Measured on MI355X at V = 151,936
+// bf16: the gradient pass takes 6.0 ms instead of 7.3 (a row-per-block walk
+// over the same bytes).  Two chunks per thread measured slower, and so did
+// loading the policy chunk before the row's G is known once a third of the
+// rows are masked (their policy rows are never read).  The values are those
+// of grpo_rows_kernel's pass 2, bit for bit (the same expressions per
+// element).  Rows up to 64 KB keep the row kernel at 1024 threads: there the
+// two measured alike.
+constexpr int kFlatThreads = 256;
+constexpr int kFlatChunks = 1;
+constexpr int64_t kFlatMinRowBytes = 65536;  // rows longer than this take the flat map
+
+template <typename TI, typename TG>
+__global__ __launch_bounds__(kFlatThreads) void grpo_grad_flat_kernel(RowArgs a, uint32_t bpr) {
+  typedef In<TI, true> IN;
+  constexpr int N = IN::N;
+  typedef typename IN::raw_t raw_t;
+  const uint32_t b = blockIdx.x;
+  const uint32_t row32 = b / bpr;
+  const int64_t row = row32;
+  const uint32_t seg = b - row32 * bpr;
+  const int64_t V = a.V;
+  const int64_t nvec = V / N;
+  const int64_t tail0 = nvec * N;
+  const void* xrow = static_cast<const char*>(a.x) + row * a.ld * int64_t(sizeof(TI));
+  void* grow = static_cast<char*>(a.g) + row * a.ldg * int64_t(sizeof(TG));
+  const int64_t c0 = int64_t(seg) * (kFlatThreads * kFlatChunks) + threadIdx.x;
+  const bool last = seg == bpr - 1;
+  const RowStash st = a.stash[row];
+  const float G = st.act != 0.0f
+                      ? (st.G + a.useq[row / a.T]) * (a.grad_scale ? *a.grad_scale : 1.0f)
+                      : 0.0f;
+  if (G == 0.0f) {
+#pragma unroll
+    for (int u = 0; u < kFlatChunks; ++u)
+      if (c0 + u * kFlatThreads < nvec) Out<TG, N>::zero(grow, c0 + u * kFlatThreads);
+    if (last)
+      for (int64_t v = tail0 + threadIdx.x; v < V; v += kFlatThreads) store_one(grow, v, 0.0f, (TG*)nullptr);
+    return;
+  }
+  raw_t rx[kFlatChunks];
+#pragma unroll
+  for (int u = 0; u < kFlatChunks; ++u)
+    if (c0 + u * kFlatThreads < nvec) rx[u] = IN::load(xrow, c0 + u * kFlatThreads);
+  const int64_t aid = load_action(a, row);
+  const int64_t ca = aid / N;
+  const int ja = int(aid - ca * N);
+  const float c2 = st.c;
+  const float ga = G * st.omp;
+  const float mG = -G;
+#pragma unroll
+  for (int u = 0; u < kFlatChunks; ++u) {
+    const int64_t c = c0 + u * kFlatThreads;
+    if (c < nvec) {
+      float f[N], g[N];
+      IN::cvt(rx[u], f);
+#pragma unroll
+      for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
+      if (c == ca) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+          if (j == ja) g[j] = ga;
+      }
+      Out<TG, N>::store(grow, c, g);
+    }
+  }
+  if (last) {
+    for (int64_t v = tail0 + threadIdx.x; v < V; v += kFlatThreads) {
+      const float xv = load_one(xrow, v, (TI*)nullptr);
+      store_one(grow, v, (v == aid) ? ga : mG * fast_exp2(fmaf(xv, kLog2e, -c2)), (TG*)nullptr);
+    }
+  }
+}
+
+// Blocks per row of the flat gradient pass, or 0 when the grid would not fit
+// a 32-bit block index (such launches use the row kernel).
+static uint32_t flat_blocks_per_row(const RowArgs& a, int n) {
+  const int64_t nvec = a.V / n;
+  const int64_t per = int64_t(kFlatThreads) * kFlatChunks;
+  const int64_t bpr = nvec > 0 ? (nvec + per - 1) / per : 1;
+  if (a.rows <= 0 || bpr * a.rows > int64_t(INT32_MAX)) return 0;
+  return uint32_t(bpr);
+}
+
+template <typename TI, typename TG>
+static hipError_t launch_flat(const RowArgs& a, uint32_t bpr, hipStream_t s) {
+  hipLaunchKernelGGL((grpo_grad_flat_kernel<TI, TG>), dim3(unsigned(int64_t(bpr) * a.rows)),
+                     dim3(kFlatThreads), 0, s, a, bpr);
+  return hipGetLastError();
+}
+
+// The gradient-only pass over 16-byte-aligned rows above kFlatMinRowBytes:
+// the flat map.  Returns hipErrorNotSupported when it does not apply (the
+// caller runs the row kernel).
+static hipError_t launch_grad_flat(const RowArgs& a, const RowLaunch& l, hipStream_t s) {
+  const int n = l.tin == GRPO_F32 ? 4 : 8;
+  if (!l.vec || a.rows <= 0 || a.V * int64_t(16 / n) <= kFlatMinRowBytes) return hipErrorNotSupported;
+  const uint32_t bpr = flat_blocks_per_row(a, n);
+  if (bpr == 0) return hipErrorNotSupported;
+  if (l.tin == GRPO_BF16)
+    return l.tg == GRPO_BF16 ? launch_flat<uint16_t, uint16_t>(a, bpr, s)
+                             : launch_flat<uint16_t, float>(a, bpr, s);
+  if (l.tin == GRPO_F16)
+    return l.tg == GRPO_F16 ? launch_flat<_Float16, _Float16>(a, bpr, s)
+                            : launch_flat<_Float16, float>(a, bpr, s);
+  return l.tg == GRPO_BF16 ? launch_flat<float, uint16_t>(a, bpr, s)
+                           : launch_flat<float, float>(a, bpr, s);
+}
+
 // --- launch ------------------------------------------------------------------
 template <typename TI, typename TG, int NT, int MODE, bool VEC>
 static hipError_t launch_t(const RowArgs& a, hipStream_t stream) {
@@ -388,7 +502,12 @@ hipError_t launch_rows(const RowArgs& a, const RowLaunch& l, hipStream_t s) {
   switch (l.mode) {
     case kFused: return launch_types<kFused>(a, l, s);
     case kForward: return launch_types<kForward>(a, l, s);
-    case kBackward: return launch_types<kBackward>(a, l, s);
+    case kBackward:
+      {
+        const hipError_t e = launch_grad_flat(a, l, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch_types<kBackward>(a, l, s);
   }
   return hipErrorInvalidValue;
 }

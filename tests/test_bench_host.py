@@ -73,10 +73,60 @@ def test_summarize_pmc_scales_by_the_calibration_kernel(tmp_path):
     d = json.load(open(out / "grpo_rows_kernel_wl_pmc.json"))
     fetch = 45.0 * bench.CALIB_BYTES / 1024.0
     write = 6.0 * bench.CALIB_BYTES / 2048.0
-    assert d["counters"]["FETCH_SIZE"]["kernel_counter_per_dispatch"] == [1.0, 30.0, 60.0]
-    assert d["counters"]["FETCH_SIZE"]["dispatches_averaged"] == 2
+    per = d["per_kernel"]["grpo_rows_kernel<unsigned short>"]["FETCH_SIZE"]
+    assert per["counter_per_dispatch"] == [1.0, 30.0, 60.0]
+    assert per["dispatches_averaged"] == 2
     assert abs(d["traffic_bytes_per_launch"] - (fetch + write)) <= 1e-9 * (fetch + write)
     assert d["kernel_source_hash"] == bench.kernel_source_hash()
+    assert (out / "grpo_rows_kernel_wl_pmc.md").read_text().count("| FETCH_SIZE |") == 1
+
+
+def test_summarize_pmc_sums_a_kernel_family(tmp_path):
+    """The estimator's traffic per call: the averages of its kernels, summed."""
+    scan = "grpo::grpo_tokadv_kernel(grpo::TokAdvArgs)"
+    norm = "void grpo::grpo_tokadv_norm_kernel<true>(grpo::TokAdvArgs, int)"
+    cal = "void at::native::elementwise_kernel<_add<float>>(...)"
+    dirs = [str(tmp_path / n) for n in ("f", "w", "cf", "cw")]
+    import csv
+    for d, counter, vals in ((dirs[0], "FETCH_SIZE", (4.0, 2.0)), (dirs[1], "WRITE_SIZE", (1.0, 3.0))):
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                              "Counter_Value"])
+            w.writeheader()
+            for call in range(3):   # call 0 is the warm-up
+                w.writerow(dict(Dispatch_Id=2 * call, Kernel_Name=scan, Counter_Name=counter,
+                                Counter_Value=vals[0] * (1 + call)))
+                w.writerow(dict(Dispatch_Id=2 * call + 1, Kernel_Name=norm, Counter_Name=counter,
+                                Counter_Value=vals[1] * (1 + call)))
+    _counter_csv(dirs[2], cal, "FETCH_SIZE", [[1024.0]])
+    _counter_csv(dirs[3], cal, "WRITE_SIZE", [[1024.0]])
+    out = tmp_path / "profiles"
+    bench.summarize_pmc(dirs, "wl", "grpo_tokadv_kernels", str(out), regex="grpo_tokadv")
+    d = json.load(open(out / "grpo_tokadv_kernels_wl_pmc.json"))
+    unit = bench.CALIB_BYTES / 1024.0
+    want = (4.0 + 2.0) * 2.5 * unit + (1.0 + 3.0) * 2.5 * unit   # calls 1 and 2 averaged
+    assert abs(d["traffic_bytes_per_launch"] - want) <= 1e-9 * want
+    assert d["members"] == list(bench.KERNEL_FAMILIES["grpo_tokadv_kernels"])
+
+
+def test_summarize_trace_skips_the_warmup(tmp_path):
+    import csv
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                          "End_Timestamp"])
+        w.writeheader()
+        for k, us in enumerate((50.0, 10.0, 12.0, 11.0)):
+            w.writerow(dict(Dispatch_Id=k, Kernel_Name="void grpo::grpo_token_kernel<false, 2>(x)",
+                            Start_Timestamp=1000 * k * 100, End_Timestamp=int(1000 * (k * 100 + us))))
+        w.writerow(dict(Dispatch_Id=9, Kernel_Name="other_kernel", Start_Timestamp=0, End_Timestamp=5))
+    out = tmp_path / "profiles"
+    bench.summarize_trace(str(d), "wl", "grpo_token_kernel", str(out), "rocprofv3 ...", 1)
+    text = (out / "grpo_token_kernel_wl_kernel_trace.md").read_text()
+    assert "| grpo_token_kernel<false, 2> | 4 | 11.0 | 11.0 | 10.0 | 12.0 | 20.8 |" in text
+    assert "other_kernel" not in text
 
 
 def test_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
@@ -94,7 +144,8 @@ def test_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
 
 def test_cpu_baselines_over_worker_processes():
     """The oracle baselines run on spawned worker processes: the token loss
-    over whole groups, the logits rows from float32 sample files."""
+    and the advantage estimators over whole groups, the logits rows from
+    float32 sample files."""
     import torch
     pool = bench.start_pool(2)
     try:
@@ -107,6 +158,9 @@ def test_cpu_baselines_over_worker_processes():
         linp = make_logits_inputs(lw, device="cpu", seed=1)
         res = bench.cpu_baseline_logits(pool, 2, lw, linp, "token_mean", {}, 0.05, 64)
         assert res["value"] > 0 and res["cores"] == 2 and "slots 0..63" in res["sample"]
+        for est in ("reinforce_pp", "reinforce_pp_baseline"):
+            res = bench.cpu_baseline_adv(pool, 2, wl, est, inp, 0.05)
+            assert res["value"] > 0 and res["cores"] == 2 and "one group (16 sequences)" in res["sample"]
     finally:
         pool.terminate()
 

@@ -196,7 +196,7 @@ def test_autograd_split_forward_backward(gpu_lib, V):
         assert torch.equal(_bits(pol.grad), _bits(fused.grad))
     else:
         ref = oracle_ref(1.0)
-        rel = abs(float(loss) - ref.loss) / abs(ref.loss)
+        rel = abs(float(loss.detach()) - ref.loss) / abs(ref.loss)
         print(f"  split loss rel {rel:.3g} against the oracle (bar 1e-4)", flush=True)
         assert rel <= 1e-4
         compare_logits_grad(to_np(pol.grad), ref, cfg, h["mask"], "bf16", "split backward")
@@ -215,6 +215,53 @@ def test_autograd_split_forward_backward(gpu_lib, V):
     else:
         compare_logits_grad(to_np(pol.grad), oracle_ref(2.0), cfg, h["mask"], "bf16",
                             "split backward, upstream 2")
+
+
+@pytest.mark.parametrize("V,dtype,ld,gdtype", [
+    (32768, "bf16", None, None),            # 64 KB rows: the row kernel (the flat map's limit)
+    (32776, "bf16", None, None),            # one chunk more: the flat gradient map
+    (40000, "bf16", None, None),            # 80 KB rows
+    (40003, "bf16", 40008, None),           # padded 16-byte rows: the flat map's scalar tail
+    (20000, "f32", None, None),             # float32 rows of 80 KB
+    (40000, "bf16", None, torch.float32),   # bf16 logits, float32 gradient
+])
+def test_split_backward_long_rows(gpu_lib, V, dtype, ld, gdtype):
+    """The gradient-only pass on rows above 64 KB (the flat map over 16-byte
+    chunks, a block per 4 KB of a row) after a forward-only pass on the same
+    workspace, with an upstream gradient of 1 and 2, against the oracle; the
+    gradient buffer's row padding stays untouched."""
+    wl = _wl(V, dtype, T=6)
+    announce(f"split backward long rows V={V} {dtype} ld={ld} grad={gdtype}")
+    cpu, inp = _inputs(wl, seed=23)
+    B, T = wl.B, wl.T
+    pol, ref = inp["policy"], inp["ref"]
+    gdt = pol.dtype if gdtype is None else gdtype
+    if ld is not None:
+        pbuf = torch.full((B, T, ld), float("nan"), dtype=pol.dtype, device=DEV)
+        rbuf = torch.full((B, T, ld), float("inf"), dtype=pol.dtype, device=DEV)
+        pbuf[..., :V] = pol
+        rbuf[..., :V] = ref
+        pol, ref = pbuf[..., :V], rbuf[..., :V]
+    gbuf = torch.full((B, T, ld or V), 7.0, dtype=gdt, device=DEV)
+    h = host_inputs(cpu)
+    cfg = cfg_from(wl)
+    for scale in (1.0, 2.0):
+        ws = gpu_lib.workspace(B, T, 0, DEV, dedicated=True)
+        res = gpu_lib.grpo_loss_fwd_bwd(pol, ref, inp["action_ids"], inp["old_logps"],
+                                        inp["rewards"], inp["mask"], grad_out=False, _ws=ws,
+                                        **gpu_kwargs(wl))
+        gs = torch.tensor([scale], dtype=torch.float32, device=DEV)
+        gpu_lib.grpo_loss_bwd(pol, inp["action_ids"], inp["mask"], ws, grad_out=gbuf[..., :V],
+                              grad_scale=gs)
+        torch.cuda.synchronize()
+        if ld is not None:
+            assert torch.all(gbuf[..., V:] == 7.0), "padding of the gradient must stay untouched"
+        ref64 = oracle.grpo_loss_fwd_bwd(h["policy"], h["ref"], h["action_ids"], h["old_logps"],
+                                         h["mask"], h["rewards"], groups=wl.groups_kwargs(),
+                                         cfg=cfg, grad_scale=scale)
+        compare_scalars(res, ref64, cfg, 1e-4 if dtype != "f32" else 1e-5, f"forward V={V}")
+        compare_logits_grad(to_np(gbuf[..., :V]), ref64, cfg, h["mask"],
+                            "f32" if gdt == torch.float32 else "bf16", f"backward x{scale}")
 
 
 def test_confident_token_gradient_relative_accuracy(gpu_lib):
