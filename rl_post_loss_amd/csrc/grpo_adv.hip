@@ -14,17 +14,20 @@
 // Everything is binary64 with contraction off and rounded once to float32.
 // The returns run as a tiled backward scan: a sequence's block walks tiles of
 // kAdvTile slots from the right end; a tile's token rewards are staged in LDS
-// with coalesced loads, thread j folds its kAdvChunk consecutive slots into
-// an affine map x -> h + g x of the return after the chunk, a suffix scan of
-// those maps (wave shuffles, then the waves in order) gives every chunk its
-// carry and the carry into the next tile, every chunk replays its slots from
-// its carry, and the returns leave LDS with coalesced accesses again.
+// with coalesced loads as they arrive (the terminal reward is added at the
+// last active slot, found in the first tile from the right that has an
+// active slot, so the mask is read once), thread j folds its kAdvChunk
+// consecutive slots into an affine map x -> h + g x of the return after the
+// chunk, a suffix scan of those maps (wave shuffles, then the waves in
+// order) gives every chunk its carry and the carry into the next tile, every
+// chunk replays its slots from its carry, and the returns leave LDS with
+// coalesced accesses again.
 //
 // With the global normalization the returns are kept in binary64 in the
 // workspace and each sequence leaves the moments (count, mean, sum of squared
 // deviations) of its active values: per thread from sums of deviations
 // from its first value, merged across the block.  The output pass then
-// writes (A - mu) / sd; each of its blocks first issues its loads, then
+// writes (A - mu) x (1 / sd); each of its blocks first issues its loads, then
 // merges the sequences' moments with Chan et al.'s pairwise update in one
 // fixed tree (the same bits in every block, so results repeat bit for bit).
 // Two launches in all (three beyond kFusedMomentsMaxB sequences, where one
@@ -38,6 +41,8 @@
 namespace grpo {
 
 constexpr int kAdvThreads = 256;
+// 16 slots per thread (one tile for T = 4,096) measured slower: the extra
+// registers halve the waves per SIMD or spill
 constexpr int kAdvChunk = 8;                           // consecutive slots per thread in a tile
 constexpr int kAdvTile = kAdvThreads * kAdvChunk;      // slots per tile
 constexpr int kAdvPad = kAdvChunk + 1;                 // LDS row per thread (bank spread)
@@ -46,13 +51,12 @@ constexpr int kGdpoThreads = 1024;
 
 struct AdvShared {
   double v[kAdvThreads * kAdvPad];  // a tile's token rewards, then its returns
-  uint8_t act[kAdvTile];            // a tile's mask
+  int wmax[kAdvThreads / kWave];    // per wave: its last active tile slot (-1: none)
   double wh[kAdvThreads / kWave];  // per wave: its chunks' composed map (h + g x)
   double wg[kAdvThreads / kWave];
   double red[kAdvThreads / kWave];
   long long red_i[kAdvThreads / kWave];
   double cval;                // baseline difference of the sequence
-  long long last;             // last active slot (-1: none)
 };
 
 // LDS index of tile slot q (thread q / kAdvChunk owns kAdvChunk consecutive slots)
@@ -95,7 +99,9 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
     return;
   }
   const double R = double(a.rewards[i]);
-  const long long last = sh.last;
+  // the last active slot (it takes the terminal reward), found in the first
+  // tile from the right that has an active slot; the same in every thread
+  int64_t last = -1;
   const bool shaped = a.kl_coef != 0.0;
   constexpr int kPer = kAdvTile / kAdvThreads;
   constexpr int NW = kAdvThreads / kWave;
@@ -103,18 +109,18 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
   double tile_carry = 0.0;  // return at the slot after the current tile (same in every thread)
   // a tile's inputs in registers: every load of the tile is issued before any
   // is used (loading the next tile during this one's scan measured slower)
-  uint8_t mk[kPer];
+  uint32_t mk = 0;  // bit k: slot tid + k NT of the tile is active
   float ov[kPer], rv[kPer];
   auto load_tile = [&](int64_t end) {
     const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
     const int n = int(end - start);
+    mk = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = tid + k * kAdvThreads;
-      mk[k] = 0;
       ov[k] = rv[k] = 0.0f;
       if (q < n) {
-        mk[k] = a.mask ? a.mask[base + start + q] : 1;
+        if (a.mask == nullptr || a.mask[base + start + q] != 0) mk |= 1u << k;
         if (shaped) {
           ov[k] = a.old[base + start + q];
           rv[k] = a.ref[base + start + q];
@@ -126,24 +132,39 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
   for (int64_t end = T; end > 0; end -= kAdvTile) {
     const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
     const int n = int(end - start);
-    if (end != T) load_tile(end);
-    __syncthreads();  // the previous tile's values are consumed
-    // token rewards r_t = m_t (-kl_coef (old - ref) + [t = T_i] R); masked
-    // values are discarded by selection
+    if (end != T) {
+      load_tile(end);
+      __syncthreads();  // the previous tile's values are consumed
+    }
+    // token rewards m_t (-kl_coef (old - ref)) go to LDS as soon as they
+    // arrive (masked values are discarded by selection); the terminal reward
+    // is added at the last active slot once that is known, below
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = tid + k * kAdvThreads;
       if (q >= n) continue;
-      const bool act = mk[k] != 0;
       double v = 0.0;
-      if (act) {
-        if (shaped) v = -a.kl_coef * (double(ov[k]) - double(rv[k]));
-        if (start + q == last) v = v + R;
-      }
+      if (shaped && ((mk >> k) & 1u)) v = -a.kl_coef * (double(ov[k]) - double(rv[k]));
       sh.v[adv_lds(q)] = v;
-      sh.act[q] = act ? 1 : 0;
     }
-    __syncthreads();
+    if (last < 0) {
+      int qm = -1;
+      if (mk != 0) qm = tid + (31 - __builtin_clz(mk)) * kAdvThreads;  // q < n wherever mk is set
+      qm = wave_max_i32(qm);
+      if (lane == 0) sh.wmax[wv] = qm;
+    }
+    __syncthreads();  // the tile's rewards and wmax are complete
+    if (last < 0) {
+      int m = -1;
+      for (int w = 0; w < NW; ++w) m = sh.wmax[w] > m ? sh.wmax[w] : m;
+      if (m >= 0) {
+        last = start + m;
+        // r_T = shaped + R at the last active slot: the thread that folds the
+        // slot's chunk adds it (nobody else touches that chunk before the
+        // next barrier)
+        if (m / kAdvChunk == tid) sh.v[adv_lds(m)] = sh.v[adv_lds(m)] + R;
+      }
+    }
     // this thread's chunk as an affine map x -> h + g x of the return after it
     const int q0 = tid * kAdvChunk < n ? tid * kAdvChunk : n;
     const int q1 = q0 + kAdvChunk < n ? q0 + kAdvChunk : n;
@@ -187,9 +208,14 @@ __device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& 
       sh.v[adv_lds(q)] = acc;
     }
     __syncthreads();
-    for (int q = tid; q < n; q += kAdvThreads) {
-      const bool act = sh.act[q] != 0;
-      f(start + q, act, act ? sh.v[adv_lds(q)] : 0.0);
+    // the mask comes from the registers: thread tid loaded slots tid + k NT
+#pragma unroll 2
+    for (int k = 0; k < kPer; ++k) {
+      const int q = tid + k * kAdvThreads;
+      if (q < n) {
+        const bool act = (mk >> k) & 1u;
+        f(start + q, act, act ? sh.v[adv_lds(q)] : 0.0);
+      }
     }
   }
 }
@@ -253,34 +279,7 @@ __global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) 
   const int64_t base = i * a.T;
   if (i == 0 && tid == 0) a.hdr->status = 0;
 
-  if (a.estimator == GRPO_ADV_REINFORCE_PP) {
-    // last active slot of the sequence (the terminal reward goes there)
-    long long mx = -1;
-    constexpr int U = 8;
-    for (int64_t t0 = tid; t0 < a.T; t0 += int64_t(U) * kAdvThreads) {
-      bool act[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t t = t0 + int64_t(k) * kAdvThreads;
-        act[k] = t < a.T && adv_active(a, base + t);
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k)
-        if (act[k]) mx = t0 + int64_t(k) * kAdvThreads;
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const long long o = __shfl_xor(mx, off);
-      mx = o > mx ? o : mx;
-    }
-    if (tid % kWave == 0) sh.red_i[tid / kWave] = mx;
-    __syncthreads();
-    if (tid == 0) {
-      long long m = -1;
-      for (int k = 0; k < kAdvThreads / kWave; ++k) m = sh.red_i[k] > m ? sh.red_i[k] : m;
-      sh.last = m;
-    }
-  } else {
+  if (a.estimator != GRPO_ADV_REINFORCE_PP) {
     // group mean (the sample itself included), summed in index order by one
     // thread from rewards the whole block stages in LDS (rounds of kAdvTile)
     GroupSpec g{};
@@ -377,6 +376,16 @@ __global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(Tok
   if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
 }
 
+// (v - mu) / sd as a product with the binary64 reciprocal of sd, formed once
+// per block: a division per slot measured 1.1-1.3 us more per call.  The
+// product is within one binary64 ulp of the quotient, so after the rounding
+// to float32 the two differ only where the quotient lies that close to a
+// float32 rounding boundary.
+__device__ __forceinline__ double adv_scale(double v, double mu, double inv) {
+#pragma clang fp contract(off)
+  return (v - mu) * inv;
+}
+
 constexpr int kNormThreads = 256;
 #ifndef GRPO_NORM_QUADS
 #define GRPO_NORM_QUADS 4
@@ -462,6 +471,7 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
       mu = sh_musd[0];
       sd = sh_musd[1];
     }
+    const double inv = 1.0 / sd;
 #pragma unroll
     for (int u = 0; u < kNormQuads; ++u) {
       const int64_t q = q0 + int64_t(u) * kNormThreads;
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
       float o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        o[j] = ((m4[u] >> (8 * j)) & 0xffu) ? float(clamp_adv(a, (v[j] - mu) / sd)) : 0.0f;
+        o[j] = ((m4[u] >> (8 * j)) & 0xffu) ? float(clamp_adv(a, adv_scale(v[j], mu, inv))) : 0.0f;
       __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(a.out + 4 * q));
     }
     if (q0 == 0 && a.status) *a.status = a.hdr->status;  // block 0, after it published
@@ -488,13 +498,14 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
       mu = sh_musd[0];
       sd = sh_musd[1];
     }
+    const double inv = 1.0 / sd;
     const int64_t gid = int64_t(blockIdx.x) * kNormThreads + threadIdx.x;
     if (gid >= rows) return;
     const bool act = adv_active(a, gid);
     float o = 0.0f;
     if (act) {
       const double v = rpp ? a.V[gid] : a.mean[gid / a.T];
-      o = float(clamp_adv(a, (v - mu) / sd));
+      o = float(clamp_adv(a, adv_scale(v, mu, inv)));
     }
     a.out[gid] = o;
     if (gid == 0 && a.status) *a.status = a.hdr->status;

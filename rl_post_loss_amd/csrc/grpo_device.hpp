@@ -202,6 +202,21 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return wave_step_i32<5>(v);
 }
 
+template <int STEP>
+__device__ __forceinline__ int wave_step_max(int v) {
+  const Pair32 p = wave_step_u32<STEP>(uint32_t(v));
+  return int(p.a) > int(p.b) ? int(p.a) : int(p.b);
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = wave_step_max<0>(v);
+  v = wave_step_max<1>(v);
+  v = wave_step_max<2>(v);
+  v = wave_step_max<3>(v);
+  v = wave_step_max<4>(v);
+  return wave_step_max<5>(v);
+}
+
 __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
   v = wave_step_or<0>(v);
   v = wave_step_or<1>(v);
