@@ -961,9 +961,12 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
             total += sum(used) / len(used) * scale
         for name, rows in by_name.items():
             used = rows[skip_first:] if len(rows) > skip_first else rows
-            per_kernel.setdefault(_short(name), {})[counter] = dict(
-                counter_per_dispatch=rows, dispatches_averaged=len(used),
-                bytes_avg=sum(used) / len(used) * scale)
+            d = dict(dispatches=len(rows), dispatches_averaged=len(used),
+                     bytes_avg=sum(used) / len(used) * scale,
+                     counter_median=_median(used), counter_min=min(used), counter_max=max(used))
+            if len(rows) <= 16:
+                d["counter_per_dispatch"] = rows
+            per_kernel.setdefault(_short(name), {})[counter] = d
         res[counter] = dict(calibration_counter=c, calibration_bytes=CALIB_BYTES,
                             scale_bytes_per_unit=scale, kernel_bytes_avg=total)
     traffic = res["FETCH_SIZE"]["kernel_bytes_avg"] + res["WRITE_SIZE"]["kernel_bytes_avg"]
@@ -991,7 +994,7 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
     lines += ["", "| kernel | dispatches | read (MB, avg) | written (MB, avg) |", "|---|---|---|---|"]
     for name, d in sorted(per_kernel.items()):
         f_, w_ = d.get("FETCH_SIZE", {}), d.get("WRITE_SIZE", {})
-        lines.append(f"| {name} | {len(f_.get('counter_per_dispatch', []))} | "
+        lines.append(f"| {name} | {f_.get('dispatches', 0)} | "
                      f"{f_.get('bytes_avg', 0) / 1e6:.3f} | {w_.get('bytes_avg', 0) / 1e6:.3f} |")
     lines += ["", f"Traffic per launch of {kernel}"
               + (" (" + " + ".join(_family(kernel)) + ")" if kernel in KERNEL_FAMILIES else "")
