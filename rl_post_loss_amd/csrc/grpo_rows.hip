@@ -34,7 +34,11 @@
 #define GRPO_PASS2_REVERSE 1   // gradient pass walks each thread's chunks backwards
 #endif
 #ifndef GRPO_UNROLL
-#define GRPO_UNROLL 8          // 16-byte chunks of x (and of y) in flight per thread
+#define GRPO_UNROLL 6          // 16-byte chunks of x (and of y) in flight per thread: at 8
+                               // the fused 1024-thread kernel spilled (128 VGPRs) and the
+                               // 256-thread forward-only kernel fit three waves per SIMD
+                               // instead of four (V = 151,936: 11.87 -> 11.60 ms fused;
+                               // GSPO at V = 32,000: 1.84 -> 1.74 ms)
 #endif
 #ifndef GRPO_Y_NONTEMPORAL
 #define GRPO_Y_NONTEMPORAL 1   // the reference row is read once: non-temporal loads
