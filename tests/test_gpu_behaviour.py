@@ -224,6 +224,7 @@ def test_autograd_split_forward_backward(gpu_lib, V):
     (40003, "bf16", 40008, None),           # padded 16-byte rows: the flat map's scalar tail
     (20000, "f32", None, None),             # float32 rows of 80 KB
     (40000, "bf16", None, torch.float32),   # bf16 logits, float32 gradient
+    (40000, "f16", None, None),             # IEEE half logits and gradient
 ])
 def test_split_backward_long_rows(gpu_lib, V, dtype, ld, gdtype):
     """The gradient-only pass on rows above 64 KB (the flat map over 16-byte
@@ -260,8 +261,8 @@ def test_split_backward_long_rows(gpu_lib, V, dtype, ld, gdtype):
                                          h["mask"], h["rewards"], groups=wl.groups_kwargs(),
                                          cfg=cfg, grad_scale=scale)
         compare_scalars(res, ref64, cfg, 1e-4 if dtype != "f32" else 1e-5, f"forward V={V}")
-        compare_logits_grad(to_np(gbuf[..., :V]), ref64, cfg, h["mask"],
-                            "f32" if gdt == torch.float32 else "bf16", f"backward x{scale}")
+        gname = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[gdt]
+        compare_logits_grad(to_np(gbuf[..., :V]), ref64, cfg, h["mask"], gname, f"backward x{scale}")
 
 
 def test_confident_token_gradient_relative_accuracy(gpu_lib):
