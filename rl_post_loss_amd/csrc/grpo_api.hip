@@ -304,7 +304,9 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 #endif
 #ifndef GRPO_NT_SPLIT
 #define GRPO_NT_SPLIT 256   // threads per row above 4 KB for the forward-only and
-                            // gradient-only kernels (several rows per CU, measured best)
+                            // gradient-only kernels (several rows per CU, measured best;
+                            // the gradient-only pass over aligned rows above 64 KB is
+                            // grpo_rows.hip's flat map instead)
 #endif
 #ifndef GRPO_NT_BWD_MID
 #define GRPO_NT_BWD_MID 1024  // the gradient-only kernel on rows of 32-64 KB (measured at

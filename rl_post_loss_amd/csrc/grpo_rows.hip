@@ -12,7 +12,9 @@
 //   pass 2  re-reads x and writes g_v = G * (onehot(a)_v - softmax(x)_v)
 //           ("GRPO Loss", Entry Point: the gradient lands in policy_logits).
 // Pass 2 walks the row backwards, so the bytes pass 1 read last are the
-// first ones re-read, while they are still in L2 / the memory-side cache.
+// first ones re-read, while they are still in L2 / the memory-side cache;
+// with a whole block per row (1024 threads, one block per CU) the row's first
+// GRPO_HOLD_CHUNKS x 1024 chunks, re-read last, are kept in LDS instead.
 //
 // Numerics (all float32): every thread accumulates
 //   S_t = sum 2^(fma(x_v, log2e, -mL_t)),  mL_t = fl(m_t * log2e),
@@ -39,6 +41,12 @@
                                // 256-thread forward-only kernel fit three waves per SIMD
                                // instead of four (V = 151,936: 11.87 -> 11.60 ms fused;
                                // GSPO at V = 32,000: 1.84 -> 1.74 ms)
+#endif
+#ifndef GRPO_HOLD_CHUNKS
+#define GRPO_HOLD_CHUNKS 6     // fused 1024-thread rows: chunks per thread kept in LDS from
+                               // pass 1 to pass 2, the row's first ones, which pass 2 re-reads
+                               // last (96 KB per block; V = 151,936: 11.69 -> 11.04 ms; 4, 5,
+                               // 7, 8, 9 chunks: 11.30, 11.14, 11.07, 11.10, 11.18 ms)
 #endif
 #ifndef GRPO_Y_NONTEMPORAL
 #define GRPO_Y_NONTEMPORAL 1   // the reference row is read once: non-temporal loads
@@ -69,6 +77,11 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
   __shared__ Lse sh_lse[2][NW > 1 ? NW : 1];
   __shared__ float sh_xa[2];
   __shared__ float sh_bcast[4];
+  // the row's first kHoldN chunks stay in LDS between the passes (thread lid
+  // keeps its own chunks lid + k NT at index lid + k NT, so no barrier)
+  constexpr int64_t kHoldN = (MODE == kFused && VEC && NT == 1024) ? int64_t(GRPO_HOLD_CHUNKS) * NT : 0;
+  extern __shared__ __align__(16) unsigned char grpo_rows_hold[];
+  typename IN::raw_t* const hold = reinterpret_cast<typename IN::raw_t*>(grpo_rows_hold);
 
   const int lid = threadIdx.x % NT;
   const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / NT;
@@ -123,6 +136,9 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
     // one chunk of x (and y) into the running sums; the owner of the taken
     // token's chunk lifts it out first
     auto consume = [&](const raw_t* px, const raw_t* py, int u, int64_t cc) {
+      if constexpr (kHoldN > 0) {
+        if (cc < kHoldN) hold[cc] = px[u];
+      }
       float fx[N], fy[N];
       IN::cvt(px[u], fx);
       if (has_ref) IN::cvt(py[u], fy);
@@ -194,7 +210,11 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
 #endif
     for (; c < nvec; c += NT) {
       float fx[N], fy[N];
-      IN::cvt(IN::load(xrow, c), fx);
+      const raw_t rxc = IN::load(xrow, c);
+      if constexpr (kHoldN > 0) {
+        if (c < kHoldN) hold[c] = rxc;
+      }
+      IN::cvt(rxc, fx);
       if (has_ref) IN::cvt(GRPO_Y_NONTEMPORAL ? IN::load_nt(yrow, c) : IN::load(yrow, c), fy);
       if (c == ca) {
         own = true;
@@ -311,7 +331,17 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
         typename IN::raw_t rx[U];
         if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(GRPO_LOAD_PRIO);
 #pragma unroll
-        for (int u = 0; u < U; ++u) rx[u] = IN::load(xrow, c + u * step);
+        for (int u = 0; u < U; ++u) {
+          const int64_t cc = c + u * step;
+          if constexpr (kHoldN > 0) {
+            if (cc < kHoldN)
+              rx[u] = hold[cc];
+            else
+              rx[u] = IN::load(xrow, cc);
+          } else {
+            rx[u] = IN::load(xrow, cc);
+          }
+        }
         if constexpr (GRPO_LOAD_PRIO > 0) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -329,7 +359,16 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
       }
       for (; more(c); c += step) {
         float f[N], g[N];
-        IN::cvt(IN::load(xrow, c), f);
+        typename IN::raw_t r;
+        if constexpr (kHoldN > 0) {
+          if (c < kHoldN)
+            r = hold[c];
+          else
+            r = IN::load(xrow, c);
+        } else {
+          r = IN::load(xrow, c);
+        }
+        IN::cvt(r, f);
 #pragma unroll
         for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
         if (c == ca) {
@@ -464,8 +503,9 @@ static hipError_t launch_t(const RowArgs& a, hipStream_t stream) {
   constexpr int RPB = BLOCK / NT;
   constexpr int U = VEC ? GRPO_UNROLL : 8;
   const int64_t blocks = (a.rows + RPB - 1) / RPB;
+  constexpr size_t kHoldBytes = (MODE == kFused && VEC && NT == 1024) ? size_t(GRPO_HOLD_CHUNKS) * NT * 16 : 0;
   hipLaunchKernelGGL((grpo_rows_kernel<TI, TG, NT, MODE, VEC, U>), dim3(unsigned(blocks)),
-                     dim3(BLOCK), 0, stream, a);
+                     dim3(BLOCK), kHoldBytes, stream, a);
   return hipGetLastError();
 }
 
