@@ -92,14 +92,20 @@ def byte_model(wl, active, rows):
     return active * V * (3 * bx + bg) + (rows - active) * V * bg + rows * (8 + 4 + 1)
 
 
+HELD_CHUNKS = 6 * 1024   # 16-byte policy chunks per row the fused streaming kernel keeps in LDS
+
+
 def min_bytes(wl, active, rows, resident):
     """The bytes the chosen row kernel must move at least: the resident kernel
-    reads each active policy row once (policy + reference + gradient), the
-    streaming kernel twice (the byte model itself)."""
-    if not resident:
-        return byte_model(wl, active, rows)
+    reads each active policy row once (policy + reference + gradient); the
+    streaming kernel reads it twice except the first HELD_CHUNKS 16-byte
+    chunks of the row, which it keeps in LDS between its passes."""
     bx = 4 if wl.dtype == "f32" else 2
     V = wl.V
+    if not resident:
+        # only the 1024-thread kernel (rows above 64 KB) holds chunks
+        held = min(V * bx // 16, HELD_CHUNKS) * 16 if V * bx > 65536 else 0
+        return byte_model(wl, active, rows) - active * held
     return active * V * (2 * bx + bx) + (rows - active) * V * bx + rows * (8 + 4 + 1)
 
 
@@ -513,7 +519,10 @@ def run_logits_record(args, wl, inp, reduction, objective="default", pool=None, 
         "bit_reproducible": bool(repro),
         "roofline": roofline(kname, key, alg, kern, {
             "byte_model": "policy row read twice, reference once, gradient written once per active "
-                          "row; zero gradient per masked row; 13 B of side inputs per slot",
+                          "row; zero gradient per masked row; 13 B of side inputs per slot; "
+                          "kernel_min_bytes: what the chosen kernel must move (the resident kernel "
+                          "reads the policy row once, the streaming kernel keeps its first "
+                          f"{HELD_CHUNKS} 16-byte chunks in LDS between its passes)",
             "kernel_min_bytes": mb,
             "kernel_min_frac": mb / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS}),
     }
