@@ -79,9 +79,14 @@ def test_masked_nan_inf_garbage_ids_do_not_leak(gpu_lib):
     assert int(dirty.status[0]) == 0
 
 
-def test_in_place_gradient_matches_out_of_place(gpu_lib):
-    wl = _wl(8192, "bf16", T=8)
-    announce("in place")
+@pytest.mark.parametrize("V", [8192, 40000, 151936])
+def test_in_place_gradient_matches_out_of_place(gpu_lib, V):
+    """The gradient written over the policy logits equals the out-of-place
+    one bit for bit: resident rows at 256 and 1024 threads, and streaming
+    rows whose first chunks pass 2 takes from LDS rather than from the
+    (by then partly overwritten) logits."""
+    wl = _wl(V, "bf16", T=8 if V < 100000 else 4)
+    announce(f"in place V={V}")
     _, inp = _inputs(wl, seed=13)
     out = _call(gpu_lib, inp, wl)
     pol = inp["policy"].clone()
