@@ -1021,6 +1021,47 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
     print(json.dumps(dict(kernel=kernel, workload=workload, traffic=traffic)), flush=True)
 
 
+def summarize_counters(run_dirs, workload, name, out_dir, commands, skip_first=1):
+    """profiles/<name>_<workload>_counters.md from rocprofv3 --pmc runs of
+    SQ/GRBM counters: per libgrpo kernel, the median per dispatch of every
+    counter (the first ``skip_first`` dispatches left out), and instructions
+    per wave."""
+    per = {}
+    for d in run_dirs:
+        for row in _csv_rows(d, "counter_collection.csv"):
+            k = _short(row.get("Kernel_Name", ""))
+            if "grpo" not in row.get("Kernel_Name", ""):
+                continue
+            did = int(row["Dispatch_Id"])
+            c = row["Counter_Name"]
+            per.setdefault(k, {}).setdefault(c, {})
+            per[k][c][did] = per[k][c].get(did, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no libgrpo counter rows")
+    lines = [f"# {name} on {workload}: wave and instruction counters", "",
+             f"Kernel sources hash {kernel_source_hash()}.  Medians per dispatch over every "
+             f"dispatch but the first {skip_first} (warm-up); each counter set in a run of its own.",
+             "", "Commands (repository root, one MI355X):", ""] + ["    " + c for c in commands]
+    for k in sorted(per):
+        lines += ["", f"## {k}", "", "| counter | median per dispatch | dispatches |", "|---|---|---|"]
+        med = {}
+        for c in sorted(per[k]):
+            vals = [v for _, v in sorted(per[k][c].items())]
+            used = vals[skip_first:] if len(vals) > skip_first else vals
+            med[c] = _median(used)
+            lines.append(f"| {c} | {med[c]:.6g} | {len(used)} |")
+        waves = med.get("SQ_WAVES")
+        if waves:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+                      "SQ_INSTS_VMEM_WR"):
+                if c in med:
+                    lines.append(f"| {c} per wave | {med[c] / waves:.1f} | |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{name}_{workload}_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[-12:]), flush=True)
+
+
 def summarize_trace(run_dir, workload, kernel, out_dir, command, skip_first):
     """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3
     --kernel-trace --stats run: per libgrpo kernel, the dispatch count and
@@ -1077,6 +1118,9 @@ def main():
                     help="rocprofv3 --kernel-trace output directory to summarise")
     ap.add_argument("--trace-command", default="", help="the command that made --summarize-trace's run")
     ap.add_argument("--skip-first", type=int, default=1, help="warm-up dispatches left out")
+    ap.add_argument("--summarize-counters", nargs="+", default=None,
+                    help="rocprofv3 --pmc output directories of SQ/GRBM counter runs to summarise")
+    ap.add_argument("--commands", nargs="*", default=[], help="the commands that made those runs")
     args = ap.parse_args()
     if args.calibrate_only:
         calibrate_only()
@@ -1085,6 +1129,11 @@ def main():
         key = args.workload.replace(":", "_")
         summarize_pmc(args.summarize_pmc, key, args.kernel, os.path.join(ROOT, "profiles"),
                       args.skip_first, args.regex)
+        return
+    if args.summarize_counters:
+        key = args.workload.replace(":", "_")
+        summarize_counters(args.summarize_counters, key, args.kernel, os.path.join(ROOT, "profiles"),
+                           args.commands, args.skip_first)
         return
     if args.summarize_trace:
         key = args.workload.replace(":", "_")
