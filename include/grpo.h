@@ -95,7 +95,9 @@ extern "C" {
 typedef enum grpo_status {
   GRPO_OK = 0,
   GRPO_ERR_NULL = 1,       /* a required pointer is NULL */
-  GRPO_ERR_SHAPE = 2,      /* B, T or V not positive, a row stride < V, or sizes overflow */
+  GRPO_ERR_SHAPE = 2,      /* B, T or V not positive, a row stride < V, or sizes overflow
+                              (the logits entry points take at most 2^31 - 1 rows B*T, the
+                              token advantages at most 2^31 - 1 blocks of 256 slots) */
   GRPO_ERR_DTYPE = 3,      /* unknown dtype code */
   GRPO_ERR_GROUPS = 4,     /* group specification invalid ([GRPO-LOSS] Group specification) */
   GRPO_ERR_CONFIG = 5,     /* a grpo_cfg field invalid, or beta > 0 without a reference */

@@ -38,6 +38,9 @@ hipEvent_t g_ev_stop = nullptr;
 // Largest element count we accept for one tensor: keeps every byte offset
 // far inside int64 and every row index inside the kernels' arithmetic.
 constexpr int64_t kMaxElems = int64_t(1) << 50;
+// Largest grid dimension: the row kernels launch a block per row (B*T rows),
+// the token-advantage output pass a block per 256 slots at most.
+constexpr int64_t kMaxGridBlocks = (int64_t(1) << 31) - 1;
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
   if (a <= 0 || b <= 0) return false;
@@ -573,6 +576,7 @@ static grpo_status logits_common_checks(const void* policy, int32_t logits_dtype
   if (V <= 0 || row_stride < V || !mul_ok(*rows, row_stride, kMaxElems, &tmp))
     return GRPO_ERR_SHAPE;
   if (V > (int64_t(1) << 40)) return GRPO_ERR_SHAPE;
+  if (*rows > kMaxGridBlocks) return GRPO_ERR_SHAPE;
   if (grad_out && (grad_row_stride < V || !mul_ok(*rows, grad_row_stride, kMaxElems, &tmp)))
     return GRPO_ERR_SHAPE;
   return GRPO_OK;
@@ -820,6 +824,7 @@ grpo_status grpo_token_advantages(int32_t estimator, const float* rewards, const
   if (!rewards || !adv_out) return GRPO_ERR_NULL;
   int64_t rows;
   if (!mul_ok(B, T, kMaxElems, &rows) || B > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if ((rows + 255) / 256 > kMaxGridBlocks) return GRPO_ERR_SHAPE;
   if (estimator != GRPO_ADV_REINFORCE_PP && estimator != GRPO_ADV_REINFORCE_PP_BASELINE)
     return GRPO_ERR_CONFIG;
   if (!(kl_coef >= 0.0 && isfinite(kl_coef)) || !(gamma > 0.0 && gamma <= 1.0))

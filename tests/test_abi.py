@@ -131,6 +131,10 @@ def test_fwd_bwd_argument_validation():
     assert _fwd(lib, V=0) == E["GRPO_ERR_SHAPE"]
     assert _fwd(lib, ld=16) == E["GRPO_ERR_SHAPE"]          # row stride < V
     assert _fwd(lib, gld=16) == E["GRPO_ERR_SHAPE"]
+    # a block per row: B*T above 2^31 - 1 rows is refused, not truncated
+    assert _fwd(lib, B=1 << 16, T=1 << 15, V=1) == E["GRPO_ERR_SHAPE"]
+    assert lib.grpo_loss_bwd(FAKE, 0, 1, FAKE, 0, None, 1 << 16, 1 << 15, 1, FAKE + 0x4000000, 0, 1,
+                             None, FAKE_WS, 1 << 30, None) == E["GRPO_ERR_SHAPE"]
     assert _fwd(lib, dtype=7) == E["GRPO_ERR_DTYPE"]
     assert _fwd(lib, gdtype=9) == E["GRPO_ERR_DTYPE"]
     assert _fwd(lib, ids_dtype=3) == E["GRPO_ERR_DTYPE"]
@@ -250,6 +254,9 @@ def test_token_loss_and_advantages_validation():
     assert tok(gamma=1.5) == E["GRPO_ERR_CONFIG"]
     assert tok(norm=2) == E["GRPO_ERR_CONFIG"]
     assert tok(ref=None) == E["GRPO_ERR_NULL"]                     # KL shaping needs ref
+    # the output pass launches a block per 256 slots at most: 2^31 such blocks are refused
+    assert lib.grpo_token_advantages(0, FAKE, FAKE, FAKE, None, 1 << 20, 1 << 19, None, 0.1, 1.0,
+                                     1, FAKE, None, FAKE_WS, 1 << 30, None) == E["GRPO_ERR_SHAPE"]
     assert tok(est=1) == E["GRPO_ERR_NULL"]                        # baseline needs groups
     gb, _ = _groups(scale=1)
     assert tok(est=1, g=gb) == E["GRPO_ERR_GROUPS"]                # inclusive mean, no std
