@@ -26,10 +26,11 @@
 // With the global normalization the returns are kept in binary64 in the
 // workspace and each sequence leaves the moments (count, mean, sum of squared
 // deviations) of its active values: per thread from sums of deviations
-// from its first value, merged across the block.  The output pass then
-// writes (A - mu) x (1 / sd); each of its blocks first issues its loads, then
-// merges the sequences' moments with Chan et al.'s pairwise update in one
-// fixed tree (the same bits in every block, so results repeat bit for bit).
+// from its first value, merged across the block with Chan et al.'s pairwise
+// update.  The output pass then writes (A - mu) x (1 / sd); each of its
+// blocks first issues its loads, then forms mu and sd from the sequences'
+// moments in fixed-order sums (the same bits in every block, so results
+// repeat bit for bit).
 // Two launches in all (three beyond kFusedMomentsMaxB sequences, where one
 // block merges the moments once).
 
@@ -352,30 +353,6 @@ __global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) 
   }
 }
 
-// One block: the moments of every active slot of the batch, merged over the
-// sequences in a fixed tree; mu and the floored std for the output pass.
-__global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(TokAdvArgs a) {
-#pragma clang fp contract(off)
-  __shared__ double sh_mom[3 * (kMomentThreads / kWave)];
-  const int tid = threadIdx.x;
-  Moments mo{0.0, 0.0, 0.0};
-  for (int64_t k = tid; k < a.B; k += kMomentThreads) {
-    const int32_t n = a.L[k];
-    if (n > 0) {
-      // L_i copies of the baseline value enter as one set of n equal values
-      mo = moments_merge(mo, Moments{double(n), a.mean[k], a.M2[k]});
-    }
-  }
-  mo = block_moments<kMomentThreads>(mo, sh_mom);
-  if (tid != 0) return;
-  const long long n = (long long)mo.n;
-  a.hdr->num_tokens = n;
-  a.hdr->mu = n > 0 ? mo.m : 0.0;
-  const double var = n > 0 ? mo.M2 / mo.n : 0.0;
-  a.hdr->sd = sqrt(var > 1e-8 ? var : 1e-8);
-  if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
-}
-
 // (v - mu) / sd as a product with the binary64 reciprocal of sd, formed once
 // per block: a division per slot measured 1.1-1.3 us more per call.  The
 // product is within one binary64 ulp of the quotient, so after the rounding
@@ -396,37 +373,85 @@ constexpr int kNormQuads = GRPO_NORM_QUADS;  // quads of 4 slots per thread
 // beyond it the merge runs once in grpo_tokadv_moments_kernel.
 constexpr int64_t kFusedMomentsMaxB = 4096;
 
-// mu and the floored sd of the global masked normalization, from the
-// sequences' moments merged in one fixed tree: thread t merges sequences
-// t, t + NT, ... in order, then the block tree of block_moments.  Every block
-// that runs it holds the same bits; with `publish` it also stores the count,
-// the moments and the no-token fault in the header.
+// mu and the floored sd of the global masked normalization from the
+// sequences' moments (count L_i, mean_i, sum of squared deviations M2_i), in
+// fixed-order sums: every block that runs it holds the same bits; with
+// `publish` it also stores the count, the moments and the no-token fault in
+// the header.
+// Block sums of two binary64 values through one LDS exchange: the butterfly
+// in each wave, then the wave partials in wave order (every thread gets the
+// totals).  sh holds 2 * NT / kWave doubles.
+template <int NT>
+__device__ __forceinline__ void block_sum2_f64(double& x, double& y, double* sh) {
+  constexpr int NW = NT / kWave;
+  x = wave_sum_f64<kWave>(x);
+  y = wave_sum_f64<kWave>(y);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) {
+    sh[w] = x;
+    sh[NW + w] = y;
+  }
+  __syncthreads();
+  double tx = 0.0, ty = 0.0;
+  for (int k = 0; k < NW; ++k) {
+    tx += sh[k];
+    ty += sh[NW + k];
+  }
+  x = tx;
+  y = ty;
+}
+
 template <int NT>
 __device__ void merge_global_moments(const TokAdvArgs& a, double* sh_mom, double* sh_out,
                                      bool publish) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
-  Moments mo{0.0, 0.0, 0.0};
+  // N and sum_i L_i mean_i give mu; then M2 = sum_i (M2_i + L_i (mean_i - mu)^2),
+  // every term non-negative; thread t takes sequences t, t + NT, ... in order.
+  // (Chan et al.'s pairwise merge in a shuffle tree, a division per merge,
+  // measured 0.7 us more per call at B = 1024 and gave the same outputs.)
+  double s = 0.0, cnt = 0.0;
   for (int64_t k = tid; k < a.B; k += NT) {
     const int32_t n = a.L[k];
-    if (n > 0) mo = moments_merge(mo, Moments{double(n), a.mean[k], a.M2[k]});
+    if (n > 0) {
+      s = s + double(n) * a.mean[k];
+      cnt = cnt + double(n);
+    }
   }
-  mo = block_moments<NT>(mo, sh_mom);
+  block_sum2_f64<NT>(s, cnt, sh_mom);
+  const double mu = cnt > 0.0 ? s / cnt : 0.0;
+  double q = 0.0, unused = 0.0;
+  for (int64_t k = tid; k < a.B; k += NT) {
+    const int32_t n = a.L[k];
+    if (n > 0) {
+      const double d = a.mean[k] - mu;
+      q = q + (a.M2[k] + double(n) * (d * d));
+    }
+  }
+  block_sum2_f64<NT>(q, unused, sh_mom);
   if (tid == 0) {
-    const long long n = (long long)mo.n;
-    const double mu = n > 0 ? mo.m : 0.0;
-    const double var = n > 0 ? mo.M2 / mo.n : 0.0;
+    const double var = cnt > 0.0 ? q / cnt : 0.0;
     const double sd = sqrt(var > 1e-8 ? var : 1e-8);
     sh_out[0] = mu;
     sh_out[1] = sd;
     if (publish) {
-      a.hdr->num_tokens = n;
+      a.hdr->num_tokens = (long long)cnt;
       a.hdr->mu = mu;
       a.hdr->sd = sd;
-      if (n == 0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
+      if (cnt == 0.0) a.hdr->status |= GRPO_FAULT_NO_TOKENS;
     }
   }
   __syncthreads();
+}
+
+// One block: the batch's moments from the sequences' (beyond
+// kFusedMomentsMaxB sequences, where every output block merging them would
+// cost more than this launch); mu and the floored std for the output pass.
+__global__ __launch_bounds__(kMomentThreads) void grpo_tokadv_moments_kernel(TokAdvArgs a) {
+  __shared__ double sh_mom[3 * (kMomentThreads / kWave)];
+  __shared__ double sh_out[2];
+  merge_global_moments<kMomentThreads>(a, sh_mom, sh_out, true);
 }
 
 // Output pass over the slots: (A - mu) / sd at active slots, 0 elsewhere;
