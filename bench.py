@@ -748,6 +748,61 @@ def run_adv_record(args, name, pool=None, workers=1):
     return rec
 
 
+def run_pages_shapes(args):
+    """The fused logits call at the shapes of the grpo.cpp README's CUDA table
+    (1,024 token slots as B = 8 x T = 128 in groups of 4, f32 logits and
+    gradient, V = 32,768 and 131,072), full and ragged masks, with and
+    without reference logits.  Each call timed with events around it on the
+    current stream (its launches and the gaps between them included); the
+    median of ``steps`` calls."""
+    import torch
+    import rl_post_loss_amd as rpl
+    from workloads import LogitsWorkload, make_logits_inputs
+
+    rpl.load_library()
+    dev = torch.device("cuda:0")
+    recs = {}
+    for V in (32768, 131072):
+        for ragged in (False, True):
+            wl = LogitsWorkload(name=f"pages_v{V}", group_sizes=(4, 4), T=128, V=V, dtype="f32",
+                                logit_std=1.0, ref_noise_std=0.1 ** 0.5, old_noise_std=0.05 ** 0.5,
+                                reward_p=0.5, len_range=(1, 128) if ragged else None)
+            inp = make_logits_inputs(wl, device=dev, seed=args.seed)
+            grad = torch.empty_like(inp["policy"])
+            active = int(inp["mask"].sum())
+            for with_ref in (False, True):
+                kw = dict(eps_low=wl.eps_low, eps_high=wl.eps_high, reduction="token_mean",
+                          beta=wl.beta if with_ref else 0.0, **wl.groups_kwargs())
+                ref = inp["ref"] if with_ref else None
+                out = [None]
+
+                def call():
+                    out[0] = rpl.grpo_loss_fwd_bwd(inp["policy"], ref, inp["action_ids"],
+                                                   inp["old_logps"], inp["rewards"], inp["mask"],
+                                                   grad_out=grad, out=out[0], **kw)
+
+                for _ in range(max(3, args.warmup)):
+                    call()
+                torch.cuda.synchronize()
+                ms = []
+                for _ in range(max(20, args.steps)):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    call()
+                    b.record()
+                    b.synchronize()
+                    ms.append(a.elapsed_time(b))
+                key = f"v{V}_{'ragged' if ragged else 'full'}_{'ref' if with_ref else 'noref'}"
+                recs[key] = {"ms_per_call": _median(ms), "active_slots": active,
+                             "V": V, "B": wl.B, "T": wl.T, "reference_logits": with_ref}
+            del inp, grad
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "ms per fused logits call at the grpo.cpp README table shapes "
+                                "(1,024 token slots, f32)", "unit": "ms", "higher_is_better": False,
+                      "timing": "events around each call on the current stream, median of the calls",
+                      "data": "synthetic", "configs": recs}), flush=True)
+
+
 def _line(rec, args, wl_key):
     """The bench line around one record."""
     return {
@@ -1102,7 +1157,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     help="all | a logits workload (optionally name:reduction) | token_loss_full | "
-                         "token_loss_ragged | adv_reinforce_pp | adv_reinforce_pp_baseline")
+                         "token_loss_ragged | adv_reinforce_pp | adv_reinforce_pp_baseline | "
+                         "pages_shapes")
     ap.add_argument("--objective", default="default", choices=sorted(OBJECTIVES))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1129,6 +1185,9 @@ def main():
         key = args.workload.replace(":", "_")
         summarize_pmc(args.summarize_pmc, key, args.kernel, os.path.join(ROOT, "profiles"),
                       args.skip_first, args.regex)
+        return
+    if args.workload == "pages_shapes":
+        run_pages_shapes(args)
         return
     if args.summarize_counters:
         key = args.workload.replace(":", "_")
