@@ -366,6 +366,10 @@ constexpr int kNormQuads = GRPO_NORM_QUADS;  // quads of 4 slots per thread
 // sequences' moments itself (no separate one-block kernel and launch);
 // beyond it the merge runs once in grpo_tokadv_moments_kernel.
 constexpr int64_t kFusedMomentsMaxB = 4096;
+#ifndef GRPO_MERGE_BATCH
+#define GRPO_MERGE_BATCH 4
+#endif
+constexpr int kMergeBatch = GRPO_MERGE_BATCH;  // sequences per thread per batch of loads
 
 // mu and the floored sd of the global masked normalization from the
 // sequences' moments (count L_i, mean_i, sum of squared deviations M2_i), in
@@ -381,23 +385,59 @@ __device__ void merge_global_moments(const TokAdvArgs& a, double* sh_mom, double
   // every term non-negative; thread t takes sequences t, t + NT, ... in order.
   // (Chan et al.'s pairwise merge in a shuffle tree, a division per merge,
   // measured 0.7 us more per call at B = 1024 and gave the same outputs.)
-  double s = 0.0, cnt = 0.0;
-  for (int64_t k = tid; k < a.B; k += NT) {
-    const int32_t n = a.L[k];
-    if (n > 0) {
-      s = s + double(n) * a.mean[k];
-      cnt = cnt + double(n);
+  // The loads go in batches of kMergeBatch sequences per thread, every load
+  // of a batch issued before any is used (a load after each test of L_i made
+  // a chain of dependent cache round trips); the first batch stays in
+  // registers for the second sum.  Per thread the order of the terms is the
+  // sequence order either way.
+  constexpr int kB = kMergeBatch;
+  auto load = [&](int64_t k0, int32_t* n, double* m, double* q2) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int64_t k = k0 + int64_t(u) * NT;
+      const bool in = k < a.B;
+      n[u] = in ? a.L[k] : 0;
+      m[u] = in ? a.mean[k] : 0.0;
+      q2[u] = in ? a.M2[k] : 0.0;
     }
+  };
+  auto add_first = [&](const int32_t* n, const double* m, double& s, double& cnt) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (n[u] > 0) {
+        s = s + double(n[u]) * m[u];
+        cnt = cnt + double(n[u]);
+      }
+  };
+  auto add_second = [&](const int32_t* n, const double* m, const double* q2, double mu, double& q) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (n[u] > 0) {
+        const double d = m[u] - mu;
+        q = q + (q2[u] + double(n[u]) * (d * d));
+      }
+  };
+  constexpr int64_t kStride = int64_t(NT) * kB;
+  int32_t n0[kB];
+  double m0[kB], q0[kB];
+  load(tid, n0, m0, q0);
+  double s = 0.0, cnt = 0.0;
+  add_first(n0, m0, s, cnt);
+  for (int64_t k0 = tid + kStride; k0 < a.B; k0 += kStride) {
+    int32_t n[kB];
+    double m[kB], q2[kB];
+    load(k0, n, m, q2);
+    add_first(n, m, s, cnt);
   }
   block_sum2_f64<NT>(s, cnt, sh_mom);
   const double mu = cnt > 0.0 ? s / cnt : 0.0;
   double q = 0.0, unused = 0.0;
-  for (int64_t k = tid; k < a.B; k += NT) {
-    const int32_t n = a.L[k];
-    if (n > 0) {
-      const double d = a.mean[k] - mu;
-      q = q + (a.M2[k] + double(n) * (d * d));
-    }
+  add_second(n0, m0, q0, mu, q);
+  for (int64_t k0 = tid + kStride; k0 < a.B; k0 += kStride) {
+    int32_t n[kB];
+    double m[kB], q2[kB];
+    load(k0, n, m, q2);
+    add_second(n, m, q2, mu, q);
   }
   block_sum2_f64<NT>(q, unused, sh_mom);
   if (tid == 0) {
