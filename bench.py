@@ -952,7 +952,8 @@ def calibrate_only():
 
 
 # the dominant "kernel" of a record that launches several kernels per call
-KERNEL_FAMILIES = {"grpo_tokadv_kernels": ("grpo_tokadv_kernel(", "grpo_tokadv_norm_kernel")}
+KERNEL_FAMILIES = {"grpo_tokadv_kernels": ("grpo_tokadv_kernel(", "grpo_tokadv_returns_kernel",
+                                           "grpo_tokadv_norm_kernel")}
 
 
 def _family(kernel):
@@ -1023,13 +1024,16 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
             raise SystemExit(f"missing {counter} values (calibration {len(cal)}, kernels {len(by_name)})")
         c = max(cal)
         scale = CALIB_BYTES / c
-        total = 0.0
+        total, present = 0.0, []
         for part in _family(kernel):
             rows = _matching(by_name, part)
             if not rows:
-                raise SystemExit(f"no {counter} dispatches of {part}")
+                continue   # a family member this estimator does not launch
+            present.append(part)
             used = rows[skip_first:] if len(rows) > skip_first else rows
             total += sum(used) / len(used) * scale
+        if not present:
+            raise SystemExit(f"no {counter} dispatches of {kernel}")
         for name, rows in by_name.items():
             used = rows[skip_first:] if len(rows) > skip_first else rows
             d = dict(dispatches=len(rows), dispatches_averaged=len(used),
@@ -1044,7 +1048,8 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
     cmds = pmc_commands(workload, regex, dirs) + [
         f"python bench.py --workload {workload} --kernel {kernel} --regex {regex} --summarize-pmc "
         f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"]
-    summary = dict(kernel=kernel, members=list(_family(kernel)), workload=workload,
+    summary = dict(kernel=kernel, members=[m for m in _family(kernel) if _matching(by_name, m)],
+                   workload=workload,
                    kernel_source_hash=kernel_source_hash(), counters=res, per_kernel=per_kernel,
                    traffic_bytes_per_launch=traffic, warmup_dispatches_skipped=skip_first,
                    commands=cmds)
@@ -1068,7 +1073,7 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
         lines.append(f"| {name} | {f_.get('dispatches', 0)} | "
                      f"{f_.get('bytes_avg', 0) / 1e6:.3f} | {w_.get('bytes_avg', 0) / 1e6:.3f} |")
     lines += ["", f"Traffic per launch of {kernel}"
-              + (" (" + " + ".join(_family(kernel)) + ")" if kernel in KERNEL_FAMILIES else "")
+              + (" (" + " + ".join(summary["members"]) + ")" if kernel in KERNEL_FAMILIES else "")
               + f": {traffic / 1e6:.3f} MB (read {res['FETCH_SIZE']['kernel_bytes_avg'] / 1e6:.3f}, "
               f"written {res['WRITE_SIZE']['kernel_bytes_avg'] / 1e6:.3f})."]
     with open(base + ".md", "w") as f:

@@ -14,14 +14,13 @@
 // Everything is binary64 with contraction off and rounded once to float32.
 // The returns run as a tiled backward scan: a sequence's block walks tiles of
 // kAdvTile slots from the right end; a tile's token rewards are staged in LDS
-// with coalesced loads as they arrive (the terminal reward is added at the
-// last active slot, found in the first tile from the right that has an
-// active slot, so the mask is read once), thread j folds its kAdvChunk
-// consecutive slots into an affine map x -> h + g x of the return after the
-// chunk, a suffix scan of those maps (wave shuffles, then the waves in
-// order) gives every chunk its carry and the carry into the next tile, every
-// chunk replays its slots from its carry, and the returns leave LDS with
-// coalesced accesses again.
+// as they arrive (the terminal reward is added at the last active slot,
+// found in the first tile from the right that has an active slot, so the
+// mask is read once), every thread folds one chunk of kAdvChunk consecutive
+// slots into an affine map x -> h + g x of the return after the chunk, a
+// scan of those maps (DPP lane patterns within a wave, then the waves in
+// order) gives every chunk its carry and the carry into the next tile,
+// every chunk replays its slots from its carry, and the returns leave LDS.
 //
 // With the global normalization the returns are kept in binary64 in the
 // workspace and each sequence leaves the moments (count, mean, sum of squared
@@ -59,7 +58,7 @@ struct AdvShared {
   double cval;                // baseline difference of the sequence
 };
 
-// LDS index of tile slot q (thread q / kAdvChunk owns kAdvChunk consecutive slots)
+// LDS index of tile slot q (chunk q / kAdvChunk: kAdvChunk consecutive slots)
 __device__ __forceinline__ int adv_lds(int q) { return (q / kAdvChunk) * kAdvPad + q % kAdvChunk; }
 
 __device__ __forceinline__ bool adv_active(const TokAdvArgs& a, int64_t r) {
@@ -71,151 +70,25 @@ __device__ __forceinline__ double clamp_adv(const TokAdvArgs& a, double v) {
   return v < a.clip_lo ? a.clip_lo : (v > a.clip_hi ? a.clip_hi : v);  // keeps a NaN
 }
 
-// Calls f(t, active, A_t) once for every slot t of sequence i (A_t the raw
-// advantage, 0 at masked slots); each thread visits slots t = tile start +
-// threadIdx.x + k * blockDim.x, tiles from the right end.  All threads of
-// the block must call it.
+// The baseline's raw advantage at every slot of sequence i: f(t, active, A_t)
+// with A_t = c at active slots and 0 elsewhere; thread j visits slots
+// j + k * blockDim.x.  All threads of the block must call it.
 template <typename F>
-__device__ void for_each_raw(const TokAdvArgs& a, int64_t i, AdvShared& sh, F&& f) {
-#pragma clang fp contract(off)
+__device__ void for_each_baseline(const TokAdvArgs& a, int64_t i, double c, F&& f) {
   const int tid = threadIdx.x;
   const int64_t T = a.T, base = i * a.T;
-  if (a.estimator == GRPO_ADV_REINFORCE_PP_BASELINE) {
-    const double c = sh.cval;
-    constexpr int U = 8;
-    for (int64_t t0 = tid; t0 < T; t0 += int64_t(U) * kAdvThreads) {
-      bool act[U];
+  constexpr int U = 8;
+  for (int64_t t0 = tid; t0 < T; t0 += int64_t(U) * kAdvThreads) {
+    bool act[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t t = t0 + int64_t(k) * kAdvThreads;
-        act[k] = t < T && adv_active(a, base + t);
-      }
+    for (int k = 0; k < U; ++k) {
+      const int64_t t = t0 + int64_t(k) * kAdvThreads;
+      act[k] = t < T && adv_active(a, base + t);
+    }
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t t = t0 + int64_t(k) * kAdvThreads;
-        if (t < T) f(t, act[k], act[k] ? c : 0.0);
-      }
-    }
-    return;
-  }
-  const double R = double(a.rewards[i]);
-  // the last active slot (it takes the terminal reward), found in the first
-  // tile from the right that has an active slot; the same in every thread
-  int64_t last = -1;
-  const bool shaped = a.kl_coef != 0.0;
-  constexpr int kPer = kAdvTile / kAdvThreads;
-  constexpr int NW = kAdvThreads / kWave;
-  const int lane = tid % kWave, wv = tid / kWave;
-  double tile_carry = 0.0;  // return at the slot after the current tile (same in every thread)
-  // a tile's inputs in registers: every load of the tile is issued before any
-  // is used (loading the next tile during this one's scan measured slower)
-  uint32_t mk = 0;  // bit k: slot tid + k NT of the tile is active
-  float ov[kPer], rv[kPer];
-  auto load_tile = [&](int64_t end) {
-    const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
-    const int n = int(end - start);
-    mk = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int q = tid + k * kAdvThreads;
-      ov[k] = rv[k] = 0.0f;
-      if (q < n) {
-        if (a.mask == nullptr || a.mask[base + start + q] != 0) mk |= 1u << k;
-        if (shaped) {
-          ov[k] = a.old[base + start + q];
-          rv[k] = a.ref[base + start + q];
-        }
-      }
-    }
-  };
-  if (T > 0) load_tile(T);
-  for (int64_t end = T; end > 0; end -= kAdvTile) {
-    const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
-    const int n = int(end - start);
-    if (end != T) {
-      load_tile(end);
-      __syncthreads();  // the previous tile's values are consumed
-    }
-    // token rewards m_t (-kl_coef (old - ref)) go to LDS as soon as they
-    // arrive (masked values are discarded by selection); the terminal reward
-    // is added at the last active slot once that is known, below
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int q = tid + k * kAdvThreads;
-      if (q >= n) continue;
-      double v = 0.0;
-      if (shaped && ((mk >> k) & 1u)) v = -a.kl_coef * (double(ov[k]) - double(rv[k]));
-      sh.v[adv_lds(q)] = v;
-    }
-    if (last < 0) {
-      int qm = -1;
-      if (mk != 0) qm = tid + (31 - __builtin_clz(mk)) * kAdvThreads;  // q < n wherever mk is set
-      qm = wave_max_i32(qm);
-      if (lane == 0) sh.wmax[wv] = qm;
-    }
-    __syncthreads();  // the tile's rewards and wmax are complete
-    if (last < 0) {
-      int m = -1;
-      for (int w = 0; w < NW; ++w) m = sh.wmax[w] > m ? sh.wmax[w] : m;
-      if (m >= 0) {
-        last = start + m;
-        // r_T = shaped + R at the last active slot: the thread that folds the
-        // slot's chunk adds it (nobody else touches that chunk before the
-        // next barrier)
-        if (m / kAdvChunk == tid) sh.v[adv_lds(m)] = sh.v[adv_lds(m)] + R;
-      }
-    }
-    // this thread's chunk as an affine map x -> h + g x of the return after it
-    const int q0 = tid * kAdvChunk < n ? tid * kAdvChunk : n;
-    const int q1 = q0 + kAdvChunk < n ? q0 + kAdvChunk : n;
-    double h = 0.0, g = 1.0;
-    for (int q = q1 - 1; q >= q0; --q) {
-      h = sh.v[adv_lds(q)] + a.gamma * h;
-      g = g * a.gamma;
-    }
-    // suffix scan of the maps (chunk j composed with chunks j+1 ...): in the
-    // wave, then across waves, in a fixed tree
-    double sh_ = h, sg = g;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const double oh = __shfl_down(sh_, off), og = __shfl_down(sg, off);
-      if (lane + off < kWave) {
-        sh_ = sh_ + sg * oh;
-        sg = sg * og;
-      }
-    }
-    if (lane == 0) {
-      sh.wh[wv] = sh_;
-      sh.wg[wv] = sg;
-    }
-    __syncthreads();
-    // the map of the waves after this one, applied to the tile's carry
-    double x = tile_carry;
-    for (int w = NW - 1; w > wv; --w) x = sh.wh[w] + sh.wg[w] * x;
-    // exclusive suffix in the wave: the next lane's inclusive map
-    double nh = __shfl_down(sh_, 1), ng = __shfl_down(sg, 1);
-    if (lane == kWave - 1) {
-      nh = 0.0;
-      ng = 1.0;
-    }
-    double acc = nh + ng * x;  // return at the slot after this chunk
-    // the carry into the next tile: the whole tile's map applied to tile_carry
-    double tc = tile_carry;
-    for (int w = NW - 1; w >= 0; --w) tc = sh.wh[w] + sh.wg[w] * tc;
-    tile_carry = tc;
-    for (int q = q1 - 1; q >= q0; --q) {
-      acc = sh.v[adv_lds(q)] + a.gamma * acc;
-      sh.v[adv_lds(q)] = acc;
-    }
-    __syncthreads();
-    // the mask comes from the registers: thread tid loaded slots tid + k NT
-#pragma unroll 2
-    for (int k = 0; k < kPer; ++k) {
-      const int q = tid + k * kAdvThreads;
-      if (q < n) {
-        const bool act = (mk >> k) & 1u;
-        f(start + q, act, act ? sh.v[adv_lds(q)] : 0.0);
-      }
+    for (int k = 0; k < U; ++k) {
+      const int64_t t = t0 + int64_t(k) * kAdvThreads;
+      if (t < T) f(t, act[k], act[k] ? c : 0.0);
     }
   }
 }
@@ -249,101 +122,364 @@ __device__ __forceinline__ void block_sum2_f64(double& x, double& y, double* sh)
   y = ty;
 }
 
-// One block per sequence: the raw advantages.  Without normalization they are
-// the output; with it, REINFORCE++'s returns go to the workspace and every
-// sequence leaves the moments of its active slots' values (the baseline's
-// value is the same at every active slot: L_i copies of R_i - group mean).
+// A thread's moments from sums of the deviations from its first value (no
+// division per value, and no cancellation unless that value is an outlier
+// many spreads away), then the block's in two fixed-order sums: count and
+// n mean give the mean, then M2 = sum (M2_t + n_t (mean_t - mean)^2).  (A
+// tree of Chan et al.'s pairwise merges, a division each, measured 1.7 us
+// more per call at 1024 x 4096 and gave the same outputs.)  Sequence i's
+// moments go to L, mean and M2.
+struct MomentSums {
+  double c = 0.0, s1 = 0.0, s2 = 0.0, n = 0.0;
+  __device__ __forceinline__ void add(double v) {
+#pragma clang fp contract(off)
+    if (n == 0.0) c = v;
+    const double d = v - c;
+    s1 = s1 + d;
+    s2 = s2 + d * d;
+    n = n + 1.0;
+  }
+};
+
+__device__ void store_sequence_moments(const TokAdvArgs& a, int64_t i, const MomentSums& ms,
+                                       double* sh_mom) {
+#pragma clang fp contract(off)
+  Moments mo{0.0, 0.0, 0.0};
+  if (ms.n > 0.0) {
+    const double dm = ms.s1 / ms.n;
+    const double m2 = ms.s2 - ms.s1 * dm;
+    mo = Moments{ms.n, ms.c + dm, m2 > 0.0 ? m2 : 0.0};
+  }
+  double sx = mo.n * mo.m, sn = mo.n;
+  block_sum2_f64<kAdvThreads>(sx, sn, sh_mom);
+  const double mean = sn > 0.0 ? sx / sn : 0.0;
+  const double d = mo.m - mean;
+  double q = mo.n > 0.0 ? mo.M2 + mo.n * (d * d) : 0.0, unused = 0.0;
+  block_sum2_f64<kAdvThreads>(q, unused, sh_mom);
+  if (threadIdx.x == 0) {
+    a.L[i] = int32_t(sn);
+    a.mean[i] = mean;
+    a.M2[i] = q;
+  }
+}
+
+// REINFORCE++-baseline, one block per sequence: C_i = R_i - (group mean, i
+// included).  Without normalization the output is written here; with it,
+// the sequence leaves L_i (its active slots), mean C_i and M2 = 0 (L_i
+// copies of one value) for the output pass.
 __global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_kernel(TokAdvArgs a) {
 #pragma clang fp contract(off)
   __shared__ AdvShared sh;
-  __shared__ double sh_mom[3 * (kAdvThreads / kWave)];
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
   if (i == 0 && tid == 0) a.hdr->status = 0;
 
-  if (a.estimator != GRPO_ADV_REINFORCE_PP) {
-    // group mean (the sample itself included), summed in index order by one
-    // thread from rewards the whole block stages in LDS (rounds of kAdvTile)
-    GroupSpec g{};
-    g.spp = a.spp;
-    g.num_groups = a.num_groups;
-    g.offsets = a.offsets;
-    int64_t s, e;
-    group_bounds(g, i, &s, &e);
-    float* stage = reinterpret_cast<float*>(sh.v);
-    double total = 0.0;
-    for (int64_t b = s; b < e; b += kAdvTile) {
-      const int64_t m = (e - b) < kAdvTile ? (e - b) : kAdvTile;
-      __syncthreads();
-      for (int64_t k = tid; k < m; k += kAdvThreads) stage[k] = a.rewards[b + k];
-      __syncthreads();
-      if (tid == 0)
-        for (int64_t k = 0; k < m; ++k) total = total + double(stage[k]);
-    }
-    if (tid == 0) sh.cval = double(a.rewards[i]) - total / double(e - s);
+  // group mean (the sample itself included), summed in index order by one
+  // thread from rewards the whole block stages in LDS (rounds of kAdvTile)
+  GroupSpec g{};
+  g.spp = a.spp;
+  g.num_groups = a.num_groups;
+  g.offsets = a.offsets;
+  int64_t s, e;
+  group_bounds(g, i, &s, &e);
+  float* stage = reinterpret_cast<float*>(sh.v);
+  double total = 0.0;
+  for (int64_t b = s; b < e; b += kAdvTile) {
+    const int64_t m = (e - b) < kAdvTile ? (e - b) : kAdvTile;
+    __syncthreads();
+    for (int64_t k = tid; k < m; k += kAdvThreads) stage[k] = a.rewards[b + k];
+    __syncthreads();
+    if (tid == 0)
+      for (int64_t k = 0; k < m; ++k) total = total + double(stage[k]);
   }
+  if (tid == 0) sh.cval = double(a.rewards[i]) - total / double(e - s);
   __syncthreads();
+  const double c = sh.cval;
 
   if (!a.normalize) {
-    for_each_raw(a, i, sh, [&](int64_t t, bool, double v) { a.out[base + t] = float(clamp_adv(a, v)); });
+    for_each_baseline(a, i, c, [&](int64_t t, bool, double v) { a.out[base + t] = float(clamp_adv(a, v)); });
     if (i == 0 && tid == 0 && a.status) *a.status = 0u;
     return;
   }
-  if (a.estimator == GRPO_ADV_REINFORCE_PP) {
-    // per thread, sums of the deviations from its first value (no division
-    // per value, and no cancellation unless that value is an outlier many
-    // spreads away); the threads' moments then merge in a fixed tree
-    double c = 0.0, s1 = 0.0, s2 = 0.0, n = 0.0;
-    for_each_raw(a, i, sh, [&](int64_t t, bool act, double v) {
-      if (!act) return;
-      a.V[base + t] = v;
-      if (n == 0.0) c = v;
-      const double d = v - c;
-      s1 = s1 + d;
-      s2 = s2 + d * d;
-      n = n + 1.0;
-    });
-    Moments mo{0.0, 0.0, 0.0};
-    if (n > 0.0) {
-      const double dm = s1 / n;
-      const double m2 = s2 - s1 * dm;
-      mo = Moments{n, c + dm, m2 > 0.0 ? m2 : 0.0};
-    }
-    {
-      // the threads' moments in two block sums: count and n mean give the
-      // mean, then M2 = sum (M2_t + n_t (mean_t - mean)^2) (a tree of Chan
-      // et al.'s pairwise merges, a division each, measured 1.7 us more per
-      // call at 1024 x 4096 and gave the same outputs)
-      double sx = mo.n * mo.m, sn = mo.n;
-      block_sum2_f64<kAdvThreads>(sx, sn, sh_mom);
-      const double mean = sn > 0.0 ? sx / sn : 0.0;
-      const double d = mo.m - mean;
-      double q = mo.n > 0.0 ? mo.M2 + mo.n * (d * d) : 0.0, unused = 0.0;
-      block_sum2_f64<kAdvThreads>(q, unused, sh_mom);
-      mo = Moments{sn, mean, q};
-    }
-    if (tid == 0) {
-      a.L[i] = int32_t(mo.n);
-      a.mean[i] = mo.m;
-      a.M2[i] = mo.M2;
-    }
+  long long cnt = 0;
+  if (a.mask == nullptr) {
+    cnt = tid == 0 ? a.T : 0;
+  } else if (a.T % 4 == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
+    const uint32_t* w4 = reinterpret_cast<const uint32_t*>(a.mask + base);
+    for (int64_t k = tid; k < a.T / 4; k += kAdvThreads) cnt += nonzero_bytes(w4[k]);
   } else {
-    long long cnt = 0;
-    if (a.mask == nullptr) {
-      cnt = tid == 0 ? a.T : 0;
-    } else if (a.T % 4 == 0 && (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0) {
-      const uint32_t* w4 = reinterpret_cast<const uint32_t*>(a.mask + base);
-      for (int64_t k = tid; k < a.T / 4; k += kAdvThreads) cnt += nonzero_bytes(w4[k]);
+    for (int64_t t = tid; t < a.T; t += kAdvThreads) cnt += a.mask[base + t] != 0 ? 1 : 0;
+  }
+  cnt = block_sum_i64<kAdvThreads>(cnt, sh.red_i);
+  if (tid == 0) {
+    a.L[i] = int32_t(cnt);
+    a.mean[i] = c;
+    a.M2[i] = 0.0;
+  }
+}
+
+// --- REINFORCE++ returns -----------------------------------------------------
+// A chunk's returns depend on the return after it through an affine map
+// x -> h + g x (h: the chunk's discounted rewards, g: gamma to the chunk's
+// length); the map of a run of chunks is the composition
+// (h, g) o (h', g') = (h + g h', g g'), the left map belonging to the chunk
+// further left.
+
+// A binary64 value moved between lanes by a DPP lane pattern (both halves);
+// lanes whose source lies outside the pattern, or whose row the row mask
+// leaves out, take `old`.  Every lane of the wave must be active.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_f64(double x, double old) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(x), CTRL, ROWMASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(x), CTRL, ROWMASK, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// One step of the inclusive lane-order scan of chunk maps: this lane's map is
+// composed with the one the pattern selects from a lower lane (a chunk
+// further right).  Unselected lanes compose with (-0, 1), which is exact:
+// h + g (-0) = h for every g >= 0, and g 1 = g.
+template <int CTRL, int ROWMASK, bool kG1>
+__device__ __forceinline__ void map_scan_step(double& h, double& g) {
+#pragma clang fp contract(off)
+  const double oh = dpp_f64<CTRL, ROWMASK>(h, -0.0);
+  if constexpr (kG1) {
+    h = h + oh;  // g = 1 throughout: the same bits as h + 1 oh
+  } else {
+    const double og = dpp_f64<CTRL, ROWMASK>(g, 1.0);
+    h = h + g * oh;
+    g = g * og;
+  }
+}
+
+// Inclusive scan over the wave's lanes, lane 0 first: row shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then row 0's last lane into row 1 and
+// row 2's into row 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31).  Lane l ends with the composition of lanes l, l-1, ..., 0.
+template <bool kG1>
+__device__ __forceinline__ void wave_map_scan(double& h, double& g) {
+  map_scan_step<0x111, 0xF, kG1>(h, g);
+  map_scan_step<0x112, 0xF, kG1>(h, g);
+  map_scan_step<0x114, 0xF, kG1>(h, g);
+  map_scan_step<0x118, 0xF, kG1>(h, g);
+  map_scan_step<0x142, 0xA, kG1>(h, g);
+  map_scan_step<0x143, 0xC, kG1>(h, g);
+}
+
+typedef double d2 __attribute__((ext_vector_type(2)));
+
+// REINFORCE++, one block per sequence: tiles of kAdvTile slots from the right
+// end.  A tile's token rewards m_t (-kl_coef (old - ref)) go to LDS (the
+// terminal reward is added at the last active slot, found in the first tile
+// from the right that has one, so the mask is read once); thread j folds
+// chunk own(j) = 64 w + 63 - l (w its wave, l its lane) of kAdvChunk
+// consecutive slots into its map.  Chunks run right to left across a wave's
+// lanes, so the suffix scan over chunks is a prefix scan over lanes (DPP row
+// shifts and row broadcasts, no LDS traffic); the waves' maps then compose
+// in wave order, every chunk replays its slots from its carry, and the
+// returns leave LDS.  kVec: T % 4 == 0 and 16-byte aligned rows, so each
+// thread loads and stores quads of four consecutive slots (tile slots
+// 4 (j + 256 u) + c, u = 0, 1); otherwise single slots j + 256 k.  kG1:
+// gamma = 1, where every slope is exactly 1 and is not carried (the same
+// bits as the general maps).  Without normalization the advantages are
+// written here; with it, the returns of active slots go to V and the
+// sequence leaves the moments of its active returns.
+template <bool kVec, bool kG1>
+__global__ __launch_bounds__(kAdvThreads) void grpo_tokadv_returns_kernel(TokAdvArgs a) {
+#pragma clang fp contract(off)
+  __shared__ AdvShared sh;
+  __shared__ double sh_mom[2 * (kAdvThreads / kWave)];
+  constexpr int NW = kAdvThreads / kWave;
+  constexpr int kBits = kAdvTile / kAdvThreads;  // slots per thread per tile
+  static_assert(kBits == 8 && kAdvChunk == 8, "two quads or eight slots per thread");
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int64_t T = a.T, base = i * T;
+  if (i == 0 && tid == 0) a.hdr->status = 0;
+  const double R = double(a.rewards[i]);
+  const bool shaped = a.kl_coef != 0.0;
+  const double gam = kG1 ? 1.0 : a.gamma;
+  const int own = wv * kWave + (kWave - 1 - lane);
+  // slope of a full chunk: kAdvChunk factors of gamma in the partial fold's order
+  double g_full = 1.0;
+  if constexpr (!kG1)
+    for (int j = 0; j < kAdvChunk; ++j) g_full = g_full * gam;
+  // tile slot of bit b of this thread's mask word (increasing in b)
+  auto slot = [&](int b) -> int {
+    return kVec ? 4 * (tid + kAdvThreads * (b >> 2)) + (b & 3) : tid + kAdvThreads * b;
+  };
+  int64_t last = -1;
+  double tile_carry = 0.0;  // return at the slot after the current tile (same in every thread)
+  MomentSums ms;
+  for (int64_t end = T; end > 0; end -= kAdvTile) {
+    const int64_t start = end > kAdvTile ? end - kAdvTile : 0;
+    const int n = int(end - start);  // a multiple of 4 when kVec
+    const int64_t row0 = base + start;
+    // the tile's mask bits and log-probs: every load issued before any is used
+    uint32_t mk = 0;  // bit b: slot(b) is active
+    float ov[kBits], rv[kBits];
+    if constexpr (kVec) {
+      uint32_t m4[2];
+      f32x4 o4[2], r4[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = slot(4 * u);
+        m4[u] = 0u;
+        o4[u] = r4[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (q < n) {
+          m4[u] = a.mask ? *reinterpret_cast<const uint32_t*>(a.mask + row0 + q) : 0x01010101u;
+          if (shaped) {
+            o4[u] = *reinterpret_cast<const f32x4*>(a.old + row0 + q);
+            r4[u] = *reinterpret_cast<const f32x4*>(a.ref + row0 + q);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((m4[u] >> (8 * c)) & 0xffu) mk |= 1u << (4 * u + c);
+          ov[4 * u + c] = o4[u][c];
+          rv[4 * u + c] = r4[u][c];
+        }
     } else {
-      for (int64_t t = tid; t < a.T; t += kAdvThreads) cnt += a.mask[base + t] != 0 ? 1 : 0;
+#pragma unroll
+      for (int b = 0; b < kBits; ++b) {
+        const int q = slot(b);
+        ov[b] = rv[b] = 0.0f;
+        if (q < n) {
+          if (a.mask == nullptr || a.mask[row0 + q] != 0) mk |= 1u << b;
+          if (shaped) {
+            ov[b] = a.old[row0 + q];
+            rv[b] = a.ref[row0 + q];
+          }
+        }
+      }
     }
-    cnt = block_sum_i64<kAdvThreads>(cnt, sh.red_i);
-    if (tid == 0) {
-      a.L[i] = int32_t(cnt);
-      a.mean[i] = sh.cval;
-      a.M2[i] = 0.0;
+    if (end != T) __syncthreads();  // the previous tile's returns are consumed
+    // token rewards to LDS (masked slots hold 0)
+#pragma unroll
+    for (int b = 0; b < kBits; ++b) {
+      const int q = slot(b);
+      if (q >= n) continue;
+      double v = 0.0;
+      if (shaped && ((mk >> b) & 1u)) v = -a.kl_coef * (double(ov[b]) - double(rv[b]));
+      sh.v[adv_lds(q)] = v;
     }
+    if (last < 0) {
+      int qm = mk != 0 ? slot(31 - __builtin_clz(mk)) : -1;
+      qm = wave_max_i32(qm);
+      if (lane == 0) sh.wmax[wv] = qm;
+    }
+    __syncthreads();  // the tile's rewards and wmax are complete
+    if (last < 0) {
+      int m = -1;
+      for (int w = 0; w < NW; ++w) m = sh.wmax[w] > m ? sh.wmax[w] : m;
+      if (m >= 0) {
+        last = start + m;
+        // r_T = shaped + R at the last active slot, added by the thread whose
+        // chunk holds it (nobody else touches that chunk before the next barrier)
+        if (m / kAdvChunk == own) sh.v[adv_lds(m)] = sh.v[adv_lds(m)] + R;
+      }
+    }
+    // this thread's chunk as a map
+    const int q0 = own * kAdvChunk;
+    const bool full = q0 + kAdvChunk <= n;
+    const int q1 = full ? q0 + kAdvChunk : (q0 < n ? n : q0);
+    double cv[kAdvChunk];
+    double h = 0.0, g = 1.0;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < kAdvChunk; ++j) cv[j] = sh.v[own * kAdvPad + j];
+#pragma unroll
+      for (int j = kAdvChunk - 1; j >= 0; --j) h = cv[j] + gam * h;
+      g = g_full;
+    } else {
+      for (int q = q1 - 1; q >= q0; --q) {
+        h = sh.v[adv_lds(q)] + gam * h;
+        if constexpr (!kG1) g = g * gam;
+      }
+    }
+    double ih = h, ig = g;
+    wave_map_scan<kG1>(ih, ig);
+    if (lane == kWave - 1) {
+      sh.wh[wv] = ih;
+      sh.wg[wv] = ig;
+    }
+    // the previous lane's inclusive map (lane 0: the identity) is the map
+    // from the return after the wave to the return after this chunk
+    const double eh = dpp_f64<0x138, 0xF>(ih, -0.0);  // wave_shr:1
+    const double eg = kG1 ? 1.0 : dpp_f64<0x138, 0xF>(ig, 1.0);
+    __syncthreads();
+    // the return after this wave: the later waves' maps applied to the tile's carry
+    double x = tile_carry;
+    for (int w = NW - 1; w > wv; --w) x = sh.wh[w] + sh.wg[w] * x;
+    double acc = eh + eg * x;  // return after this chunk
+    double tc = tile_carry;
+    for (int w = NW - 1; w >= 0; --w) tc = sh.wh[w] + sh.wg[w] * tc;
+    tile_carry = tc;
+    if (full) {
+#pragma unroll
+      for (int j = kAdvChunk - 1; j >= 0; --j) {
+        acc = cv[j] + gam * acc;
+        cv[j] = acc;
+      }
+#pragma unroll
+      for (int j = 0; j < kAdvChunk; ++j) sh.v[own * kAdvPad + j] = cv[j];
+    } else {
+      for (int q = q1 - 1; q >= q0; --q) {
+        acc = sh.v[adv_lds(q)] + gam * acc;
+        sh.v[adv_lds(q)] = acc;
+      }
+    }
+    __syncthreads();  // the tile's returns are in LDS
+    if constexpr (kVec) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = slot(4 * u);
+        if (q >= n) continue;
+        const uint32_t bits = (mk >> (4 * u)) & 0xFu;
+        const int r = adv_lds(q);  // the quad's four returns are consecutive in LDS
+        const double v[4] = {sh.v[r], sh.v[r + 1], sh.v[r + 2], sh.v[r + 3]};
+        if (a.normalize) {
+          if (bits != 0u) {
+            d2* dst = reinterpret_cast<d2*>(a.V + row0 + q);
+            dst[0] = d2{v[0], v[1]};
+            dst[1] = d2{v[2], v[3]};
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if ((bits >> c) & 1u) ms.add(v[c]);
+        } else {
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[c] = ((bits >> c) & 1u) ? float(clamp_adv(a, v[c])) : 0.0f;
+          *reinterpret_cast<f32x4*>(a.out + row0 + q) = f32x4{o[0], o[1], o[2], o[3]};
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int b = 0; b < kBits; ++b) {
+        const int q = slot(b);
+        if (q >= n) continue;
+        const bool act = (mk >> b) & 1u;
+        const double v = sh.v[adv_lds(q)];
+        if (a.normalize) {
+          if (act) {
+            a.V[row0 + q] = v;
+            ms.add(v);
+          }
+        } else {
+          a.out[row0 + q] = act ? float(clamp_adv(a, v)) : 0.0f;
+        }
+      }
+    }
+  }
+  if (a.normalize) {
+    store_sequence_moments(a, i, ms, sh_mom);
+  } else if (i == 0 && tid == 0 && a.status) {
+    *a.status = 0u;
   }
 }
 
@@ -548,7 +684,20 @@ __global__ __launch_bounds__(kNormThreads) void grpo_tokadv_norm_kernel(TokAdvAr
 }
 
 hipError_t launch_token_advantages(const TokAdvArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(grpo_tokadv_kernel, dim3(unsigned(a.B)), dim3(kAdvThreads), 0, s, a);
+  if (a.estimator == GRPO_ADV_REINFORCE_PP) {
+    auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
+    const bool shaped = a.kl_coef != 0.0;
+    const bool vec = a.T % 4 == 0 && al(a.mask, 3) && (!shaped || (al(a.old, 15) && al(a.ref, 15))) &&
+                     (a.normalize ? al(a.V, 15) : al(a.out, 15));
+    const bool g1 = a.gamma == 1.0;
+    const dim3 grid(unsigned(a.B)), block(kAdvThreads);
+    if (vec && g1) hipLaunchKernelGGL((grpo_tokadv_returns_kernel<true, true>), grid, block, 0, s, a);
+    else if (vec) hipLaunchKernelGGL((grpo_tokadv_returns_kernel<true, false>), grid, block, 0, s, a);
+    else if (g1) hipLaunchKernelGGL((grpo_tokadv_returns_kernel<false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((grpo_tokadv_returns_kernel<false, false>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL(grpo_tokadv_kernel, dim3(unsigned(a.B)), dim3(kAdvThreads), 0, s, a);
+  }
   if (!a.normalize) return hipGetLastError();
   const bool fused = a.B <= kFusedMomentsMaxB;
   if (!fused) hipLaunchKernelGGL(grpo_tokadv_moments_kernel, dim3(1), dim3(kMomentThreads), 0, s, a);
