@@ -51,11 +51,21 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "tokens/s for fused GRPO fwd+bwd from [B,T,V] logits; % of MI355X peak HBM GB/s"
-KERNEL_SOURCES = ["rl_post_loss_amd/csrc/grpo_rows.hip", "rl_post_loss_amd/csrc/grpo_rows_resident.hip",
-                  "rl_post_loss_amd/csrc/grpo_rowcore.hpp", "rl_post_loss_amd/csrc/grpo_device.hpp",
-                  "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_objective.hpp",
-                  "rl_post_loss_amd/csrc/grpo_reduce.hip", "rl_post_loss_amd/csrc/grpo_adv.hip",
-                  "rl_post_loss_amd/csrc/grpo_api.hip"]
+# The sources each kernel family is built from (its own files and the shared
+# headers, the C ABI and its launch code): a profile summary records their
+# hash, and its HBM traffic is reported only while that hash still matches.
+_SHARED_SOURCES = ["include/grpo.h", "rl_post_loss_amd/csrc/grpo_device.hpp",
+                   "rl_post_loss_amd/csrc/grpo_internal.hpp", "rl_post_loss_amd/csrc/grpo_api.hip"]
+_LOGITS_SOURCES = ["rl_post_loss_amd/csrc/grpo_rows.hip", "rl_post_loss_amd/csrc/grpo_rows_resident.hip",
+                   "rl_post_loss_amd/csrc/grpo_rowcore.hpp", "rl_post_loss_amd/csrc/grpo_objective.hpp",
+                   "rl_post_loss_amd/csrc/grpo_seq.hip"]
+_TOKEN_SOURCES = ["rl_post_loss_amd/csrc/grpo_reduce.hip", "rl_post_loss_amd/csrc/grpo_objective.hpp",
+                  "rl_post_loss_amd/csrc/grpo_groupadv.hpp", "rl_post_loss_amd/csrc/grpo_prep.hip"]
+_ESTIMATOR_SOURCES = ["rl_post_loss_amd/csrc/grpo_adv.hip", "rl_post_loss_amd/csrc/grpo_groupadv.hpp"]
+FAMILY_SOURCES = {"grpo_rows_kernel": _LOGITS_SOURCES, "grpo_rows_resident_kernel": _LOGITS_SOURCES,
+                  "grpo_seq_path": _LOGITS_SOURCES, "grpo_token_kernel": _TOKEN_SOURCES,
+                  "grpo_tokadv_kernels": _ESTIMATOR_SOURCES}
+KERNEL_SOURCES = sorted(set(_SHARED_SOURCES + _LOGITS_SOURCES + _TOKEN_SOURCES + _ESTIMATOR_SOURCES))
 CALIB_BYTES = 1 << 31   # 2 GiB copy for counter calibration
 MAX_WORKERS = 16        # host processes for the oracle (the machine's CPU share per GPU)
 
@@ -69,9 +79,12 @@ OBJECTIVES = {
 }
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel=None):
+    """Hash of the sources ``kernel``'s family is built from (every kernel
+    source when ``kernel`` is None or not a known family)."""
+    rels = _SHARED_SOURCES + FAMILY_SOURCES[kernel] if kernel in FAMILY_SOURCES else KERNEL_SOURCES
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in rels:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -374,7 +387,7 @@ def load_traffic(kernel, workload):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -1050,7 +1063,7 @@ def summarize_pmc(dirs, workload, kernel, out_dir, skip_first=1, regex=None):
         f"{fetch_dir} {write_dir} {cal_fetch_dir} {cal_write_dir}"]
     summary = dict(kernel=kernel, members=[m for m in _family(kernel) if _matching(by_name, m)],
                    workload=workload,
-                   kernel_source_hash=kernel_source_hash(), counters=res, per_kernel=per_kernel,
+                   kernel_source_hash=kernel_source_hash(kernel), counters=res, per_kernel=per_kernel,
                    traffic_bytes_per_launch=traffic, warmup_dispatches_skipped=skip_first,
                    commands=cmds)
     os.makedirs(out_dir, exist_ok=True)
@@ -1099,7 +1112,7 @@ def summarize_counters(run_dirs, workload, name, out_dir, commands, skip_first=1
     if not per:
         raise SystemExit("no libgrpo counter rows")
     lines = [f"# {name} on {workload}: wave and instruction counters", "",
-             f"Kernel sources hash {kernel_source_hash()}.  Medians per dispatch over every "
+             f"Kernel sources hash {kernel_source_hash(name)}.  Medians per dispatch over every "
              f"dispatch but the first {skip_first} (warm-up); each counter set in a run of its own.",
              "", "Commands (repository root, one MI355X):", ""] + ["    " + c for c in commands]
     for k in sorted(per):
@@ -1137,7 +1150,7 @@ def summarize_trace(run_dir, workload, kernel, out_dir, command, skip_first):
     if not per:
         raise SystemExit(f"no libgrpo dispatches under {run_dir}")
     lines = [f"# {kernel} on {workload}: kernel trace", "",
-             f"Kernel sources hash {kernel_source_hash()}.  Durations in microseconds from the "
+             f"Kernel sources hash {kernel_source_hash(kernel)}.  Durations in microseconds from the "
              f"trace's start and end timestamps; the first {skip_first} dispatches of each kernel "
              "(warm-up) are left out of the average, median, minimum and maximum.", "",
              "Command (repository root, one MI355X):", "", "    " + command, "",

@@ -81,7 +81,7 @@ def test_summarize_pmc_scales_by_the_calibration_kernel(tmp_path):
     assert per["counter_per_dispatch"] == [1.0, 30.0, 60.0]
     assert per["dispatches_averaged"] == 2
     assert abs(d["traffic_bytes_per_launch"] - (fetch + write)) <= 1e-9 * (fetch + write)
-    assert d["kernel_source_hash"] == bench.kernel_source_hash()
+    assert d["kernel_source_hash"] == bench.kernel_source_hash("grpo_rows_kernel")
     assert (out / "grpo_rows_kernel_wl_pmc.md").read_text().count("| FETCH_SIZE |") == 1
 
 
@@ -138,7 +138,7 @@ def test_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
     prof.mkdir()
     path = prof / "grpo_token_kernel_wl_pmc.json"
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel=None: "abc")
     assert bench.load_traffic("grpo_token_kernel", "wl") is None
     path.write_text(json.dumps(dict(kernel_source_hash="abc", traffic_bytes_per_launch=123.0)))
     assert bench.load_traffic("grpo_token_kernel", "wl") == 123.0
@@ -177,3 +177,26 @@ def test_profiler_guard(monkeypatch):
     assert not bench.under_profiler()
     monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/librocprofiler-sdk-tool.so")
     assert bench.under_profiler()
+
+
+def test_source_hash_follows_the_family(tmp_path, monkeypatch):
+    """An edit to the estimator's source leaves the logits kernels' profiles
+    current and makes the estimator's stale; an edit to a shared header makes
+    every family's stale."""
+    import shutil
+    for rel in bench.KERNEL_SOURCES:
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    fams = ("grpo_rows_kernel", "grpo_token_kernel", "grpo_tokadv_kernels")
+    before = {k: bench.kernel_source_hash(k) for k in fams}
+    with open(tmp_path / "rl_post_loss_amd/csrc/grpo_adv.hip", "a") as f:
+        f.write("\n// edited\n")
+    after = {k: bench.kernel_source_hash(k) for k in fams}
+    assert after["grpo_rows_kernel"] == before["grpo_rows_kernel"]
+    assert after["grpo_token_kernel"] == before["grpo_token_kernel"]
+    assert after["grpo_tokadv_kernels"] != before["grpo_tokadv_kernels"]
+    with open(tmp_path / "rl_post_loss_amd/csrc/grpo_device.hpp", "a") as f:
+        f.write("\n// edited\n")
+    assert all(bench.kernel_source_hash(k) != after[k] for k in fams)
