@@ -126,12 +126,13 @@ def test_token_advantages_empty_mask(gpu_lib):
     assert torch.all(A == 0) and int(st[0]) & rpl.GRPO_FAULT_NO_TOKENS
 
 
-def test_token_advantages_bitwise_repeat_and_masked_garbage(gpu_lib):
+@pytest.mark.parametrize("T", [777, 776])   # single slots, quads of four slots
+def test_token_advantages_bitwise_repeat_and_masked_garbage(gpu_lib, T):
     rpl = gpu_lib
-    B, T = 12, 777
+    B = 12
     mask, old, ref, R = _token_case(B, T, seed=3)
     d = dict(mask=mask.to(DEV), old=old.to(DEV), ref=ref.to(DEV), R=R.to(DEV))
-    announce("token advantages repeat / garbage")
+    announce(f"token advantages repeat / garbage T={T}")
     kw = dict(old_logps=d["old"], ref_logps=d["ref"], kl_coef=0.03, gamma=0.97)
     a = rpl.grpo_token_advantages("reinforce_pp", d["R"], d["mask"], **kw)
     b = rpl.grpo_token_advantages("reinforce_pp", d["R"], d["mask"], **kw)
@@ -143,6 +144,35 @@ def test_token_advantages_bitwise_repeat_and_masked_garbage(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+@pytest.mark.parametrize("normalize", [True, False])
+def test_token_advantages_unaligned_rows(gpu_lib, normalize):
+    """T % 4 == 0 but log-prob and mask rows that start off a 16-byte (and
+    4-byte) boundary: the returns kernel takes single slots instead of quads
+    and still matches the oracle."""
+    rpl = gpu_lib
+    B, T = 16, 4096
+    mask, old, ref, R = _token_case(B, T, seed=11)
+    announce(f"token advantages unaligned rows normalize={normalize}")
+
+    def shifted(x, k):
+        buf = torch.empty(x.numel() + k, dtype=x.dtype, device=DEV)
+        v = buf[k:].view(x.shape)
+        v.copy_(x.to(DEV))
+        return v
+
+    o, r, mk = shifted(old, 1), shifted(ref, 3), shifted(mask, 1)
+    assert o.data_ptr() % 16 and r.data_ptr() % 16 and mk.data_ptr() % 4
+    A = rpl.grpo_token_advantages("reinforce_pp", R.to(DEV), mk, old_logps=o, ref_logps=r,
+                                  kl_coef=0.02, gamma=1.0, normalize=normalize)
+    torch.cuda.synchronize()
+    want = oracle.token_advantages("reinforce_pp", R.numpy(), old.numpy(), ref.numpy(), mask.numpy(),
+                                   kl_coef=0.02, gamma=1.0, normalize=normalize)
+    got = A.cpu().numpy()
+    assert np.all(got[~mask.numpy()] == 0.0)
+    exact, n = _within_ulp(got, want, "token advantages, unaligned rows")
+    print(f"  bit-exact {exact}/{n}", flush=True)
 
 
 GDPO_CASES = [
