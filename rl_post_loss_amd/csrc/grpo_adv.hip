@@ -53,7 +53,6 @@ struct AdvShared {
   int wmax[kAdvThreads / kWave];    // per wave: its last active tile slot (-1: none)
   double wh[kAdvThreads / kWave];  // per wave: its chunks' composed map (h + g x)
   double wg[kAdvThreads / kWave];
-  double red[kAdvThreads / kWave];
   long long red_i[kAdvThreads / kWave];
   double cval;                // baseline difference of the sequence
 };
