@@ -467,10 +467,10 @@ def _row_kernel_name(wl, resident):
 
 def _resident(wl):
     """Whether the fused call takes the resident-row kernel: rows above 4 KB
-    and up to 264 KB, 16-byte aligned (the library's own choice, restated
+    and up to 128 KB, 16-byte aligned (the library's own choice, restated
     for labelling the record; the kernel trace names the kernel that ran)."""
     b = wl.V * (4 if wl.dtype == "f32" else 2)
-    return 4096 < b <= 270336 and b % 16 == 0
+    return 4096 < b <= 131072 and b % 16 == 0
 
 
 def run_logits_record(args, wl, inp, reduction, objective="default", pool=None, workers=1,

@@ -6,8 +6,8 @@
 // the registers instead of re-reading HBM.  Per active row that is
 // V * (2 b_x + b_g) bytes instead of V * (3 b_x + b_g).  A block of NT
 // threads owns one row; thread `lid` holds the 16-byte chunks
-// lid, lid + NT, ..., lid + (K-1) NT.  With NT = 1024 and K = 17 a block
-// holds up to 17 x 16 B x 1024 = 272 KB, enough for a 128,256-entry bf16 row.
+// lid, lid + NT, ..., lid + (K-1) NT.  With NT = 512 and K = 16 a block
+// holds up to 16 x 16 B x 512 = 128 KB, a 65,536-entry bf16 row.
 //
 // The x chunks are issued first, interleaved with the first UY reference
 // chunks; each reference slot is refilled as soon as it has been consumed,
@@ -217,24 +217,26 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
   }
 }
 
-// Launch shapes, measured on MI355X (V = 32,000 and 128,256 bf16): how many
-// rows are in flight per CU matters as much as how many waves.  Rows of up to
-// 1,024 chunks: 256-thread blocks.  Rows of up to 4,096 chunks (64 KB of
-// bf16): 512 threads x 8 chunks, held to two blocks per CU by a 64 KB LDS
-// reservation each (measured at 4,000 chunks: two rows in flight per CU beat
-// three or four by 3-4%;
-// one 1024-thread row per CU is a third slower, its serial epilogue idles
-// the CU).  Longer rows: 1024 threads x up to 17 chunks, one block per CU
-// (2% ahead of 768 x 22).  Rows of 8 chunks or more per thread stream the
-// reference row first, shorter ones walk both rows together.
+// Launch shapes, measured on MI355X (bf16 rows): how many rows are in flight
+// per CU matters as much as how many waves.  Rows of up to 1,024 chunks:
+// 256-thread blocks.  Rows of up to 4,096 chunks (64 KB of bf16): 512 threads
+// x 8 chunks, held to two blocks per CU by a 64 KB LDS reservation each
+// (measured at 4,000 chunks: two rows in flight per CU beat three or four by
+// 3-4%; one 1024-thread row per CU is a third slower, its serial epilogue
+// idles the CU).  Rows of up to 8,192 chunks (128 KB): 512 threads x 12 or 16
+// chunks, two blocks per CU by their registers.  Longer rows take the
+// streaming kernel: a 1024-thread resident block per CU leaves the policy
+// row's log-sum-exp and the gradient exponentials without memory traffic to
+// overlap (V = 100,000 and 128,256 with every row active: 13.6 and 15.7 ms
+// against 11.5 and 13.8 for the streaming kernel).  Rows of 8 chunks or more
+// per thread stream the reference row first, shorter ones walk both rows
+// together.
 constexpr unsigned kResCapLds = 65536;  // a third block would need more than the CU's 160 KB
 
 template <typename TI, typename TG, int NT, int K>
 static hipError_t launch_res(const RowArgs& a, unsigned lds, hipStream_t s) {
   constexpr bool kYFirst = K >= 8;
-  // reference chunks in flight per thread: 8 at 1024 threads (1% ahead of 4
-  // at V = 128,256), 4 below (8 measured no better at V = 32,000)
-  constexpr int kUY = NT >= 1024 ? 8 : 4;
+  constexpr int kUY = 4;  // reference chunks in flight per thread (8 measured no better at V = 32,000)
   hipLaunchKernelGGL((grpo_rows_resident_kernel<TI, TG, NT, K, kUY, kYFirst>), dim3(unsigned(a.rows)),
                      dim3(NT), lds, s, a);
   return hipGetLastError();
@@ -244,19 +246,16 @@ template <typename TI, typename TG>
 static hipError_t launch_res_types(const RowArgs& a, int64_t nvec, hipStream_t s) {
   if (nvec <= 256 * 4) return launch_res<TI, TG, 256, 4>(a, 0, s);
   if (nvec <= 512 * 8) return launch_res<TI, TG, 512, 8>(a, kResCapLds, s);
-  const int64_t k = (nvec + 1023) / 1024;
-  if (k <= 8) return launch_res<TI, TG, 1024, 8>(a, 0, s);
-  if (k <= 12) return launch_res<TI, TG, 1024, 12>(a, 0, s);
-  if (k <= 16) return launch_res<TI, TG, 1024, 16>(a, 0, s);
-  if (k <= 17) return launch_res<TI, TG, 1024, 17>(a, 0, s);
+  if (nvec <= 512 * 12) return launch_res<TI, TG, 512, 12>(a, 0, s);
+  if (nvec <= 512 * 16) return launch_res<TI, TG, 512, 16>(a, 0, s);
   return hipErrorInvalidValue;
 }
 
 // esize: bytes per logit (2 or 4); a 16-byte chunk holds 16 / esize logits.
-// Up to 16,896 chunks (264 KB; a 135,168-entry bf16 row) stay resident.
+// Up to 8,192 chunks (128 KB; a 65,536-entry bf16 row) stay resident.
 bool resident_fits(int64_t V, int esize) {
   const int64_t nvec = V / (16 / esize);
-  return nvec <= int64_t(16896);
+  return nvec <= int64_t(8192);
 }
 
 hipError_t launch_rows_resident(const RowArgs& a, const RowLaunch& l, hipStream_t s) {

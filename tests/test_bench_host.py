@@ -44,7 +44,8 @@ def test_byte_model():
     held = min(wl.V * 2 // 16, bench.HELD_CHUNKS) * 16
     assert bench.min_bytes(wl, rows, rows, False) == bench.byte_model(wl, rows, rows) - rows * held
     assert bench.min_bytes(tiny, 10, n, False) == bench.byte_model(tiny, 10, n)
-    assert bench._resident(v32) and bench._resident(WORKLOADS["logits_csr_v128256"])
+    assert bench._resident(v32)
+    assert not bench._resident(WORKLOADS["logits_csr_v128256"])
     assert not bench._resident(wl) and not bench._resident(tiny)
     # token loss: 17 B per active token, 5 B per masked one
     assert bench.token_bytes(4_194_304, 4_194_304) == 71_303_168

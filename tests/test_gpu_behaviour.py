@@ -82,7 +82,7 @@ def test_masked_nan_inf_garbage_ids_do_not_leak(gpu_lib):
 @pytest.mark.parametrize("V", [8192, 40000, 151936])
 def test_in_place_gradient_matches_out_of_place(gpu_lib, V):
     """The gradient written over the policy logits equals the out-of-place
-    one bit for bit: resident rows at 256 and 1024 threads, and streaming
+    one bit for bit: resident rows at 256 and 512 threads, and streaming
     rows whose first chunks pass 2 takes from LDS rather than from the
     (by then partly overwritten) logits."""
     wl = _wl(V, "bf16", T=8 if V < 100000 else 4)

@@ -104,13 +104,13 @@ def test_vocab_sizes_and_paths(gpu_lib, V, dtype):
 @pytest.mark.parametrize("V,dtype", [
     (2048, "bf16"), (2056, "bf16"),        # 4 KB rows: wave per row, then a resident block
     (8192, "bf16"), (8200, "bf16"),        # 16 KB: resident at 256 threads (4 chunks), then 512
-    (32768, "bf16"), (32776, "bf16"),      # 64 KB: 512 threads (8 chunks), then 1024
-    (65536, "bf16"), (65544, "bf16"),      # 1024 threads: 8 chunks, then 12
-    (131072, "bf16"), (131080, "bf16"),    # 1024 threads: 16 chunks, then 17
-    (135168, "bf16"), (135176, "bf16"),    # 264 KB: the largest resident row, then streaming
+    (32768, "bf16"), (32776, "bf16"),      # 64 KB: 512 threads x 8 chunks, then 12
+    (49152, "bf16"), (49160, "bf16"),      # 96 KB: 512 threads x 12 chunks, then 16
+    (65536, "bf16"), (65544, "bf16"),      # 128 KB: the largest resident row, then streaming
     (4096, "f32"), (4100, "f32"),          # the same limits for float32 rows
     (16384, "f32"), (16388, "f32"),
-    (67584, "f32"), (67588, "f32"),
+    (24576, "f32"), (24580, "f32"),
+    (32768, "f32"), (32772, "f32"),
 ])
 def test_kernel_variant_boundaries(gpu_lib, V, dtype):
     """Row sizes exactly at each kernel variant's limit and one chunk past
