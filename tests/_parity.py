@@ -250,6 +250,36 @@ def compare_token_values(res, ref, cfg, mask, rtol, e_logp=LOGP_ABS_ERR, e_d=2 *
                                f"{np.argwhere(bad)[0]}: gpu={g[bad][0]!r} oracle={r[bad][0]!r}")
 
 
+def compare_token_grad(g, ref, cfg, mask, bar=1e-5, what=""):
+    """d loss / d logp of the log-prob token path against the oracle at
+    bar * max|G|.  The inputs are float32 log-probs, so the one place where
+    two results are correct is a token whose float32 ratio sits at a clip
+    bound (within 4e-7 relative): there the value must match the oracle's G
+    or the other branch's (clipped: the KL part alone; unclipped: -A rho
+    plus it), never be skipped.  Masked tokens must be exactly 0.  Returns
+    (ambiguous tokens, how many took the other branch)."""
+    g = np.asarray(g, dtype=np.float64)
+    G = ref.grad
+    lim = bar * float(np.max(np.abs(G)))
+    rho = ref.tok["rho"]
+    lo, hi = 1.0 - cfg.eps_low, 1.0 + cfg.eps_high
+    amb = ((np.abs(rho - hi) <= 4e-7 * rho) | (np.abs(rho - lo) <= 4e-7 * rho)) & mask
+    t = _terms_at(ref, cfg)
+    adv = ref.tok["adv"] if "adv" in ref.tok else ref.advantages[:, None]
+    other = np.where(t["clipped"], -adv * t["rho"], 0.0)
+    G_other = ref.seq_weight[:, None] * (other + cfg.beta * t["dkl"])
+    near = np.abs(g - G) <= lim
+    near_other = amb & (np.abs(g - G_other) <= lim)
+    bad = mask & ~(near | near_other)
+    assert not bad.any(), (f"{what} {int(bad.sum())} dlogp values out of tolerance (bar {bar:g} "
+                           f"x max|G| = {lim:.3g})")
+    assert np.all(g[~mask] == 0.0), what
+    n_amb, n_other = int(amb.sum()), int((near_other & ~near).sum())
+    print(f"  [{what}] dlogp: {n_amb} tokens at a clip bound, {n_other} took the other branch",
+          flush=True)
+    return n_amb, n_other
+
+
 def compare_exact_parts(res, ref, what=""):
     assert_bits_equal(to_np(res.advantages), ref.advantages, what + " advantages")
     assert_bits_equal(to_np(res.seq_weight), ref.seq_weight, what + " seq_weight")

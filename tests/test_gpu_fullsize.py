@@ -22,7 +22,8 @@ import torch
 import oracle
 from _fullsize import masked_rows_zero, stream_oracle
 from _parity import (LOGP_ABS_ERR, assert_grad_rows_sum_to_zero, branch_ambiguity, cfg_from,
-                     compare_exact_parts, compare_scalars, compare_token_values, gpu_kwargs, to_np)
+                     compare_exact_parts, compare_scalars, compare_token_grad, compare_token_values,
+                     gpu_kwargs, to_np)
 from workloads import TOKEN_WORKLOADS, WORKLOADS, make_logits_inputs, make_token_inputs
 
 pytestmark = pytest.mark.gpu
@@ -106,15 +107,9 @@ def test_fullsize_token_loss(gpu_lib, name):
     compare_exact_parts(res, ref, name)
     compare_scalars(res, ref, cfg, 1e-5, name)
     compare_token_values(res, ref, cfg, h["mask"].astype(bool), 1e-5)
-    g = to_np(res.grad)
-    rho = ref.tok["rho"]
-    lo, hi = 1 - wl.eps_low, 1 + wl.eps_high
-    amb = (np.abs(rho - hi) <= 4e-7 * rho) | (np.abs(rho - lo) <= 4e-7 * rho)
-    err = np.abs(g - ref.grad)
-    bad = (err > 1e-5 * np.max(np.abs(ref.grad))) & ~amb
-    assert not bad.any(), int(bad.sum())
+    n_amb, _ = compare_token_grad(to_np(res.grad), ref, cfg, h["mask"].astype(bool), 1e-5, name)
     clipped = int(res.counts[1])
-    assert abs(clipped - ref.clipped) <= int((amb & h["mask"]).sum())
+    assert abs(clipped - ref.clipped) <= n_amb
     res2 = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
                                    inp["mask"], eps_low=wl.eps_low, eps_high=wl.eps_high,
                                    beta=wl.beta, samples_per_prompt=wl.group_size,

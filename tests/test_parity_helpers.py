@@ -326,3 +326,50 @@ def test_stream_oracle_sequence_level():
     bad[i, tt] = (bad[i, tt].float() * 1.05).to(torch.bfloat16)
     with pytest.raises(AssertionError):
         stream_oracle(t, bad, None, cfg, groups, chunk=5, workers=2, announce=lambda m: None)
+
+
+def test_token_grad_other_branch_only_at_a_clip_bound():
+    """compare_token_grad: the oracle's float32 dlogp passes; a token whose
+    ratio sits on a clip bound may take the other branch; the same flip at a
+    token away from the bounds fails, and so does a nonzero masked token."""
+    from _parity import compare_token_grad
+    rng = np.random.default_rng(5)
+    B, T = 8, 64
+    logp = np.log(rng.uniform(1e-3, 1.0, (B, T))).astype(np.float32)
+    old = (logp + rng.normal(0, 0.3, (B, T))).astype(np.float32)
+    # two tokens per sequence exactly on the bounds 1 + eps and 1 - eps (in float32)
+    old[:, 3] = (logp[:, 3].astype(np.float64) - np.log(1.2)).astype(np.float32)
+    old[:, 5] = (logp[:, 5].astype(np.float64) - np.log(0.8)).astype(np.float32)
+    ref_lp = (logp + rng.normal(0, 0.3, (B, T))).astype(np.float32)
+    mask = np.arange(T)[None, :] < rng.integers(8, T + 1, B)[:, None]
+    r = np.array([0, 1, 1, 0, 1, 0, 0, 1], dtype=np.float32)
+    cfg = oracle.LossConfig(eps_low=0.2, eps_high=0.2, beta=0.04, reduction="sequence_mean")
+    ref = oracle.grpo_token_loss(logp, old, ref_lp, mask, r, groups=dict(samples_per_prompt=4),
+                                 cfg=cfg)
+    g = ref.grad.astype(np.float32).astype(np.float64)
+    assert compare_token_grad(g, ref, cfg, mask, 1e-5, "oracle")[1] == 0
+    adv = ref.advantages[:, None]
+    rho = ref.tok["rho"]
+    w = ref.seq_weight[:, None]
+    # flip the bound tokens to the other branch: the unclipped value is -A rho w
+    # plus the KL part, the clipped one the KL part alone
+    flip = g.copy()
+    for t in (3, 5):
+        kl_part = g[:, t] - np.where(ref.tok["clipped"][:, t], 0.0, -adv[:, 0] * rho[:, t] * w[:, 0])
+        flip[:, t] = np.where(ref.tok["clipped"][:, t], kl_part - adv[:, 0] * rho[:, t] * w[:, 0],
+                              kl_part)
+    n_amb, n_other = compare_token_grad(flip, ref, cfg, mask, 1e-5, "flipped at bounds")
+    assert n_amb >= 2 * B and n_other > 0
+    # the same flip away from a bound fails
+    far = g.copy()
+    t = 10
+    i = int(np.argmax(mask[:, t] & (adv[:, 0] != 0) & ~ref.tok["clipped"][:, t]))
+    assert mask[i, t] and adv[i, 0] != 0
+    far[i, t] = g[i, t] + adv[i, 0] * rho[i, t] * w[i, 0]
+    with pytest.raises(AssertionError):
+        compare_token_grad(far, ref, cfg, mask, 1e-5, "flipped away")
+    bad = g.copy()
+    mi, mt = np.argwhere(~mask)[0]
+    bad[mi, mt] = 1e-3
+    with pytest.raises(AssertionError):
+        compare_token_grad(bad, ref, cfg, mask, 1e-5, "masked")
