@@ -79,7 +79,7 @@ def test_masked_nan_inf_garbage_ids_do_not_leak(gpu_lib):
     assert int(dirty.status[0]) == 0
 
 
-@pytest.mark.parametrize("V", [8192, 40000, 151936])
+@pytest.mark.parametrize("V", [8192, 40000, 60000, 151936])
 def test_in_place_gradient_matches_out_of_place(gpu_lib, V):
     """The gradient written over the policy logits equals the out-of-place
     one bit for bit: resident rows at 256 and 512 threads, and streaming

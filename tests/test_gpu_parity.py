@@ -150,14 +150,19 @@ def test_f16_logits_f32_gradient(gpu_lib):
     compare_logits_grad(to_np(res.grad), r, cfg_from(wl), h["mask"], "f32")
 
 
-def test_padded_row_stride_vector_tail(gpu_lib):
-    """Rows padded to a 16-byte multiple: the vector path with a scalar tail."""
+@pytest.mark.parametrize("V,ld", [
+    (4097, 4104),     # the vector path with a scalar tail
+    (40000, 40008),   # 80 KB rows held at 512 threads x 12 chunks, padded 16-byte stride
+    (60000, 60064),   # 120 KB rows held at 512 threads x 16 chunks
+])
+def test_padded_row_stride_vector_tail(gpu_lib, V, ld):
+    """Rows padded to a 16-byte multiple: the row stride differs from V in
+    the policy, reference and gradient, and the padding stays untouched."""
     rpl = gpu_lib
-    wl = _custom(4097, "bf16", T=5)
-    announce("padded stride V=4097 ld=4104")
+    wl = _custom(V, "bf16", T=5)
+    announce(f"padded stride V={V} ld={ld}")
     inp_cpu = make_logits_inputs(wl, device="cpu", seed=5)
     B, T, V = wl.B, wl.T, wl.V
-    ld = 4104
     pol = torch.full((B, T, ld), float("nan"), dtype=torch.bfloat16)
     ref = torch.full((B, T, ld), float("inf"), dtype=torch.bfloat16)
     pol[..., :V] = inp_cpu["policy"]
