@@ -349,11 +349,6 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
           IN::cvt(rx[u], f);
 #pragma unroll
           for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
-          if (c + u * step == ca) {
-#pragma unroll
-            for (int j = 0; j < N; ++j)
-              if (j == ja) g[j] = ga;
-          }
           Out<TG, N>::store(grow, c + u * step, g);
         }
       }
@@ -371,13 +366,12 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
         IN::cvt(r, f);
 #pragma unroll
         for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
-        if (c == ca) {
-#pragma unroll
-          for (int j = 0; j < N; ++j)
-            if (j == ja) g[j] = ga;
-        }
         Out<TG, N>::store(grow, c, g);
       }
+      // the taken token's element: its chunk went out with -G p_a there; the
+      // owner overwrites that one element (a later store of the same thread
+      // to the same address lands after the first)
+      if (ca < nvec && lid == ca % NT) store_one(grow, aid, ga, (TG*)nullptr);
     }
   }
 }
@@ -445,12 +439,10 @@ __global__ __launch_bounds__(kFlatThreads) void grpo_grad_flat_kernel(RowArgs a,
       IN::cvt(rx[u], f);
 #pragma unroll
       for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
-      if (c == ca) {
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-          if (j == ja) g[j] = ga;
-      }
       Out<TG, N>::store(grow, c, g);
+      // the taken token's element, over the value just stored (same thread,
+      // same address: the later store lands last)
+      if (c == ca) store_one(grow, aid, ga, (TG*)nullptr);
     }
   }
   if (last) {

@@ -207,14 +207,12 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
       IN::cvt(xr[k], f);
 #pragma unroll
       for (int j = 0; j < N; ++j) g[j] = mG * fast_exp2(fmaf(f[j], kLog2e, -c2));
-      if (k == ka && mine) {
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-          if (j == ja) g[j] = ga;
-      }
       Out<TG, N>::store(grow, lid + k * NT, g);
     }
   }
+  // the taken token's element, over the value its chunk carried (same
+  // thread, same address: the later store lands last)
+  if (mine && ca < nvec) store_one(grow, aid, ga, (TG*)nullptr);
 }
 
 // Launch shapes, measured on MI355X (bf16 rows): how many rows are in flight
