@@ -192,15 +192,16 @@ __device__ __forceinline__ void store_one(void* row, int64_t v, float g, _Float1
 // --- per-thread online log-sum-exp over one chunk -----------------------------
 template <int N>
 __device__ __forceinline__ void lse_add(Lse& s, const float (&f)[N]) {
-  float vm = f[0];
+  // the running maximum without a branch: when it does not grow, mL is
+  // recomputed to the same rounded value and the sum is scaled by 2^0 = 1
+  // exactly, so the bits equal those of a conditional rescale
+  float vm = s.m;
 #pragma unroll
-  for (int j = 1; j < N; ++j) vm = fmaxf(vm, f[j]);
-  if (vm > s.m) {
-    const float nmL = vm * kLog2e;
-    s.s = s.s * fast_exp2(s.mL - nmL);
-    s.m = vm;
-    s.mL = nmL;
-  }
+  for (int j = 0; j < N; ++j) vm = fmaxf(vm, f[j]);
+  const float nmL = vm * kLog2e;
+  s.s = s.s * fast_exp2(s.mL - nmL);
+  s.m = vm;
+  s.mL = nmL;
   float e[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) e[j] = fast_exp2(fmaf(f[j], kLog2e, -s.mL));
