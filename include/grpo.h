@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define GRPO_ABI_VERSION 7
+#define GRPO_ABI_VERSION 8
 
 #ifndef GRPO_API
 #define GRPO_API __attribute__((visibility("default")))
@@ -117,18 +117,24 @@ typedef enum grpo_idtype { GRPO_I64 = 0, GRPO_I32 = 1 } grpo_idtype;
 
 /* Per-sequence token weight w_i ([GRPO-LOSS] Normalizer semantics; [RPP] PPO
  * and KL reduction; [GRPO-CPP] The length-normalization detail).  L_i is the
- * number of active tokens of sequence i and N = sum_i L_i.
+ * number of active tokens of sequence i, N = sum_i L_i and B_live the number
+ * of sequences with L_i > 0.
  *   GRPO_TOKEN_MEAN     w_i = 1 / max(N, 1)              (global token mean)
  *   GRPO_SEQUENCE_MEAN  w_i = 1 / (B * max(L_i, 1))      (mean in sequence, then over B)
  *   GRPO_LENGTH_ALPHA   w_i = L_i^alpha / (B * L_i), 0 when L_i = 0
  *   GRPO_FIXED_CONSTANT w_i = 1 / norm_constant          (a declared denominator)
+ *   GRPO_SEQUENCE_MEAN_LIVE  w_i = 1 / (B_live * L_i), 0 when L_i = 0
+ *                       (mean in sequence, then over the sequences with an
+ *                       active token: [GRPO-LOSS] Normalizer semantics,
+ *                       per_sequence_then_mean)
  * The weights are computed in binary64 and are bit-exact for alpha in
  * {0, 0.5, 1}; other alpha use pow() and may differ in the last bit. */
 typedef enum grpo_reduction {
   GRPO_TOKEN_MEAN = 0,
   GRPO_SEQUENCE_MEAN = 1,
   GRPO_LENGTH_ALPHA = 2,
-  GRPO_FIXED_CONSTANT = 3
+  GRPO_FIXED_CONSTANT = 3,
+  GRPO_SEQUENCE_MEAN_LIVE = 4
 } grpo_reduction;
 
 /* Per-token policy loss l(logp) and its derivative, rho = exp(logp - old),

@@ -102,7 +102,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-REDUCTIONS = ("token_mean", "sequence_mean", "length_alpha", "fixed_constant")
+REDUCTIONS = ("token_mean", "sequence_mean", "length_alpha", "fixed_constant",
+              "per_sequence_then_mean")
 
 
 class OracleInputError(ValueError):
@@ -220,6 +221,11 @@ def sequence_weights(mask, reduction="token_mean", alpha=None, norm_constant=Non
       sequence_mean  1 / (B * max(L_i, 1))          (mean within, then over B)
       length_alpha   L_i**alpha / (B * L_i), 0 if L_i = 0
       fixed_constant 1 / norm_constant            (a declared denominator)
+      per_sequence_then_mean
+                     1 / (B_live * L_i), 0 if L_i = 0, with B_live the
+                     number of sequences that have an active token (the
+                     mean within each sequence, then over the live ones:
+                     [GRPO-LOSS] Normalizer semantics)
     """
     m = np.asarray(mask).astype(bool)
     if m.ndim != 2:
@@ -248,6 +254,11 @@ def sequence_weights(mask, reduction="token_mean", alpha=None, norm_constant=Non
         if norm_constant is None or not norm_constant > 0:
             raise OracleInputError("fixed_constant needs norm_constant > 0")
         w = np.full(B, 1.0 / float(norm_constant), dtype=np.float64)
+    elif reduction == "per_sequence_then_mean":
+        live = L > 0
+        n_live = int(live.sum())
+        w = np.zeros(B, dtype=np.float64)
+        w[live] = 1.0 / (float(n_live) * L[live].astype(np.float64))
     else:
         raise OracleInputError(f"unknown reduction {reduction!r}")
     return L, N, w

@@ -8,13 +8,19 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgrpo.so")
 
-GRPO_ABI_VERSION = 7
+GRPO_ABI_VERSION = 8
 
 GRPO_F32, GRPO_BF16, GRPO_F16 = 0, 1, 2
 GRPO_I64, GRPO_I32 = 0, 1
 GRPO_TOKEN_MEAN, GRPO_SEQUENCE_MEAN, GRPO_LENGTH_ALPHA, GRPO_FIXED_CONSTANT = 0, 1, 2, 3
+GRPO_SEQUENCE_MEAN_LIVE = 4
+# "global_active_tokens" and "per_sequence_then_mean" are the "GRPO Loss"
+# page's names (Normalizer semantics) for the token mean and the mean over
+# live sequences
 REDUCTION_CODES = {"token_mean": GRPO_TOKEN_MEAN, "sequence_mean": GRPO_SEQUENCE_MEAN,
-                   "length_alpha": GRPO_LENGTH_ALPHA, "fixed_constant": GRPO_FIXED_CONSTANT}
+                   "length_alpha": GRPO_LENGTH_ALPHA, "fixed_constant": GRPO_FIXED_CONSTANT,
+                   "per_sequence_then_mean": GRPO_SEQUENCE_MEAN_LIVE,
+                   "global_active_tokens": GRPO_TOKEN_MEAN}
 PG_LOSS_CODES = {"clip": 0, "cispo": 1, "sapo": 2, "reinforce": 3, "on_policy": 4, "gspo": 5,
                  "real": 6}
 KL_ESTIMATOR_CODES = {"k3": 0, "k1": 1, "k2": 2}

@@ -81,7 +81,7 @@ grpo_status check_cfg(const grpo_cfg* c, bool has_ref, bool has_gen) {
   if (!(c->eps_high >= 0.0) || !isfinite(c->eps_high)) return GRPO_ERR_CONFIG;
   if (!(c->beta >= 0.0) || !isfinite(c->beta)) return GRPO_ERR_CONFIG;
   if (c->beta > 0.0 && !has_ref) return GRPO_ERR_CONFIG;
-  if (c->reduction < GRPO_TOKEN_MEAN || c->reduction > GRPO_FIXED_CONSTANT) return GRPO_ERR_CONFIG;
+  if (c->reduction < GRPO_TOKEN_MEAN || c->reduction > GRPO_SEQUENCE_MEAN_LIVE) return GRPO_ERR_CONFIG;
   if (c->reduction == GRPO_LENGTH_ALPHA && !(c->alpha >= 0.0 && c->alpha <= 1.0))
     return GRPO_ERR_CONFIG;
   if (c->reduction == GRPO_FIXED_CONSTANT && !(c->norm_constant > 0.0 && isfinite(c->norm_constant)))
@@ -500,7 +500,11 @@ grpo_status grpo_token_loss(const float* logp, const float* old_logp, const floa
   // the sequence-level losses need everything before their sequence phase
   const bool seqlv = is_sequence_level(cfg);
   const bool seq_stat = gen_logp != nullptr && cfg->tis_type == GRPO_TIS_SEQ_MASK;
-  const int weights_mode = seqlv ? 0 : ((cfg->reduction != GRPO_TOKEN_MEAN && !seq_stat) ? 2 : 1);
+  // weights needing a batch count (N, or the live sequences) take the prep
+  // kernel's counts (mode 1); the others are formed by the token kernel alone
+  const bool needs_count =
+      cfg->reduction == GRPO_TOKEN_MEAN || cfg->reduction == GRPO_SEQUENCE_MEAN_LIVE;
+  const int weights_mode = seqlv ? 0 : ((!needs_count && !seq_stat) ? 2 : 1);
   GroupSpec grp{};
   if (weights_mode == 2) {
     st = copy_offsets(w, groups, s, &grp);

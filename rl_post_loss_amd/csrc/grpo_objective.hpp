@@ -84,14 +84,19 @@ __device__ __forceinline__ float clamp_sym(float x, float v) {
 
 // Per-sequence token weight w_i of the reduction (binary64, contraction
 // off): token mean 1/N ("GRPO Loss", Normalizer semantics), sequence mean
-// 1/(B L_i) (Relax REINFORCE++ page, PPO and KL reduction), length weighting
-// L_i^alpha / (B L_i) (grpo.cpp README, The length-normalization detail), or a
-// declared constant.  Shared by the weights kernel and the token kernel so
-// both give the same bits.
+// 1/(B L_i) (Relax REINFORCE++ page, PPO and KL reduction), the mean over
+// live sequences 1/(B_live L_i) ("GRPO Loss", Normalizer semantics,
+// per_sequence_then_mean), length weighting L_i^alpha / (B L_i) (grpo.cpp
+// README, The length-normalization detail), or a declared constant.  `cnt`
+// is the batch count the reduction needs: N for the token mean, B_live for
+// the live-sequence mean (reduction_count).  Shared by the weights kernel
+// and the token kernel so both give the same bits.
 __device__ inline double sequence_weight(int32_t reduction, double alpha, double norm_constant,
-                                  int64_t B, int64_t L, int64_t N) {
+                                  int64_t B, int64_t L, int64_t cnt) {
 #pragma clang fp contract(off)
-  if (reduction == GRPO_TOKEN_MEAN) return 1.0 / double(N > 0 ? N : 1);
+  if (reduction == GRPO_TOKEN_MEAN) return 1.0 / double(cnt > 0 ? cnt : 1);
+  if (reduction == GRPO_SEQUENCE_MEAN_LIVE)
+    return L > 0 ? 1.0 / (double(cnt > 0 ? cnt : 1) * double(L)) : 0.0;
   if (reduction == GRPO_FIXED_CONSTANT) return 1.0 / norm_constant;
   if (reduction == GRPO_SEQUENCE_MEAN) return 1.0 / (double(B) * double(L > 0 ? L : 1));
   if (L == 0) return 0.0;
@@ -102,6 +107,12 @@ __device__ inline double sequence_weight(int32_t reduction, double alpha, double
   else if (alpha == 1.0) num = Lf;
   else num = pow(Lf, alpha);
   return num / (double(B) * Lf);
+}
+
+// A sequence's share of the batch count sequence_weight needs: its L_i for
+// the token mean, 1 if it has an active token for the live-sequence mean.
+__device__ __forceinline__ long long reduction_count(int32_t reduction, long long L) {
+  return reduction == GRPO_SEQUENCE_MEAN_LIVE ? (L > 0 ? 1 : 0) : L;
 }
 
 // Off-policy weight of one token: exp(old - gen), truncated for tis/icepop.

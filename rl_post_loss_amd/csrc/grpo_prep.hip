@@ -117,11 +117,16 @@ __global__ __launch_bounds__(kPrepThreads) void grpo_prep_kernel(PrepArgs a) {
 __global__ __launch_bounds__(kWeightThreads) void grpo_weights_kernel(PrepArgs a) {
   __shared__ long long sh_i64[kWeightThreads / kWave];
   const int tid = threadIdx.x;
-  long long n = 0;
-  for (int64_t k = tid; k < a.B; k += kWeightThreads) n += a.L[k];
-  const long long N = block_sum_i64<kWeightThreads>(n, sh_i64);
+  long long n = 0, nc = 0;
   for (int64_t k = tid; k < a.B; k += kWeightThreads) {
-    const double wk = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[k], N);
+    n += a.L[k];
+    nc += reduction_count(a.reduction, a.L[k]);
+  }
+  const long long N = block_sum_i64<kWeightThreads>(n, sh_i64);
+  // the reduction's own count (N again, or the live sequences)
+  const long long C = a.reduction == GRPO_SEQUENCE_MEAN_LIVE ? block_sum_i64<kWeightThreads>(nc, sh_i64) : N;
+  for (int64_t k = tid; k < a.B; k += kWeightThreads) {
+    const double wk = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[k], C);
     a.w[k] = wk;
     if (a.seq_weight_out) a.seq_weight_out[k] = float(wk);
   }

@@ -290,14 +290,15 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
     wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, Li, 0);
   } else if constexpr (kWeights == 1) {
     adv = a.A[i];
-    // token mean needs N = sum_j L_j (the prep kernel's counts, fixed tree)
-    long long N = 0;
-    if (a.reduction == GRPO_TOKEN_MEAN) {
+    // the token mean needs N = sum_j L_j, the live-sequence mean the number
+    // of sequences with an active token (the prep kernel's counts, fixed tree)
+    long long C = 0;
+    if (a.reduction == GRPO_TOKEN_MEAN || a.reduction == GRPO_SEQUENCE_MEAN_LIVE) {
       long long n = 0;
-      for (int64_t j = tid; j < a.B; j += kTokThreads) n += a.L[j];
-      N = block_sum_i64<kTokThreads>(n, sh_i64);
+      for (int64_t j = tid; j < a.B; j += kTokThreads) n += reduction_count(a.reduction, a.L[j]);
+      C = block_sum_i64<kTokThreads>(n, sh_i64);
     }
-    wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[i], N);
+    wi = sequence_weight(a.reduction, a.alpha, a.norm_constant, a.B, a.L[i], C);
   } else {
     adv = a.A[i];
     wi = a.w[i];

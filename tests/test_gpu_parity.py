@@ -41,9 +41,13 @@ def oracle_logits(h, wl, reduction=None, with_ref=True):
                                     groups=wl.groups_kwargs(), cfg=cfg_from(wl, reduction))
 
 
-def check_logits_case(rpl, wl, seed=0, reduction=None):
-    announce(f"logits parity {wl.name} reduction={reduction or wl.reductions[0]} seed={seed}")
+def check_logits_case(rpl, wl, seed=0, reduction=None, empty=()):
+    """``empty``: sequences whose whole mask row is cleared first."""
+    announce(f"logits parity {wl.name} reduction={reduction or wl.reductions[0]} seed={seed}"
+             + (f" empty={list(empty)}" if empty else ""))
     inp_cpu = make_logits_inputs(wl, device="cpu", seed=seed)
+    for i in empty:
+        inp_cpu["mask"][i] = False
     inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
     res = run_logits(rpl, inp, wl, reduction)
     h = host_inputs(inp_cpu)
@@ -368,3 +372,85 @@ def test_token_loss_other_reductions(gpu_lib, reduction):
 def test_token_loss_unaligned_scalar_path(gpu_lib):
     """T not a multiple of 4: the scalar path of the token kernel."""
     check_token_case(gpu_lib, TOKEN_WORKLOADS["token_loss_ragged"], B=32, T=131)
+
+
+# ---------------------------------------------------------------------------
+# the mean over live sequences ("GRPO Loss", Normalizer semantics,
+# per_sequence_then_mean) and the page's reduction names
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,dtype", [(1000, "f32"), (8200, "bf16"), (40000, "bf16"),
+                                     (70001, "bf16"), (151936, "bf16")])
+def test_per_sequence_then_mean_logits(gpu_lib, V, dtype):
+    """Fused logits call on each row-kernel path with two empty sequences:
+    the weights bit-exact (1 / (B_live L_i), 0 for the empty ones), the
+    scalars and every gradient row against the oracle."""
+    check_logits_case(gpu_lib, _custom(V, dtype, T=6 if V < 100000 else 3, sizes=(4, 4)), seed=31,
+                      reduction="per_sequence_then_mean", empty=(1, 5))
+
+
+@pytest.mark.parametrize("T", [300, 301])
+def test_per_sequence_then_mean_token_loss(gpu_lib, T):
+    """Log-prob token loss (vector and scalar paths) with three empty
+    sequences: the live count comes from the prep kernel's counts."""
+    from _parity import compare_token_grad
+    wl = TOKEN_WORKLOADS["token_loss_ragged"]
+    announce(f"token loss per_sequence_then_mean T={T}")
+    inp_cpu = make_token_inputs(wl, device="cpu", seed=5, B=64, T=T)
+    inp_cpu["mask"][[3, 17, 40]] = False
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    res = gpu_lib.grpo_token_loss(inp["logp"], inp["old_logps"], inp["ref_logp"], inp["rewards"],
+                                  inp["mask"], eps_low=wl.eps_low, eps_high=wl.eps_high,
+                                  beta=wl.beta, samples_per_prompt=wl.group_size,
+                                  reduction="per_sequence_then_mean", per_token=True)
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    cfg = oracle.LossConfig(eps_low=wl.eps_low, eps_high=wl.eps_high, beta=wl.beta,
+                            reduction="per_sequence_then_mean")
+    ref = oracle.grpo_token_loss(h["logp"], h["old_logps"], h["ref_logp"], h["mask"], h["rewards"],
+                                 groups=dict(samples_per_prompt=wl.group_size), cfg=cfg)
+    w = to_np(res.seq_weight)
+    assert np.all(w[[3, 17, 40]] == 0.0)
+    compare_exact_parts(res, ref)
+    compare_scalars(res, ref, cfg, 1e-5)
+    compare_token_grad(to_np(res.grad), ref, cfg, h["mask"].astype(bool), 1e-5, "live mean")
+
+
+def test_per_sequence_then_mean_autograd_split(gpu_lib):
+    """grpo_loss (forward pass, then the gradient-only pass) under the live
+    mean with empty sequences, against the oracle."""
+    wl = _custom(40000, "bf16", T=6, sizes=(4, 4))
+    red = "per_sequence_then_mean"
+    announce("autograd split per_sequence_then_mean")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=33)
+    inp_cpu["mask"][[2, 6]] = False
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    pol = inp["policy"].clone().requires_grad_(True)
+    loss, _, _ = gpu_lib.grpo_loss(pol, inp["ref"], inp["action_ids"], inp["old_logps"],
+                                   inp["rewards"], inp["mask"], **gpu_kwargs(wl, red))
+    loss.backward()
+    torch.cuda.synchronize()
+    h = host_inputs(inp_cpu)
+    ref = oracle_logits(h, wl, red)
+    cfg = cfg_from(wl, red)
+    assert abs(float(loss.detach()) - ref.loss) <= 1e-4 * abs(ref.loss)
+    compare_logits_grad(to_np(pol.grad), ref, cfg, h["mask"], "bf16", "live mean split")
+
+
+def test_reduction_names_of_the_loss_page(gpu_lib):
+    """'global_active_tokens' is the token mean under another name: the
+    same bits; 'per_sequence_then_mean' equals the sequence mean when no
+    sequence is empty."""
+    wl = _custom(3000, "bf16", T=6, sizes=(4, 4))
+    announce("reduction names")
+    inp_cpu = make_logits_inputs(wl, device="cpu", seed=35)
+    inp = {k: v.to(DEV) for k, v in inp_cpu.items()}
+    assert bool(inp["mask"].any(dim=1).all())
+    a = run_logits(gpu_lib, inp, wl, "token_mean")
+    b = run_logits(gpu_lib, inp, wl, "global_active_tokens")
+    assert torch.equal(a.scalars.view(torch.int32), b.scalars.view(torch.int32))
+    assert torch.equal(a.grad.view(torch.int16), b.grad.view(torch.int16))
+    c = run_logits(gpu_lib, inp, wl, "sequence_mean")
+    d = run_logits(gpu_lib, inp, wl, "per_sequence_then_mean")
+    assert torch.equal(c.scalars.view(torch.int32), d.scalars.view(torch.int32))
+    assert torch.equal(c.grad.view(torch.int16), d.grad.view(torch.int16))

@@ -33,6 +33,7 @@ SEQ_CASES = [
     dict(pg_loss="gspo", reduction="length_alpha", alpha=0.5, kl_estimator="k2"),
     dict(pg_loss="gspo", reduction="sequence_mean", tis_type="tis", tis_ratio_max=1.3),
     dict(pg_loss="gspo", reduction="fixed_constant", norm_constant=300.0, is_only=True),
+    dict(pg_loss="gspo", reduction="per_sequence_then_mean"),
     dict(pg_loss="real"),
     dict(pg_loss="real", real_tau=0.2, kl_input_clamp=0.2),
     dict(tis_type="seq_mask", tis_ratio_min=0.8, tis_ratio_max=1.25),

@@ -227,6 +227,40 @@ def test_reduction_weight_relations():
     assert ws[2] == 1.0 / 6
 
 
+def test_per_sequence_then_mean_weights():
+    """The live-sequence mean ("GRPO Loss", Normalizer semantics): every
+    sequence with an active token carries total weight 1 / B_live, an empty
+    one 0; with no empty sequence it equals the sequence mean; the scalar is
+    the plain mean over live sequences of each sequence's token mean."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 10, 7)
+    ragged = np.arange(9)[None, :] < lens[:, None]
+    _, _, wl = orc.sequence_weights(ragged, "per_sequence_then_mean")
+    _, _, ws = orc.sequence_weights(ragged, "sequence_mean")
+    assert np.array_equal(wl, ws)
+    ragged[[1, 4]] = False
+    L, N, wl = orc.sequence_weights(ragged, "per_sequence_then_mean")
+    assert wl[1] == 0.0 and wl[4] == 0.0
+    live = L > 0
+    np.testing.assert_allclose((wl * L)[live], 1.0 / 5, rtol=1e-15)
+    assert abs(float(np.sum(wl * L)) - 1.0) < 1e-15
+    # no active token anywhere: every weight is 0
+    _, N0, w0 = orc.sequence_weights(np.zeros((3, 4), dtype=bool), "per_sequence_then_mean")
+    assert N0 == 0 and np.all(w0 == 0.0)
+    # the token loss with these weights is the mean over live sequences of
+    # the per-sequence mean token loss (brute force from the token values)
+    T = 9
+    logp = np.log(rng.uniform(0.05, 1.0, (7, T)))
+    old = logp + rng.normal(0, 0.3, (7, T))
+    ref = logp + rng.normal(0, 0.3, (7, T))
+    r = np.array([1, 0, 1, 1, 0, 0, 1], dtype=np.float64)
+    cfg = LossConfig(eps_low=0.2, eps_high=0.2, beta=0.0, reduction="per_sequence_then_mean")
+    res = orc.grpo_token_loss(logp, old, ref, ragged, r, groups=dict(group_boundaries=[0, 3, 7]),
+                              cfg=cfg)
+    per_seq = [np.mean(res.tok["loss"][i][ragged[i]]) for i in range(7) if ragged[i].any()]
+    assert abs(res.policy_loss - float(np.mean(per_seq))) < 1e-14
+
+
 # ---------------------------------------------------------------------------
 # closed-form tiny cases (worked out by hand from the definitions)
 # ---------------------------------------------------------------------------
@@ -507,6 +541,9 @@ def _torch_objective(x, y, ids, old, mask, r, offsets, cfg, loo, scale_std, std_
         w = torch.full((B,), 1.0 / max(float(L.sum()), 1.0), dtype=torch.float64)
     elif cfg.reduction == "sequence_mean":
         w = 1.0 / (B * torch.clamp(L, min=1.0))
+    elif cfg.reduction == "per_sequence_then_mean":
+        n_live = float((L > 0).sum())
+        w = torch.where(L > 0, 1.0 / (max(n_live, 1.0) * torch.clamp(L, min=1.0)), torch.zeros_like(L))
     else:
         w = torch.where(L > 0, L ** cfg.alpha / (B * torch.clamp(L, min=1.0)), torch.zeros_like(L))
     zero = torch.zeros_like(per_tok)
@@ -517,16 +554,19 @@ def _torch_objective(x, y, ids, old, mask, r, offsets, cfg, loo, scale_std, std_
     return total.item(), pol.item(), klv.item(), xt.grad.numpy()
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_against_independent_autograd(seed):
     rng = np.random.default_rng(100 + seed)
-    red, alpha = [("token_mean", None), ("sequence_mean", None), ("length_alpha", 0.5)][seed % 3]
+    red, alpha = [("token_mean", None), ("sequence_mean", None), ("length_alpha", 0.5),
+                  ("per_sequence_then_mean", None)][seed % 4]
     loo = bool(seed % 2)
     cfg = LossConfig(eps_low=0.2, eps_high=0.28 if seed % 2 else 0.2, beta=0.04, reduction=red, alpha=alpha)
     sizes = [2, 4, 2] if seed < 3 else [4, 4]
     offsets = list(np.concatenate([[0], np.cumsum(sizes)]))
     B = offsets[-1]
     x, y, ids, old, mask, r = _rand_case(rng, B=B, T=6, V=13, spp=2, scale=2.0, old_noise=0.3)
+    if red == "per_sequence_then_mean":
+        mask[1] = False   # an empty sequence: the live count differs from B
     g = dict(group_boundaries=offsets, leave_one_out=loo)
     res = orc.grpo_loss_fwd_bwd(x, y, ids, old, mask, r, groups=g, cfg=cfg)
     tot, pol, klv, grad = _torch_objective(x, y, ids, old, mask, r, offsets, cfg, loo, True)
