@@ -59,10 +59,11 @@ def test_noalloc_matches_workspace_entry_two_calls(gpu_lib):
 
 
 def test_noalloc_csr_groups_and_reductions(gpu_lib):
-    """CSR groups (the offsets copied into the scratch array), three
+    """CSR groups (the offsets copied into the scratch array), four
     reductions in a row, each smaller than the one before."""
     wl = WORKLOADS["logits_csr_v128256"]
-    for red, T in (("token_mean", 24), ("sequence_mean", 12), ("length_alpha", 5)):
+    for red, T in (("token_mean", 24), ("sequence_mean", 12), ("length_alpha", 5),
+                   ("per_sequence_then_mean", 3)):
         _check(gpu_lib, wl.scaled(T=T, prompts=4 if T > 12 else 3), reduction=red, seed=T)
 
 
