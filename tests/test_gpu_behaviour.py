@@ -153,7 +153,7 @@ def test_no_active_tokens(gpu_lib):
     announce("no active tokens")
     _, inp = _inputs(wl, seed=16)
     mask = torch.zeros_like(inp["mask"])
-    for red in ("token_mean", "sequence_mean", "length_alpha"):
+    for red in ("token_mean", "sequence_mean", "length_alpha", "per_sequence_then_mean"):
         res = gpu_lib.grpo_loss_fwd_bwd(inp["policy"], inp["ref"], inp["action_ids"],
                                         inp["old_logps"], inp["rewards"], mask,
                                         **dict(gpu_kwargs(wl), reduction=red, alpha=0.5))
@@ -300,10 +300,11 @@ def test_confident_token_gradient_relative_accuracy(gpu_lib):
 
 
 @pytest.mark.parametrize("reduction", ["token_mean", "sequence_mean", "length_alpha",
-                                       "fixed_constant"])
+                                       "fixed_constant", "per_sequence_then_mean"])
 def test_token_loss_fault_bits(gpu_lib, reduction):
     """The log-prob entry point's fault bits, on both of its launch
-    structures (token mean: counts, token and scalar kernels; the others: the
+    structures (token mean and the mean over live sequences, whose weights
+    need a batch count: counts, token and scalar kernels; the others: the
     token kernel forms its own counts and reports faults per sequence): no
     active token gives NO_TOKENS with zero loss and gradient; a non-finite
     per-token value at an active slot gives NONFINITE; the next clean call
