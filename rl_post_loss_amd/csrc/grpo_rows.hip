@@ -84,7 +84,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void grpo_rows_kernel(RowArgs 
   typename IN::raw_t* const hold = reinterpret_cast<typename IN::raw_t*>(grpo_rows_hold);
 
   const int lid = threadIdx.x % NT;
-  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / NT;
+  const int64_t row = int64_t(xcd_runs(blockIdx.x, gridDim.x, GRPO_XCD_ROWS)) * RPB + threadIdx.x / NT;
   if (row >= a.rows) return;  // only possible when RPB > 1 (no block barriers then)
 
   const int64_t V = a.V;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kFlatThreads) void grpo_grad_flat_kernel(RowArgs a,
   typedef In<TI, true> IN;
   constexpr int N = IN::N;
   typedef typename IN::raw_t raw_t;
-  const uint32_t b = blockIdx.x;
+  const uint32_t b = xcd_runs(blockIdx.x, gridDim.x, GRPO_XCD_FLAT);
   const uint32_t row32 = b / bpr;
   const int64_t row = row32;
   const uint32_t seg = b - row32 * bpr;

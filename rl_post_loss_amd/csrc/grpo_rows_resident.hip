@@ -33,7 +33,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_resident_kernel(RowArgs a) {
   __shared__ float sh_bcast[4];
 
   const int lid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int64_t row = xcd_runs(blockIdx.x, gridDim.x, GRPO_XCD_ROWS);
   const int64_t V = a.V;
   const int64_t nvec = V / N;
   const int64_t tail0 = nvec * N;
