@@ -36,6 +36,9 @@ constexpr int kTokQuads = GRPO_TOK_QUADS;
 // arithmetic and stores (mask words two rounds ahead).  GRPO_TOK_SPEC: data
 // loads that do not wait for the mask words (1: the first round, 2: every
 // round); a masked quad's values are then read but never used.
+#ifndef GRPO_XCD_TOK
+#define GRPO_XCD_TOK 4  // token kernel: runs of 4 consecutive sequences per XCD (xcd_runs)
+#endif
 #ifndef GRPO_TOK_PIPE
 #define GRPO_TOK_PIPE 0
 #endif
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kTokThreads) void grpo_token_kernel(TokenArgs a) {
   __shared__ long long sh_i64[kTokThreads / kWave];
   __shared__ float sh_r[kWeights == 2 ? kRewardStage : 1];
   __shared__ float sh_adv;
-  const int64_t i = blockIdx.x;
+  const int64_t i = xcd_runs(blockIdx.x, gridDim.x, GRPO_XCD_TOK);
   const int tid = threadIdx.x;
   const int64_t base = i * a.T;
   const bool vec = (a.T & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.logp) |

@@ -22,25 +22,8 @@ enum RowMode { kFused = 0, kForward = 1, kBackward = 2 };
 #ifndef GRPO_XCD_FLAT
 #define GRPO_XCD_FLAT 16  // the flat gradient pass: runs of 16 consecutive 4 KB blocks per XCD
 #endif
+// (xcd_runs() in grpo_device.hpp; the launch order is remapped on the device)
 
-// The dispatcher hands a launch's blocks to the chip's 8 XCDs in turn (block
-// b to XCD b mod 8), and each XCD has its own L2 and address translation
-// caches.  xcd_runs() permutes [0, n) so that each XCD takes runs of C
-// consecutive work items: the items are cut into spans of 8 C, and in span
-// s the XCD's blocks take its run (x + s) mod 8 in order.  The rows an XCD
-// has in flight are then neighbours in memory, not spread over eight times
-// the address range, while every span is still shared evenly by the XCDs;
-// the rotation keeps a span that is only partly busy (the end of a ragged
-// sequence) from loading the same XCDs every time.  Items past the last
-// whole span keep their place.  C = 0 keeps the launch order.
-__device__ __forceinline__ uint32_t xcd_runs(uint32_t b, uint32_t n, uint32_t C) {
-  if (C == 0u) return b;
-  const uint32_t span = 8u * C;
-  const uint32_t whole = n - n % span;
-  if (b >= whole) return b;
-  const uint32_t x = b % 8u, k = b / 8u, s = k / C;
-  return s * span + ((x + s) % 8u) * C + k % C;
-}
 
 // --- element access ---------------------------------------------------------
 // In<T, VEC>::N values per chunk; a chunk is one 16-byte load when VEC.
