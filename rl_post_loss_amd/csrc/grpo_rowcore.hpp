@@ -20,7 +20,7 @@ enum RowMode { kFused = 0, kForward = 1, kBackward = 2 };
 #define GRPO_XCD_ROWS 16  // row kernels: runs of 16 consecutive rows (row blocks) per XCD
 #endif
 #ifndef GRPO_XCD_FLAT
-#define GRPO_XCD_FLAT 16  // the flat gradient pass: runs of 16 consecutive 4 KB blocks per XCD
+#define GRPO_XCD_FLAT 64  // the flat gradient pass: runs of 64 consecutive 4 KB blocks (256 KB) per XCD
 #endif
 // (xcd_runs() in grpo_device.hpp; the launch order is remapped on the device)
 
