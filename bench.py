@@ -105,7 +105,7 @@ def byte_model(wl, active, rows):
     return active * V * (3 * bx + bg) + (rows - active) * V * bg + rows * (8 + 4 + 1)
 
 
-HELD_CHUNKS = 6 * 1024   # 16-byte policy chunks per row the fused streaming kernel keeps in LDS
+HELD_CHUNKS = 8 * 1024   # 16-byte policy chunks per row the fused streaming kernel keeps in LDS
 
 
 def min_bytes(wl, active, rows, resident):

@@ -43,10 +43,11 @@
                                // GSPO at V = 32,000: 1.84 -> 1.74 ms)
 #endif
 #ifndef GRPO_HOLD_CHUNKS
-#define GRPO_HOLD_CHUNKS 6     // fused 1024-thread rows: chunks per thread kept in LDS from
+#define GRPO_HOLD_CHUNKS 8     // fused 1024-thread rows: chunks per thread kept in LDS from
                                // pass 1 to pass 2, the row's first ones, which pass 2 re-reads
-                               // last (96 KB per block; V = 151,936: 11.69 -> 11.04 ms; 4, 5,
-                               // 7, 8, 9 chunks: 11.30, 11.14, 11.07, 11.10, 11.18 ms)
+                               // last (128 KB per block; none -> 6 took V = 151,936 from 11.69
+                               // to 11.04 ms; with the XCD-aware row order 8 beats 6 by
+                               // 0.3-0.8%: 10.47 -> 10.44 ms, CSR V = 128,256 8.72 -> 8.67 ms)
 #endif
 #ifndef GRPO_Y_NONTEMPORAL
 #define GRPO_Y_NONTEMPORAL 1   // the reference row is read once: non-temporal loads
